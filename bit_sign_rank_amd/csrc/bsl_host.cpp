@@ -1,0 +1,481 @@
+// Host side of libbitstack_linear: argument checking, the sign packer ("bitstack_pack"),
+// the device-resident block stack and forward dispatch.  See include/bitstack_linear.h
+// for the interface contract.
+#include "bitstack_linear.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "bsl_internal.h"
+
+using namespace bsl;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();  // clear the sticky error so the next call starts clean
+  return fail(e == hipErrorOutOfMemory ? BSL_ENOMEM : BSL_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool shape_ok(int64_t m, int64_t d) { return m >= 1 && m <= (1 << 20) && d >= 8 && d <= (1 << 20) && d % 8 == 0; }
+
+// ------------------------------------------------------------------ packing
+// Word q of lane L = 16 g + i in tile (row tile t, chunk c) collects, for plane b and
+// half h, the sign of column 512 c + 32 b + 8 g + 2 q + h of row 16 t + i.  In the
+// row-major source that sign is bit (2 q + h) of byte 64 c + 4 b + g of the row.
+void pack_rows(const uint8_t* src, int64_t m, int64_t d, uint8_t* out, int64_t r0, int64_t r1) {
+  const int64_t nch = pad_cols(d) / kChunkCols;
+  const int64_t rowbytes = d / 8;
+  for (int64_t r = r0; r < r1; ++r) {
+    const int64_t t = r / kTileRows, i = r % kTileRows;
+    const uint8_t* row = r < m ? src + r * rowbytes : nullptr;
+    for (int64_t c = 0; c < nch; ++c) {
+      uint8_t* tile = out + (t * nch + c) * kTileBytes;
+      for (int g = 0; g < 4; ++g) {
+        uint8_t bytes[kPlanes];
+        for (int b = 0; b < kPlanes; ++b) {
+          const int64_t byte = 64 * c + 4 * b + g;  // within the row
+          bytes[b] = (row && byte < rowbytes) ? row[byte] : 0;
+        }
+        uint32_t words[4];
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w = 0;
+          for (int b = 0; b < kPlanes; ++b) {
+            w |= (uint32_t)((bytes[b] >> (2 * q)) & 1u) << b;
+            w |= (uint32_t)((bytes[b] >> (2 * q + 1)) & 1u) << (b + 16);
+          }
+          words[q] = w;
+        }
+        std::memcpy(tile + (16 * g + i) * 16, words, 16);  // little-endian words
+      }
+    }
+  }
+}
+
+void pack_signs_mt(const uint8_t* src, int64_t m, int64_t d, uint8_t* out) {
+  const int64_t mp = pad_rows(m);
+  unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  const int64_t work = mp * pad_cols(d);
+  if (work < (int64_t)1 << 22) nt = 1;
+  std::vector<std::thread> th;
+  const int64_t per = (mp / kTileRows + nt - 1) / nt * kTileRows;
+  for (unsigned k = 0; k < nt; ++k) {
+    const int64_t r0 = k * per, r1 = std::min(mp, r0 + per);
+    if (r0 >= r1) break;
+    th.emplace_back(pack_rows, src, m, d, out, r0, r1);
+  }
+  for (auto& t : th) t.join();
+}
+
+// U (m x 16, row-major fp16) -> [m_pad/16][64][4]: lane L, slot v holds U[16 t + 4 (L/16) + v][L % 16].
+void tile_u(const uint16_t* u, int64_t m, uint16_t* out) {
+  const int64_t mt = pad_rows(m) / kTileRows;
+  for (int64_t t = 0; t < mt; ++t)
+    for (int L = 0; L < 64; ++L)
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = 16 * t + 4 * (L / 16) + v;
+        out[(t * 64 + L) * 4 + v] = row < m ? u[row * kRank + (L % 16)] : 0;
+      }
+}
+
+// V (d x 16, row-major fp16) -> [d_pad/512][16][64][8]: lane L of plane b, slot j holds
+// V[512 c + 32 b + 8 (L/16) + j][L % 16].
+void tile_v(const uint16_t* v, int64_t d, uint16_t* out) {
+  const int64_t nch = pad_cols(d) / kChunkCols;
+  for (int64_t c = 0; c < nch; ++c)
+    for (int b = 0; b < kPlanes; ++b)
+      for (int L = 0; L < 64; ++L)
+        for (int j = 0; j < 8; ++j) {
+          const int64_t col = 512 * c + 32 * b + 8 * (L / 16) + j;
+          out[((c * kPlanes + b) * 64 + L) * 8 + j] = col < d ? v[col * kRank + (L % 16)] : 0;
+        }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ stack
+struct Slot {
+  void* mem = nullptr;  // one device allocation per block
+  size_t bytes = 0;
+};
+
+struct Weight {
+  int32_t m = 0, d = 0, mt = 0, nch = 0;
+  int32_t n = 0;  // loaded blocks
+  std::vector<bsl_block_src> src;
+  std::vector<Slot> slots;          // [n_cap]
+  BlockPtrs* dtable = nullptr;      // device [n_cap]
+  float* partial = nullptr;         // workspace
+  uint32_t* counters = nullptr;
+  size_t partial_floats = 0, counter_count = 0;
+};
+
+struct bsl_stack {
+  int device = 0;
+  int32_t k = 16, n_cap = 0;
+  uint64_t budget = 0, resident = 0;
+  std::vector<Weight> w;
+};
+
+namespace {
+
+size_t slot_bytes(int64_t m, int64_t d) {
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + (size_t)pad_cols(d) * kRank * 2;
+}
+
+BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
+  BlockPtrs p;
+  const uint8_t* base = static_cast<const uint8_t*>(s.mem);
+  const size_t sb = (size_t)pad_rows(m) * pad_cols(d) / 8;
+  const size_t ub = (size_t)pad_rows(m) * kRank * 2;
+  p.signs = base;
+  p.u = reinterpret_cast<const uint16_t*>(base + sb);
+  p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
+  return p;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
+  std::vector<BlockPtrs> tab(s->n_cap);
+  for (int32_t i = 0; i < s->n_cap; ++i)
+    tab[i] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr};
+  hipError_t e = hipMemcpyAsync(W.dtable, tab.data(), sizeof(BlockPtrs) * s->n_cap, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
+}
+
+int decode_groups(const Weight& W) { return (W.mt + kDecodeRowTiles - 1) / kDecodeRowTiles; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsl_last_error(void) { return g_err.c_str(); }
+
+size_t bsl_block_bytes(int64_t m, int64_t d, int32_t k) {
+  if (m < 1 || d < 8 || d % 8 || k < 1) return 0;
+  return (size_t)(m * d / 8 + 2 * (int64_t)k * (m + d));
+}
+
+size_t bsl_packed_sign_bytes(int64_t m, int64_t d) {
+  if (!shape_ok(m, d)) return 0;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8;
+}
+
+int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* tiled_out) {
+  if (!rowmajor_bits || !tiled_out) return fail(BSL_EINVAL, "bsl_pack_signs: null pointer");
+  if (!shape_ok(m, d)) return fail(BSL_EUNSUPPORTED, "bsl_pack_signs: need 1 <= m, 8 <= d, d % 8 == 0");
+  pack_signs_mt(rowmajor_bits, m, d, tiled_out);
+  return BSL_OK;
+}
+
+int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out) {
+  if (!tiled || !pm1_out) return fail(BSL_EINVAL, "bsl_unpack_signs: null pointer");
+  if (!shape_ok(m, d)) return fail(BSL_EUNSUPPORTED, "bsl_unpack_signs: need 1 <= m, 8 <= d, d % 8 == 0");
+  const int64_t nch = pad_cols(d) / kChunkCols;
+  for (int64_t r = 0; r < m; ++r) {
+    const int64_t t = r / kTileRows, i = r % kTileRows;
+    for (int64_t col = 0; col < d; ++col) {
+      const int64_t c = col / kChunkCols, cc = col % kChunkCols;
+      const int b = (int)(cc / 32), rem = (int)(cc % 32), g = rem / 8, q = (rem % 8) / 2, h = rem % 2;
+      uint32_t word;
+      std::memcpy(&word, tiled + (t * nch + c) * kTileBytes + (16 * g + i) * 16 + 4 * q, 4);
+      const uint32_t bit = (word >> (b + 16 * h)) & 1u;
+      pm1_out[r * d + col] = bit ? -1 : 1;
+    }
+  }
+  return BSL_OK;
+}
+
+int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m, const int32_t* d, int32_t k,
+             int32_t n_cap, uint64_t budget_bytes) {
+  if (!out || !m || !d) return fail(BSL_EINVAL, "bsl_init: null pointer");
+  *out = nullptr;
+  if (num_weights < 1 || num_weights > (1 << 20)) return fail(BSL_EINVAL, "bsl_init: num_weights out of range");
+  if (n_cap < 1 || n_cap > 1024) return fail(BSL_EINVAL, "bsl_init: n_cap must be in 1..1024");
+  if (k != kRank) return fail(BSL_EUNSUPPORTED, "bsl_init: only k = 16 is supported");
+  for (int32_t w = 0; w < num_weights; ++w)
+    if (!shape_ok(m[w], d[w])) return fail(BSL_EUNSUPPORTED, "bsl_init: weight " + std::to_string(w) + " has an unsupported shape");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) return fail(BSL_EINVAL, "bsl_init: no such device");
+  DeviceGuard guard(device);
+  bsl_stack* s = new (std::nothrow) bsl_stack;
+  if (!s) return fail(BSL_ENOMEM, "bsl_init: host allocation failed");
+  s->device = device;
+  s->k = k;
+  s->n_cap = n_cap;
+  s->budget = budget_bytes;
+  s->w.resize(num_weights);
+  int rc = BSL_OK;
+  for (int32_t w = 0; w < num_weights && rc == BSL_OK; ++w) {
+    Weight& W = s->w[w];
+    W.m = m[w];
+    W.d = d[w];
+    W.mt = (int32_t)(pad_rows(W.m) / kTileRows);
+    W.nch = (int32_t)(pad_cols(W.d) / kChunkCols);
+    W.slots.resize(n_cap);
+    const size_t mpad = (size_t)pad_rows(W.m);
+    W.partial_floats = std::max((size_t)W.nch * mpad, (size_t)kGemmMaxSplits * kGemmMaxSplitM * mpad);
+    W.counter_count = (size_t)decode_groups(W) + (size_t)((W.mt + kGemmRowTiles - 1) / kGemmRowTiles) * kGemmMaxSplitM + 64;
+    if ((e = hipMalloc(&W.dtable, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(table)");
+    else if ((e = hipMalloc(&W.partial, W.partial_floats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(workspace)");
+    else if ((e = hipMalloc(&W.counters, W.counter_count * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(counters)");
+    else if ((e = hipMemset(W.counters, 0, W.counter_count * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
+    else if ((e = hipMemset(W.dtable, 0, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMemset(table)");
+  }
+  if (rc == BSL_OK && (e = hipDeviceSynchronize()) != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
+  if (rc != BSL_OK) {
+    std::string msg = g_err;
+    bsl_destroy(s);
+    g_err = msg;
+    return rc;
+  }
+  *out = s;
+  return BSL_OK;
+}
+
+int bsl_set_source(bsl_stack* s, int32_t w, int32_t n_avail, const bsl_block_src* blocks) {
+  if (!s) return fail(BSL_EINVAL, "bsl_set_source: null stack");
+  if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "bsl_set_source: weight index out of range");
+  if (n_avail < 0 || n_avail > s->n_cap) return fail(BSL_EINVAL, "bsl_set_source: n_avail must be in 0..n_cap");
+  if (n_avail > 0 && !blocks) return fail(BSL_EINVAL, "bsl_set_source: null block array");
+  for (int32_t i = 0; i < n_avail; ++i)
+    if (!blocks[i].sign_bits || !blocks[i].u || !blocks[i].v) return fail(BSL_EINVAL, "bsl_set_source: block " + std::to_string(i) + " has a null array");
+  s->w[w].src.assign(blocks, blocks + n_avail);
+  return BSL_OK;
+}
+
+int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
+  if (!s || !n_per_weight) return fail(BSL_EINVAL, "bsl_load_blocks: null pointer");
+  const int32_t nw = (int32_t)s->w.size();
+  for (int32_t w = 0; w < nw; ++w) {
+    const int32_t n = n_per_weight[w];
+    if (n < 0 || n > s->n_cap) return fail(BSL_EINVAL, "bsl_load_blocks: count out of range for weight " + std::to_string(w));
+    if (n > s->w[w].n && n > (int32_t)s->w[w].src.size())
+      return fail(BSL_EINVAL, "bsl_load_blocks: weight " + std::to_string(w) + " has only " + std::to_string(s->w[w].src.size()) + " source blocks");
+  }
+  // budget check over the final state
+  uint64_t after = s->resident;
+  for (int32_t w = 0; w < nw; ++w) {
+    const Weight& W = s->w[w];
+    const uint64_t sb = slot_bytes(W.m, W.d);
+    const int32_t n = n_per_weight[w];
+    if (n > W.n) after += sb * (uint64_t)(n - W.n);
+    else after -= sb * (uint64_t)(W.n - n);
+  }
+  if (s->budget && after > s->budget)
+    return fail(BSL_ENOMEM, "bsl_load_blocks: " + std::to_string(after) + " bytes exceed the budget of " + std::to_string(s->budget));
+  DeviceGuard guard(s->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // phase 1: allocate every new slot; undo all on failure
+  struct NewSlot { int32_t w, i; };
+  std::vector<NewSlot> added;
+  hipError_t e = hipSuccess;
+  for (int32_t w = 0; w < nw && e == hipSuccess; ++w) {
+    Weight& W = s->w[w];
+    for (int32_t i = W.n; i < n_per_weight[w]; ++i) {
+      const size_t sb = slot_bytes(W.m, W.d);
+      void* mem = nullptr;
+      e = hipMalloc(&mem, sb);
+      if (e != hipSuccess) break;
+      W.slots[i].mem = mem;
+      W.slots[i].bytes = sb;
+      added.push_back({w, i});
+    }
+  }
+  auto undo = [&]() {
+    for (const NewSlot& a : added) {
+      Slot& sl = s->w[a.w].slots[a.i];
+      (void)hipFree(sl.mem);
+      sl.mem = nullptr;
+      sl.bytes = 0;
+    }
+  };
+  if (e != hipSuccess) {
+    undo();
+    return hip_fail(e, "hipMalloc(block)");
+  }
+  // phase 2: pack on the host and copy the new blocks
+  std::vector<uint8_t> staging;
+  for (const NewSlot& a : added) {
+    Weight& W = s->w[a.w];
+    const bsl_block_src& src = W.src[a.i];
+    const size_t sb = (size_t)pad_rows(W.m) * pad_cols(W.d) / 8;
+    const size_t ub = (size_t)pad_rows(W.m) * kRank * 2;
+    const size_t vb = (size_t)pad_cols(W.d) * kRank * 2;
+    staging.resize(sb + ub + vb);
+    pack_signs_mt(src.sign_bits, W.m, W.d, staging.data());
+    tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(staging.data() + sb));
+    tile_v(src.v, W.d, reinterpret_cast<uint16_t*>(staging.data() + sb + ub));
+    e = hipMemcpyAsync(W.slots[a.i].mem, staging.data(), staging.size(), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);  // staging is reused
+    if (e != hipSuccess) {
+      undo();
+      return hip_fail(e, "block upload");
+    }
+  }
+  // phase 3: publish the new slots in each grown weight's device table.  The table
+  // lists every allocated slot; the kernels read only the first n entries, so a
+  // shrink needs no table change and entries past n are never dereferenced.
+  for (int32_t w = 0; w < nw; ++w) {
+    if (n_per_weight[w] <= s->w[w].n) continue;
+    int rc = upload_table(s, s->w[w], st);
+    if (rc != BSL_OK) {
+      undo();
+      return rc;
+    }
+  }
+  // phase 4: commit.  Shrinking waits for the stream so no queued forward still reads a slot.
+  bool shrink = false;
+  for (int32_t w = 0; w < nw; ++w) shrink |= n_per_weight[w] < s->w[w].n;
+  if (shrink && (e = hipStreamSynchronize(st)) != hipSuccess) {
+    undo();
+    return hip_fail(e, "hipStreamSynchronize");
+  }
+  for (int32_t w = 0; w < nw; ++w) {
+    Weight& W = s->w[w];
+    const int32_t n = n_per_weight[w];
+    for (int32_t i = n; i < W.n; ++i) {
+      (void)hipFree(W.slots[i].mem);
+      s->resident -= W.slots[i].bytes;
+      W.slots[i] = Slot{};
+    }
+    W.n = n;
+  }
+  for (const NewSlot& a : added) s->resident += s->w[a.w].slots[a.i].bytes;
+  return BSL_OK;
+}
+
+int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out) {
+  if (!s || !n_out) return fail(BSL_EINVAL, "bsl_active_blocks: null pointer");
+  if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "bsl_active_blocks: weight index out of range");
+  *n_out = s->w[w].n;
+  return BSL_OK;
+}
+
+uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
+
+namespace {
+
+int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
+                 int32_t y_is_fp32, void* stream) {
+  if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");
+  if (M < 1 || M > (1 << 24)) return fail(BSL_EINVAL, "forward: M must be >= 1");
+  GroupArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.count = count;
+  args.M = M;
+  args.y_fp32 = y_is_fp32 ? 1 : 0;
+  const int nt = M >= 8 ? 8 : 4;  // GEMM token tile
+  const int token_groups = (M + nt - 1) / nt;
+  int32_t items = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int32_t w = weights[j];
+    if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
+    for (int32_t jj = 0; jj < j; ++jj)
+      if (weights[jj] == w) return fail(BSL_EINVAL, "forward: a weight appears twice in one launch");
+    if (!x[j] || !y[j]) return fail(BSL_EINVAL, "forward: null x or y");
+    if ((reinterpret_cast<uintptr_t>(x[j]) & 15) != 0) return fail(BSL_EINVAL, "forward: x must be 16-byte aligned");
+    const Weight& W = s->w[w];
+    WeightDesc& D = args.w[j];
+    D.blocks = W.dtable;
+    D.x = static_cast<const uint16_t*>(x[j]);
+    D.y = y[j];
+    D.partial = W.partial;
+    D.counters = W.counters;
+    D.m = W.m;
+    D.d = W.d;
+    D.mt = W.mt;
+    D.nch = W.nch;
+    D.nblocks = W.n;
+    D.item_begin = items;
+    if (M == 1) {
+      D.groups = decode_groups(W);
+      D.splits = W.nch;
+      items += D.groups * W.nch;
+    } else {
+      const int rgroups = (W.mt + kGemmRowTiles - 1) / kGemmRowTiles;
+      int splits = 1;
+      if (M <= kGemmMaxSplitM) splits = std::min<int>(W.nch, kGemmMaxSplits);
+      D.groups = rgroups * token_groups;
+      D.splits = splits;
+      items += D.groups * splits;
+    }
+  }
+  args.total_items = items;
+  DeviceGuard guard(s->device);
+  int e;
+  if (M == 1) e = launch_decode_m1(args, kDecodeRowTiles, stream);
+  else e = launch_gemm(args, nt, token_groups, stream);
+  if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+  return BSL_OK;
+}
+
+}  // namespace
+
+int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int32_t y_is_fp32, void* stream) {
+  if (!s) return fail(BSL_EINVAL, "bsl_forward: null stack");
+  const void* xs[1] = {x};
+  void* ys[1] = {y};
+  return forward_impl(s, 1, &w, xs, ys, M, y_is_fp32, stream);
+}
+
+int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
+                      int32_t M, int32_t y_is_fp32, void* stream) {
+  if (!s || !weights || !x || !y) return fail(BSL_EINVAL, "bsl_forward_group: null pointer");
+  return forward_impl(s, count, weights, x, y, M, y_is_fp32, stream);
+}
+
+int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream) {
+  if (!s || !pm1_out) return fail(BSL_EINVAL, "bsl_debug_unpack: null pointer");
+  if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "bsl_debug_unpack: weight index out of range");
+  const Weight& W = s->w[w];
+  if (i < 0 || i >= W.n) return fail(BSL_EINVAL, "bsl_debug_unpack: block not loaded");
+  if (path != 0 && path != 1) return fail(BSL_EINVAL, "bsl_debug_unpack: path must be 0 or 1");
+  DeviceGuard guard(s->device);
+  int e = launch_debug_unpack(slot_ptrs(W.slots[i], W.m, W.d), W.m, W.d, W.mt, W.nch, path, pm1_out, stream);
+  if (e != 0) return hip_fail(static_cast<hipError_t>(e), "debug unpack launch");
+  return BSL_OK;
+}
+
+void bsl_destroy(bsl_stack* s) {
+  if (!s) return;
+  DeviceGuard guard(s->device);
+  (void)hipDeviceSynchronize();
+  for (Weight& W : s->w) {
+    for (Slot& sl : W.slots)
+      if (sl.mem) (void)hipFree(sl.mem);
+    if (W.dtable) (void)hipFree(W.dtable);
+    if (W.partial) (void)hipFree(W.partial);
+    if (W.counters) (void)hipFree(W.counters);
+  }
+  delete s;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the host side (bsl_host.cpp) and the kernels
+// (bsl_kernels.hip) of libbitstack_linear.  Not part of the public interface.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace bsl {
+
+// Tile geometry of the packed sign layout (one 16x32x32 fp16 MFMA fragment per
+// plane, 16 planes per 512-column chunk; see bsl_pack_signs in the public header).
+constexpr int kRank = 16;         // k: rank of U_i, V_i (also the MFMA N width)
+constexpr int kTileRows = 16;     // rows per sign tile
+constexpr int kChunkCols = 512;   // columns per sign tile
+constexpr int kPlanes = 16;       // 32-column planes per chunk
+constexpr int kTileBytes = 1024;  // 16 x 512 bits
+constexpr int kMaxGroup = 8;      // weights per grouped launch
+
+inline int64_t pad_rows(int64_t m) { return (m + kTileRows - 1) / kTileRows * kTileRows; }
+inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * kChunkCols; }
+
+// Device addresses of one loaded block.  One allocation holds, in order:
+//   signs: [m_pad/16][d_pad/512][64 lanes][16 B]                 (tiled bits)
+//   u:     [m_pad/16][64 lanes][4] fp16  lane L holds U[16 t + 4 (L/16) + v][L % 16]
+//   v:     [d_pad/512][16 planes][64 lanes][8] fp16
+//          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
+struct BlockPtrs {
+  const uint8_t* signs;
+  const uint16_t* u;
+  const uint16_t* v;
+};
+
+// One weight of a (grouped) forward launch; passed by value in the kernel arguments.
+struct WeightDesc {
+  const BlockPtrs* blocks;  // device table of the loaded blocks
+  const uint16_t* x;        // [M][d] fp16
+  void* y;                  // [M][m] fp16 or fp32
+  float* partial;           // split-K partial sums (workspace)
+  uint32_t* counters;       // arrival counters, one per output group (workspace, zero between calls)
+  int32_t m, d;             // true sizes
+  int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
+  int32_t nblocks;          // loaded blocks
+  int32_t item_begin;       // first work item of this weight in the launch
+  int32_t groups;           // output groups (row groups x token groups) of this weight
+  int32_t splits;           // K splits (chunks per split = ceil(nch / splits))
+};
+
+struct GroupArgs {
+  WeightDesc w[kMaxGroup];
+  int32_t count;
+  int32_t total_items;
+  int32_t M;
+  int32_t y_fp32;
+};
+
+// Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
+int launch_decode_m1(const GroupArgs& args, int rows_per_item, void* stream);
+int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream);
+int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
+                        void* stream);
+
+// Row tiles per decode work item and the workspace each weight needs.
+constexpr int kDecodeRowTiles = 8;
+constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
+constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
+constexpr int kGemmMaxSplits = 8;
+
+}  // namespace bsl

@@ -1,0 +1,476 @@
+// HIP kernels of libbitstack_linear for gfx950 (MI355X).
+//
+// The layer (BitStack OpenReview discussion, weight-restoration reply; paper-review
+// page, Figure 3 caption) is y = x W_hat^T with W_hat = sum_i S_i * (U_i V_i^T).  By
+// linearity,
+//     y[t, j] = sum_i sum_r U_i[j, r] * P_i[j, (t, r)],   P_i = S_i Z_i,
+//     Z_i[c, (t, r)] = V_i[c, r] * x[t, c],
+// so each block costs one dense contraction of the sign matrix with Z_i (width 16 M)
+// on the matrix cores (v_mfma_f32_16x16x32_f16: fp16 inputs, fp32 accumulation), a
+// Hadamard product with U_i and a sum over r that is done once for all blocks.
+//
+// Sign tiles (16 rows x 512 columns, 1 KiB) are read with one 16-byte load per lane
+// and turned into MFMA A fragments in registers; nothing is staged through LDS on the
+// single-token path, where the unpack and the MFMA issue share each SIMD and any LDS
+// round trip would cost more than the HBM read it serves.
+//
+// Two sign encodings share the stored layout:
+//  * single-token kernel (M = 1): "bit planes".  Plane b of a lane's four words keeps
+//    bits (pos, pos + 16) after one optional shift, so the A fragment is one AND per
+//    dword.  The fp16 element is then bit * 2^(pos - 24) (exact subnormal or normal
+//    powers of two, honoured exactly by the MFMA), i.e. a 0/1 encoding of the sign.
+//    The power of two and the factor -2 of S = 1 - 2 bit are folded exactly into the
+//    activations of that plane, and the missing "sum of Z over the chunk" term is put
+//    into the accumulator's initial value, so
+//        acc = 2^-17 * (sum_c Z_c - 2 sum_c bit_c Z_c) = 2^-17 * P.
+//  * multi-token kernel (M >= 2): "+-1".  Shift the plane's bits to positions 15/31
+//    and OR in 1.0, giving exact +-1 fp16 elements (unpack cost is amortised over the
+//    token tile there).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "bsl_internal.h"
+
+namespace bsl {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Accumulators of the bit-plane path hold 2^-17 times the layer's partial sums.
+constexpr float kPlaneAccScale = 1.0f / 131072.0f;
+constexpr float kPlaneOutScale = 131072.0f;
+
+// Bit position (within each 16-bit half) that plane b occupies after its shift:
+// planes 0-5 come from (w << 6), planes 6-11 from w, planes 12-15 from (w >> 6).
+__host__ __device__ constexpr int plane_pos(int b) { return b < 6 ? b + 6 : (b < 12 ? b : b - 6); }
+
+// fp16 bit pattern of the exact factor -2^(8 - pos) applied to the plane's activations.
+// The A element is 2^(pos - 24) for a set bit, so A * x * factor = -2 * bit * x * 2^-17.
+__host__ __device__ constexpr uint16_t plane_x_factor_bits(int b) {
+  // -2^(8 - pos): pos = 6..11 -> -4, -2, -1, -0.5, -0.25, -0.125
+  return (uint16_t)(0x8000u | (uint16_t)((15 + 8 - plane_pos(b)) << 10));
+}
+// fp16 bit pattern of 1 / factor = -2^(pos - 8) (to recover Z from the scaled products).
+__host__ __device__ constexpr uint16_t plane_inv_factor_bits(int b) {
+  return (uint16_t)(0x8000u | (uint16_t)((15 + plane_pos(b) - 8) << 10));
+}
+
+__device__ __forceinline__ half8 as_half8(u32x4 v) { return __builtin_bit_cast(half8, v); }
+__device__ __forceinline__ half2v as_half2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+__device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// A fragment of plane b (bit-plane encoding) from a lane's four raw words.
+template <int B>
+__device__ __forceinline__ u32x4 plane_fragment(const u32x4& w, const u32x4& lo, const u32x4& hi) {
+  constexpr uint32_t mask = 0x00010001u << plane_pos(B);
+  const u32x4& src = B < 6 ? lo : (B < 12 ? w : hi);
+  return src & mask;
+}
+
+// A fragment of plane b (+-1 encoding).
+__device__ __forceinline__ u32x4 pm1_fragment(const u32x4& w, int b) {
+  const int s = 15 - b;
+  u32x4 a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) a[q] = ((w[q] << s) & 0x80008000u) | 0x3C003C00u;
+  return a;
+}
+
+// Sum a C fragment (lane L holds rows 4 (L/16) + v, v = 0..3, of column L % 16) over
+// the 16 columns.  Returns, in every lane, the sum for row 4 (L/16) + vsel(L) with
+// vsel(L) = 2 ((L >> 3) & 1) + ((L >> 2) & 1); lanes with L % 4 == 0 hold distinct rows.
+__device__ __forceinline__ float reduce_columns(float4v a, int lane) {
+  const bool hi8 = lane & 8, hi4 = lane & 4;
+  const float keep0 = hi8 ? a[2] : a[0], keep1 = hi8 ? a[3] : a[1];
+  const float send0 = hi8 ? a[0] : a[2], send1 = hi8 ? a[1] : a[3];
+  const float k0 = keep0 + __shfl_xor(send0, 8);
+  const float k1 = keep1 + __shfl_xor(send1, 8);
+  const float keep = hi4 ? k1 : k0, send = hi4 ? k0 : k1;
+  float r = keep + __shfl_xor(send, 4);
+  r += __shfl_xor(r, 2);
+  r += __shfl_xor(r, 1);
+  return r;
+}
+__device__ __forceinline__ int reduced_row(int lane) { return 4 * (lane >> 4) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1); }
+
+__device__ __forceinline__ void store_y(void* y, size_t idx, float v, int fp32) {
+  if (fp32) reinterpret_cast<float*>(y)[idx] = v;
+  else reinterpret_cast<_Float16*>(y)[idx] = (_Float16)v;
+}
+
+// Pick the descriptor of the weight that owns `item` (uniform across the wave).
+__device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int item) {
+  WeightDesc W = args.w[0];
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j)
+    if (j < args.count && item >= args.w[j].item_begin) W = args.w[j];
+  return W;
+}
+
+// ============================================================ single-token kernel
+// One wave per work item = (weight, group of R row tiles, one 512-column chunk); the
+// wave loops over all loaded blocks, accumulating U_i-weighted partial products per
+// row tile, reduces over r once, writes its partial sums, and the last wave of a row
+// group to arrive adds the chunks in a fixed order and writes y.
+template <int R>
+__global__ __launch_bounds__(256) void decode_m1_kernel(GroupArgs args) {
+  __shared__ u32x4 xs_all[4][64];  // per wave: the chunk's 512 activations, plane-scaled
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= args.total_items) return;  // no block-wide barrier below this point
+  const WeightDesc W = find_weight(args, item);
+  const int local = item - W.item_begin;
+  const int rg = local / W.nch;
+  const int ch = local - rg * W.nch;
+  const int g = lane >> 4;
+  const int col0 = ch * kChunkCols;
+  const int rows_pad = W.mt * kTileRows;
+
+  u32x4* xs = xs_all[wave];
+  {
+    const int col = col0 + 8 * lane;  // this lane's 8 columns belong to plane lane / 4
+    u32x4 xv = {0u, 0u, 0u, 0u};
+    if (col < W.d) xv = load16(W.x + col);
+    uint32_t fbits = 0;
+#pragma unroll
+    for (int b = 0; b < kPlanes; ++b)
+      if ((lane >> 2) == b) fbits = plane_x_factor_bits(b);
+    const half2v f = as_half2(fbits | (fbits << 16));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = as_u32(as_half2(xv[q]) * f);
+    xs[lane] = xv;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  float4v accy[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) accy[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+  const int rt0 = rg * R;
+  const int ntiles = min(R, W.mt - rt0);
+
+  for (int i = 0; i < W.nblocks; ++i) {
+    const BlockPtrs bp = W.blocks[i];
+    u32x4 raw[R];
+    u32x2 uf[R];
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      if (t < ntiles) {
+        raw[t] = load16(bp.signs + ((size_t)(rt0 + t) * W.nch + ch) * kTileBytes + lane * 16);
+        uf[t] = load8(bp.u + ((size_t)(rt0 + t) * 64 + lane) * 4);
+      }
+    }
+    half8 zb[kPlanes];
+    float cs = 0.f;
+#pragma unroll
+    for (int b = 0; b < kPlanes; ++b) {
+      const u32x4 vv = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + lane) * 8);
+      const u32x4 xx = xs[4 * b + g];
+      const half2v inv = as_half2((uint32_t)plane_inv_factor_bits(b) * 0x00010001u);
+      u32x4 z;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const half2v zq = as_half2(vv[q]) * as_half2(xx[q]);
+        z[q] = as_u32(zq);
+        cs = __builtin_amdgcn_fdot2(zq, inv, cs, false);
+      }
+      zb[b] = as_half8(z);
+    }
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+    const float init = cs * kPlaneAccScale;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      if (t < ntiles) {
+        const u32x4 w = raw[t];
+        const u32x4 lo = w << 6u;
+        const u32x4 hi = w >> 6u;
+        float4v acc = {init, init, init, init};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<0>(w, lo, hi)), zb[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<1>(w, lo, hi)), zb[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<2>(w, lo, hi)), zb[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<3>(w, lo, hi)), zb[3], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<4>(w, lo, hi)), zb[4], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<5>(w, lo, hi)), zb[5], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<6>(w, lo, hi)), zb[6], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<7>(w, lo, hi)), zb[7], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<8>(w, lo, hi)), zb[8], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<9>(w, lo, hi)), zb[9], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<10>(w, lo, hi)), zb[10], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<11>(w, lo, hi)), zb[11], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<12>(w, lo, hi)), zb[12], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<13>(w, lo, hi)), zb[13], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<14>(w, lo, hi)), zb[14], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<15>(w, lo, hi)), zb[15], acc, 0, 0, 0);
+        const half2v u01 = as_half2(uf[t][0]), u23 = as_half2(uf[t][1]);
+        accy[t][0] += (float)u01[0] * acc[0];
+        accy[t][1] += (float)u01[1] * acc[1];
+        accy[t][2] += (float)u23[0] * acc[2];
+        accy[t][3] += (float)u23[1] * acc[3];
+      }
+    }
+  }
+
+  // partial sums of this chunk
+  const int rsel = reduced_row(lane);
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    if (t < ntiles) {
+      const float v = reduce_columns(accy[t], lane);
+      const int row = (rt0 + t) * kTileRows + rsel;
+      if ((lane & 3) == 0) W.partial[(size_t)ch * rows_pad + row] = v;
+    }
+  }
+  // last wave of the row group to arrive sums the chunks in order and writes y
+  __threadfence();
+  uint32_t prev = 0;
+  if (lane == 0) prev = atomicAdd(&W.counters[rg], 1u);
+  prev = __shfl(prev, 0);
+  if (prev != (uint32_t)(W.nch - 1)) return;
+  __threadfence();
+  const int row_begin = rt0 * kTileRows;
+  const int row_end = min(W.m, (rt0 + ntiles) * kTileRows);
+  for (int row = row_begin + lane; row < row_end; row += 64) {
+    float s = 0.f;
+    for (int c = 0; c < W.nch; ++c) s += __builtin_nontemporal_load(&W.partial[(size_t)c * rows_pad + row]);
+    store_y(W.y, row, s * kPlaneOutScale, args.y_fp32);
+  }
+  if (lane == 0) __hip_atomic_store(&W.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ============================================================ multi-token kernel
+// One workgroup (4 waves) per item = (weight, 256-row group, NT-token group, K split).
+// Each wave owns 4 row tiles x NT tokens of accumulators.  For every block and every
+// 512-column chunk of its split, the workgroup builds the Z tile (V (.) x, 8 planes at a
+// time) in LDS, each wave unpacks its sign tiles to +-1 fragments and runs the MFMAs;
+// after a block's K loop the U-weighted tile is reduced over r into per-row sums.
+template <int NT>
+__global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_groups) {
+  __shared__ u32x4 zs[8 * NT * 64];  // [plane][token][lane] 16 B each: NT * 8 KiB
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x;
+  const WeightDesc W = find_weight(args, item);
+  const int M = args.M;
+  const int local = item - W.item_begin;
+  const int split = local % W.splits;
+  const int rest = local / W.splits;
+  const int tg = rest % token_groups;
+  const int rg = rest / token_groups;
+  const int g = lane >> 4;
+  const int cps = (W.nch + W.splits - 1) / W.splits;
+  const int c_begin = split * cps;
+  const int c_end = min(W.nch, c_begin + cps);
+  const int rt0 = rg * kGemmRowTiles + wave * 4;  // this wave's first row tile
+  const int tok0 = tg * NT;
+  const int rows_pad = W.mt * kTileRows;
+
+  float accy[4][NT];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) accy[a][t] = 0.f;
+
+  for (int i = 0; i < W.nblocks; ++i) {
+    const BlockPtrs bp = W.blocks[i];
+    float4v acc[4][NT];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[a][t] = (float4v){0.f, 0.f, 0.f, 0.f};
+    for (int ch = c_begin; ch < c_end; ++ch) {
+      u32x4 raw[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        raw[a] = (u32x4){0u, 0u, 0u, 0u};
+        if (rt0 + a < W.mt) raw[a] = load16(bp.signs + ((size_t)(rt0 + a) * W.nch + ch) * kTileBytes + lane * 16);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // consumers of the previous Z tile are done
+        // build 8 planes x NT tokens; wave builds planes 2*wave, 2*wave+1
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int p = 2 * wave + pp;
+          const int b = 8 * half + p;
+          const u32x4 vv = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + lane) * 8);
+          const int col = ch * kChunkCols + 32 * b + 8 * g;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int tok = tok0 + t;
+            u32x4 xx = {0u, 0u, 0u, 0u};
+            if (tok < M && col < W.d) xx = load16(W.x + (size_t)tok * W.d + col);
+            u32x4 z;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) z[q] = as_u32(as_half2(vv[q]) * as_half2(xx[q]));
+            zs[(p * NT + t) * 64 + lane] = z;
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int b = 8 * half + p;
+          u32x4 afr[4];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) afr[a] = pm1_fragment(raw[a], b);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const half8 bfr = as_half8(zs[(p * NT + t) * 64 + lane]);
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(afr[a]), bfr, acc[a][t], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // U weighting and reduction over r for this block
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      if (rt0 + a < W.mt) {
+        const u32x2 uf = load8(bp.u + ((size_t)(rt0 + a) * 64 + lane) * 4);
+        const half2v u01 = as_half2(uf[0]), u23 = as_half2(uf[1]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float4v v = acc[a][t];
+          v[0] *= (float)u01[0];
+          v[1] *= (float)u01[1];
+          v[2] *= (float)u23[0];
+          v[3] *= (float)u23[1];
+          accy[a][t] += reduce_columns(v, lane);
+        }
+      }
+    }
+  }
+
+  const int rsel = reduced_row(lane);
+  const bool writer = (lane & 3) == 0;
+  if (W.splits == 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int row = (rt0 + a) * kTileRows + rsel;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int tok = tok0 + t;
+        if (writer && row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, accy[a][t], args.y_fp32);
+      }
+    }
+    return;
+  }
+  // split-K: partial[split][token][row], then the last workgroup of the (rg, tg) group adds
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int row = (rt0 + a) * kTileRows + rsel;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int tok = tok0 + t;
+      if (writer && rt0 + a < W.mt && tok < M) W.partial[((size_t)split * M + tok) * rows_pad + row] = accy[a][t];
+    }
+  }
+  __threadfence();
+  __syncthreads();  // all partial stores issued and every wave is past its last use of zs
+  uint32_t* last = reinterpret_cast<uint32_t*>(zs);
+  if (threadIdx.x == 0) *last = atomicAdd(&W.counters[rest], 1u) == (uint32_t)(W.splits - 1);
+  __syncthreads();
+  if (!*last) return;
+  __threadfence();
+  const int row_begin = rg * kGemmRowTiles * kTileRows;
+  const int row_end = min(W.m, row_begin + kGemmRowTiles * kTileRows);
+  const int nrows = row_end - row_begin;
+  const int ntok = min(NT, M - tok0);
+  for (int e = threadIdx.x; e < nrows * ntok; e += 256) {
+    const int t = e / nrows, row = row_begin + e % nrows;
+    const int tok = tok0 + t;
+    float s = 0.f;
+    for (int sp = 0; sp < W.splits; ++sp) s += __builtin_nontemporal_load(&W.partial[((size_t)sp * M + tok) * rows_pad + row]);
+    store_y(W.y, (size_t)tok * W.m + row, s, args.y_fp32);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ============================================================ debug unpack
+// One wave per sign tile: unpack exactly as the forward kernels do and write +-1.
+__global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t m, int32_t d, int32_t nch, int path,
+                                                          int8_t* out) {
+  const int lane = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int rt = tile / nch, ch = tile % nch;
+  const u32x4 w = load16(blk.signs + (size_t)tile * kTileBytes + lane * 16);
+  const u32x4 lo = w << 6u, hi = w >> 6u;
+  const int row = rt * kTileRows + (lane & 15);
+  const int g = lane >> 4;
+  u32x4 fr[kPlanes];
+  if (path == 0) {
+    fr[0] = plane_fragment<0>(w, lo, hi);
+    fr[1] = plane_fragment<1>(w, lo, hi);
+    fr[2] = plane_fragment<2>(w, lo, hi);
+    fr[3] = plane_fragment<3>(w, lo, hi);
+    fr[4] = plane_fragment<4>(w, lo, hi);
+    fr[5] = plane_fragment<5>(w, lo, hi);
+    fr[6] = plane_fragment<6>(w, lo, hi);
+    fr[7] = plane_fragment<7>(w, lo, hi);
+    fr[8] = plane_fragment<8>(w, lo, hi);
+    fr[9] = plane_fragment<9>(w, lo, hi);
+    fr[10] = plane_fragment<10>(w, lo, hi);
+    fr[11] = plane_fragment<11>(w, lo, hi);
+    fr[12] = plane_fragment<12>(w, lo, hi);
+    fr[13] = plane_fragment<13>(w, lo, hi);
+    fr[14] = plane_fragment<14>(w, lo, hi);
+    fr[15] = plane_fragment<15>(w, lo, hi);
+  } else {
+#pragma unroll
+    for (int b = 0; b < kPlanes; ++b) fr[b] = pm1_fragment(w, b);
+  }
+  if (row >= m) return;
+#pragma unroll
+  for (int b = 0; b < kPlanes; ++b) {
+    const half8 h = as_half8(fr[b]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = ch * kChunkCols + 32 * b + 8 * g + j;
+      if (col < d) {
+        // bit-plane path: a set bit is a non-zero element and means -1; +-1 path: the value itself
+        const float v = (float)h[j];
+        out[(size_t)row * d + col] = path == 0 ? (v != 0.f ? -1 : 1) : (v < 0.f ? -1 : 1);
+      }
+    }
+  }
+}
+
+// ============================================================ launchers
+int launch_decode_m1(const GroupArgs& args, int rows_per_item, void* stream) {
+  if (rows_per_item != kDecodeRowTiles) return (int)hipErrorInvalidValue;
+  if (args.total_items == 0) return 0;
+  const int blocks = (args.total_items + 3) / 4;
+  hipLaunchKernelGGL(decode_m1_kernel<kDecodeRowTiles>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), args);
+  return (int)hipGetLastError();
+}
+
+int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream) {
+  if (args.total_items == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (token_tile == 8)
+    hipLaunchKernelGGL(gemm_kernel<8>, dim3(args.total_items), dim3(256), 0, st, args, token_groups);
+  else if (token_tile == 4)
+    hipLaunchKernelGGL(gemm_kernel<4>, dim3(args.total_items), dim3(256), 0, st, args, token_groups);
+  else
+    return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
+                        void* stream) {
+  hipLaunchKernelGGL(debug_unpack_kernel, dim3(mt * nch), dim3(64), 0, static_cast<hipStream_t>(stream), blk, m, d, nch,
+                     path, out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace bsl

@@ -1,0 +1,150 @@
+/*
+ * bitstack_linear -- BitStack residual-block linear layer on one MI355X (gfx950).
+ *
+ * A weight W (m = out_features rows, d = in_features columns) is held as a stack of
+ * residual blocks.  Block i is a +-1 sign matrix S_i (m x d, stored at one bit per
+ * entry) and two rank-k factors U_i (m x k) and V_i (d x k) in fp16.  The first n
+ * loaded blocks restore the weight as
+ *
+ *     W_hat_n = sum_{i < n} S_i (elementwise *) (U_i V_i^T)
+ *
+ * (BitStack OpenReview discussion, the authors' reply giving the weight restoration
+ * code; residual block = packed sign matrix + singular vectors from an absolute value
+ * decomposition, paper-review page, Figure 3 caption).  This library computes the
+ * layer output y = x W_hat_n^T directly from the loaded blocks and never forms
+ * W_hat: per block it builds Z_i = V_i (.) x, contracts S_i Z_i on the matrix cores
+ * (fp16 inputs, fp32 accumulation) and reduces the row-wise dot with U_i over all
+ * blocks in one pass.
+ *
+ * Blocks live in a device-resident stack.  The number of loaded blocks per weight
+ * can grow (new blocks are copied in) or shrink (the last blocks are released)
+ * without touching the blocks that stay, which mirrors BitStack's load/offload of
+ * residual blocks as memory availability changes (paper-review page, Figure 2
+ * caption; OpenReview reply A1.B).
+ *
+ * Conventions for every entry point:
+ *   - Return value: BSL_OK (0) or a negative BSL_E* code; no call aborts and no
+ *     C++ exception crosses this interface.  bsl_last_error() returns a message for
+ *     the calling thread's most recent failure.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP device
+ *     memory of the stack's device.  Streams are hipStream_t passed as void*; NULL
+ *     means the default stream.
+ *   - Host inputs are read during the call (or, for bsl_set_source, until the next
+ *     bsl_set_source / bsl_destroy of that weight) and never retained otherwise.
+ *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
+ *   - Supported shapes: k == 16, 1 <= m <= 2^20, 8 <= d <= 2^20 with d % 8 == 0.
+ *     Internally rows are padded to a multiple of 16 and columns to a multiple of
+ *     512 (padding signs are +1 and padding factor entries are 0, so padding never
+ *     changes a result).
+ *   - A stack is not thread-safe: calls on one stack must not run concurrently.
+ */
+#ifndef BITSTACK_LINEAR_H
+#define BITSTACK_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSL_OK 0
+#define BSL_EINVAL (-1)       /* bad argument: null pointer, index or size out of range */
+#define BSL_ENOMEM (-2)       /* device allocation failed or the stack's byte budget is exceeded */
+#define BSL_EHIP (-3)         /* a HIP runtime call failed; the message holds HIP's error text */
+#define BSL_EUNSUPPORTED (-4) /* shape, k or batch outside what this build supports */
+
+/* Opaque handle; owns all device memory of the loaded blocks and the workspace. */
+typedef struct bsl_stack bsl_stack;
+
+/* One residual block as the caller provides it (host memory).
+ *   sign_bits: m rows of d/8 bytes, row-major; bit (c % 8) of byte c/8 of a row is
+ *              column c (least significant bit first); a set bit means the sign is -1.
+ *   u:         fp16 [m][k] row-major.
+ *   v:         fp16 [d][k] row-major (the right factor, not transposed).
+ * With k = 16 the block occupies m*d/8 + 2*k*(m + d) bytes of payload (one bit per
+ * sign, 16 bits per factor entry; OpenReview reply A1.A: the largest block of an 8B
+ * model, 14336 x 4096, is 7.56 MB). */
+typedef struct bsl_block_src {
+  const uint8_t* sign_bits;
+  const uint16_t* u;
+  const uint16_t* v;
+} bsl_block_src;
+
+/* Payload bytes of one block: m*d/8 + 2*k*(m + d).  Returns 0 for invalid sizes. */
+size_t bsl_block_bytes(int64_t m, int64_t d, int32_t k);
+
+/* Bytes of the tiled sign layout of one m x d block (rows padded to 16, columns to 512). */
+size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
+
+/* Host-side "bitstack_pack": convert row-major sign bits (format of bsl_block_src)
+ * into the tiled device layout.  tiled_out (host) must hold bsl_packed_sign_bytes(m, d)
+ * bytes.  Layout: tiles of 16 rows x 512 columns, ordered [row tile][column chunk];
+ * each tile is 64 lanes x 16 bytes; lane L = 16*g + i holds row i of the tile and four
+ * little-endian 32-bit words q = 0..3, where bit p of word q is the sign of column
+ * 32*(p % 16) + 8*g + 2*q + (p / 16) of the chunk.  One 16-byte load per lane fetches
+ * a whole tile (1 KiB, eight full 128-byte lines). */
+int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* tiled_out);
+
+/* Inverse of bsl_pack_signs, for checking: writes int8 +1/-1 into pm1_out (host,
+ * m*d bytes, row-major).  Padding is ignored. */
+int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out);
+
+/* Create a stack for num_weights weights with shapes m[w] x d[w] (host arrays), rank k
+ * (must be 16), at most n_cap blocks per weight (the paper's runs decompose with 16
+ * iterations: README, "Decomposition"), on HIP device `device`.  budget_bytes caps
+ * the device bytes held by loaded blocks (0 = no cap).  The per-weight workspace used
+ * by bsl_forward is allocated here, so forward never allocates.  *out receives the
+ * handle. */
+int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m, const int32_t* d, int32_t k,
+             int32_t n_cap, uint64_t budget_bytes);
+
+/* Register the host source of weight w's blocks, in load order (the presorted order of
+ * the weight's stack): blocks[0 .. n_avail-1].  The arrays must stay valid until the
+ * next bsl_set_source for w or bsl_destroy; only bsl_load_blocks reads them. */
+int bsl_set_source(bsl_stack* s, int32_t w, int32_t n_avail, const bsl_block_src* blocks);
+
+/* Set the number of loaded blocks of every weight to n_per_weight[w] (host array of
+ * num_weights entries, 0 <= n <= min(n_cap, n_avail)).  Growing packs and copies only
+ * the new blocks [n_old, n_new) (host -> device on `stream`, then waits for them);
+ * shrinking waits for `stream` to drain and then releases blocks [n_new, n_old).  The
+ * call is all-or-nothing: on any failure every weight keeps its previous count and no
+ * memory is leaked.  Blocks that stay loaded are never moved or rewritten. */
+int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
+
+/* Number of loaded blocks of weight w. */
+int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
+
+/* Device bytes currently held by loaded blocks (what budget_bytes caps). */
+uint64_t bsl_resident_bytes(const bsl_stack* s);
+
+/* y = x W_hat_n^T for weight w with its n loaded blocks.
+ *   x: device, fp16 [M][d] row-major, 16-byte aligned.
+ *   y: device, [M][m] row-major, fp16 (y_is_fp32 == 0, round to nearest even) or fp32.
+ *   M >= 1 tokens.  With n = 0 loaded blocks y is all zeros.
+ * Only enqueues kernels on `stream` (no synchronisation, no allocation).  Two forwards
+ * of the same weight must not run concurrently (they share its workspace). */
+int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int32_t y_is_fp32, void* stream);
+
+/* Several weights in one kernel launch (count <= 8, distinct weights): weights[j] reads
+ * x[j] and writes y[j] exactly as bsl_forward would.  All share M and y_is_fp32. */
+int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
+                      int32_t M, int32_t y_is_fp32, void* stream);
+
+/* Run a forward kernel's own sign-unpack code on block i of weight w and write the
+ * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes).
+ * path 0: the single-token kernel's bit-plane masks; path 1: the multi-token
+ * kernel's +-1 fp16 conversion. */
+int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream);
+
+/* Message for the calling thread's last failure ("" if none). */
+const char* bsl_last_error(void);
+
+/* Release all device memory of the stack (waits for the device first).  NULL is ignored. */
+void bsl_destroy(bsl_stack* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITSTACK_LINEAR_H */

@@ -1,0 +1,212 @@
+"""GPU parity of the HIP path (through the C-ABI) against the fp64 CPU oracle.
+
+Bars: sign unpacking and the integer-valued forward are bit-exact; every other output
+is within a relative Frobenius error of 5e-3 of the oracle (the layer's stated
+tolerance).  Large shapes are checked on seeded row samples that the oracle computes
+one by one, in the same launch configuration the benchmark times.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import bit_sign_rank_amd as bsl  # noqa: E402  (no skip: a missing library must fail here)
+from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    bsl.lib()  # raises if the library is missing
+    yield
+
+
+def integer_blocks(m, d, n, seed=21):
+    return [
+        {"bits": synth.sign_bits(seed, m, d, i), "u": np.full((m, 16), 0.25, np.float16), "v": np.full((d, 16), 0.25, np.float16)}
+        for i in range(n)
+    ]
+
+
+# ---------------------------------------------------------------- sign unpack
+@pytest.mark.parametrize("m,d", [(1024, 1024), (48, 1536), (37, 520), (4096, 4096), (16, 8)])
+@pytest.mark.parametrize("path", [0, 1])
+def test_debug_unpack_bit_exact(m, d, path):
+    blocks = synth.synthetic_blocks(5, m, d, 2, 16, m, d)
+    with Stack([(m, d, blocks)]) as st:
+        st.load([2])
+        for i in range(2):
+            out = torch.empty((m, d), dtype=torch.int8, device="cuda")
+            bsl.bsl_debug_unpack(st.h, 0, i, path, out.data_ptr(), 0)
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), oracle.signs_from_bits(blocks[i]["bits"], d))
+
+
+# ---------------------------------------------------------------- exact integer forward
+@pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1)])
+@pytest.mark.parametrize("M", [1, 3, 8, 17])
+def test_integer_forward_bit_exact(m, d, n, M):
+    # U = V = 0.25 with k = 16 makes U V^T == 1, so y = x (sum_i S_i)^T is an integer of
+    # magnitude < 2^20; every partial sum is exact in fp32, so any order gives the same bits.
+    blocks = integer_blocks(m, d, n)
+    x = synth.integer_activations(9, M, d)
+    with Stack([(m, d, blocks)]) as st:
+        st.load([n])
+        y = st.forward(0, x, fp32=True)
+    assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+# ---------------------------------------------------------------- decomposed 1024 x 1024
+@pytest.fixture(scope="module")
+def cfg1_blocks():
+    W = synth.gaussian_weight(0, 1024, 1024)
+    blocks, _ = oracle.decompose(W, 16, 4)
+    return blocks
+
+
+@pytest.mark.parametrize("fp32", [True, False])
+def test_decomposed_weight_all_block_counts(cfg1_blocks, fp32):
+    x1 = synth.activations(1, 1, 1024)
+    x8 = synth.activations(2, 8, 1024)
+    with Stack([(1024, 1024, cfg1_blocks)]) as st:
+        for n in (1, 2, 3, 4):  # grow one block at a time, no repacking of the others
+            st.load([n])
+            assert bsl.bsl_active_blocks(st.h, 0) == n
+            for x in (x1, x8):
+                y = st.forward(0, x, fp32=fp32)
+                ref = oracle.forward(x, cfg1_blocks, n)
+                assert rel_err(y, ref) <= REL_TOL
+
+
+def test_grow_shrink_and_zero_blocks(cfg1_blocks):
+    x = synth.activations(3, 1, 1024)
+    with Stack([(1024, 1024, cfg1_blocks)]) as st:
+        for n in (4, 2, 3, 0, 1, 4):
+            st.load([n])
+            y = st.forward(0, x)
+            if n == 0:
+                assert not y.any()
+            else:
+                assert rel_err(y, oracle.forward(x, cfg1_blocks, n)) <= REL_TOL
+        resident = bsl.bsl_resident_bytes(st.h)
+        st.load([0])
+        assert bsl.bsl_resident_bytes(st.h) == 0 and resident > 0
+
+
+def test_non_default_stream(cfg1_blocks):
+    x = synth.activations(4, 1, 1024)
+    s = torch.cuda.Stream()
+    with Stack([(1024, 1024, cfg1_blocks)]) as st:
+        st.load([4], stream=s)
+        with torch.cuda.stream(s):
+            y = st.forward(0, x, stream=s)
+    assert rel_err(y, oracle.forward(x, cfg1_blocks, 4)) <= REL_TOL
+
+
+# ---------------------------------------------------------------- 8B decoder layer
+def layer_blocks(shapes, counts, seed, layer=0):
+    return [(m, d, synth.synthetic_blocks(seed, m, d, int(n), 16, layer, j)) for j, ((_, m, d), n) in enumerate(zip(shapes, counts))]
+
+
+def check_sampled(weights, counts, ys, xs, rows_per_weight=48, seed=0):
+    for j, ((m, d, blocks), n, y, x) in enumerate(zip(weights, counts, ys, xs)):
+        rows = synth.sample_rows(seed, m, rows_per_weight, j)
+        ref = oracle.forward_rows(x, blocks, rows, int(n))
+        err = rel_err(y[:, rows], ref)
+        assert err <= REL_TOL, (j, m, d, n, err)
+
+
+@pytest.mark.slow
+def test_llama3_8b_layer_decode_grouped():
+    shapes = synth.LLAMA3_8B_LAYER
+    counts = [8] * 7
+    weights = layer_blocks(shapes, counts, seed=11)
+    xs = [synth.activations(12, 1, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(7)), xs)
+        check_sampled(weights, counts, ys, xs)
+        # single-weight launches agree with the grouped launch bit for bit
+        for j in (1, 4, 6):
+            assert np.array_equal(st.forward(j, xs[j]), ys[j])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_llama3_8b_variable_block_counts(M):
+    shapes = synth.LLAMA3_8B_LAYER
+    counts = synth.block_counts(13, 7, 1, 16)
+    weights = layer_blocks(shapes, counts, seed=14)
+    xs = [synth.activations(15, M, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(7)), xs)
+        check_sampled(weights, counts, ys, xs, rows_per_weight=32)
+
+
+@pytest.mark.slow
+def test_llama3_8b_prefill_2048_tokens():
+    shapes = [("q", 4096, 4096), ("down", 4096, 14336)]
+    counts = [8, 8]
+    weights = layer_blocks(shapes, counts, seed=16)
+    xs = [synth.activations(17, 2048, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load(counts)
+        ys = [st.forward(j, xs[j], fp32=False) for j in range(2)]
+        check_sampled(weights, counts, ys, xs, rows_per_weight=24)
+
+
+@pytest.mark.slow
+def test_llama2_70b_layer_decode():
+    shapes = synth.LLAMA2_70B_LAYER
+    counts = synth.block_counts(18, 7, 1, 6)
+    weights = layer_blocks(shapes, counts, seed=19)
+    xs = [synth.activations(20, 1, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(7)), xs, fp32=False)
+        check_sampled(weights, counts, ys, xs, rows_per_weight=32)
+
+
+# ---------------------------------------------------------------- ragged shapes
+@pytest.mark.parametrize("m,d,M", [(37, 520, 1), (37, 520, 5), (300, 11008 // 4, 1), (1000, 1544, 9), (16, 8, 2)])
+def test_ragged_shapes_random_blocks(m, d, M):
+    blocks = synth.synthetic_blocks(23, m, d, 3, 16, m, d)
+    x = synth.activations(24, M, d)
+    with Stack([(m, d, blocks)]) as st:
+        st.load([3])
+        y = st.forward(0, x)
+    assert rel_err(y, oracle.forward(x, blocks, 3)) <= REL_TOL
+
+
+# ---------------------------------------------------------------- error handling
+def test_errors_leave_state_unchanged(cfg1_blocks):
+    x = torch.zeros((1, 1024 + 8), dtype=torch.float16, device="cuda")
+    y = torch.zeros((1, 1024), dtype=torch.float32, device="cuda")
+    budget = bsl.bsl_block_bytes(1024, 1024) * 2 + 200_000
+    with Stack([(1024, 1024, cfg1_blocks)], budget=budget) as st:
+        st.load([2])
+        before = bsl.bsl_resident_bytes(st.h)
+        with pytest.raises(bsl.BslError) as e:
+            st.load([3])
+        assert e.value.code == bsl.BSL_ENOMEM
+        assert bsl.bsl_active_blocks(st.h, 0) == 2 and bsl.bsl_resident_bytes(st.h) == before
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_forward(st.h, 0, x.data_ptr() + 2, y.data_ptr(), 1, True, 0)  # misaligned x
+        assert e.value.code == bsl.BSL_EINVAL
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_forward(st.h, 1, x.data_ptr(), y.data_ptr(), 1, True, 0)  # no such weight
+        assert e.value.code == bsl.BSL_EINVAL
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_load_blocks(st.h, [5], 0)  # only 4 source blocks
+        assert e.value.code == bsl.BSL_EINVAL
+        assert bsl.bsl_active_blocks(st.h, 0) == 2
+        # still works after the failures
+        xx = synth.activations(5, 1, 1024)
+        assert rel_err(st.forward(0, xx), oracle.forward(xx, cfg1_blocks, 2)) <= REL_TOL

@@ -189,7 +189,7 @@ def test_ragged_shapes_random_blocks(m, d, M):
 def test_errors_leave_state_unchanged(cfg1_blocks):
     x = torch.zeros((1, 1024 + 8), dtype=torch.float16, device="cuda")
     y = torch.zeros((1, 1024), dtype=torch.float32, device="cuda")
-    budget = bsl.bsl_block_bytes(1024, 1024) * 2 + 200_000
+    budget = bsl.bsl_block_bytes(1024, 1024) * 2 + 100_000  # room for 2 blocks, not 3
     with Stack([(1024, 1024, cfg1_blocks)], budget=budget) as st:
         st.load([2])
         before = bsl.bsl_resident_bytes(st.h)

@@ -1,0 +1,306 @@
+"""Benchmark of the BitStack residual-block linear layer on one MI355X.
+
+Headline (printed as one JSON line): HBM GB/s of single-token decode through the
+seven linears of a Llama-3-8B-shaped decoder layer (q/o 4096x4096, k/v 1024x4096,
+gate/up 14336x4096, down 4096x14336), each held as n = 8 residual blocks with k = 16
+(synthetic Bernoulli(0.5) signs, U and V = |N(0,1)| * 0.05 in fp16, x ~ N(0,1) fp16).
+One step is one grouped launch over the layer's seven linears.  Four distinct copies
+of the layer are resident (about 0.96 GB) and the steps rotate over them, so the
+256 MB last-level cache cannot serve the reads.  Bytes are the algorithmic bytes of
+the loaded blocks, n * (m d / 8 + 2 k (m + d)) per weight, counted once.
+
+Also reported: prefill at M = 2048 tokens through one such layer (MFMA TFLOP/s of the
+S Z contraction, 2 n k M m d per weight), the decode kernel's roofline from per-launch
+HIP events, and the CPU oracle (fp64 reconstruct-then-matmul) on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
+                       [--prefill-steps P] [--no-cpu] [--sweep] [--llama70b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "BitStack linear HBM GB/s + MFMA TFLOP/s (% of peak), M=1 decode & M=2048 prefill"
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+K_RANK = 16
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def block_bytes(m: int, d: int) -> int:
+    return m * d // 8 + 2 * K_RANK * (m + d)
+
+
+class Layers:
+    """One bitstack stack holding `layers` copies of a decoder layer's linears."""
+
+    def __init__(self, bsl, torch, shapes, counts, layers, seed, M):
+        self.bsl, self.torch = bsl, torch
+        self.shapes = shapes
+        self.layers = layers
+        self.per = len(shapes)
+        ms = [m for _ in range(layers) for (_, m, _) in shapes]
+        ds = [d for _ in range(layers) for (_, _, d) in shapes]
+        self.h = bsl.bsl_init(0, ms, ds, 16, 16, 0)
+        self.counts = []
+        for l in range(layers):
+            for j, (_, m, d) in enumerate(shapes):
+                n = int(counts[l][j])
+                blocks = synth.synthetic_blocks(seed, m, d, n, 16, l, j)
+                bsl.bsl_set_source(self.h, l * self.per + j, blocks)
+                self.counts.append(n)
+            log(f"  generated layer {l + 1}/{layers}")
+        bsl.bsl_load_blocks(self.h, self.counts, 0)
+        # the host copies are no longer needed once loaded
+        for key in [k for k in bsl._sources if k[0] == self.h]:
+            del bsl._sources[key]
+        self.x, self.y = [], []
+        for l in range(layers):
+            xs, ys = [], []
+            for j, (_, m, d) in enumerate(shapes):
+                x = synth.activations(seed + 1, M, d, l, j)
+                xs.append(torch.from_numpy(x).cuda())
+                ys.append(torch.empty((M, m), dtype=torch.float16, device="cuda"))
+            self.x.append(xs)
+            self.y.append(ys)
+        self.M = M
+
+    def launch(self, l: int, stream: int) -> None:
+        ws = list(range(l * self.per, (l + 1) * self.per))
+        self.bsl.bsl_forward_group(self.h, ws, [t.data_ptr() for t in self.x[l]], [t.data_ptr() for t in self.y[l]],
+                                   self.M, False, stream)
+
+    def bytes(self, l: int) -> int:
+        return sum(self.counts[l * self.per + j] * block_bytes(m, d) for j, (_, m, d) in enumerate(self.shapes))
+
+    def flops(self, l: int) -> int:
+        return sum(2 * self.counts[l * self.per + j] * K_RANK * self.M * m * d for j, (_, m, d) in enumerate(self.shapes))
+
+    def close(self):
+        self.torch.cuda.synchronize()
+        self.bsl.bsl_destroy(self.h)
+
+
+def time_steps(torch, layers: Layers, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps (one grouped launch each) between two
+    device synchronisations; per-launch HIP events on the launch stream give the
+    kernel durations."""
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    for s in range(warmup):
+        layers.launch(s % layers.layers, sp)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    total_bytes = total_flops = 0
+    t0 = time.perf_counter()
+    for s in range(steps):
+        l = s % layers.layers
+        ev[s][0].record(stream)
+        layers.launch(l, sp)
+        ev[s][1].record(stream)
+        total_bytes += layers.bytes(l)
+        total_flops += layers.flops(l)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, kern_ms, total_bytes, total_flops
+
+
+def cpu_baseline(seed: int) -> dict:
+    """The oracle, untouched, on a bounded sample of the decode workload: one
+    8B-shaped layer (all seven linears) with n = 8 and M = 1 (one step of the GPU
+    benchmark; about 10-20 s of CPU work)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sample = list(synth.LLAMA3_8B_LAYER)
+    total_bytes = 0
+    elapsed = 0.0
+    for j, (_, m, d) in enumerate(sample):
+        blocks = synth.synthetic_blocks(seed, m, d, 8, 16, 99, j)
+        x = synth.activations(seed + 1, 1, d, 99, j)
+        t0 = time.perf_counter()
+        oracle.forward(x, blocks, 8)
+        elapsed += time.perf_counter() - t0
+        total_bytes += 8 * block_bytes(m, d)
+    return {
+        "value": round(total_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": "one Llama-3-8B-shaped layer (7 linears), n=8, M=1: fp64 reconstruct-then-matmul per linear",
+        "seconds": round(elapsed, 2),
+    }
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
+    ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_sign_rank_amd as bsl
+
+    bsl.lib()  # fails loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device: {dev.name} ({getattr(dev, 'gcnArchName', '?')}), {dev.multi_processor_count} CUs")
+
+    shapes = synth.LLAMA3_8B_LAYER
+    result = {"metric": METRIC}
+
+    # ---------------- decode (headline)
+    log(f"decode: building {args.layers} resident 8B-shaped layers (n=8, k=16)")
+    dec = Layers(bsl, torch, shapes, [[8] * 7] * args.layers, args.layers, args.seed, M=1)
+    wall, kern_ms, tbytes, tflops = time_steps(torch, dec, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = tbytes / wall / 1e9
+    kavg = float(np.mean(kern_ms))
+    per_launch_bytes = dec.bytes(0)
+    achieved = per_launch_bytes / (kavg * 1e-3) / 1e9
+    log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s wall, kernel avg {kavg * 1e3:.1f} us -> {achieved:.0f} GB/s")
+    per_weight = []
+    for j, (name, m, d) in enumerate(shapes):
+        # single-weight launches, for the per-shape picture
+        h = dec.h
+        x, y = dec.x[0][j], dec.y[0][j]
+        st = torch.cuda.current_stream()
+        for _ in range(5):
+            bsl.bsl_forward(h, j, x.data_ptr(), y.data_ptr(), 1, False, int(st.cuda_stream))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 50
+        e0.record(st)
+        for r in range(reps):
+            lw = (r % args.layers) * 7 + j
+            bsl.bsl_forward(h, lw, dec.x[r % args.layers][j].data_ptr(), dec.y[r % args.layers][j].data_ptr(), 1, False,
+                            int(st.cuda_stream))
+        e1.record(st)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        b = 8 * block_bytes(m, d)
+        per_weight.append({"weight": name, "m": m, "d": d, "us": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1)})
+    dec.close()
+    del dec
+    torch.cuda.empty_cache()
+
+    result.update(
+        {
+            "value": round(value, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "f16",
+            "data": "synthetic",
+            "config": {
+                "workload": "Llama-3-8B-shaped decoder-layer linears (q,k,v,o,gate,up,down), n=8 blocks, k=16, M=1 decode, "
+                f"one grouped launch per step, {args.layers} resident layer copies rotated",
+                "bytes_per_step": per_launch_bytes,
+                "mfma_flops_per_step": int(tflops // args.steps),
+                "hbm_frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+                "mfma_tflops": round(tflops / wall / 1e12, 1),
+            },
+            "roofline": {
+                "bound": "hbm",
+                "kernel": "decode_m1_kernel",
+                "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "avg_launch_us": round(kavg * 1e3, 2),
+            },
+            "decode_single_weight_launches": per_weight,
+        }
+    )
+
+    # ---------------- prefill M = 2048
+    if not args.no_prefill:
+        log("prefill: one 8B-shaped layer, n=8, M=2048")
+        pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048)
+        wall_p, kms_p, tb_p, tf_p = time_steps(torch, pre, args.prefill_steps, 1)
+        tfl = tf_p / wall_p / 1e12
+        result["prefill"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, one grouped launch per step",
+            "ms_per_step": round(wall_p * 1e3 / args.prefill_steps, 2),
+            "mfma_tflops": round(tfl, 1),
+            "mfma_frac_of_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4),
+            "kernel": "gemm_kernel",
+            "flops_per_step": int(tf_p // args.prefill_steps),
+        }
+        log(f"prefill: {wall_p * 1e3 / args.prefill_steps:.1f} ms/step, {tfl:.1f} TFLOP/s")
+        pre.close()
+        del pre
+        torch.cuda.empty_cache()
+
+    # ---------------- optional sweeps
+    if args.sweep:
+        sweep = []
+        counts = synth.block_counts(13, 7, 1, 16)
+        for M in (1, 4, 16):
+            lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M)
+            w_, k_, b_, f_ = time_steps(torch, lay, 50, 5)
+            sweep.append({"M": M, "n_w": [int(c) for c in counts], "GB/s": round(b_ / w_ / 1e9, 1),
+                          "mfma_tflops": round(f_ / w_ / 1e12, 1), "us_per_step": round(w_ * 1e6 / 50, 1)})
+            lay.close()
+            del lay
+            torch.cuda.empty_cache()
+            log(f"sweep M={M}: {sweep[-1]}")
+        result["variable_blocks_sweep"] = sweep
+    if args.llama70b:
+        counts = [synth.block_counts(18, 7, 1, 6, l) for l in range(synth.LLAMA2_70B_LAYERS)]
+        log("llama70b: building 80 layers (this takes a while)")
+        lay = Layers(bsl, torch, synth.LLAMA2_70B_LAYER, counts, synth.LLAMA2_70B_LAYERS, args.seed + 21, M=1)
+        w_, k_, b_, f_ = time_steps(torch, lay, synth.LLAMA2_70B_LAYERS * 3, synth.LLAMA2_70B_LAYERS)
+        tok_ms = w_ * 1e3 / 3
+        result["llama2_70b_decode"] = {"ms_per_token": round(tok_ms, 3), "GB/s": round(b_ / w_ / 1e9, 1),
+                                       "bytes_per_token": int(b_ // 3)}
+        lay.close()
+
+    # ---------------- CPU oracle
+    if not args.no_cpu:
+        log("cpu baseline: oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(args.seed + 5)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -168,7 +168,8 @@ int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
 }
 
-int decode_groups(const Weight& W) { return (W.mt + kDecodeRowTiles - 1) / kDecodeRowTiles; }
+// Row groups of the single-token kernel: 4 waves x kDecodeRowTiles row tiles each.
+int decode_groups(const Weight& W) { return (W.mt + 4 * kDecodeRowTiles - 1) / (4 * kDecodeRowTiles); }
 
 }  // namespace
 
@@ -216,7 +217,7 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
   if (!out || !m || !d) return fail(BSL_EINVAL, "bsl_init: null pointer");
   *out = nullptr;
   if (num_weights < 1 || num_weights > (1 << 20)) return fail(BSL_EINVAL, "bsl_init: num_weights out of range");
-  if (n_cap < 1 || n_cap > 1024) return fail(BSL_EINVAL, "bsl_init: n_cap must be in 1..1024");
+  if (n_cap < 1 || n_cap > kMaxBlocks) return fail(BSL_EINVAL, "bsl_init: n_cap must be in 1..64");
   if (k != kRank) return fail(BSL_EUNSUPPORTED, "bsl_init: only k = 16 is supported");
   for (int32_t w = 0; w < num_weights; ++w)
     if (!shape_ok(m[w], d[w])) return fail(BSL_EUNSUPPORTED, "bsl_init: weight " + std::to_string(w) + " has an unsupported shape");

@@ -15,6 +15,7 @@ constexpr int kChunkCols = 512;   // columns per sign tile
 constexpr int kPlanes = 16;       // 32-column planes per chunk
 constexpr int kTileBytes = 1024;  // 16 x 512 bits
 constexpr int kMaxGroup = 8;      // weights per grouped launch
+constexpr int kMaxBlocks = 64;    // blocks per weight (the kernels keep the table in LDS)
 
 inline int64_t pad_rows(int64_t m) { return (m + kTileRows - 1) / kTileRows * kTileRows; }
 inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * kChunkCols; }

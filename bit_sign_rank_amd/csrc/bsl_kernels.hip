@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "bsl_internal.h"
 
@@ -59,12 +60,41 @@ __host__ __device__ constexpr uint16_t plane_inv_factor_bits(int b) {
   return (uint16_t)(0x8000u | (uint16_t)((15 + plane_pos(b) - 8) << 10));
 }
 
+// Same factors for a plane index that is only known at run time (wave-uniform).
+__device__ __forceinline__ uint32_t plane_x_factor_bits_dyn(int b) {
+  const int pos = b < 6 ? b + 6 : (b < 12 ? b : b - 6);
+  return 0x8000u | (uint32_t)((23 - pos) << 10);
+}
+__device__ __forceinline__ uint32_t plane_inv_factor_bits_dyn(int b) {
+  const int pos = b < 6 ? b + 6 : (b < 12 ? b : b - 6);
+  return 0x8000u | (uint32_t)((7 + pos) << 10);
+}
+
 __device__ __forceinline__ half8 as_half8(u32x4 v) { return __builtin_bit_cast(half8, v); }
 __device__ __forceinline__ half2v as_half2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 __device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 
-__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 load8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+// Loads through the global address space.  Pointers read from the block table are
+// generic; without the cast the compiler emits flat loads, which also count against
+// the LDS wait counter, so every LDS wait would stall on outstanding HBM reads.
+#define BSL_GLOBAL __attribute__((address_space(1)))
+#define BSL_CONST __attribute__((address_space(4)))
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const BSL_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(p));
+}
+__device__ __forceinline__ u32x2 load8(const void* p) {
+  return *reinterpret_cast<const BSL_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
+}
+// Block table entries are read with scalar loads (the table does not change while a
+// kernel runs and the index is uniform).
+__device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
+  const BSL_CONST BlockPtrs* t = reinterpret_cast<const BSL_CONST BlockPtrs*>(reinterpret_cast<uintptr_t>(table)) + i;
+  BlockPtrs b;
+  b.signs = t->signs;
+  b.u = t->u;
+  b.v = t->v;
+  return b;
+}
 
 // A fragment of plane b (bit-plane encoding) from a lane's four raw words.
 template <int B>
@@ -83,26 +113,53 @@ __device__ __forceinline__ u32x4 pm1_fragment(const u32x4& w, int b) {
   return a;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRowRor8 = 0x128;        // lane i <- lane (i + 8) mod 16 of its row
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7 - i of its 8-lane half
+constexpr int kDppQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+
 // Sum a C fragment (lane L holds rows 4 (L/16) + v, v = 0..3, of column L % 16) over
-// the 16 columns.  Returns, in every lane, the sum for row 4 (L/16) + vsel(L) with
-// vsel(L) = 2 ((L >> 3) & 1) + ((L >> 2) & 1); lanes with L % 4 == 0 hold distinct rows.
+// the 16 columns, in registers (DPP).  Returns, in every lane, the sum for row
+// 4 (L/16) + vsel(L) with vsel(L) = 2 ((L >> 3) & 1) + ((L >> 2) & 1); lanes with
+// L % 4 == 0 hold distinct rows.  Round 1 pairs lanes L, L^8 and keeps rows {0,1} or
+// {2,3}; round 2 pairs L with 7 - L (other half of its bit-2 group) and keeps one row;
+// rounds 3-4 add over the quad.
 __device__ __forceinline__ float reduce_columns(float4v a, int lane) {
   const bool hi8 = lane & 8, hi4 = lane & 4;
   const float keep0 = hi8 ? a[2] : a[0], keep1 = hi8 ? a[3] : a[1];
   const float send0 = hi8 ? a[0] : a[2], send1 = hi8 ? a[1] : a[3];
-  const float k0 = keep0 + __shfl_xor(send0, 8);
-  const float k1 = keep1 + __shfl_xor(send1, 8);
+  const float k0 = keep0 + dpp_mov<kDppRowRor8>(send0);
+  const float k1 = keep1 + dpp_mov<kDppRowRor8>(send1);
   const float keep = hi4 ? k1 : k0, send = hi4 ? k0 : k1;
-  float r = keep + __shfl_xor(send, 4);
-  r += __shfl_xor(r, 2);
-  r += __shfl_xor(r, 1);
+  float r = keep + dpp_mov<kDppRowHalfMirror>(send);
+  r += dpp_mov<kDppQuadSwap2>(r);
+  r += dpp_mov<kDppQuadSwap1>(r);
   return r;
+}
+
+// Sum over the four 16-lane groups (lanes L, L^16, L^32, L^48).
+__device__ __forceinline__ float sum_over_lane_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
 }
 __device__ __forceinline__ int reduced_row(int lane) { return 4 * (lane >> 4) + 2 * ((lane >> 3) & 1) + ((lane >> 2) & 1); }
 
 __device__ __forceinline__ void store_y(void* y, size_t idx, float v, int fp32) {
   if (fp32) reinterpret_cast<float*>(y)[idx] = v;
   else reinterpret_cast<_Float16*>(y)[idx] = (_Float16)v;
+}
+
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads() it does not
+// wait for this wave's outstanding global loads, so prefetches stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Pick the descriptor of the weight that owns `item` (uniform across the wave).
@@ -115,136 +172,200 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 }
 
 // ============================================================ single-token kernel
-// One wave per work item = (weight, group of R row tiles, one 512-column chunk); the
-// wave loops over all loaded blocks, accumulating U_i-weighted partial products per
-// row tile, reduces over r once, writes its partial sums, and the last wave of a row
-// group to arrive adds the chunks in a fixed order and writes y.
+// One workgroup (4 waves) per work item = (weight, group of 4 R row tiles, one
+// 512-column chunk).  For every loaded block the workgroup builds the chunk's Z tile
+// once, in LDS (double buffered; wave w builds planes 4w..4w+3), and each wave reads
+// the 16 B fragments into registers and runs its R row tiles against them.  Block i's
+// sign tiles and block i+1's V fragments are fetched one block ahead, U fragments
+// right after the previous block's tiles, so the HBM stream never waits on compute.
+// After the last block each wave reduces its U-weighted accumulators over r, stores
+// the chunk's partial sums (write-through, coherent across XCDs), and the last
+// workgroup of a row group to arrive adds the chunks in a fixed order and writes y.
 template <int R>
-__global__ __launch_bounds__(256) void decode_m1_kernel(GroupArgs args) {
-  __shared__ u32x4 xs_all[4][64];  // per wave: the chunk's 512 activations, plane-scaled
-  const int wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_m1_kernel(GroupArgs args) {
+  __shared__ u32x4 zs[2][kPlanes][64];   // Z fragments of two blocks (32 KiB)
+  __shared__ u32x4 xsh[kPlanes][4];      // plane-scaled activations, [plane][lane group]
+  __shared__ float csum[2][4][16];       // per-wave partial column sums of Z
+  __shared__ BlockPtrs btab[kMaxBlocks]; // the weight's block table
+  __shared__ uint32_t last_flag;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= args.total_items) return;  // no block-wide barrier below this point
-  const WeightDesc W = find_weight(args, item);
-  const int local = item - W.item_begin;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  const WeightDesc W = find_weight(args, blockIdx.x);
+  const int local = blockIdx.x - W.item_begin;
   const int rg = local / W.nch;
   const int ch = local - rg * W.nch;
-  const int g = lane >> 4;
-  const int col0 = ch * kChunkCols;
   const int rows_pad = W.mt * kTileRows;
-
-  u32x4* xs = xs_all[wave];
-  {
-    const int col = col0 + 8 * lane;  // this lane's 8 columns belong to plane lane / 4
-    u32x4 xv = {0u, 0u, 0u, 0u};
-    if (col < W.d) xv = load16(W.x + col);
-    uint32_t fbits = 0;
-#pragma unroll
-    for (int b = 0; b < kPlanes; ++b)
-      if ((lane >> 2) == b) fbits = plane_x_factor_bits(b);
-    const half2v f = as_half2(fbits | (fbits << 16));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xv[q] = as_u32(as_half2(xv[q]) * f);
-    xs[lane] = xv;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rt0 = rg * 4 * R + wave * R;
+  const int ntiles = max(0, min(R, W.mt - rt0));
+  const int nb = W.nblocks;
+  const int tmax = max(0, W.mt - 1);
 
   float4v accy[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) accy[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-  const int rt0 = rg * R;
-  const int ntiles = min(R, W.mt - rt0);
+  // Every load is issued unconditionally (row tiles past the end read a clamped, valid
+  // tile) so the number of loads in flight is the same on every path and the
+  // compiler's in-order wait counts never drain the prefetches; tiles past the end
+  // get U = 0 and add nothing.
+  u32x4 raw[R], rawn[R];
+  u32x2 uf[R];
+  u32x4 vv[4];
 
-  for (int i = 0; i < W.nblocks; ++i) {
-    const BlockPtrs bp = W.blocks[i];
-    u32x4 raw[R];
-    u32x2 uf[R];
+  auto load_signs = [&](const BlockPtrs& bp, u32x4* rw) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      if (t < ntiles) {
-        raw[t] = load16(bp.signs + ((size_t)(rt0 + t) * W.nch + ch) * kTileBytes + lane * 16);
-        uf[t] = load8(bp.u + ((size_t)(rt0 + t) * 64 + lane) * 4);
-      }
-    }
-    half8 zb[kPlanes];
+    for (int t = 0; t < R; ++t)
+      rw[t] = load16(bp.signs + ((size_t)min(rt0 + t, tmax) * W.nch + ch) * kTileBytes + lane * 16);
+  };
+  auto load_u = [&](const BlockPtrs& bp) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) uf[t] = load8(bp.u + ((size_t)min(rt0 + t, tmax) * 64 + lane) * 4);
+  };
+  auto load_v = [&](const BlockPtrs& bp) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) vv[p] = load16(bp.v + (((size_t)ch * kPlanes + 4 * wave + p) * 64 + lane) * 8);
+  };
+  // Z fragments of this wave's 4 planes from vv, and their column sums over the chunk.
+  auto build_z = [&](int buf) {
     float cs = 0.f;
 #pragma unroll
-    for (int b = 0; b < kPlanes; ++b) {
-      const u32x4 vv = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + lane) * 8);
-      const u32x4 xx = xs[4 * b + g];
-      const half2v inv = as_half2((uint32_t)plane_inv_factor_bits(b) * 0x00010001u);
+    for (int p = 0; p < 4; ++p) {
+      const int b = 4 * wave + p;
+      const u32x4 xw = xsh[b][g];
+      const half2v inv = as_half2(plane_inv_factor_bits_dyn(b) * 0x00010001u);
       u32x4 z;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const half2v zq = as_half2(vv[q]) * as_half2(xx[q]);
+        const half2v zq = as_half2(vv[p][q]) * as_half2(xw[q]);
         z[q] = as_u32(zq);
         cs = __builtin_amdgcn_fdot2(zq, inv, cs, false);
       }
-      zb[b] = as_half8(z);
+      zs[buf][b][lane] = z;
     }
-    cs += __shfl_xor(cs, 16);
-    cs += __shfl_xor(cs, 32);
-    const float init = cs * kPlaneAccScale;
+    cs = sum_over_lane_groups(cs);
+    if (lane < 16) csum[buf][wave][lane] = cs;
+  };
+
+  if (nb > 0) {
+    if (threadIdx.x < nb) btab[threadIdx.x] = load_block(W.blocks, threadIdx.x);
+    const BlockPtrs b0 = load_block(W.blocks, 0);
+    load_signs(b0, raw);
+    load_v(b0);
+    // plane-scaled activations of this wave's planes (lanes with r = 0 keep them in LDS)
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      if (t < ntiles) {
-        const u32x4 w = raw[t];
-        const u32x4 lo = w << 6u;
-        const u32x4 hi = w >> 6u;
-        float4v acc = {init, init, init, init};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<0>(w, lo, hi)), zb[0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<1>(w, lo, hi)), zb[1], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<2>(w, lo, hi)), zb[2], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<3>(w, lo, hi)), zb[3], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<4>(w, lo, hi)), zb[4], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<5>(w, lo, hi)), zb[5], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<6>(w, lo, hi)), zb[6], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<7>(w, lo, hi)), zb[7], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<8>(w, lo, hi)), zb[8], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<9>(w, lo, hi)), zb[9], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<10>(w, lo, hi)), zb[10], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<11>(w, lo, hi)), zb[11], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<12>(w, lo, hi)), zb[12], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<13>(w, lo, hi)), zb[13], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<14>(w, lo, hi)), zb[14], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(plane_fragment<15>(w, lo, hi)), zb[15], acc, 0, 0, 0);
-        const half2v u01 = as_half2(uf[t][0]), u23 = as_half2(uf[t][1]);
-        accy[t][0] += (float)u01[0] * acc[0];
-        accy[t][1] += (float)u01[1] * acc[1];
-        accy[t][2] += (float)u23[0] * acc[2];
-        accy[t][3] += (float)u23[1] * acc[3];
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int b = 4 * wave + p;
+      const int col = ch * kChunkCols + 32 * b + 8 * g;
+      u32x4 xv = {0u, 0u, 0u, 0u};
+      if (col < W.d) xv = load16(W.x + col);
+      const uint32_t f = plane_x_factor_bits_dyn(b) * 0x00010001u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[q] = as_u32(as_half2(xv[q]) * as_half2(f));
+      if (r16 == 0) xsh[b][g] = xv;
     }
+    build_z(0);
+    load_v(load_block(W.blocks, min(1, nb - 1)));
+    load_u(b0);
   }
 
-  // partial sums of this chunk
+  // One block step: block i's signs are in `cur` and its U fragments in uf; the step
+  // prefetches block i+1's signs into `nxt`, block i+2's V fragments and, after its
+  // tiles, block i+1's U fragments.  Scheduling barriers pin the issue order.
+  auto step = [&](int i, u32x4 (&cur)[R], u32x4 (&nxt)[R], auto prefetch) {
+    const int buf = i & 1;
+    lds_barrier();  // Z_i and its column sums are complete; buffer buf^1 is free
+    const float init = (csum[buf][0][r16] + csum[buf][1][r16] + csum[buf][2][r16] + csum[buf][3][r16]) * kPlaneAccScale;
+    half8 zb[kPlanes];
+#pragma unroll
+    for (int b = 0; b < kPlanes; ++b) zb[b] = as_half8(zs[buf][b][lane]);
+    BlockPtrs bn;
+    if constexpr (decltype(prefetch)::value) {
+      bn = btab[i + 1];
+      const BlockPtrs bv = btab[min(i + 2, nb - 1)];
+      build_z(buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_signs(bn, nxt);
+      load_v(bv);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < R; ++t)
+      if (t >= ntiles) uf[t] = (u32x2){0u, 0u};
+    // Four row tiles at a time: four independent accumulator chains per plane.
+#pragma unroll
+    for (int t0 = 0; t0 < R; t0 += 4) {
+      float4v acc[4];
+      u32x4 sh[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[k] = (float4v){init, init, init, init};
+        sh[k] = cur[t0 + k] << 6u;
+      }
+#define BSL_PLANE(B, SRC)                                                                                        \
+  _Pragma("unroll") for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(              \
+      as_half8((SRC) & (0x00010001u << plane_pos(B))), zb[B], acc[k], 0, 0, 0);
+      BSL_PLANE(0, sh[k]) BSL_PLANE(1, sh[k]) BSL_PLANE(2, sh[k]) BSL_PLANE(3, sh[k]) BSL_PLANE(4, sh[k]) BSL_PLANE(5, sh[k])
+      BSL_PLANE(6, cur[t0 + k]) BSL_PLANE(7, cur[t0 + k]) BSL_PLANE(8, cur[t0 + k]) BSL_PLANE(9, cur[t0 + k])
+      BSL_PLANE(10, cur[t0 + k]) BSL_PLANE(11, cur[t0 + k])
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sh[k] = cur[t0 + k] >> 6u;
+      BSL_PLANE(12, sh[k]) BSL_PLANE(13, sh[k]) BSL_PLANE(14, sh[k]) BSL_PLANE(15, sh[k])
+#undef BSL_PLANE
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const half2v u01 = as_half2(uf[t0 + k][0]), u23 = as_half2(uf[t0 + k][1]);
+        accy[t0 + k][0] += (float)u01[0] * acc[k][0];
+        accy[t0 + k][1] += (float)u01[1] * acc[k][1];
+        accy[t0 + k][2] += (float)u23[0] * acc[k][2];
+        accy[t0 + k][3] += (float)u23[1] * acc[k][3];
+      }
+    }
+    if constexpr (decltype(prefetch)::value) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_u(bn);
+    }
+  };
+
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  int i = 0;
+  for (; i + 2 < nb; i += 2) {
+    step(i, raw, rawn, yes{});
+    step(i + 1, rawn, raw, yes{});
+  }
+  if (i + 1 < nb) {
+    step(i, raw, rawn, yes{});
+    step(i + 1, rawn, raw, no{});
+  } else if (i < nb) {
+    step(i, raw, rawn, no{});
+  }
+
+  // This chunk's partial sums, stored write-through at device scope so the last
+  // workgroup (possibly on another XCD) reads them without any cache flush.
   const int rsel = reduced_row(lane);
 #pragma unroll
   for (int t = 0; t < R; ++t) {
-    if (t < ntiles) {
-      const float v = reduce_columns(accy[t], lane);
-      const int row = (rt0 + t) * kTileRows + rsel;
-      if ((lane & 3) == 0) W.partial[(size_t)ch * rows_pad + row] = v;
-    }
+    const float v = reduce_columns(accy[t], lane);
+    if ((lane & 3) == 0 && t < ntiles)
+      __hip_atomic_store(&W.partial[(size_t)ch * rows_pad + (rt0 + t) * kTileRows + rsel], v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
-  // last wave of the row group to arrive sums the chunks in order and writes y
-  __threadfence();
-  uint32_t prev = 0;
-  if (lane == 0) prev = atomicAdd(&W.counters[rg], 1u);
-  prev = __shfl(prev, 0);
-  if (prev != (uint32_t)(W.nch - 1)) return;
-  __threadfence();
-  const int row_begin = rt0 * kTileRows;
-  const int row_end = min(W.m, (rt0 + ntiles) * kTileRows);
-  for (int row = row_begin + lane; row < row_end; row += 64) {
+  __builtin_amdgcn_s_waitcnt(0);  // the stores above have completed before the arrival below
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_flag = __hip_atomic_fetch_add(&W.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.nch - 1);
+  __syncthreads();
+  if (!last_flag) return;
+  const int row_begin = rg * 4 * R * kTileRows;
+  const int row_end = min(W.m, row_begin + 4 * R * kTileRows);
+  for (int row = row_begin + threadIdx.x; row < row_end; row += 256) {
     float s = 0.f;
-    for (int c = 0; c < W.nch; ++c) s += __builtin_nontemporal_load(&W.partial[(size_t)c * rows_pad + row]);
+    for (int c = 0; c < W.nch; ++c)
+      s += __hip_atomic_load(&W.partial[(size_t)c * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     store_y(W.y, row, s * kPlaneOutScale, args.y_fp32);
   }
-  if (lane == 0) __hip_atomic_store(&W.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ============================================================ multi-token kernel
@@ -281,7 +402,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
     for (int t = 0; t < NT; ++t) accy[a][t] = 0.f;
 
   for (int i = 0; i < W.nblocks; ++i) {
-    const BlockPtrs bp = W.blocks[i];
+    const BlockPtrs bp = load_block(W.blocks, i);
     float4v acc[4][NT];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -296,7 +417,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        __syncthreads();  // consumers of the previous Z tile are done
+        lds_barrier();  // consumers of the previous Z tile are done
         // build 8 planes x NT tokens; wave builds planes 2*wave, 2*wave+1
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
@@ -315,7 +436,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
             zs[(p * NT + t) * 64 + lane] = z;
           }
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
           const int b = 8 * half + p;
@@ -372,16 +493,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int tok = tok0 + t;
-      if (writer && rt0 + a < W.mt && tok < M) W.partial[((size_t)split * M + tok) * rows_pad + row] = accy[a][t];
+      if (writer && rt0 + a < W.mt && tok < M)
+        __hip_atomic_store(&W.partial[((size_t)split * M + tok) * rows_pad + row], accy[a][t], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __threadfence();
-  __syncthreads();  // all partial stores issued and every wave is past its last use of zs
+  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
+  __syncthreads();                // ... in every wave, and every wave is past its last use of zs
   uint32_t* last = reinterpret_cast<uint32_t*>(zs);
-  if (threadIdx.x == 0) *last = atomicAdd(&W.counters[rest], 1u) == (uint32_t)(W.splits - 1);
+  if (threadIdx.x == 0)
+    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
   __syncthreads();
   if (!*last) return;
-  __threadfence();
   const int row_begin = rg * kGemmRowTiles * kTileRows;
   const int row_end = min(W.m, row_begin + kGemmRowTiles * kTileRows);
   const int nrows = row_end - row_begin;
@@ -390,7 +513,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
     const int t = e / nrows, row = row_begin + e % nrows;
     const int tok = tok0 + t;
     float s = 0.f;
-    for (int sp = 0; sp < W.splits; ++sp) s += __builtin_nontemporal_load(&W.partial[((size_t)sp * M + tok) * rows_pad + row]);
+    for (int sp = 0; sp < W.splits; ++sp)
+      s += __hip_atomic_load(&W.partial[((size_t)sp * M + tok) * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     store_y(W.y, (size_t)tok * W.m + row, s, args.y_fp32);
   }
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -449,8 +573,8 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
 int launch_decode_m1(const GroupArgs& args, int rows_per_item, void* stream) {
   if (rows_per_item != kDecodeRowTiles) return (int)hipErrorInvalidValue;
   if (args.total_items == 0) return 0;
-  const int blocks = (args.total_items + 3) / 4;
-  hipLaunchKernelGGL(decode_m1_kernel<kDecodeRowTiles>, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), args);
+  hipLaunchKernelGGL(decode_m1_kernel<kDecodeRowTiles>, dim3(args.total_items), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     args);
   return (int)hipGetLastError();
 }
 

@@ -91,8 +91,8 @@ int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* 
 int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out);
 
 /* Create a stack for num_weights weights with shapes m[w] x d[w] (host arrays), rank k
- * (must be 16), at most n_cap blocks per weight (the paper's runs decompose with 16
- * iterations: README, "Decomposition"), on HIP device `device`.  budget_bytes caps
+ * (must be 16), at most n_cap blocks per weight (1 <= n_cap <= 64; the paper's runs
+ * decompose with 16 iterations: README, "Decomposition"), on HIP device `device`.  budget_bytes caps
  * the device bytes held by loaded blocks (0 = no cap).  The per-weight workspace used
  * by bsl_forward is allocated here, so forward never allocates.  *out receives the
  * handle. */

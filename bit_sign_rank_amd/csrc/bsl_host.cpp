@@ -39,12 +39,13 @@ bool shape_ok(int64_t m, int64_t d) { return m >= 1 && m <= (1 << 20) && d >= 8 
 // row-major source that sign is bit (2 q + h) of byte 64 c + 4 b + g of the row.
 void pack_rows(const uint8_t* src, int64_t m, int64_t d, uint8_t* out, int64_t r0, int64_t r1) {
   const int64_t nch = pad_cols(d) / kChunkCols;
+  const int64_t mt = pad_rows(m) / kTileRows;
   const int64_t rowbytes = d / 8;
   for (int64_t r = r0; r < r1; ++r) {
     const int64_t t = r / kTileRows, i = r % kTileRows;
     const uint8_t* row = r < m ? src + r * rowbytes : nullptr;
     for (int64_t c = 0; c < nch; ++c) {
-      uint8_t* tile = out + (t * nch + c) * kTileBytes;
+      uint8_t* tile = out + (c * mt + t) * kTileBytes;
       for (int g = 0; g < 4; ++g) {
         uint8_t bytes[kPlanes];
         for (int b = 0; b < kPlanes; ++b) {
@@ -168,8 +169,8 @@ int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
 }
 
-// Row groups of the single-token kernel: 4 waves x kDecodeRowTiles row tiles each.
-int decode_groups(const Weight& W) { return (W.mt + 4 * kDecodeRowTiles - 1) / (4 * kDecodeRowTiles); }
+// Row groups of the single-token kernel (kDecodeGroupTiles row tiles each).
+int decode_groups(const Weight& W) { return (W.mt + kDecodeGroupTiles - 1) / kDecodeGroupTiles; }
 
 }  // namespace
 
@@ -197,14 +198,14 @@ int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* 
 int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out) {
   if (!tiled || !pm1_out) return fail(BSL_EINVAL, "bsl_unpack_signs: null pointer");
   if (!shape_ok(m, d)) return fail(BSL_EUNSUPPORTED, "bsl_unpack_signs: need 1 <= m, 8 <= d, d % 8 == 0");
-  const int64_t nch = pad_cols(d) / kChunkCols;
+  const int64_t mt = pad_rows(m) / kTileRows;
   for (int64_t r = 0; r < m; ++r) {
     const int64_t t = r / kTileRows, i = r % kTileRows;
     for (int64_t col = 0; col < d; ++col) {
       const int64_t c = col / kChunkCols, cc = col % kChunkCols;
       const int b = (int)(cc / 32), rem = (int)(cc % 32), g = rem / 8, q = (rem % 8) / 2, h = rem % 2;
       uint32_t word;
-      std::memcpy(&word, tiled + (t * nch + c) * kTileBytes + (16 * g + i) * 16 + 4 * q, 4);
+      std::memcpy(&word, tiled + (c * mt + t) * kTileBytes + (16 * g + i) * 16 + 4 * q, 4);
       const uint32_t bit = (word >> (b + 16 * h)) & 1u;
       pm1_out[r * d + col] = bit ? -1 : 1;
     }
@@ -432,7 +433,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.total_items = items;
   DeviceGuard guard(s->device);
   int e;
-  if (M == 1) e = launch_decode_m1(args, kDecodeRowTiles, stream);
+  if (M == 1) e = launch_decode_m1(args, stream);
   else e = launch_gemm(args, nt, token_groups, stream);
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;

@@ -17,11 +17,15 @@ constexpr int kTileBytes = 1024;  // 16 x 512 bits
 constexpr int kMaxGroup = 8;      // weights per grouped launch
 constexpr int kMaxBlocks = 64;    // blocks per weight (the kernels keep the table in LDS)
 
-inline int64_t pad_rows(int64_t m) { return (m + kTileRows - 1) / kTileRows * kTileRows; }
+// Rows are padded to a multiple of 512 (32 tiles, the largest row group any kernel
+// takes), so every kernel can read whole row groups without bounds checks; padding
+// rows have +1 signs and zero U, so they add nothing.
+constexpr int kRowAlign = 512;
+inline int64_t pad_rows(int64_t m) { return (m + kRowAlign - 1) / kRowAlign * kRowAlign; }
 inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * kChunkCols; }
 
 // Device addresses of one loaded block.  One allocation holds, in order:
-//   signs: [m_pad/16][d_pad/512][64 lanes][16 B]                 (tiled bits)
+//   signs: [d_pad/512][m_pad/16][64 lanes][16 B]                 (tiled bits)
 //   u:     [m_pad/16][64 lanes][4] fp16  lane L holds U[16 t + 4 (L/16) + v][L % 16]
 //   v:     [d_pad/512][16 planes][64 lanes][8] fp16
 //          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
@@ -55,13 +59,13 @@ struct GroupArgs {
 };
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
-int launch_decode_m1(const GroupArgs& args, int rows_per_item, void* stream);
+int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
-// Row tiles per decode work item and the workspace each weight needs.
-constexpr int kDecodeRowTiles = 8;
+// Row tiles per single-token work item (512 rows) and the workspace each weight needs.
+constexpr int kDecodeGroupTiles = 32;
 constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
 constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
 constexpr int kGemmMaxSplits = 8;

@@ -85,6 +85,22 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const BSL_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
 }
+// A wave-uniform 64-bit pointer held in vector registers, moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
+  BlockPtrs r;
+  r.signs = uniform_ptr(b.signs);
+  r.u = uniform_ptr(b.u);
+  r.v = uniform_ptr(b.v);
+  return r;
+}
+
 // Block table entries are read with scalar loads (the table does not change while a
 // kernel runs and the index is uniform).
 __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
@@ -172,20 +188,23 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 }
 
 // ============================================================ single-token kernel
-// One workgroup (4 waves) per work item = (weight, group of 4 R row tiles, one
+// One workgroup (NW waves) per work item = (weight, group of NW R = 32 row tiles, one
 // 512-column chunk).  For every loaded block the workgroup builds the chunk's Z tile
-// once, in LDS (double buffered; wave w builds planes 4w..4w+3), and each wave reads
-// the 16 B fragments into registers and runs its R row tiles against them.  Block i's
+// once, in LDS (double buffered; wave w builds planes PP w .. PP w + PP - 1), and each
+// wave runs its R row tiles against it, reading the fragments just ahead of use.  Block i's
 // sign tiles and block i+1's V fragments are fetched one block ahead, U fragments
 // right after the previous block's tiles, so the HBM stream never waits on compute.
 // After the last block each wave reduces its U-weighted accumulators over r, stores
 // the chunk's partial sums (write-through, coherent across XCDs), and the last
 // workgroup of a row group to arrive adds the chunks in a fixed order and writes y.
-template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_m1_kernel(GroupArgs args) {
+template <int NW, int R, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_m1_kernel(GroupArgs args) {
+  static_assert(NW * R == kDecodeGroupTiles && kPlanes % NW == 0 && R % 4 == 0, "decode tiling");
+  constexpr int PP = kPlanes / NW;       // Z planes each wave builds
   __shared__ u32x4 zs[2][kPlanes][64];   // Z fragments of two blocks (32 KiB)
   __shared__ u32x4 xsh[kPlanes][4];      // plane-scaled activations, [plane][lane group]
-  __shared__ float csum[2][4][16];       // per-wave partial column sums of Z
+  __shared__ float csum[2][NW][16];      // per-wave partial column sums of Z
+  __shared__ float4v accl[NW][R][64];    // U-weighted accumulators (LDS, not registers)
   __shared__ BlockPtrs btab[kMaxBlocks]; // the weight's block table
   __shared__ uint32_t last_flag;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -197,41 +216,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rg = local / W.nch;
   const int ch = local - rg * W.nch;
   const int rows_pad = W.mt * kTileRows;
-  const int rt0 = rg * 4 * R + wave * R;
-  const int ntiles = max(0, min(R, W.mt - rt0));
+  const int rt0 = rg * kDecodeGroupTiles + wave * R;  // rows are padded to whole row groups
   const int nb = W.nblocks;
-  const int tmax = max(0, W.mt - 1);
 
-  float4v accy[R];
+  // The U-weighted products of every block are accumulated in LDS (each lane owns its
+  // 16 bytes per tile): the accumulators live across the whole block loop but are
+  // touched once per block, so keeping them in registers would cost occupancy.
 #pragma unroll
-  for (int t = 0; t < R; ++t) accy[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-  // Every load is issued unconditionally (row tiles past the end read a clamped, valid
-  // tile) so the number of loads in flight is the same on every path and the
-  // compiler's in-order wait counts never drain the prefetches; tiles past the end
-  // get U = 0 and add nothing.
+  for (int t = 0; t < R; ++t) accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
+  // Every load is issued unconditionally (padding rows are stored, with +1 signs and
+  // zero U) so the number of loads in flight is the same on every path and the
+  // compiler's in-order wait counts never drain the prefetches.  A wave's R sign
+  // tiles of one block and chunk are contiguous, as are its R U fragments.
   u32x4 raw[R], rawn[R];
   u32x2 uf[R];
-  u32x4 vv[4];
+  u32x4 vv[PP];
 
   auto load_signs = [&](const BlockPtrs& bp, u32x4* rw) {
+    const uint8_t* base = bp.signs + ((size_t)ch * W.mt + rt0) * kTileBytes + lane * 16;
 #pragma unroll
-    for (int t = 0; t < R; ++t)
-      rw[t] = load16(bp.signs + ((size_t)min(rt0 + t, tmax) * W.nch + ch) * kTileBytes + lane * 16);
+    for (int t = 0; t < R; ++t) rw[t] = load16(base + t * kTileBytes);
   };
   auto load_u = [&](const BlockPtrs& bp) {
+    const uint16_t* base = bp.u + ((size_t)rt0 * 64 + lane) * 4;
 #pragma unroll
-    for (int t = 0; t < R; ++t) uf[t] = load8(bp.u + ((size_t)min(rt0 + t, tmax) * 64 + lane) * 4);
+    for (int t = 0; t < R; ++t) uf[t] = load8(base + t * 256);
   };
   auto load_v = [&](const BlockPtrs& bp) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) vv[p] = load16(bp.v + (((size_t)ch * kPlanes + 4 * wave + p) * 64 + lane) * 8);
+    for (int p = 0; p < PP; ++p) vv[p] = load16(bp.v + (((size_t)ch * kPlanes + PP * wave + p) * 64 + lane) * 8);
   };
-  // Z fragments of this wave's 4 planes from vv, and their column sums over the chunk.
+  // Z fragments of this wave's PP planes from vv, and their column sums over the chunk.
   auto build_z = [&](int buf) {
     float cs = 0.f;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int b = 4 * wave + p;
+    for (int p = 0; p < PP; ++p) {
+      const int b = PP * wave + p;
       const u32x4 xw = xsh[b][g];
       const half2v inv = as_half2(plane_inv_factor_bits_dyn(b) * 0x00010001u);
       u32x4 z;
@@ -254,8 +274,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     load_v(b0);
     // plane-scaled activations of this wave's planes (lanes with r = 0 keep them in LDS)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int b = 4 * wave + p;
+    for (int p = 0; p < PP; ++p) {
+      const int b = PP * wave + p;
       const int col = ch * kChunkCols + 32 * b + 8 * g;
       u32x4 xv = {0u, 0u, 0u, 0u};
       if (col < W.d) xv = load16(W.x + col);
@@ -264,35 +284,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int q = 0; q < 4; ++q) xv[q] = as_u32(as_half2(xv[q]) * as_half2(f));
       if (r16 == 0) xsh[b][g] = xv;
     }
+    // Other lanes read these entries: without a barrier that is a data race, and the
+    // compiler may (and does) move their reads before the writing lane's store.
+    lds_barrier();
     build_z(0);
+    __builtin_amdgcn_sched_barrier(0);
     load_v(load_block(W.blocks, min(1, nb - 1)));
     load_u(b0);
   }
 
-  // One block step: block i's signs are in `cur` and its U fragments in uf; the step
-  // prefetches block i+1's signs into `nxt`, block i+2's V fragments and, after its
-  // tiles, block i+1's U fragments.  Scheduling barriers pin the issue order.
+  // One block step.  On entry block i's signs are in `cur` (fetched at the start of
+  // step i-1), its U fragments in uf and block i+1's V fragments in vv (both fetched
+  // at the end of step i-1).  The step fetches block i+1's signs into `nxt`, runs
+  // block i's tiles, builds Z_{i+1} from vv, then fetches block i+2's V fragments and
+  // block i+1's U fragments.  Every load so gets a whole step of lead time, and
+  // scheduling barriers pin the issue order that the in-order wait counts rely on.
   auto step = [&](int i, u32x4 (&cur)[R], u32x4 (&nxt)[R], auto prefetch) {
     const int buf = i & 1;
     lds_barrier();  // Z_i and its column sums are complete; buffer buf^1 is free
-    const float init = (csum[buf][0][r16] + csum[buf][1][r16] + csum[buf][2][r16] + csum[buf][3][r16]) * kPlaneAccScale;
-    half8 zb[kPlanes];
+    float init = 0.f;
 #pragma unroll
-    for (int b = 0; b < kPlanes; ++b) zb[b] = as_half8(zs[buf][b][lane]);
-    BlockPtrs bn;
+    for (int w = 0; w < NW; ++w) init += csum[buf][w][r16];
+    init *= kPlaneAccScale;
+    BlockPtrs bn, bv;
     if constexpr (decltype(prefetch)::value) {
-      bn = btab[i + 1];
-      const BlockPtrs bv = btab[min(i + 2, nb - 1)];
-      build_z(buf ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
+      bn = uniform_block(btab[i + 1]);
+      bv = uniform_block(btab[min(i + 2, nb - 1)]);
       load_signs(bn, nxt);
-      load_v(bv);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < R; ++t)
-      if (t >= ntiles) uf[t] = (u32x2){0u, 0u};
-    // Four row tiles at a time: four independent accumulator chains per plane.
+    // Row tiles in groups of four: four independent accumulator chains per plane.  Z
+    // fragments are read from LDS two planes ahead of their use.
 #pragma unroll
     for (int t0 = 0; t0 < R; t0 += 4) {
       float4v acc[4];
@@ -302,27 +324,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         acc[k] = (float4v){init, init, init, init};
         sh[k] = cur[t0 + k] << 6u;
       }
+      u32x4 zf[3];
+      zf[0] = zs[buf][0][lane];
+      zf[1] = zs[buf][1][lane];
+      // (a scheduling barrier per plane keeps the compiler from computing fragments of
+      // later planes early, which would raise register pressure past two waves/SIMD)
 #define BSL_PLANE(B, SRC)                                                                                        \
-  _Pragma("unroll") for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(              \
-      as_half8((SRC) & (0x00010001u << plane_pos(B))), zb[B], acc[k], 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);                                                                             \
+  if ((B) + 2 < kPlanes) zf[((B) + 2) % 3] = zs[buf][(B) + 2][lane];                                          \
+  _Pragma("unroll") for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(               \
+      as_half8((SRC) & (0x00010001u << plane_pos(B))), as_half8(zf[(B) % 3]), acc[k], 0, 0, 0);
       BSL_PLANE(0, sh[k]) BSL_PLANE(1, sh[k]) BSL_PLANE(2, sh[k]) BSL_PLANE(3, sh[k]) BSL_PLANE(4, sh[k]) BSL_PLANE(5, sh[k])
-      BSL_PLANE(6, cur[t0 + k]) BSL_PLANE(7, cur[t0 + k]) BSL_PLANE(8, cur[t0 + k]) BSL_PLANE(9, cur[t0 + k])
-      BSL_PLANE(10, cur[t0 + k]) BSL_PLANE(11, cur[t0 + k])
 #pragma unroll
       for (int k = 0; k < 4; ++k) sh[k] = cur[t0 + k] >> 6u;
+      BSL_PLANE(6, cur[t0 + k]) BSL_PLANE(7, cur[t0 + k]) BSL_PLANE(8, cur[t0 + k]) BSL_PLANE(9, cur[t0 + k])
+      BSL_PLANE(10, cur[t0 + k]) BSL_PLANE(11, cur[t0 + k])
       BSL_PLANE(12, sh[k]) BSL_PLANE(13, sh[k]) BSL_PLANE(14, sh[k]) BSL_PLANE(15, sh[k])
 #undef BSL_PLANE
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const half2v u01 = as_half2(uf[t0 + k][0]), u23 = as_half2(uf[t0 + k][1]);
-        accy[t0 + k][0] += (float)u01[0] * acc[k][0];
-        accy[t0 + k][1] += (float)u01[1] * acc[k][1];
-        accy[t0 + k][2] += (float)u23[0] * acc[k][2];
-        accy[t0 + k][3] += (float)u23[1] * acc[k][3];
+        const int t = t0 + k;
+        const half2v u01 = as_half2(uf[t][0]), u23 = as_half2(uf[t][1]);
+        float4v a = accl[wave][t][lane];
+        a[0] += (float)u01[0] * acc[k][0];
+        a[1] += (float)u01[1] * acc[k][1];
+        a[2] += (float)u23[0] * acc[k][2];
+        a[3] += (float)u23[1] * acc[k][3];
+        accl[wave][t][lane] = a;
       }
     }
     if constexpr (decltype(prefetch)::value) {
       __builtin_amdgcn_sched_barrier(0);
+      build_z(buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(bv);
       load_u(bn);
     }
   };
@@ -346,8 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rsel = reduced_row(lane);
 #pragma unroll
   for (int t = 0; t < R; ++t) {
-    const float v = reduce_columns(accy[t], lane);
-    if ((lane & 3) == 0 && t < ntiles)
+    const float v = reduce_columns(accl[wave][t][lane], lane);
+    if ((lane & 3) == 0)
       __hip_atomic_store(&W.partial[(size_t)ch * rows_pad + (rt0 + t) * kTileRows + rsel], v, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -357,9 +392,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     last_flag = __hip_atomic_fetch_add(&W.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.nch - 1);
   __syncthreads();
   if (!last_flag) return;
-  const int row_begin = rg * 4 * R * kTileRows;
-  const int row_end = min(W.m, row_begin + 4 * R * kTileRows);
-  for (int row = row_begin + threadIdx.x; row < row_end; row += 256) {
+  const int row_begin = rg * kDecodeGroupTiles * kTileRows;
+  const int row_end = min(W.m, row_begin + kDecodeGroupTiles * kTileRows);
+  for (int row = row_begin + threadIdx.x; row < row_end; row += NW * 64) {
     float s = 0.f;
     for (int c = 0; c < W.nch; ++c)
       s += __hip_atomic_load(&W.partial[(size_t)c * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -413,7 +448,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         raw[a] = (u32x4){0u, 0u, 0u, 0u};
-        if (rt0 + a < W.mt) raw[a] = load16(bp.signs + ((size_t)(rt0 + a) * W.nch + ch) * kTileBytes + lane * 16);
+        raw[a] = load16(bp.signs + ((size_t)ch * W.mt + rt0 + a) * kTileBytes + lane * 16);
       }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -522,11 +557,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
 
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write +-1.
-__global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t m, int32_t d, int32_t nch, int path,
+__global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int path,
                                                           int8_t* out) {
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
-  const int rt = tile / nch, ch = tile % nch;
+  const int ch = tile / mt, rt = tile % mt;
   const u32x4 w = load16(blk.signs + (size_t)tile * kTileBytes + lane * 16);
   const u32x4 lo = w << 6u, hi = w >> 6u;
   const int row = rt * kTileRows + (lane & 15);
@@ -570,10 +605,10 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
 }
 
 // ============================================================ launchers
-int launch_decode_m1(const GroupArgs& args, int rows_per_item, void* stream) {
-  if (rows_per_item != kDecodeRowTiles) return (int)hipErrorInvalidValue;
+int launch_decode_m1(const GroupArgs& args, void* stream) {
   if (args.total_items == 0) return 0;
-  hipLaunchKernelGGL(decode_m1_kernel<kDecodeRowTiles>, dim3(args.total_items), dim3(256), 0, static_cast<hipStream_t>(stream),
+  // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU)
+  hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(args.total_items), dim3(512), 0, static_cast<hipStream_t>(stream),
                      args);
   return (int)hipGetLastError();
 }
@@ -592,7 +627,7 @@ int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* s
 
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream) {
-  hipLaunchKernelGGL(debug_unpack_kernel, dim3(mt * nch), dim3(64), 0, static_cast<hipStream_t>(stream), blk, m, d, nch,
+  hipLaunchKernelGGL(debug_unpack_kernel, dim3(mt * nch), dim3(64), 0, static_cast<hipStream_t>(stream), blk, m, d, mt,
                      path, out);
   return (int)hipGetLastError();
 }

@@ -33,7 +33,7 @@
  *     bsl_set_source / bsl_destroy of that weight) and never retained otherwise.
  *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
  *   - Supported shapes: k == 16, 1 <= m <= 2^20, 8 <= d <= 2^20 with d % 8 == 0.
- *     Internally rows are padded to a multiple of 16 and columns to a multiple of
+ *     Internally rows are padded to a multiple of 512 and columns to a multiple of
  *     512 (padding signs are +1 and padding factor entries are 0, so padding never
  *     changes a result).
  *   - A stack is not thread-safe: calls on one stack must not run concurrently.
@@ -74,12 +74,12 @@ typedef struct bsl_block_src {
 /* Payload bytes of one block: m*d/8 + 2*k*(m + d).  Returns 0 for invalid sizes. */
 size_t bsl_block_bytes(int64_t m, int64_t d, int32_t k);
 
-/* Bytes of the tiled sign layout of one m x d block (rows padded to 16, columns to 512). */
+/* Bytes of the tiled sign layout of one m x d block (rows and columns padded to 512). */
 size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
 
 /* Host-side "bitstack_pack": convert row-major sign bits (format of bsl_block_src)
  * into the tiled device layout.  tiled_out (host) must hold bsl_packed_sign_bytes(m, d)
- * bytes.  Layout: tiles of 16 rows x 512 columns, ordered [row tile][column chunk];
+ * bytes.  Layout: tiles of 16 rows x 512 columns, ordered [column chunk][row tile];
  * each tile is 64 lanes x 16 bytes; lane L = 16*g + i holds row i of the tile and four
  * little-endian 32-bit words q = 0..3, where bit p of word q is the sign of column
  * 32*(p % 16) + 8*g + 2*q + (p / 16) of the chunk.  One 16-byte load per lane fetches

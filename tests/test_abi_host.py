@@ -53,16 +53,17 @@ def test_block_bytes_printed_value():
 
 
 def _expected_tiled(bits, m, d):
-    """The documented layout, written out independently of the library: bit p of word
-    q of lane 16 g + i in tile (t, c) is the sign of row 16 t + i, column
-    512 c + 32 (p % 16) + 8 g + 2 q + p // 16 (padding reads as +1, i.e. bit 0)."""
+    """The documented layout, written out independently of the library: tiles ordered
+    [column chunk c][row tile t], rows padded to 512; bit p of word q of lane 16 g + i
+    in tile (c, t) is the sign of row 16 t + i, column 512 c + 32 (p % 16) + 8 g + 2 q
+    + p // 16 (padding reads as +1, i.e. bit 0)."""
     signs_neg = np.unpackbits(bits, axis=1, bitorder="little")[:, :d].astype(np.uint8)
-    mp = -(-m // 16) * 16
+    mp = -(-m // 512) * 512  # rows padded to 512
     dp = -(-d // 512) * 512
     full = np.zeros((mp, dp), np.uint8)
     full[:m, :d] = signs_neg
     nch = dp // 512
-    out = np.zeros((mp // 16, nch, 64, 4), np.uint32)
+    out = np.zeros((nch, mp // 16, 64, 4), np.uint32)  # [chunk][row tile][lane][word]
     p = np.arange(32)
     for g in range(4):
         for q in range(4):
@@ -71,7 +72,7 @@ def _expected_tiled(bits, m, d):
                 blk = full[:, 512 * c + cols].reshape(mp // 16, 16, 32).astype(np.uint64)
                 words = (blk << p.astype(np.uint64)).sum(axis=2).astype(np.uint32)
                 for i in range(16):
-                    out[:, c, 16 * g + i, q] = words[:, i]
+                    out[c, :, 16 * g + i, q] = words[:, i]
     return out.view(np.uint8).reshape(-1)
 
 

@@ -14,7 +14,8 @@ S Z contraction, 2 n k M m d per weight), the decode kernel's roofline from per-
 HIP events, and the CPU oracle (fp64 reconstruct-then-matmul) on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
-                       [--prefill-steps P] [--no-cpu] [--sweep] [--llama70b]
+                       [--prefill-steps P] [--no-cpu] [--no-prefill] [--sweep] [--llama70b]
+                       [--per-weight] [--calibrate-copy] [--cpu-layers C]
 """
 from __future__ import annotations
 
@@ -120,10 +121,10 @@ def time_steps(torch, layers: Layers, steps: int, warmup: int):
     return wall, kern_ms, total_bytes, total_flops
 
 
-def cpu_baseline(seed: int) -> dict:
-    """The oracle, untouched, on a bounded sample of the decode workload: one
-    8B-shaped layer (all seven linears) with n = 8 and M = 1 (one step of the GPU
-    benchmark; about 10-20 s of CPU work)."""
+def cpu_baseline(seed: int, layers: int = 4) -> dict:
+    """The oracle, untouched, on a bounded sample of the decode workload: `layers`
+    distinct 8B-shaped layers (all seven linears each) with n = 8 and M = 1, i.e.
+    `layers` steps of the GPU benchmark (about 10-30 s of CPU work)."""
     import oracle
 
     try:
@@ -132,24 +133,61 @@ def cpu_baseline(seed: int) -> dict:
         cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    sample = list(synth.LLAMA3_8B_LAYER)
     total_bytes = 0
     elapsed = 0.0
-    for j, (_, m, d) in enumerate(sample):
-        blocks = synth.synthetic_blocks(seed, m, d, 8, 16, 99, j)
-        x = synth.activations(seed + 1, 1, d, 99, j)
-        t0 = time.perf_counter()
-        oracle.forward(x, blocks, 8)
-        elapsed += time.perf_counter() - t0
-        total_bytes += 8 * block_bytes(m, d)
+    for l in range(layers):
+        for j, (_, m, d) in enumerate(synth.LLAMA3_8B_LAYER):
+            blocks = synth.synthetic_blocks(seed, m, d, 8, 16, 99, l, j)
+            x = synth.activations(seed + 1, 1, d, 99, l, j)
+            t0 = time.perf_counter()
+            oracle.forward(x, blocks, 8)
+            elapsed += time.perf_counter() - t0
+            total_bytes += 8 * block_bytes(m, d)
     return {
         "value": round(total_bytes / elapsed / 1e9, 4),
         "unit": "GB/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": "one Llama-3-8B-shaped layer (7 linears), n=8, M=1: fp64 reconstruct-then-matmul per linear",
+        "sample": f"{layers} Llama-3-8B-shaped layers (7 linears each), n=8, M=1: fp64 reconstruct-then-matmul per linear",
         "seconds": round(elapsed, 2),
     }
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_m1_kernel_llama3_8b_layer_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "bit_sign_rank_amd", "csrc", "bsl_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, copy-calibrated), or None when the kernel source has changed since
+    the counters were taken (the summary records the source's SHA-256)."""
+    import hashlib
+
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest or "hbm_bytes_per_launch" not in fields:
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def copy_calibration(torch, mib: int = 1024, reps: int = 3) -> None:
+    """A plain elementwise copy (y = -x, fp16) of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: each dispatch reads and writes exactly `mib` MiB."""
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.float16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {mib} MiB")
 
 
 def main() -> None:
@@ -163,6 +201,9 @@ def main() -> None:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
     ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
+    ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
+    ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -193,7 +234,7 @@ def main() -> None:
     achieved = per_launch_bytes / (kavg * 1e-3) / 1e9
     log(f"decode: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s wall, kernel avg {kavg * 1e3:.1f} us -> {achieved:.0f} GB/s")
     per_weight = []
-    for j, (name, m, d) in enumerate(shapes):
+    for j, (name, m, d) in enumerate(shapes if args.per_weight else []):
         # single-weight launches, for the per-shape picture
         h = dec.h
         x, y = dec.x[0][j], dec.y[0][j]
@@ -244,12 +285,13 @@ def main() -> None:
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(),
                 "avg_launch_us": round(kavg * 1e3, 2),
             },
-            "decode_single_weight_launches": per_weight,
         }
     )
+    if per_weight:
+        result["decode_single_weight_launches"] = per_weight
 
     # ---------------- prefill M = 2048
     if not args.no_prefill:
@@ -297,7 +339,9 @@ def main() -> None:
     # ---------------- CPU oracle
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(args.seed + 5)
+        result["cpu_baseline"] = cpu_baseline(args.seed + 5, args.cpu_layers)
+    if args.calibrate_copy:
+        copy_calibration(torch)
 
     print(json.dumps(result), flush=True)
 

@@ -121,14 +121,18 @@ struct Weight {
   std::vector<Slot> slots;          // [n_cap]
   BlockPtrs* dtable = nullptr;      // device [n_cap]
   float* partial = nullptr;         // workspace
-  uint32_t* counters = nullptr;
+  uint32_t* counters = nullptr;     // workspace: arrival counters of the multi-token path
   size_t partial_floats = 0, counter_count = 0;
 };
 
 struct bsl_stack {
   int device = 0;
   int32_t k = 16, n_cap = 0;
+  int32_t decode_grid_max = 512;  // largest power of two <= 2 x compute units
   uint64_t budget = 0, resident = 0;
+  void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
+  float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
+  uint32_t* arrivals = nullptr;   // single-token arrival counters, one per row group of a launch
   std::vector<Weight> w;
 };
 
@@ -235,6 +239,16 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
   s->budget = budget_bytes;
   s->w.resize(num_weights);
   int rc = BSL_OK;
+  size_t max_groups = 0;
+  int cus = 0;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device)) != hipSuccess)
+    rc = hip_fail(e, "hipDeviceGetAttribute(multiprocessors)");
+  else {
+    s->decode_grid_max = 1;
+    while (s->decode_grid_max * 2 <= std::max(1, 2 * cus)) s->decode_grid_max *= 2;
+    if ((e = hipMalloc(&s->zero_page, kZeroPageBytes)) != hipSuccess) rc = hip_fail(e, "hipMalloc(zero page)");
+    else if ((e = hipMemset(s->zero_page, 0, kZeroPageBytes)) != hipSuccess) rc = hip_fail(e, "hipMemset(zero page)");
+  }
   for (int32_t w = 0; w < num_weights && rc == BSL_OK; ++w) {
     Weight& W = s->w[w];
     W.m = m[w];
@@ -243,13 +257,23 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     W.nch = (int32_t)(pad_cols(W.d) / kChunkCols);
     W.slots.resize(n_cap);
     const size_t mpad = (size_t)pad_rows(W.m);
-    W.partial_floats = std::max((size_t)W.nch * mpad, (size_t)kGemmMaxSplits * kGemmMaxSplitM * mpad);
-    W.counter_count = (size_t)decode_groups(W) + (size_t)((W.mt + kGemmRowTiles - 1) / kGemmRowTiles) * kGemmMaxSplitM + 64;
+    W.partial_floats = (size_t)kGemmMaxSplits * kGemmMaxSplitM * mpad;
+    W.counter_count = (size_t)((W.mt + kGemmRowTiles - 1) / kGemmRowTiles) * kGemmMaxSplitM + 64;
+    const size_t words = W.counter_count;
+    max_groups = std::max<size_t>(max_groups, (size_t)decode_groups(W));
     if ((e = hipMalloc(&W.dtable, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(table)");
     else if ((e = hipMalloc(&W.partial, W.partial_floats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(workspace)");
-    else if ((e = hipMalloc(&W.counters, W.counter_count * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(counters)");
-    else if ((e = hipMemset(W.counters, 0, W.counter_count * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
+    else if ((e = hipMalloc(&W.counters, words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(counters)");
+    else if ((e = hipMemset(W.counters, 0, words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
     else if ((e = hipMemset(W.dtable, 0, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMemset(table)");
+  }
+  if (rc == BSL_OK) {
+    // single-token pieces: at most (row groups of one launch) + (workgroups) of them
+    const size_t n = ((size_t)kMaxGroup * max_groups + (size_t)s->decode_grid_max) * kDecodeGroupRows;
+    const size_t na = (size_t)kMaxGroup * max_groups;
+    if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
+    else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
+    else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
   }
   if (rc == BSL_OK && (e = hipDeviceSynchronize()) != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
   if (rc != BSL_OK) {
@@ -397,6 +421,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   const int nt = M >= 8 ? 8 : 4;  // GEMM token tile
   const int token_groups = (M + nt - 1) / nt;
   int32_t items = 0;
+  uint64_t units = 0, groups = 0;
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -420,7 +445,12 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     if (M == 1) {
       D.groups = decode_groups(W);
       D.splits = W.nch;
-      items += D.groups * W.nch;
+      const uint64_t wu = (uint64_t)D.groups * W.nch * W.n;
+      D.unit_begin = (uint32_t)units;
+      D.units = (uint32_t)wu;
+      D.rg_begin = (uint32_t)groups;
+      units += wu;
+      groups += D.groups;
     } else {
       const int rgroups = (W.mt + kGemmRowTiles - 1) / kGemmRowTiles;
       int splits = 1;
@@ -432,9 +462,24 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   }
   args.total_items = items;
   DeviceGuard guard(s->device);
-  int e;
-  if (M == 1) e = launch_decode_m1(args, stream);
-  else e = launch_gemm(args, nt, token_groups, stream);
+  int e = 0;
+  if (M == 1) {
+    // Persistent grid: the largest power of two that is no more than two workgroups per
+    // CU and no more than the number of units (so no workgroup's share is empty).
+    int32_t grid = s->decode_grid_max, lg = 0;
+    while (grid > 1 && (uint64_t)grid > units) grid /= 2;
+    while ((1 << lg) < grid) ++lg;
+    if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+    args.total_units = (uint32_t)units;
+    args.total_groups = (uint32_t)groups;
+    args.grid_log2 = lg;
+    args.zero_page = s->zero_page;
+    args.pieces = s->pieces;
+    args.arrivals = s->arrivals;
+    e = launch_decode_m1(args, stream);
+  } else {
+    e = launch_gemm(args, nt, token_groups, stream);
+  }
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
 }
@@ -477,6 +522,9 @@ void bsl_destroy(bsl_stack* s) {
     if (W.partial) (void)hipFree(W.partial);
     if (W.counters) (void)hipFree(W.counters);
   }
+  if (s->zero_page) (void)hipFree(s->zero_page);
+  if (s->pieces) (void)hipFree(s->pieces);
+  if (s->arrivals) (void)hipFree(s->arrivals);
   delete s;
 }
 

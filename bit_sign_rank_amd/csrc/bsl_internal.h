@@ -42,20 +42,30 @@ struct WeightDesc {
   void* y;                  // [M][m] fp16 or fp32
   float* partial;           // split-K partial sums (workspace)
   uint32_t* counters;       // arrival counters, one per output group (workspace, zero between calls)
+  uint32_t* pieces;         // single-token path: pieces per (row group, chunk) item (workspace)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks
-  int32_t item_begin;       // first work item of this weight in the launch
+  int32_t item_begin;       // multi-token path: first work item of this weight in the launch
   int32_t groups;           // output groups (row groups x token groups) of this weight
-  int32_t splits;           // K splits (chunks per split = ceil(nch / splits))
+  int32_t splits;           // multi-token path: K splits (chunks per split = ceil(nch / splits))
+  uint32_t unit_begin;      // single-token path: first (row group, block, chunk) unit of this weight
+  uint32_t units;           // single-token path: groups * nblocks * nch
+  uint32_t rg_begin;        // single-token path: first row group of this weight in the launch
 };
 
 struct GroupArgs {
   WeightDesc w[kMaxGroup];
   int32_t count;
-  int32_t total_items;
+  int32_t total_items;   // multi-token path: workgroups
   int32_t M;
   int32_t y_fp32;
+  uint32_t total_units;  // single-token path: (row group, block, chunk) units over all weights
+  uint32_t total_groups; // single-token path: row groups over all weights
+  int32_t grid_log2;     // single-token path: log2 of the (power-of-two) grid
+  const void* zero_page; // kZeroPageBytes of zeros: target of prefetches past the end of the work
+  float* pieces;         // single-token path: [total_groups + grid][512] partial sums (workspace)
+  uint32_t* arrivals;    // single-token path: [total_groups] counters, zero between launches (workspace)
 };
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
@@ -64,8 +74,14 @@ int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* s
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
-// Row tiles per single-token work item (512 rows) and the workspace each weight needs.
+// Single-token path: rows are taken in row groups of 32 tiles (512 rows).  A persistent
+// workgroup walks an equal share of the (row group, block, chunk) units and stores one
+// 512-float "piece" of partial sums per row group it touches; the last workgroup to
+// finish a row group adds its pieces in a fixed order.
 constexpr int kDecodeGroupTiles = 32;
+constexpr int kDecodeGroupRows = kDecodeGroupTiles * 16;
+constexpr int kZeroPageBytes = 65536;
+constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCDs
 constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
 constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
 constexpr int kGemmMaxSplits = 8;

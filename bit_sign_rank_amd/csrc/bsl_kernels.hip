@@ -28,6 +28,7 @@
 //    token tile there).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <type_traits>
 
@@ -59,6 +60,10 @@ __host__ __device__ constexpr uint16_t plane_x_factor_bits(int b) {
 __host__ __device__ constexpr uint16_t plane_inv_factor_bits(int b) {
   return (uint16_t)(0x8000u | (uint16_t)((15 + plane_pos(b) - 8) << 10));
 }
+
+// Order in which the single-token kernel visits the planes: 6-11 straight from the
+// loaded words, 12-15 after rotating them right by 6, 0-5 after rotating by 20 more.
+__host__ __device__ constexpr int plane_order(int s) { return s < 10 ? s + 6 : s - 10; }
 
 // Same factors for a plane index that is only known at run time (wave-uniform).
 __device__ __forceinline__ uint32_t plane_x_factor_bits_dyn(int b) {
@@ -188,219 +193,322 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 }
 
 // ============================================================ single-token kernel
-// One workgroup (NW waves) per work item = (weight, group of NW R = 32 row tiles, one
-// 512-column chunk).  For every loaded block the workgroup builds the chunk's Z tile
-// once, in LDS (double buffered; wave w builds planes PP w .. PP w + PP - 1), and each
-// wave runs its R row tiles against it, reading the fragments just ahead of use.  Block i's
-// sign tiles and block i+1's V fragments are fetched one block ahead, U fragments
-// right after the previous block's tiles, so the HBM stream never waits on compute.
-// After the last block each wave reduces its U-weighted accumulators over r, stores
-// the chunk's partial sums (write-through, coherent across XCDs), and the last
-// workgroup of a row group to arrive adds the chunks in a fixed order and writes y.
+// Persistent workgroups of NW waves.  The work is a list of units (weight, row group of
+// NW R = 32 row tiles, block, 512-column chunk) in that order; with U units and G
+// workgroups, workgroup L walks units [L U / G, (L + 1) U / G).
+//
+// For every unit the workgroup builds the chunk's Z tile once, in LDS (double buffered;
+// wave w builds planes PP w .. PP w + PP - 1) and each wave runs its R row tiles against
+// it, accumulating the raw products over the chunks of a block in registers.  After a
+// block's last chunk (or the end of the range) the products get the block's column-sum
+// term and are weighted by U (the r-sum is linear, so a block split over two workgroups
+// is fine); after a row group's last unit (or the end of the range) each wave sums its
+// tiles over r and stores the workgroup's 512-row "piece" of the row group.  A second
+// kernel adds the pieces of each row group in workgroup order and writes y.
+//
+// Sign tiles are fetched one unit ahead, V fragments and activations two units ahead and
+// U fragments one unit ahead, across block, row-group and weight boundaries, so the HBM
+// stream never waits on compute; fetches past the end of the range read a page of zeros.
+// The main kernel has no atomics, fences or waits on outstanding loads.
+struct DecodeCursor {
+  int32_t j, rg, i, ch;  // weight slot in the launch, row group, block, chunk
+  uint32_t u;            // unit index
+  bool valid;            // false past the end of the workgroup's range
+};
+
+// Units [start(o), start(o + 1)) belong to workgroup o.
+__device__ __forceinline__ uint32_t range_start(uint32_t o, uint32_t units, int lg) {
+  return (uint32_t)(((uint64_t)o * units) >> lg);
+}
+
 template <int NW, int R, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_m1_kernel(GroupArgs args) {
-  static_assert(NW * R == kDecodeGroupTiles && kPlanes % NW == 0 && R % 4 == 0, "decode tiling");
+  static_assert(NW * R == kDecodeGroupTiles && kPlanes % NW == 0 && R == 4, "decode tiling");
   constexpr int PP = kPlanes / NW;       // Z planes each wave builds
-  __shared__ u32x4 zs[2][kPlanes][64];   // Z fragments of two blocks (32 KiB)
-  __shared__ u32x4 xsh[kPlanes][4];      // plane-scaled activations, [plane][lane group]
-  __shared__ float csum[2][NW][16];      // per-wave partial column sums of Z
+  __shared__ u32x4 zs[2][kPlanes][64];   // Z fragments of two units (32 KiB)
+  __shared__ float csum[2][NW][16];      // per-wave column sums of Z over a block's chunks
   __shared__ float4v accl[NW][R][64];    // U-weighted accumulators (LDS, not registers)
-  __shared__ BlockPtrs btab[kMaxBlocks]; // the weight's block table
-  __shared__ uint32_t last_flag;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4;
   const int r16 = lane & 15;
-  const WeightDesc W = find_weight(args, blockIdx.x);
-  const int local = blockIdx.x - W.item_begin;
-  const int rg = local / W.nch;
-  const int ch = local - rg * W.nch;
-  const int rows_pad = W.mt * kTileRows;
-  const int rt0 = rg * kDecodeGroupTiles + wave * R;  // rows are padded to whole row groups
-  const int nb = W.nblocks;
+  const uint32_t U = args.total_units;
+  const int lg = args.grid_log2;
+  const uint32_t G = 1u << lg;
+  // Workgroups are dealt round-robin over the XCDs; give each XCD a contiguous share of
+  // the units, so the workgroups sharing an L2 also share V and U fragments.
+  const uint32_t bid = blockIdx.x;
+  const uint32_t L = G >= (uint32_t)kXcds ? (bid % kXcds) * (G / kXcds) + bid / kXcds : bid;
+  const uint32_t u_begin = range_start(L, U, lg), u_end = range_start(L + 1, U, lg);
+  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
 
-  // The U-weighted products of every block are accumulated in LDS (each lane owns its
-  // 16 bytes per tile): the accumulators live across the whole block loop but are
-  // touched once per block, so keeping them in registers would cost occupancy.
-#pragma unroll
-  for (int t = 0; t < R; ++t) accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
-  // Every load is issued unconditionally (padding rows are stored, with +1 signs and
-  // zero U) so the number of loads in flight is the same on every path and the
-  // compiler's in-order wait counts never drain the prefetches.  A wave's R sign
-  // tiles of one block and chunk are contiguous, as are its R U fragments.
+  // ---- cursor over the unit list (wave-uniform state)
+  auto locate = [&](uint32_t u) {
+    DecodeCursor c;
+    int j = 0;
+    while (j + 1 < args.count && u >= args.w[j + 1].unit_begin) ++j;
+    const WeightDesc& W = args.w[j];
+    const uint32_t local = u - W.unit_begin;
+    const uint32_t per_rg = (uint32_t)W.nch * W.nblocks;
+    c.j = j;
+    c.rg = local / per_rg;
+    const uint32_t rem = local - c.rg * per_rg;
+    c.i = rem / W.nch;
+    c.ch = rem - c.i * W.nch;
+    c.u = u;
+    c.valid = true;
+    return c;
+  };
+  auto next = [&](DecodeCursor c) {
+    if (!c.valid || c.u + 1 >= u_end) {
+      c.valid = false;
+      return c;
+    }
+    ++c.u;
+    const WeightDesc& W = args.w[c.j];
+    if (++c.ch == W.nch) {
+      c.ch = 0;
+      if (++c.i == W.nblocks) {
+        c.i = 0;
+        if (++c.rg == W.groups) {
+          c.rg = 0;
+          do ++c.j;
+          while (args.w[c.j].units == 0);
+        }
+      }
+    }
+    return c;
+  };
+  // the unit closes this workgroup's share of a block / of a row group
+  auto block_end = [&](const DecodeCursor& c) { return c.ch == args.w[c.j].nch - 1 || c.u + 1 == u_end; };
+  auto group_end = [&](const DecodeCursor& c) {
+    const WeightDesc& W = args.w[c.j];
+    return (c.ch == W.nch - 1 && c.i == W.nblocks - 1) || c.u + 1 == u_end;
+  };
+  // Per-wave base addresses of a unit's loads (the zero page for an invalid cursor).
+  struct UnitPtrs {
+    const uint8_t* signs;
+    const uint16_t* u;
+    const uint16_t* v;
+    const uint16_t* x;
+    int32_t xcols;  // valid activation columns from x (the rest read zeros)
+  };
+  auto unit_ptrs = [&](const DecodeCursor& c) {
+    UnitPtrs p;
+    if (c.valid) {
+      const WeightDesc& W = args.w[c.j];
+      const BlockPtrs b = load_block(W.blocks, c.i);
+      const int rt0 = c.rg * kDecodeGroupTiles + wave * R;
+      p.signs = b.signs + ((size_t)c.ch * W.mt + rt0) * kTileBytes;
+      p.u = b.u + (size_t)rt0 * 64 * 4;
+      p.v = b.v + ((size_t)c.ch * kPlanes + PP * wave) * 64 * 8;
+      p.x = W.x + (size_t)c.ch * kChunkCols;
+      p.xcols = W.d - c.ch * kChunkCols;
+    } else {
+      p.signs = zero_page;
+      p.u = reinterpret_cast<const uint16_t*>(zero_page);
+      p.v = reinterpret_cast<const uint16_t*>(zero_page);
+      p.x = reinterpret_cast<const uint16_t*>(zero_page);
+      p.xcols = 0;
+    }
+    return p;
+  };
+
+  // ---- loads.  Every load is issued unconditionally (padding rows are stored with +1
+  // signs and zero U, and out-of-range addresses are redirected to the zero page), so
+  // the number of loads in flight is the same on every path and the compiler's in-order
+  // wait counts never drain the prefetches.
   u32x4 raw[R], rawn[R];
   u32x2 uf[R];
-  u32x4 vv[PP];
-
-  auto load_signs = [&](const BlockPtrs& bp, u32x4* rw) {
-    const uint8_t* base = bp.signs + ((size_t)ch * W.mt + rt0) * kTileBytes + lane * 16;
+  u32x4 vv[PP], xv[PP];
+  auto load_signs = [&](const UnitPtrs& p, u32x4* rw) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) rw[t] = load16(base + t * kTileBytes);
+    for (int t = 0; t < R; ++t) rw[t] = load16(p.signs + t * kTileBytes + lane * 16);
   };
-  auto load_u = [&](const BlockPtrs& bp) {
-    const uint16_t* base = bp.u + ((size_t)rt0 * 64 + lane) * 4;
+  auto load_u = [&](const UnitPtrs& p) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) uf[t] = load8(base + t * 256);
+    for (int t = 0; t < R; ++t) uf[t] = load8(p.u + (t * 64 + lane) * 4);
   };
-  auto load_v = [&](const BlockPtrs& bp) {
+  auto load_vx = [&](const UnitPtrs& p) {
 #pragma unroll
-    for (int p = 0; p < PP; ++p) vv[p] = load16(bp.v + (((size_t)ch * kPlanes + PP * wave + p) * 64 + lane) * 8);
+    for (int q = 0; q < PP; ++q) {
+      vv[q] = load16(p.v + (q * 64 + lane) * 8);
+      const int col = 32 * (PP * wave + q) + 8 * g;
+      xv[q] = load16(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
+    }
   };
-  // Z fragments of this wave's PP planes from vv, and their column sums over the chunk.
-  auto build_z = [&](int buf) {
+  // Z fragments of this wave's PP planes (V times the plane-scaled activations).  Their
+  // column sums over the chunk are added up over the block's chunks; the total goes to
+  // LDS with the block's last chunk (parity `wpar` alternates per block).
+  float cs_run = 0.f;
+  int wpar = 0, rpar = 0;
+  auto build_z = [&](int buf, const DecodeCursor& c) {
     float cs = 0.f;
 #pragma unroll
-    for (int p = 0; p < PP; ++p) {
-      const int b = PP * wave + p;
-      const u32x4 xw = xsh[b][g];
+    for (int q = 0; q < PP; ++q) {
+      const int b = PP * wave + q;
+      const half2v f = as_half2(plane_x_factor_bits_dyn(b) * 0x00010001u);
       const half2v inv = as_half2(plane_inv_factor_bits_dyn(b) * 0x00010001u);
       u32x4 z;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const half2v zq = as_half2(vv[p][q]) * as_half2(xw[q]);
-        z[q] = as_u32(zq);
+      for (int k = 0; k < 4; ++k) {
+        const half2v zq = as_half2(vv[q][k]) * (as_half2(xv[q][k]) * f);
+        z[k] = as_u32(zq);
         cs = __builtin_amdgcn_fdot2(zq, inv, cs, false);
       }
       zs[buf][b][lane] = z;
     }
-    cs = sum_over_lane_groups(cs);
-    if (lane < 16) csum[buf][wave][lane] = cs;
-  };
-
-  if (nb > 0) {
-    if (threadIdx.x < nb) btab[threadIdx.x] = load_block(W.blocks, threadIdx.x);
-    const BlockPtrs b0 = load_block(W.blocks, 0);
-    load_signs(b0, raw);
-    load_v(b0);
-    // plane-scaled activations of this wave's planes (lanes with r = 0 keep them in LDS)
-#pragma unroll
-    for (int p = 0; p < PP; ++p) {
-      const int b = PP * wave + p;
-      const int col = ch * kChunkCols + 32 * b + 8 * g;
-      u32x4 xv = {0u, 0u, 0u, 0u};
-      if (col < W.d) xv = load16(W.x + col);
-      const uint32_t f = plane_x_factor_bits_dyn(b) * 0x00010001u;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[q] = as_u32(as_half2(xv[q]) * as_half2(f));
-      if (r16 == 0) xsh[b][g] = xv;
-    }
-    // Other lanes read these entries: without a barrier that is a data race, and the
-    // compiler may (and does) move their reads before the writing lane's store.
-    lds_barrier();
-    build_z(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v(load_block(W.blocks, min(1, nb - 1)));
-    load_u(b0);
-  }
-
-  // One block step.  On entry block i's signs are in `cur` (fetched at the start of
-  // step i-1), its U fragments in uf and block i+1's V fragments in vv (both fetched
-  // at the end of step i-1).  The step fetches block i+1's signs into `nxt`, runs
-  // block i's tiles, builds Z_{i+1} from vv, then fetches block i+2's V fragments and
-  // block i+1's U fragments.  Every load so gets a whole step of lead time, and
-  // scheduling barriers pin the issue order that the in-order wait counts rely on.
-  auto step = [&](int i, u32x4 (&cur)[R], u32x4 (&nxt)[R], auto prefetch) {
-    const int buf = i & 1;
-    lds_barrier();  // Z_i and its column sums are complete; buffer buf^1 is free
-    float init = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) init += csum[buf][w][r16];
-    init *= kPlaneAccScale;
-    BlockPtrs bn, bv;
-    if constexpr (decltype(prefetch)::value) {
-      bn = uniform_block(btab[i + 1]);
-      bv = uniform_block(btab[min(i + 2, nb - 1)]);
-      load_signs(bn, nxt);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Row tiles in groups of four: four independent accumulator chains per plane.  Z
-    // fragments are read from LDS two planes ahead of their use.
-#pragma unroll
-    for (int t0 = 0; t0 < R; t0 += 4) {
-      float4v acc[4];
-      u32x4 sh[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[k] = (float4v){init, init, init, init};
-        sh[k] = cur[t0 + k] << 6u;
-      }
-      u32x4 zf[3];
-      zf[0] = zs[buf][0][lane];
-      zf[1] = zs[buf][1][lane];
-      // (a scheduling barrier per plane keeps the compiler from computing fragments of
-      // later planes early, which would raise register pressure past two waves/SIMD)
-#define BSL_PLANE(B, SRC)                                                                                        \
-  __builtin_amdgcn_sched_barrier(0);                                                                             \
-  if ((B) + 2 < kPlanes) zf[((B) + 2) % 3] = zs[buf][(B) + 2][lane];                                          \
-  _Pragma("unroll") for (int k = 0; k < 4; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(               \
-      as_half8((SRC) & (0x00010001u << plane_pos(B))), as_half8(zf[(B) % 3]), acc[k], 0, 0, 0);
-      BSL_PLANE(0, sh[k]) BSL_PLANE(1, sh[k]) BSL_PLANE(2, sh[k]) BSL_PLANE(3, sh[k]) BSL_PLANE(4, sh[k]) BSL_PLANE(5, sh[k])
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sh[k] = cur[t0 + k] >> 6u;
-      BSL_PLANE(6, cur[t0 + k]) BSL_PLANE(7, cur[t0 + k]) BSL_PLANE(8, cur[t0 + k]) BSL_PLANE(9, cur[t0 + k])
-      BSL_PLANE(10, cur[t0 + k]) BSL_PLANE(11, cur[t0 + k])
-      BSL_PLANE(12, sh[k]) BSL_PLANE(13, sh[k]) BSL_PLANE(14, sh[k]) BSL_PLANE(15, sh[k])
-#undef BSL_PLANE
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int t = t0 + k;
-        const half2v u01 = as_half2(uf[t][0]), u23 = as_half2(uf[t][1]);
-        float4v a = accl[wave][t][lane];
-        a[0] += (float)u01[0] * acc[k][0];
-        a[1] += (float)u01[1] * acc[k][1];
-        a[2] += (float)u23[0] * acc[k][2];
-        a[3] += (float)u23[1] * acc[k][3];
-        accl[wave][t][lane] = a;
-      }
-    }
-    if constexpr (decltype(prefetch)::value) {
-      __builtin_amdgcn_sched_barrier(0);
-      build_z(buf ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(bv);
-      load_u(bn);
+    cs_run += sum_over_lane_groups(cs);
+    if (c.valid && block_end(c)) {
+      if (lane < 16) csum[wpar][wave][lane] = cs_run;
+      cs_run = 0.f;
+      wpar ^= 1;
     }
   };
 
-  using yes = std::integral_constant<bool, true>;
-  using no = std::integral_constant<bool, false>;
-  int i = 0;
-  for (; i + 2 < nb; i += 2) {
-    step(i, raw, rawn, yes{});
-    step(i + 1, rawn, raw, yes{});
-  }
-  if (i + 1 < nb) {
-    step(i, raw, rawn, yes{});
-    step(i + 1, rawn, raw, no{});
-  } else if (i < nb) {
-    step(i, raw, rawn, no{});
-  }
-
-  // This chunk's partial sums, stored write-through at device scope so the last
-  // workgroup (possibly on another XCD) reads them without any cache flush.
-  const int rsel = reduced_row(lane);
+  float4v acc[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) {
-    const float v = reduce_columns(accl[wave][t][lane], lane);
-    if ((lane & 3) == 0)
-      __hip_atomic_store(&W.partial[(size_t)ch * rows_pad + (rt0 + t) * kTileRows + rsel], v, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+    accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the stores above have completed before the arrival below
-  __syncthreads();
-  if (threadIdx.x == 0)
-    last_flag = __hip_atomic_fetch_add(&W.counters[rg], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.nch - 1);
-  __syncthreads();
-  if (!last_flag) return;
-  const int row_begin = rg * kDecodeGroupTiles * kTileRows;
-  const int row_end = min(W.m, row_begin + kDecodeGroupTiles * kTileRows);
-  for (int row = row_begin + threadIdx.x; row < row_end; row += NW * 64) {
-    float s = 0.f;
-    for (int c = 0; c < W.nch; ++c)
-      s += __hip_atomic_load(&W.partial[(size_t)c * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_y(W.y, row, s * kPlaneOutScale, args.y_fp32);
+  // After a block: U-weight the products (plus the block's column-sum term) into LDS.
+  auto weight_block = [&]() {
+    float cs_tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cs_tot += csum[rpar][w][r16];
+    cs_tot *= kPlaneAccScale;
+    rpar ^= 1;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const half2v u01 = as_half2(uf[k][0]), u23 = as_half2(uf[k][1]);
+      float4v a = accl[wave][k][lane];
+      a[0] += (float)u01[0] * (acc[k][0] + cs_tot);
+      a[1] += (float)u01[1] * (acc[k][1] + cs_tot);
+      a[2] += (float)u23[0] * (acc[k][2] + cs_tot);
+      a[3] += (float)u23[1] * (acc[k][3] + cs_tot);
+      accl[wave][k][lane] = a;
+      acc[k] = (float4v){0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // After a row group: this workgroup's piece of it, summed over r (plain stores; the
+  // pieces are read by the next kernel on the stream).
+  const int rsel = reduced_row(lane);
+  auto store_piece = [&](const DecodeCursor& c) {
+    const uint32_t item = args.w[c.j].rg_begin + c.rg;
+    float* piece = args.pieces + (size_t)(item + L) * kDecodeGroupRows;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      const float v = reduce_columns(accl[wave][t][lane], lane);
+      accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
+      if ((lane & 3) == 0) piece[(wave * R + t) * kTileRows + rsel] = v;
+    }
+  };
+
+  // ---- prologue: the first unit's signs, Z tile and U fragments, the second unit's V
+  // fragments and activations
+  DecodeCursor c0 = locate(u_begin);
+  DecodeCursor c1 = next(c0);
+  DecodeCursor c2 = next(c1);
+  const UnitPtrs p0 = unit_ptrs(c0);
+  UnitPtrs p1 = unit_ptrs(c1);
+  UnitPtrs p2 = unit_ptrs(c2);
+  load_signs(p0, raw);
+  load_vx(p0);
+  build_z(0, c0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_vx(p1);
+  load_u(p0);
+
+  // ---- one unit.  On entry unit c0's signs are in `cur`, its Z tile in zs[buf], its U
+  // fragments in uf, and unit c1's V fragments and activations in vv / xv.
+  auto step = [&](u32x4 (&cur)[R], u32x4 (&nxt)[R], const int buf) {
+    lds_barrier();  // Z of c0 (and the column sums of a finished block) are complete
+    load_signs(p1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // Row tiles: four independent accumulator chains per plane.  Planes 6-11 are read
+      // from the words as loaded; the words are then rotated right by 6 in place (planes
+      // 12-15 land on bits 6-9) and by 20 more (planes 0-5 land on bits 6-11), so no
+      // second copy of the words is kept.  Z fragments are read from LDS two planes ahead.
+      u32x4 zf[3];
+      zf[0] = zs[buf][plane_order(0)][lane];
+      zf[1] = zs[buf][plane_order(1)][lane];
+      // (a scheduling barrier per plane keeps the compiler from computing fragments of
+      // later planes early, which would raise register pressure past two waves/SIMD)
+#define BSL_PLANE(S)                                                                                              \
+  __builtin_amdgcn_sched_barrier(0);                                                                              \
+  if ((S) + 2 < kPlanes) zf[((S) + 2) % 3] = zs[buf][plane_order((S) + 2)][lane];                              \
+  _Pragma("unroll") for (int k = 0; k < R; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(                \
+      as_half8(cur[k] & (0x00010001u << plane_pos(plane_order(S)))), as_half8(zf[(S) % 3]), acc[k], 0, 0, 0);
+#define BSL_ROTATE(N)                                                                                             \
+  _Pragma("unroll") for (int k = 0; k < R; ++k) _Pragma("unroll") for (int q = 0; q < 4; ++q) cur[k][q] =      \
+      __builtin_amdgcn_alignbit(cur[k][q], cur[k][q], (N));
+      BSL_PLANE(0) BSL_PLANE(1) BSL_PLANE(2) BSL_PLANE(3) BSL_PLANE(4) BSL_PLANE(5)
+      BSL_ROTATE(6)
+      BSL_PLANE(6) BSL_PLANE(7) BSL_PLANE(8) BSL_PLANE(9)
+      BSL_ROTATE(20)
+      BSL_PLANE(10) BSL_PLANE(11) BSL_PLANE(12) BSL_PLANE(13) BSL_PLANE(14) BSL_PLANE(15)
+#undef BSL_ROTATE
+#undef BSL_PLANE
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (block_end(c0)) weight_block();
+    __builtin_amdgcn_sched_barrier(0);
+    build_z(buf ^ 1, c1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (group_end(c0)) store_piece(c0);
+    load_vx(p2);
+    load_u(p1);
+    c0 = c1;
+    c1 = c2;
+    p1 = p2;
+    c2 = next(c2);
+    p2 = unit_ptrs(c2);
+  };
+
+  const uint32_t n = u_end - u_begin;
+  for (uint32_t s = 0; s < n; s += 2) {
+    step(raw, rawn, 0);
+    if (s + 1 < n) step(rawn, raw, 1);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum the pieces of each row group (one workgroup of 512 threads per row group, one row
+// per thread) in workgroup order and write y.  A row group of a weight without blocks
+// has no pieces: y = 0, the empty sum.
+__global__ __launch_bounds__(kDecodeGroupRows) void decode_combine_kernel(GroupArgs args) {
+  const uint32_t item = blockIdx.x;
+  int j = 0;
+  while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
+  const WeightDesc& W = args.w[j];
+  const int rg = (int)(item - W.rg_begin);
+  const int row = rg * kDecodeGroupRows + threadIdx.x;
+  const uint32_t U = args.total_units;
+  const int lg = args.grid_log2;
+  const uint32_t G = 1u << lg;
+  float acc = 0.f;
+  if (W.units > 0) {
+    const uint32_t per_rg = (uint32_t)W.nblocks * W.nch;
+    const uint32_t first = W.unit_begin + (uint32_t)rg * per_rg, last = first + per_rg - 1;
+    // workgroups holding units of this row group: owner(first) .. owner(last)
+    auto owner = [&](uint32_t u) {
+      uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+      while (o + 1 < G && range_start(o + 1, U, lg) <= u) ++o;
+      while (range_start(o, U, lg) > u) --o;
+      return o;
+    };
+    const uint32_t o0 = owner(first), o1 = owner(last);
+    const float* base = args.pieces + (size_t)item * kDecodeGroupRows + threadIdx.x;
+    for (uint32_t o = o0; o <= o1; o += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = base[(size_t)min(o + k, o1) * kDecodeGroupRows];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc += o + k <= o1 ? v[k] : 0.f;
+    }
+  }
+  if (row < W.m) store_y(W.y, row, acc * kPlaneOutScale, args.y_fp32);
 }
 
 // ============================================================ multi-token kernel
@@ -606,10 +714,12 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
 
 // ============================================================ launchers
 int launch_decode_m1(const GroupArgs& args, void* stream) {
-  if (args.total_items == 0) return 0;
-  // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU)
-  hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(args.total_items), dim3(512), 0, static_cast<hipStream_t>(stream),
-                     args);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (args.total_units > 0) {
+    // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU)
+    hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(1u << args.grid_log2), dim3(512), 0, st, args);
+  }
+  if (args.total_groups > 0) hipLaunchKernelGGL(decode_combine_kernel, dim3(args.total_groups), dim3(kDecodeGroupRows), 0, st, args);
   return (int)hipGetLastError();
 }
 

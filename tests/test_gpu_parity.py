@@ -132,9 +132,13 @@ def test_llama3_8b_layer_decode_grouped():
         st.load(counts)
         ys = st.forward_group(list(range(7)), xs)
         check_sampled(weights, counts, ys, xs)
-        # single-weight launches agree with the grouped launch bit for bit
+        # the same launch again gives the same bits (the pieces are summed in a fixed order)
+        again = st.forward_group(list(range(7)), xs)
+        assert all(np.array_equal(a, b) for a, b in zip(ys, again))
+        # a single-weight launch splits the blocks over workgroups differently, so only
+        # the fp32 summation order differs
         for j in (1, 4, 6):
-            assert np.array_equal(st.forward(j, xs[j]), ys[j])
+            assert rel_err(st.forward(j, xs[j]), ys[j]) <= 1e-5
 
 
 @pytest.mark.slow

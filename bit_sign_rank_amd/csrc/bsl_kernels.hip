@@ -87,6 +87,10 @@ __device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const BSL_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(p));
 }
+// Data read exactly once (sign tiles): non-temporal, so it does not evict reused lines.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const BSL_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(p)));
+}
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const BSL_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
 }
@@ -203,13 +207,16 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 // block's last chunk (or the end of the range) the products get the block's column-sum
 // term and are weighted by U (the r-sum is linear, so a block split over two workgroups
 // is fine); after a row group's last unit (or the end of the range) each wave sums its
-// tiles over r and stores the workgroup's 512-row "piece" of the row group.  A second
-// kernel adds the pieces of each row group in workgroup order and writes y.
+// tiles over r and stores the workgroup's 512-row "piece" of the row group.  At the end
+// of its range the workgroup counts itself in for every row group it touched; the last
+// workgroup to arrive at a row group adds its pieces in workgroup order and writes y.
 //
 // Sign tiles are fetched one unit ahead, V fragments and activations two units ahead and
 // U fragments one unit ahead, across block, row-group and weight boundaries, so the HBM
 // stream never waits on compute; fetches past the end of the range read a page of zeros.
-// The main kernel has no atomics, fences or waits on outstanding loads.
+// Sign tiles are read once, so they are loaded non-temporally and leave the L2 to the V
+// and U fragments that other workgroups re-read.  Nothing waits on outstanding loads
+// before the end of the range.
 struct DecodeCursor {
   int32_t j, rg, i, ch;  // weight slot in the launch, row group, block, chunk
   uint32_t u;            // unit index
@@ -241,6 +248,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t L = G >= (uint32_t)kXcds ? (bid % kXcds) * (G / kXcds) + bid / kXcds : bid;
   const uint32_t u_begin = range_start(L, U, lg), u_end = range_start(L + 1, U, lg);
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+  // A weight without blocks has no units: y = 0, the empty sum (written by workgroup 0).
+  if (L == 0) {
+    for (int j = 0; j < args.count; ++j)
+      if (args.w[j].units == 0)
+        for (int row = threadIdx.x; row < args.w[j].m; row += NW * 64) store_y(args.w[j].y, row, 0.f, args.y_fp32);
+  }
+  if (U == 0) return;
 
   // ---- cursor over the unit list (wave-uniform state)
   auto locate = [&](uint32_t u) {
@@ -323,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   u32x4 vv[PP], xv[PP];
   auto load_signs = [&](const UnitPtrs& p, u32x4* rw) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) rw[t] = load16(p.signs + t * kTileBytes + lane * 16);
+    for (int t = 0; t < R; ++t) rw[t] = load16_stream(p.signs + t * kTileBytes + lane * 16);
   };
   auto load_u = [&](const UnitPtrs& p) {
 #pragma unroll
@@ -360,7 +374,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
     cs_run += sum_over_lane_groups(cs);
     if (c.valid && block_end(c)) {
-      if (lane < 16) csum[wpar][wave][lane] = cs_run;
+      // the sums are replicated in the four 16-lane groups; every lane stores its r's
+      csum[wpar][wave][r16] = cs_run;
       cs_run = 0.f;
       wpar ^= 1;
     }
@@ -391,8 +406,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       acc[k] = (float4v){0.f, 0.f, 0.f, 0.f};
     }
   };
-  // After a row group: this workgroup's piece of it, summed over r (plain stores; the
-  // pieces are read by the next kernel on the stream).
+  // After a row group: this workgroup's piece of it, summed over r.  Stored write-through
+  // at device scope: the workgroup that adds the pieces may sit on another XCD.
   const int rsel = reduced_row(lane);
   auto store_piece = [&](const DecodeCursor& c) {
     const uint32_t item = args.w[c.j].rg_begin + c.rg;
@@ -401,7 +416,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     for (int t = 0; t < R; ++t) {
       const float v = reduce_columns(accl[wave][t][lane], lane);
       accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
-      if ((lane & 3) == 0) piece[(wave * R + t) * kTileRows + rsel] = v;
+      if ((lane & 3) == 0)
+        __hip_atomic_store(&piece[(wave * R + t) * kTileRows + rsel], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -430,17 +446,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       // Row tiles: four independent accumulator chains per plane.  Planes 6-11 are read
       // from the words as loaded; the words are then rotated right by 6 in place (planes
       // 12-15 land on bits 6-9) and by 20 more (planes 0-5 land on bits 6-11), so no
-      // second copy of the words is kept.  Z fragments are read from LDS two planes ahead.
-      u32x4 zf[3];
+      // second copy of the words is kept.  Z fragments are read from LDS one plane ahead.
+      u32x4 zf[2];
       zf[0] = zs[buf][plane_order(0)][lane];
-      zf[1] = zs[buf][plane_order(1)][lane];
       // (a scheduling barrier per plane keeps the compiler from computing fragments of
       // later planes early, which would raise register pressure past two waves/SIMD)
 #define BSL_PLANE(S)                                                                                              \
   __builtin_amdgcn_sched_barrier(0);                                                                              \
-  if ((S) + 2 < kPlanes) zf[((S) + 2) % 3] = zs[buf][plane_order((S) + 2)][lane];                              \
+  if ((S) + 1 < kPlanes) zf[((S) + 1) % 2] = zs[buf][plane_order((S) + 1)][lane];                              \
   _Pragma("unroll") for (int k = 0; k < R; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(                \
-      as_half8(cur[k] & (0x00010001u << plane_pos(plane_order(S)))), as_half8(zf[(S) % 3]), acc[k], 0, 0, 0);
+      as_half8(cur[k] & (0x00010001u << plane_pos(plane_order(S)))), as_half8(zf[(S) % 2]), acc[k], 0, 0, 0);
 #define BSL_ROTATE(N)                                                                                             \
   _Pragma("unroll") for (int k = 0; k < R; ++k) _Pragma("unroll") for (int q = 0; q < 4; ++q) cur[k][q] =      \
       __builtin_amdgcn_alignbit(cur[k][q], cur[k][q], (N));
@@ -468,47 +483,78 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   };
 
   const uint32_t n = u_end - u_begin;
+  const uint32_t item_first = args.w[c0.j].rg_begin + c0.rg;
   for (uint32_t s = 0; s < n; s += 2) {
     step(raw, rawn, 0);
     if (s + 1 < n) step(rawn, raw, 1);
   }
-}
 
-// Sum the pieces of each row group (one workgroup of 512 threads per row group, one row
-// per thread) in workgroup order and write y.  A row group of a weight without blocks
-// has no pieces: y = 0, the empty sum.
-__global__ __launch_bounds__(kDecodeGroupRows) void decode_combine_kernel(GroupArgs args) {
-  const uint32_t item = blockIdx.x;
-  int j = 0;
-  while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
-  const WeightDesc& W = args.w[j];
-  const int rg = (int)(item - W.rg_begin);
-  const int row = rg * kDecodeGroupRows + threadIdx.x;
-  const uint32_t U = args.total_units;
-  const int lg = args.grid_log2;
-  const uint32_t G = 1u << lg;
-  float acc = 0.f;
-  if (W.units > 0) {
+  // ---- end of the range: count this workgroup in for every row group it touched; the
+  // last one to arrive at a row group adds the pieces (one per workgroup owner(first) ..
+  // owner(last), in that order) and writes y.
+  __shared__ uint32_t last_items[kDecodeGroupRows];
+  __shared__ uint32_t n_last;
+  const uint32_t tid = threadIdx.x;
+  auto owner = [&](uint32_t u) {
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < G && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  // global row group -> its weight slot and its first and last unit
+  auto group_units = [&](uint32_t item, uint32_t& first, uint32_t& last) {
+    int j = 0;
+    while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
+    const WeightDesc& W = args.w[j];
     const uint32_t per_rg = (uint32_t)W.nblocks * W.nch;
-    const uint32_t first = W.unit_begin + (uint32_t)rg * per_rg, last = first + per_rg - 1;
-    // workgroups holding units of this row group: owner(first) .. owner(last)
-    auto owner = [&](uint32_t u) {
-      uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
-      while (o + 1 < G && range_start(o + 1, U, lg) <= u) ++o;
-      while (range_start(o, U, lg) > u) --o;
-      return o;
-    };
-    const uint32_t o0 = owner(first), o1 = owner(last);
-    const float* base = args.pieces + (size_t)item * kDecodeGroupRows + threadIdx.x;
-    for (uint32_t o = o0; o <= o1; o += 8) {
-      float v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = base[(size_t)min(o + k, o1) * kDecodeGroupRows];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc += o + k <= o1 ? v[k] : 0.f;
+    first = W.unit_begin + (item - W.rg_begin) * per_rg;
+    last = first + per_rg - 1;
+    return j;
+  };
+  // row group of the range's last unit
+  int je = 0;
+  while (je + 1 < args.count && u_end - 1 >= args.w[je + 1].unit_begin) ++je;
+  const uint32_t item_last = args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's piece stores have completed
+  __syncthreads();
+  // row groups of the range, 512 at a time: one thread each counts the workgroup in
+  for (uint32_t k0 = 0; k0 <= item_last - item_first; k0 += kDecodeGroupRows) {
+    if (tid == 0) n_last = 0;
+    __syncthreads();
+    if (k0 + tid <= item_last - item_first) {
+      const uint32_t item = item_first + k0 + tid;
+      uint32_t first, last;
+      group_units(item, first, last);
+      const uint32_t expected = owner(last) - owner(first) + 1;
+      const uint32_t seen = __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      if (seen == expected) {
+        __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_items[atomicAdd(&n_last, 1u)] = item;
+      }
     }
+    __syncthreads();
+    const uint32_t nl = n_last;
+    for (uint32_t k = 0; k < nl; ++k) {
+      const uint32_t item = __builtin_amdgcn_readfirstlane(last_items[k]);
+      uint32_t first, last;
+      const int j = group_units(item, first, last);
+      const WeightDesc& W = args.w[j];
+      const uint32_t o0 = owner(first), o1 = owner(last);
+      const float* base = args.pieces + (size_t)item * kDecodeGroupRows + tid;
+      float acc_y = 0.f;
+      for (uint32_t o = o0; o <= o1; o += 8) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          v[q] = __hip_atomic_load(base + (size_t)min(o + q, o1) * kDecodeGroupRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
+      }
+      const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + tid;
+      if (row < W.m) store_y(W.y, row, acc_y * kPlaneOutScale, args.y_fp32);
+    }
+    __syncthreads();  // n_last and last_items are rewritten by the next batch
   }
-  if (row < W.m) store_y(W.y, row, acc * kPlaneOutScale, args.y_fp32);
 }
 
 // ============================================================ multi-token kernel
@@ -715,11 +761,9 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
 // ============================================================ launchers
 int launch_decode_m1(const GroupArgs& args, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (args.total_units > 0) {
-    // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU)
-    hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(1u << args.grid_log2), dim3(512), 0, st, args);
-  }
-  if (args.total_groups > 0) hipLaunchKernelGGL(decode_combine_kernel, dim3(args.total_groups), dim3(kDecodeGroupRows), 0, st, args);
+  // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU).  With no units at
+  // all (every weight empty) one workgroup still runs, to write y = 0.
+  hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(1u << args.grid_log2), dim3(512), 0, st, args);
   return (int)hipGetLastError();
 }
 

@@ -178,6 +178,71 @@ def measured_traffic():
     return int(fields["hbm_bytes_per_launch"])
 
 
+def write_profile_summaries(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> None:
+    """Turn rocprofv3 outputs (kernel-trace --stats of a bench run, then one --pmc
+    FETCH_SIZE and one --pmc WRITE_SIZE pass of a bench run with --calibrate-copy) into
+    the short text summaries kept under profiles/."""
+    import csv
+    import glob
+    import hashlib
+
+    def one(pattern):
+        files = glob.glob(os.path.join(pattern))
+        assert files, pattern
+        return files[0]
+
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    stats = list(csv.DictReader(open(one(os.path.join(trace_dir, "*kernel_stats.csv")))))
+    lines = [f"# rocprofv3 --kernel-trace --stats, Llama-3-8B-shaped layer (n=8, k=16): decode M=1 and prefill M=2048",
+             f"command: {command.split(';')[0]}",
+             "", f"{'kernel':58s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    for r in stats:
+        lines.append(f"{r['Name'][:58]:58s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    with open(os.path.join(ROOT, "profiles", "kernel_stats_llama3_8b_layer.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def counters(d, name):
+        vals = {}
+        for r in csv.DictReader(open(one(os.path.join(d, "*counter_collection.csv")))):
+            if r["Counter_Name"] == name:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
+    copy_name = next(k for k in fetch if "neg_kernel" in k)  # the torch.neg copy of copy_calibration()
+    dec_name = next(k for k in fetch if "decode_m1_kernel" in k)
+    med = lambda v: sorted(v)[len(v) // 2]
+    copy_bytes = 1024 * (1 << 20)  # each copy dispatch reads and writes exactly 1 GiB
+    f_copy = med(fetch[copy_name])
+    w_copy = med(write[copy_name])
+    f_scale = copy_bytes / (f_copy * 1024)
+    w_scale = copy_bytes / (w_copy * 1024)
+    f_dec = med(fetch[dec_name]) * 1024 * f_scale
+    w_dec = med(write[dec_name]) * 1024 * w_scale
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    algo = sum(8 * block_bytes(m, d) for _, m, d in synth.LLAMA3_8B_LAYER)
+    text = f"""# HBM traffic of decode_m1_kernel, one grouped launch over a Llama-3-8B-shaped layer (n=8, k=16, M=1)
+fetch command: {command.split(';')[1].strip() if ';' in command else ''}
+write command: {command.split(';')[2].strip() if command.count(';') > 1 else ''}
+calibration: a 1 GiB fp16 elementwise copy (torch.neg) in the same runs reads FETCH_SIZE {f_copy:.1f} KiB and writes WRITE_SIZE {w_copy:.1f} KiB per dispatch
+fetch_scale: {f_scale:.4f}
+write_scale: {w_scale:.4f}
+decode_fetch_kib_median: {med(fetch[dec_name]):.2f} over {len(fetch[dec_name])} dispatches
+decode_write_kib_median: {med(write[dec_name]):.2f} over {len(write[dec_name])} dispatches
+fetch_bytes_per_launch: {int(f_dec)}
+write_bytes_per_launch: {int(w_dec)}
+hbm_bytes_per_launch: {int(f_dec + w_dec)}
+algorithmic_bytes_per_launch: {algo}
+traffic_over_algorithmic: {(f_dec + w_dec) / algo:.4f}
+kernel_source_sha256: {digest}
+"""
+    with open(TRAFFIC_SUMMARY, "w") as f:
+        f.write(text)
+    print(open(TRAFFIC_SUMMARY).read())
+
+
 def copy_calibration(torch, mib: int = 1024, reps: int = 3) -> None:
     """A plain elementwise copy (y = -x, fp16) of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters: each dispatch reads and writes exactly `mib` MiB."""
@@ -205,7 +270,12 @@ def main() -> None:
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--write-profile-summaries", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
+                    help="write profiles/ summaries from rocprofv3 outputs (no GPU work)")
     args = ap.parse_args()
+    if args.write_profile_summaries:
+        write_profile_summaries(*args.write_profile_summaries)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)

@@ -418,7 +418,8 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  const int nt = M >= 8 ? 8 : 4;  // GEMM token tile
+  const bool prefill = M >= kPrefillMinM;
+  const int nt = prefill ? kPrefillTokenTile : (M >= 8 ? 8 : 4);  // token tile
   const int token_groups = (M + nt - 1) / nt;
   int32_t items = 0;
   uint64_t units = 0, groups = 0;
@@ -451,6 +452,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       D.rg_begin = (uint32_t)groups;
       units += wu;
       groups += D.groups;
+    } else if (prefill) {
+      D.groups = decode_groups(W) * token_groups;
+      D.splits = 1;
+      items += D.groups;
     } else {
       const int rgroups = (W.mt + kGemmRowTiles - 1) / kGemmRowTiles;
       int splits = 1;
@@ -477,6 +482,9 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
     e = launch_decode_m1(args, stream);
+  } else if (prefill) {
+    args.zero_page = s->zero_page;
+    e = launch_prefill(args, token_groups, stream);
   } else {
     e = launch_gemm(args, nt, token_groups, stream);
   }

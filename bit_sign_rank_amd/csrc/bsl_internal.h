@@ -71,6 +71,7 @@ struct GroupArgs {
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream);
+int launch_prefill(const GroupArgs& args, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
@@ -85,5 +86,7 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
 constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
 constexpr int kGemmMaxSplits = 8;
+constexpr int kPrefillMinM = 128;  // from this M on, the 32x32 prefill kernel (8-token groups)
+constexpr int kPrefillTokenTile = 8;
 
 }  // namespace bsl

@@ -709,6 +709,203 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// ============================================================ prefill kernel
+// Large M.  One workgroup of 8 waves per item = (weight, 512-row group, 8-token group);
+// wave w owns rows 64 w .. 64 w + 63 as two 32-row fragments against the 8 tokens as
+// four token pairs, i.e. 2 x 4 accumulators of v_mfma_f32_32x32x16_f16 (32 rows x
+// (2 tokens x 16 r)): the N width 2 x 16 = 32 is filled exactly, and each +-1 A fragment
+// feeds four MFMAs.  Z is built 4 planes (128 columns) at a time into double-buffered
+// LDS as B fragments; sign words for the next chunk and V / activations for the next
+// 4 planes are fetched while the current ones run.  After a block's K loop the
+// accumulators are weighted by U and summed over r with a 16-lane butterfly.
+//
+// Operand layouts (v_mfma_f32_32x32x16_f16): lane l holds A[l % 32][8 (l / 32) + e] and
+// B[8 (l / 32) + e][l % 32], e = 0..7; C[m][n] sits in lane n + 32 ((m / 4) % 2), value
+// 4 (m / 8) + m % 4.  K step s (0, 1) of plane b covers the plane's columns 16 s .. 16 s +
+// 15, which the stored tiles hold in lane group 2 s + l / 32 of row l % 32: a lane loads
+// the 16 stored bytes of that (row, group) and gets every plane of it.
+typedef float float16v __attribute__((ext_vector_type(16)));
+constexpr int kPrefillTokens = 8;
+constexpr int kPrefillPlanes = 4;  // planes per Z stage
+
+// Sum 16 values over the 16 lanes of a DPP row; lane r ends with the sum of value r.
+// Four butterfly stages (partners r^8, r^7, r^2, r^1) halve the values each time.
+__device__ __forceinline__ float reduce16x16(float (&v)[16], int lane) {
+  const int r = lane & 15;
+  float a[8], b2[4], c2[2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float keep = (r & 8) ? v[8 + k] : v[k], send = (r & 8) ? v[k] : v[8 + k];
+    a[k] = keep + dpp_mov<kDppRowRor8>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = (r & 4) ? a[4 + k] : a[k], send = (r & 4) ? a[k] : a[4 + k];
+    b2[k] = keep + dpp_mov<kDppRowHalfMirror>(send);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = (r & 2) ? b2[2 + k] : b2[k], send = (r & 2) ? b2[k] : b2[2 + k];
+    c2[k] = keep + dpp_mov<kDppQuadSwap2>(send);
+  }
+  const float keep = (r & 1) ? c2[1] : c2[0], send = (r & 1) ? c2[0] : c2[1];
+  return keep + dpp_mov<kDppQuadSwap1>(send);
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(GroupArgs args, int token_groups) {
+  constexpr int T = kPrefillTokens, NP = T / 2, PL = kPrefillPlanes;
+  constexpr int FRAGS = PL * 2 * NP;          // B fragments per stage (32)
+  constexpr int FPW = FRAGS / 8;              // built per wave (4)
+  __shared__ u32x4 zs[2][FRAGS][64];          // [stage buffer][(plane, step, pair)][lane], 64 KiB
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int kg = lane >> 5;                   // K group of this lane (A and B)
+  const int n32 = lane & 31;
+  const WeightDesc W = find_weight(args, blockIdx.x);
+  const int local = blockIdx.x - W.item_begin;
+  const int tg = local % token_groups;
+  const int rg = local / token_groups;
+  const int M = args.M;
+  const int tok0 = tg * T;
+  const int row0 = rg * kDecodeGroupRows + wave * 64;  // this wave's first row
+  const int nb = W.nblocks;
+  const int nch = W.nch;
+  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+
+  // sign words: [fragment rf][K step s] = the 16 stored bytes of (row row0 + 32 rf + l % 32,
+  // lane group 2 s + kg) of the current chunk
+  auto load_signs = [&](const BlockPtrs& bp, int ch, u32x4 (&w)[2][2]) {
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) {
+      const int row = row0 + 32 * rf + n32;
+      const uint8_t* tile = bp.signs + ((size_t)ch * W.mt + (row >> 4)) * kTileBytes;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) w[rf][st] = load16(tile + ((row & 15) + 16 * (2 * st + kg)) * 16);
+    }
+  };
+  // V fragment and activations of this wave's B fragments of stage (ch, q)
+  auto load_vx = [&](const BlockPtrs& bp, int ch, int q, u32x4 (&vv)[FPW], u32x4 (&xv)[FPW]) {
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+      const int id = wave * FPW + f;          // (plane pl, step st, pair pp)
+      const int pl = id / (2 * NP), st = (id / NP) % 2, pp = id % NP;
+      const int b = q * PL + pl;
+      vv[f] = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + (lane & 15) + 16 * (2 * st + kg)) * 8);
+      const int tok = tok0 + 2 * pp + (n32 >> 4);
+      const int col = ch * kChunkCols + 32 * b + 16 * st + 8 * kg;
+      const bool ok = tok < M && col < W.d;
+      xv[f] = load16(ok ? static_cast<const void*>(W.x + (size_t)tok * W.d + col) : static_cast<const void*>(zero_page));
+    }
+  };
+  auto build = [&](int buf, const u32x4 (&vv)[FPW], const u32x4 (&xv)[FPW]) {
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+      u32x4 z;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = as_u32(as_half2(vv[f][e]) * as_half2(xv[f][e]));
+      zs[buf][wave * FPW + f][lane] = z;
+    }
+  };
+
+  float yacc[2][NP];
+#pragma unroll
+  for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) yacc[rf][pp] = 0.f;
+
+  const int stages = nb * nch * (kPlanes / PL);
+  if (stages > 0) {
+    u32x4 w[2][2], wn[2][2];
+    u32x4 vv[FPW], xv[FPW];
+    float16v acc[2][NP];
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) acc[rf][pp] = (float16v){};
+    BlockPtrs bp = load_block(W.blocks, 0);
+    load_signs(bp, 0, w);
+    load_vx(bp, 0, 0, vv, xv);
+    build(0, vv, xv);
+    int i = 0, ch = 0, q = 0;  // current stage
+    for (int sidx = 0; sidx < stages; ++sidx) {
+      const int buf = sidx & 1;
+      // next stage
+      int ni = i, nc = ch, nq = q + 1;
+      if (nq == kPlanes / PL) { nq = 0; if (++nc == nch) { nc = 0; ++ni; } }
+      const bool more = sidx + 1 < stages;
+      const BlockPtrs nbp = load_block(W.blocks, more ? ni : i);
+      lds_barrier();  // Z of this stage is in zs[buf]; zs[buf ^ 1] is free
+      if (nq == 0 && more) load_signs(nbp, nc, wn);
+      load_vx(more ? nbp : bp, more ? nc : ch, more ? nq : q, vv, xv);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pl = 0; pl < PL; ++pl) {
+        const int b = q * PL + pl;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const half8 a0 = as_half8(pm1_fragment(w[0][st], b));
+          const half8 a1 = as_half8(pm1_fragment(w[1][st], b));
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+            const half8 bf = as_half8(zs[buf][(pl * 2 + st) * NP + pp][lane]);
+            acc[0][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bf, acc[0][pp], 0, 0, 0);
+            acc[1][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bf, acc[1][pp], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) build(buf ^ 1, vv, xv);
+      // after a block's last stage: U weighting and the sum over r
+      if (nq == 0 && nc == 0) {
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+          // U[row(v)][r] for v = 0..15: rows 8 (v / 4) + 4 kg + v % 4 of the fragment
+          half2v uu[8];
+          const int rbase = row0 + 32 * rf;
+#pragma unroll
+          for (int vg = 0; vg < 4; ++vg) {
+            const int tile = (rbase >> 4) + (vg >> 1);
+            const u32x2 u = load8(bp.u + ((size_t)tile * 64 + (lane & 15) + 16 * (2 * (vg & 1) + kg)) * 4);
+            uu[2 * vg] = as_half2(u[0]);
+            uu[2 * vg + 1] = as_half2(u[1]);
+          }
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+            float v[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = acc[rf][pp][e] * (float)uu[e >> 1][e & 1];
+            yacc[rf][pp] += reduce16x16(v, lane);
+            acc[rf][pp] = (float16v){};
+          }
+        }
+      }
+      if (nq == 0 && more) {
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+          for (int st = 0; st < 2; ++st) w[rf][st] = wn[rf][st];
+      }
+      bp = nbp;
+      i = ni;
+      ch = nc;
+      q = nq;
+    }
+  }
+  // lane l holds, for each (fragment, pair), row 8 (v / 4) + 4 kg + v % 4 with v = l % 16,
+  // token 2 pair + (l % 32) / 16
+  const int v = lane & 15;
+#pragma unroll
+  for (int rf = 0; rf < 2; ++rf) {
+    const int row = row0 + 32 * rf + 8 * (v >> 2) + 4 * kg + (v & 3);
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int tok = tok0 + 2 * pp + (n32 >> 4);
+      if (row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, yacc[rf][pp], args.y_fp32);
+    }
+  }
+}
+
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write +-1.
 __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int path,
@@ -764,6 +961,13 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
   // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU).  With no units at
   // all (every weight empty) one workgroup still runs, to write y = 0.
   hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(1u << args.grid_log2), dim3(512), 0, st, args);
+  return (int)hipGetLastError();
+}
+
+int launch_prefill(const GroupArgs& args, int token_groups, void* stream) {
+  if (args.total_items == 0) return 0;
+  hipLaunchKernelGGL(prefill_kernel, dim3(args.total_items), dim3(512), 0, static_cast<hipStream_t>(stream), args,
+                     token_groups);
   return (int)hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ def test_debug_unpack_bit_exact(m, d, path):
 
 # ---------------------------------------------------------------- exact integer forward
 @pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1)])
-@pytest.mark.parametrize("M", [1, 3, 8, 17])
+@pytest.mark.parametrize("M", [1, 3, 8, 17, 130])
 def test_integer_forward_bit_exact(m, d, n, M):
     # U = V = 0.25 with k = 16 makes U V^T == 1, so y = x (sum_i S_i)^T is an integer of
     # magnitude < 2^20; every partial sum is exact in fp32, so any order gives the same bits.
@@ -187,6 +187,31 @@ def test_ragged_shapes_random_blocks(m, d, M):
         st.load([3])
         y = st.forward(0, x)
     assert rel_err(y, oracle.forward(x, blocks, 3)) <= REL_TOL
+
+
+# ---------------------------------------------------------------- many tokens (the 32x32 prefill path)
+@pytest.mark.parametrize("m,d,M", [(1000, 1544, 133), (37, 520, 128), (512, 1024, 256)])
+def test_prefill_ragged_shapes(m, d, M):
+    blocks = synth.synthetic_blocks(25, m, d, 3, 16, m, d)
+    x = synth.activations(26, M, d)
+    with Stack([(m, d, blocks)]) as st:
+        st.load([3])
+        y = st.forward(0, x, fp32=False)
+    assert rel_err(y, oracle.forward(x, blocks, 3)) <= REL_TOL
+
+
+def test_prefill_grouped_launch_and_zero_blocks():
+    shapes = [(1024, 1024, 2), (512, 2048, 0), (1536, 512, 4)]
+    weights = [(m, d, synth.synthetic_blocks(27, m, d, max(n, 1), 16, j)) for j, (m, d, n) in enumerate(shapes)]
+    xs = [synth.activations(28, 256, d, j) for j, (_, d, _) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load([n for _, _, n in shapes])
+        ys = st.forward_group([0, 1, 2], xs)
+    for (m, d, blocks), (_, _, n), y, x in zip(weights, shapes, ys, xs):
+        if n == 0:
+            assert not y.any()
+        else:
+            assert rel_err(y, oracle.forward(x, blocks, n)) <= REL_TOL
 
 
 # ---------------------------------------------------------------- error handling

@@ -128,7 +128,7 @@ struct Weight {
 struct bsl_stack {
   int device = 0;
   int32_t k = 16, n_cap = 0;
-  int32_t decode_grid_max = 512;  // largest power of two <= 2 x compute units
+  int32_t decode_grid_max = 256;  // largest power of two <= compute units
   uint64_t budget = 0, resident = 0;
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
@@ -175,6 +175,7 @@ int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
 
 // Row groups of the single-token kernel (kDecodeGroupTiles row tiles each).
 int decode_groups(const Weight& W) { return (W.mt + kDecodeGroupTiles - 1) / kDecodeGroupTiles; }
+int prefill_groups(const Weight& W) { return (W.mt * kTileRows + kPrefillGroupRows - 1) / kPrefillGroupRows; }
 
 }  // namespace
 
@@ -245,7 +246,7 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     rc = hip_fail(e, "hipDeviceGetAttribute(multiprocessors)");
   else {
     s->decode_grid_max = 1;
-    while (s->decode_grid_max * 2 <= std::max(1, 2 * cus)) s->decode_grid_max *= 2;
+    while (s->decode_grid_max * 2 <= std::max(1, cus)) s->decode_grid_max *= 2;
     if ((e = hipMalloc(&s->zero_page, kZeroPageBytes)) != hipSuccess) rc = hip_fail(e, "hipMalloc(zero page)");
     else if ((e = hipMemset(s->zero_page, 0, kZeroPageBytes)) != hipSuccess) rc = hip_fail(e, "hipMemset(zero page)");
   }
@@ -453,7 +454,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       units += wu;
       groups += D.groups;
     } else if (prefill) {
-      D.groups = decode_groups(W) * token_groups;
+      D.groups = prefill_groups(W) * token_groups;
       D.splits = 1;
       items += D.groups;
     } else {
@@ -469,7 +470,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   DeviceGuard guard(s->device);
   int e = 0;
   if (M == 1) {
-    // Persistent grid: the largest power of two that is no more than two workgroups per
+    // Persistent grid: the largest power of two that is no more than one workgroup per
     // CU and no more than the number of units (so no workgroup's share is empty).
     int32_t grid = s->decode_grid_max, lg = 0;
     while (grid > 1 && (uint64_t)grid > units) grid /= 2;

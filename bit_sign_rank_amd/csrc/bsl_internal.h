@@ -17,10 +17,10 @@ constexpr int kTileBytes = 1024;  // 16 x 512 bits
 constexpr int kMaxGroup = 8;      // weights per grouped launch
 constexpr int kMaxBlocks = 64;    // blocks per weight (the kernels keep the table in LDS)
 
-// Rows are padded to a multiple of 512 (32 tiles, the largest row group any kernel
+// Rows are padded to a multiple of 1024 (64 tiles, the largest row group any kernel
 // takes), so every kernel can read whole row groups without bounds checks; padding
 // rows have +1 signs and zero U, so they add nothing.
-constexpr int kRowAlign = 512;
+constexpr int kRowAlign = 1024;
 inline int64_t pad_rows(int64_t m) { return (m + kRowAlign - 1) / kRowAlign * kRowAlign; }
 inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * kChunkCols; }
 
@@ -75,11 +75,13 @@ int launch_prefill(const GroupArgs& args, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
-// Single-token path: rows are taken in row groups of 32 tiles (512 rows).  A persistent
-// workgroup walks an equal share of the (row group, block, chunk) units and stores one
-// 512-float "piece" of partial sums per row group it touches; the last workgroup to
-// finish a row group adds its pieces in a fixed order.
-constexpr int kDecodeGroupTiles = 32;
+// Single-token path: rows are taken in row groups of 64 tiles (1024 rows), one
+// persistent 16-wave workgroup per CU.  A workgroup walks an equal share of the (row
+// group, block, chunk) units and stores one 1024-float "piece" of partial sums per row
+// group it touches; the last workgroup to finish a row group adds its pieces in a fixed
+// order.
+constexpr int kDecodeGroupTiles = 64;
+constexpr int kDecodeWaves = 16;
 constexpr int kDecodeGroupRows = kDecodeGroupTiles * 16;
 constexpr int kZeroPageBytes = 65536;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCDs
@@ -88,5 +90,6 @@ constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEM
 constexpr int kGemmMaxSplits = 8;
 constexpr int kPrefillMinM = 128;  // from this M on, the 32x32 prefill kernel (8-token groups)
 constexpr int kPrefillTokenTile = 8;
+constexpr int kPrefillGroupRows = 512;  // rows per prefill workgroup (8 waves x 64)
 
 }  // namespace bsl

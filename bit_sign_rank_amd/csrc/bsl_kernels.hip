@@ -198,7 +198,7 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 
 // ============================================================ single-token kernel
 // Persistent workgroups of NW waves.  The work is a list of units (weight, row group of
-// NW R = 32 row tiles, block, 512-column chunk) in that order; with U units and G
+// NW R = 64 row tiles, block, 512-column chunk) in that order; with U units and G
 // workgroups, workgroup L walks units [L U / G, (L + 1) U / G).
 //
 // For every unit the workgroup builds the chunk's Z tile once, in LDS (double buffered;
@@ -207,7 +207,7 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 // block's last chunk (or the end of the range) the products get the block's column-sum
 // term and are weighted by U (the r-sum is linear, so a block split over two workgroups
 // is fine); after a row group's last unit (or the end of the range) each wave sums its
-// tiles over r and stores the workgroup's 512-row "piece" of the row group.  At the end
+// tiles over r and stores the workgroup's 1024-row "piece" of the row group.  At the end
 // of its range the workgroup counts itself in for every row group it touched; the last
 // workgroup to arrive at a row group adds its pieces in workgroup order and writes y.
 //
@@ -221,6 +221,10 @@ struct DecodeCursor {
   int32_t j, rg, i, ch;  // weight slot in the launch, row group, block, chunk
   uint32_t u;            // unit index
   bool valid;            // false past the end of the workgroup's range
+  // fields of weight j, kept in scalar registers (reloaded only when j changes)
+  int32_t nb, nch, groups, mt, d;
+  uint32_t rg_begin;
+  const uint16_t* x;
 };
 
 // Units [start(o), start(o + 1)) belong to workgroup o.
@@ -256,19 +260,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
   if (U == 0) return;
 
+  // Base address of every loaded block of every weight of the launch, in LDS (a block's
+  // signs, U and V share one allocation, in that order), so that the unit loop issues no
+  // scalar loads: on this hardware those share a wait counter with LDS reads, and every
+  // LDS wait would also wait for them.
+  __shared__ uint64_t bbase[kMaxGroup][kMaxBlocks];
+  {
+    const int j = threadIdx.x / kMaxBlocks, i = threadIdx.x % kMaxBlocks;
+    if (j < args.count && i < args.w[j].nblocks) {
+      const u32x2 t = load8(&args.w[j].blocks[i].signs);
+      bbase[j][i] = t[0] | ((uint64_t)t[1] << 32);
+    }
+  }
+  __syncthreads();
+
   // ---- cursor over the unit list (wave-uniform state)
+  auto load_weight = [&](DecodeCursor& c) {
+    const WeightDesc& W = args.w[c.j];
+    c.nb = W.nblocks;
+    c.nch = W.nch;
+    c.groups = W.groups;
+    c.mt = W.mt;
+    c.d = W.d;
+    c.rg_begin = W.rg_begin;
+    c.x = W.x;
+  };
   auto locate = [&](uint32_t u) {
     DecodeCursor c;
     int j = 0;
     while (j + 1 < args.count && u >= args.w[j + 1].unit_begin) ++j;
-    const WeightDesc& W = args.w[j];
-    const uint32_t local = u - W.unit_begin;
-    const uint32_t per_rg = (uint32_t)W.nch * W.nblocks;
     c.j = j;
+    load_weight(c);
+    const uint32_t local = u - args.w[j].unit_begin;
+    const uint32_t per_rg = (uint32_t)c.nch * c.nb;
     c.rg = local / per_rg;
     const uint32_t rem = local - c.rg * per_rg;
-    c.i = rem / W.nch;
-    c.ch = rem - c.i * W.nch;
+    c.i = rem / c.nch;
+    c.ch = rem - c.i * c.nch;
     c.u = u;
     c.valid = true;
     return c;
@@ -279,26 +307,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       return c;
     }
     ++c.u;
-    const WeightDesc& W = args.w[c.j];
-    if (++c.ch == W.nch) {
+    if (++c.ch == c.nch) {
       c.ch = 0;
-      if (++c.i == W.nblocks) {
+      if (++c.i == c.nb) {
         c.i = 0;
-        if (++c.rg == W.groups) {
+        if (++c.rg == c.groups) {
           c.rg = 0;
           do ++c.j;
           while (args.w[c.j].units == 0);
+          load_weight(c);
         }
       }
     }
     return c;
   };
   // the unit closes this workgroup's share of a block / of a row group
-  auto block_end = [&](const DecodeCursor& c) { return c.ch == args.w[c.j].nch - 1 || c.u + 1 == u_end; };
-  auto group_end = [&](const DecodeCursor& c) {
-    const WeightDesc& W = args.w[c.j];
-    return (c.ch == W.nch - 1 && c.i == W.nblocks - 1) || c.u + 1 == u_end;
-  };
+  auto block_end = [&](const DecodeCursor& c) { return c.ch == c.nch - 1 || c.u + 1 == u_end; };
+  auto group_end = [&](const DecodeCursor& c) { return (c.ch == c.nch - 1 && c.i == c.nb - 1) || c.u + 1 == u_end; };
   // Per-wave base addresses of a unit's loads (the zero page for an invalid cursor).
   struct UnitPtrs {
     const uint8_t* signs;
@@ -310,14 +335,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   auto unit_ptrs = [&](const DecodeCursor& c) {
     UnitPtrs p;
     if (c.valid) {
-      const WeightDesc& W = args.w[c.j];
-      const BlockPtrs b = load_block(W.blocks, c.i);
+      const uint8_t* base = uniform_ptr(reinterpret_cast<const uint8_t*>(bbase[c.j][c.i]));
+      const size_t sign_bytes = (size_t)c.mt * c.nch * kTileBytes;
       const int rt0 = c.rg * kDecodeGroupTiles + wave * R;
-      p.signs = b.signs + ((size_t)c.ch * W.mt + rt0) * kTileBytes;
-      p.u = b.u + (size_t)rt0 * 64 * 4;
-      p.v = b.v + ((size_t)c.ch * kPlanes + PP * wave) * 64 * 8;
-      p.x = W.x + (size_t)c.ch * kChunkCols;
-      p.xcols = W.d - c.ch * kChunkCols;
+      p.signs = base + ((size_t)c.ch * c.mt + rt0) * kTileBytes;
+      p.u = reinterpret_cast<const uint16_t*>(base + sign_bytes) + (size_t)rt0 * 64 * 4;
+      p.v = reinterpret_cast<const uint16_t*>(base + sign_bytes + (size_t)c.mt * 64 * 4 * 2) +
+            ((size_t)c.ch * kPlanes + PP * wave) * 64 * 8;
+      p.x = c.x + (size_t)c.ch * kChunkCols;
+      p.xcols = c.d - c.ch * kChunkCols;
     } else {
       p.signs = zero_page;
       p.u = reinterpret_cast<const uint16_t*>(zero_page);
@@ -410,7 +436,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // at device scope: the workgroup that adds the pieces may sit on another XCD.
   const int rsel = reduced_row(lane);
   auto store_piece = [&](const DecodeCursor& c) {
-    const uint32_t item = args.w[c.j].rg_begin + c.rg;
+    const uint32_t item = c.rg_begin + c.rg;
     float* piece = args.pieces + (size_t)(item + L) * kDecodeGroupRows;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
@@ -483,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   };
 
   const uint32_t n = u_end - u_begin;
-  const uint32_t item_first = args.w[c0.j].rg_begin + c0.rg;
+  const uint32_t item_first = c0.rg_begin + c0.rg;
   for (uint32_t s = 0; s < n; s += 2) {
     step(raw, rawn, 0);
     if (s + 1 < n) step(rawn, raw, 1);
@@ -768,7 +794,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rg = local / token_groups;
   const int M = args.M;
   const int tok0 = tg * T;
-  const int row0 = rg * kDecodeGroupRows + wave * 64;  // this wave's first row
+  const int row0 = rg * kPrefillGroupRows + wave * 64;  // this wave's first row
   const int nb = W.nblocks;
   const int nch = W.nch;
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
@@ -958,9 +984,11 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
 // ============================================================ launchers
 int launch_decode_m1(const GroupArgs& args, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // 8 waves x 4 row tiles, 4 waves per SIMD (two workgroups per CU).  With no units at
-  // all (every weight empty) one workgroup still runs, to write y = 0.
-  hipLaunchKernelGGL((decode_m1_kernel<8, 4, 4>), dim3(1u << args.grid_log2), dim3(512), 0, st, args);
+  // 16 waves x 4 row tiles, 4 waves per SIMD (one workgroup per CU: all waves advance
+  // together, so no workgroup is left running alone on a CU at the end).  With no units
+  // at all (every weight empty) one workgroup still runs, to write y = 0.
+  hipLaunchKernelGGL((decode_m1_kernel<kDecodeWaves, 4, 4>), dim3(1u << args.grid_log2), dim3(kDecodeWaves * 64), 0, st,
+                     args);
   return (int)hipGetLastError();
 }
 

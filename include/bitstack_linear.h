@@ -33,7 +33,7 @@
  *     bsl_set_source / bsl_destroy of that weight) and never retained otherwise.
  *   - fp16 values are passed as their IEEE binary16 bit patterns (uint16_t).
  *   - Supported shapes: k == 16, 1 <= m <= 2^20, 8 <= d <= 2^20 with d % 8 == 0.
- *     Internally rows are padded to a multiple of 512 and columns to a multiple of
+ *     Internally rows are padded to a multiple of 1024 and columns to a multiple of
  *     512 (padding signs are +1 and padding factor entries are 0, so padding never
  *     changes a result).
  *   - A stack is not thread-safe: calls on one stack must not run concurrently.
@@ -74,7 +74,7 @@ typedef struct bsl_block_src {
 /* Payload bytes of one block: m*d/8 + 2*k*(m + d).  Returns 0 for invalid sizes. */
 size_t bsl_block_bytes(int64_t m, int64_t d, int32_t k);
 
-/* Bytes of the tiled sign layout of one m x d block (rows and columns padded to 512). */
+/* Bytes of the tiled sign layout of one m x d block (rows padded to 1024, columns to 512). */
 size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
 
 /* Host-side "bitstack_pack": convert row-major sign bits (format of bsl_block_src)

@@ -54,11 +54,11 @@ def test_block_bytes_printed_value():
 
 def _expected_tiled(bits, m, d):
     """The documented layout, written out independently of the library: tiles ordered
-    [column chunk c][row tile t], rows padded to 512; bit p of word q of lane 16 g + i
+    [column chunk c][row tile t], rows padded to 1024; bit p of word q of lane 16 g + i
     in tile (c, t) is the sign of row 16 t + i, column 512 c + 32 (p % 16) + 8 g + 2 q
     + p // 16 (padding reads as +1, i.e. bit 0)."""
     signs_neg = np.unpackbits(bits, axis=1, bitorder="little")[:, :d].astype(np.uint8)
-    mp = -(-m // 512) * 512  # rows padded to 512
+    mp = -(-m // 1024) * 1024  # rows padded to 1024
     dp = -(-d // 512) * 512
     full = np.zeros((mp, dp), np.uint8)
     full[:m, :d] = signs_neg

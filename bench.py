@@ -98,26 +98,26 @@ class Layers:
 
 def time_steps(torch, layers: Layers, steps: int, warmup: int):
     """Warm up, then time exactly `steps` steps (one grouped launch each) between two
-    device synchronisations; per-launch HIP events on the launch stream give the
-    kernel durations."""
+    device synchronisations.  One HIP event pair on the launch stream brackets the same
+    steps, so the average launch duration carries no per-launch event overhead."""
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     for s in range(warmup):
         layers.launch(s % layers.layers, sp)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     total_bytes = total_flops = 0
     t0 = time.perf_counter()
+    e0.record(stream)
     for s in range(steps):
         l = s % layers.layers
-        ev[s][0].record(stream)
         layers.launch(l, sp)
-        ev[s][1].record(stream)
         total_bytes += layers.bytes(l)
         total_flops += layers.flops(l)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms = [e0.elapsed_time(e1) / steps]
     return wall, kern_ms, total_bytes, total_flops
 
 

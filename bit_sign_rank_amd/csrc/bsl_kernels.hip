@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // signs and zero U, and out-of-range addresses are redirected to the zero page), so
   // the number of loads in flight is the same on every path and the compiler's in-order
   // wait counts never drain the prefetches.
-  u32x4 raw[R], rawn[R];
+  u32x4 raw[R], rawn[R];  // sign words of the current and the next unit
   u32x2 uf[R];
   u32x4 vv[PP], xv[PP];
   auto load_signs = [&](const UnitPtrs& p, u32x4* rw) {
@@ -455,19 +455,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const UnitPtrs p0 = unit_ptrs(c0);
   UnitPtrs p1 = unit_ptrs(c1);
   UnitPtrs p2 = unit_ptrs(c2);
-  load_signs(p0, raw);
   load_vx(p0);
-  build_z(0, c0);
+  load_signs(p0, raw);
   __builtin_amdgcn_sched_barrier(0);
+  build_z(0, c0);  // (waits only for the first unit's V fragments and activations)
+  __builtin_amdgcn_sched_barrier(0);
+  load_signs(p1, rawn);
   load_vx(p1);
   load_u(p0);
 
-  // ---- one unit.  On entry unit c0's signs are in `cur`, its Z tile in zs[buf], its U
-  // fragments in uf, and unit c1's V fragments and activations in vv / xv.
-  auto step = [&](u32x4 (&cur)[R], u32x4 (&nxt)[R], const int buf) {
+  // ---- one unit.  On entry unit c0's signs are in `cur` and unit c1's in the other
+  // buffer, c0's Z tile in zs[buf], its U fragments in uf, and unit c1's V fragments
+  // and activations in vv / xv.  Unit c2's signs are fetched into `cur` as soon as the
+  // tiles are done with it, so a sign tile is requested well over one unit ahead.
+  auto step = [&](u32x4 (&cur)[R], const int buf) {
     lds_barrier();  // Z of c0 (and the column sums of a finished block) are complete
-    load_signs(p1, nxt);
-    __builtin_amdgcn_sched_barrier(0);
     {
       // Row tiles: four independent accumulator chains per plane.  Planes 6-11 are read
       // from the words as loaded; the words are then rotated right by 6 in place (planes
@@ -494,6 +496,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #undef BSL_PLANE
     }
     __builtin_amdgcn_sched_barrier(0);
+    load_signs(p2, cur);
+    __builtin_amdgcn_sched_barrier(0);
     if (block_end(c0)) weight_block();
     __builtin_amdgcn_sched_barrier(0);
     build_z(buf ^ 1, c1);
@@ -511,8 +515,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t n = u_end - u_begin;
   const uint32_t item_first = c0.rg_begin + c0.rg;
   for (uint32_t s = 0; s < n; s += 2) {
-    step(raw, rawn, 0);
-    if (s + 1 < n) step(rawn, raw, 1);
+    step(raw, 0);
+    if (s + 1 < n) step(rawn, 1);
   }
 
   // ---- end of the range: count this workgroup in for every row group it touched; the

@@ -374,7 +374,7 @@ def main() -> None:
             "ms_per_step": round(wall_p * 1e3 / args.prefill_steps, 2),
             "mfma_tflops": round(tfl, 1),
             "mfma_frac_of_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4),
-            "kernel": "gemm_kernel",
+            "kernel": "prefill_kernel",
             "flops_per_step": int(tf_p // args.prefill_steps),
         }
         log(f"prefill: {wall_p * 1e3 / args.prefill_steps:.1f} ms/step, {tfl:.1f} TFLOP/s")

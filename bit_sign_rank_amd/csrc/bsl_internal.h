@@ -88,7 +88,7 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
 constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
 constexpr int kGemmMaxSplits = 8;
-constexpr int kPrefillMinM = 128;  // from this M on, the 32x32 prefill kernel (8-token groups)
+constexpr int kPrefillMinM = 64;  // from this M on, the 32x32 prefill kernel (8-token groups)
 constexpr int kPrefillTokenTile = 8;
 constexpr int kPrefillGroupRows = 512;  // rows per prefill workgroup (8 waves x 64)
 

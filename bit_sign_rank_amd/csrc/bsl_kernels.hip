@@ -265,14 +265,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // scalar loads: on this hardware those share a wait counter with LDS reads, and every
   // LDS wait would also wait for them.
   __shared__ uint64_t bbase[kMaxGroup][kMaxBlocks];
-  {
-    const int j = threadIdx.x / kMaxBlocks, i = threadIdx.x % kMaxBlocks;
-    if (j < args.count && i < args.w[j].nblocks) {
-      const u32x2 t = load8(&args.w[j].blocks[i].signs);
-      bbase[j][i] = t[0] | ((uint64_t)t[1] << 32);
-    }
-  }
-  __syncthreads();
 
   // ---- cursor over the unit list (wave-uniform state)
   auto load_weight = [&](DecodeCursor& c) {
@@ -332,10 +324,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     const uint16_t* x;
     int32_t xcols;  // valid activation columns from x (the rest read zeros)
   };
-  auto unit_ptrs = [&](const DecodeCursor& c) {
+  // (`direct` reads the block's base from the device table instead: the prologue does,
+  // so its first loads do not wait for the LDS copy of the table)
+  auto unit_ptrs = [&](const DecodeCursor& c, bool direct = false) {
     UnitPtrs p;
     if (c.valid) {
-      const uint8_t* base = uniform_ptr(reinterpret_cast<const uint8_t*>(bbase[c.j][c.i]));
+      const uint8_t* base = direct ? load_block(args.w[c.j].blocks, c.i).signs
+                                   : uniform_ptr(reinterpret_cast<const uint8_t*>(bbase[c.j][c.i]));
       const size_t sign_bytes = (size_t)c.mt * c.nch * kTileBytes;
       const int rt0 = c.rg * kDecodeGroupTiles + wave * R;
       p.signs = base + ((size_t)c.ch * c.mt + rt0) * kTileBytes;
@@ -452,11 +447,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   DecodeCursor c0 = locate(u_begin);
   DecodeCursor c1 = next(c0);
   DecodeCursor c2 = next(c1);
-  const UnitPtrs p0 = unit_ptrs(c0);
-  UnitPtrs p1 = unit_ptrs(c1);
-  UnitPtrs p2 = unit_ptrs(c2);
+  const UnitPtrs p0 = unit_ptrs(c0, true);
+  UnitPtrs p1 = unit_ptrs(c1, true);
+  UnitPtrs p2 = unit_ptrs(c2, true);
   load_vx(p0);
   load_signs(p0, raw);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const int j = threadIdx.x / kMaxBlocks, i = threadIdx.x % kMaxBlocks;
+    if (j < args.count && i < args.w[j].nblocks) {
+      const u32x2 t = load8(&args.w[j].blocks[i].signs);
+      bbase[j][i] = t[0] | ((uint64_t)t[1] << 32);
+    }
+  }
+  lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   build_z(0, c0);  // (waits only for the first unit's V fragments and activations)
   __builtin_amdgcn_sched_barrier(0);
@@ -572,13 +576,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const uint32_t o0 = owner(first), o1 = owner(last);
       const float* base = args.pieces + (size_t)item * kDecodeGroupRows + tid;
       float acc_y = 0.f;
-      for (uint32_t o = o0; o <= o1; o += 8) {
-        float v[8];
+      for (uint32_t o = o0; o <= o1; o += 32) {  // (32 loads in flight per round trip)
+        float v[32];
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 32; ++q)
           v[q] = __hip_atomic_load(base + (size_t)min(o + q, o1) * kDecodeGroupRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
+        for (int q = 0; q < 32; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
       }
       const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + tid;
       if (row < W.m) store_y(W.y, row, acc_y * kPlaneOutScale, args.y_fp32);

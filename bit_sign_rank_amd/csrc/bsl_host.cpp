@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -258,8 +259,9 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     W.nch = (int32_t)(pad_cols(W.d) / kChunkCols);
     W.slots.resize(n_cap);
     const size_t mpad = (size_t)pad_rows(W.m);
-    W.partial_floats = (size_t)kGemmMaxSplits * kGemmMaxSplitM * mpad;
-    W.counter_count = (size_t)((W.mt + kGemmRowTiles - 1) / kGemmRowTiles) * kGemmMaxSplitM + 64;
+    W.partial_floats = (size_t)kSplitTokens * mpad;
+    // split items have at most kSplitTokens / 2 padded tokens, so at most 32 token groups
+    W.counter_count = (size_t)prefill_groups(W) * (kSplitTokens / 4);
     const size_t words = W.counter_count;
     max_groups = std::max<size_t>(max_groups, (size_t)decode_groups(W));
     if ((e = hipMalloc(&W.dtable, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(table)");
@@ -419,11 +421,25 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  const bool prefill = M >= kPrefillMinM;
-  const int nt = prefill ? kPrefillTokenTile : (M >= 8 ? 8 : 4);  // token tile
+  const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
   const int token_groups = (M + nt - 1) / nt;
-  int32_t items = 0;
-  uint64_t units = 0, groups = 0;
+  // Multi-token items are cut along their (block, chunk) sequence when there are too few
+  // of them: aim at about two equal items per CU, within the split-K workspace.
+  uint64_t split_target = 1;
+  int max_splits = 1;
+  if (M > 1) {
+    uint64_t work = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const int32_t w = weights[j];
+      if (w < 0 || w >= (int32_t)s->w.size()) break;  // rejected below
+      const Weight& W = s->w[w];
+      work += (uint64_t)prefill_groups(W) * token_groups * W.n * W.nch;
+    }
+    const uint64_t slots = 2 * (uint64_t)s->decode_grid_max;
+    split_target = std::max<uint64_t>(1, (work + slots - 1) / slots);
+    max_splits = std::max(1, std::min(kMaxSplits, kSplitTokens / (token_groups * nt)));
+  }
+  uint64_t items = 0, units = 0, groups = 0;
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -443,7 +459,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     D.mt = W.mt;
     D.nch = W.nch;
     D.nblocks = W.n;
-    D.item_begin = items;
+    D.item_begin = (int32_t)items;
     if (M == 1) {
       D.groups = decode_groups(W);
       D.splits = W.nch;
@@ -453,20 +469,17 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       D.rg_begin = (uint32_t)groups;
       units += wu;
       groups += D.groups;
-    } else if (prefill) {
-      D.groups = prefill_groups(W) * token_groups;
-      D.splits = 1;
-      items += D.groups;
     } else {
-      const int rgroups = (W.mt + kGemmRowTiles - 1) / kGemmRowTiles;
-      int splits = 1;
-      if (M <= kGemmMaxSplitM) splits = std::min<int>(W.nch, kGemmMaxSplits);
-      D.groups = rgroups * token_groups;
-      D.splits = splits;
-      items += D.groups * splits;
+      const uint64_t wunits = (uint64_t)W.n * W.nch;
+      const uint64_t wgroups = (uint64_t)prefill_groups(W) * token_groups;
+      const uint64_t splits = std::min<uint64_t>(max_splits, std::max<uint64_t>(1, (wunits + split_target - 1) / split_target));
+      if (items + wgroups * splits > (uint64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
+      D.groups = (int32_t)wgroups;
+      D.splits = (int32_t)splits;
+      items += wgroups * splits;
     }
   }
-  args.total_items = items;
+  args.total_items = (int32_t)items;
   DeviceGuard guard(s->device);
   int e = 0;
   if (M == 1) {
@@ -483,11 +496,9 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
     e = launch_decode_m1(args, stream);
-  } else if (prefill) {
-    args.zero_page = s->zero_page;
-    e = launch_prefill(args, token_groups, stream);
   } else {
-    e = launch_gemm(args, nt, token_groups, stream);
+    args.zero_page = s->zero_page;
+    e = launch_prefill(args, nt, token_groups, stream);
   }
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;

@@ -40,15 +40,16 @@ struct WeightDesc {
   const BlockPtrs* blocks;  // device table of the loaded blocks
   const uint16_t* x;        // [M][d] fp16
   void* y;                  // [M][m] fp16 or fp32
-  float* partial;           // split-K partial sums (workspace)
-  uint32_t* counters;       // arrival counters, one per output group (workspace, zero between calls)
-  uint32_t* pieces;         // single-token path: pieces per (row group, chunk) item (workspace)
+  float* partial;           // multi-token path: [split][token][row] partial sums (workspace)
+  uint32_t* counters;       // multi-token path: arrival counters, one per (row group, token group)
+                            // (workspace, zero between calls)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks
   int32_t item_begin;       // multi-token path: first work item of this weight in the launch
   int32_t groups;           // output groups (row groups x token groups) of this weight
-  int32_t splits;           // multi-token path: K splits (chunks per split = ceil(nch / splits))
+  int32_t splits;           // single-token path: nch; multi-token path: ranges of the (block, chunk)
+                            // sequence, ceil(nblocks nch / splits) pairs each
   uint32_t unit_begin;      // single-token path: first (row group, block, chunk) unit of this weight
   uint32_t units;           // single-token path: groups * nblocks * nch
   uint32_t rg_begin;        // single-token path: first row group of this weight in the launch
@@ -70,8 +71,7 @@ struct GroupArgs {
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
-int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream);
-int launch_prefill(const GroupArgs& args, int token_groups, void* stream);
+int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
@@ -85,11 +85,11 @@ constexpr int kDecodeWaves = 16;
 constexpr int kDecodeGroupRows = kDecodeGroupTiles * 16;
 constexpr int kZeroPageBytes = 65536;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCDs
-constexpr int kGemmRowTiles = 16;   // row tiles per GEMM workgroup (4 waves x 4 tiles)
-constexpr int kGemmMaxSplitM = 16;  // largest M that may use split-K in the GEMM path
-constexpr int kGemmMaxSplits = 8;
-constexpr int kPrefillMinM = 64;  // from this M on, the 32x32 prefill kernel (8-token groups)
-constexpr int kPrefillTokenTile = 8;
-constexpr int kPrefillGroupRows = 512;  // rows per prefill workgroup (8 waves x 64)
+// Multi-token path (M >= 2): one 8-wave workgroup per item = (512-row group, token
+// group of 2, 4 or 8 tokens, range of the (block, chunk) sequence).  A weight's items are
+// split along that sequence only while splits x padded tokens fit the workspace.
+constexpr int kPrefillGroupRows = 512;  // rows per workgroup (8 waves x 64)
+constexpr int kMaxSplits = 8;
+constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-sum workspace holds
 
 }  // namespace bsl

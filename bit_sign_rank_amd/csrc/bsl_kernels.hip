@@ -592,167 +592,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 }
 
 // ============================================================ multi-token kernel
-// One workgroup (4 waves) per item = (weight, 256-row group, NT-token group, K split).
-// Each wave owns 4 row tiles x NT tokens of accumulators.  For every block and every
-// 512-column chunk of its split, the workgroup builds the Z tile (V (.) x, 8 planes at a
-// time) in LDS, each wave unpacks its sign tiles to +-1 fragments and runs the MFMAs;
-// after a block's K loop the U-weighted tile is reduced over r into per-row sums.
-template <int NT>
-__global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_groups) {
-  __shared__ u32x4 zs[8 * NT * 64];  // [plane][token][lane] 16 B each: NT * 8 KiB
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x;
-  const WeightDesc W = find_weight(args, item);
-  const int M = args.M;
-  const int local = item - W.item_begin;
-  const int split = local % W.splits;
-  const int rest = local / W.splits;
-  const int tg = rest % token_groups;
-  const int rg = rest / token_groups;
-  const int g = lane >> 4;
-  const int cps = (W.nch + W.splits - 1) / W.splits;
-  const int c_begin = split * cps;
-  const int c_end = min(W.nch, c_begin + cps);
-  const int rt0 = rg * kGemmRowTiles + wave * 4;  // this wave's first row tile
-  const int tok0 = tg * NT;
-  const int rows_pad = W.mt * kTileRows;
-
-  float accy[4][NT];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) accy[a][t] = 0.f;
-
-  for (int i = 0; i < W.nblocks; ++i) {
-    const BlockPtrs bp = load_block(W.blocks, i);
-    float4v acc[4][NT];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[a][t] = (float4v){0.f, 0.f, 0.f, 0.f};
-    for (int ch = c_begin; ch < c_end; ++ch) {
-      u32x4 raw[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        raw[a] = (u32x4){0u, 0u, 0u, 0u};
-        raw[a] = load16(bp.signs + ((size_t)ch * W.mt + rt0 + a) * kTileBytes + lane * 16);
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        lds_barrier();  // consumers of the previous Z tile are done
-        // build 8 planes x NT tokens; wave builds planes 2*wave, 2*wave+1
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int p = 2 * wave + pp;
-          const int b = 8 * half + p;
-          const u32x4 vv = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + lane) * 8);
-          const int col = ch * kChunkCols + 32 * b + 8 * g;
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int tok = tok0 + t;
-            u32x4 xx = {0u, 0u, 0u, 0u};
-            if (tok < M && col < W.d) xx = load16(W.x + (size_t)tok * W.d + col);
-            u32x4 z;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) z[q] = as_u32(as_half2(vv[q]) * as_half2(xx[q]));
-            zs[(p * NT + t) * 64 + lane] = z;
-          }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int b = 8 * half + p;
-          u32x4 afr[4];
-#pragma unroll
-          for (int a = 0; a < 4; ++a) afr[a] = pm1_fragment(raw[a], b);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const half8 bfr = as_half8(zs[(p * NT + t) * 64 + lane]);
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-              acc[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(afr[a]), bfr, acc[a][t], 0, 0, 0);
-          }
-        }
-      }
-    }
-    // U weighting and reduction over r for this block
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      if (rt0 + a < W.mt) {
-        const u32x2 uf = load8(bp.u + ((size_t)(rt0 + a) * 64 + lane) * 4);
-        const half2v u01 = as_half2(uf[0]), u23 = as_half2(uf[1]);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          float4v v = acc[a][t];
-          v[0] *= (float)u01[0];
-          v[1] *= (float)u01[1];
-          v[2] *= (float)u23[0];
-          v[3] *= (float)u23[1];
-          accy[a][t] += reduce_columns(v, lane);
-        }
-      }
-    }
-  }
-
-  const int rsel = reduced_row(lane);
-  const bool writer = (lane & 3) == 0;
-  if (W.splits == 1) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int row = (rt0 + a) * kTileRows + rsel;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int tok = tok0 + t;
-        if (writer && row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, accy[a][t], args.y_fp32);
-      }
-    }
-    return;
-  }
-  // split-K: partial[split][token][row], then the last workgroup of the (rg, tg) group adds
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int row = (rt0 + a) * kTileRows + rsel;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int tok = tok0 + t;
-      if (writer && rt0 + a < W.mt && tok < M)
-        __hip_atomic_store(&W.partial[((size_t)split * M + tok) * rows_pad + row], accy[a][t], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
-  __syncthreads();                // ... in every wave, and every wave is past its last use of zs
-  uint32_t* last = reinterpret_cast<uint32_t*>(zs);
-  if (threadIdx.x == 0)
-    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
-  __syncthreads();
-  if (!*last) return;
-  const int row_begin = rg * kGemmRowTiles * kTileRows;
-  const int row_end = min(W.m, row_begin + kGemmRowTiles * kTileRows);
-  const int nrows = row_end - row_begin;
-  const int ntok = min(NT, M - tok0);
-  for (int e = threadIdx.x; e < nrows * ntok; e += 256) {
-    const int t = e / nrows, row = row_begin + e % nrows;
-    const int tok = tok0 + t;
-    float s = 0.f;
-    for (int sp = 0; sp < W.splits; ++sp)
-      s += __hip_atomic_load(&W.partial[((size_t)sp * M + tok) * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    store_y(W.y, (size_t)tok * W.m + row, s, args.y_fp32);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-
-// ============================================================ prefill kernel
-// Large M.  One workgroup of 8 waves per item = (weight, 512-row group, 8-token group);
-// wave w owns rows 64 w .. 64 w + 63 as two 32-row fragments against the 8 tokens as
-// four token pairs, i.e. 2 x 4 accumulators of v_mfma_f32_32x32x16_f16 (32 rows x
-// (2 tokens x 16 r)): the N width 2 x 16 = 32 is filled exactly, and each +-1 A fragment
-// feeds four MFMAs.  Z is built 4 planes (128 columns) at a time into double-buffered
-// LDS as B fragments; sign words for the next chunk and V / activations for the next
-// 4 planes are fetched while the current ones run.  After a block's K loop the
-// accumulators are weighted by U and summed over r with a 16-lane butterfly.
+// M >= 2.  One workgroup of 8 waves per item = (weight, 512-row group, T-token group,
+// range of the (block, chunk) sequence), T = 2, 4 or 8; wave w owns rows 64 w .. 64 w + 63
+// as two 32-row fragments against the T tokens as T / 2 token pairs, i.e. 2 x T / 2
+// accumulators of v_mfma_f32_32x32x16_f16 (32 rows x (2 tokens x 16 r)): the N width
+// 2 x 16 = 32 is filled exactly, and each +-1 A fragment feeds T / 2 MFMAs.  Z is built
+// 4 planes (128 columns) at a time into double-buffered LDS as B fragments; sign words
+// for the next chunk and V / activations for the next 4 planes are fetched while the
+// current ones run.  After a block's K loop (or the end of the item's range) the
+// accumulators are weighted by U and summed over r with a 16-lane butterfly.  When a
+// weight has too few items to fill the chip its (block, chunk) sequence is cut into
+// ranges; each range stores its partial sums and the last of them to finish adds all
+// ranges in order.
 //
 // Operand layouts (v_mfma_f32_32x32x16_f16): lane l holds A[l % 32][8 (l / 32) + e] and
 // B[8 (l / 32) + e][l % 32], e = 0..7; C[m][n] sits in lane n + 32 ((m / 4) % 2), value
@@ -760,7 +611,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(GroupArgs args, int token_gro
 // 15, which the stored tiles hold in lane group 2 s + l / 32 of row l % 32: a lane loads
 // the 16 stored bytes of that (row, group) and gets every plane of it.
 typedef float float16v __attribute__((ext_vector_type(16)));
-constexpr int kPrefillTokens = 8;
 constexpr int kPrefillPlanes = 4;  // planes per Z stage
 
 // Sum 16 values over the 16 lanes of a DPP row; lane r ends with the sum of value r.
@@ -787,24 +637,31 @@ __device__ __forceinline__ float reduce16x16(float (&v)[16], int lane) {
   return keep + dpp_mov<kDppQuadSwap1>(send);
 }
 
+template <int T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(GroupArgs args, int token_groups) {
-  constexpr int T = kPrefillTokens, NP = T / 2, PL = kPrefillPlanes;
-  constexpr int FRAGS = PL * 2 * NP;          // B fragments per stage (32)
-  constexpr int FPW = FRAGS / 8;              // built per wave (4)
-  __shared__ u32x4 zs[2][FRAGS][64];          // [stage buffer][(plane, step, pair)][lane], 64 KiB
+  constexpr int NP = T / 2, PL = kPrefillPlanes;
+  constexpr int FRAGS = PL * 2 * NP;          // B fragments per stage (32 for 8 tokens)
+  constexpr int FPW = FRAGS / 8;              // built per wave
+  __shared__ u32x4 zs[2][FRAGS][64];          // [stage buffer][(plane, step, pair)][lane], 64 KiB for 8 tokens
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int kg = lane >> 5;                   // K group of this lane (A and B)
   const int n32 = lane & 31;
   const WeightDesc W = find_weight(args, blockIdx.x);
   const int local = blockIdx.x - W.item_begin;
-  const int tg = local % token_groups;
-  const int rg = local / token_groups;
+  // the (block, chunk) sequence i * nch + ch is cut into W.splits equal ranges
+  const int split = local % W.splits;
+  const int rest = local / W.splits;
+  const int tg = rest % token_groups;
+  const int rg = rest / token_groups;
   const int M = args.M;
   const int tok0 = tg * T;
   const int row0 = rg * kPrefillGroupRows + wave * 64;  // this wave's first row
-  const int nb = W.nblocks;
   const int nch = W.nch;
+  const int units = W.nblocks * nch;
+  const int ups = (units + W.splits - 1) / W.splits;
+  const int u_begin = min(units, split * ups);
+  const int u_end = min(units, u_begin + ups);
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
 
   // sign words: [fragment rf][K step s] = the 16 stored bytes of (row row0 + 32 rf + l % 32,
@@ -848,7 +705,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) yacc[rf][pp] = 0.f;
 
-  const int stages = nb * nch * (kPlanes / PL);
+  const int stages = (u_end - u_begin) * (kPlanes / PL);
   if (stages > 0) {
     u32x4 w[2][2], wn[2][2];
     u32x4 vv[FPW], xv[FPW];
@@ -857,11 +714,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int rf = 0; rf < 2; ++rf)
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) acc[rf][pp] = (float16v){};
-    BlockPtrs bp = load_block(W.blocks, 0);
-    load_signs(bp, 0, w);
-    load_vx(bp, 0, 0, vv, xv);
+    int i = u_begin / nch, ch = u_begin % nch, q = 0;  // current stage
+    BlockPtrs bp = load_block(W.blocks, i);
+    load_signs(bp, ch, w);
+    load_vx(bp, ch, 0, vv, xv);
     build(0, vv, xv);
-    int i = 0, ch = 0, q = 0;  // current stage
     for (int sidx = 0; sidx < stages; ++sidx) {
       const int buf = sidx & 1;
       // next stage
@@ -890,8 +747,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       __builtin_amdgcn_sched_barrier(0);
       if (more) build(buf ^ 1, vv, xv);
-      // after a block's last stage: U weighting and the sum over r
-      if (nq == 0 && nc == 0) {
+      // after a block's last stage, or the range's: U weighting and the sum over r
+      if ((nq == 0 && nc == 0) || !more) {
 #pragma unroll
         for (int rf = 0; rf < 2; ++rf) {
           // U[row(v)][r] for v = 0..15: rows 8 (v / 4) + 4 kg + v % 4 of the fragment
@@ -929,15 +786,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // lane l holds, for each (fragment, pair), row 8 (v / 4) + 4 kg + v % 4 with v = l % 16,
   // token 2 pair + (l % 32) / 16
   const int v = lane & 15;
+  if (W.splits == 1) {
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) {
+      const int row = row0 + 32 * rf + 8 * (v >> 2) + 4 * kg + (v & 3);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int tok = tok0 + 2 * pp + (n32 >> 4);
+        if (row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, yacc[rf][pp], args.y_fp32);
+      }
+    }
+    return;
+  }
+  // Split over blocks: partial[split][token][row] (write-through at device scope), then
+  // the last workgroup of the (row group, token group) adds the splits in order.
+  const int mpad = token_groups * T;
+  const int rows_pad = W.mt * kTileRows;
 #pragma unroll
   for (int rf = 0; rf < 2; ++rf) {
     const int row = row0 + 32 * rf + 8 * (v >> 2) + 4 * kg + (v & 3);
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) {
       const int tok = tok0 + 2 * pp + (n32 >> 4);
-      if (row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, yacc[rf][pp], args.y_fp32);
+      __hip_atomic_store(&W.partial[((size_t)split * mpad + tok) * rows_pad + row], yacc[rf][pp], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
+  __syncthreads();                // ... in every wave, and every wave is done with zs
+  uint32_t* last = reinterpret_cast<uint32_t*>(&zs[0][0][0]);
+  if (threadIdx.x == 0)
+    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
+  __syncthreads();
+  if (!*last) return;
+  const int rbeg = rg * kPrefillGroupRows;
+  for (int e = threadIdx.x; e < kPrefillGroupRows * T; e += 512) {
+    const int t = e / kPrefillGroupRows, row = rbeg + e % kPrefillGroupRows;
+    const int tok = tok0 + t;
+    float sum = 0.f;
+    for (int sp = 0; sp < W.splits; ++sp)
+      sum += __hip_atomic_load(&W.partial[((size_t)sp * mpad + tok) * rows_pad + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (row < W.m && tok < M) store_y(W.y, (size_t)tok * W.m + row, sum, args.y_fp32);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ============================================================ debug unpack
@@ -1000,20 +891,15 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_prefill(const GroupArgs& args, int token_groups, void* stream) {
-  if (args.total_items == 0) return 0;
-  hipLaunchKernelGGL(prefill_kernel, dim3(args.total_items), dim3(512), 0, static_cast<hipStream_t>(stream), args,
-                     token_groups);
-  return (int)hipGetLastError();
-}
-
-int launch_gemm(const GroupArgs& args, int token_tile, int token_groups, void* stream) {
+int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream) {
   if (args.total_items == 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (token_tile == 8)
-    hipLaunchKernelGGL(gemm_kernel<8>, dim3(args.total_items), dim3(256), 0, st, args, token_groups);
+  if (token_tile == 2)
+    hipLaunchKernelGGL(prefill_kernel<2>, dim3(args.total_items), dim3(512), 0, st, args, token_groups);
   else if (token_tile == 4)
-    hipLaunchKernelGGL(gemm_kernel<4>, dim3(args.total_items), dim3(256), 0, st, args, token_groups);
+    hipLaunchKernelGGL(prefill_kernel<4>, dim3(args.total_items), dim3(512), 0, st, args, token_groups);
+  else if (token_tile == 8)
+    hipLaunchKernelGGL(prefill_kernel<8>, dim3(args.total_items), dim3(512), 0, st, args, token_groups);
   else
     return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();

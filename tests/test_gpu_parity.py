@@ -50,7 +50,7 @@ def test_debug_unpack_bit_exact(m, d, path):
 
 # ---------------------------------------------------------------- exact integer forward
 @pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1)])
-@pytest.mark.parametrize("M", [1, 3, 8, 17, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 17, 130])
 def test_integer_forward_bit_exact(m, d, n, M):
     # U = V = 0.25 with k = 16 makes U V^T == 1, so y = x (sum_i S_i)^T is an integer of
     # magnitude < 2^20; every partial sum is exact in fp32, so any order gives the same bits.

@@ -35,9 +35,20 @@ int hip_fail(hipError_t e, const char* what) {
 bool shape_ok(int64_t m, int64_t d) { return m >= 1 && m <= (1 << 20) && d >= 8 && d <= (1 << 20) && d % 8 == 0; }
 
 // ------------------------------------------------------------------ packing
-// Word q of lane L = 16 g + i in tile (row tile t, chunk c) collects, for plane b and
-// half h, the sign of column 512 c + 32 b + 8 g + 2 q + h of row 16 t + i.  In the
-// row-major source that sign is bit (2 q + h) of byte 64 c + 4 b + g of the row.
+// Lane L = 16 g + i of tile (row tile t, chunk c) holds row 16 t + i and, of every
+// plane b (columns 512 c + 32 b .. + 31), the columns 32 b + 8 g + e, e = 0..7: these
+// eight signs are bit e of byte 64 c + 4 b + g of the row-major source row.  They go to
+// word b / 4, half b % 2, bit 2 e + 1 (planes with (b / 2) % 2 == 0, "odd" positions) or
+// bit 2 e ("even" positions), so the word is the sum of the four planes' bytes spread
+// out to every second bit.
+
+// Spread the 8 bits of a byte to bit positions 0, 2, .., 14.
+uint32_t spread2(uint32_t x) {
+  x = (x | (x << 4)) & 0x0F0Fu;
+  x = (x | (x << 2)) & 0x3333u;
+  x = (x | (x << 1)) & 0x5555u;
+  return x;
+}
 void pack_rows(const uint8_t* src, int64_t m, int64_t d, uint8_t* out, int64_t r0, int64_t r1) {
   const int64_t nch = pad_cols(d) / kChunkCols;
   const int64_t mt = pad_rows(m) / kTileRows;
@@ -56,9 +67,9 @@ void pack_rows(const uint8_t* src, int64_t m, int64_t d, uint8_t* out, int64_t r
         uint32_t words[4];
         for (int q = 0; q < 4; ++q) {
           uint32_t w = 0;
-          for (int b = 0; b < kPlanes; ++b) {
-            w |= (uint32_t)((bytes[b] >> (2 * q)) & 1u) << b;
-            w |= (uint32_t)((bytes[b] >> (2 * q + 1)) & 1u) << (b + 16);
+          for (int k = 0; k < 4; ++k) {  // plane 4 q + k: half k % 2, odd positions for k < 2
+            const int half = k & 1, odd = k < 2 ? 1 : 0;
+            w |= spread2(bytes[4 * q + k]) << (16 * half + odd);
           }
           words[q] = w;
         }
@@ -209,10 +220,11 @@ int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out
     const int64_t t = r / kTileRows, i = r % kTileRows;
     for (int64_t col = 0; col < d; ++col) {
       const int64_t c = col / kChunkCols, cc = col % kChunkCols;
-      const int b = (int)(cc / 32), rem = (int)(cc % 32), g = rem / 8, q = (rem % 8) / 2, h = rem % 2;
+      const int b = (int)(cc / 32), rem = (int)(cc % 32), g = rem / 8, e = rem % 8;
+      const int q = b / 4, half = b % 2, odd = (b / 2) % 2 == 0 ? 1 : 0;
       uint32_t word;
       std::memcpy(&word, tiled + (c * mt + t) * kTileBytes + (16 * g + i) * 16 + 4 * q, 4);
-      const uint32_t bit = (word >> (b + 16 * h)) & 1u;
+      const uint32_t bit = (word >> (16 * half + 2 * e + odd)) & 1u;
       pm1_out[r * d + col] = bit ? -1 : 1;
     }
   }

@@ -6,31 +6,33 @@
 //     y[t, j] = sum_i sum_r U_i[j, r] * P_i[j, (t, r)],   P_i = S_i Z_i,
 //     Z_i[c, (t, r)] = V_i[c, r] * x[t, c],
 // so each block costs one dense contraction of the sign matrix with Z_i (width 16 M)
-// on the matrix cores (v_mfma_f32_16x16x32_f16: fp16 inputs, fp32 accumulation), a
-// Hadamard product with U_i and a sum over r that is done once for all blocks.
+// on the matrix cores (fp16 inputs, fp32 accumulation), a Hadamard product with U_i
+// and a sum over r that is done once for all blocks.
 //
-// Sign tiles (16 rows x 512 columns, 1 KiB) are read with one 16-byte load per lane
-// and turned into MFMA A fragments in registers; nothing is staged through LDS on the
-// single-token path, where the unpack and the MFMA issue share each SIMD and any LDS
-// round trip would cost more than the HBM read it serves.
-//
-// Two sign encodings share the stored layout:
-//  * single-token kernel (M = 1): "bit planes".  Plane b of a lane's four words keeps
-//    bits (pos, pos + 16) after one optional shift, so the A fragment is one AND per
-//    dword.  The fp16 element is then bit * 2^(pos - 24) (exact subnormal or normal
-//    powers of two, honoured exactly by the MFMA), i.e. a 0/1 encoding of the sign.
-//    The power of two and the factor -2 of S = 1 - 2 bit are folded exactly into the
-//    activations of that plane, and the missing "sum of Z over the chunk" term is put
-//    into the accumulator's initial value, so
-//        acc = 2^-17 * (sum_c Z_c - 2 sum_c bit_c Z_c) = 2^-17 * P.
-//  * multi-token kernel (M >= 2): "+-1".  Shift the plane's bits to positions 15/31
-//    and OR in 1.0, giving exact +-1 fp16 elements (unpack cost is amortised over the
-//    token tile there).
+// Signs stay packed at one bit per entry in HBM; the stored tiles keep each 32-column
+// plane's bits at the odd or at the even bit positions of one 16-bit half of a word.
+//  * single-token kernel (M = 1): the contraction runs on the 2:4 structured-sparse MFMA
+//    v_smfmac_f32_16x16x64_f16, used so that the packed sign bits ARE the sparse
+//    indices and no sign is ever expanded to an fp16 value.  Every 4-row group of the B
+//    operand holds two activation columns a, b in both signs and the A operand is all
+//    ones; the group's two index fields pick one row each:
+//        "odd" form  rows [+Z_a, +Z_b, -Z_a, -Z_b]: idx0 = 2 s_a,  idx1 = 2 s_b + 1
+//        "even" form rows [+Z_a, -Z_a, +Z_b, -Z_b]: idx0 = s_a,    idx1 = s_b + 2
+//    (s = 1 for a -1 sign), so the MFMA adds exactly +-Z_a +- Z_b: P = S Z with no
+//    rounding beyond the fp32 accumulation.  A plane's index is the stored word with the
+//    other bits masked off and the two constant index bits ORed in: one v_and_or_b32
+//    serves two planes (the MFMA's abid field picks the half).  The sparse MFMA issues at
+//    the dense rate, so the contraction costs what the dense one does while the unpack
+//    falls from four VALU operations per MFMA to half of one.
+//  * multi-token kernel (M >= 2): dense v_mfma_f32_32x32x16_f16 on exact +-1 fp16 A
+//    fragments (a packed 16-bit shift and one AND-OR per word); there the unpack is
+//    amortised over the token pairs, and the sparse 32x32 MFMA measured slower.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <type_traits>
+#include <utility>
 
 #include "bsl_internal.h"
 
@@ -42,37 +44,50 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Accumulators of the bit-plane path hold 2^-17 times the layer's partial sums.
-constexpr float kPlaneAccScale = 1.0f / 131072.0f;
-constexpr float kPlaneOutScale = 131072.0f;
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
-// Bit position (within each 16-bit half) that plane b occupies after its shift:
-// planes 0-5 come from (w << 6), planes 6-11 from w, planes 12-15 from (w >> 6).
-__host__ __device__ constexpr int plane_pos(int b) { return b < 6 ? b + 6 : (b < 12 ? b : b - 6); }
+// Stored tile layout (16 rows x 512 columns, 1 KiB): lane L = 16 g + i holds row i and,
+// of every 32-column plane b, the columns 8 g .. 8 g + 7, in four little-endian words.
+// Plane b lives in word b / 4, half b % 2, at the odd bit positions if (b / 2) % 2 == 0
+// and at the even ones otherwise: column 8 g + e of the plane is bit 16 (b % 2) + 2 e +
+// 1 - (b / 2) % 2.  A set bit is a -1 sign.
+__host__ __device__ constexpr int plane_word(int b) { return b >> 2; }
+__host__ __device__ constexpr int plane_half(int b) { return b & 1; }
+__host__ __device__ constexpr int plane_even(int b) { return (b >> 1) & 1; }
 
-// fp16 bit pattern of the exact factor -2^(8 - pos) applied to the plane's activations.
-// The A element is 2^(pos - 24) for a set bit, so A * x * factor = -2 * bit * x * 2^-17.
-__host__ __device__ constexpr uint16_t plane_x_factor_bits(int b) {
-  // -2^(8 - pos): pos = 6..11 -> -4, -2, -1, -0.5, -0.25, -0.125
-  return (uint16_t)(0x8000u | (uint16_t)((15 + 8 - plane_pos(b)) << 10));
+// Sparse-MFMA index of the planes kept at the odd (even = false) or even bit positions
+// of stored word w: the planes' bits, plus the constant bit of every 2-bit index field
+// (bit 0 of field 2n + 1 for the odd form, bit 1 of field 2n + 1 for the even form).
+__device__ __forceinline__ uint32_t sign_index(uint32_t w, bool even) {
+  return even ? (w & 0x55555555u) | 0x88888888u : (w & 0xAAAAAAAAu) | 0x44444444u;
 }
-// fp16 bit pattern of 1 / factor = -2^(pos - 8) (to recover Z from the scaled products).
-__host__ __device__ constexpr uint16_t plane_inv_factor_bits(int b) {
-  return (uint16_t)(0x8000u | (uint16_t)((15 + plane_pos(b) - 8) << 10));
+// The same with the masks passed in registers: VOP3 instructions take no literal
+// operands on this target, so with both constants literal the compiler emits an AND and
+// an OR; with the mask in a VGPR it is one v_and_or_b32.
+__device__ __forceinline__ uint32_t sign_index_v(uint32_t w, uint32_t vmask, bool even) {
+  return (w & vmask) | (even ? 0x88888888u : 0x44444444u);
 }
 
-// Order in which the single-token kernel visits the planes: 6-11 straight from the
-// loaded words, 12-15 after rotating them right by 6, 0-5 after rotating by 20 more.
-__host__ __device__ constexpr int plane_order(int s) { return s < 10 ? s + 6 : s - 10; }
-
-// Same factors for a plane index that is only known at run time (wave-uniform).
-__device__ __forceinline__ uint32_t plane_x_factor_bits_dyn(int b) {
-  const int pos = b < 6 ? b + 6 : (b < 12 ? b : b - 6);
-  return 0x8000u | (uint32_t)((23 - pos) << 10);
+// B-operand words of one 4-row group from z = (Z_a, Z_b) (fp16 pair): odd form
+// (Z_a, Z_b), (-Z_a, -Z_b); even form (Z_a, -Z_a), (Z_b, -Z_b).
+// B operands in LDS are stored as [operand][half][lane] 16-byte pieces, so that every
+// ds_read_b128 / ds_write_b128 touches 64 consecutive 16-byte slots (no bank conflicts).
+__device__ __forceinline__ void store_operand(u32x4 (&slot)[2][64], int lane, const u32x8& t) {
+  slot[0][lane] = (u32x4){t[0], t[1], t[2], t[3]};
+  slot[1][lane] = (u32x4){t[4], t[5], t[6], t[7]};
 }
-__device__ __forceinline__ uint32_t plane_inv_factor_bits_dyn(int b) {
-  const int pos = b < 6 ? b + 6 : (b < 12 ? b : b - 6);
-  return 0x8000u | (uint32_t)((7 + pos) << 10);
+__device__ __forceinline__ u32x8 load_operand(const u32x4 (&slot)[2][64], int lane) {
+  const u32x4 a = slot[0][lane], b = slot[1][lane];
+  return (u32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+template <bool EVEN>
+__device__ __forceinline__ u32x2 group_words(uint32_t z) {
+  const uint32_t nz = z ^ 0x80008000u;
+  if (EVEN) return (u32x2){__builtin_amdgcn_perm(nz, z, 0x05040100u),   // (z.lo, -z.lo)
+                           __builtin_amdgcn_perm(nz, z, 0x07060302u)};  // (z.hi, -z.hi)
+  return (u32x2){z, nz};
 }
 
 __device__ __forceinline__ half8 as_half8(u32x4 v) { return __builtin_bit_cast(half8, v); }
@@ -90,6 +105,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
 // Data read exactly once (sign tiles): non-temporal, so it does not evict reused lines.
 __device__ __forceinline__ u32x4 load16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const BSL_GLOBAL u32x4*>(reinterpret_cast<uintptr_t>(p)));
+}
+// Loads at a wave-uniform 64-bit base plus a 32-bit per-lane byte offset (one VGPR per
+// address instead of two: the base stays in scalar registers).
+template <typename T>
+__device__ __forceinline__ T load_at(const void* base, uint32_t off) {
+  return *reinterpret_cast<const BSL_GLOBAL T*>(reinterpret_cast<uintptr_t>(base) + off);
 }
 __device__ __forceinline__ u32x2 load8(const void* p) {
   return *reinterpret_cast<const BSL_GLOBAL u32x2*>(reinterpret_cast<uintptr_t>(p));
@@ -119,23 +140,6 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.u = t->u;
   b.v = t->v;
   return b;
-}
-
-// A fragment of plane b (bit-plane encoding) from a lane's four raw words.
-template <int B>
-__device__ __forceinline__ u32x4 plane_fragment(const u32x4& w, const u32x4& lo, const u32x4& hi) {
-  constexpr uint32_t mask = 0x00010001u << plane_pos(B);
-  const u32x4& src = B < 6 ? lo : (B < 12 ? w : hi);
-  return src & mask;
-}
-
-// A fragment of plane b (+-1 encoding).
-__device__ __forceinline__ u32x4 pm1_fragment(const u32x4& w, int b) {
-  const int s = 15 - b;
-  u32x4 a;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) a[q] = ((w[q] << s) & 0x80008000u) | 0x3C003C00u;
-  return a;
 }
 
 template <int CTRL>
@@ -201,12 +205,14 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 // NW R = 64 row tiles, block, 512-column chunk) in that order; with U units and G
 // workgroups, workgroup L walks units [L U / G, (L + 1) U / G).
 //
-// For every unit the workgroup builds the chunk's Z tile once, in LDS (double buffered;
-// wave w builds planes PP w .. PP w + PP - 1) and each wave runs its R row tiles against
-// it, accumulating the raw products over the chunks of a block in registers.  After a
-// block's last chunk (or the end of the range) the products get the block's column-sum
-// term and are weighted by U (the r-sum is linear, so a block split over two workgroups
-// is fine); after a row group's last unit (or the end of the range) each wave sums its
+// For every unit the workgroup builds the chunk's B operands (+-Z in the odd or even
+// group form of each plane) once, in LDS (double buffered; wave w builds plane w), and
+// each wave runs its R row tiles against them with v_smfmac_f32_16x16x64_f16, the stored
+// sign words of a tile giving the sparse indices of all 16 planes (one v_and_or_b32 per
+// two planes), accumulating P over the chunks of a block in registers.  After a block's
+// last chunk (or the end of the range) P is weighted by U (the r-sum is linear, so a
+// block split over two workgroups is fine); after a row group's last unit (or the end
+// of the range) each wave sums its
 // tiles over r and stores the workgroup's 1024-row "piece" of the row group.  At the end
 // of its range the workgroup counts itself in for every row group it touched; the last
 // workgroup to arrive at a row group adds its pieces in workgroup order and writes y.
@@ -234,10 +240,8 @@ __device__ __forceinline__ uint32_t range_start(uint32_t o, uint32_t units, int 
 
 template <int NW, int R, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_m1_kernel(GroupArgs args) {
-  static_assert(NW * R == kDecodeGroupTiles && kPlanes % NW == 0 && R == 4, "decode tiling");
-  constexpr int PP = kPlanes / NW;       // Z planes each wave builds
-  __shared__ u32x4 zs[2][kPlanes][64];   // Z fragments of two units (32 KiB)
-  __shared__ float csum[2][NW][16];      // per-wave column sums of Z over a block's chunks
+  static_assert(NW * R == kDecodeGroupTiles && NW == kPlanes && R == 4, "decode tiling");
+  __shared__ u32x4 zs[2][kPlanes][2][64];  // B operands (+-Z) of two units (64 KiB)
   __shared__ float4v accl[NW][R][64];    // U-weighted accumulators (LDS, not registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       p.signs = base + ((size_t)c.ch * c.mt + rt0) * kTileBytes;
       p.u = reinterpret_cast<const uint16_t*>(base + sign_bytes) + (size_t)rt0 * 64 * 4;
       p.v = reinterpret_cast<const uint16_t*>(base + sign_bytes + (size_t)c.mt * 64 * 4 * 2) +
-            ((size_t)c.ch * kPlanes + PP * wave) * 64 * 8;
+            ((size_t)c.ch * kPlanes + wave) * 64 * 8;
       p.x = c.x + (size_t)c.ch * kChunkCols;
       p.xcols = c.d - c.ch * kChunkCols;
     } else {
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // wait counts never drain the prefetches.
   u32x4 raw[R], rawn[R];  // sign words of the current and the next unit
   u32x2 uf[R];
-  u32x4 vv[PP], xv[PP];
+  u32x2 vv[2], xv[2];     // this wave's plane: V and x of columns 4 kk .. 4 kk + 3 and 16 + 4 kk ..
   auto load_signs = [&](const UnitPtrs& p, u32x4* rw) {
 #pragma unroll
     for (int t = 0; t < R; ++t) rw[t] = load16_stream(p.signs + t * kTileBytes + lane * 16);
@@ -364,42 +368,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
     for (int t = 0; t < R; ++t) uf[t] = load8(p.u + (t * 64 + lane) * 4);
   };
+  // Lane (r, kk) = (lane % 16, lane / 16) of the B operand of plane b holds the groups
+  // 2 kk, 2 kk + 1, 8 + 2 kk, 9 + 2 kk, i.e. the plane's columns 4 kk .. 4 kk + 3 and
+  // 16 + 4 kk .. 16 + 4 kk + 3 (group G <-> columns 2 G, 2 G + 1); in the stored V tile
+  // those are the halves kk % 2 of lanes 16 (kk / 2) + r and 16 (2 + kk / 2) + r.
+  const int kk = lane >> 4;
   auto load_vx = [&](const UnitPtrs& p) {
 #pragma unroll
-    for (int q = 0; q < PP; ++q) {
-      vv[q] = load16(p.v + (q * 64 + lane) * 8);
-      const int col = 32 * (PP * wave + q) + 8 * g;
-      xv[q] = load16(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
+    for (int hpart = 0; hpart < 2; ++hpart) {
+      vv[hpart] = load8(p.v + (16 * (2 * hpart + (kk >> 1)) + r16) * 8 + 4 * (kk & 1));
+      const int col = 32 * wave + 16 * hpart + 4 * kk;
+      xv[hpart] = load8(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
     }
   };
-  // Z fragments of this wave's PP planes (V times the plane-scaled activations).  Their
-  // column sums over the chunk are added up over the block's chunks; the total goes to
-  // LDS with the block's last chunk (parity `wpar` alternates per block).
-  float cs_run = 0.f;
-  int wpar = 0, rpar = 0;
-  auto build_z = [&](int buf, const DecodeCursor& c) {
-    float cs = 0.f;
+  // B operand of this wave's plane: Z = V x (fp16 products, as the layer defines Z)
+  // in the plane's group form, both signs of every column.
+  auto build_z = [&](int buf) {
+    uint32_t z[4];
 #pragma unroll
-    for (int q = 0; q < PP; ++q) {
-      const int b = PP * wave + q;
-      const half2v f = as_half2(plane_x_factor_bits_dyn(b) * 0x00010001u);
-      const half2v inv = as_half2(plane_inv_factor_bits_dyn(b) * 0x00010001u);
-      u32x4 z;
+    for (int hpart = 0; hpart < 2; ++hpart)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) z[2 * hpart + k] = as_u32(as_half2(vv[hpart][k]) * as_half2(xv[hpart][k]));
+    u32x8 t;
+    if (plane_even(wave)) {  // (wave-uniform branch)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const half2v zq = as_half2(vv[q][k]) * (as_half2(xv[q][k]) * f);
-        z[k] = as_u32(zq);
-        cs = __builtin_amdgcn_fdot2(zq, inv, cs, false);
+        const u32x2 g2 = group_words<true>(z[k]);
+        t[2 * k] = g2[0];
+        t[2 * k + 1] = g2[1];
       }
-      zs[buf][b][lane] = z;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x2 g2 = group_words<false>(z[k]);
+        t[2 * k] = g2[0];
+        t[2 * k + 1] = g2[1];
+      }
     }
-    cs_run += sum_over_lane_groups(cs);
-    if (c.valid && block_end(c)) {
-      // the sums are replicated in the four 16-lane groups; every lane stores its r's
-      csum[wpar][wave][r16] = cs_run;
-      cs_run = 0.f;
-      wpar ^= 1;
-    }
+    store_operand(zs[buf][wave], lane, t);
   };
 
   float4v acc[R];
@@ -408,21 +414,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
     accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
   }
-  // After a block: U-weight the products (plus the block's column-sum term) into LDS.
+  // After a block: U-weight the products into LDS.
   auto weight_block = [&]() {
-    float cs_tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) cs_tot += csum[rpar][w][r16];
-    cs_tot *= kPlaneAccScale;
-    rpar ^= 1;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       const half2v u01 = as_half2(uf[k][0]), u23 = as_half2(uf[k][1]);
       float4v a = accl[wave][k][lane];
-      a[0] += (float)u01[0] * (acc[k][0] + cs_tot);
-      a[1] += (float)u01[1] * (acc[k][1] + cs_tot);
-      a[2] += (float)u23[0] * (acc[k][2] + cs_tot);
-      a[3] += (float)u23[1] * (acc[k][3] + cs_tot);
+      a[0] += (float)u01[0] * acc[k][0];
+      a[1] += (float)u01[1] * acc[k][1];
+      a[2] += (float)u23[0] * acc[k][2];
+      a[3] += (float)u23[1] * acc[k][3];
       accl[wave][k][lane] = a;
       acc[k] = (float4v){0.f, 0.f, 0.f, 0.f};
     }
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  build_z(0, c0);  // (waits only for the first unit's V fragments and activations)
+  build_z(0);  // (waits only for the first unit's V fragments and activations)
   __builtin_amdgcn_sched_barrier(0);
   load_signs(p1, rawn);
   load_vx(p1);
@@ -473,47 +474,63 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // and activations in vv / xv.  Unit c2's signs are fetched into `cur` as soon as the
   // tiles are done with it, so a sign tile is requested well over one unit ahead.
   auto step = [&](u32x4 (&cur)[R], const int buf) {
-    lds_barrier();  // Z of c0 (and the column sums of a finished block) are complete
+    lds_barrier();  // the B operands of c0 are complete; zs[buf ^ 1] (unit c - 1) is free
+    // Unit c1's B operands, the next V / x loads and the cursor advance: waves 8-15 do
+    // them before their tiles and waves 0-7 after, so on every SIMD two waves keep the
+    // matrix cores busy while the other two do this work.
+    DecodeCursor c3;
+    UnitPtrs p3;
+    auto prework = [&]() {
+      build_z(buf ^ 1);
+      load_vx(p2);
+      c3 = next(c2);
+      p3 = unit_ptrs(c3);
+    };
+    const bool early = wave >= 8;  // (uniform)
+    if (early) prework();
+    __builtin_amdgcn_sched_barrier(0);
     {
-      // Row tiles: four independent accumulator chains per plane.  Planes 6-11 are read
-      // from the words as loaded; the words are then rotated right by 6 in place (planes
-      // 12-15 land on bits 6-9) and by 20 more (planes 0-5 land on bits 6-11), so no
-      // second copy of the words is kept.  Z fragments are read from LDS one plane ahead.
-      u32x4 zf[2];
-      zf[0] = zs[buf][plane_order(0)][lane];
-      // (a scheduling barrier per plane keeps the compiler from computing fragments of
-      // later planes early, which would raise register pressure past two waves/SIMD)
-#define BSL_PLANE(S)                                                                                              \
-  __builtin_amdgcn_sched_barrier(0);                                                                              \
-  if ((S) + 1 < kPlanes) zf[((S) + 1) % 2] = zs[buf][plane_order((S) + 1)][lane];                              \
-  _Pragma("unroll") for (int k = 0; k < R; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(                \
-      as_half8(cur[k] & (0x00010001u << plane_pos(plane_order(S)))), as_half8(zf[(S) % 2]), acc[k], 0, 0, 0);
-#define BSL_ROTATE(N)                                                                                             \
-  _Pragma("unroll") for (int k = 0; k < R; ++k) _Pragma("unroll") for (int q = 0; q < 4; ++q) cur[k][q] =      \
-      __builtin_amdgcn_alignbit(cur[k][q], cur[k][q], (N));
-      BSL_PLANE(0) BSL_PLANE(1) BSL_PLANE(2) BSL_PLANE(3) BSL_PLANE(4) BSL_PLANE(5)
-      BSL_ROTATE(6)
-      BSL_PLANE(6) BSL_PLANE(7) BSL_PLANE(8) BSL_PLANE(9)
-      BSL_ROTATE(20)
-      BSL_PLANE(10) BSL_PLANE(11) BSL_PLANE(12) BSL_PLANE(13) BSL_PLANE(14) BSL_PLANE(15)
-#undef BSL_ROTATE
+      // Row tiles: four independent accumulator chains per plane.  Word q of a tile's
+      // stored signs gives the indices of planes 4 q .. 4 q + 3 (odd-position planes
+      // 4 q, 4 q + 1, even-position planes 4 q + 2, 4 q + 3; abid picks the half); the B
+      // operand of the next plane is read from LDS while the current one runs.
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      u32x8 zf[2];
+      zf[0] = load_operand(zs[buf][0], lane);
+      uint32_t ix[2][R];
+      uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
+      asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs)
+      // (a scheduling barrier per plane keeps the compiler from hoisting later planes'
+      // work, which would raise register pressure past four waves per SIMD)
+#define BSL_PLANE(B)                                                                                           \
+  __builtin_amdgcn_sched_barrier(0);                                                                           \
+  if ((B) % 4 == 0) {                                                                                          \
+    _Pragma("unroll") for (int k = 0; k < R; ++k) {                                                            \
+      ix[0][k] = sign_index_v(cur[k][plane_word(B)], m_odd, false);                                            \
+      ix[1][k] = sign_index_v(cur[k][plane_word(B)], m_even, true);                                            \
+    }                                                                                                          \
+  }                                                                                                            \
+  if ((B) + 1 < kPlanes) zf[((B) + 1) % 2] = load_operand(zs[buf][(B) + 1], lane);                          \
+  _Pragma("unroll") for (int k = 0; k < R; ++k) acc[k] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(           \
+      ones, __builtin_bit_cast(half16, zf[(B) % 2]), acc[k], (int)ix[plane_even(B)][k], 0, plane_half(B));
+      BSL_PLANE(0) BSL_PLANE(1) BSL_PLANE(2) BSL_PLANE(3) BSL_PLANE(4) BSL_PLANE(5) BSL_PLANE(6) BSL_PLANE(7)
+      BSL_PLANE(8) BSL_PLANE(9) BSL_PLANE(10) BSL_PLANE(11) BSL_PLANE(12) BSL_PLANE(13) BSL_PLANE(14) BSL_PLANE(15)
 #undef BSL_PLANE
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!early) prework();
     __builtin_amdgcn_sched_barrier(0);
     load_signs(p2, cur);
     __builtin_amdgcn_sched_barrier(0);
     if (block_end(c0)) weight_block();
     __builtin_amdgcn_sched_barrier(0);
-    build_z(buf ^ 1, c1);
-    __builtin_amdgcn_sched_barrier(0);
     if (group_end(c0)) store_piece(c0);
-    load_vx(p2);
     load_u(p1);
     c0 = c1;
     c1 = c2;
+    c2 = c3;
     p1 = p2;
-    c2 = next(c2);
-    p2 = unit_ptrs(c2);
+    p2 = p3;
   };
 
   const uint32_t n = u_end - u_begin;
@@ -585,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         for (int q = 0; q < 32; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
       }
       const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + tid;
-      if (row < W.m) store_y(W.y, row, acc_y * kPlaneOutScale, args.y_fp32);
+      if (row < W.m) store_y(W.y, row, acc_y, args.y_fp32);
     }
     __syncthreads();  // n_last and last_items are rewritten by the next batch
   }
@@ -596,9 +613,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // range of the (block, chunk) sequence), T = 2, 4 or 8; wave w owns rows 64 w .. 64 w + 63
 // as two 32-row fragments against the T tokens as T / 2 token pairs, i.e. 2 x T / 2
 // accumulators of v_mfma_f32_32x32x16_f16 (32 rows x (2 tokens x 16 r)): the N width
-// 2 x 16 = 32 is filled exactly, and each +-1 A fragment feeds T / 2 MFMAs.  Z is built
-// 4 planes (128 columns) at a time into double-buffered LDS as B fragments; sign words
-// for the next chunk and V / activations for the next 4 planes are fetched while the
+// 2 x 16 = 32 is filled exactly, and each +-1 A fragment feeds T / 2 MFMAs.  Here the
+// dense MFMA is used: measured on MI355X inside this kernel the 32x32 sparse MFMA runs
+// about 13% slower than the dense one, while the unpack is cheap (the A fragment of a
+// plane is two VALU operations per word, see pm1_fragment).  Z is built 4 planes (one
+// stored word, 128 columns) at a time into double-buffered LDS as B fragments; the sign
+// words of the next stage and V / activations of the next 4 planes are fetched while the
 // current ones run.  After a block's K loop (or the end of the item's range) the
 // accumulators are weighted by U and summed over r with a 16-lane butterfly.  When a
 // weight has too few items to fill the chip its (block, chunk) sequence is cut into
@@ -609,9 +629,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 // B[8 (l / 32) + e][l % 32], e = 0..7; C[m][n] sits in lane n + 32 ((m / 4) % 2), value
 // 4 (m / 8) + m % 4.  K step s (0, 1) of plane b covers the plane's columns 16 s .. 16 s +
 // 15, which the stored tiles hold in lane group 2 s + l / 32 of row l % 32: a lane loads
-// the 16 stored bytes of that (row, group) and gets every plane of it.
+// word b / 4 of that (row, group) and gets the plane's 8 signs of its A fragment.
 typedef float float16v __attribute__((ext_vector_type(16)));
-constexpr int kPrefillPlanes = 4;  // planes per Z stage
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+constexpr int kPrefillPlanes = 4;  // planes per Z stage (one stored word)
+
+// +-1 fp16 A fragment (8 consecutive columns e = 0..7 of the lane) of plane b from its
+// stored word w: column e is bit 16 h + 2 e + odd (h = b % 2, odd = 1 for the planes at
+// odd positions).  A packed 16-bit shift with per-half amounts moves the bits of columns
+// 2 n and 2 n + 1 to bit 15 of the two halves; masking and ORing in 1.0 gives the pair
+// (one v_pk_lshlrev_b16 and one v_and_or_b32 per word; vmask holds 0x80008000).
+template <int B>
+__device__ __forceinline__ u32x4 pm1_fragment(uint32_t w, uint32_t vmask) {
+  constexpr int H = plane_half(B), ODD = plane_even(B) ? 0 : 1;
+  const unsigned short hw = (unsigned short)(w >> (16 * H));
+  u32x4 a;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const ushort2v sh = {(unsigned short)(15 - 4 * n - ODD), (unsigned short)(13 - 4 * n - ODD)};
+    const ushort2v v = (ushort2v){hw, hw} << sh;
+    a[n] = (__builtin_bit_cast(uint32_t, v) & vmask) | 0x3C003C00u;
+  }
+  return a;
+}
 
 // Sum 16 values over the 16 lanes of a DPP row; lane r ends with the sum of value r.
 // Four butterfly stages (partners r^8, r^7, r^2, r^1) halve the values each time.
@@ -641,7 +681,8 @@ template <int T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(GroupArgs args, int token_groups) {
   constexpr int NP = T / 2, PL = kPrefillPlanes;
   constexpr int FRAGS = PL * 2 * NP;          // B fragments per stage (32 for 8 tokens)
-  constexpr int FPW = FRAGS / 8;              // built per wave
+  constexpr int FPW = FRAGS / 8;              // built per wave (= NP: one (plane, step) per wave)
+  static_assert(FPW == NP, "one (plane, step) per wave");
   __shared__ u32x4 zs[2][FRAGS][64];          // [stage buffer][(plane, step, pair)][lane], 64 KiB for 8 tokens
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -664,38 +705,47 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int u_end = min(units, u_begin + ups);
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
 
-  // sign words: [fragment rf][K step s] = the 16 stored bytes of (row row0 + 32 rf + l % 32,
-  // lane group 2 s + kg) of the current chunk
-  auto load_signs = [&](const BlockPtrs& bp, int ch, u32x4 (&w)[2][2]) {
+  // sign word q of [fragment rf][K step s]: word q of the 16 stored bytes of (row row0 +
+  // 32 rf + l % 32, lane group 2 s + kg) of chunk ch
+  auto load_sign_word = [&](const BlockPtrs& bp, int ch, int q, uint32_t (&w)[2][2]) {
+    const uint8_t* chunk = bp.signs + (size_t)ch * W.mt * kTileBytes;  // (uniform)
 #pragma unroll
     for (int rf = 0; rf < 2; ++rf) {
-      const int row = row0 + 32 * rf + n32;
-      const uint8_t* tile = bp.signs + ((size_t)ch * W.mt + (row >> 4)) * kTileBytes;
+      const uint32_t row = row0 + 32 * rf + n32;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) w[rf][st] = load16(tile + ((row & 15) + 16 * (2 * st + kg)) * 16);
+      for (int st = 0; st < 2; ++st)
+        w[rf][st] = load_at<uint32_t>(chunk, (row >> 4) * kTileBytes + ((row & 15) + 16 * (2 * st + kg)) * 16 + 4 * q);
     }
   };
-  // V fragment and activations of this wave's B fragments of stage (ch, q)
-  auto load_vx = [&](const BlockPtrs& bp, int ch, int q, u32x4 (&vv)[FPW], u32x4 (&xv)[FPW]) {
+  // V fragment and activations of this wave's B fragments of stage (ch, q): wave w builds
+  // (plane pl, step st) = (w / 2, w % 2) for all token pairs; lane (n, kg) needs columns
+  // 16 st + 8 kg + 0..7 of the plane for r = n % 16 (stored V lane 16 (2 st + kg) + r)
+  // and token tok0 + 2 pp + n / 16.  A token past M reads row M - 1 instead (its outputs
+  // are never stored), so only a chunk that runs past column d needs the zero page.
+  const int pl_w = wave >> 1, st_w = wave & 1;
+  const uint16_t* xbase = W.x + (size_t)tok0 * W.d;  // (uniform; tok0 < M)
+  auto xoff = [&](int pp, int col) {
+    return (uint32_t)((min(tok0 + 2 * pp + (n32 >> 4), M - 1) - tok0) * W.d + col) * 2u;
+  };
+  auto load_vx = [&](const BlockPtrs& bp, int ch, int q, u32x4& vv, u32x4 (&xv)[NP]) {
+    const int b = q * PL + pl_w;
+    vv = load_at<u32x4>(bp.v, ((((uint32_t)ch * kPlanes + b) * 64 + (lane & 15) + 16 * (2 * st_w + kg)) * 8) * 2u);
+    const int col = ch * kChunkCols + 32 * b + 16 * st_w + 8 * kg;
+    if ((ch + 1) * kChunkCols <= W.d) {  // (uniform)
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) {
-      const int id = wave * FPW + f;          // (plane pl, step st, pair pp)
-      const int pl = id / (2 * NP), st = (id / NP) % 2, pp = id % NP;
-      const int b = q * PL + pl;
-      vv[f] = load16(bp.v + (((size_t)ch * kPlanes + b) * 64 + (lane & 15) + 16 * (2 * st + kg)) * 8);
-      const int tok = tok0 + 2 * pp + (n32 >> 4);
-      const int col = ch * kChunkCols + 32 * b + 16 * st + 8 * kg;
-      const bool ok = tok < M && col < W.d;
-      xv[f] = load16(ok ? static_cast<const void*>(W.x + (size_t)tok * W.d + col) : static_cast<const void*>(zero_page));
+      for (int pp = 0; pp < NP; ++pp) xv[pp] = load_at<u32x4>(xbase, xoff(pp, col));
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) xv[pp] = col < W.d ? load_at<u32x4>(xbase, xoff(pp, col)) : load_at<u32x4>(zero_page, 0);
     }
   };
-  auto build = [&](int buf, const u32x4 (&vv)[FPW], const u32x4 (&xv)[FPW]) {
+  auto build = [&](int buf, const u32x4& vv, const u32x4 (&xv)[NP]) {
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) {
+    for (int pp = 0; pp < NP; ++pp) {
       u32x4 z;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = as_u32(as_half2(vv[f][e]) * as_half2(xv[f][e]));
-      zs[buf][wave * FPW + f][lane] = z;
+      for (int e = 0; e < 4; ++e) z[e] = as_u32(as_half2(vv[e]) * as_half2(xv[pp][e]));
+      zs[buf][wave * NP + pp][lane] = z;
     }
   };
 
@@ -705,50 +755,56 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp) yacc[rf][pp] = 0.f;
 
-  const int stages = (u_end - u_begin) * (kPlanes / PL);
-  if (stages > 0) {
-    u32x4 w[2][2], wn[2][2];
-    u32x4 vv[FPW], xv[FPW];
+  if (u_end > u_begin) {
+    uint32_t vmask = 0x80008000u;
+    asm volatile("" : "+v"(vmask));  // (a VGPR operand, so that AND and OR fuse into v_and_or_b32)
+    uint32_t sw[2][2][2];            // sign words of this stage and the next: [stage parity][rf][st]
+    u32x4 vv, xv[NP];
     float16v acc[2][NP];
 #pragma unroll
     for (int rf = 0; rf < 2; ++rf)
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) acc[rf][pp] = (float16v){};
-    int i = u_begin / nch, ch = u_begin % nch, q = 0;  // current stage
+    int i = u_begin / nch, ch = u_begin % nch;  // current unit (block, chunk)
     BlockPtrs bp = load_block(W.blocks, i);
-    load_signs(bp, ch, w);
+    load_sign_word(bp, ch, 0, sw[0]);
     load_vx(bp, ch, 0, vv, xv);
     build(0, vv, xv);
-    for (int sidx = 0; sidx < stages; ++sidx) {
-      const int buf = sidx & 1;
-      // next stage
-      int ni = i, nc = ch, nq = q + 1;
-      if (nq == kPlanes / PL) { nq = 0; if (++nc == nch) { nc = 0; ++ni; } }
-      const bool more = sidx + 1 < stages;
+    for (int u = u_begin; u < u_end; ++u) {
+      int ni = i, nc = ch + 1;
+      if (nc == nch) { nc = 0; ++ni; }
+      const bool more = u + 1 < u_end;
       const BlockPtrs nbp = load_block(W.blocks, more ? ni : i);
-      lds_barrier();  // Z of this stage is in zs[buf]; zs[buf ^ 1] is free
-      if (nq == 0 && more) load_signs(nbp, nc, wn);
-      load_vx(more ? nbp : bp, more ? nc : ch, more ? nq : q, vv, xv);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int pl = 0; pl < PL; ++pl) {
-        const int b = q * PL + pl;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const half8 a0 = as_half8(pm1_fragment(w[0][st], b));
-          const half8 a1 = as_half8(pm1_fragment(w[1][st], b));
-#pragma unroll
-          for (int pp = 0; pp < NP; ++pp) {
-            const half8 bf = as_half8(zs[buf][(pl * 2 + st) * NP + pp][lane]);
-            acc[0][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bf, acc[0][pp], 0, 0, 0);
-            acc[1][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bf, acc[1][pp], 0, 0, 0);
-          }
+      for (int q = 0; q < 4; ++q) {  // stage = stored word q of the chunk: planes 4 q .. 4 q + 3
+        const int buf = q & 1;
+        lds_barrier();  // the B fragments of this stage are in zs[buf]; zs[buf ^ 1] is free
+        if (q < 3) {
+          load_sign_word(bp, ch, q + 1, sw[(q + 1) & 1]);
+          load_vx(bp, ch, q + 1, vv, xv);
+        } else if (more) {
+          load_sign_word(nbp, nc, 0, sw[0]);
+          load_vx(nbp, nc, 0, vv, xv);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#define BSL_PREFILL_PLANE(PLN)                                                                              \
+  _Pragma("unroll") for (int st = 0; st < 2; ++st) {                                                        \
+    const half8 a0 = as_half8(pm1_fragment<PLN>(sw[q & 1][0][st], vmask));                                  \
+    const half8 a1 = as_half8(pm1_fragment<PLN>(sw[q & 1][1][st], vmask));                                  \
+    _Pragma("unroll") for (int pp = 0; pp < NP; ++pp) {                                                     \
+      const half8 bf = as_half8(zs[buf][((PLN) * 2 + st) * NP + pp][lane]);                                 \
+      acc[0][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, bf, acc[0][pp], 0, 0, 0);                     \
+      acc[1][pp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, bf, acc[1][pp], 0, 0, 0);                     \
+    }                                                                                                       \
+  }
+        // (the fragment of plane 4 q + pl depends on pl only: word q is the stage's word)
+        BSL_PREFILL_PLANE(0) BSL_PREFILL_PLANE(1) BSL_PREFILL_PLANE(2) BSL_PREFILL_PLANE(3)
+#undef BSL_PREFILL_PLANE
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < 3 || more) build(buf ^ 1, vv, xv);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) build(buf ^ 1, vv, xv);
-      // after a block's last stage, or the range's: U weighting and the sum over r
-      if ((nq == 0 && nc == 0) || !more) {
+      // after a block's last chunk, or the range's: U weighting and the sum over r
+      if (nc == 0 || !more) {
 #pragma unroll
         for (int rf = 0; rf < 2; ++rf) {
           // U[row(v)][r] for v = 0..15: rows 8 (v / 4) + 4 kg + v % 4 of the fragment
@@ -757,9 +813,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
           for (int vg = 0; vg < 4; ++vg) {
             const int tile = (rbase >> 4) + (vg >> 1);
-            const u32x2 u = load8(bp.u + ((size_t)tile * 64 + (lane & 15) + 16 * (2 * (vg & 1) + kg)) * 4);
-            uu[2 * vg] = as_half2(u[0]);
-            uu[2 * vg + 1] = as_half2(u[1]);
+            const u32x2 uw = load8(bp.u + ((size_t)tile * 64 + (lane & 15) + 16 * (2 * (vg & 1) + kg)) * 4);
+            uu[2 * vg] = as_half2(uw[0]);
+            uu[2 * vg + 1] = as_half2(uw[1]);
           }
 #pragma unroll
           for (int pp = 0; pp < NP; ++pp) {
@@ -771,16 +827,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         }
       }
-      if (nq == 0 && more) {
-#pragma unroll
-        for (int rf = 0; rf < 2; ++rf)
-#pragma unroll
-          for (int st = 0; st < 2; ++st) w[rf][st] = wn[rf][st];
-      }
       bp = nbp;
       i = ni;
       ch = nc;
-      q = nq;
     }
   }
   // lane l holds, for each (fragment, pair), row 8 (v / 4) + 4 kg + v % 4 with v = l % 16,
@@ -832,52 +881,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ============================================================ debug unpack
-// One wave per sign tile: unpack exactly as the forward kernels do and write +-1.
+// One wave per sign tile: unpack exactly as the forward kernels do and write the signs.
+// Path 0: the single-token kernel's sparse indices (odd form: field 2 s + j, even form:
+// field s + 2 j for slot j of a group; s = 1 for a -1 sign).  Path 1: the multi-token
+// kernel's +-1 fp16 A fragments.  Lane group g holds columns 8 g .. 8 g + 7 of each plane.
+template <int B>
+__device__ __forceinline__ void debug_plane(const u32x4& w, int path, int g, int ch, int row, int32_t d, int8_t* out) {
+  int8_t sg[8];
+  if (path == 0) {
+    const uint32_t half = (sign_index(w[plane_word(B)], plane_even(B)) >> (16 * plane_half(B))) & 0xFFFFu;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t field = (half >> (2 * e)) & 3u;
+      const uint32_t neg = plane_even(B) ? (field & 1u) : (field >> 1);
+      sg[e] = neg ? -1 : 1;
+    }
+  } else {
+    const half8 h = as_half8(pm1_fragment<B>(w[plane_word(B)], 0x80008000u));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = (float)h[e] < 0.f ? -1 : 1;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int col = ch * kChunkCols + 32 * B + 8 * g + e;
+    if (col < d) out[(size_t)row * d + col] = sg[e];
+  }
+}
+template <int... Bs>
+__device__ __forceinline__ void debug_planes(std::integer_sequence<int, Bs...>, const u32x4& w, int path, int g, int ch,
+                                             int row, int32_t d, int8_t* out) {
+  (debug_plane<Bs>(w, path, g, ch, row, d, out), ...);
+}
 __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int path,
                                                           int8_t* out) {
   const int lane = threadIdx.x;
   const int tile = blockIdx.x;
   const int ch = tile / mt, rt = tile % mt;
   const u32x4 w = load16(blk.signs + (size_t)tile * kTileBytes + lane * 16);
-  const u32x4 lo = w << 6u, hi = w >> 6u;
   const int row = rt * kTileRows + (lane & 15);
-  const int g = lane >> 4;
-  u32x4 fr[kPlanes];
-  if (path == 0) {
-    fr[0] = plane_fragment<0>(w, lo, hi);
-    fr[1] = plane_fragment<1>(w, lo, hi);
-    fr[2] = plane_fragment<2>(w, lo, hi);
-    fr[3] = plane_fragment<3>(w, lo, hi);
-    fr[4] = plane_fragment<4>(w, lo, hi);
-    fr[5] = plane_fragment<5>(w, lo, hi);
-    fr[6] = plane_fragment<6>(w, lo, hi);
-    fr[7] = plane_fragment<7>(w, lo, hi);
-    fr[8] = plane_fragment<8>(w, lo, hi);
-    fr[9] = plane_fragment<9>(w, lo, hi);
-    fr[10] = plane_fragment<10>(w, lo, hi);
-    fr[11] = plane_fragment<11>(w, lo, hi);
-    fr[12] = plane_fragment<12>(w, lo, hi);
-    fr[13] = plane_fragment<13>(w, lo, hi);
-    fr[14] = plane_fragment<14>(w, lo, hi);
-    fr[15] = plane_fragment<15>(w, lo, hi);
-  } else {
-#pragma unroll
-    for (int b = 0; b < kPlanes; ++b) fr[b] = pm1_fragment(w, b);
-  }
   if (row >= m) return;
-#pragma unroll
-  for (int b = 0; b < kPlanes; ++b) {
-    const half8 h = as_half8(fr[b]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = ch * kChunkCols + 32 * b + 8 * g + j;
-      if (col < d) {
-        // bit-plane path: a set bit is a non-zero element and means -1; +-1 path: the value itself
-        const float v = (float)h[j];
-        out[(size_t)row * d + col] = path == 0 ? (v != 0.f ? -1 : 1) : (v < 0.f ? -1 : 1);
-      }
-    }
-  }
+  debug_planes(std::make_integer_sequence<int, kPlanes>{}, w, path, lane >> 4, ch, row, d, out);
 }
 
 // ============================================================ launchers

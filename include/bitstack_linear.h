@@ -81,9 +81,12 @@ size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
  * into the tiled device layout.  tiled_out (host) must hold bsl_packed_sign_bytes(m, d)
  * bytes.  Layout: tiles of 16 rows x 512 columns, ordered [column chunk][row tile];
  * each tile is 64 lanes x 16 bytes; lane L = 16*g + i holds row i of the tile and four
- * little-endian 32-bit words q = 0..3, where bit p of word q is the sign of column
- * 32*(p % 16) + 8*g + 2*q + (p / 16) of the chunk.  One 16-byte load per lane fetches
- * a whole tile (1 KiB, eight full 128-byte lines). */
+ * little-endian 32-bit words q = 0..3.  Of the chunk's 32-column plane b = 4*q + k
+ * (k = 0..3), the lane keeps columns 32*b + 8*g + e (e = 0..7) in word q at bit
+ * 16*(k % 2) + 2*e + 1 when k < 2 and at bit 16*(k % 2) + 2*e when k >= 2.  Each plane
+ * thereby sits at the odd or the even positions of one 16-bit half, which is the form
+ * the forward kernels use directly as 2:4 sparse-MFMA indices.  One 16-byte load per
+ * lane fetches a whole tile (1 KiB, eight full 128-byte lines). */
 int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* tiled_out);
 
 /* Inverse of bsl_pack_signs, for checking: writes int8 +1/-1 into pm1_out (host,
@@ -133,8 +136,8 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
 
 /* Run a forward kernel's own sign-unpack code on block i of weight w and write the
  * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes).
- * path 0: the single-token kernel's bit-plane masks; path 1: the multi-token
- * kernel's +-1 fp16 conversion. */
+ * path 0: the single-token kernel's sparse-MFMA indices; path 1: the multi-token
+ * kernel's +-1 fp16 A fragments. */
 int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream);
 
 /* Message for the calling thread's last failure ("" if none). */

@@ -54,9 +54,10 @@ def test_block_bytes_printed_value():
 
 def _expected_tiled(bits, m, d):
     """The documented layout, written out independently of the library: tiles ordered
-    [column chunk c][row tile t], rows padded to 1024; bit p of word q of lane 16 g + i
-    in tile (c, t) is the sign of row 16 t + i, column 512 c + 32 (p % 16) + 8 g + 2 q
-    + p // 16 (padding reads as +1, i.e. bit 0)."""
+    [column chunk c][row tile t], rows padded to 1024; in tile (c, t), bit p of word q of
+    lane 16 g + i is the sign of row 16 t + i, column 512 c + 32 b + 8 g + e with
+    e = (p % 16) // 2, b = 4 q + k, k = p // 16 + (0 if p is odd else 2) (padding reads
+    as +1, i.e. bit 0)."""
     signs_neg = np.unpackbits(bits, axis=1, bitorder="little")[:, :d].astype(np.uint8)
     mp = -(-m // 1024) * 1024  # rows padded to 1024
     dp = -(-d // 512) * 512
@@ -65,9 +66,11 @@ def _expected_tiled(bits, m, d):
     nch = dp // 512
     out = np.zeros((nch, mp // 16, 64, 4), np.uint32)  # [chunk][row tile][lane][word]
     p = np.arange(32)
+    k = p // 16 + np.where(p % 2 == 1, 0, 2)
+    e = (p % 16) // 2
     for g in range(4):
         for q in range(4):
-            cols = 32 * (p % 16) + 8 * g + 2 * q + p // 16
+            cols = 32 * (4 * q + k) + 8 * g + e
             for c in range(nch):
                 blk = full[:, 512 * c + cols].reshape(mp // 16, 16, 32).astype(np.uint64)
                 words = (blk << p.astype(np.uint64)).sum(axis=2).astype(np.uint32)

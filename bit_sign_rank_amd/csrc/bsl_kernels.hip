@@ -240,7 +240,8 @@ __device__ __forceinline__ uint32_t range_start(uint32_t o, uint32_t units, int 
 
 template <int NW, int R, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_m1_kernel(GroupArgs args) {
-  static_assert(NW * R == kDecodeGroupTiles && NW == kPlanes && R == 4, "decode tiling");
+  static_assert(NW * R == kDecodeGroupTiles && kPlanes % NW == 0 && NW % 2 == 0, "decode tiling");
+  constexpr int PP = kPlanes / NW;       // B operands (planes) each wave builds
   __shared__ u32x4 zs[2][kPlanes][2][64];  // B operands (+-Z) of two units (64 KiB)
   __shared__ float4v accl[NW][R][64];    // U-weighted accumulators (LDS, not registers)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       p.signs = base + ((size_t)c.ch * c.mt + rt0) * kTileBytes;
       p.u = reinterpret_cast<const uint16_t*>(base + sign_bytes) + (size_t)rt0 * 64 * 4;
       p.v = reinterpret_cast<const uint16_t*>(base + sign_bytes + (size_t)c.mt * 64 * 4 * 2) +
-            ((size_t)c.ch * kPlanes + wave) * 64 * 8;
+            ((size_t)c.ch * kPlanes + PP * wave) * 64 * 8;
       p.x = c.x + (size_t)c.ch * kChunkCols;
       p.xcols = c.d - c.ch * kChunkCols;
     } else {
@@ -359,7 +360,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // wait counts never drain the prefetches.
   u32x4 raw[R], rawn[R];  // sign words of the current and the next unit
   u32x2 uf[R];
-  u32x2 vv[2], xv[2];     // this wave's plane: V and x of columns 4 kk .. 4 kk + 3 and 16 + 4 kk ..
+  // This wave's planes: V and x of columns 4 kk .. 4 kk + 3 and 16 + 4 kk ..; the waves
+  // that build after their tiles keep them in their own registers (see step).
+  struct VX {
+    u32x2 v[PP][2], x[PP][2];
+  } vx_early, vx_late;
   auto load_signs = [&](const UnitPtrs& p, u32x4* rw) {
 #pragma unroll
     for (int t = 0; t < R; ++t) rw[t] = load16_stream(p.signs + t * kTileBytes + lane * 16);
@@ -373,24 +378,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // 16 + 4 kk .. 16 + 4 kk + 3 (group G <-> columns 2 G, 2 G + 1); in the stored V tile
   // those are the halves kk % 2 of lanes 16 (kk / 2) + r and 16 (2 + kk / 2) + r.
   const int kk = lane >> 4;
-  auto load_vx = [&](const UnitPtrs& p) {
+  auto load_vx = [&](const UnitPtrs& p, VX& d) {
 #pragma unroll
-    for (int hpart = 0; hpart < 2; ++hpart) {
-      vv[hpart] = load8(p.v + (16 * (2 * hpart + (kk >> 1)) + r16) * 8 + 4 * (kk & 1));
-      const int col = 32 * wave + 16 * hpart + 4 * kk;
-      xv[hpart] = load8(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
-    }
+    for (int pp = 0; pp < PP; ++pp)
+#pragma unroll
+      for (int hpart = 0; hpart < 2; ++hpart) {
+        d.v[pp][hpart] = load8(p.v + (pp * 64 + 16 * (2 * hpart + (kk >> 1)) + r16) * 8 + 4 * (kk & 1));
+        const int col = 32 * (PP * wave + pp) + 16 * hpart + 4 * kk;
+        d.x[pp][hpart] = load8(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
+      }
   };
   // B operand of this wave's plane: Z = V x (fp16 products, as the layer defines Z)
   // in the plane's group form, both signs of every column.
-  auto build_z = [&](int buf) {
+  auto build_z = [&](int buf, const VX& d) {
+#pragma unroll
+    for (int pp = 0; pp < PP; ++pp) {
+    const int b = PP * wave + pp;
     uint32_t z[4];
 #pragma unroll
     for (int hpart = 0; hpart < 2; ++hpart)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) z[2 * hpart + k] = as_u32(as_half2(vv[hpart][k]) * as_half2(xv[hpart][k]));
+      for (int k = 0; k < 2; ++k) z[2 * hpart + k] = as_u32(as_half2(d.v[pp][hpart][k]) * as_half2(d.x[pp][hpart][k]));
     u32x8 t;
-    if (plane_even(wave)) {  // (wave-uniform branch)
+    if (plane_even(b)) {  // (wave-uniform branch)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x2 g2 = group_words<true>(z[k]);
@@ -405,7 +415,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         t[2 * k + 1] = g2[1];
       }
     }
-    store_operand(zs[buf][wave], lane, t);
+    store_operand(zs[buf][b], lane, t);
+    }
   };
 
   float4v acc[R];
@@ -451,7 +462,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const UnitPtrs p0 = unit_ptrs(c0, true);
   UnitPtrs p1 = unit_ptrs(c1, true);
   UnitPtrs p2 = unit_ptrs(c2, true);
-  load_vx(p0);
+  load_vx(p0, vx_early);
   load_signs(p0, raw);
   __builtin_amdgcn_sched_barrier(0);
   {
@@ -463,10 +474,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  build_z(0);  // (waits only for the first unit's V fragments and activations)
+  build_z(0, vx_early);  // (waits only for the first unit's V fragments and activations)
   __builtin_amdgcn_sched_barrier(0);
   load_signs(p1, rawn);
-  load_vx(p1);
+  if (wave >= NW / 2) load_vx(p1, vx_early);
+  else load_vx(p1, vx_late);
   load_u(p0);
 
   // ---- one unit.  On entry unit c0's signs are in `cur` and unit c1's in the other
@@ -475,19 +487,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // tiles are done with it, so a sign tile is requested well over one unit ahead.
   auto step = [&](u32x4 (&cur)[R], const int buf) {
     lds_barrier();  // the B operands of c0 are complete; zs[buf ^ 1] (unit c - 1) is free
-    // Unit c1's B operands, the next V / x loads and the cursor advance: waves 8-15 do
-    // them before their tiles and waves 0-7 after, so on every SIMD two waves keep the
-    // matrix cores busy while the other two do this work.
+    // Unit c1's B operands, the next V / x loads and the cursor advance: the upper half
+    // of the waves does them before its tiles and the lower half after, so on every SIMD
+    // some waves keep the matrix cores busy while the others do this work.
     DecodeCursor c3;
     UnitPtrs p3;
-    auto prework = [&]() {
-      build_z(buf ^ 1);
-      load_vx(p2);
+    // (each half uses its own V / x registers: with one set, the compiler's load wait
+    // before the build after the tiles would also cover the loads the other placement
+    // may have issued, i.e. the sign loads just sent to HBM)
+    auto prework = [&](VX& d) {
+      build_z(buf ^ 1, d);
+      load_vx(p2, d);
       c3 = next(c2);
       p3 = unit_ptrs(c3);
     };
-    const bool early = wave >= 8;  // (uniform)
-    if (early) prework();
+    const bool early = wave >= NW / 2;  // (uniform)
+    if (early) prework(vx_early);
     __builtin_amdgcn_sched_barrier(0);
     {
       // Row tiles: four independent accumulator chains per plane.  Word q of a tile's
@@ -518,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #undef BSL_PLANE
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (!early) prework();
+    if (!early) prework(vx_late);
     __builtin_amdgcn_sched_barrier(0);
     load_signs(p2, cur);
     __builtin_amdgcn_sched_barrier(0);
@@ -568,8 +583,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t item_last = args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's piece stores have completed
   __syncthreads();
-  // row groups of the range, 512 at a time: one thread each counts the workgroup in
-  for (uint32_t k0 = 0; k0 <= item_last - item_first; k0 += kDecodeGroupRows) {
+  // row groups of the range, NW * 64 at a time: one thread each counts the workgroup in
+  for (uint32_t k0 = 0; k0 <= item_last - item_first; k0 += NW * 64) {
     if (tid == 0) n_last = 0;
     __syncthreads();
     if (k0 + tid <= item_last - item_first) {
@@ -591,18 +606,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const int j = group_units(item, first, last);
       const WeightDesc& W = args.w[j];
       const uint32_t o0 = owner(first), o1 = owner(last);
-      const float* base = args.pieces + (size_t)item * kDecodeGroupRows + tid;
-      float acc_y = 0.f;
-      for (uint32_t o = o0; o <= o1; o += 32) {  // (32 loads in flight per round trip)
-        float v[32];
+      for (uint32_t rr = tid; rr < (uint32_t)kDecodeGroupRows; rr += NW * 64) {
+        const float* base = args.pieces + (size_t)item * kDecodeGroupRows + rr;
+        float acc_y = 0.f;
+        for (uint32_t o = o0; o <= o1; o += 32) {  // (32 loads in flight per round trip)
+          float v[32];
 #pragma unroll
-        for (int q = 0; q < 32; ++q)
-          v[q] = __hip_atomic_load(base + (size_t)min(o + q, o1) * kDecodeGroupRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int q = 0; q < 32; ++q)
+            v[q] = __hip_atomic_load(base + (size_t)min(o + q, o1) * kDecodeGroupRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-        for (int q = 0; q < 32; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
+          for (int q = 0; q < 32; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
+        }
+        const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + rr;
+        if (row < W.m) store_y(W.y, row, acc_y, args.y_fp32);
       }
-      const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + tid;
-      if (row < W.m) store_y(W.y, row, acc_y, args.y_fp32);
     }
     __syncthreads();  // n_last and last_items are rewritten by the next batch
   }
@@ -929,8 +946,8 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
   // 16 waves x 4 row tiles, 4 waves per SIMD (one workgroup per CU: all waves advance
   // together, so no workgroup is left running alone on a CU at the end).  With no units
   // at all (every weight empty) one workgroup still runs, to write y = 0.
-  hipLaunchKernelGGL((decode_m1_kernel<kDecodeWaves, 4, 4>), dim3(1u << args.grid_log2), dim3(kDecodeWaves * 64), 0, st,
-                     args);
+  hipLaunchKernelGGL((decode_m1_kernel<kDecodeWaves, kDecodeGroupTiles / kDecodeWaves, kDecodeWaves / 4>),
+                     dim3(1u << args.grid_log2), dim3(kDecodeWaves * 64), 0, st, args);
   return (int)hipGetLastError();
 }
 

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // signs and zero U, and out-of-range addresses are redirected to the zero page), so
   // the number of loads in flight is the same on every path and the compiler's in-order
   // wait counts never drain the prefetches.
-  u32x4 raw[R], rawn[R];  // sign words of the current and the next unit
+  u32x4 sgn[2][R];  // sign words of the current and the next unit
   u32x2 uf[R];
   // This wave's planes: V and x of columns 4 kk .. 4 kk + 3 and 16 + 4 kk ..; the waves
   // that build after their tiles keep them in their own registers (see step).
@@ -462,24 +462,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const UnitPtrs p0 = unit_ptrs(c0, true);
   UnitPtrs p1 = unit_ptrs(c1, true);
   UnitPtrs p2 = unit_ptrs(c2, true);
-  load_vx(p0, vx_early);
-  load_signs(p0, raw);
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const int j = threadIdx.x / kMaxBlocks, i = threadIdx.x % kMaxBlocks;
-    if (j < args.count && i < args.w[j].nblocks) {
-      const u32x2 t = load8(&args.w[j].blocks[i].signs);
-      bbase[j][i] = t[0] | ((uint64_t)t[1] << 32);
-    }
+  // Every load of the first two units is issued before anything waits: the block-table
+  // entry for the LDS copy first (so that waiting for it waits for nothing else), then
+  // the first unit's V / x and signs, the second unit's V / x, the first unit's U and
+  // the second unit's signs.  No barrier here: the first barrier of the unit loop also
+  // orders the LDS copy of the table and the first unit's B operands.
+  const int bj = threadIdx.x / kMaxBlocks, bi = threadIdx.x % kMaxBlocks;
+  bool bvalid = false;
+  const void* bsrc = &args.w[0].blocks[0].signs;  // (always a valid entry: tables hold >= 1)
+  if (bj < args.count && bi < args.w[bj].nblocks) {
+    bvalid = true;
+    bsrc = &args.w[bj].blocks[bi].signs;
   }
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  build_z(0, vx_early);  // (waits only for the first unit's V fragments and activations)
-  __builtin_amdgcn_sched_barrier(0);
-  load_signs(p1, rawn);
+  const u32x2 btab = load8(bsrc);
+  VX vx0;
+  load_vx(p0, vx0);
+  load_signs(p0, sgn[0]);
   if (wave >= NW / 2) load_vx(p1, vx_early);
   else load_vx(p1, vx_late);
   load_u(p0);
+  load_signs(p1, sgn[1]);
+  __builtin_amdgcn_sched_barrier(0);
+  if (bvalid) bbase[bj][bi] = btab[0] | ((uint64_t)btab[1] << 32);
+  build_z(0, vx0);  // (waits only for the table entry and the first unit's V / x)
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- one unit.  On entry unit c0's signs are in `cur` and unit c1's in the other
   // buffer, c0's Z tile in zs[buf], its U fragments in uf, and unit c1's V fragments
@@ -551,8 +557,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint32_t n = u_end - u_begin;
   const uint32_t item_first = c0.rg_begin + c0.rg;
   for (uint32_t s = 0; s < n; s += 2) {
-    step(raw, 0);
-    if (s + 1 < n) step(rawn, 1);
+    step(sgn[0], 0);
+    if (s + 1 < n) step(sgn[1], 1);
   }
 
   // ---- end of the range: count this workgroup in for every row group it touched; the

@@ -21,6 +21,9 @@ BSL_EINVAL = -1
 BSL_ENOMEM = -2
 BSL_EHIP = -3
 BSL_EUNSUPPORTED = -4
+BSL_PATH_AUTO = 0
+BSL_PATH_FACTORED = 1
+BSL_PATH_TILE = 2
 
 EXPORTED = (
     "bsl_block_bytes",
@@ -28,6 +31,7 @@ EXPORTED = (
     "bsl_pack_signs",
     "bsl_unpack_signs",
     "bsl_init",
+    "bsl_set_path",
     "bsl_set_source",
     "bsl_load_blocks",
     "bsl_active_blocks",
@@ -75,13 +79,14 @@ def lib() -> ctypes.CDLL:
         L.bsl_resident_bytes.argtypes = [c_vp]
         L.bsl_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
+        L.bsl_set_path.argtypes = [c_vp, c_i32]
         L.bsl_debug_unpack.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.bsl_last_error.restype = ctypes.c_char_p
         L.bsl_last_error.argtypes = []
         L.bsl_destroy.restype = None
         L.bsl_destroy.argtypes = [c_vp]
         for f in ("bsl_pack_signs", "bsl_unpack_signs", "bsl_init", "bsl_set_source", "bsl_load_blocks",
-                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_debug_unpack"):
+                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack"):
             getattr(L, f).restype = c_i32
         _lib = L
     return _lib
@@ -177,6 +182,10 @@ def bsl_forward_group(stack: int, weights, x_ptrs, y_ptrs, M: int, y_is_fp32: bo
     ys = (ctypes.c_void_p * n)(*y_ptrs)
     _check(lib().bsl_forward_group(stack, n, ctypes.addressof(ws), ctypes.addressof(xs), ctypes.addressof(ys), M,
                                    1 if y_is_fp32 else 0, stream))
+
+
+def bsl_set_path(stack: int, path: int) -> None:
+    _check(lib().bsl_set_path(stack, path))
 
 
 def bsl_debug_unpack(stack: int, w: int, i: int, path: int, out_ptr: int, stream: int = 0) -> None:

@@ -118,6 +118,12 @@ void tile_v(const uint16_t* v, int64_t d, uint16_t* out) {
         }
 }
 
+// V (d x 16, row-major fp16) -> [d_pad][16], zero past d.
+void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
+  std::memcpy(out, v, (size_t)d * kRank * 2);
+  std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ stack
@@ -141,6 +147,7 @@ struct bsl_stack {
   int device = 0;
   int32_t k = 16, n_cap = 0;
   int32_t decode_grid_max = 256;  // largest power of two <= compute units
+  int32_t path = BSL_PATH_AUTO;   // multi-token formulation (bsl_set_path)
   uint64_t budget = 0, resident = 0;
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
@@ -150,8 +157,9 @@ struct bsl_stack {
 
 namespace {
 
+// signs + tiled U + tiled V + row-major V (see BlockPtrs)
 size_t slot_bytes(int64_t m, int64_t d) {
-  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + (size_t)pad_cols(d) * kRank * 2;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 2 * (size_t)pad_cols(d) * kRank * 2;
 }
 
 BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
@@ -159,9 +167,11 @@ BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
   const uint8_t* base = static_cast<const uint8_t*>(s.mem);
   const size_t sb = (size_t)pad_rows(m) * pad_cols(d) / 8;
   const size_t ub = (size_t)pad_rows(m) * kRank * 2;
+  const size_t vb = (size_t)pad_cols(d) * kRank * 2;
   p.signs = base;
   p.u = reinterpret_cast<const uint16_t*>(base + sb);
   p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
+  p.vr = reinterpret_cast<const uint16_t*>(base + sb + ub + vb);
   return p;
 }
 
@@ -179,7 +189,7 @@ struct DeviceGuard {
 int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
   std::vector<BlockPtrs> tab(s->n_cap);
   for (int32_t i = 0; i < s->n_cap; ++i)
-    tab[i] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr};
+    tab[i] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
   hipError_t e = hipMemcpyAsync(W.dtable, tab.data(), sizeof(BlockPtrs) * s->n_cap, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
@@ -370,10 +380,11 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     const size_t sb = (size_t)pad_rows(W.m) * pad_cols(W.d) / 8;
     const size_t ub = (size_t)pad_rows(W.m) * kRank * 2;
     const size_t vb = (size_t)pad_cols(W.d) * kRank * 2;
-    staging.resize(sb + ub + vb);
+    staging.resize(sb + ub + 2 * vb);
     pack_signs_mt(src.sign_bits, W.m, W.d, staging.data());
     tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(staging.data() + sb));
     tile_v(src.v, W.d, reinterpret_cast<uint16_t*>(staging.data() + sb + ub));
+    rowmajor_v(src.v, W.d, reinterpret_cast<uint16_t*>(staging.data() + sb + ub + vb));
     e = hipMemcpyAsync(W.slots[a.i].mem, staging.data(), staging.size(), hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);  // staging is reused
     if (e != hipSuccess) {
@@ -424,6 +435,56 @@ uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
 
 namespace {
 
+// Tile-reconstruct path: items are (token group, weight, 128-row group), token group
+// outermost so the workgroups that run together share one group's activations in L2;
+// within a token group the weights go in decreasing d (longest items first).
+int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
+                 int32_t y_is_fp32, void* stream) {
+  GroupArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.count = count;
+  args.M = M;
+  args.y_fp32 = y_is_fp32 ? 1 : 0;
+  args.zero_page = s->zero_page;
+  int tt = 1;  // 32-token tiles per workgroup: the power of two that covers M, at most 16
+  while (tt < kTileMaxTokenTiles && 32 * tt < M) tt *= 2;
+  const int64_t token_groups = (M + 32 * tt - 1) / (32 * tt);
+  std::vector<int32_t> order(count);
+  for (int32_t j = 0; j < count; ++j) {
+    const int32_t w = weights[j];
+    if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
+    for (int32_t jj = 0; jj < j; ++jj)
+      if (weights[jj] == w) return fail(BSL_EINVAL, "forward: a weight appears twice in one launch");
+    if (!x[j] || !y[j]) return fail(BSL_EINVAL, "forward: null x or y");
+    if ((reinterpret_cast<uintptr_t>(x[j]) & 15) != 0) return fail(BSL_EINVAL, "forward: x must be 16-byte aligned");
+    order[j] = j;
+  }
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return s->w[weights[a]].d > s->w[weights[b]].d; });
+  int64_t row_groups = 0;
+  for (int32_t k = 0; k < count; ++k) {
+    const int32_t j = order[k];
+    const Weight& W = s->w[weights[j]];
+    WeightDesc& D = args.w[k];
+    D.blocks = W.dtable;
+    D.x = static_cast<const uint16_t*>(x[j]);
+    D.y = y[j];
+    D.m = W.m;
+    D.d = W.d;
+    D.mt = W.mt;
+    D.nch = W.nch;
+    D.nblocks = W.n;
+    D.groups = (int32_t)(pad_rows(W.m) / kTileGroupRows);
+    D.rg_begin = (uint32_t)row_groups;
+    row_groups += D.groups;
+  }
+  if (row_groups * token_groups > (int64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
+  DeviceGuard guard(s->device);
+  const int e = launch_tile(args, tt, (int)token_groups, (int)row_groups, stream);
+  if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+  return BSL_OK;
+}
+
 int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
                  int32_t y_is_fp32, void* stream) {
   if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");
@@ -433,6 +494,8 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
+  const bool tile = s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens);
+  if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
   const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
   const int token_groups = (M + nt - 1) / nt;
   // Multi-token items are cut along their (block, chunk) sequence when there are too few
@@ -531,12 +594,20 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
   return forward_impl(s, count, weights, x, y, M, y_is_fp32, stream);
 }
 
+int bsl_set_path(bsl_stack* s, int32_t path) {
+  if (!s) return fail(BSL_EINVAL, "bsl_set_path: null stack");
+  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE)
+    return fail(BSL_EINVAL, "bsl_set_path: unknown path");
+  s->path = path;
+  return BSL_OK;
+}
+
 int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream) {
   if (!s || !pm1_out) return fail(BSL_EINVAL, "bsl_debug_unpack: null pointer");
   if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "bsl_debug_unpack: weight index out of range");
   const Weight& W = s->w[w];
   if (i < 0 || i >= W.n) return fail(BSL_EINVAL, "bsl_debug_unpack: block not loaded");
-  if (path != 0 && path != 1) return fail(BSL_EINVAL, "bsl_debug_unpack: path must be 0 or 1");
+  if (path < 0 || path > 2) return fail(BSL_EINVAL, "bsl_debug_unpack: path must be 0, 1 or 2");
   DeviceGuard guard(s->device);
   int e = launch_debug_unpack(slot_ptrs(W.slots[i], W.m, W.d), W.m, W.d, W.mt, W.nch, path, pm1_out, stream);
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "debug unpack launch");

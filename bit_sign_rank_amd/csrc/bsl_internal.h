@@ -29,10 +29,13 @@ inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * 
 //   u:     [m_pad/16][64 lanes][4] fp16  lane L holds U[16 t + 4 (L/16) + v][L % 16]
 //   v:     [d_pad/512][16 planes][64 lanes][8] fp16
 //          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
+//   vr:    [d_pad][16] fp16, V row-major (zero past d): the tile-reconstruct kernel's
+//          matrix-core operand, 8 consecutive ranks of one column per 16-byte load
 struct BlockPtrs {
   const uint8_t* signs;
   const uint16_t* u;
   const uint16_t* v;
+  const uint16_t* vr;
 };
 
 // One weight of a (grouped) forward launch; passed by value in the kernel arguments.
@@ -72,6 +75,7 @@ struct GroupArgs {
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
+int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, int row_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
@@ -91,5 +95,12 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 constexpr int kPrefillGroupRows = 512;  // rows per workgroup (8 waves x 64)
 constexpr int kMaxSplits = 8;
 constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-sum workspace holds
+// Tile-reconstruct path: one 4-wave workgroup per (128-row group, group of up to 512
+// tokens); wave w rebuilds rows 32 w .. 32 w + 31 of W_hat for each 64-column step and
+// multiplies them with the staged activations.
+constexpr int kTileGroupRows = 128;
+constexpr int kTileMaxTokenTiles = 16;  // 32-token tiles per workgroup
+constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
+constexpr int kTileAutoMinTokens = 4;   // BSL_PATH_AUTO takes the tile path from this M on
 
 }  // namespace bsl

@@ -128,6 +128,7 @@ __device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
   r.signs = uniform_ptr(b.signs);
   r.u = uniform_ptr(b.u);
   r.v = uniform_ptr(b.v);
+  r.vr = uniform_ptr(b.vr);
   return r;
 }
 
@@ -139,6 +140,7 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.signs = t->signs;
   b.u = t->u;
   b.v = t->v;
+  b.vr = t->vr;
   return b;
 }
 
@@ -903,11 +905,182 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+// ============================================================ tile-reconstruct kernel
+// Any M (chosen for batches of tokens).  The weight restoration the pages give (add each
+// block's unpacked signs times U_i V_i^T into W) is done per tile in registers and the
+// rebuilt tile is multiplied with the activations at once, so the sign / low-rank work
+// is paid once per group of up to 512 tokens instead of once per token:
+//     W_hat[j, c] = sum_i S_i[j, c] (U_i V_i^T)[j, c],     y[t, j] = sum_c x[t, c] W_hat[j, c].
+// One workgroup of 4 waves (one per SIMD, so each wave's VALU work overlaps its own MFMAs)
+// per item = (weight, 128-row group, group of 32 TT tokens); wave w owns rows 32 w ..
+// 32 w + 31 and all the group's tokens.  The column loop runs in steps of two planes (64
+// columns).  For each step and block, two v_mfma_f32_32x32x16_f16 with K = 16 = the rank
+// give (U_i V_i^T) for the wave's 32 rows and the step's two planes; each fp32 result pair
+// (same row and column offset in both planes) is rounded to an fp16 pair and added into
+// the running W_hat pair with a +-1 fp16 pair built from the stored sign word (one shift
+// and one AND-OR).  After the batch's blocks the pairs are split by plane and feed the
+// GEMM: 4 MFMAs per 32-token tile and step, fp16 inputs, fp32 accumulation.
+//
+// Layouts (lane l, h = l / 32, j = l % 32):
+//  * reconstruct: A = V rows (the step plane's column sigma(j), ranks 8 h .. 8 h + 7,
+//    one 16-byte load from the row-major copy), B = U (row row0 + j, ranks 8 h ..);
+//    result value i of lane l is column 16 h + i of the plane for row row0 + j (sigma
+//    orders the A rows so).  Those columns are lane groups g = 2 h, 2 h + 1 of the stored
+//    sign tile, so a lane reads the 16 stored bytes of (row, g) for its two groups.
+//  * GEMM: A = activations (token t = l % 32 of the tile, 8 columns), B = W_hat (row j,
+//    same 8 columns), C[t][j] in lane j + 32 ((t / 4) % 2).  The activations of a step
+//    are staged in LDS as 16-byte units u = 4 z + 2 h + s (plane z of the pair, columns
+//    16 h + 8 s .. + 7), [tile][u][slot], token t at slot t ^ 2 u (conflict-free writes
+//    of 8 units per token and reads of 32 tokens per unit).
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+// +-1 fp16 pair for planes (4 q + 2 kp, 4 q + 2 kp + 1) at column 8 g + e of lane group
+// g, from that group's stored word q: their bits sit at 16 half + 2 e + 1 - kp, so one
+// shift puts both at bits 15 and 31 (vmask holds 0x80008000).
+__device__ __forceinline__ uint32_t tile_sign_pair(uint32_t w, int e, int kp, uint32_t vmask) {
+  return ((w << (14 - 2 * e + kp)) & vmask) | 0x3C003C00u;
+}
+
+template <int TT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_kernel(GroupArgs args, int row_groups) {
+  constexpr int P1 = (TT + 1) / 2;  // activation tiles staged in the first half of a step
+  __shared__ u32x4 xs[2][TT][8][32];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, jl = lane & 31;
+  const int tg = blockIdx.x / row_groups;
+  const int local = blockIdx.x - tg * row_groups;
+  WeightDesc W = args.w[0];
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j)
+    if (j < args.count && local >= (int)args.w[j].rg_begin) W = args.w[j];
+  const int rg = local - (int)W.rg_begin;
+  const int M = args.M;
+  const int tok0 = tg * 32 * TT;
+  const int row0 = rg * kTileGroupRows + wave * 32;
+  const int nch = W.nch, nb = W.nblocks, d = W.d;
+  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+
+  float16v acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = (float16v){};
+
+  // activation staging: thread -> unit su of token stok of every tile (clamped to M - 1)
+  const int su = threadIdx.x & 7, stok = threadIdx.x >> 3;
+  const uint16_t* xbase = W.x + (size_t)tok0 * d;  // (uniform)
+  const uint32_t xr0 = (uint32_t)stok * 2u * (uint32_t)d, xstep = 64u * (uint32_t)d;
+  const uint32_t xmax = (uint32_t)(M - 1 - tok0) * 2u * (uint32_t)d;
+  const int sslot = stok ^ (2 * su);
+  // reconstruct operands: A row sigma(j) of a plane; this lane's sign-tile row and groups
+  const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
+  const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
+  const int row = row0 + jl;
+  const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
+
+  uint32_t vmask = 0x80008000u;
+  asm volatile("" : "+v"(vmask));  // (a VGPR operand, so that AND and OR fuse into v_and_or_b32)
+
+  for (int b0 = 0; b0 < nb; b0 += kTileBatch) {
+    const int nbb = min(kTileBatch, nb - b0);
+    BlockPtrs bp[kTileBatch];
+    half8 uf[kTileBatch];
+#pragma unroll
+    for (int i = 0; i < kTileBatch; ++i) {
+      bp[i] = load_block(W.blocks, b0 + min(i, nbb - 1));
+      // U[row][8 h + e] from the tiled copy: tile row / 16, lane 16 ((row / 4) % 4) + 8 h + e, slot row % 4
+      const uint16_t* ut = bp[i].u + ((size_t)(row >> 4) * 64 + 16 * ((row >> 2) & 3) + 8 * h) * 4 + (row & 3);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) uf[i][e] = __builtin_bit_cast(_Float16, load_at<uint16_t>(ut, 8u * e));
+    }
+    for (int c = 0; c < nch; ++c) {
+      u32x4 sg[kTileBatch][2];
+#pragma unroll
+      for (int i = 0; i < kTileBatch; ++i)
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2)
+          sg[i][g2] = load_at<u32x4>(bp[i].signs + (size_t)c * W.mt * kTileBytes, soff + 256u * g2);
+      const bool full = (c + 1) * kChunkCols <= d;  // (uniform)
+#pragma unroll
+      for (int qk = 0; qk < 8; ++qk) {  // step: planes 2 qk, 2 qk + 1 (stored word q, kp = qk % 2)
+        const int q = qk >> 1, kp = qk & 1, buf = qk & 1;
+        const int col0 = c * kChunkCols + 64 * qk;  // first column of the step
+        const int ucol = col0 + 8 * su;             // first column of this thread's staged unit
+        auto stage_load = [&](int tt) -> u32x4 {
+          if (full || ucol < d) return load_at<u32x4>(xbase, min(xr0 + (uint32_t)tt * xstep, xmax) + 2u * ucol);
+          return load_at<u32x4>(zero_page, 0);
+        };
+        u32x4 xv[P1];
+#pragma unroll
+        for (int tt = 0; tt < P1; ++tt) xv[tt] = stage_load(tt);
+        half2v wp[16];  // W_hat pairs (plane 2 qk, plane 2 qk + 1) at column 16 h + v, row `row`
+#pragma unroll
+        for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+#pragma unroll
+        for (int i = 0; i < kTileBatch; ++i) {
+          if (i == kTileBatch / 2) {  // first half staged, second half requested
+#pragma unroll
+            for (int tt = 0; tt < P1; ++tt) xs[buf][tt][su][sslot] = xv[tt];
+#pragma unroll
+            for (int tt = P1; tt < TT; ++tt) xv[tt - P1] = stage_load(tt);
+          }
+          if (i < nbb) {
+            const uint16_t* vcol = bp[i].vr + (size_t)col0 * kRank;  // (uniform)
+            const half8 va = as_half8(load_at<u32x4>(vcol, voff));
+            const half8 vb = as_half8(load_at<u32x4>(vcol, voff + 32u * kRank * 2u));
+            const float16v d0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, uf[i], (float16v){}, 0, 0, 0);
+            const float16v d1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, uf[i], (float16v){}, 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const uint32_t sp = tile_sign_pair(sg[i][v >> 3][q], v & 7, kp, vmask);
+              const half2v dp = __builtin_convertvector((float2v){d0[v], d1[v]}, half2v);
+              wp[v] = as_half2(sp) * dp + wp[v];
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = P1; tt < TT; ++tt) xs[buf][tt][su][sslot] = xv[tt - P1];
+        // split the pairs by plane: bw[z][s] = W_hat[row][plane 2 qk + z, columns 16 h + 8 s .. + 7]
+        u32x4 bw[2][2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int m2 = 0; m2 < 4; ++m2) {
+            const uint32_t lo = as_u32(wp[8 * s2 + 2 * m2]), hi = as_u32(wp[8 * s2 + 2 * m2 + 1]);
+            bw[0][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            bw[1][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+          }
+        lds_barrier();  // this step's activations are staged (the buffer written next was last read two steps ago)
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+          for (int z = 0; z < 2; ++z)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              const int u = 4 * z + 2 * h + s2;
+              const half8 xa = as_half8(xs[buf][tt][u][jl ^ (2 * u)]);
+              acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, as_half8(bw[z][s2]), acc[tt], 0, 0, 0);
+            }
+      }
+    }
+  }
+  // lane (h, j) holds row row0 + j and tokens 8 (v / 4) + 4 h + v % 4 of every tile
+  if (row < W.m) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = tok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (t < M) store_y(W.y, (size_t)t * W.m + row, acc[tt][v], args.y_fp32);
+      }
+  }
+}
+
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write the signs.
 // Path 0: the single-token kernel's sparse indices (odd form: field 2 s + j, even form:
 // field s + 2 j for slot j of a group; s = 1 for a -1 sign).  Path 1: the multi-token
-// kernel's +-1 fp16 A fragments.  Lane group g holds columns 8 g .. 8 g + 7 of each plane.
+// kernel's +-1 fp16 A fragments.  Path 2: the tile-reconstruct kernel's +-1 pairs.  Lane group g holds columns 8 g .. 8 g + 7 of each plane.
 template <int B>
 __device__ __forceinline__ void debug_plane(const u32x4& w, int path, int g, int ch, int row, int32_t d, int8_t* out) {
   int8_t sg[8];
@@ -919,10 +1092,16 @@ __device__ __forceinline__ void debug_plane(const u32x4& w, int path, int g, int
       const uint32_t neg = plane_even(B) ? (field & 1u) : (field >> 1);
       sg[e] = neg ? -1 : 1;
     }
-  } else {
+  } else if (path == 1) {
     const half8 h = as_half8(pm1_fragment<B>(w[plane_word(B)], 0x80008000u));
 #pragma unroll
     for (int e = 0; e < 8; ++e) sg[e] = (float)h[e] < 0.f ? -1 : 1;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const half2v p = as_half2(tile_sign_pair(w[plane_word(B)], e, plane_even(B), 0x80008000u));
+      sg[e] = (float)p[plane_half(B)] < 0.f ? -1 : 1;
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -968,6 +1147,21 @@ int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void
     hipLaunchKernelGGL(prefill_kernel<8>, dim3(args.total_items), dim3(512), 0, st, args, token_groups);
   else
     return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
+
+int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, int row_groups, void* stream) {
+  if (row_groups == 0) return 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(token_groups * row_groups));
+  switch (token_tiles) {
+    case 1: hipLaunchKernelGGL(tile_kernel<1>, grid, dim3(256), 0, st, args, row_groups); break;
+    case 2: hipLaunchKernelGGL(tile_kernel<2>, grid, dim3(256), 0, st, args, row_groups); break;
+    case 4: hipLaunchKernelGGL(tile_kernel<4>, grid, dim3(256), 0, st, args, row_groups); break;
+    case 8: hipLaunchKernelGGL(tile_kernel<8>, grid, dim3(256), 0, st, args, row_groups); break;
+    case 16: hipLaunchKernelGGL(tile_kernel<16>, grid, dim3(256), 0, st, args, row_groups); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

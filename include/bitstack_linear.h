@@ -118,7 +118,9 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
 /* Number of loaded blocks of weight w. */
 int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
 
-/* Device bytes currently held by loaded blocks (what budget_bytes caps). */
+/* Device bytes currently held by loaded blocks (what budget_bytes caps).  A loaded block
+ * occupies its padded tiled signs and factors plus a row-major copy of V (32 bytes per
+ * padded column) that the tile-reconstruct path reads. */
 uint64_t bsl_resident_bytes(const bsl_stack* s);
 
 /* y = x W_hat_n^T for weight w with its n loaded blocks.
@@ -134,10 +136,26 @@ int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int3
 int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
                       int32_t M, int32_t y_is_fp32, void* stream);
 
+/* Formulation of the forward for a batch of tokens (bsl_set_path):
+ *   BSL_PATH_FACTORED: never form W_hat.  Per block, contract S_i with Z_i = V_i (.) x on
+ *     the matrix cores and reduce with U_i (the single-token kernel at M = 1, the
+ *     multi-token kernel otherwise).  Work grows as n * k * M * m * d.
+ *   BSL_PATH_TILE: the weight restoration the authors give (add each block's unpacked
+ *     signs times U_i V_i^T; OpenReview discussion, weight-restoration reply), done per
+ *     128-row x 64-column tile in registers and multiplied at once with up to 512 tokens:
+ *     the tile of W_hat is rounded to fp16 (each block's U_i V_i^T and the running sum
+ *     over blocks), then y accumulates in fp32.  Work grows as n * k * m * d per group of
+ *     512 tokens plus M * m * d, so it is the fast form for batches.
+ *   BSL_PATH_AUTO (the default): FACTORED for M below 4, TILE from M = 4 on. */
+#define BSL_PATH_AUTO 0
+#define BSL_PATH_FACTORED 1
+#define BSL_PATH_TILE 2
+int bsl_set_path(bsl_stack* s, int32_t path);
+
 /* Run a forward kernel's own sign-unpack code on block i of weight w and write the
  * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes).
  * path 0: the single-token kernel's sparse-MFMA indices; path 1: the multi-token
- * kernel's +-1 fp16 A fragments. */
+ * kernel's +-1 fp16 A fragments; path 2: the tile-reconstruct kernel's +-1 fp16 pairs. */
 int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream);
 
 /* Message for the calling thread's last failure ("" if none). */

@@ -3,7 +3,9 @@
 Bars: sign unpacking and the integer-valued forward are bit-exact; every other output
 is within a relative Frobenius error of 5e-3 of the oracle (the layer's stated
 tolerance).  Large shapes are checked on seeded row samples that the oracle computes
-one by one, in the same launch configuration the benchmark times.
+one by one, in the same launch configuration the benchmark times.  Both formulations
+are covered: FACTORED (S_i Z_i on the matrix cores, never forming W_hat) and TILE
+(W_hat rebuilt per tile in registers, then a GEMM with the activations).
 """
 from __future__ import annotations
 
@@ -18,6 +20,9 @@ pytestmark = pytest.mark.gpu
 
 import bit_sign_rank_amd as bsl  # noqa: E402  (no skip: a missing library must fail here)
 from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
+
+PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE]
+PATH_IDS = ["factored", "tile"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,7 +41,7 @@ def integer_blocks(m, d, n, seed=21):
 
 # ---------------------------------------------------------------- sign unpack
 @pytest.mark.parametrize("m,d", [(1024, 1024), (48, 1536), (37, 520), (4096, 4096), (16, 8)])
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_debug_unpack_bit_exact(m, d, path):
     blocks = synth.synthetic_blocks(5, m, d, 2, 16, m, d)
     with Stack([(m, d, blocks)]) as st:
@@ -51,12 +56,14 @@ def test_debug_unpack_bit_exact(m, d, path):
 # ---------------------------------------------------------------- exact integer forward
 @pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 17, 130])
-def test_integer_forward_bit_exact(m, d, n, M):
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_integer_forward_bit_exact(m, d, n, M, path):
     # U = V = 0.25 with k = 16 makes U V^T == 1, so y = x (sum_i S_i)^T is an integer of
     # magnitude < 2^20; every partial sum is exact in fp32, so any order gives the same bits.
+    # (On the tile path W_hat itself is a sum of n <= 16 signs: exact in fp16.)
     blocks = integer_blocks(m, d, n)
     x = synth.integer_activations(9, M, d)
-    with Stack([(m, d, blocks)]) as st:
+    with Stack([(m, d, blocks)], path=path) as st:
         st.load([n])
         y = st.forward(0, x, fp32=True)
     assert np.array_equal(y, oracle.forward(x, blocks, n))
@@ -71,10 +78,11 @@ def cfg1_blocks():
 
 
 @pytest.mark.parametrize("fp32", [True, False])
-def test_decomposed_weight_all_block_counts(cfg1_blocks, fp32):
+@pytest.mark.parametrize("path", [bsl.BSL_PATH_AUTO] + PATHS, ids=["auto"] + PATH_IDS)
+def test_decomposed_weight_all_block_counts(cfg1_blocks, fp32, path):
     x1 = synth.activations(1, 1, 1024)
     x8 = synth.activations(2, 8, 1024)
-    with Stack([(1024, 1024, cfg1_blocks)]) as st:
+    with Stack([(1024, 1024, cfg1_blocks)], path=path) as st:
         for n in (1, 2, 3, 4):  # grow one block at a time, no repacking of the others
             st.load([n])
             assert bsl.bsl_active_blocks(st.h, 0) == n
@@ -143,27 +151,45 @@ def test_llama3_8b_layer_decode_grouped():
 
 @pytest.mark.slow
 @pytest.mark.parametrize("M", [1, 4, 16])
-def test_llama3_8b_variable_block_counts(M):
+@pytest.mark.parametrize("path", [bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED], ids=["auto", "factored"])
+def test_llama3_8b_variable_block_counts(M, path):
+    if M == 1 and path == bsl.BSL_PATH_FACTORED:
+        pytest.skip("M = 1 takes the same kernel under both settings")
     shapes = synth.LLAMA3_8B_LAYER
     counts = synth.block_counts(13, 7, 1, 16)
     weights = layer_blocks(shapes, counts, seed=14)
     xs = [synth.activations(15, M, d, j) for j, (_, _, d) in enumerate(shapes)]
-    with Stack(weights) as st:
+    with Stack(weights, path=path) as st:
         st.load(counts)
         ys = st.forward_group(list(range(7)), xs)
         check_sampled(weights, counts, ys, xs, rows_per_weight=32)
 
 
 @pytest.mark.slow
-def test_llama3_8b_prefill_2048_tokens():
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_llama3_8b_prefill_2048_tokens(path):
     shapes = [("q", 4096, 4096), ("down", 4096, 14336)]
     counts = [8, 8]
     weights = layer_blocks(shapes, counts, seed=16)
     xs = [synth.activations(17, 2048, d, j) for j, (_, _, d) in enumerate(shapes)]
-    with Stack(weights) as st:
+    with Stack(weights, path=path) as st:
         st.load(counts)
         ys = [st.forward(j, xs[j], fp32=False) for j in range(2)]
         check_sampled(weights, counts, ys, xs, rows_per_weight=24)
+
+
+@pytest.mark.slow
+def test_llama3_8b_layer_prefill_grouped_tile():
+    # the benchmark's prefill launch: all seven linears of a layer in one grouped launch,
+    # n = 8, M = 2048, default (AUTO -> tile) path, fp16 y
+    shapes = synth.LLAMA3_8B_LAYER
+    counts = [8] * 7
+    weights = layer_blocks(shapes, counts, seed=29)
+    xs = [synth.activations(30, 2048, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(7)), xs, fp32=False)
+        check_sampled(weights, counts, ys, xs, rows_per_weight=16)
 
 
 @pytest.mark.slow
@@ -191,20 +217,38 @@ def test_ragged_shapes_random_blocks(m, d, M):
 
 # ---------------------------------------------------------------- many tokens (the 32x32 prefill path)
 @pytest.mark.parametrize("m,d,M", [(1000, 1544, 133), (37, 520, 64), (512, 1024, 256)])
-def test_prefill_ragged_shapes(m, d, M):
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_prefill_ragged_shapes(m, d, M, path):
     blocks = synth.synthetic_blocks(25, m, d, 3, 16, m, d)
     x = synth.activations(26, M, d)
-    with Stack([(m, d, blocks)]) as st:
+    with Stack([(m, d, blocks)], path=path) as st:
         st.load([3])
         y = st.forward(0, x, fp32=False)
     assert rel_err(y, oracle.forward(x, blocks, 3)) <= REL_TOL
 
 
-def test_prefill_grouped_launch_and_zero_blocks():
+# token-group edges of the tile path (groups of up to 512 tokens; the last group partial),
+# one and two 8-block batches, ragged rows / columns
+@pytest.mark.parametrize("m,d,M,n", [(130, 1032, 511, 3), (256, 512, 512, 9), (37, 520, 513, 1), (300, 1536, 1100, 11),
+                                     (1024, 2048, 7, 16), (16, 8, 40, 2)])
+def test_tile_token_groups_and_batches(m, d, M, n):
+    blocks = synth.synthetic_blocks(31, m, d, n, 16, m, d)
+    x = synth.activations(32, M, d)
+    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_TILE) as st:
+        st.load([n])
+        y = st.forward(0, x)
+        y16 = st.forward(0, x, fp32=False)
+    ref = oracle.forward(x, blocks, n)
+    assert rel_err(y, ref) <= REL_TOL
+    assert rel_err(y16, ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_prefill_grouped_launch_and_zero_blocks(path):
     shapes = [(1024, 1024, 2), (512, 2048, 0), (1536, 512, 4)]
     weights = [(m, d, synth.synthetic_blocks(27, m, d, max(n, 1), 16, j)) for j, (m, d, n) in enumerate(shapes)]
     xs = [synth.activations(28, 256, d, j) for j, (_, d, _) in enumerate(shapes)]
-    with Stack(weights) as st:
+    with Stack(weights, path=path) as st:
         st.load([n for _, _, n in shapes])
         ys = st.forward_group([0, 1, 2], xs)
     for (m, d, blocks), (_, _, n), y, x in zip(weights, shapes, ys, xs):
@@ -234,6 +278,9 @@ def test_errors_leave_state_unchanged(cfg1_blocks):
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_load_blocks(st.h, [5], 0)  # only 4 source blocks
+        assert e.value.code == bsl.BSL_EINVAL
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_set_path(st.h, 3)  # no such formulation
         assert e.value.code == bsl.BSL_EINVAL
         assert bsl.bsl_active_blocks(st.h, 0) == 2
         # still works after the failures

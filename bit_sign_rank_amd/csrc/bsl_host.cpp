@@ -152,6 +152,8 @@ struct bsl_stack {
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
   uint32_t* arrivals = nullptr;   // single-token arrival counters, one per row group of a launch
+  float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
+  uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
   std::vector<Weight> w;
 };
 
@@ -299,6 +301,9 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
     else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
     else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
+    else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
+    else if ((e = hipMalloc(&s->tile_ctr, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile counters)");
+    else if ((e = hipMemset(s->tile_ctr, 0, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(tile counters)");
   }
   if (rc == BSL_OK && (e = hipDeviceSynchronize()) != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
   if (rc != BSL_OK) {
@@ -435,9 +440,10 @@ uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
 
 namespace {
 
-// Tile-reconstruct path: items are (token group, weight, 128-row group), token group
-// outermost so the workgroups that run together share one group's activations in L2;
-// within a token group the weights go in decreasing d (longest items first).
+// Tile-reconstruct path.  Items are (weight, token group, 128-row group, column range);
+// weights go longest item first, so the long items of a launch start first.  A weight's
+// chunks are cut into ranges when the launch has too few items to keep every CU busy, as
+// far as the stack's tile workspace holds the ranges' partial sums.
 int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
                  int32_t y_is_fp32, void* stream) {
   GroupArgs args;
@@ -446,10 +452,16 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
   args.zero_page = s->zero_page;
-  int tt = 1;  // 32-token tiles per workgroup: the power of two that covers M, at most 16
-  while (tt < kTileMaxTokenTiles && 32 * tt < M) tt *= 2;
-  const int64_t token_groups = (M + 32 * tt - 1) / (32 * tt);
-  std::vector<int32_t> order(count);
+  int tt = 1;  // 32-token tiles per wave (two waves per row tile): covers M, at most 8
+  while (tt < kTileMaxTokenTiles && 64 * tt < M) tt *= 2;
+  const int64_t token_groups = (M + 64 * tt - 1) / (64 * tt);
+  const int64_t tokpad = token_groups * 64 * tt;
+  struct Plan {
+    int32_t j;
+    int64_t rgroups, batches, splits, cps;
+  };
+  std::vector<Plan> plan(count);
+  int64_t total = 0;  // chunk passes over all items
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -457,30 +469,64 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
       if (weights[jj] == w) return fail(BSL_EINVAL, "forward: a weight appears twice in one launch");
     if (!x[j] || !y[j]) return fail(BSL_EINVAL, "forward: null x or y");
     if ((reinterpret_cast<uintptr_t>(x[j]) & 15) != 0) return fail(BSL_EINVAL, "forward: x must be 16-byte aligned");
-    order[j] = j;
+    const Weight& W = s->w[w];
+    if ((uint64_t)pad_rows(W.m) * pad_cols(W.d) / 8 >= (1ull << 31))
+      return fail(BSL_EUNSUPPORTED, "forward: the tile path needs each block's signs below 2 GiB");
+    Plan& p = plan[j];
+    p.j = j;
+    p.rgroups = pad_rows(W.m) / kTileGroupRows;
+    p.batches = (W.n + kTileBatch - 1) / kTileBatch;
+    p.splits = 1;
+    p.cps = W.nch;
+    total += p.rgroups * token_groups * W.nch * p.batches;
   }
-  std::stable_sort(order.begin(), order.end(),
-                   [&](int32_t a, int32_t b) { return s->w[weights[a]].d > s->w[weights[b]].d; });
-  int64_t row_groups = 0;
+  const int64_t target = std::max<int64_t>(1, (total + 2 * s->decode_grid_max - 1) / (2 * s->decode_grid_max));
+  size_t ws_used = 0, ctr_used = 0;
+  for (Plan& p : plan) {
+    const Weight& W = s->w[weights[p.j]];
+    if (p.batches == 0) continue;
+    const int64_t want = std::min<int64_t>(W.nch, (W.nch * p.batches + target - 1) / target);
+    if (want <= 1) continue;
+    const int64_t cps = (W.nch + want - 1) / want, splits = (W.nch + cps - 1) / cps;
+    const size_t floats = (size_t)splits * tokpad * pad_rows(W.m);
+    const size_t ctrs = (size_t)token_groups * p.rgroups;
+    if (splits > 1 && ws_used + floats <= kTileWorkspaceFloats && ctr_used + ctrs <= (size_t)kTileCounters) {
+      p.splits = splits;
+      p.cps = cps;
+      ws_used += floats;
+      ctr_used += ctrs;
+    }
+  }
+  std::stable_sort(plan.begin(), plan.end(), [](const Plan& a, const Plan& b) { return a.cps * a.batches > b.cps * b.batches; });
+  int64_t items = 0;
+  ws_used = ctr_used = 0;
   for (int32_t k = 0; k < count; ++k) {
-    const int32_t j = order[k];
-    const Weight& W = s->w[weights[j]];
+    const Plan& p = plan[k];
+    const Weight& W = s->w[weights[p.j]];
     WeightDesc& D = args.w[k];
     D.blocks = W.dtable;
-    D.x = static_cast<const uint16_t*>(x[j]);
-    D.y = y[j];
+    D.x = static_cast<const uint16_t*>(x[p.j]);
+    D.y = y[p.j];
     D.m = W.m;
     D.d = W.d;
     D.mt = W.mt;
     D.nch = W.nch;
     D.nblocks = W.n;
-    D.groups = (int32_t)(pad_rows(W.m) / kTileGroupRows);
-    D.rg_begin = (uint32_t)row_groups;
-    row_groups += D.groups;
+    D.groups = (int32_t)p.rgroups;
+    D.splits = (int32_t)p.splits;
+    if (p.splits > 1) {
+      D.partial = s->tile_ws + ws_used;
+      D.counters = s->tile_ctr + ctr_used;
+      ws_used += (size_t)p.splits * tokpad * pad_rows(W.m);
+      ctr_used += (size_t)token_groups * p.rgroups;
+    }
+    D.item_begin = (int32_t)items;
+    items += token_groups * p.rgroups * p.splits;
+    if (items > (int64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
   }
-  if (row_groups * token_groups > (int64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
+  args.total_items = (int32_t)items;
   DeviceGuard guard(s->device);
-  const int e = launch_tile(args, tt, (int)token_groups, (int)row_groups, stream);
+  const int e = launch_tile(args, tt, (int)token_groups, stream);
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
 }
@@ -628,6 +674,8 @@ void bsl_destroy(bsl_stack* s) {
   if (s->zero_page) (void)hipFree(s->zero_page);
   if (s->pieces) (void)hipFree(s->pieces);
   if (s->arrivals) (void)hipFree(s->arrivals);
+  if (s->tile_ws) (void)hipFree(s->tile_ws);
+  if (s->tile_ctr) (void)hipFree(s->tile_ctr);
   delete s;
 }
 

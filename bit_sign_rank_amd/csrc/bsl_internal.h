@@ -75,7 +75,7 @@ struct GroupArgs {
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
-int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, int row_groups, void* stream);
+int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 
@@ -95,12 +95,16 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 constexpr int kPrefillGroupRows = 512;  // rows per workgroup (8 waves x 64)
 constexpr int kMaxSplits = 8;
 constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-sum workspace holds
-// Tile-reconstruct path: one 4-wave workgroup per (128-row group, group of up to 512
-// tokens); wave w rebuilds rows 32 w .. 32 w + 31 of W_hat for each 64-column step and
-// multiplies them with the staged activations.
-constexpr int kTileGroupRows = 128;
-constexpr int kTileMaxTokenTiles = 16;  // 32-token tiles per workgroup
+// Tile-reconstruct path: one 4-wave workgroup per (64-row group, group of 64 TT tokens,
+// TT = 1, 2, 4 or 8).  Each 32-row tile is shared by two waves that rebuild half of the
+// blocks each, swap their partial tiles through LDS and own half of the tokens each.
+constexpr int kTileGroupRows = 64;
+constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
 constexpr int kTileAutoMinTokens = 4;   // BSL_PATH_AUTO takes the tile path from this M on
+// Tile-path items may be cut along the columns (chunk ranges) when a launch has too few
+// of them to fill the chip; the ranges' partial sums go to a workspace of the stack.
+constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB
+constexpr int kTileCounters = 1 << 16;
 
 }  // namespace bsl

@@ -942,25 +942,68 @@ __device__ __forceinline__ uint32_t tile_sign_pair(uint32_t w, int e, int kp, ui
   return ((w << (14 - 2 * e + kp)) & vmask) | 0x3C003C00u;
 }
 
-template <int TT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_kernel(GroupArgs args, int row_groups) {
-  constexpr int P1 = (TT + 1) / 2;  // activation tiles staged in the first half of a step
-  __shared__ u32x4 xs[2][TT][8][32];
+// Raw buffer loads: a descriptor in scalar registers plus a 32-bit per-lane byte offset
+// (no 64-bit address arithmetic per load).  An offset at or past kBufOutOfRange reads
+// zeros without touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kBufOutOfRange = 0x80000000u;
+// (The base is passed through readfirstlane: should the compiler keep a uniform pointer
+// in vector registers, the descriptor still ends up in scalar registers without a
+// per-lane loop around the load.)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), (short)0, (int)(kBufOutOfRange - 1), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
+}
+
+// The rebuild's K = 16 MFMA, written out so that its result lands in VGPRs: a kernel
+// that may use all 512 registers gets every compiler-built MFMA in the accumulator-
+// register form, and each result would be copied back one dword per VALU operation.
+// The leading s_nop covers a VALU write of an operand just before; the result is read
+// only after mfma_result_ready.  (Neither statement is volatile: data dependences order
+// them, and the compiler stays free to move loads across them.)
+__device__ __forceinline__ float16v rebuild_mfma(const half8& a, const half8& b) {
+  float16v d;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+// Hands the results of rebuild_mfma to ordinary code after the wait states an MFMA
+// result needs before a VALU operation may read it (at most 19).
+__device__ __forceinline__ void mfma_result_ready(float16v& d0, float16v& d1) {
+  asm("s_nop 15\n\ts_nop 3" : "+v"(d0), "+v"(d1));
+}
+
+template <int TT, int TH>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_kernel(GroupArgs args, int token_groups) {
+  constexpr int TG = TT * TH;             // 32-token tiles per workgroup
+  constexpr int RT = 4 / TH;              // 32-row tiles per workgroup
+  constexpr int GROUP_ROWS = 32 * RT;
+  constexpr int BPW = kTileBatch / TH;    // blocks each wave rebuilds per batch
+  constexpr int NQ = TG >= 4 ? 4 : TG;    // activation staging quarters per step
+  constexpr int TQ = TG / NQ;
+  __shared__ u32x4 xs[2][TG][8][32];
+  __shared__ u32x4 ex[TH == 2 ? 2 : 1][TH == 2 ? 4 : 1][4][64];  // partial W_hat tiles of the wave pairs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, jl = lane & 31;
-  const int tg = blockIdx.x / row_groups;
-  const int local = blockIdx.x - tg * row_groups;
-  WeightDesc W = args.w[0];
-#pragma unroll
-  for (int j = 1; j < kMaxGroup; ++j)
-    if (j < args.count && local >= (int)args.w[j].rg_begin) W = args.w[j];
-  const int rg = local - (int)W.rg_begin;
+  const int rtile = wave / TH, th = wave % TH;
+  const WeightDesc W = find_weight(args, blockIdx.x);
+  const int local = blockIdx.x - W.item_begin;
+  const int split = local % W.splits;
+  const int rest = local / W.splits;
+  const int rg = rest % W.groups;
+  const int tg = rest / W.groups;
   const int M = args.M;
-  const int tok0 = tg * 32 * TT;
-  const int row0 = rg * kTileGroupRows + wave * 32;
-  const int nch = W.nch, nb = W.nblocks, d = W.d;
-  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+  const int tok0 = tg * 32 * TG;          // the workgroup's first token
+  const int wtok0 = tok0 + th * 32 * TT;  // this wave's first token
+  const int row0 = rg * GROUP_ROWS + 32 * rtile;
+  const int nb = W.nblocks, d = W.d;
+  const int cps = (W.nch + W.splits - 1) / W.splits;  // chunks per split
+  const int c_begin = split * cps, c_end = min(W.nch, c_begin + cps);
 
   float16v acc[TT];
 #pragma unroll
@@ -972,108 +1015,226 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t xr0 = (uint32_t)stok * 2u * (uint32_t)d, xstep = 64u * (uint32_t)d;
   const uint32_t xmax = (uint32_t)(M - 1 - tok0) * 2u * (uint32_t)d;
   const int sslot = stok ^ (2 * su);
-  // reconstruct operands: A row sigma(j) of a plane; this lane's sign-tile row and groups
+  // rebuild operands: A row sigma(j) of a plane; this lane's sign-tile row and groups
   const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
   const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
   const int row = row0 + jl;
   const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
+  const uint32_t uoff = (((uint32_t)(row >> 4) * 64u + 16u * ((row >> 2) & 3) + 8u * h) * 4u + (row & 3)) * 2u;
+  const uint32_t chunk_sign_bytes = (uint32_t)W.mt * kTileBytes;  // (a block's signs are < 2 GiB here)
 
   uint32_t vmask = 0x80008000u;
   asm volatile("" : "+v"(vmask));  // (a VGPR operand, so that AND and OR fuse into v_and_or_b32)
 
-  for (int b0 = 0; b0 < nb; b0 += kTileBatch) {
-    const int nbb = min(kTileBatch, nb - b0);
-    BlockPtrs bp[kTileBatch];
-    half8 uf[kTileBatch];
+  for (int b0 = 0; b0 < nb && c_begin < c_end; b0 += kTileBatch) {
+    // this wave's blocks: b0 + th BPW + i; slots past the weight's last block repeat a
+    // loaded block with U = 0 (read out of range): they add exact zeros, and every load
+    // stays valid, so the block loop has no branches
+    const int nbw = min(BPW, max(0, nb - b0 - th * BPW));
+    const uint8_t* sbase[BPW];  // (chunk offsets go in the loads' scalar offset)
+    const uint16_t* vbase[BPW];
+    half8 uf[BPW];
 #pragma unroll
-    for (int i = 0; i < kTileBatch; ++i) {
-      bp[i] = load_block(W.blocks, b0 + min(i, nbb - 1));
+    for (int i = 0; i < BPW; ++i) {
+      const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + th * BPW + i : b0);
+      sbase[i] = bp.signs;
+      vbase[i] = bp.vr;
       // U[row][8 h + e] from the tiled copy: tile row / 16, lane 16 ((row / 4) % 4) + 8 h + e, slot row % 4
-      const uint16_t* ut = bp[i].u + ((size_t)(row >> 4) * 64 + 16 * ((row >> 2) & 3) + 8 * h) * 4 + (row & 3);
+      const rsrc_t ures = make_rsrc(bp.u);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) uf[i][e] = __builtin_bit_cast(_Float16, load_at<uint16_t>(ut, 8u * e));
+      for (int e = 0; e < 8; ++e)
+        uf[i][e] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(ures, i < nbw ? uoff + 8u * e : kBufOutOfRange, 0, 0));
     }
-    for (int c = 0; c < nch; ++c) {
-      u32x4 sg[kTileBatch][2];
+    // sign words sw[i][g2][q] of the current chunk (quads 0-1 and 2-3 refilled separately)
+    uint32_t sw[BPW][2][4];
+    auto load_signs = [&](int c, int half) {
+      const uint32_t cb = __builtin_amdgcn_readfirstlane((uint32_t)min(c, c_end - 1) * chunk_sign_bytes);  // (uniform)
 #pragma unroll
-      for (int i = 0; i < kTileBatch; ++i)
+      for (int i = 0; i < BPW; ++i) {
 #pragma unroll
-        for (int g2 = 0; g2 < 2; ++g2)
-          sg[i][g2] = load_at<u32x4>(bp[i].signs + (size_t)c * W.mt * kTileBytes, soff + 256u * g2);
-      const bool full = (c + 1) * kChunkCols <= d;  // (uniform)
-#pragma unroll
-      for (int qk = 0; qk < 8; ++qk) {  // step: planes 2 qk, 2 qk + 1 (stored word q, kp = qk % 2)
-        const int q = qk >> 1, kp = qk & 1, buf = qk & 1;
-        const int col0 = c * kChunkCols + 64 * qk;  // first column of the step
-        const int ucol = col0 + 8 * su;             // first column of this thread's staged unit
-        auto stage_load = [&](int tt) -> u32x4 {
-          if (full || ucol < d) return load_at<u32x4>(xbase, min(xr0 + (uint32_t)tt * xstep, xmax) + 2u * ucol);
-          return load_at<u32x4>(zero_page, 0);
-        };
-        u32x4 xv[P1];
-#pragma unroll
-        for (int tt = 0; tt < P1; ++tt) xv[tt] = stage_load(tt);
-        half2v wp[16];  // W_hat pairs (plane 2 qk, plane 2 qk + 1) at column 16 h + v, row `row`
-#pragma unroll
-        for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
-#pragma unroll
-        for (int i = 0; i < kTileBatch; ++i) {
-          if (i == kTileBatch / 2) {  // first half staged, second half requested
-#pragma unroll
-            for (int tt = 0; tt < P1; ++tt) xs[buf][tt][su][sslot] = xv[tt];
-#pragma unroll
-            for (int tt = P1; tt < TT; ++tt) xv[tt - P1] = stage_load(tt);
-          }
-          if (i < nbb) {
-            const uint16_t* vcol = bp[i].vr + (size_t)col0 * kRank;  // (uniform)
-            const half8 va = as_half8(load_at<u32x4>(vcol, voff));
-            const half8 vb = as_half8(load_at<u32x4>(vcol, voff + 32u * kRank * 2u));
-            const float16v d0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, uf[i], (float16v){}, 0, 0, 0);
-            const float16v d1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, uf[i], (float16v){}, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const uint32_t sp = tile_sign_pair(sg[i][v >> 3][q], v & 7, kp, vmask);
-              const half2v dp = __builtin_convertvector((float2v){d0[v], d1[v]}, half2v);
-              wp[v] = as_half2(sp) * dp + wp[v];
-            }
-          }
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const u32x2 v = buf_load8(make_rsrc(sbase[i]), soff + 256u * g2 + 8u * half, cb);
+          sw[i][g2][2 * half] = v[0];
+          sw[i][g2][2 * half + 1] = v[1];
         }
-#pragma unroll
-        for (int tt = P1; tt < TT; ++tt) xs[buf][tt][su][sslot] = xv[tt - P1];
-        // split the pairs by plane: bw[z][s] = W_hat[row][plane 2 qk + z, columns 16 h + 8 s .. + 7]
-        u32x4 bw[2][2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int m2 = 0; m2 < 4; ++m2) {
-            const uint32_t lo = as_u32(wp[8 * s2 + 2 * m2]), hi = as_u32(wp[8 * s2 + 2 * m2 + 1]);
-            bw[0][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-            bw[1][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-          }
-        lds_barrier();  // this step's activations are staged (the buffer written next was last read two steps ago)
-#pragma unroll
-        for (int tt = 0; tt < TT; ++tt)
-#pragma unroll
-          for (int z = 0; z < 2; ++z)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int u = 4 * z + 2 * h + s2;
-              const half8 xa = as_half8(xs[buf][tt][u][jl ^ (2 * u)]);
-              acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, as_half8(bw[z][s2]), acc[tt], 0, 0, 0);
-            }
       }
-    }
-  }
-  // lane (h, j) holds row row0 + j and tokens 8 (v / 4) + 4 h + v % 4 of every tile
-  if (row < W.m) {
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt)
+    };
+    // V rows of block i for step (c, qk): planes 2 qk, 2 qk + 1
+    struct VP { u32x4 a, b; };
+    auto load_v = [&](int c, int qk, int i) {
+      const int cc = min(c, c_end - 1);
+      const uint32_t cb = __builtin_amdgcn_readfirstlane((uint32_t)(cc * kChunkCols + 64 * qk) * (kRank * 2));  // (uniform)
+      VP v;
+      v.a = buf_load16(make_rsrc(vbase[i]), voff, cb);
+      v.b = buf_load16(make_rsrc(vbase[i]), voff + 32u * kRank * 2u, cb);
+      return v;
+    };
+    auto stage_load = [&](int c, int qk, int tt) -> u32x4 {
+      const int ucol = c * kChunkCols + 64 * qk + 8 * su;
+      return buf_load16(make_rsrc(xbase), ucol < d ? min(xr0 + (uint32_t)tt * xstep, xmax) + 2u * ucol : kBufOutOfRange);
+    };
+    // one block of a step's rebuild: W_hat pairs += sign pair * (U_i V_i^T) pair
+    auto recon_math = [&](const float16v& d0, const float16v& d1, int i, int qk, half2v (&wp)[16]) {
+      const int q = qk >> 1, kp = qk & 1;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int t = tok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (t < M) store_y(W.y, (size_t)t * W.m + row, acc[tt][v], args.y_fp32);
+        const uint32_t sp = tile_sign_pair(sw[i][v >> 3][q], v & 7, kp, vmask);
+        const half2v dp = __builtin_convertvector((float2v){d0[v], d1[v]}, half2v);
+        wp[v] = as_half2(sp) * dp + wp[v];
       }
+    };
+    // the step's W_hat pairs, completed with the partner wave's share (TH = 2), split by
+    // plane: bw[z][s] = W_hat[row][plane 2 qk + z, columns 16 h + 8 s .. + 7]
+    auto finish_tile = [&](const half2v (&wp)[16], int slot, u32x4 (&bw)[2][2]) {
+      half2v full[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) full[v] = wp[v];
+      if constexpr (TH == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 o = ex[slot][wave ^ 1][k][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) full[4 * k + e] = full[4 * k + e] + as_half2(o[e]);
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int m2 = 0; m2 < 4; ++m2) {
+          const uint32_t lo = as_u32(full[8 * s2 + 2 * m2]), hi = as_u32(full[8 * s2 + 2 * m2 + 1]);
+          bw[0][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          bw[1][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+        }
+    };
+    auto publish = [&](const half2v (&wp)[16], int slot) {
+      if constexpr (TH == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          ex[slot][wave][k][lane] = (u32x4){as_u32(wp[4 * k]), as_u32(wp[4 * k + 1]), as_u32(wp[4 * k + 2]), as_u32(wp[4 * k + 3])};
+      }
+    };
+    auto gemm_one = [&](int g, int buf, const u32x4 (&bw)[2][2]) {  // MFMA g = 4 tt + 2 z + s of a step
+      const int tt = g >> 2, z = (g >> 1) & 1, s2 = g & 1;
+      const int u = 4 * z + 2 * h + s2;
+      const half8 xa = as_half8(xs[buf][th * TT + tt][u][jl ^ (2 * u)]);
+      acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, as_half8(bw[z][s2]), acc[tt], 0, 0, 0);
+    };
+
+    // ---- prologue: step (c_begin, 0) rebuilt and staged
+    load_signs(c_begin, 0);
+    load_signs(c_begin, 1);
+    VP vq[2] = {load_v(c_begin, 0, 0), load_v(c_begin, 0, 1 % BPW)};  // V of the next two blocks to rebuild
+    half2v wp[16];  // this wave's share of the next step's W_hat pairs
+    {
+      u32x4 xv[TG];
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) xv[tt] = stage_load(c_begin, 0, tt);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const VP cur = vq[i & 1];
+        vq[i & 1] = i + 2 < BPW ? load_v(c_begin, 0, i + 2) : load_v(c_begin, 1, i + 2 - BPW);
+        float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
+        float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
+        mfma_result_ready(d0, d1);
+        recon_math(d0, d1, i, 0, wp);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TG; ++tt) xs[0][tt][su][sslot] = xv[tt];
+      publish(wp, 0);
+    }
+    lds_barrier();
+
+    // ---- steps: the body of step (c, qk) multiplies its tile with the staged activations
+    // and, interleaved, rebuilds and stages the next step (past the range's last step
+    // that work repeats the last chunk and is discarded).
+    for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+      for (int qk = 0; qk < 8; ++qk) {
+        const int buf = qk & 1;
+        const int cn = qk == 7 ? c + 1 : c, qkn = (qk + 1) & 7;       // next step
+        const int cnn = qk >= 6 ? c + 1 : c, qknn = (qk + 2) & 7;     // the one after
+        u32x4 bw[2][2];
+        finish_tile(wp, qk & 1, bw);
+        if (qk == 3) load_signs(c + 1, 0);  // quads 0-1 of this chunk are done with
+        if (qk == 7) load_signs(c + 1, 1);  // quads 2-3 likewise (refilled words are needed from (c + 1, 4))
+#pragma unroll
+        for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+        u32x4 xv[TQ];
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) {
+          // activations of the next step, a quarter at a time
+          if (i % (BPW / NQ > 0 ? BPW / NQ : 1) == 0 && i / (BPW / NQ > 0 ? BPW / NQ : 1) < NQ) {
+            const int qtr = i / (BPW / NQ > 0 ? BPW / NQ : 1);
+            if (qtr > 0) {
+#pragma unroll
+              for (int k = 0; k < TQ; ++k) xs[buf ^ 1][(qtr - 1) * TQ + k][su][sslot] = xv[k];
+            }
+#pragma unroll
+            for (int k = 0; k < TQ; ++k) xv[k] = stage_load(cn, qkn, qtr * TQ + k);
+          }
+          // next step's block i: its two MFMAs, this step's share of the GEMM, then the
+          // sign / accumulate work on the (by then finished) MFMA results
+          const VP cur = vq[i & 1];
+          vq[i & 1] = i + 2 < BPW ? load_v(cn, qkn, i + 2) : load_v(cnn, qknn, i + 2 - BPW);
+          float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
+          float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
+#pragma unroll
+          for (int g = (4 * TT * i) / BPW; g < (4 * TT * (i + 1)) / BPW; ++g) gemm_one(g, buf, bw);
+          mfma_result_ready(d0, d1);
+          recon_math(d0, d1, i, qkn, wp);
+        }
+#pragma unroll
+        for (int k = 0; k < TQ; ++k) xs[buf ^ 1][(NQ - 1) * TQ + k][su][sslot] = xv[k];
+        publish(wp, (qk + 1) & 1);
+        lds_barrier();  // next step staged and published; this step's buffers are free
+      }
+    }
   }
+
+  // lane (h, j) holds row row0 + j and tokens 8 (v / 4) + 4 h + v % 4 of every tile
+  if (W.splits == 1) {
+    if (row < W.m) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = wtok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (t < M) store_y(W.y, (size_t)t * W.m + row, acc[tt][v], args.y_fp32);
+        }
+    }
+    return;
+  }
+  // Column ranges: partial[split][token][row] (write-through at device scope), then the
+  // last workgroup of the (token group, row group) adds the ranges in order.
+  const size_t tokpad = (size_t)token_groups * 32 * TG;
+  const size_t rows_pad = (size_t)W.mt * kTileRows;
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int t = wtok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+      __hip_atomic_store(&W.partial[((size_t)split * tokpad + t) * rows_pad + row], acc[tt][v], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
+  __syncthreads();                // ... in every wave, and every wave is done with xs
+  uint32_t* last = reinterpret_cast<uint32_t*>(&xs[0][0][0][0]);
+  if (threadIdx.x == 0)
+    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
+  __syncthreads();
+  if (!*last) return;
+  const int rbeg = rg * GROUP_ROWS;
+  for (int e = threadIdx.x; e < GROUP_ROWS * 32 * TG; e += 256) {
+    const int t = tok0 + e / GROUP_ROWS, r = rbeg + e % GROUP_ROWS;
+    if (r >= W.m || t >= M) continue;
+    float sum = 0.f;
+    for (int sp = 0; sp < W.splits; ++sp)
+      sum += __hip_atomic_load(&W.partial[((size_t)sp * tokpad + t) * rows_pad + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_y(W.y, (size_t)t * W.m + r, sum, args.y_fp32);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ============================================================ debug unpack
@@ -1150,16 +1311,15 @@ int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void
   return (int)hipGetLastError();
 }
 
-int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, int row_groups, void* stream) {
-  if (row_groups == 0) return 0;
+int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream) {
+  if (args.total_items == 0) return 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(token_groups * row_groups));
+  const dim3 grid((unsigned)args.total_items);
   switch (token_tiles) {
-    case 1: hipLaunchKernelGGL(tile_kernel<1>, grid, dim3(256), 0, st, args, row_groups); break;
-    case 2: hipLaunchKernelGGL(tile_kernel<2>, grid, dim3(256), 0, st, args, row_groups); break;
-    case 4: hipLaunchKernelGGL(tile_kernel<4>, grid, dim3(256), 0, st, args, row_groups); break;
-    case 8: hipLaunchKernelGGL(tile_kernel<8>, grid, dim3(256), 0, st, args, row_groups); break;
-    case 16: hipLaunchKernelGGL(tile_kernel<16>, grid, dim3(256), 0, st, args, row_groups); break;
+    case 1: hipLaunchKernelGGL((tile_kernel<1, 2>), grid, dim3(256), 0, st, args, token_groups); break;
+    case 2: hipLaunchKernelGGL((tile_kernel<2, 2>), grid, dim3(256), 0, st, args, token_groups); break;
+    case 4: hipLaunchKernelGGL((tile_kernel<4, 2>), grid, dim3(256), 0, st, args, token_groups); break;
+    case 8: hipLaunchKernelGGL((tile_kernel<8, 2>), grid, dim3(256), 0, st, args, token_groups); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -101,7 +101,7 @@ constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-su
 constexpr int kTileGroupRows = 64;
 constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
-constexpr int kTileAutoMinTokens = 4;   // BSL_PATH_AUTO takes the tile path from this M on
+constexpr int kTileAutoMinTokens = 8;   // BSL_PATH_AUTO takes the tile path from this M on
 // Tile-path items may be cut along the columns (chunk ranges) when a launch has too few
 // of them to fill the chip; the ranges' partial sums go to a workspace of the stack.
 constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB

@@ -942,6 +942,10 @@ __device__ __forceinline__ uint32_t tile_sign_pair(uint32_t w, int e, int kp, ui
   return ((w << (14 - 2 * e + kp)) & vmask) | 0x3C003C00u;
 }
 
+// s_waitcnt immediate for "at most 4 vector memory operations outstanding" (vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima, i.e. not waited for).
+constexpr int kWaitVmcnt4 = 4 | (0x7 << 4) | (0xF << 8);
+
 // Raw buffer loads: a descriptor in scalar registers plus a 32-bit per-lane byte offset
 // (no 64-bit address arithmetic per load).  An offset at or past kBufOutOfRange reads
 // zeros without touching memory.
@@ -950,8 +954,9 @@ constexpr uint32_t kBufOutOfRange = 0x80000000u;
 // (The base is passed through readfirstlane: should the compiler keep a uniform pointer
 // in vector registers, the descriptor still ends up in scalar registers without a
 // per-lane loop around the load.)
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), (short)0, (int)(kBufOutOfRange - 1), 0x00020000);
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes = kBufOutOfRange - 1) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
@@ -983,9 +988,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int RT = 4 / TH;              // 32-row tiles per workgroup
   constexpr int GROUP_ROWS = 32 * RT;
   constexpr int BPW = kTileBatch / TH;    // blocks each wave rebuilds per batch
-  constexpr int NQ = TG >= 4 ? 4 : TG;    // activation staging quarters per step
-  constexpr int TQ = TG / NQ;
-  __shared__ u32x4 xs[2][TG][8][32];
+  // activations of a step, two buffers: [token half][tile][token][slot], token t's 16-byte
+  // unit u at slot u ^ ((t / 2) % 8) (the staging loads write 8 whole tokens per
+  // instruction; the GEMM's reads of one unit of 16 tokens hit 16 distinct bank groups)
+  __shared__ u32x4 xs0[TH][TT][32][8];
+  __shared__ u32x4 xs1[TH][TT][32][8];
   __shared__ u32x4 ex[TH == 2 ? 2 : 1][TH == 2 ? 4 : 1][4][64];  // partial W_hat tiles of the wave pairs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1009,12 +1016,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int tt = 0; tt < TT; ++tt) acc[tt] = (float16v){};
 
-  // activation staging: thread -> unit su of token stok of every tile (clamped to M - 1)
-  const int su = threadIdx.x & 7, stok = threadIdx.x >> 3;
+  // activation staging, straight into LDS: wave w fetches tokens 8 w .. 8 w + 7 of every
+  // tile, lane l the unit that belongs at slot l % 8 of token 8 w + l / 8.  The row part
+  // of each address is in the per-lane offset, which the descriptor bounds: rows past M
+  // read zeros.
   const uint16_t* xbase = W.x + (size_t)tok0 * d;  // (uniform)
-  const uint32_t xr0 = (uint32_t)stok * 2u * (uint32_t)d, xstep = 64u * (uint32_t)d;
-  const uint32_t xmax = (uint32_t)(M - 1 - tok0) * 2u * (uint32_t)d;
-  const int sslot = stok ^ (2 * su);
+  const uint32_t xbytes = (uint32_t)min(M - tok0, 32 * TG) * 2u * (uint32_t)d;
+  const int dtok = 8 * wave + (lane >> 3);
+  const int dunit = (lane & 7) ^ ((dtok >> 1) & 7);
+  const uint32_t dvo = (uint32_t)dtok * 2u * (uint32_t)d + 16u * dunit, xstep = 64u * (uint32_t)d;
   // rebuild operands: A row sigma(j) of a plane; this lane's sign-tile row and groups
   const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
   const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
@@ -1069,9 +1079,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       v.b = buf_load16(make_rsrc(vbase[i]), voff + 32u * kRank * 2u, cb);
       return v;
     };
-    auto stage_load = [&](int c, int qk, int tt) -> u32x4 {
-      const int ucol = c * kChunkCols + 64 * qk + 8 * su;
-      return buf_load16(make_rsrc(xbase), ucol < d ? min(xr0 + (uint32_t)tt * xstep, xmax) + 2u * ucol : kBufOutOfRange);
+    // activations of step (c, qk) into buffer `nb1` (0: xs0, 1: xs1): one 1 KiB load per
+    // tile per wave.  Columns past d (only in a last, partial chunk) read zeros.
+    auto stage_dma = [&](int c, int qk, int nb1) {
+      const int col0 = c * kChunkCols + 64 * qk;  // (uniform)
+      const uint32_t so = __builtin_amdgcn_readfirstlane(2u * (uint32_t)col0);
+      const rsrc_t xr = make_rsrc(xbase, xbytes);
+      uint32_t vo = dvo;
+      asm volatile("" : "+v"(vo));  // (keeps the per-tile offsets below from being hoisted out of the loop)
+      if (col0 + 8 * dunit >= d) vo = kBufOutOfRange;
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        __attribute__((address_space(3))) void* dst = nb1 ? (__attribute__((address_space(3))) void*)&xs1[t / TT][t % TT][8 * wave][0]
+                                                            : (__attribute__((address_space(3))) void*)&xs0[t / TT][t % TT][8 * wave][0];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, vo >= kBufOutOfRange ? vo : vo + (uint32_t)t * xstep, so, 0, 0);
+      }
     };
     // one block of a step's rebuild: W_hat pairs += sign pair * (U_i V_i^T) pair
     auto recon_math = [&](const float16v& d0, const float16v& d1, int i, int qk, half2v (&wp)[16]) {
@@ -1113,10 +1135,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           ex[slot][wave][k][lane] = (u32x4){as_u32(wp[4 * k]), as_u32(wp[4 * k + 1]), as_u32(wp[4 * k + 2]), as_u32(wp[4 * k + 3])};
       }
     };
-    auto gemm_one = [&](int g, int buf, const u32x4 (&bw)[2][2]) {  // MFMA g = 4 tt + 2 z + s of a step
+    // GEMM MFMA g = 4 tt + 2 z + s of a step: its activation fragment, then the product
+    auto gemm_frag = [&](int g, int buf) -> half8 {
       const int tt = g >> 2, z = (g >> 1) & 1, s2 = g & 1;
-      const int u = 4 * z + 2 * h + s2;
-      const half8 xa = as_half8(xs[buf][th * TT + tt][u][jl ^ (2 * u)]);
+      const int slot = (4 * z + 2 * h + s2) ^ ((jl >> 1) & 7);
+      return as_half8(buf ? xs1[th][tt][jl][slot] : xs0[th][tt][jl][slot]);
+    };
+    auto gemm_one = [&](int g, const half8& xa, const u32x4 (&bw)[2][2]) {
+      const int tt = g >> 2, z = (g >> 1) & 1, s2 = g & 1;
       acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa, as_half8(bw[z][s2]), acc[tt], 0, 0, 0);
     };
 
@@ -1126,9 +1152,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     VP vq[2] = {load_v(c_begin, 0, 0), load_v(c_begin, 0, 1 % BPW)};  // V of the next two blocks to rebuild
     half2v wp[16];  // this wave's share of the next step's W_hat pairs
     {
-      u32x4 xv[TG];
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) xv[tt] = stage_load(c_begin, 0, tt);
+      stage_dma(c_begin, 0, 0);
 #pragma unroll
       for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
 #pragma unroll
@@ -1140,10 +1164,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mfma_result_ready(d0, d1);
         recon_math(d0, d1, i, 0, wp);
       }
-#pragma unroll
-      for (int tt = 0; tt < TG; ++tt) xs[0][tt][su][sslot] = xv[tt];
       publish(wp, 0);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // (the staged activations are in LDS)
     lds_barrier();
 
     // ---- steps: the body of step (c, qk) multiplies its tile with the staged activations
@@ -1159,34 +1182,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         finish_tile(wp, qk & 1, bw);
         if (qk == 3) load_signs(c + 1, 0);  // quads 0-1 of this chunk are done with
         if (qk == 7) load_signs(c + 1, 1);  // quads 2-3 likewise (refilled words are needed from (c + 1, 4))
+        stage_dma(cn, qkn, buf ^ 1);        // the next step's activations, all requested up front
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
-        u32x4 xv[TQ];
 #pragma unroll
         for (int i = 0; i < BPW; ++i) {
-          // activations of the next step, a quarter at a time
-          if (i % (BPW / NQ > 0 ? BPW / NQ : 1) == 0 && i / (BPW / NQ > 0 ? BPW / NQ : 1) < NQ) {
-            const int qtr = i / (BPW / NQ > 0 ? BPW / NQ : 1);
-            if (qtr > 0) {
-#pragma unroll
-              for (int k = 0; k < TQ; ++k) xs[buf ^ 1][(qtr - 1) * TQ + k][su][sslot] = xv[k];
-            }
-#pragma unroll
-            for (int k = 0; k < TQ; ++k) xv[k] = stage_load(cn, qkn, qtr * TQ + k);
-          }
           // next step's block i: its two MFMAs, this step's share of the GEMM, then the
           // sign / accumulate work on the (by then finished) MFMA results
           const VP cur = vq[i & 1];
           vq[i & 1] = i + 2 < BPW ? load_v(cn, qkn, i + 2) : load_v(cnn, qknn, i + 2 - BPW);
+          constexpr int GPB = (4 * TT + BPW - 1) / BPW;  // GEMM MFMAs per block (at most)
+          const int g0 = (4 * TT * i) / BPW, g1 = (4 * TT * (i + 1)) / BPW;
+          half8 xa[GPB];  // (all of the block's activation fragments are requested up front)
+#pragma unroll
+          for (int g = g0; g < g1; ++g) xa[g - g0] = gemm_frag(g, buf);
           float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
           float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
 #pragma unroll
-          for (int g = (4 * TT * i) / BPW; g < (4 * TT * (i + 1)) / BPW; ++g) gemm_one(g, buf, bw);
+          for (int g = g0; g < g1; ++g) gemm_one(g, xa[g - g0], bw);
           mfma_result_ready(d0, d1);
           recon_math(d0, d1, i, qkn, wp);
         }
-#pragma unroll
-        for (int k = 0; k < TQ; ++k) xs[buf ^ 1][(NQ - 1) * TQ + k][su][sslot] = xv[k];
+        // Every load issued after this body's activation loads is one of the four V loads
+        // for the next body's first two blocks, and loads complete in order: with at most
+        // four outstanding, this wave's staging is in LDS.
+        __builtin_amdgcn_sched_barrier(0);
+        static_assert(BPW == 4, "four V loads follow the staging loads");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
         publish(wp, (qk + 1) & 1);
         lds_barrier();  // next step staged and published; this step's buffers are free
       }
@@ -1220,7 +1243,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
   __syncthreads();                // ... in every wave, and every wave is done with xs
-  uint32_t* last = reinterpret_cast<uint32_t*>(&xs[0][0][0][0]);
+  uint32_t* last = reinterpret_cast<uint32_t*>(&xs0[0][0][0][0]);
   if (threadIdx.x == 0)
     *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
   __syncthreads();

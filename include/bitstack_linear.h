@@ -146,7 +146,7 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *     the tile of W_hat is rounded to fp16 (each block's U_i V_i^T and the running sum
  *     over blocks), then y accumulates in fp32.  Work grows as n * k * m * d per group of
  *     512 tokens plus M * m * d, so it is the fast form for batches.
- *   BSL_PATH_AUTO (the default): FACTORED for M below 4, TILE from M = 4 on. */
+ *   BSL_PATH_AUTO (the default): FACTORED for M below 8, TILE from M = 8 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2

@@ -9,9 +9,11 @@ of the layer are resident (about 0.96 GB) and the steps rotate over them, so the
 256 MB last-level cache cannot serve the reads.  Bytes are the algorithmic bytes of
 the loaded blocks, n * (m d / 8 + 2 k (m + d)) per weight, counted once.
 
-Also reported: prefill at M = 2048 tokens through one such layer (MFMA TFLOP/s of the
-S Z contraction, 2 n k M m d per weight), the decode kernel's roofline from per-launch
-HIP events, and the CPU oracle (fp64 reconstruct-then-matmul) on a bounded sample.
+Also reported: prefill at M = 2048 tokens through one such layer, on the tile path
+(W_hat rebuilt per tile, then a GEMM; executed MFMA work (2 k n G + 2 M) m d per weight
+with G = ceil(M / 512) token groups) and on the factored path (the S Z contraction,
+2 n k M m d per weight); the decode kernel's roofline from per-launch HIP events; and
+the CPU oracle (fp64 reconstruct-then-matmul) on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--prefill-steps P] [--no-cpu] [--no-prefill] [--sweep] [--llama70b]
@@ -49,7 +51,7 @@ def block_bytes(m: int, d: int) -> int:
 class Layers:
     """One bitstack stack holding `layers` copies of a decoder layer's linears."""
 
-    def __init__(self, bsl, torch, shapes, counts, layers, seed, M):
+    def __init__(self, bsl, torch, shapes, counts, layers, seed, M, path=None):
         self.bsl, self.torch = bsl, torch
         self.shapes = shapes
         self.layers = layers
@@ -57,6 +59,8 @@ class Layers:
         ms = [m for _ in range(layers) for (_, m, _) in shapes]
         ds = [d for _ in range(layers) for (_, _, d) in shapes]
         self.h = bsl.bsl_init(0, ms, ds, 16, 16, 0)
+        if path is not None:
+            bsl.bsl_set_path(self.h, path)
         self.counts = []
         for l in range(layers):
             for j, (_, m, d) in enumerate(shapes):
@@ -89,7 +93,18 @@ class Layers:
         return sum(self.counts[l * self.per + j] * block_bytes(m, d) for j, (_, m, d) in enumerate(self.shapes))
 
     def flops(self, l: int) -> int:
+        """MFMA work of the factored formulation (the S Z contraction)."""
         return sum(2 * self.counts[l * self.per + j] * K_RANK * self.M * m * d for j, (_, m, d) in enumerate(self.shapes))
+
+    def tile_flops(self, l: int) -> int:
+        """MFMA work of the tile formulation: every group of up to 512 tokens rebuilds W_hat
+        (K = k products, 2 k n m d) and multiplies it with its tokens (2 M m d)."""
+        groups = -(-self.M // 512)
+        return sum((2 * K_RANK * self.counts[l * self.per + j] * groups + 2 * self.M) * m * d
+                   for j, (_, m, d) in enumerate(self.shapes))
+
+    def gemm_flops(self, l: int) -> int:
+        return sum(2 * self.M * m * d for (_, m, d) in self.shapes)
 
     def close(self):
         self.torch.cuda.synchronize()
@@ -261,7 +276,8 @@ def main() -> None:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=4)
-    ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--prefill-steps", type=int, default=2, help="timed steps of the factored M=2048 prefill")
+    ap.add_argument("--tile-steps", type=int, default=20, help="timed steps of the tile-path M=2048 prefill")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
@@ -363,21 +379,44 @@ def main() -> None:
     if per_weight:
         result["decode_single_weight_launches"] = per_weight
 
-    # ---------------- prefill M = 2048
+    # ---------------- prefill M = 2048: tile path (the default for batches), then factored
     if not args.no_prefill:
-        log("prefill: one 8B-shaped layer, n=8, M=2048")
-        pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048)
+        log("prefill: one 8B-shaped layer, n=8, M=2048, tile path")
+        pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_TILE)
+        wall_t, kms_t, _, _ = time_steps(torch, pre, args.tile_steps, 2)
+        t_step = wall_t / args.tile_steps
+        tfl_t = pre.tile_flops(0) / t_step / 1e12
+        k_step = float(np.mean(kms_t)) * 1e-3
+        result["prefill"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, one grouped launch per step, tile path",
+            "ms_per_step": round(t_step * 1e3, 3),
+            "tokens_per_s": round(2048 / t_step, 1),
+            "kernel": "tile_kernel",
+            "mfma_flops_per_step": pre.tile_flops(0),
+            "roofline": {"bound": "mfma", "achieved": round(pre.tile_flops(0) / k_step / 1e12, 1),
+                         "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(pre.tile_flops(0) / k_step / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                         "avg_launch_us": round(k_step * 1e6, 1)},
+            "gemm_equivalent_tflops": round(pre.gemm_flops(0) / t_step / 1e12, 1),
+        }
+        log(f"prefill (tile): {t_step * 1e3:.2f} ms/step, {tfl_t:.1f} TFLOP/s executed MFMA work")
+        pre.close()
+        del pre
+        torch.cuda.empty_cache()
+        log("prefill: one 8B-shaped layer, n=8, M=2048, factored path")
+        pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_FACTORED)
         wall_p, kms_p, tb_p, tf_p = time_steps(torch, pre, args.prefill_steps, 1)
         tfl = tf_p / wall_p / 1e12
-        result["prefill"] = {
-            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, one grouped launch per step",
+        result["prefill_factored"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, one grouped launch per step, factored path",
             "ms_per_step": round(wall_p * 1e3 / args.prefill_steps, 2),
             "mfma_tflops": round(tfl, 1),
             "mfma_frac_of_peak": round(tfl / FP16_MFMA_PEAK_TFLOPS, 4),
             "kernel": "prefill_kernel",
             "flops_per_step": int(tf_p // args.prefill_steps),
         }
-        log(f"prefill: {wall_p * 1e3 / args.prefill_steps:.1f} ms/step, {tfl:.1f} TFLOP/s")
+        result["prefill"]["speedup_vs_factored"] = round(result["prefill_factored"]["ms_per_step"] / result["prefill"]["ms_per_step"], 1)
+        log(f"prefill (factored): {wall_p * 1e3 / args.prefill_steps:.1f} ms/step, {tfl:.1f} TFLOP/s")
         pre.close()
         del pre
         torch.cuda.empty_cache()
@@ -390,7 +429,8 @@ def main() -> None:
             lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M)
             w_, k_, b_, f_ = time_steps(torch, lay, 50, 5)
             sweep.append({"M": M, "n_w": [int(c) for c in counts], "GB/s": round(b_ / w_ / 1e9, 1),
-                          "mfma_tflops": round(f_ / w_ / 1e12, 1), "us_per_step": round(w_ * 1e6 / 50, 1)})
+                          "path": "single-token" if M == 1 else ("tile" if M >= 8 else "factored"),
+                          "sz_equivalent_tflops": round(f_ / w_ / 1e12, 1), "us_per_step": round(w_ * 1e6 / 50, 1)})
             lay.close()
             del lay
             torch.cuda.empty_cache()

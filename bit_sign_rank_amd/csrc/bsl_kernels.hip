@@ -27,6 +27,10 @@
 //  * multi-token kernel (M >= 2): dense v_mfma_f32_32x32x16_f16 on exact +-1 fp16 A
 //    fragments (a packed 16-bit shift and one AND-OR per word); there the unpack is
 //    amortised over the token pairs, and the sparse 32x32 MFMA measured slower.
+//  * tile-reconstruct kernel (batches): the other formulation of the same layer.  W_hat
+//    is restored tile by tile in registers (one K = 16 MFMA per block and 32 x 32 tile,
+//    signs applied as +-1 fp16 pairs) and multiplied at once with up to 512 tokens, so
+//    the sign and low-rank work is paid once per token group instead of once per token.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -105,6 +105,7 @@ constexpr int kTileAutoMinTokens = 8;   // BSL_PATH_AUTO takes the tile path fro
 // Tile-path items may be cut along the columns (chunk ranges) when a launch has too few
 // of them to fill the chip; the ranges' partial sums go to a workspace of the stack.
 constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB
+constexpr int kTileItemsPerCu = 2;     // aim of the column-range cutting
 constexpr int kTileCounters = 1 << 16;
 
 }  // namespace bsl

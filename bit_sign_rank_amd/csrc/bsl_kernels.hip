@@ -946,9 +946,9 @@ __device__ __forceinline__ uint32_t tile_sign_pair(uint32_t w, int e, int kp, ui
   return ((w << (14 - 2 * e + kp)) & vmask) | 0x3C003C00u;
 }
 
-// s_waitcnt immediate for "at most 4 vector memory operations outstanding" (vmcnt in
+// s_waitcnt immediate for "at most 8 vector memory operations outstanding" (vmcnt in
 // bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima, i.e. not waited for).
-constexpr int kWaitVmcnt4 = 4 | (0x7 << 4) | (0xF << 8);
+constexpr int kWaitVmcnt8 = 8 | (0x7 << 4) | (0xF << 8);
 
 // Raw buffer loads: a descriptor in scalar registers plus a 32-bit per-lane byte offset
 // (no 64-bit address arithmetic per load).  An offset at or past kBufOutOfRange reads
@@ -984,6 +984,13 @@ __device__ __forceinline__ float16v rebuild_mfma(const half8& a, const half8& b)
 // result needs before a VALU operation may read it (at most 19).
 __device__ __forceinline__ void mfma_result_ready(float16v& d0, float16v& d1) {
   asm("s_nop 15\n\ts_nop 3" : "+v"(d0), "+v"(d1));
+}
+// The same once two later rebuild MFMAs (whose results n0, n1 are) have been issued:
+// each waits for the matrix pipe (32 cycles per 32x32x16 MFMA), so d0 and d1 are long
+// ready; tying the hand-over to n0, n1 keeps it from moving above those MFMAs.
+__device__ __forceinline__ void mfma_result_ready_after(float16v& d0, float16v& d1, const float16v& n0,
+                                                        const float16v& n1) {
+  asm("" : "+v"(d0), "+v"(d1) : "v"(n0), "v"(n1));
 }
 
 template <int TT, int TH>
@@ -1153,7 +1160,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- prologue: step (c_begin, 0) rebuilt and staged
     load_signs(c_begin, 0);
     load_signs(c_begin, 1);
-    VP vq[2] = {load_v(c_begin, 0, 0), load_v(c_begin, 0, 1 % BPW)};  // V of the next two blocks to rebuild
+    VP vq[BPW];  // V rows of every block of the next step to rebuild (a full step ahead)
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) vq[i] = load_v(c_begin, 0, i);
     half2v wp[16];  // this wave's share of the next step's W_hat pairs
     {
       stage_dma(c_begin, 0, 0);
@@ -1161,8 +1170,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
-        const VP cur = vq[i & 1];
-        vq[i & 1] = i + 2 < BPW ? load_v(c_begin, 0, i + 2) : load_v(c_begin, 1, i + 2 - BPW);
+        const VP cur = vq[i];
+        vq[i] = load_v(c_begin, 1, i);
         float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
         float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
         mfma_result_ready(d0, d1);
@@ -1190,30 +1199,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+        // With few GEMM MFMAs per block (TT <= 4) nothing would cover the rebuild MFMAs'
+        // latency, so their results are consumed one block later.
+        constexpr bool PIPE = TT <= 4;
+        float16v dn0, dn1;
+        if constexpr (PIPE) {
+          dn0 = rebuild_mfma(as_half8(vq[0].a), uf[0]);
+          dn1 = rebuild_mfma(as_half8(vq[0].b), uf[0]);
+        }
 #pragma unroll
         for (int i = 0; i < BPW; ++i) {
           // next step's block i: its two MFMAs, this step's share of the GEMM, then the
           // sign / accumulate work on the (by then finished) MFMA results
-          const VP cur = vq[i & 1];
-          vq[i & 1] = i + 2 < BPW ? load_v(cn, qkn, i + 2) : load_v(cnn, qknn, i + 2 - BPW);
+          const VP cur = vq[i];
+          vq[i] = load_v(cnn, qknn, i);
           constexpr int GPB = (4 * TT + BPW - 1) / BPW;  // GEMM MFMAs per block (at most)
           const int g0 = (4 * TT * i) / BPW, g1 = (4 * TT * (i + 1)) / BPW;
           half8 xa[GPB];  // (all of the block's activation fragments are requested up front)
 #pragma unroll
           for (int g = g0; g < g1; ++g) xa[g - g0] = gemm_frag(g, buf);
-          float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
-          float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
+          float16v d0, d1;
+          if constexpr (PIPE) {
+            d0 = dn0;
+            d1 = dn1;
+            if (i + 1 < BPW) {
+              dn0 = rebuild_mfma(as_half8(vq[i + 1].a), uf[i + 1]);
+              dn1 = rebuild_mfma(as_half8(vq[i + 1].b), uf[i + 1]);
+            }
+          } else {
+            d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
+            d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
+          }
 #pragma unroll
           for (int g = g0; g < g1; ++g) gemm_one(g, xa[g - g0], bw);
-          mfma_result_ready(d0, d1);
+          if (PIPE && i + 1 < BPW)
+            mfma_result_ready_after(d0, d1, dn0, dn1);
+          else
+            mfma_result_ready(d0, d1);
           recon_math(d0, d1, i, qkn, wp);
         }
-        // Every load issued after this body's activation loads is one of the four V loads
-        // for the next body's first two blocks, and loads complete in order: with at most
-        // four outstanding, this wave's staging is in LDS.
+        // Every load issued after this body's activation loads is one of the 2 BPW V loads
+        // for the next body, and loads complete in order: with at most that many
+        // outstanding, this wave's staging is in LDS.
         __builtin_amdgcn_sched_barrier(0);
-        static_assert(BPW == 4, "four V loads follow the staging loads");
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt4);
+        static_assert(2 * BPW == 8, "eight V loads follow the staging loads");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt8);
         publish(wp, (qk + 1) & 1);
         lds_barrier();  // next step staged and published; this step's buffers are free
       }

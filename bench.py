@@ -17,7 +17,7 @@ the CPU oracle (fp64 reconstruct-then-matmul) on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers L]
                        [--prefill-steps P] [--no-cpu] [--no-prefill] [--sweep] [--llama70b]
-                       [--per-weight] [--calibrate-copy] [--cpu-layers C]
+                       [--per-weight] [--calibrate-copy] [--load] [--cpu-layers C]
 """
 from __future__ import annotations
 
@@ -258,6 +258,75 @@ kernel_source_sha256: {digest}
     print(open(TRAFFIC_SUMMARY).read())
 
 
+def block_streaming(bsl, torch, seed: int) -> dict:
+    """Host -> device block loading (pack on the host into pinned staging, asynchronous
+    copy) of one 8B-shaped layer at n = 8: its rate alone, and while single-token decode
+    forwards of another stack run on a second stream (both rates reported)."""
+    shapes = synth.LLAMA3_8B_LAYER
+    src = [synth.synthetic_blocks(seed, m, d, 8, 16, 0, j) for j, (_, m, d) in enumerate(shapes)]
+    layer_bytes = sum(8 * block_bytes(m, d) for _, m, d in shapes)
+    h = bsl.bsl_init(0, [m for _, m, _ in shapes], [d for _, _, d in shapes], 16, 16, 0)
+    for j, b in enumerate(src):
+        bsl.bsl_set_source(h, j, b)
+    s2 = torch.cuda.Stream()
+    sp2 = int(s2.cuda_stream)
+
+    def unload():  # (a shrink waits for the whole device, so it is done beforehand)
+        bsl.bsl_load_blocks(h, [0] * 7, sp2)
+
+    def load_all():
+        t0 = time.perf_counter()
+        bsl.bsl_load_blocks(h, [8] * 7, sp2)
+        return time.perf_counter() - t0
+
+    load_all()  # (first call allocates the pinned staging)
+    times = []
+    for _ in range(2):
+        unload()
+        times.append(load_all())
+    alone = min(times)
+    # one more block of the largest weight (gate, 14336 x 4096)
+    bsl.bsl_load_blocks(h, [8, 8, 8, 8, 7, 8, 8], sp2)
+    t0 = time.perf_counter()
+    bsl.bsl_load_blocks(h, [8] * 7, sp2)
+    one_block = time.perf_counter() - t0
+    # decode on another stack and stream, alone and during a load
+    dec = Layers(bsl, torch, shapes, [[8] * 7] * 2, 2, seed + 1, M=1)
+    s1 = torch.cuda.current_stream()
+    sp1 = int(s1.cuda_stream)
+
+    def decode_span(k, during_load):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if during_load:
+            unload()
+        torch.cuda.synchronize()
+        e0.record(s1)
+        for i in range(k):
+            dec.launch(i % 2, sp1)
+        e1.record(s1)
+        wall = load_all() if during_load else None
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k, wall
+
+    k = max(200, int(alone / 80e-6))  # enough decode work to cover the load
+    dec_alone, _ = decode_span(k, False)
+    dec_during, load_during = decode_span(k, True)
+    dec.close()
+    bsl.bsl_destroy(h)
+    return {
+        "workload": "Llama-3-8B-shaped layer, 7 linears x 8 blocks (k=16), packed on the host and copied to the device",
+        "layer_bytes": layer_bytes,
+        "load_ms": round(alone * 1e3, 1),
+        "load_GB_per_s": round(layer_bytes / alone / 1e9, 2),
+        "one_gate_block_ms": round(one_block * 1e3, 2),
+        "one_gate_block_bytes": block_bytes(14336, 4096),
+        "load_during_decode_ms": round(load_during * 1e3, 1),
+        "load_during_decode_GB_per_s": round(layer_bytes / load_during / 1e9, 2),
+        "decode_us_per_step_alone": round(dec_alone, 2),
+        "decode_us_per_step_during_load": round(dec_during, 2),
+    }
+
+
 def copy_calibration(torch, mib: int = 1024, reps: int = 3) -> None:
     """A plain elementwise copy (y = -x, fp16) of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters: each dispatch reads and writes exactly `mib` MiB."""
@@ -284,6 +353,7 @@ def main() -> None:
     ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
     ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--load", action="store_true", help="also measure host -> device block streaming, alone and beside decode")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--write-profile-summaries", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
@@ -445,6 +515,11 @@ def main() -> None:
         result["llama2_70b_decode"] = {"ms_per_token": round(tok_ms, 3), "GB/s": round(b_ / w_ / 1e9, 1),
                                        "bytes_per_token": int(b_ // 3)}
         lay.close()
+
+    if args.load:
+        log("block streaming: loading an 8B-shaped layer, alone and beside decode")
+        result["block_streaming"] = block_streaming(bsl, torch, args.seed + 31)
+        log(f"block streaming: {result['block_streaming']}")
 
     # ---------------- CPU oracle
     if not args.no_cpu:

@@ -153,6 +153,9 @@ struct bsl_stack {
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
   uint32_t* arrivals = nullptr;   // single-token arrival counters, one per row group of a launch
   float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
+  uint8_t* staging[2] = {nullptr, nullptr};  // pinned host buffers of bsl_load_blocks (allocated on first use)
+  size_t staging_bytes = 0;
+  hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] finished
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
   std::vector<Weight> w;
 };
@@ -188,11 +191,14 @@ struct DeviceGuard {
   }
 };
 
-int upload_table(bsl_stack* s, Weight& W, hipStream_t st) {
-  std::vector<BlockPtrs> tab(s->n_cap);
-  for (int32_t i = 0; i < s->n_cap; ++i)
-    tab[i] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
-  hipError_t e = hipMemcpyAsync(W.dtable, tab.data(), sizeof(BlockPtrs) * s->n_cap, hipMemcpyHostToDevice, st);
+// Writes table entries [lo, hi) only: entries below lo may be read meanwhile by forwards
+// still running on other streams (a grown weight keeps its first blocks).
+int upload_table(Weight& W, int32_t lo, int32_t hi, hipStream_t st) {
+  if (hi <= lo) return BSL_OK;
+  std::vector<BlockPtrs> tab(hi - lo);
+  for (int32_t i = lo; i < hi; ++i)
+    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
+  hipError_t e = hipMemcpyAsync(W.dtable + lo, tab.data(), sizeof(BlockPtrs) * (hi - lo), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
 }
@@ -377,43 +383,66 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     undo();
     return hip_fail(e, "hipMalloc(block)");
   }
-  // phase 2: pack on the host and copy the new blocks
-  std::vector<uint8_t> staging;
-  for (const NewSlot& a : added) {
+  // phase 2: pack on the host and copy the new blocks.  Two pinned staging buffers take
+  // turns: block k is packed into one while the copy of block k - 1 runs from the other
+  // (asynchronous DMA on `stream`, so forwards queued on other streams keep running).
+  size_t need = 0;
+  for (const NewSlot& a : added) need = std::max(need, slot_bytes(s->w[a.w].m, s->w[a.w].d));
+  if (need > s->staging_bytes) {
+    for (int k = 0; k < 2; ++k) {
+      if (s->staging[k]) (void)hipHostFree(s->staging[k]);
+      s->staging[k] = nullptr;
+    }
+    s->staging_bytes = 0;
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipHostMalloc(reinterpret_cast<void**>(&s->staging[k]), need, hipHostMallocDefault);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k)
+      if (!s->staged[k]) e = hipEventCreateWithFlags(&s->staged[k], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      undo();
+      return hip_fail(e, "pinned staging buffers");
+    }
+    s->staging_bytes = need;
+  }
+  for (size_t k = 0; k < added.size() && e == hipSuccess; ++k) {
+    const NewSlot& a = added[k];
     Weight& W = s->w[a.w];
     const bsl_block_src& src = W.src[a.i];
     const size_t sb = (size_t)pad_rows(W.m) * pad_cols(W.d) / 8;
     const size_t ub = (size_t)pad_rows(W.m) * kRank * 2;
     const size_t vb = (size_t)pad_cols(W.d) * kRank * 2;
-    staging.resize(sb + ub + 2 * vb);
-    pack_signs_mt(src.sign_bits, W.m, W.d, staging.data());
-    tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(staging.data() + sb));
-    tile_v(src.v, W.d, reinterpret_cast<uint16_t*>(staging.data() + sb + ub));
-    rowmajor_v(src.v, W.d, reinterpret_cast<uint16_t*>(staging.data() + sb + ub + vb));
-    e = hipMemcpyAsync(W.slots[a.i].mem, staging.data(), staging.size(), hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);  // staging is reused
-    if (e != hipSuccess) {
-      undo();
-      return hip_fail(e, "block upload");
-    }
+    uint8_t* buf = s->staging[k % 2];
+    if (k >= 2 && (e = hipEventSynchronize(s->staged[k % 2])) != hipSuccess) break;  // its last copy is done
+    pack_signs_mt(src.sign_bits, W.m, W.d, buf);
+    tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(buf + sb));
+    tile_v(src.v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
+    rowmajor_v(src.v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
+    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + ub + 2 * vb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(st);
+    undo();
+    return hip_fail(e, "block upload");
   }
   // phase 3: publish the new slots in each grown weight's device table.  The table
   // lists every allocated slot; the kernels read only the first n entries, so a
   // shrink needs no table change and entries past n are never dereferenced.
   for (int32_t w = 0; w < nw; ++w) {
     if (n_per_weight[w] <= s->w[w].n) continue;
-    int rc = upload_table(s, s->w[w], st);
+    int rc = upload_table(s->w[w], s->w[w].n, n_per_weight[w], st);
     if (rc != BSL_OK) {
       undo();
       return rc;
     }
   }
-  // phase 4: commit.  Shrinking waits for the stream so no queued forward still reads a slot.
+  // phase 4: commit.  Shrinking waits for the whole device: a forward that reads a slot
+  // about to be released may be queued on any stream.
   bool shrink = false;
   for (int32_t w = 0; w < nw; ++w) shrink |= n_per_weight[w] < s->w[w].n;
-  if (shrink && (e = hipStreamSynchronize(st)) != hipSuccess) {
+  if (shrink && (e = hipDeviceSynchronize()) != hipSuccess) {
     undo();
-    return hip_fail(e, "hipStreamSynchronize");
+    return hip_fail(e, "hipDeviceSynchronize");
   }
   for (int32_t w = 0; w < nw; ++w) {
     Weight& W = s->w[w];
@@ -679,6 +708,10 @@ void bsl_destroy(bsl_stack* s) {
   if (s->arrivals) (void)hipFree(s->arrivals);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);
+  for (int k = 0; k < 2; ++k) {
+    if (s->staging[k]) (void)hipHostFree(s->staging[k]);
+    if (s->staged[k]) (void)hipEventDestroy(s->staged[k]);
+  }
   delete s;
 }
 

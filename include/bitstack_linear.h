@@ -109,10 +109,16 @@ int bsl_set_source(bsl_stack* s, int32_t w, int32_t n_avail, const bsl_block_src
 
 /* Set the number of loaded blocks of every weight to n_per_weight[w] (host array of
  * num_weights entries, 0 <= n <= min(n_cap, n_avail)).  Growing packs and copies only
- * the new blocks [n_old, n_new) (host -> device on `stream`, then waits for them);
- * shrinking waits for `stream` to drain and then releases blocks [n_new, n_old).  The
- * call is all-or-nothing: on any failure every weight keeps its previous count and no
- * memory is leaked.  Blocks that stay loaded are never moved or rewritten. */
+ * the new blocks [n_old, n_new): each is packed on the host into one of two pinned
+ * staging buffers while the previous one is copied to the device asynchronously on
+ * `stream`, and the call returns once the copies are done.  Forwards already queued on
+ * other streams keep running meanwhile and keep using the counts they were queued with
+ * (only the new entries of the device block table are written).  Shrinking waits for
+ * the device to drain and then releases blocks [n_new, n_old).  The call is
+ * all-or-nothing: on any failure every weight keeps its previous count and no memory is
+ * leaked.  Blocks that stay loaded are never moved or rewritten.  (Universal stack:
+ * blocks are loaded and offloaded as memory allows; paper-review page, Figure 2
+ * caption.) */
 int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
 
 /* Number of loaded blocks of weight w. */

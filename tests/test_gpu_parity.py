@@ -117,6 +117,38 @@ def test_non_default_stream(cfg1_blocks):
     assert rel_err(y, oracle.forward(x, cfg1_blocks, 4)) <= REL_TOL
 
 
+def test_load_overlaps_forwards_on_another_stream(cfg1_blocks):
+    # Forwards of weight 0 with 2 blocks are queued on one stream; while they run, weight 0
+    # grows to 4 blocks and weight 1 is loaded on a second stream.  The queued forwards
+    # keep their block count (the load writes only new table entries), later ones see the
+    # new counts.
+    other = synth.synthetic_blocks(33, 1024, 1024, 3, 16, 1)
+    x = synth.activations(34, 8, 1024)
+    xt = torch.from_numpy(x).cuda()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with Stack([(1024, 1024, cfg1_blocks), (1024, 1024, other)]) as st:
+        st.load([2, 0])
+        torch.cuda.synchronize()
+        before = []
+        with torch.cuda.stream(s1):
+            for _ in range(16):
+                y = torch.empty((8, 1024), dtype=torch.float32, device="cuda")
+                bsl.bsl_forward(st.h, 0, xt.data_ptr(), y.data_ptr(), 8, True, int(s1.cuda_stream))
+                before.append(y)
+        bsl.bsl_load_blocks(st.h, [4, 3], int(s2.cuda_stream))
+        with torch.cuda.stream(s1):
+            y0 = torch.empty((8, 1024), dtype=torch.float32, device="cuda")
+            y1 = torch.empty((8, 1024), dtype=torch.float32, device="cuda")
+            bsl.bsl_forward(st.h, 0, xt.data_ptr(), y0.data_ptr(), 8, True, int(s1.cuda_stream))
+            bsl.bsl_forward(st.h, 1, xt.data_ptr(), y1.data_ptr(), 8, True, int(s1.cuda_stream))
+        torch.cuda.synchronize()
+        ref2 = oracle.forward(x, cfg1_blocks, 2)
+        for y in before:
+            assert rel_err(y.cpu().numpy().astype(np.float64), ref2) <= REL_TOL
+        assert rel_err(y0.cpu().numpy().astype(np.float64), oracle.forward(x, cfg1_blocks, 4)) <= REL_TOL
+        assert rel_err(y1.cpu().numpy().astype(np.float64), oracle.forward(x, other, 3)) <= REL_TOL
+
+
 # ---------------------------------------------------------------- 8B decoder layer
 def layer_blocks(shapes, counts, seed, layer=0):
     return [(m, d, synth.synthetic_blocks(seed, m, d, int(n), 16, layer, j)) for j, ((_, m, d), n) in enumerate(zip(shapes, counts))]

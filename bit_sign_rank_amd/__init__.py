@@ -33,6 +33,7 @@ EXPORTED = (
     "bsl_init",
     "bsl_set_path",
     "bsl_set_source",
+    "bsl_set_input_scale",
     "bsl_load_blocks",
     "bsl_active_blocks",
     "bsl_resident_bytes",
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_unpack_signs.argtypes = [c_vp, c_i64, c_i64, c_vp]
         L.bsl_init.argtypes = [ctypes.POINTER(c_vp), ctypes.c_int, c_i32, c_vp, c_vp, c_i32, c_i32, c_u64]
         L.bsl_set_source.argtypes = [c_vp, c_i32, c_i32, c_vp]
+        L.bsl_set_input_scale.argtypes = [c_vp, c_i32, c_vp]
         L.bsl_load_blocks.argtypes = [c_vp, c_vp, c_vp]
         L.bsl_active_blocks.argtypes = [c_vp, c_i32, ctypes.POINTER(c_i32)]
         L.bsl_resident_bytes.restype = c_u64
@@ -154,6 +156,15 @@ def bsl_set_source(stack: int, w: int, blocks) -> None:
         arr[i].sign_bits, arr[i].u, arr[i].v = _ptr(bits), _ptr(u), _ptr(v)
     _check(lib().bsl_set_source(stack, w, len(blocks), ctypes.addressof(arr)))
     _sources[(stack, w)] = keep
+
+
+def bsl_set_input_scale(stack: int, w: int, inv_scale) -> None:
+    """inv_scale: ``d`` positive floats (1 / the per-input-channel scale), or None."""
+    if inv_scale is None:
+        _check(lib().bsl_set_input_scale(stack, w, None))
+        return
+    a = np.ascontiguousarray(inv_scale, dtype=np.float32)
+    _check(lib().bsl_set_input_scale(stack, w, _ptr(a)))
 
 
 def bsl_load_blocks(stack: int, n_per_weight, stream: int = 0) -> None:

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -14,6 +15,7 @@
 #include <thread>
 #include <vector>
 
+#include "bsl_fp16.h"
 #include "bsl_internal.h"
 
 using namespace bsl;
@@ -124,6 +126,14 @@ void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
   std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
 }
 
+// V (d x 16) with row c multiplied by inv_scale[c]: one rounding of the exact product.
+bool scale_v(const uint16_t* v, int64_t d, const float* inv_scale, uint16_t* out) {
+  for (int64_t c = 0; c < d; ++c)
+    for (int r = 0; r < kRank; ++r)
+      if (!double_to_fp16(fp16_to_double(v[c * kRank + r]) * (double)inv_scale[c], &out[c * kRank + r])) return false;
+  return true;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ stack
@@ -137,6 +147,7 @@ struct Weight {
   int32_t n = 0;  // loaded blocks
   std::vector<bsl_block_src> src;
   std::vector<Slot> slots;          // [n_cap]
+  std::vector<float> inv_scale;     // [d] input-channel scale folded into V at load (empty: none)
   BlockPtrs* dtable = nullptr;      // device [n_cap]
   float* partial = nullptr;         // workspace
   uint32_t* counters = nullptr;     // workspace: arrival counters of the multi-token path
@@ -333,6 +344,22 @@ int bsl_set_source(bsl_stack* s, int32_t w, int32_t n_avail, const bsl_block_src
   return BSL_OK;
 }
 
+int bsl_set_input_scale(bsl_stack* s, int32_t w, const float* inv_scale) {
+  if (!s) return fail(BSL_EINVAL, "bsl_set_input_scale: null stack");
+  if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "bsl_set_input_scale: weight index out of range");
+  Weight& W = s->w[w];
+  if (W.n != 0) return fail(BSL_EINVAL, "bsl_set_input_scale: weight " + std::to_string(w) + " has loaded blocks");
+  if (!inv_scale) {
+    W.inv_scale.clear();
+    return BSL_OK;
+  }
+  for (int32_t c = 0; c < W.d; ++c)
+    if (!(std::isfinite(inv_scale[c]) && inv_scale[c] > 0.0f))
+      return fail(BSL_EINVAL, "bsl_set_input_scale: inv_scale[" + std::to_string(c) + "] is not finite and positive");
+  W.inv_scale.assign(inv_scale, inv_scale + W.d);
+  return BSL_OK;
+}
+
 int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
   if (!s || !n_per_weight) return fail(BSL_EINVAL, "bsl_load_blocks: null pointer");
   const int32_t nw = (int32_t)s->w.size();
@@ -403,6 +430,8 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     }
     s->staging_bytes = need;
   }
+  std::vector<uint16_t> vscaled;  // V of a scaled weight
+  NewSlot overflow = {-1, -1};
   for (size_t k = 0; k < added.size() && e == hipSuccess; ++k) {
     const NewSlot& a = added[k];
     Weight& W = s->w[a.w];
@@ -414,8 +443,17 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     if (k >= 2 && (e = hipEventSynchronize(s->staged[k % 2])) != hipSuccess) break;  // its last copy is done
     pack_signs_mt(src.sign_bits, W.m, W.d, buf);
     tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(buf + sb));
-    tile_v(src.v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
-    rowmajor_v(src.v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
+    const uint16_t* v = src.v;
+    if (!W.inv_scale.empty()) {
+      vscaled.resize((size_t)W.d * kRank);
+      if (!scale_v(v, W.d, W.inv_scale.data(), vscaled.data())) {
+        overflow = a;
+        break;
+      }
+      v = vscaled.data();
+    }
+    tile_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
+    rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
     e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + ub + 2 * vb, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }
@@ -424,6 +462,11 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     (void)hipStreamSynchronize(st);
     undo();
     return hip_fail(e, "block upload");
+  }
+  if (overflow.w >= 0) {  // the copies queued before it are done (synchronised above)
+    undo();
+    return fail(BSL_EINVAL, "bsl_load_blocks: block " + std::to_string(overflow.i) + " of weight " +
+                                std::to_string(overflow.w) + ": V times the input scale overflows fp16");
   }
   // phase 3: publish the new slots in each grown weight's device table.  The table
   // lists every allocated slot; the kernels read only the first n entries, so a

@@ -107,6 +107,22 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
  * next bsl_set_source for w or bsl_destroy; only bsl_load_blocks reads them. */
 int bsl_set_source(bsl_stack* s, int32_t w, int32_t n_avail, const bsl_block_src* blocks);
 
+/* Activation-aware scaling (paper-review page, Figure 5 caption: the "w/o scaling"
+ * ablation drops the scaling of Eq. 4; the equation itself is not printed there).
+ * Reading taken: the blocks of weight w decompose W diag(s), where s > 0 holds one
+ * factor per input channel drawn from activation statistics, so the layer is
+ *     y = (x (.) inv_scale) W_hat_n^T,   inv_scale[c] = 1 / s[c]   (c < d).
+ * Column scaling commutes with the elementwise sign product, so inv_scale is folded
+ * into V at load: bsl_load_blocks stores fp16(V_i[c][r] * inv_scale[c]) (exact product,
+ * one rounding to nearest even) and every forward path then costs exactly what the
+ * unscaled layer costs.
+ *   inv_scale: host, d[w] floats, each finite and > 0; copied, so the caller may free
+ *     it on return.  NULL removes the scale (inv_scale = 1).
+ * Only allowed while weight w has no loaded blocks (BSL_EINVAL otherwise), so every
+ * loaded block of a weight carries the same scale.  bsl_load_blocks fails with
+ * BSL_EINVAL, loading nothing, if a scaled V entry would overflow fp16. */
+int bsl_set_input_scale(bsl_stack* s, int32_t w, const float* inv_scale);
+
 /* Set the number of loaded blocks of every weight to n_per_weight[w] (host array of
  * num_weights entries, 0 <= n <= min(n_cap, n_avail)).  Growing packs and copies only
  * the new blocks [n_old, n_new): each is packed on the host into one of two pinned
@@ -148,7 +164,7 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *     multi-token kernel otherwise).  Work grows as n * k * M * m * d.
  *   BSL_PATH_TILE: the weight restoration the authors give (add each block's unpacked
  *     signs times U_i V_i^T; OpenReview discussion, weight-restoration reply), done per
- *     128-row x 64-column tile in registers and multiplied at once with up to 512 tokens:
+ *     32 x 32 tile in registers and multiplied at once with up to 512 tokens:
  *     the tile of W_hat is rounded to fp16 (each block's U_i V_i^T and the running sum
  *     over blocks), then y accumulates in fp32.  Work grows as n * k * m * d per group of
  *     512 tokens plus M * m * d, so it is the fast form for batches.

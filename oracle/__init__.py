@@ -13,6 +13,8 @@ computes, written from the pages that describe the method:
   block is a +-1 sign matrix (packed into GPU data types) plus singular vectors
   from an absolute value decomposition (AVD); Figure 5 caption: the equal-size
   rank k' of a vanilla-SVD block.
+* Same page, Figure 5 caption: the "w/o scaling" ablation (activation-aware scaling
+  of Eq. 4, whose formula the pages do not print; see ``scaling`` for the reading).
 * Abstract (codewithpapers page "BitStack: Any-Size Compression of Large Language
   Models in Variable Memory Environments"): each decomposition iteration yields an
   approximately 1-bit-per-parameter residual block.
@@ -26,6 +28,7 @@ Modules:
   signs    -- row-major sign-bit <-> +-1 conversion (the input format)
   avd      -- one absolute-value-decomposition step and the iterated decomposition
   restore  -- dense fp64 reconstruct-then-matmul forward, block byte count
+  scaling  -- the layer with an input-channel scale (activation-aware scaling)
 
 Parity status: every function is pinned by ``tests/test_oracle.py`` against
 closed forms, invariants, special cases and brute force (see the list there).
@@ -33,3 +36,4 @@ closed forms, invariants, special cases and brute force (see the list there).
 from .signs import signs_from_bits, bits_from_signs  # noqa: F401
 from .avd import avd_step, decompose  # noqa: F401
 from .restore import reconstruct, forward, forward_rows, block_bytes  # noqa: F401
+from .scaling import forward_scaled, decompose_scaled  # noqa: F401

@@ -111,3 +111,28 @@ def sample_rows(seed: int, m: int, count: int, *tags: int) -> np.ndarray:
     picked = set(g.choice(m, size=count, replace=False).tolist())
     picked.update({0, m - 1})
     return np.array(sorted(picked), dtype=np.int64)
+
+
+def channel_magnitudes(seed: int, d: int, *tags: int, outlier_frac: float = 0.01) -> np.ndarray:
+    """Positive per-input-channel activation magnitudes ``float32[d]``: log-normal
+    exp(N(0, 0.5^2)), with a fraction ``outlier_frac`` of channels (at least one) made
+    8 to 32 times larger, the outlier channels of LLM activations."""
+    g = rng(seed, 8, *tags)
+    mag = np.exp(0.5 * g.standard_normal(d))
+    n_out = max(1, int(round(outlier_frac * d)))
+    idx = g.choice(d, size=n_out, replace=False)
+    mag[idx] *= g.uniform(8.0, 32.0, size=n_out)
+    return mag.astype(np.float32)
+
+
+def outlier_activations(seed: int, M: int, d: int, magnitudes: np.ndarray, *tags: int) -> np.ndarray:
+    """fp16 activations ``x[M, d]``: N(0, 1) times the channel's magnitude."""
+    g = rng(seed, 9, *tags)
+    return (g.standard_normal((M, d)) * np.asarray(magnitudes, dtype=np.float64)[None, :]).astype(np.float16)
+
+
+def inv_input_scale(seed: int, d: int, *tags: int) -> np.ndarray:
+    """A positive per-input-channel factor ``float32[d]`` to fold into V: the reciprocal
+    of ``channel_magnitudes(...) ** 0.5`` (a square-root damping of the channel
+    magnitudes), so ordinary channels get factors near 1 and outlier channels ~1/3..1/6."""
+    return (1.0 / np.sqrt(channel_magnitudes(seed, d, *tags).astype(np.float64))).astype(np.float32)

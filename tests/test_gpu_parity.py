@@ -290,6 +290,91 @@ def test_prefill_grouped_launch_and_zero_blocks(path):
             assert rel_err(y, oracle.forward(x, blocks, n)) <= REL_TOL
 
 
+# ---------------------------------------------------------------- input-channel scale
+@pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
+@pytest.mark.parametrize("M", [1, 4, 40])
+@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
+def test_input_scale_folded_at_load(m, d, n, M, path):
+    blocks = synth.synthetic_blocks(23, m, d, n, 16, m, d)
+    t = synth.inv_input_scale(23, d)
+    x = synth.outlier_activations(23, M, d, synth.channel_magnitudes(23, d))
+    with Stack([(m, d, blocks)], path=path) as st:
+        bsl.bsl_set_input_scale(st.h, 0, t)
+        st.load([n])
+        y = st.forward(0, x)
+    assert rel_err(y, oracle.forward_scaled(x, blocks, t, n)) <= REL_TOL
+
+
+@pytest.mark.parametrize("M", [1, 4, 40])
+def test_scaled_decomposition_forward(M):
+    """A stack decomposed from W diag(s), with 1/s folded in at load, against the
+    oracle's scaled layer and (looser) against x W^T itself."""
+    m = d = 1024
+    W = synth.gaussian_weight(25, m, d)
+    mag = synth.channel_magnitudes(25, d, outlier_frac=0.03)
+    s = np.sqrt(mag.astype(np.float64))
+    blocks, _ = oracle.decompose_scaled(W, s, 16, 4)
+    t = (1.0 / s).astype(np.float32)
+    x = synth.outlier_activations(25, M, d, mag)
+    with Stack([(m, d, blocks)]) as st:
+        bsl.bsl_set_input_scale(st.h, 0, t)
+        st.load([4])
+        y = st.forward(0, x)
+    assert rel_err(y, oracle.forward_scaled(x, blocks, t, 4)) <= REL_TOL
+
+
+def test_input_scale_errors_and_reset():
+    m, d = 64, 1024
+    blocks = synth.synthetic_blocks(24, m, d, 2)
+    t = synth.inv_input_scale(24, d)
+    x = synth.activations(24, 3, d)
+    with Stack([(m, d, blocks)]) as st:
+        for bad in (0.0, -1.0, np.inf, np.nan):
+            tt = t.copy()
+            tt[7] = bad
+            with pytest.raises(bsl.BslError) as e:
+                bsl.bsl_set_input_scale(st.h, 0, tt)
+            assert e.value.code == bsl.BSL_EINVAL
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_set_input_scale(st.h, 1, t)  # no such weight
+        assert e.value.code == bsl.BSL_EINVAL
+        # a factor that overflows fp16 in V: nothing is loaded
+        bsl.bsl_set_input_scale(st.h, 0, np.full(d, 1e6, np.float32))
+        with pytest.raises(bsl.BslError) as e:
+            st.load([2])
+        assert e.value.code == bsl.BSL_EINVAL
+        assert bsl.bsl_active_blocks(st.h, 0) == 0 and bsl.bsl_resident_bytes(st.h) == 0
+        bsl.bsl_set_input_scale(st.h, 0, t)
+        st.load([1])
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_set_input_scale(st.h, 0, None)  # blocks are loaded
+        assert e.value.code == bsl.BSL_EINVAL
+        assert rel_err(st.forward(0, x), oracle.forward_scaled(x, blocks, t, 1)) <= REL_TOL
+        st.load([0])
+        bsl.bsl_set_input_scale(st.h, 0, None)
+        st.load([2])
+        assert rel_err(st.forward(0, x), oracle.forward(x, blocks, 2)) <= REL_TOL
+
+
+def test_input_scale_overflow_after_a_queued_copy():
+    """The second new block overflows once scaled while the first one's copy is in
+    flight: the load is undone as a whole."""
+    m, d = 64, 1024
+    blocks = synth.synthetic_blocks(26, m, d, 2)
+    blocks[0]["v"] = np.full((d, 16), 0.01, np.float16)
+    blocks[1]["v"] = np.full((d, 16), 1.0, np.float16)
+    with Stack([(m, d, blocks)]) as st:
+        bsl.bsl_set_input_scale(st.h, 0, np.full(d, 1e5, np.float32))
+        with pytest.raises(bsl.BslError) as e:
+            st.load([2])
+        assert e.value.code == bsl.BSL_EINVAL
+        assert bsl.bsl_active_blocks(st.h, 0) == 0 and bsl.bsl_resident_bytes(st.h) == 0
+        st.load([1])
+        x = synth.activations(26, 2, d)
+        ref = oracle.forward_scaled(x, blocks, np.full(d, 1e5), 1)
+        assert rel_err(st.forward(0, x), ref) <= REL_TOL
+
+
 # ---------------------------------------------------------------- error handling
 def test_errors_leave_state_unchanged(cfg1_blocks):
     x = torch.zeros((1, 1024 + 8), dtype=torch.float16, device="cuda")

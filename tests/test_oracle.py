@@ -188,10 +188,11 @@ def test_zero_blocks_give_zero_output():
 
 
 # ---------------------------------------------------------------- brute force
-def _brute_force(x, blocks, n):
+def _brute_force(x, blocks, n, inv_scale=None):
     M, d = x.shape
     m, k = blocks[0]["u"].shape
-    xf = [[Fraction(float(v)) for v in row] for row in x]
+    sf = [Fraction(1)] * d if inv_scale is None else [Fraction(float(v)) for v in inv_scale]
+    xf = [[Fraction(float(v)) * sf[c] for c, v in enumerate(row)] for row in x]
     out = []
     for t in range(M):
         row = []
@@ -224,6 +225,74 @@ def test_forward_rows_agrees_with_full_forward():
     x = synth.activations(5, 3, 32)
     rows = synth.sample_rows(5, 64, 9)
     assert np.array_equal(oracle.forward_rows(x, blocks, rows), oracle.forward(x, blocks)[:, rows])
+
+
+# ---------------------------------------------------------------- input-channel scale
+@pytest.mark.parametrize("m,d,k,n,M", [(3, 8, 1, 1, 1), (5, 16, 2, 3, 2), (8, 8, 2, 2, 2)])
+def test_forward_scaled_matches_exact_rational_brute_force(m, d, k, n, M):
+    blocks = synth.synthetic_blocks(19, m, d, n, k)
+    x = synth.activations(4, M, d)
+    s = synth.inv_input_scale(6, d)
+    exact = _brute_force(x, blocks, n, inv_scale=s)
+    y = oracle.forward_scaled(x, blocks, s, n)
+    for t in range(M):
+        for j in range(m):
+            e = float(exact[t][j])
+            assert abs(y[t, j] - e) <= 1e-15 * max(1.0, abs(e)) * d * n
+
+
+def test_forward_scaled_with_unit_scale_is_the_layer():
+    blocks = synth.synthetic_blocks(3, 48, 64, 3)
+    x = synth.activations(3, 5, 64)
+    assert np.array_equal(oracle.forward_scaled(x, blocks, np.ones(64, np.float32)), oracle.forward(x, blocks))
+    assert np.array_equal(oracle.forward_scaled(x, blocks, np.ones(64), 0), np.zeros((5, 48)))
+
+
+def test_input_scale_folds_into_v_exactly():
+    """Column scaling commutes with the elementwise sign product:
+    (S (.) U V^T) diag(t) = S (.) U (diag(t) V)^T.  With power-of-two factors (and no
+    underflow) the folded V is exact in fp16, so both sides agree to fp64 rounding."""
+    m, d, n = 40, 96, 3
+    blocks = synth.synthetic_blocks(8, m, d, n)
+    # factors 1..8 (dividing could push small V entries into fp16 subnormals)
+    t = np.ldexp(1.0, synth.rng(8, 99).integers(0, 4, size=d)).astype(np.float32)
+    folded = [{"bits": b["bits"], "u": b["u"], "v": (b["v"].astype(np.float64) * t[:, None]).astype(np.float16)} for b in blocks]
+    for b, f in zip(blocks, folded):
+        assert np.array_equal(f["v"].astype(np.float64), b["v"].astype(np.float64) * t[:, None])
+    x = synth.activations(8, 4, d)
+    ref = oracle.forward_scaled(x, blocks, t)
+    assert np.abs(oracle.forward(x, folded) - ref).max() <= 1e-13 * np.abs(ref).max()
+    # the same factors on the output channels instead give another layer
+    assert np.abs(oracle.forward(x, blocks) * 1.0 - ref).max() > 1e-3 * np.abs(ref).max()
+
+
+def test_scaled_decomposition_restores_w():
+    """decompose_scaled stores W diag(s): undoing s on the columns of its restoration
+    gives back W within the residual left after n blocks."""
+    W = synth.gaussian_weight(12, 64, 96)
+    s = 1.0 / synth.inv_input_scale(12, 96).astype(np.float64)
+    blocks, norms = oracle.decompose_scaled(W, s, 16, 6, round_fp16=False)
+    R = W.astype(np.float64) * s[None, :] - orest.reconstruct(blocks)
+    assert abs(np.linalg.norm(R) - norms[-1]) <= 1e-9 * norms[0]
+    assert norms[-1] < 0.5 * norms[0]
+
+
+def test_scaling_lowers_output_error_under_outlier_channels():
+    """The direction of the "w/o scaling" ablation (Figure 5 caption) on synthetic
+    activations with outlier channels: at the same block count, decomposing W diag(s)
+    with s = channel magnitude^0.5 and undoing s on x leaves a smaller output error
+    than decomposing W itself."""
+    m = d = 256
+    W = synth.gaussian_weight(14, m, d)
+    mag = synth.channel_magnitudes(14, d, outlier_frac=0.03)
+    x = synth.outlier_activations(14, 64, d, mag)
+    y = x.astype(np.float64) @ W.astype(np.float64).T
+    s = np.sqrt(mag.astype(np.float64))
+    plain, _ = oracle.decompose(W, 16, 4)
+    scaled, _ = oracle.decompose_scaled(W, s, 16, 4)
+    err_plain = np.linalg.norm(oracle.forward(x, plain) - y)
+    err_scaled = np.linalg.norm(oracle.forward_scaled(x, scaled, 1.0 / s) - y)
+    assert err_scaled < 0.9 * err_plain
 
 
 # ---------------------------------------------------------------- planted mistakes
@@ -263,3 +332,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
     exact = np.array([[float(v) for v in row] for row in _brute_force(xx, blocks, 2)])
     assert np.abs(wrong - exact).max() > 1e-3 * np.abs(exact).max()
     assert np.abs(oracle.forward(xx, blocks, 2) - exact).max() <= 1e-13 * np.abs(exact).max()
+    # 5) the input-channel factor applied to the output channels fails brute force
+    t = synth.inv_input_scale(6, 8)
+    wrong = orest.forward(xx, blocks, 2) * t[None, :].astype(np.float64)
+    exact = np.array([[float(v) for v in row] for row in _brute_force(xx, blocks, 2, inv_scale=t)])
+    assert np.abs(wrong - exact).max() > 1e-3 * np.abs(exact).max()
+    assert np.abs(oracle.forward_scaled(xx, blocks, t, 2) - exact).max() <= 1e-13 * np.abs(exact).max()

@@ -29,6 +29,7 @@ Modules:
   avd      -- one absolute-value-decomposition step and the iterated decomposition
   restore  -- dense fp64 reconstruct-then-matmul forward, block byte count
   scaling  -- the layer with an input-channel scale (activation-aware scaling)
+  lowrank  -- vanilla-SVD blocks of the equal-size rank k' and their forward
 
 Parity status: every function is pinned by ``tests/test_oracle.py`` against
 closed forms, invariants, special cases and brute force (see the list there).
@@ -37,3 +38,4 @@ from .signs import signs_from_bits, bits_from_signs  # noqa: F401
 from .avd import avd_step, decompose  # noqa: F401
 from .restore import reconstruct, forward, forward_rows, block_bytes  # noqa: F401
 from .scaling import forward_scaled, decompose_scaled  # noqa: F401
+from .lowrank import equal_bytes_rank, lowrank_block_bytes, svd_step, decompose_svd, forward_lowrank  # noqa: F401

@@ -295,6 +295,90 @@ def test_scaling_lowers_output_error_under_outlier_channels():
     assert err_scaled < 0.9 * err_plain
 
 
+# ---------------------------------------------------------------- vanilla-SVD blocks ("w/o AVD")
+def _brute_force_lowrank(x, blocks, n):
+    M, d = x.shape
+    m, kp = blocks[0]["u"].shape
+    xf = [[Fraction(float(v)) for v in row] for row in x]
+    out = []
+    for t in range(M):
+        row = []
+        for j in range(m):
+            acc = Fraction(0)
+            for i in range(n):
+                for c in range(d):
+                    for r in range(kp):
+                        acc += Fraction(float(blocks[i]["u"][j, r])) * Fraction(float(blocks[i]["v"][c, r])) * xf[t][c]
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+def _lowrank_blocks(seed, m, d, kp, n):
+    return [{"u": synth.factor(seed, m, kp, i, 0), "v": (synth.factor(seed, d, kp, i, 1) * np.float16(-1) ** i)} for i in range(n)]
+
+
+@pytest.mark.parametrize("m,d,kp,n,M", [(3, 8, 2, 1, 1), (5, 8, 3, 2, 2), (6, 6, 2, 2, 1)])
+def test_forward_lowrank_matches_exact_rational_brute_force(m, d, kp, n, M):
+    blocks = _lowrank_blocks(9, m, d, kp, n)
+    x = synth.activations(9, M, d)
+    exact = _brute_force_lowrank(x, blocks, n)
+    y = oracle.forward_lowrank(x, blocks, n)
+    for t in range(M):
+        for j in range(m):
+            e = float(exact[t][j])
+            assert abs(y[t, j] - e) <= 1e-15 * max(1.0, abs(e)) * d * n * kp
+
+
+@pytest.mark.parametrize("m,d", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (8192, 28672), (37, 520)])
+def test_equal_bytes_rank_is_the_largest_that_fits(m, d):
+    kp = oracle.equal_bytes_rank(m, d, 16)
+    assert oracle.lowrank_block_bytes(m, d, kp) <= oracle.block_bytes(m, d, 16) < oracle.lowrank_block_bytes(m, d, kp + 1)
+
+
+def test_equal_bytes_rank_values():
+    # k' for the 8B-shaped layer's q/o, k/v and gate/up/down shapes
+    assert [oracle.equal_bytes_rank(m, d) for m, d in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]] == [144, 67, 215, 215]
+
+
+def test_svd_iteration_follows_eckart_young():
+    """With exact factors the i-th residual is W minus its best rank i k' approximation:
+    ||R_i||^2 = sum of the squared singular values of W past index i k'."""
+    W = synth.gaussian_weight(15, 48, 40).astype(np.float64)
+    sig = np.linalg.svd(W, compute_uv=False)
+    kp, n = 5, 8  # n kp = 40 = rank of W: the last residual is zero
+    blocks, norms = oracle.decompose_svd(W, kp, n, round_fp16=False)
+    for i in range(n + 1):
+        assert abs(norms[i] ** 2 - np.sum(sig[i * kp:] ** 2)) <= 1e-10 * np.sum(sig ** 2)
+    x = synth.activations(15, 3, 40)
+    full = x.astype(np.float64) @ W.T
+    assert np.abs(oracle.forward_lowrank(x, blocks) - full).max() <= 1e-10 * np.abs(full).max()
+
+
+def test_svd_block_of_a_low_rank_weight_is_exact():
+    g = synth.rng(16, 1)
+    W = g.standard_normal((30, 3)) @ g.standard_normal((3, 24))
+    blocks, norms = oracle.decompose_svd(W, 4, 1, round_fp16=False)
+    assert norms[1] <= 1e-12 * norms[0]
+    assert blocks[0]["u"].shape == (30, 4) and blocks[0]["v"].shape == (24, 4)
+
+
+def test_avd_beats_svd_at_equal_bytes_on_a_gaussian_weight():
+    """The direction of the "w/o AVD" ablation (Figure 5 caption) on a synthetic
+    Gaussian weight: at the same block count and block size, AVD blocks leave a smaller
+    output error than vanilla-SVD blocks of rank k'."""
+    m = d = 256
+    W = synth.gaussian_weight(17, m, d)
+    x = synth.activations(17, 16, d)
+    y = x.astype(np.float64) @ W.astype(np.float64).T
+    n = 4
+    avd, _ = oracle.decompose(W, 16, n)
+    svd, _ = oracle.decompose_svd(W, oracle.equal_bytes_rank(m, d), n)
+    e_avd = np.linalg.norm(oracle.forward(x, avd) - y)
+    e_svd = np.linalg.norm(oracle.forward_lowrank(x, svd) - y)
+    assert e_avd < 0.5 * e_svd
+
+
 # ---------------------------------------------------------------- planted mistakes
 def _mutant_svd_of_R(R, k, round_fp16=True):
     R = np.asarray(R, dtype=np.float64)
@@ -338,3 +422,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
     exact = np.array([[float(v) for v in row] for row in _brute_force(xx, blocks, 2, inv_scale=t)])
     assert np.abs(wrong - exact).max() > 1e-3 * np.abs(exact).max()
     assert np.abs(oracle.forward_scaled(xx, blocks, t, 2) - exact).max() <= 1e-13 * np.abs(exact).max()
+    # 6) a low-rank forward with the factors swapped (x U V^T) fails brute force
+    lb = _lowrank_blocks(9, 6, 6, 2, 2)
+    xs = synth.activations(9, 1, 6)
+    exact = np.array([[float(v) for v in row] for row in _brute_force_lowrank(xs, lb, 2)])
+    swapped = sum((xs.astype(np.float64) @ b["u"].astype(np.float64)) @ b["v"].astype(np.float64).T for b in lb)
+    assert np.abs(swapped - exact).max() > 1e-3 * np.abs(exact).max()

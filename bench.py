@@ -9,7 +9,9 @@ of the layer are resident (about 0.96 GB) and the steps rotate over them, so the
 256 MB last-level cache cannot serve the reads.  Bytes are the algorithmic bytes of
 the loaded blocks, n * (m d / 8 + 2 k (m + d)) per weight, counted once.
 
-Also reported: prefill at M = 2048 tokens through one such layer, on the tile path
+Also reported: the same decode with every linear held as n = 8 equal-size vanilla-SVD
+blocks (rank k' = 16 + m d / (16 (m + d)), fp16 factors, no signs: the "w/o AVD"
+baseline, the same bytes per block); prefill at M = 2048 tokens through one such layer, on the tile path
 (W_hat rebuilt per tile, then a GEMM; executed MFMA work (2 k n G + 2 M) m d per weight
 with G = ceil(M / 512) token groups) and on the factored path (the S Z contraction,
 2 n k M m d per weight); the decode kernel's roofline from per-launch HIP events; and
@@ -327,6 +329,61 @@ def block_streaming(bsl, torch, seed: int) -> dict:
     }
 
 
+def equal_size_svd_decode(bsl, torch, seed: int, layers: int, steps: int, warmup: int) -> dict:
+    """The "w/o AVD" baseline at equal bytes: every linear of the 8B-shaped layer held as
+    n = 8 vanilla-SVD blocks of rank k' = 16 + m d / (16 (m + d)) (fp16 U', V', no signs),
+    single-token decode through one grouped launch pair per step, `layers` resident
+    copies rotated like the headline decode.  Bytes are 8 * 2 k' (m + d) per weight."""
+    shapes = synth.LLAMA3_8B_LAYER
+    kps = [bsl.bsl_lr_equal_rank(m, d, K_RANK) for _, m, d in shapes]
+    h = bsl.bsl_lr_init(0, [m for _ in range(layers) for _, m, _ in shapes], [d for _ in range(layers) for _, _, d in shapes],
+                        kps * layers, 8)
+    for j, (_, m, d) in enumerate(shapes):
+        g = synth.rng(seed, 50, j)
+        blocks = [{"u": (g.standard_normal((m, kps[j]), dtype=np.float32) * 0.05).astype(np.float16),
+                   "v": (g.standard_normal((d, kps[j]), dtype=np.float32) * 0.05).astype(np.float16)} for _ in range(8)]
+        for l in range(layers):  # the same host factors, one device copy per layer
+            bsl.bsl_lr_set_source(h, l * 7 + j, blocks)
+    bsl.bsl_lr_load_blocks(h, [8] * (7 * layers), 0)
+    for key in [k for k in bsl._sources if k[0] == "lr" and k[1] == h]:
+        del bsl._sources[key]
+    xs = [[torch.from_numpy(synth.activations(seed + 1, 1, d, l, j)).cuda() for j, (_, _, d) in enumerate(shapes)]
+          for l in range(layers)]
+    ys = [[torch.empty((1, m), dtype=torch.float16, device="cuda") for _, m, _ in shapes] for _ in range(layers)]
+    layer_bytes = sum(8 * bsl.bsl_lr_block_bytes(m, d, kps[j]) for j, (_, m, d) in enumerate(shapes))
+    st = torch.cuda.current_stream()
+    sp = int(st.cuda_stream)
+
+    def launch(l):
+        bsl.bsl_lr_forward_group(h, list(range(l * 7, l * 7 + 7)), [t.data_ptr() for t in xs[l]],
+                                 [t.data_ptr() for t in ys[l]], 1, False, sp)
+
+    for i in range(warmup):
+        launch(i % layers)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(st)
+    for i in range(steps):
+        launch(i % layers)
+    e1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    bsl.bsl_lr_destroy(h)
+    return {
+        "workload": "Llama-3-8B-shaped layer linears, n=8 vanilla-SVD blocks of the equal-size rank k' "
+                    f"({', '.join(f'{nm} {kp}' for (nm, _, _), kp in zip(shapes, kps))}), M=1 decode, "
+                    f"one grouped launch pair per step, {layers} resident layer copies rotated",
+        "bytes_per_step": layer_bytes,
+        "us_per_step": round(us, 2),
+        "wall_us_per_step": round(wall * 1e6 / steps, 2),
+        "GB_per_s": round(layer_bytes / (us * 1e-6) / 1e9, 1),
+        "hbm_frac_of_peak": round(layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels": "lowrank_xv_kernel + lowrank_tu_kernel",
+    }
+
+
 def copy_calibration(torch, mib: int = 1024, reps: int = 3) -> None:
     """A plain elementwise copy (y = -x, fp16) of known size, for scaling the
     FETCH_SIZE / WRITE_SIZE counters: each dispatch reads and writes exactly `mib` MiB."""
@@ -349,6 +406,7 @@ def main() -> None:
     ap.add_argument("--tile-steps", type=int, default=20, help="timed steps of the tile-path M=2048 prefill")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-svd", action="store_true", help="skip the equal-size vanilla-SVD decode baseline")
     ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
     ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
     ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
@@ -489,6 +547,17 @@ def main() -> None:
         log(f"prefill (factored): {wall_p * 1e3 / args.prefill_steps:.1f} ms/step, {tfl:.1f} TFLOP/s")
         pre.close()
         del pre
+        torch.cuda.empty_cache()
+
+    # ---------------- equal-size vanilla-SVD baseline ("w/o AVD"), decode
+    if not args.no_svd:
+        log("equal-size SVD baseline: 8B-shaped layer, n=8 blocks of rank k', M=1")
+        result["equal_size_svd_decode"] = equal_size_svd_decode(bsl, torch, args.seed + 41, args.layers, args.steps,
+                                                                args.warmup)
+        r = result["equal_size_svd_decode"]
+        r["bitstack_decode_us_per_step"] = result["roofline"]["avg_launch_us"]
+        r["bitstack_speedup"] = round(r["us_per_step"] / result["roofline"]["avg_launch_us"], 2)
+        log(f"equal-size SVD baseline: {r['us_per_step']} us/step, {r['GB_per_s']} GB/s")
         torch.cuda.empty_cache()
 
     # ---------------- optional sweeps

@@ -42,6 +42,16 @@ EXPORTED = (
     "bsl_debug_unpack",
     "bsl_last_error",
     "bsl_destroy",
+    # equal-size vanilla-SVD baseline (bitstack_lowrank.h)
+    "bsl_lr_equal_rank",
+    "bsl_lr_block_bytes",
+    "bsl_lr_init",
+    "bsl_lr_set_source",
+    "bsl_lr_load_blocks",
+    "bsl_lr_resident_bytes",
+    "bsl_lr_forward",
+    "bsl_lr_forward_group",
+    "bsl_lr_destroy",
 )
 
 
@@ -53,6 +63,10 @@ class BslError(RuntimeError):
 
 class _BlockSrc(ctypes.Structure):
     _fields_ = [("sign_bits", ctypes.c_void_p), ("u", ctypes.c_void_p), ("v", ctypes.c_void_p)]
+
+
+class _LrBlockSrc(ctypes.Structure):
+    _fields_ = [("u", ctypes.c_void_p), ("v", ctypes.c_void_p)]
 
 
 _lib = None
@@ -87,8 +101,23 @@ def lib() -> ctypes.CDLL:
         L.bsl_last_error.argtypes = []
         L.bsl_destroy.restype = None
         L.bsl_destroy.argtypes = [c_vp]
+        L.bsl_lr_equal_rank.restype = c_i32
+        L.bsl_lr_equal_rank.argtypes = [c_i64, c_i64, c_i32]
+        L.bsl_lr_block_bytes.restype = c_sz
+        L.bsl_lr_block_bytes.argtypes = [c_i64, c_i64, c_i32]
+        L.bsl_lr_init.argtypes = [ctypes.POINTER(c_vp), ctypes.c_int, c_i32, c_vp, c_vp, c_vp, c_i32]
+        L.bsl_lr_set_source.argtypes = [c_vp, c_i32, c_i32, c_vp]
+        L.bsl_lr_load_blocks.argtypes = [c_vp, c_vp, c_vp]
+        L.bsl_lr_resident_bytes.restype = c_u64
+        L.bsl_lr_resident_bytes.argtypes = [c_vp]
+        L.bsl_lr_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
+        L.bsl_lr_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
+        L.bsl_lr_destroy.restype = None
+        L.bsl_lr_destroy.argtypes = [c_vp]
         for f in ("bsl_pack_signs", "bsl_unpack_signs", "bsl_init", "bsl_set_source", "bsl_load_blocks",
-                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack"):
+                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack",
+                  "bsl_set_input_scale", "bsl_lr_init", "bsl_lr_set_source", "bsl_lr_load_blocks", "bsl_lr_forward",
+                  "bsl_lr_forward_group"):
             getattr(L, f).restype = c_i32
         _lib = L
     return _lib
@@ -211,4 +240,66 @@ def bsl_destroy(stack: int) -> None:
     if stack:
         lib().bsl_destroy(stack)
         for key in [k for k in _sources if k[0] == stack]:
+            del _sources[key]
+
+
+# ---------------------------------------------------------------- vanilla-SVD baseline (bitstack_lowrank.h)
+def bsl_lr_equal_rank(m: int, d: int, k: int = 16) -> int:
+    return int(lib().bsl_lr_equal_rank(m, d, k))
+
+
+def bsl_lr_block_bytes(m: int, d: int, k_prime: int) -> int:
+    return int(lib().bsl_lr_block_bytes(m, d, k_prime))
+
+
+def bsl_lr_init(device: int, m, d, k_prime, n_cap: int = 16) -> int:
+    m = np.ascontiguousarray(m, dtype=np.int32)
+    d = np.ascontiguousarray(d, dtype=np.int32)
+    kp = np.ascontiguousarray(k_prime, dtype=np.int32)
+    if m.shape != d.shape or m.shape != kp.shape or m.ndim != 1:
+        raise ValueError("m, d and k_prime must be 1-D of equal length")
+    h = ctypes.c_void_p()
+    _check(lib().bsl_lr_init(ctypes.byref(h), device, m.size, _ptr(m), _ptr(d), _ptr(kp), n_cap))
+    return int(h.value)
+
+
+def bsl_lr_set_source(stack: int, w: int, blocks) -> None:
+    """blocks: sequence of dicts with ``u`` (fp16 [m, k']) and ``v`` (fp16 [d, k'])."""
+    keep = []
+    arr = (_LrBlockSrc * max(1, len(blocks)))()
+    for i, b in enumerate(blocks):
+        u = np.ascontiguousarray(b["u"], dtype=np.float16)
+        v = np.ascontiguousarray(b["v"], dtype=np.float16)
+        keep.append((u, v))
+        arr[i].u, arr[i].v = _ptr(u), _ptr(v)
+    _check(lib().bsl_lr_set_source(stack, w, len(blocks), ctypes.addressof(arr)))
+    _sources[("lr", stack, w)] = keep
+
+
+def bsl_lr_load_blocks(stack: int, n_per_weight, stream: int = 0) -> None:
+    n = np.ascontiguousarray(n_per_weight, dtype=np.int32)
+    _check(lib().bsl_lr_load_blocks(stack, _ptr(n), stream))
+
+
+def bsl_lr_resident_bytes(stack: int) -> int:
+    return int(lib().bsl_lr_resident_bytes(stack))
+
+
+def bsl_lr_forward(stack: int, w: int, x_ptr: int, y_ptr: int, M: int, y_is_fp32: bool, stream: int = 0) -> None:
+    _check(lib().bsl_lr_forward(stack, w, x_ptr, y_ptr, M, 1 if y_is_fp32 else 0, stream))
+
+
+def bsl_lr_forward_group(stack: int, weights, x_ptrs, y_ptrs, M: int, y_is_fp32: bool, stream: int = 0) -> None:
+    n = len(weights)
+    ws = (ctypes.c_int32 * n)(*weights)
+    xs = (ctypes.c_void_p * n)(*x_ptrs)
+    ys = (ctypes.c_void_p * n)(*y_ptrs)
+    _check(lib().bsl_lr_forward_group(stack, n, ctypes.addressof(ws), ctypes.addressof(xs), ctypes.addressof(ys), M,
+                                      1 if y_is_fp32 else 0, stream))
+
+
+def bsl_lr_destroy(stack: int) -> None:
+    if stack:
+        lib().bsl_lr_destroy(stack)
+        for key in [k for k in _sources if k[0] == "lr" and k[1] == stack]:
             del _sources[key]

@@ -220,6 +220,8 @@ int prefill_groups(const Weight& W) { return (W.mt * kTileRows + kPrefillGroupRo
 
 }  // namespace
 
+int bsl::set_error(int code, const std::string& msg) { return fail(code, msg); }
+
 extern "C" {
 
 const char* bsl_last_error(void) { return g_err.c_str(); }

@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <string>
 
 namespace bsl {
 
@@ -107,5 +108,46 @@ constexpr int kTileAutoMinTokens = 8;   // BSL_PATH_AUTO takes the tile path fro
 constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB
 constexpr int kTileItemsPerCu = 2;     // aim of the column-range cutting
 constexpr int kTileCounters = 1 << 16;
+
+// Records the calling thread's error message (bsl_last_error) and returns code.
+int set_error(int code, const std::string& msg);
+
+// ---------------------------------------------------------------- vanilla-SVD baseline
+// Factors of one weight, for n_cap blocks of rank k' padded to kp8 = roundup(k', 8)
+// (padding ranks are zero):
+//   vt: [n_cap kp8][d_pad512] fp16: row i kp8 + r holds V'_i[:, r] (zero past d)
+//   ut: [m_pad64 / 64][n_cap kp8 / 8][64][8] fp16: lane L of row group g, column group q
+//       holds U'[64 g + L][8 q .. 8 q + 7] over the blocks' concatenated ranks
+// Phase 1 (one wave per row of vt): t[token][row] = x[token] . vt[row]  (fp32)
+// Phase 2 (one workgroup per 64 rows): y[token][row] = sum over loaded columns of
+//         ut[row][col] t[token][col]
+constexpr int kLrTokens = 8;       // tokens per launch pair
+constexpr int kLrColAlign = 512;
+constexpr int kLrRowGroup = 64;
+constexpr int kLrPhase2Waves = 8;
+
+struct LrWeight {
+  const uint16_t* vt;
+  const uint16_t* ut;
+  const uint16_t* x;  // [T][d] fp16
+  void* y;            // [T][m]
+  float* t;           // [kLrTokens][ld] workspace
+  int32_t m, d, d_pad;
+  int32_t ld;         // n_cap kp8: row stride of t, column groups x 8 of ut
+  int32_t kcat;       // n kp8: loaded rows of vt / columns of ut
+  int32_t row_begin;  // phase 1: first vt row of this weight in the launch
+  int32_t rg_begin;   // phase 2: first row group of this weight in the launch
+};
+
+struct LrArgs {
+  LrWeight w[kMaxGroup];
+  int32_t count;
+  int32_t T;          // tokens of this launch pair (1..kLrTokens)
+  int32_t y_fp32;
+  int32_t total_rows; // phase 1 rows (waves)
+  int32_t total_rgs;  // phase 2 row groups (workgroups)
+};
+
+int launch_lowrank(const LrArgs& args, void* stream);
 
 }  // namespace bsl

@@ -129,3 +129,18 @@ def test_init_validates_before_touching_a_device():
     with pytest.raises(bsl.BslError) as e:
         bsl.bsl_init(0, [64], [512], n_cap=0)
     assert e.value.code == bsl.BSL_EINVAL
+
+
+def test_lowrank_init_validates_before_touching_a_device():
+    for m, d, kp, n_cap, code in [([64], [100], [8], 4, bsl.BSL_EUNSUPPORTED), ([64], [512], [0], 4, bsl.BSL_EUNSUPPORTED),
+                                  ([64], [512], [2000], 4, bsl.BSL_EUNSUPPORTED), ([64], [512], [8], 0, bsl.BSL_EINVAL)]:
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_lr_init(0, m, d, kp, n_cap)
+        assert e.value.code == code
+
+
+@pytest.mark.parametrize("m,d", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (8192, 28672), (37, 520)])
+def test_lowrank_sizes_match_the_oracle(m, d):
+    kp = bsl.bsl_lr_equal_rank(m, d, 16)
+    assert kp == oracle.equal_bytes_rank(m, d, 16)
+    assert bsl.bsl_lr_block_bytes(m, d, kp) == oracle.lowrank_block_bytes(m, d, kp)

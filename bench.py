@@ -53,7 +53,7 @@ def block_bytes(m: int, d: int) -> int:
 class Layers:
     """One bitstack stack holding `layers` copies of a decoder layer's linears."""
 
-    def __init__(self, bsl, torch, shapes, counts, layers, seed, M, path=None):
+    def __init__(self, bsl, torch, shapes, counts, layers, seed, M, path=None, decode=None):
         self.bsl, self.torch = bsl, torch
         self.shapes = shapes
         self.layers = layers
@@ -63,6 +63,8 @@ class Layers:
         self.h = bsl.bsl_init(0, ms, ds, 16, 16, 0)
         if path is not None:
             bsl.bsl_set_path(self.h, path)
+        if decode is not None:
+            bsl.bsl_set_decode(self.h, decode)
         self.counts = []
         for l in range(layers):
             for j, (_, m, d) in enumerate(shapes):
@@ -407,6 +409,8 @@ def main() -> None:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-svd", action="store_true", help="skip the equal-size vanilla-SVD decode baseline")
+    ap.add_argument("--decode", choices=["auto", "shared", "private"], default="auto",
+                    help="single-token kernel of the headline (auto: the shared-operand kernel)")
     ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
     ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
     ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
@@ -439,7 +443,16 @@ def main() -> None:
 
     # ---------------- decode (headline)
     log(f"decode: building {args.layers} resident 8B-shaped layers (n=8, k=16)")
-    dec = Layers(bsl, torch, shapes, [[8] * 7] * args.layers, args.layers, args.seed, M=1)
+    kinds = {"auto": bsl.BSL_DECODE_AUTO, "shared": bsl.BSL_DECODE_SHARED, "private": bsl.BSL_DECODE_PRIVATE}
+    dec = Layers(bsl, torch, shapes, [[8] * 7] * args.layers, args.layers, args.seed, M=1, decode=kinds[args.decode])
+    # the other single-token kernel on the same stack, for comparison
+    private = args.decode == "private"
+    bsl.bsl_set_decode(dec.h, bsl.BSL_DECODE_SHARED if private else bsl.BSL_DECODE_PRIVATE)
+    w_o, k_o, b_o, _ = time_steps(torch, dec, args.steps, args.warmup)
+    other = {"kernel": "decode_m1_kernel" if private else "decode_wp_kernel",
+             "us_per_step": round(float(np.mean(k_o)) * 1e3, 2),
+             "GB_per_s": round(dec.bytes(0) / (float(np.mean(k_o)) * 1e-3) / 1e9, 1)}
+    bsl.bsl_set_decode(dec.h, kinds[args.decode])
     wall, kern_ms, tbytes, tflops = time_steps(torch, dec, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     value = tbytes / wall / 1e9
@@ -494,7 +507,7 @@ def main() -> None:
             },
             "roofline": {
                 "bound": "hbm",
-                "kernel": "decode_m1_kernel",
+                "kernel": "decode_wp_kernel" if args.decode == "private" else "decode_m1_kernel",
                 "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS,
                 "unit": "GB/s",
@@ -506,6 +519,7 @@ def main() -> None:
     )
     if per_weight:
         result["decode_single_weight_launches"] = per_weight
+    result["decode_other_kernel"] = other
 
     # ---------------- prefill M = 2048: tile path (the default for batches), then factored
     if not args.no_prefill:

@@ -24,6 +24,9 @@ BSL_EUNSUPPORTED = -4
 BSL_PATH_AUTO = 0
 BSL_PATH_FACTORED = 1
 BSL_PATH_TILE = 2
+BSL_DECODE_AUTO = 0
+BSL_DECODE_SHARED = 1
+BSL_DECODE_PRIVATE = 2
 
 EXPORTED = (
     "bsl_block_bytes",
@@ -32,6 +35,7 @@ EXPORTED = (
     "bsl_unpack_signs",
     "bsl_init",
     "bsl_set_path",
+    "bsl_set_decode",
     "bsl_set_source",
     "bsl_set_input_scale",
     "bsl_load_blocks",
@@ -96,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_set_path.argtypes = [c_vp, c_i32]
+        L.bsl_set_decode.argtypes = [c_vp, c_i32]
         L.bsl_debug_unpack.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
         L.bsl_last_error.restype = ctypes.c_char_p
         L.bsl_last_error.argtypes = []
@@ -115,7 +120,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_lr_destroy.restype = None
         L.bsl_lr_destroy.argtypes = [c_vp]
         for f in ("bsl_pack_signs", "bsl_unpack_signs", "bsl_init", "bsl_set_source", "bsl_load_blocks",
-                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack",
+                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack", "bsl_set_decode",
                   "bsl_set_input_scale", "bsl_lr_init", "bsl_lr_set_source", "bsl_lr_load_blocks", "bsl_lr_forward",
                   "bsl_lr_forward_group"):
             getattr(L, f).restype = c_i32
@@ -226,6 +231,10 @@ def bsl_forward_group(stack: int, weights, x_ptrs, y_ptrs, M: int, y_is_fp32: bo
 
 def bsl_set_path(stack: int, path: int) -> None:
     _check(lib().bsl_set_path(stack, path))
+
+
+def bsl_set_decode(stack: int, kind: int) -> None:
+    _check(lib().bsl_set_decode(stack, kind))
 
 
 def bsl_debug_unpack(stack: int, w: int, i: int, path: int, out_ptr: int, stream: int = 0) -> None:

@@ -126,6 +126,21 @@ void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
   std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
 }
 
+// V (d x 16, row-major fp16) -> [d_pad/512][16][64][8] in the single-token kernel's
+// B-operand order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] for
+// j < 4 and V[512 c + 32 b + 16 + 4 kk + j - 4][r] for j >= 4 (zero past d).
+void bop_v(const uint16_t* v, int64_t d, uint16_t* out) {
+  const int64_t nch = pad_cols(d) / kChunkCols;
+  for (int64_t c = 0; c < nch; ++c)
+    for (int b = 0; b < kPlanes; ++b)
+      for (int L = 0; L < 64; ++L)
+        for (int j = 0; j < 8; ++j) {
+          const int kk = L / 16, r = L % 16;
+          const int64_t col = 512 * c + 32 * b + (j < 4 ? 4 * kk + j : 16 + 4 * kk + j - 4);
+          out[((c * kPlanes + b) * 64 + L) * 8 + j] = col < d ? v[col * kRank + r] : 0;
+        }
+}
+
 // V (d x 16) with row c multiplied by inv_scale[c]: one rounding of the exact product.
 bool scale_v(const uint16_t* v, int64_t d, const float* inv_scale, uint16_t* out) {
   for (int64_t c = 0; c < d; ++c)
@@ -159,6 +174,7 @@ struct bsl_stack {
   int32_t k = 16, n_cap = 0;
   int32_t decode_grid_max = 256;  // largest power of two <= compute units
   int32_t path = BSL_PATH_AUTO;   // multi-token formulation (bsl_set_path)
+  int32_t decode = BSL_DECODE_AUTO;  // single-token kernel (bsl_set_decode)
   uint64_t budget = 0, resident = 0;
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
@@ -173,9 +189,9 @@ struct bsl_stack {
 
 namespace {
 
-// signs + tiled U + tiled V + row-major V (see BlockPtrs)
+// signs + tiled U + tiled V + row-major V + B-ordered V (see BlockPtrs)
 size_t slot_bytes(int64_t m, int64_t d) {
-  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 2 * (size_t)pad_cols(d) * kRank * 2;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 3 * (size_t)pad_cols(d) * kRank * 2;
 }
 
 BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
@@ -188,6 +204,7 @@ BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
   p.u = reinterpret_cast<const uint16_t*>(base + sb);
   p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
   p.vr = reinterpret_cast<const uint16_t*>(base + sb + ub + vb);
+  p.vb = reinterpret_cast<const uint16_t*>(base + sb + ub + 2 * vb);
   return p;
 }
 
@@ -208,7 +225,7 @@ int upload_table(Weight& W, int32_t lo, int32_t hi, hipStream_t st) {
   if (hi <= lo) return BSL_OK;
   std::vector<BlockPtrs> tab(hi - lo);
   for (int32_t i = lo; i < hi; ++i)
-    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
+    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr, nullptr};
   hipError_t e = hipMemcpyAsync(W.dtable + lo, tab.data(), sizeof(BlockPtrs) * (hi - lo), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
@@ -316,7 +333,9 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
   if (rc == BSL_OK) {
     // single-token pieces: at most (row groups of one launch) + (workgroups) of them
     const size_t n = ((size_t)kMaxGroup * max_groups + (size_t)s->decode_grid_max) * kDecodeGroupRows;
-    const size_t na = (size_t)kMaxGroup * max_groups;
+    // (counters per 256-row group: the wave-private kernel's row groups are a quarter of
+    // decode_m1_kernel's)
+    const size_t na = (size_t)kMaxGroup * max_groups * (kDecodeGroupRows / kWpRows);
     if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
     else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
     else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
@@ -456,7 +475,8 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     }
     tile_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
     rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
-    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + ub + 2 * vb, hipMemcpyHostToDevice, st);
+    bop_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + 2 * vb));
+    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + ub + 3 * vb, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -658,16 +678,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     D.nch = W.nch;
     D.nblocks = W.n;
     D.item_begin = (int32_t)items;
-    if (M == 1) {
-      D.groups = decode_groups(W);
-      D.splits = W.nch;
-      const uint64_t wu = (uint64_t)D.groups * W.nch * W.n;
-      D.unit_begin = (uint32_t)units;
-      D.units = (uint32_t)wu;
-      D.rg_begin = (uint32_t)groups;
-      units += wu;
-      groups += D.groups;
-    } else {
+    if (M > 1) {
       const uint64_t wunits = (uint64_t)W.n * W.nch;
       const uint64_t wgroups = (uint64_t)prefill_groups(W) * token_groups;
       const uint64_t splits = std::min<uint64_t>(max_splits, std::max<uint64_t>(1, (wunits + split_target - 1) / split_target));
@@ -681,19 +692,66 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   DeviceGuard guard(s->device);
   int e = 0;
   if (M == 1) {
-    // Persistent grid: the largest power of two that is no more than one workgroup per
-    // CU and no more than the number of units (so no workgroup's share is empty).
-    int32_t grid = s->decode_grid_max, lg = 0;
-    while (grid > 1 && (uint64_t)grid > units) grid /= 2;
-    while ((1 << lg) < grid) ++lg;
-    if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+    // Unit lists of both single-token kernels: (weight, row group, block, chunk) with row
+    // groups of `rows` rows.
+    auto plan_units = [&](int rows) {
+      units = groups = 0;
+      for (int32_t j = 0; j < count; ++j) {
+        const Weight& W = s->w[weights[j]];
+        WeightDesc& D = args.w[j];
+        D.groups = (int32_t)((W.mt * kTileRows + rows - 1) / rows);
+        D.splits = W.nch;
+        const uint64_t wu = (uint64_t)D.groups * W.nch * W.n;
+        D.unit_begin = (uint32_t)units;
+        D.units = (uint32_t)wu;
+        D.rg_begin = (uint32_t)groups;
+        units += wu;
+        groups += D.groups;
+      }
+    };
+    // Units [o U / 2^lg, (o + 1) U / 2^lg) of worker o, as the kernels compute them.
+    auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
+    // AUTO takes the shared-operand kernel: on the 8B-shaped layer it measured faster
+    // (77 against 80 us per launch)
+    bool wp = s->decode == BSL_DECODE_PRIVATE;
+    int lg = 0;
+    if (wp) {
+      plan_units(kWpRows);
+      // workers: four per workgroup, at most one workgroup per CU, at most one per unit
+      int32_t workers = kWpWaves * s->decode_grid_max;
+      while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
+      while ((1 << lg) < workers) ++lg;
+      // (no units at all: one workgroup writes y = 0)
+      bool fits = (units == 0 || units >= (uint64_t)workers) && (units << lg) < (1ull << 32);
+      // every workgroup keeps the activations of the weights its units belong to in LDS
+      for (int32_t L = 0; fits && units > 0 && L < workers / kWpWaves; ++L) {
+        const uint64_t a = start((uint64_t)L * kWpWaves, lg), b = start((uint64_t)(L + 1) * kWpWaves, lg) - 1;
+        int32_t ja = 0, jb = 0;
+        while (ja + 1 < count && a >= args.w[ja + 1].unit_begin) ++ja;
+        while (jb + 1 < count && b >= args.w[jb + 1].unit_begin) ++jb;
+        uint64_t bytes = 0;
+        for (int32_t j = ja; j <= jb; ++j) bytes += (uint64_t)args.w[j].nch * kChunkCols * 2;
+        fits = bytes <= (uint64_t)kWpXBytes;
+      }
+      if (!fits) return fail(BSL_EUNSUPPORTED, "forward: the wave-private single-token kernel does not fit this launch");
+    }
+    if (!wp) {
+      plan_units(kDecodeGroupRows);
+      // Persistent grid: the largest power of two that is no more than one workgroup per
+      // CU and no more than the number of units (so no workgroup's share is empty).
+      int32_t grid = s->decode_grid_max;
+      lg = 0;
+      while (grid > 1 && (uint64_t)grid > units) grid /= 2;
+      while ((1 << lg) < grid) ++lg;
+      if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+    }
     args.total_units = (uint32_t)units;
     args.total_groups = (uint32_t)groups;
     args.grid_log2 = lg;
     args.zero_page = s->zero_page;
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
-    e = launch_decode_m1(args, stream);
+    e = wp ? launch_decode_wp(args, stream) : launch_decode_m1(args, stream);
   } else {
     args.zero_page = s->zero_page;
     e = launch_prefill(args, nt, token_groups, stream);
@@ -722,6 +780,14 @@ int bsl_set_path(bsl_stack* s, int32_t path) {
   if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE)
     return fail(BSL_EINVAL, "bsl_set_path: unknown path");
   s->path = path;
+  return BSL_OK;
+}
+
+int bsl_set_decode(bsl_stack* s, int32_t kind) {
+  if (!s) return fail(BSL_EINVAL, "bsl_set_decode: null stack");
+  if (kind != BSL_DECODE_AUTO && kind != BSL_DECODE_SHARED && kind != BSL_DECODE_PRIVATE)
+    return fail(BSL_EINVAL, "bsl_set_decode: unknown kernel");
+  s->decode = kind;
   return BSL_OK;
 }
 

@@ -32,11 +32,15 @@ inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * 
 //          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
 //   vr:    [d_pad][16] fp16, V row-major (zero past d): the tile-reconstruct kernel's
 //          matrix-core operand, 8 consecutive ranks of one column per 16-byte load
+//   vb:    [d_pad/512][16 planes][64 lanes][8] fp16, V in the single-token B-operand
+//          order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] (j < 4)
+//          and V[512 c + 32 b + 16 + 4 kk + j - 4][r] (4 <= j < 8)
 struct BlockPtrs {
   const uint8_t* signs;
   const uint16_t* u;
   const uint16_t* v;
   const uint16_t* vr;
+  const uint16_t* vb;
 };
 
 // One weight of a (grouped) forward launch; passed by value in the kernel arguments.
@@ -75,6 +79,7 @@ struct GroupArgs {
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
+int launch_decode_wp(const GroupArgs& args, void* stream);
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
@@ -90,6 +95,13 @@ constexpr int kDecodeWaves = 16;
 constexpr int kDecodeGroupRows = kDecodeGroupTiles * 16;
 constexpr int kZeroPageBytes = 65536;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCDs
+// Single-token path, wave-private kernel: one worker per wave, four waves per workgroup
+// (one per SIMD), one workgroup per CU; units of 16 row tiles (256 rows).  A workgroup
+// keeps the activations of the weights its units belong to in LDS (at most kWpXBytes).
+constexpr int kWpTiles = 16;
+constexpr int kWpRows = kWpTiles * 16;
+constexpr int kWpWaves = 4;
+constexpr int kWpXBytes = 128 * 1024;
 // Multi-token path (M >= 2): one 8-wave workgroup per item = (512-row group, token
 // group of 2, 4 or 8 tokens, range of the (block, chunk) sequence).  A weight's items are
 // split along that sequence only while splits x padded tokens fit the workspace.

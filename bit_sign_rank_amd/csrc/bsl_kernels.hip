@@ -133,6 +133,7 @@ __device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
   r.u = uniform_ptr(b.u);
   r.v = uniform_ptr(b.v);
   r.vr = uniform_ptr(b.vr);
+  r.vb = uniform_ptr(b.vb);
   return r;
 }
 
@@ -145,6 +146,7 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.u = t->u;
   b.v = t->v;
   b.vr = t->vr;
+  b.vb = t->vb;
   return b;
 }
 
@@ -602,10 +604,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     if (k0 + tid <= item_last - item_first) {
       const uint32_t item = item_first + k0 + tid;
       uint32_t first, last;
-      group_units(item, first, last);
-      const uint32_t expected = owner(last) - owner(first) + 1;
-      const uint32_t seen = __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-      if (seen == expected) {
+      const int j = group_units(item, first, last);
+      // (row groups of a weight without blocks lie between those of its neighbours in
+      // the launch; they have no units and no pieces: y = 0 is written at the start)
+      const bool has_units = args.w[j].units != 0;
+      const uint32_t expected = has_units ? owner(last) - owner(first) + 1 : 0u;
+      const uint32_t seen =
+          has_units ? __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 : 0u;
+      if (has_units && seen == expected) {
         __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_items[atomicAdd(&n_last, 1u)] = item;
       }
@@ -1294,6 +1300,386 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ============================================================ single-token kernel, wave-private operands
+// One worker per wave: four waves per workgroup (one per SIMD), one workgroup per CU.  The
+// work is the list of units (weight, 256-row group = 16 row tiles, block, 512-column chunk)
+// in that order; with U units and 2^lg workers, worker o walks units [o U / 2^lg,
+// (o + 1) U / 2^lg).  No operand is shared between waves, so the unit loop has no barrier.
+//
+// Per unit a wave contracts its 16 row tiles with the chunk's 16 planes on
+// v_smfmac_f32_16x16x64_f16 with A = the plane's activations and B = +-V:
+//  * B holds V of the plane's columns in both signs, in the odd or even group form of
+//    the plane (group G = columns 2G, 2G + 1: rows (V_a, V_b, -V_a, -V_b) or (V_a, -V_a,
+//    V_b, -V_b));
+//  * the two compressed A values of group G are x_a and x_b, and their index fields come
+//    straight from the stored sign bits (as in decode_m1_kernel), so they pick +V or -V;
+//  * hence the MFMA accumulates P[j][r] = sum_c s_jc x_c V_cr with exact fp16 x fp16
+//    products: Z = V (.) x is formed inside the matrix core, never rounded.
+// A lane's 8 A values are the activations of the 8 columns whose signs its stored sign
+// word holds (columns 8 g .. 8 g + 7 of the plane for lane group g), one 16-byte read
+// from LDS, where the workgroup keeps the activations of the weights it works on.
+//
+// Vector memory loads retire in issue order, so a wait for one load also waits for every
+// load issued before it.  The issue order keeps HBM sign loads out of the waits for L2
+// operands: a unit's sign tiles are requested at the start of the previous unit, and the
+// V operands of a unit are requested during the previous unit, before the next sign
+// request.  (U is loaded only by a unit that ends its share of a block: making every unit
+// load it, from the zero page otherwise, measured 10 us slower per launch, all waves then
+// hitting the same few L2 lines.)  Plane b + 1's operands (A read, B built from V, sign indices) are prepared while plane
+// b's MFMAs run, one MFMA then two VALU operations at a time; plane 0 of the next unit is
+// prepared during plane 15.
+struct WpPtrs {
+  const uint8_t* signs;  // sign tiles of the unit's 16 row tiles (1 KiB each, consecutive)
+  const uint8_t* vb;     // B-ordered V of the unit's chunk, 16 planes x 1 KiB
+  const uint8_t* u;      // tiled U of the unit's 16 row tiles (512 B each)
+};
+
+// B operand (+-V in the plane's group form) from the lane's four V words.
+template <bool EVEN>
+__device__ __forceinline__ u32x8 pm_v_operand(const u32x4& v) {
+  u32x8 t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u32x2 g2 = group_words<EVEN>(v[k]);
+    t[2 * k] = g2[0];
+    t[2 * k + 1] = g2[1];
+  }
+  return t;
+}
+
+// s_waitcnt immediate for "at most n vector memory operations outstanding" (n < 64).
+__host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+__global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wp_kernel(GroupArgs args) {
+  constexpr int R = kWpTiles;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kWpXBytes / 2];  // activations (d_pad per weight)
+  __shared__ uint64_t bbase[kMaxGroup][kMaxBlocks];                     // block base addresses
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4;
+  const uint32_t U = args.total_units;
+  const int lg = args.grid_log2;  // log2 of the number of workers
+  const uint32_t G = gridDim.x;
+  const uint32_t bid = blockIdx.x;
+  // XCD-contiguous workgroup index (workgroups are dealt round-robin over the XCDs)
+  const uint32_t L = G >= (uint32_t)kXcds ? (bid % kXcds) * (G / kXcds) + bid / kXcds : bid;
+  const uint32_t worker = L * kWpWaves + wave;
+  const uint32_t u_begin = range_start(worker, U, lg), u_end = range_start(worker + 1, U, lg);
+  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+  if (L == 0) {  // weights without blocks: y = 0, the empty sum
+    for (int j = 0; j < args.count; ++j)
+      if (args.w[j].units == 0)
+        for (int row = threadIdx.x; row < args.w[j].m; row += kWpWaves * 64) store_y(args.w[j].y, row, 0.f, args.y_fp32);
+  }
+  if (U == 0) return;  // (uniform over the grid)
+
+  auto weight_of = [&](uint32_t u) {
+    int j = 0;
+    while (j + 1 < args.count && u >= args.w[j + 1].unit_begin) ++j;
+    return j;
+  };
+  // weights this workgroup works on: their activations go to LDS, back to back
+  const int j0 = weight_of(range_start(L * kWpWaves, U, lg));
+  const int j1 = weight_of(range_start((L + 1) * kWpWaves, U, lg) - 1);
+
+  // ---- cursor over the unit list (wave-uniform)
+  struct Cur {
+    int32_t j, rg, i, ch;
+    uint32_t u;
+    bool valid;
+    int32_t nb, nch, groups, mt, xo;  // xo: LDS offset (elements) of weight j's activations
+    uint32_t rg_begin;
+  };
+  auto load_weight = [&](Cur& c) {
+    const WeightDesc& W = args.w[c.j];
+    c.nb = W.nblocks;
+    c.nch = W.nch;
+    c.groups = W.groups;
+    c.mt = W.mt;
+    c.rg_begin = W.rg_begin;
+    int xo = 0;
+    for (int k = j0; k < c.j; ++k) xo += args.w[k].nch * kChunkCols;
+    c.xo = xo;
+  };
+  auto locate = [&](uint32_t u) {
+    Cur c;
+    c.j = weight_of(u);
+    load_weight(c);
+    const uint32_t local = u - args.w[c.j].unit_begin;
+    const uint32_t per_rg = (uint32_t)c.nch * c.nb;
+    c.rg = local / per_rg;
+    const uint32_t rem = local - c.rg * per_rg;
+    c.i = rem / c.nch;
+    c.ch = rem - c.i * c.nch;
+    c.u = u;
+    c.valid = true;
+    return c;
+  };
+  auto next = [&](Cur c) {
+    if (!c.valid || c.u + 1 >= u_end) {
+      c.valid = false;
+      return c;
+    }
+    ++c.u;
+    if (++c.ch == c.nch) {
+      c.ch = 0;
+      if (++c.i == c.nb) {
+        c.i = 0;
+        if (++c.rg == c.groups) {
+          c.rg = 0;
+          do ++c.j;
+          while (args.w[c.j].units == 0);
+          load_weight(c);
+        }
+      }
+    }
+    return c;
+  };
+  auto block_end = [&](const Cur& c) { return c.ch == c.nch - 1 || c.u + 1 == u_end; };
+  auto group_end = [&](const Cur& c) { return (c.ch == c.nch - 1 && c.i == c.nb - 1) || c.u + 1 == u_end; };
+  auto unit_ptrs = [&](const Cur& c, bool direct = false) {
+    WpPtrs p;
+    if (c.valid) {
+      const uint8_t* base = direct ? load_block(args.w[c.j].blocks, c.i).signs
+                                   : uniform_ptr(reinterpret_cast<const uint8_t*>(bbase[c.j][c.i]));
+      const size_t sb = (size_t)c.mt * c.nch * kTileBytes;  // signs
+      const size_t ub = (size_t)c.mt * 64 * 8;              // tiled U
+      const size_t vbytes = (size_t)c.nch * kPlanes * 64 * 16;  // tiled V = row-major V = B-ordered V
+      p.signs = base + ((size_t)c.ch * c.mt + (size_t)c.rg * R) * kTileBytes;
+      p.u = base + sb + (size_t)c.rg * R * 64 * 8;
+      p.vb = base + sb + ub + 2 * vbytes + (size_t)c.ch * kPlanes * 64 * 16;
+    } else {
+      p.signs = zero_page;
+      p.u = zero_page;
+      p.vb = zero_page;
+    }
+    return p;
+  };
+
+  // ---- loads
+  u32x4 sgn[2][R];  // sign words of the current and the next unit
+  u32x4 vsl[kPlanes];  // V words of the planes (see the issue order above)
+  u32x2 uw[R];
+  auto load_signs = [&](const WpPtrs& p, u32x4 (&s)[R]) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) s[t] = load16_stream(p.signs + t * kTileBytes + lane * 16);
+  };
+  auto load_v = [&](const WpPtrs& p, int b) { return load16(p.vb + (b * 64 + lane) * 16); };
+  auto load_u = [&](const uint8_t* u) {
+#pragma unroll
+    for (int t = 0; t < R; ++t) uw[t] = load8(u + (t * 64 + lane) * 8);
+  };
+  // LDS address of a unit's activations for this lane (plane 0); plane b is 64 b bytes on
+  auto a_base = [&](const Cur& c) {
+    const int off = (c.valid ? c.xo + c.ch * kChunkCols : 0) + 8 * g;
+    return reinterpret_cast<const u32x4*>(&xs[off]);
+  };
+  auto read_a = [&](const u32x4* base, int b) { return base[4 * b]; };
+
+  // ---- prologue: the first unit's signs and V, then the block table and the
+  // activations into LDS (the waits for those also cover the first unit's loads, which
+  // are needed first anyway)
+  Cur c0 = locate(u_begin);
+  Cur c1 = next(c0);
+  Cur c2 = next(c1);
+  WpPtrs p0 = unit_ptrs(c0, true);
+  WpPtrs p1 = unit_ptrs(c1, true);
+  WpPtrs p2 = unit_ptrs(c2, true);
+  load_signs(p0, sgn[0]);
+#pragma unroll
+  for (int b = 0; b < kPlanes; ++b) vsl[b] = load_v(p0, b);
+  for (int e = threadIdx.x; e < kMaxGroup * kMaxBlocks; e += kWpWaves * 64) {
+    const int bj = e / kMaxBlocks, bi = e % kMaxBlocks;
+    if (bj < args.count && bi < args.w[bj].nblocks) {
+      const u32x2 t = load8(&args.w[bj].blocks[bi].signs);
+      bbase[bj][bi] = t[0] | ((uint64_t)t[1] << 32);
+    }
+  }
+  {
+    int off = 0;
+    for (int j = j0; j <= j1; ++j) {
+      const int d = args.w[j].d, dp = args.w[j].nch * kChunkCols;
+      const uint16_t* x = args.w[j].x;
+      for (int c0s = threadIdx.x * 8; c0s < dp; c0s += 8 * kWpWaves * 64 * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = c0s + k * 8 * kWpWaves * 64;
+          v[k] = c < d ? load16(x + c) : (u32x4){0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = c0s + k * 8 * kWpWaves * 64;
+          if (c < dp) *reinterpret_cast<u32x4*>(&xs[off + c]) = v[k];
+        }
+      }
+      off += dp;
+    }
+  }
+  __syncthreads();
+
+  // acc: P of the current block; accy: its U-weighted, r-summed rows over the blocks done
+  // (one row per lane and tile, see reduce_columns)
+  float4v acc[R];
+  float accy[R];
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
+    acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+    accy[t] = 0.f;
+  }
+  uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
+  asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs: one v_and_or_b32 each)
+  uint32_t ix_odd[R], ix_even[R];
+  u32x4 av[2];
+  u32x8 bw[2];
+  // plane 0 of the first unit
+#pragma unroll
+  for (int t = 0; t < R; ++t) ix_odd[t] = sign_index_v(sgn[0][t][0], m_odd, false);
+  const u32x4* abase = a_base(c0);
+  av[0] = read_a(abase, 0);
+  bw[0] = pm_v_operand<false>(vsl[0]);
+  vsl[0] = load_v(p1, 0);
+
+  const int rsel = reduced_row(lane);
+  auto store_piece = [&](const Cur& c) {
+    const uint32_t item = c.rg_begin + c.rg;
+    float* piece = args.pieces + (size_t)(item + worker) * kWpRows;
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      if ((lane & 3) == 0)
+        __hip_atomic_store(&piece[t * kTileRows + rsel], accy[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      accy[t] = 0.f;
+    }
+  };
+
+  // ---- one unit: c0 with signs in `cur`; on entry plane 0's operands are ready, V of
+  // planes 1..15 of c0 and of plane 0 of c1 are in vsl
+  auto step = [&](u32x4 (&cur)[R], u32x4 (&nxt)[R]) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_signs(p1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    if (block_end(c0)) load_u(p0.u);
+    const Cur c3 = next(c2);
+    const WpPtrs p3 = unit_ptrs(c3);
+    const u32x4* abase_next = a_base(c1);
+#define BSL_WP_PLANE(B)                                                                                        \
+  __builtin_amdgcn_sched_barrier(0);                                                                           \
+  {                                                                                                            \
+    constexpr int NB = ((B) + 1) % kPlanes; /* plane prepared in this region */                                \
+    if ((B) < kPlanes - 1) {                                                                                   \
+      if (NB % 4 == 0) {                                                                                       \
+        _Pragma("unroll") for (int t = 0; t < R; ++t) ix_odd[t] = sign_index_v(cur[t][NB / 4], m_odd, false); \
+      }                                                                                                        \
+      if (NB % 4 == 2) {                                                                                       \
+        _Pragma("unroll") for (int t = 0; t < R; ++t) ix_even[t] = sign_index_v(cur[t][NB / 4], m_even, true); \
+      }                                                                                                        \
+      av[NB % 2] = read_a(abase, NB);                                                                          \
+      bw[NB % 2] = plane_even(NB) ? pm_v_operand<true>(vsl[NB]) : pm_v_operand<false>(vsl[NB]);             \
+      vsl[NB] = load_v(p1, NB);                                                                                \
+    } else {                                                                                                   \
+      _Pragma("unroll") for (int t = 0; t < R; ++t) ix_odd[t] = sign_index_v(nxt[t][0], m_odd, false);        \
+      av[0] = read_a(abase_next, 0);                                                                           \
+      bw[0] = pm_v_operand<false>(vsl[0]);                                                                     \
+      vsl[0] = load_v(p2, 0);                                                                                  \
+    }                                                                                                          \
+    _Pragma("unroll") for (int t = 0; t < R; ++t) acc[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(           \
+        __builtin_bit_cast(half8, av[(B) % 2]), __builtin_bit_cast(half16, bw[(B) % 2]), acc[t],              \
+        (int)(plane_even(B) ? ix_even[t] : ix_odd[t]), 0, plane_half(B));                                      \
+    /* one MFMA, then up to two VALU operations: the preparation of the next plane runs */                    \
+    /* in the matrix core's shadow instead of between bursts of MFMAs */                                      \
+    _Pragma("unroll") for (int t = 0; t < R; ++t) {                                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                       \
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                                                       \
+    }                                                                                                          \
+  }
+    BSL_WP_PLANE(0) BSL_WP_PLANE(1) BSL_WP_PLANE(2) BSL_WP_PLANE(3) BSL_WP_PLANE(4) BSL_WP_PLANE(5)
+    BSL_WP_PLANE(6) BSL_WP_PLANE(7) BSL_WP_PLANE(8) BSL_WP_PLANE(9) BSL_WP_PLANE(10) BSL_WP_PLANE(11)
+    BSL_WP_PLANE(12) BSL_WP_PLANE(13) BSL_WP_PLANE(14) BSL_WP_PLANE(15)
+#undef BSL_WP_PLANE
+    __builtin_amdgcn_sched_barrier(0);
+    if (block_end(c0)) {  // U-weight the block's products and sum them over r
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        const half2v u01 = as_half2(uw[t][0]), u23 = as_half2(uw[t][1]);
+        float4v w;
+        w[0] = (float)u01[0] * acc[t][0];
+        w[1] = (float)u01[1] * acc[t][1];
+        w[2] = (float)u23[0] * acc[t][2];
+        w[3] = (float)u23[1] * acc[t][3];
+        accy[t] += reduce_columns(w, lane);
+        acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    if (group_end(c0)) store_piece(c0);
+    c0 = c1;
+    c1 = c2;
+    c2 = c3;
+    p0 = p1;
+    p1 = p2;
+    p2 = p3;
+    abase = abase_next;
+  };
+
+  const uint32_t item_first = c0.rg_begin + c0.rg;
+  const uint32_t n = u_end - u_begin;
+  for (uint32_t s = 0; s < n; s += 2) {
+    step(sgn[0], sgn[1]);
+    if (s + 1 < n) step(sgn[1], sgn[0]);
+  }
+
+  // ---- end of the range: count this worker in for every row group it touched; the
+  // last one to arrive at a row group adds the pieces (one per worker owner(first) ..
+  // owner(last), in that order) and writes y.
+  const uint32_t W = 1u << lg;
+  auto owner = [&](uint32_t u) {
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < W && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  auto group_units = [&](uint32_t item, uint32_t& first, uint32_t& last) {
+    int j = 0;
+    while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
+    const WeightDesc& Wd = args.w[j];
+    const uint32_t per_rg = (uint32_t)Wd.nblocks * Wd.nch;
+    first = Wd.unit_begin + (item - Wd.rg_begin) * per_rg;
+    last = first + per_rg - 1;
+    return j;
+  };
+  const int je = weight_of(u_end - 1);
+  const uint32_t item_last =
+      args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's piece stores have completed
+  for (uint32_t item = item_first; item <= item_last; ++item) {
+    uint32_t first, last;
+    const int j = group_units(item, first, last);
+    if (args.w[j].units == 0) continue;  // a weight without blocks (y = 0 is written above)
+    const uint32_t o0 = owner(first), o1 = owner(last);
+    uint32_t seen = 0;
+    if (lane == 0) seen = __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    seen = __builtin_amdgcn_readfirstlane(seen);
+    if (seen != o1 - o0 + 1) continue;
+    if (lane == 0) __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const WeightDesc& Wd = args.w[j];
+#pragma unroll
+    for (int q = 0; q < kWpRows / 64; ++q) {
+      const int rr = q * 64 + lane;
+      const float* base = args.pieces + (size_t)item * kWpRows + rr;
+      float acc_y = 0.f;
+      for (uint32_t o = o0; o <= o1; o += 16) {  // (16 loads in flight per round trip)
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          v[k] = __hip_atomic_load(base + (size_t)min(o + k, o1) * kWpRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc_y += o + k <= o1 ? v[k] : 0.f;
+      }
+      const int row = (int)(item - Wd.rg_begin) * kWpRows + rr;
+      if (row < Wd.m) store_y(Wd.y, row, acc_y, args.y_fp32);
+    }
+  }
+}
+
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write the signs.
 // Path 0: the single-token kernel's sparse indices (odd form: field 2 s + j, even form:
@@ -1351,6 +1737,12 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
   // at all (every weight empty) one workgroup still runs, to write y = 0.
   hipLaunchKernelGGL((decode_m1_kernel<kDecodeWaves, kDecodeGroupTiles / kDecodeWaves, kDecodeWaves / 4>),
                      dim3(1u << args.grid_log2), dim3(kDecodeWaves * 64), 0, st, args);
+  return (int)hipGetLastError();
+}
+
+int launch_decode_wp(const GroupArgs& args, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(decode_wp_kernel, dim3((1u << args.grid_log2) / kWpWaves), dim3(kWpWaves * 64), 0, st, args);
   return (int)hipGetLastError();
 }
 

@@ -141,8 +141,9 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
 int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
 
 /* Device bytes currently held by loaded blocks (what budget_bytes caps).  A loaded block
- * occupies its padded tiled signs and factors plus a row-major copy of V (32 bytes per
- * padded column) that the tile-reconstruct path reads. */
+ * occupies its padded tiled signs and factors plus two more copies of V in the orders
+ * the tile-reconstruct kernel and the wave-private single-token kernel read (32 bytes
+ * per padded column each). */
 uint64_t bsl_resident_bytes(const bsl_stack* s);
 
 /* y = x W_hat_n^T for weight w with its n loaded blocks.
@@ -173,6 +174,20 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2
 int bsl_set_path(bsl_stack* s, int32_t path);
+
+/* Kernel of the single-token forward (M = 1; bsl_set_decode).  Both compute the same
+ * sums, in different orders (results agree to fp32 rounding, not bit for bit):
+ *   BSL_DECODE_SHARED: 16 waves per CU share each unit's B operands (+-Z = +-V x in fp16)
+ *     through LDS, one barrier per unit.
+ *   BSL_DECODE_PRIVATE: every wave builds its own B operands (+-V) and carries x in the
+ *     sparse MFMA's A operand, so the products V x are exact and no barrier is needed.
+ *     A workgroup keeps the activations of the weights it works on in LDS (128 KiB);
+ *     a launch that does not fit fails with BSL_EUNSUPPORTED.
+ *   BSL_DECODE_AUTO (the default): SHARED, the faster of the two on this hardware. */
+#define BSL_DECODE_AUTO 0
+#define BSL_DECODE_SHARED 1
+#define BSL_DECODE_PRIVATE 2
+int bsl_set_decode(bsl_stack* s, int32_t kind);
 
 /* Run a forward kernel's own sign-unpack code on block i of weight w and write the
  * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes).

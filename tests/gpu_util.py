@@ -18,12 +18,14 @@ def stream_ptr(stream=None) -> int:
 class Stack:
     """A bitstack_linear stack over the given weights (list of (m, d, blocks))."""
 
-    def __init__(self, weights, n_cap=16, budget=0, device=0, path=None):
+    def __init__(self, weights, n_cap=16, budget=0, device=0, path=None, decode=None):
         self.shapes = [(m, d) for m, d, _ in weights]
         self.blocks = [b for _, _, b in weights]
         self.h = bsl.bsl_init(device, [m for m, _ in self.shapes], [d for _, d in self.shapes], 16, n_cap, budget)
         if path is not None:
             bsl.bsl_set_path(self.h, path)
+        if decode is not None:
+            bsl.bsl_set_decode(self.h, decode)
         for w, blocks in enumerate(self.blocks):
             bsl.bsl_set_source(self.h, w, blocks)
 

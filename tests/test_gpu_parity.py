@@ -290,6 +290,71 @@ def test_prefill_grouped_launch_and_zero_blocks(path):
             assert rel_err(y, oracle.forward(x, blocks, n)) <= REL_TOL
 
 
+# ---------------------------------------------------------------- single-token kernels
+DECODES = [bsl.BSL_DECODE_SHARED, bsl.BSL_DECODE_PRIVATE]
+DECODE_IDS = ["shared", "private"]
+
+
+@pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1),
+                                   (3000, 1544, 5)])
+@pytest.mark.parametrize("decode", DECODES, ids=DECODE_IDS)
+def test_integer_decode_bit_exact_both_kernels(m, d, n, decode):
+    blocks = integer_blocks(m, d, n)
+    x = synth.integer_activations(3, 1, d)
+    with Stack([(m, d, blocks)], decode=decode) as st:
+        st.load([n])
+        y = st.forward(0, x)
+    assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+@pytest.mark.parametrize("decode", [bsl.BSL_DECODE_AUTO] + DECODES, ids=["auto"] + DECODE_IDS)
+def test_decode_grouped_with_empty_weights_between(decode):
+    """Weights without blocks in the middle and at the ends of a grouped single-token
+    launch: their y is zero and their row groups do not disturb their neighbours'."""
+    shapes = [(512, 1024), (1024, 512), (300, 1536), (64, 2048), (2048, 1024)]
+    counts = [0, 3, 0, 2, 0]
+    ws = [(m, d, synth.synthetic_blocks(41, m, d, 3, 16, j)) for j, (m, d) in enumerate(shapes)]
+    xs = [synth.activations(41, 1, d, j) for j, (_, d) in enumerate(shapes)]
+    with Stack(ws, decode=decode) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(len(shapes))), xs)
+    for j, (m, d, blocks) in enumerate(ws):
+        if counts[j] == 0:
+            assert not ys[j].any()
+        else:
+            assert rel_err(ys[j], oracle.forward(xs[j], blocks, counts[j])) <= REL_TOL
+
+
+def test_decode_kernels_agree(cfg1_blocks):
+    x = synth.activations(43, 1, 1024)
+    outs = []
+    for decode in DECODES:
+        with Stack([(1024, 1024, cfg1_blocks)], decode=decode) as st:
+            st.load([4])
+            outs.append(st.forward(0, x))
+    ref = oracle.forward(x, cfg1_blocks, 4)
+    for y in outs:
+        assert rel_err(y, ref) <= REL_TOL
+    assert rel_err(outs[0], outs[1]) <= 1e-3
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("layer", ["llama3_8b", "llama2_70b"])
+def test_private_decode_fits_the_layer_shapes(layer):
+    """The wave-private kernel takes the whole 8B- and 70B-shaped layers in one grouped
+    launch (BSL_DECODE_PRIVATE fails rather than falling back)."""
+    shapes = synth.LLAMA3_8B_LAYER if layer == "llama3_8b" else synth.LLAMA2_70B_LAYER
+    counts = [2] * len(shapes)
+    ws = [(m, d, synth.synthetic_blocks(44, m, d, 2, 16, j)) for j, (_, m, d) in enumerate(shapes)]
+    xs = [synth.activations(44, 1, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(ws, decode=bsl.BSL_DECODE_PRIVATE) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(len(shapes))), xs)
+    for j, (m, d, blocks) in enumerate(ws):
+        rows = synth.sample_rows(44, m, 64, j)
+        assert rel_err(ys[j][:, rows], oracle.forward_rows(xs[j], blocks, rows, 2)) <= REL_TOL
+
+
 # ---------------------------------------------------------------- input-channel scale
 @pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
 @pytest.mark.parametrize("M", [1, 4, 40])
@@ -379,7 +444,10 @@ def test_input_scale_overflow_after_a_queued_copy():
 def test_errors_leave_state_unchanged(cfg1_blocks):
     x = torch.zeros((1, 1024 + 8), dtype=torch.float16, device="cuda")
     y = torch.zeros((1, 1024), dtype=torch.float32, device="cuda")
-    budget = bsl.bsl_block_bytes(1024, 1024) * 2 + 100_000  # room for 2 blocks, not 3
+    with Stack([(1024, 1024, cfg1_blocks)]) as probe:
+        probe.load([1])
+        slot = bsl.bsl_resident_bytes(probe.h)  # device bytes of one loaded block
+    budget = 2 * slot + slot // 2  # room for 2 blocks, not 3
     with Stack([(1024, 1024, cfg1_blocks)], budget=budget) as st:
         st.load([2])
         before = bsl.bsl_resident_bytes(st.h)
@@ -398,6 +466,9 @@ def test_errors_leave_state_unchanged(cfg1_blocks):
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_set_path(st.h, 3)  # no such formulation
+        assert e.value.code == bsl.BSL_EINVAL
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_set_decode(st.h, 3)  # no such kernel
         assert e.value.code == bsl.BSL_EINVAL
         assert bsl.bsl_active_blocks(st.h, 0) == 2
         # still works after the failures

@@ -24,6 +24,7 @@ BSL_EUNSUPPORTED = -4
 BSL_PATH_AUTO = 0
 BSL_PATH_FACTORED = 1
 BSL_PATH_TILE = 2
+BSL_PATH_DENSE = 3
 BSL_DECODE_AUTO = 0
 BSL_DECODE_SHARED = 1
 BSL_DECODE_PRIVATE = 2

@@ -4,6 +4,7 @@
 #include "bitstack_linear.h"
 
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <climits>
@@ -184,6 +185,12 @@ struct bsl_stack {
   size_t staging_bytes = 0;
   hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] finished
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
+  // dense path (set up by bsl_set_path): restored W_hat of up to kMaxGroup weights, a
+  // rocBLAS handle and its workspace
+  uint16_t* dense_ws = nullptr;
+  size_t dense_ws_bytes = 0;
+  void* blas_ws = nullptr;
+  rocblas_handle blas = nullptr;
   std::vector<Weight> w;
 };
 
@@ -628,6 +635,65 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
   return BSL_OK;
 }
 
+// W_hat of a weight in the dense workspace: [m_pad][d_pad] fp16
+size_t dense_bytes(const Weight& W) { return (size_t)W.mt * kTileRows * W.nch * kChunkCols * 2; }
+
+// Dense path: restore W_hat of every weight of the launch into the workspace (one launch),
+// then y = x W_hat^T per weight with a library GEMM (fp16 in, fp32 accumulate).
+int forward_dense(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
+                  int32_t y_is_fp32, void* stream) {
+  if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");
+  GroupArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.count = count;
+  args.M = M;
+  args.y_fp32 = 0;
+  size_t off = 0;
+  uint64_t items = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int32_t w = weights[j];
+    if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
+    for (int32_t jj = 0; jj < j; ++jj)
+      if (weights[jj] == w) return fail(BSL_EINVAL, "forward: a weight appears twice in one launch");
+    if (!x[j] || !y[j]) return fail(BSL_EINVAL, "forward: null x or y");
+    if ((reinterpret_cast<uintptr_t>(x[j]) & 15) != 0) return fail(BSL_EINVAL, "forward: x must be 16-byte aligned");
+    const Weight& W = s->w[w];
+    WeightDesc& D = args.w[j];
+    D.blocks = W.dtable;
+    D.y = reinterpret_cast<uint8_t*>(s->dense_ws) + off;
+    D.m = W.m;
+    D.d = W.d;
+    D.mt = W.mt;
+    D.nch = W.nch;
+    D.nblocks = W.n;
+    D.item_begin = (int32_t)items;
+    items += (uint64_t)(W.mt * kTileRows / 128) * 2 * W.nch;
+    off += dense_bytes(W);
+  }
+  if (off > s->dense_ws_bytes) return fail(BSL_EUNSUPPORTED, "forward: the dense path's workspace is too small for this launch");
+  if (items > (uint64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tiles for one launch");
+  args.total_items = (int32_t)items;
+  DeviceGuard guard(s->device);
+  int e = launch_restore(args, stream);
+  if (e != 0) return hip_fail(static_cast<hipError_t>(e), "restore launch");
+  if (rocblas_set_stream(s->blas, static_cast<hipStream_t>(stream)) != rocblas_status_success)
+    return fail(BSL_EHIP, "rocblas_set_stream failed");
+  const float alpha = 1.f, beta = 0.f;
+  const rocblas_datatype yt = y_is_fp32 ? rocblas_datatype_f32_r : rocblas_datatype_f16_r;
+  for (int32_t j = 0; j < count; ++j) {
+    const Weight& W = s->w[weights[j]];
+    const int ld = W.nch * kChunkCols;
+    // column-major view: y^T (m x M) = W_hat (m x d, stored as d_pad x m) ^T  x^T (d x M)
+    const rocblas_status st = rocblas_gemm_ex(s->blas, rocblas_operation_transpose, rocblas_operation_none, W.m, M, W.d,
+                                              &alpha, args.w[j].y, rocblas_datatype_f16_r, ld, x[j], rocblas_datatype_f16_r,
+                                              W.d, &beta, y[j], yt, W.m, y[j], yt, W.m, rocblas_datatype_f32_r,
+                                              rocblas_gemm_algo_standard, 0, 0);
+    if (st != rocblas_status_success)
+      return fail(BSL_EHIP, std::string("rocblas_gemm_ex: ") + rocblas_status_to_string(st));
+  }
+  return BSL_OK;
+}
+
 int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
                  int32_t y_is_fp32, void* stream) {
   if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");
@@ -637,6 +703,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
+  if (s->path == BSL_PATH_DENSE && M > 1) return forward_dense(s, count, weights, x, y, M, y_is_fp32, stream);
   const bool tile = s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens);
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
   const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
@@ -777,8 +844,36 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
 
 int bsl_set_path(bsl_stack* s, int32_t path) {
   if (!s) return fail(BSL_EINVAL, "bsl_set_path: null stack");
-  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE)
+  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE && path != BSL_PATH_DENSE)
     return fail(BSL_EINVAL, "bsl_set_path: unknown path");
+  if (path == BSL_PATH_DENSE && !s->blas) {
+    // workspace for the kMaxGroup largest weights' W_hat, a rocBLAS handle and its workspace
+    std::vector<size_t> sizes;
+    for (const Weight& W : s->w) sizes.push_back(dense_bytes(W));
+    std::sort(sizes.rbegin(), sizes.rend());
+    size_t need = 0;
+    for (size_t k = 0; k < sizes.size() && k < (size_t)kMaxGroup; ++k) need += sizes[k];
+    DeviceGuard guard(s->device);
+    hipError_t e = hipMalloc(&s->dense_ws, need);
+    if (e != hipSuccess) {
+      s->dense_ws = nullptr;
+      return fail(BSL_ENOMEM, "bsl_set_path: " + std::to_string(need) + " bytes for the dense path's workspace");
+    }
+    e = hipMalloc(&s->blas_ws, kDenseBlasWorkspace);
+    rocblas_handle h = nullptr;
+    if (e == hipSuccess && rocblas_create_handle(&h) == rocblas_status_success &&
+        rocblas_set_workspace(h, s->blas_ws, kDenseBlasWorkspace) == rocblas_status_success) {
+      s->blas = h;
+      s->dense_ws_bytes = need;
+    } else {
+      if (h) (void)rocblas_destroy_handle(h);
+      if (s->blas_ws) (void)hipFree(s->blas_ws);
+      (void)hipFree(s->dense_ws);
+      s->blas_ws = nullptr;
+      s->dense_ws = nullptr;
+      return fail(BSL_ENOMEM, "bsl_set_path: rocBLAS set-up failed");
+    }
+  }
   s->path = path;
   return BSL_OK;
 }
@@ -819,6 +914,9 @@ void bsl_destroy(bsl_stack* s) {
   if (s->arrivals) (void)hipFree(s->arrivals);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);
+  if (s->blas) (void)rocblas_destroy_handle(s->blas);
+  if (s->blas_ws) (void)hipFree(s->blas_ws);
+  if (s->dense_ws) (void)hipFree(s->dense_ws);
   for (int k = 0; k < 2; ++k) {
     if (s->staging[k]) (void)hipHostFree(s->staging[k]);
     if (s->staged[k]) (void)hipEventDestroy(s->staged[k]);

@@ -80,6 +80,9 @@ struct GroupArgs {
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_decode_wp(const GroupArgs& args, void* stream);
+// Dense path: W_hat of each weight into WeightDesc::y (fp16, [m][d_pad]); items are
+// (128-row group, half chunk) pairs.
+int launch_restore(const GroupArgs& args, void* stream);
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
@@ -120,6 +123,8 @@ constexpr int kTileAutoMinTokens = 8;   // BSL_PATH_AUTO takes the tile path fro
 constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB
 constexpr int kTileItemsPerCu = 2;     // aim of the column-range cutting
 constexpr int kTileCounters = 1 << 16;
+// Dense path: the library GEMM's workspace (allocated when the path is selected).
+constexpr size_t kDenseBlasWorkspace = (size_t)64 << 20;
 
 // Records the calling thread's error message (bsl_last_error) and returns code.
 int set_error(int code, const std::string& msg);

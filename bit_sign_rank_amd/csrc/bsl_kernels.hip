@@ -1300,6 +1300,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ============================================================ restore kernel (dense path)
+// W_hat of every weight of a launch, written row-major in fp16 to a workspace, for a
+// library GEMM to multiply with the tokens.  One wave per 32-row x 256-column tile (half
+// a chunk: four steps of two 32-column planes).  For every loaded block the wave runs the
+// tile path's rebuild (K = 16 MFMA per plane: A = V rows of the plane in sigma order from
+// the row-major copy, B = U; lane (h, j) gets row j, plane columns 16 h .. 16 h + 15),
+// rounds the product to fp16 pairs (plane 2 qk, 2 qk + 1 at one column) and accumulates
+// them with the block's +-1 sign pairs, exactly as the tile path does; after the last
+// block the pairs are split by plane and stored.  Rows past m are not stored; columns past
+// d hold zeros (V is zero there).  (Fetching the next block's operands ahead, with one
+// wave per SIMD to make room, measured slower: the work is VALU-bound, and two waves per
+// SIMD issue it faster.)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void restore_kernel(GroupArgs args) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, jl = lane & 31;
+  const WeightDesc W = find_weight(args, blockIdx.x);
+  const int local = blockIdx.x - W.item_begin;
+  const int halves = 2 * W.nch;                       // 256-column tiles per row
+  const int rg = local / halves, hc = local % halves;  // 128-row group, half chunk
+  const int c = hc >> 1, half = hc & 1;
+  const int row0 = rg * 128 + 32 * wave;
+  const int row = row0 + jl;
+  const int nb = W.nblocks;
+  const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
+  const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
+  const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
+  const uint32_t uoff = (((uint32_t)(row >> 4) * 64u + 16u * ((row >> 2) & 3) + 8u * h) * 4u + (row & 3)) * 2u;
+  const uint32_t cb_sign = __builtin_amdgcn_readfirstlane((uint32_t)c * (uint32_t)W.mt * kTileBytes);
+  uint32_t vmask = 0x80008000u;
+  asm volatile("" : "+v"(vmask));  // (a VGPR operand, so that AND and OR fuse into v_and_or_b32)
+
+  half2v wp[4][16];  // [step][v]: (plane 2 qk, plane 2 qk + 1) at column 16 h + v
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) wp[s][v] = (half2v){0, 0};
+
+  for (int i = 0; i < nb; ++i) {
+    const BlockPtrs bp = load_block(W.blocks, i);
+    half8 uf;
+    const rsrc_t ures = make_rsrc(bp.u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) uf[e] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(ures, uoff + 8u * e, 0, 0));
+    // sign words q = 2 half, 2 half + 1 of the lane's two stored groups (g2)
+    uint32_t sw[2][2];
+    const rsrc_t sres = make_rsrc(bp.signs);
+#pragma unroll
+    for (int g2 = 0; g2 < 2; ++g2) {
+      const u32x2 v = buf_load8(sres, soff + 256u * g2 + 8u * half, cb_sign);
+      sw[g2][0] = v[0];
+      sw[g2][1] = v[1];
+    }
+    const rsrc_t vres = make_rsrc(bp.vr);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int qk = 4 * half + s;  // plane pair (2 qk, 2 qk + 1) of the chunk
+      const uint32_t cb = __builtin_amdgcn_readfirstlane((uint32_t)(c * kChunkCols + 64 * qk) * (kRank * 2));
+      const u32x4 va = buf_load16(vres, voff, cb);
+      const u32x4 vb = buf_load16(vres, voff + 32u * kRank * 2u, cb);
+      float16v d0 = rebuild_mfma(as_half8(va), uf);
+      float16v d1 = rebuild_mfma(as_half8(vb), uf);
+      mfma_result_ready(d0, d1);
+      const int q = qk >> 1, kp = qk & 1;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t sp = tile_sign_pair(sw[v >> 3][q & 1], v & 7, kp, vmask);
+        const half2v dp = __builtin_convertvector((float2v){d0[v], d1[v]}, half2v);
+        wp[s][v] = as_half2(sp) * dp + wp[s][v];
+      }
+    }
+  }
+  if (row >= W.m) return;
+  uint16_t* out = static_cast<uint16_t*>(W.y) + (size_t)row * (W.nch * kChunkCols) + c * kChunkCols;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int qk = 4 * half + s;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4 p0, p1;
+#pragma unroll
+      for (int m2 = 0; m2 < 4; ++m2) {
+        const uint32_t lo = as_u32(wp[s][8 * s2 + 2 * m2]), hi = as_u32(wp[s][8 * s2 + 2 * m2 + 1]);
+        p0[m2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // plane 2 qk
+        p1[m2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // plane 2 qk + 1
+      }
+      *reinterpret_cast<u32x4*>(out + 64 * qk + 16 * h + 8 * s2) = p0;
+      *reinterpret_cast<u32x4*>(out + 64 * qk + 32 + 16 * h + 8 * s2) = p1;
+    }
+  }
+}
+
 // ============================================================ single-token kernel, wave-private operands
 // One worker per wave: four waves per workgroup (one per SIMD), one workgroup per CU.  The
 // work is the list of units (weight, 256-row group = 16 row tiles, block, 512-column chunk)
@@ -1743,6 +1835,12 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
 int launch_decode_wp(const GroupArgs& args, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(decode_wp_kernel, dim3((1u << args.grid_log2) / kWpWaves), dim3(kWpWaves * 64), 0, st, args);
+  return (int)hipGetLastError();
+}
+
+int launch_restore(const GroupArgs& args, void* stream) {
+  if (args.total_items == 0) return 0;
+  hipLaunchKernelGGL(restore_kernel, dim3(args.total_items), dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }
 

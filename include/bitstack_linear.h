@@ -169,10 +169,18 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *     the tile of W_hat is rounded to fp16 (each block's U_i V_i^T and the running sum
  *     over blocks), then y accumulates in fp32.  Work grows as n * k * m * d per group of
  *     512 tokens plus M * m * d, so it is the fast form for batches.
+ *   BSL_PATH_DENSE: the same restoration, done once per forward for the whole weight into
+ *     a device workspace (fp16 W_hat, rounded as TILE rounds it), followed by a rocBLAS
+ *     GEMM per weight (fp16 in, fp32 accumulate).  Work: n * k * m * d once plus M * m * d,
+ *     and 2 bytes per weight element of extra HBM traffic each way.  Selecting it
+ *     allocates the workspace (the eight largest weights' W_hat) and a rocBLAS handle
+ *     (BSL_ENOMEM if that fails; the path is then unchanged).  M = 1 keeps the
+ *     single-token kernel.
  *   BSL_PATH_AUTO (the default): FACTORED for M below 8, TILE from M = 8 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2
+#define BSL_PATH_DENSE 3
 int bsl_set_path(bsl_stack* s, int32_t path);
 
 /* Kernel of the single-token forward (M = 1; bsl_set_decode).  Both compute the same

@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 import bit_sign_rank_amd as bsl  # noqa: E402  (no skip: a missing library must fail here)
 from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
 
-PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE]
-PATH_IDS = ["factored", "tile"]
+PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE, bsl.BSL_PATH_DENSE]
+PATH_IDS = ["factored", "tile", "dense"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -465,7 +465,7 @@ def test_errors_leave_state_unchanged(cfg1_blocks):
             bsl.bsl_load_blocks(st.h, [5], 0)  # only 4 source blocks
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
-            bsl.bsl_set_path(st.h, 3)  # no such formulation
+            bsl.bsl_set_path(st.h, 4)  # no such formulation
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_set_decode(st.h, 3)  # no such kernel

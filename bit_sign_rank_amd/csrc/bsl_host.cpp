@@ -45,36 +45,45 @@ bool shape_ok(int64_t m, int64_t d) { return m >= 1 && m <= (1 << 20) && d >= 8 
 // bit 2 e ("even" positions), so the word is the sum of the four planes' bytes spread
 // out to every second bit.
 
-// Spread the 8 bits of a byte to bit positions 0, 2, .., 14.
-uint32_t spread2(uint32_t x) {
-  x = (x | (x << 4)) & 0x0F0Fu;
-  x = (x | (x << 2)) & 0x3333u;
-  x = (x | (x << 1)) & 0x5555u;
-  return x;
-}
+// Spread the 8 bits of a byte to bit positions 0, 2, .., 14 (table of all 256 bytes).
+struct SpreadTable {
+  uint16_t v[256];
+  SpreadTable() {
+    for (uint32_t x = 0; x < 256; ++x) {
+      uint32_t y = 0;
+      for (int e = 0; e < 8; ++e) y |= ((x >> e) & 1u) << (2 * e);
+      v[x] = (uint16_t)y;
+    }
+  }
+};
+const SpreadTable kSpread;
+
 void pack_rows(const uint8_t* src, int64_t m, int64_t d, uint8_t* out, int64_t r0, int64_t r1) {
   const int64_t nch = pad_cols(d) / kChunkCols;
   const int64_t mt = pad_rows(m) / kTileRows;
   const int64_t rowbytes = d / 8;
+  const uint16_t* sp = kSpread.v;
+  uint8_t tail[64];
   for (int64_t r = r0; r < r1; ++r) {
     const int64_t t = r / kTileRows, i = r % kTileRows;
-    const uint8_t* row = r < m ? src + r * rowbytes : nullptr;
     for (int64_t c = 0; c < nch; ++c) {
       uint8_t* tile = out + (c * mt + t) * kTileBytes;
+      // the chunk's 64 source bytes of this row (zeros past the row's end or past m)
+      const uint8_t* seg;
+      if (r < m && 64 * (c + 1) <= rowbytes) {
+        seg = src + r * rowbytes + 64 * c;
+      } else {
+        std::memset(tail, 0, sizeof(tail));
+        if (r < m && 64 * c < rowbytes) std::memcpy(tail, src + r * rowbytes + 64 * c, (size_t)(rowbytes - 64 * c));
+        seg = tail;
+      }
       for (int g = 0; g < 4; ++g) {
-        uint8_t bytes[kPlanes];
-        for (int b = 0; b < kPlanes; ++b) {
-          const int64_t byte = 64 * c + 4 * b + g;  // within the row
-          bytes[b] = (row && byte < rowbytes) ? row[byte] : 0;
-        }
         uint32_t words[4];
         for (int q = 0; q < 4; ++q) {
-          uint32_t w = 0;
-          for (int k = 0; k < 4; ++k) {  // plane 4 q + k: half k % 2, odd positions for k < 2
-            const int half = k & 1, odd = k < 2 ? 1 : 0;
-            w |= spread2(bytes[4 * q + k]) << (16 * half + odd);
-          }
-          words[q] = w;
+          // plane 4 q + k is source byte 4 (4 q + k) + g; half k % 2, odd positions for k < 2
+          const uint8_t* bq = seg + 16 * q + g;
+          words[q] = ((uint32_t)sp[bq[0]] << 1) | ((uint32_t)sp[bq[4]] << 17) | (uint32_t)sp[bq[8]] |
+                     ((uint32_t)sp[bq[12]] << 16);
         }
         std::memcpy(tile + (16 * g + i) * 16, words, 16);  // little-endian words
       }

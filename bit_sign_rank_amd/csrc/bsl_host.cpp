@@ -136,6 +136,12 @@ void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
   std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
 }
 
+// U (m x 16, row-major fp16) -> [m_pad][16], zero past m.
+void rowmajor_u(const uint16_t* u, int64_t m, uint16_t* out) {
+  std::memcpy(out, u, (size_t)m * kRank * 2);
+  std::memset(out + m * kRank, 0, (size_t)(pad_rows(m) - m) * kRank * 2);
+}
+
 // V (d x 16, row-major fp16) -> [d_pad/512][16][64][8] in the single-token kernel's
 // B-operand order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] for
 // j < 4 and V[512 c + 32 b + 16 + 4 kk + j - 4][r] for j >= 4 (zero past d).
@@ -205,9 +211,9 @@ struct bsl_stack {
 
 namespace {
 
-// signs + tiled U + tiled V + row-major V + B-ordered V (see BlockPtrs)
+// signs + tiled U + tiled V + row-major V + B-ordered V + row-major U (see BlockPtrs)
 size_t slot_bytes(int64_t m, int64_t d) {
-  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 3 * (size_t)pad_cols(d) * kRank * 2;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + 2 * (size_t)pad_rows(m) * kRank * 2 + 3 * (size_t)pad_cols(d) * kRank * 2;
 }
 
 BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
@@ -221,6 +227,7 @@ BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
   p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
   p.vr = reinterpret_cast<const uint16_t*>(base + sb + ub + vb);
   p.vb = reinterpret_cast<const uint16_t*>(base + sb + ub + 2 * vb);
+  p.ur = reinterpret_cast<const uint16_t*>(base + sb + ub + 3 * vb);
   return p;
 }
 
@@ -241,7 +248,7 @@ int upload_table(Weight& W, int32_t lo, int32_t hi, hipStream_t st) {
   if (hi <= lo) return BSL_OK;
   std::vector<BlockPtrs> tab(hi - lo);
   for (int32_t i = lo; i < hi; ++i)
-    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr, nullptr};
+    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   hipError_t e = hipMemcpyAsync(W.dtable + lo, tab.data(), sizeof(BlockPtrs) * (hi - lo), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
@@ -492,7 +499,8 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     tile_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
     rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
     bop_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + 2 * vb));
-    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + ub + 3 * vb, hipMemcpyHostToDevice, st);
+    rowmajor_u(src.u, W.m, reinterpret_cast<uint16_t*>(buf + sb + ub + 3 * vb));
+    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + 2 * ub + 3 * vb, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);

@@ -35,12 +35,15 @@ inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * 
 //   vb:    [d_pad/512][16 planes][64 lanes][8] fp16, V in the single-token B-operand
 //          order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] (j < 4)
 //          and V[512 c + 32 b + 16 + 4 kk + j - 4][r] (4 <= j < 8)
+//   ur:    [m_pad][16] fp16, U row-major (zero past m): the rebuild MFMA's B operand, 8
+//          consecutive ranks of one row per 16-byte load
 struct BlockPtrs {
   const uint8_t* signs;
   const uint16_t* u;
   const uint16_t* v;
   const uint16_t* vr;
   const uint16_t* vb;
+  const uint16_t* ur;
 };
 
 // One weight of a (grouped) forward launch; passed by value in the kernel arguments.

@@ -134,6 +134,7 @@ __device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
   r.v = uniform_ptr(b.v);
   r.vr = uniform_ptr(b.vr);
   r.vb = uniform_ptr(b.vb);
+  r.ur = uniform_ptr(b.ur);
   return r;
 }
 
@@ -147,6 +148,7 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.v = t->v;
   b.vr = t->vr;
   b.vb = t->vb;
+  b.ur = t->ur;
   return b;
 }
 
@@ -1047,7 +1049,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
   const int row = row0 + jl;
   const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
-  const uint32_t uoff = (((uint32_t)(row >> 4) * 64u + 16u * ((row >> 2) & 3) + 8u * h) * 4u + (row & 3)) * 2u;
+  const uint32_t uoff = (uint32_t)row * (kRank * 2) + 16u * h;  // U[row][8 h ..] in the row-major copy
   const uint32_t chunk_sign_bytes = (uint32_t)W.mt * kTileBytes;  // (a block's signs are < 2 GiB here)
 
   uint32_t vmask = 0x80008000u;
@@ -1066,11 +1068,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + th * BPW + i : b0);
       sbase[i] = bp.signs;
       vbase[i] = bp.vr;
-      // U[row][8 h + e] from the tiled copy: tile row / 16, lane 16 ((row / 4) % 4) + 8 h + e, slot row % 4
-      const rsrc_t ures = make_rsrc(bp.u);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        uf[i][e] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(ures, i < nbw ? uoff + 8u * e : kBufOutOfRange, 0, 0));
+      // U[row][8 h .. 8 h + 7] from the row-major copy (zeros for the repeated slots)
+      uf[i] = as_half8(buf_load16(make_rsrc(bp.ur), i < nbw ? uoff : kBufOutOfRange));
     }
     // sign words sw[i][g2][q] of the current chunk (quads 0-1 and 2-3 refilled separately)
     uint32_t sw[BPW][2][4];
@@ -1327,7 +1326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
   const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
   const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
   const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
-  const uint32_t uoff = (((uint32_t)(row >> 4) * 64u + 16u * ((row >> 2) & 3) + 8u * h) * 4u + (row & 3)) * 2u;
+  const uint32_t uoff = (uint32_t)row * (kRank * 2) + 16u * h;  // U[row][8 h ..] in the row-major copy
   const uint32_t cb_sign = __builtin_amdgcn_readfirstlane((uint32_t)c * (uint32_t)W.mt * kTileBytes);
   uint32_t vmask = 0x80008000u;
   asm volatile("" : "+v"(vmask));  // (a VGPR operand, so that AND and OR fuse into v_and_or_b32)
@@ -1340,10 +1339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
 
   for (int i = 0; i < nb; ++i) {
     const BlockPtrs bp = load_block(W.blocks, i);
-    half8 uf;
-    const rsrc_t ures = make_rsrc(bp.u);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) uf[e] = __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(ures, uoff + 8u * e, 0, 0));
+    const half8 uf = as_half8(buf_load16(make_rsrc(bp.ur), uoff));  // U[row][8 h .. 8 h + 7]
     // sign words q = 2 half, 2 half + 1 of the lane's two stored groups (g2)
     uint32_t sw[2][2];
     const rsrc_t sres = make_rsrc(bp.signs);

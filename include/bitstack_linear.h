@@ -143,7 +143,8 @@ int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
 /* Device bytes currently held by loaded blocks (what budget_bytes caps).  A loaded block
  * occupies its padded tiled signs and factors plus two more copies of V in the orders
  * the tile-reconstruct kernel and the wave-private single-token kernel read (32 bytes
- * per padded column each). */
+ * per padded column each) and a row-major copy of U for the rebuild (32 bytes per padded
+ * row). */
 uint64_t bsl_resident_bytes(const bsl_stack* s);
 
 /* y = x W_hat_n^T for weight w with its n loaded blocks.

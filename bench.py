@@ -599,7 +599,7 @@ def main() -> None:
             lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M)
             w_, k_, b_, f_ = time_steps(torch, lay, 50, 5)
             sweep.append({"M": M, "n_w": [int(c) for c in counts], "GB/s": round(b_ / w_ / 1e9, 1),
-                          "path": "single-token" if M == 1 else ("tile" if M >= 8 else "factored"),
+                          "path": "single-token" if M == 1 else ("tile" if M >= 5 else "few-token"),
                           "sz_equivalent_tflops": round(f_ / w_ / 1e12, 1), "us_per_step": round(w_ * 1e6 / 50, 1)})
             lay.close()
             del lay

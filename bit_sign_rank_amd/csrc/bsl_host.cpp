@@ -354,11 +354,12 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     else if ((e = hipMemset(W.dtable, 0, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMemset(table)");
   }
   if (rc == BSL_OK) {
-    // single-token pieces: at most (row groups of one launch) + (workgroups) of them
-    const size_t n = ((size_t)kMaxGroup * max_groups + (size_t)s->decode_grid_max) * kDecodeGroupRows;
-    // (counters per 256-row group: the wave-private kernel's row groups are a quarter of
-    // decode_m1_kernel's)
-    const size_t na = (size_t)kMaxGroup * max_groups * (kDecodeGroupRows / kWpRows);
+    // single- and few-token pieces: at most (row groups of one launch) + (workers) of them,
+    // 1024 floats a piece for decode_m1_kernel, 256 a piece for the wave-private kernel,
+    // whose row groups take 256 / T rows for T tokens
+    const size_t n = ((size_t)kMaxGroup * max_groups * kWpMaxTokens + (size_t)s->decode_grid_max) * kDecodeGroupRows;
+    // (arrival counters per row group: the wave-private kernel's are the smallest)
+    const size_t na = (size_t)kMaxGroup * max_groups * (kDecodeGroupRows / kWpRows) * kWpMaxTokens;
     if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
     else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
     else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
@@ -723,25 +724,6 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   if (s->path == BSL_PATH_DENSE && M > 1) return forward_dense(s, count, weights, x, y, M, y_is_fp32, stream);
   const bool tile = s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens);
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
-  const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
-  const int token_groups = (M + nt - 1) / nt;
-  // Multi-token items are cut along their (block, chunk) sequence when there are too few
-  // of them: aim at about two equal items per CU, within the split-K workspace.
-  uint64_t split_target = 1;
-  int max_splits = 1;
-  if (M > 1) {
-    uint64_t work = 0;
-    for (int32_t j = 0; j < count; ++j) {
-      const int32_t w = weights[j];
-      if (w < 0 || w >= (int32_t)s->w.size()) break;  // rejected below
-      const Weight& W = s->w[w];
-      work += (uint64_t)prefill_groups(W) * token_groups * W.n * W.nch;
-    }
-    const uint64_t slots = 2 * (uint64_t)s->decode_grid_max;
-    split_target = std::max<uint64_t>(1, (work + slots - 1) / slots);
-    max_splits = std::max(1, std::min(kMaxSplits, kSplitTokens / (token_groups * nt)));
-  }
-  uint64_t items = 0, units = 0, groups = 0;
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -761,85 +743,121 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     D.mt = W.mt;
     D.nch = W.nch;
     D.nblocks = W.n;
-    D.item_begin = (int32_t)items;
-    if (M > 1) {
-      const uint64_t wunits = (uint64_t)W.n * W.nch;
-      const uint64_t wgroups = (uint64_t)prefill_groups(W) * token_groups;
-      const uint64_t splits = std::min<uint64_t>(max_splits, std::max<uint64_t>(1, (wunits + split_target - 1) / split_target));
-      if (items + wgroups * splits > (uint64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
-      D.groups = (int32_t)wgroups;
-      D.splits = (int32_t)splits;
-      items += wgroups * splits;
-    }
   }
-  args.total_items = (int32_t)items;
   DeviceGuard guard(s->device);
   int e = 0;
-  if (M == 1) {
-    // Unit lists of both single-token kernels: (weight, row group, block, chunk) with row
-    // groups of `rows` rows.
-    auto plan_units = [&](int rows) {
-      units = groups = 0;
-      for (int32_t j = 0; j < count; ++j) {
-        const Weight& W = s->w[weights[j]];
-        WeightDesc& D = args.w[j];
-        D.groups = (int32_t)((W.mt * kTileRows + rows - 1) / rows);
-        D.splits = W.nch;
-        const uint64_t wu = (uint64_t)D.groups * W.nch * W.n;
-        D.unit_begin = (uint32_t)units;
-        D.units = (uint32_t)wu;
-        D.rg_begin = (uint32_t)groups;
-        units += wu;
-        groups += D.groups;
-      }
-    };
-    // Units [o U / 2^lg, (o + 1) U / 2^lg) of worker o, as the kernels compute them.
-    auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
-    // AUTO takes the shared-operand kernel: on the 8B-shaped layer it measured faster
-    // (77 against 80 us per launch)
-    bool wp = s->decode == BSL_DECODE_PRIVATE;
-    int lg = 0;
-    if (wp) {
-      plan_units(kWpRows);
-      // workers: four per workgroup, at most one workgroup per CU, at most one per unit
-      int32_t workers = kWpWaves * s->decode_grid_max;
-      while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
-      while ((1 << lg) < workers) ++lg;
-      // (no units at all: one workgroup writes y = 0)
-      bool fits = (units == 0 || units >= (uint64_t)workers) && (units << lg) < (1ull << 32);
-      // every workgroup keeps the activations of the weights its units belong to in LDS
-      for (int32_t L = 0; fits && units > 0 && L < workers / kWpWaves; ++L) {
-        const uint64_t a = start((uint64_t)L * kWpWaves, lg), b = start((uint64_t)(L + 1) * kWpWaves, lg) - 1;
-        int32_t ja = 0, jb = 0;
-        while (ja + 1 < count && a >= args.w[ja + 1].unit_begin) ++ja;
-        while (jb + 1 < count && b >= args.w[jb + 1].unit_begin) ++jb;
-        uint64_t bytes = 0;
-        for (int32_t j = ja; j <= jb; ++j) bytes += (uint64_t)args.w[j].nch * kChunkCols * 2;
-        fits = bytes <= (uint64_t)kWpXBytes;
-      }
-      if (!fits) return fail(BSL_EUNSUPPORTED, "forward: the wave-private single-token kernel does not fit this launch");
+  uint64_t units = 0, groups = 0;
+  // Unit lists of the single- and few-token kernels: (weight, row group, block, chunk)
+  // with row groups of `rows` rows.
+  auto plan_units = [&](int rows) {
+    units = groups = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const Weight& W = s->w[weights[j]];
+      WeightDesc& D = args.w[j];
+      D.groups = (int32_t)((W.mt * kTileRows + rows - 1) / rows);
+      D.splits = W.nch;
+      const uint64_t wu = (uint64_t)D.groups * W.nch * W.n;
+      D.unit_begin = (uint32_t)units;
+      D.units = (uint32_t)wu;
+      D.rg_begin = (uint32_t)groups;
+      units += wu;
+      groups += D.groups;
     }
-    if (!wp) {
-      plan_units(kDecodeGroupRows);
-      // Persistent grid: the largest power of two that is no more than one workgroup per
-      // CU and no more than the number of units (so no workgroup's share is empty).
-      int32_t grid = s->decode_grid_max;
-      lg = 0;
-      while (grid > 1 && (uint64_t)grid > units) grid /= 2;
-      while ((1 << lg) < grid) ++lg;
-      if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+  };
+  // Units [o U / 2^lg, (o + 1) U / 2^lg) of worker o, as the kernels compute them.
+  auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
+  // Plan of the wave-private kernel for T tokens (row groups of 256 / T rows); false when
+  // a workgroup's activations do not fit its LDS.
+  auto plan_private = [&](int T, int& lg) {
+    plan_units(kWpRows / T);
+    // workers: four per workgroup, at most one workgroup per CU, at most one per unit
+    int32_t workers = kWpWaves * s->decode_grid_max;
+    while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
+    lg = 0;
+    while ((1 << lg) < workers) ++lg;
+    // (no units at all: one workgroup writes y = 0)
+    bool fits = (units == 0 || units >= (uint64_t)workers) && (units << lg) < (1ull << 32);
+    // every workgroup keeps the activations of the weights its units belong to in LDS
+    for (int32_t L = 0; fits && units > 0 && L < workers / kWpWaves; ++L) {
+      const uint64_t a = start((uint64_t)L * kWpWaves, lg), b = start((uint64_t)(L + 1) * kWpWaves, lg) - 1;
+      int32_t ja = 0, jb = 0;
+      while (ja + 1 < count && a >= args.w[ja + 1].unit_begin) ++ja;
+      while (jb + 1 < count && b >= args.w[jb + 1].unit_begin) ++jb;
+      uint64_t bytes = 0;
+      for (int32_t j = ja; j <= jb; ++j) bytes += (uint64_t)T * args.w[j].nch * kChunkCols * 2;
+      fits = bytes <= (uint64_t)kWpXBytes;
     }
+    return fits;
+  };
+  auto launch_units = [&](int lg) {
     args.total_units = (uint32_t)units;
     args.total_groups = (uint32_t)groups;
     args.grid_log2 = lg;
     args.zero_page = s->zero_page;
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
-    e = wp ? launch_decode_wp(args, stream) : launch_decode_m1(args, stream);
-  } else {
-    args.zero_page = s->zero_page;
-    e = launch_prefill(args, nt, token_groups, stream);
+  };
+  if (M == 1) {
+    // AUTO takes the shared-operand kernel: on the 8B-shaped layer it measured faster
+    // (77 against 80 us per launch)
+    const bool wp = s->decode == BSL_DECODE_PRIVATE;
+    int lg = 0;
+    if (wp) {
+      if (!plan_private(1, lg)) return fail(BSL_EUNSUPPORTED, "forward: the wave-private single-token kernel does not fit this launch");
+    } else {
+      plan_units(kDecodeGroupRows);
+      // Persistent grid: the largest power of two that is no more than one workgroup per
+      // CU and no more than the number of units (so no workgroup's share is empty).
+      int32_t grid = s->decode_grid_max;
+      while (grid > 1 && (uint64_t)grid > units) grid /= 2;
+      while ((1 << lg) < grid) ++lg;
+      if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+    }
+    launch_units(lg);
+    e = wp ? launch_decode_wp(args, 1, stream) : launch_decode_m1(args, stream);
+    if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+    return BSL_OK;
   }
+  if (M <= kWpMaxTokens && s->path == BSL_PATH_AUTO) {
+    // a few tokens: the wave-private kernel with every operand but the activations shared
+    // by the tokens (3 tokens run as 4, the fourth on zeros), when they fit its LDS
+    const int T = M <= 2 ? 2 : 4;
+    int lg = 0;
+    if (plan_private(T, lg)) {
+      launch_units(lg);
+      e = launch_decode_wp(args, T, stream);
+      if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+      return BSL_OK;
+    }
+  }
+  const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
+  const int token_groups = (M + nt - 1) / nt;
+  // Multi-token items are cut along their (block, chunk) sequence when there are too few
+  // of them: aim at about two equal items per CU, within the split-K workspace.
+  uint64_t work = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const Weight& W = s->w[weights[j]];
+    work += (uint64_t)prefill_groups(W) * token_groups * W.n * W.nch;
+  }
+  const uint64_t slots = 2 * (uint64_t)s->decode_grid_max;
+  const uint64_t split_target = std::max<uint64_t>(1, (work + slots - 1) / slots);
+  const int max_splits = std::max(1, std::min(kMaxSplits, kSplitTokens / (token_groups * nt)));
+  uint64_t items = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const Weight& W = s->w[weights[j]];
+    WeightDesc& D = args.w[j];
+    D.item_begin = (int32_t)items;
+    const uint64_t wunits = (uint64_t)W.n * W.nch;
+    const uint64_t wgroups = (uint64_t)prefill_groups(W) * token_groups;
+    const uint64_t splits = std::min<uint64_t>(max_splits, std::max<uint64_t>(1, (wunits + split_target - 1) / split_target));
+    if (items + wgroups * splits > (uint64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
+    D.groups = (int32_t)wgroups;
+    D.splits = (int32_t)splits;
+    items += wgroups * splits;
+  }
+  args.total_items = (int32_t)items;
+  args.zero_page = s->zero_page;
+  e = launch_prefill(args, nt, token_groups, stream);
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
 }

@@ -76,13 +76,13 @@ struct GroupArgs {
   uint32_t total_groups; // single-token path: row groups over all weights
   int32_t grid_log2;     // single-token path: log2 of the (power-of-two) grid
   const void* zero_page; // kZeroPageBytes of zeros: target of prefetches past the end of the work
-  float* pieces;         // single-token path: [total_groups + grid][512] partial sums (workspace)
+  float* pieces;         // single-/few-token path: [total_groups + workers][piece] partial sums (workspace)
   uint32_t* arrivals;    // single-token path: [total_groups] counters, zero between launches (workspace)
 };
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
-int launch_decode_wp(const GroupArgs& args, void* stream);
+int launch_decode_wp(const GroupArgs& args, int tokens, void* stream);  // tokens: 1, 2 or 4
 // Dense path: W_hat of each weight into WeightDesc::y (fp16, [m][d_pad]); items are
 // (128-row group, half chunk) pairs.
 int launch_restore(const GroupArgs& args, void* stream);
@@ -104,10 +104,13 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 // Single-token path, wave-private kernel: one worker per wave, four waves per workgroup
 // (one per SIMD), one workgroup per CU; units of 16 row tiles (256 rows).  A workgroup
 // keeps the activations of the weights its units belong to in LDS (at most kWpXBytes).
+// The same kernel takes T = 2 or 4 tokens with units of 16 / T row tiles, so that a
+// piece (rows x tokens) stays kWpRows floats.
 constexpr int kWpTiles = 16;
 constexpr int kWpRows = kWpTiles * 16;
 constexpr int kWpWaves = 4;
-constexpr int kWpXBytes = 128 * 1024;
+constexpr int kWpXBytes = 148 * 1024;
+constexpr int kWpMaxTokens = 4;
 // Multi-token path (M >= 2): one 8-wave workgroup per item = (512-row group, token
 // group of 2, 4 or 8 tokens, range of the (block, chunk) sequence).  A weight's items are
 // split along that sequence only while splits x padded tokens fit the workspace.
@@ -120,7 +123,7 @@ constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-su
 constexpr int kTileGroupRows = 64;
 constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
-constexpr int kTileAutoMinTokens = 8;   // BSL_PATH_AUTO takes the tile path from this M on
+constexpr int kTileAutoMinTokens = 5;   // BSL_PATH_AUTO takes the tile path from this M on
 // Tile-path items may be cut along the columns (chunk ranges) when a launch has too few
 // of them to fill the chip; the ranges' partial sums go to a workspace of the stack.
 constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB

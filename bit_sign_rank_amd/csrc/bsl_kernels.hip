@@ -1438,9 +1438,13 @@ __device__ __forceinline__ u32x8 pm_v_operand(const u32x4& v) {
 // s_waitcnt immediate for "at most n vector memory operations outstanding" (n < 64).
 __host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
+// R row tiles per wave and T tokens (R T = 16: the accumulators of a 16-tile wave): the
+// tokens share every B operand, sign index and load; each has its own A operand (its
+// activations), accumulators and pieces.  Tokens past args.M are zeros and not stored.
+template <int R, int T>
 __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wp_kernel(GroupArgs args) {
-  constexpr int R = kWpTiles;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kWpXBytes / 2];  // activations (d_pad per weight)
+  constexpr int ROWS = 16 * R;  // rows per unit
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kWpXBytes / 2];  // activations ([T][d_pad] per weight)
   __shared__ uint64_t bbase[kMaxGroup][kMaxBlocks];                     // block base addresses
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1457,7 +1461,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
   if (L == 0) {  // weights without blocks: y = 0, the empty sum
     for (int j = 0; j < args.count; ++j)
       if (args.w[j].units == 0)
-        for (int row = threadIdx.x; row < args.w[j].m; row += kWpWaves * 64) store_y(args.w[j].y, row, 0.f, args.y_fp32);
+        for (int e = threadIdx.x; e < args.w[j].m * args.M; e += kWpWaves * 64) store_y(args.w[j].y, e, 0.f, args.y_fp32);
   }
   if (U == 0) return;  // (uniform over the grid)
 
@@ -1475,7 +1479,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     int32_t j, rg, i, ch;
     uint32_t u;
     bool valid;
-    int32_t nb, nch, groups, mt, xo;  // xo: LDS offset (elements) of weight j's activations
+    int32_t nb, nch, groups, mt, xo;  // xo: LDS offset (elements) of weight j's activations ([T][d_pad])
     uint32_t rg_begin;
   };
   auto load_weight = [&](Cur& c) {
@@ -1486,7 +1490,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     c.mt = W.mt;
     c.rg_begin = W.rg_begin;
     int xo = 0;
-    for (int k = j0; k < c.j; ++k) xo += args.w[k].nch * kChunkCols;
+    for (int k = j0; k < c.j; ++k) xo += T * args.w[k].nch * kChunkCols;
     c.xo = xo;
   };
   auto locate = [&](uint32_t u) {
@@ -1557,12 +1561,14 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
     for (int t = 0; t < R; ++t) uw[t] = load8(u + (t * 64 + lane) * 8);
   };
-  // LDS address of a unit's activations for this lane (plane 0); plane b is 64 b bytes on
+  // LDS address of a unit's activations of token 0 for this lane (plane 0); plane b is 64 b
+  // bytes on, token t is d_pad elements on
   auto a_base = [&](const Cur& c) {
     const int off = (c.valid ? c.xo + c.ch * kChunkCols : 0) + 8 * g;
     return reinterpret_cast<const u32x4*>(&xs[off]);
   };
-  auto read_a = [&](const u32x4* base, int b) { return base[4 * b]; };
+  auto a_stride = [&](const Cur& c) { return c.valid ? c.nch * kChunkCols / 8 : 0; };  // (in 16-byte units)
+  auto read_a = [&](const u32x4* base, int stride, int t, int b) { return base[t * stride + 4 * b]; };
 
   // ---- prologue: the first unit's signs and V, then the block table and the
   // activations into LDS (the waits for those also cover the first unit's loads, which
@@ -1587,57 +1593,66 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     int off = 0;
     for (int j = j0; j <= j1; ++j) {
       const int d = args.w[j].d, dp = args.w[j].nch * kChunkCols;
-      const uint16_t* x = args.w[j].x;
-      for (int c0s = threadIdx.x * 8; c0s < dp; c0s += 8 * kWpWaves * 64 * 8) {
-        u32x4 v[8];
+      for (int t = 0; t < T; ++t) {
+        const uint16_t* x = args.w[j].x + (size_t)t * d;
+        const bool real = t < args.M;
+        for (int c0s = threadIdx.x * 8; c0s < dp; c0s += 8 * kWpWaves * 64 * 8) {
+          u32x4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int c = c0s + k * 8 * kWpWaves * 64;
-          v[k] = c < d ? load16(x + c) : (u32x4){0u, 0u, 0u, 0u};
-        }
+          for (int k = 0; k < 8; ++k) {
+            const int c = c0s + k * 8 * kWpWaves * 64;
+            v[k] = real && c < d ? load16(x + c) : (u32x4){0u, 0u, 0u, 0u};
+          }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int c = c0s + k * 8 * kWpWaves * 64;
-          if (c < dp) *reinterpret_cast<u32x4*>(&xs[off + c]) = v[k];
+          for (int k = 0; k < 8; ++k) {
+            const int c = c0s + k * 8 * kWpWaves * 64;
+            if (c < dp) *reinterpret_cast<u32x4*>(&xs[off + c]) = v[k];
+          }
         }
+        off += dp;
       }
-      off += dp;
     }
   }
   __syncthreads();
 
   // acc: P of the current block; accy: its U-weighted, r-summed rows over the blocks done
   // (one row per lane and tile, see reduce_columns)
-  float4v acc[R];
-  float accy[R];
+  float4v acc[T][R];
+  float accy[T][R];
 #pragma unroll
-  for (int t = 0; t < R; ++t) {
-    acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-    accy[t] = 0.f;
-  }
+  for (int q = 0; q < T; ++q)
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      acc[q][t] = (float4v){0.f, 0.f, 0.f, 0.f};
+      accy[q][t] = 0.f;
+    }
   uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
   asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs: one v_and_or_b32 each)
   uint32_t ix_odd[R], ix_even[R];
-  u32x4 av[2];
+  u32x4 av[2][T];
   u32x8 bw[2];
   // plane 0 of the first unit
 #pragma unroll
   for (int t = 0; t < R; ++t) ix_odd[t] = sign_index_v(sgn[0][t][0], m_odd, false);
   const u32x4* abase = a_base(c0);
-  av[0] = read_a(abase, 0);
+  int astride = a_stride(c0);
+#pragma unroll
+  for (int q = 0; q < T; ++q) av[0][q] = read_a(abase, astride, q, 0);
   bw[0] = pm_v_operand<false>(vsl[0]);
   vsl[0] = load_v(p1, 0);
 
   const int rsel = reduced_row(lane);
   auto store_piece = [&](const Cur& c) {
     const uint32_t item = c.rg_begin + c.rg;
-    float* piece = args.pieces + (size_t)(item + worker) * kWpRows;
+    float* piece = args.pieces + (size_t)(item + worker) * (ROWS * T);  // [T][ROWS]
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      if ((lane & 3) == 0)
-        __hip_atomic_store(&piece[t * kTileRows + rsel], accy[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      accy[t] = 0.f;
-    }
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+      for (int t = 0; t < R; ++t) {
+        if ((lane & 3) == 0)
+          __hip_atomic_store(&piece[q * ROWS + t * kTileRows + rsel], accy[q][t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        accy[q][t] = 0.f;
+      }
   };
 
   // ---- one unit: c0 with signs in `cur`; on entry plane 0's operands are ready, V of
@@ -1650,6 +1665,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     const Cur c3 = next(c2);
     const WpPtrs p3 = unit_ptrs(c3);
     const u32x4* abase_next = a_base(c1);
+    const int astride_next = a_stride(c1);
 #define BSL_WP_PLANE(B)                                                                                        \
   __builtin_amdgcn_sched_barrier(0);                                                                           \
   {                                                                                                            \
@@ -1661,21 +1677,22 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
       if (NB % 4 == 2) {                                                                                       \
         _Pragma("unroll") for (int t = 0; t < R; ++t) ix_even[t] = sign_index_v(cur[t][NB / 4], m_even, true); \
       }                                                                                                        \
-      av[NB % 2] = read_a(abase, NB);                                                                          \
+      _Pragma("unroll") for (int q = 0; q < T; ++q) av[NB % 2][q] = read_a(abase, astride, q, NB);              \
       bw[NB % 2] = plane_even(NB) ? pm_v_operand<true>(vsl[NB]) : pm_v_operand<false>(vsl[NB]);             \
       vsl[NB] = load_v(p1, NB);                                                                                \
     } else {                                                                                                   \
       _Pragma("unroll") for (int t = 0; t < R; ++t) ix_odd[t] = sign_index_v(nxt[t][0], m_odd, false);        \
-      av[0] = read_a(abase_next, 0);                                                                           \
+      _Pragma("unroll") for (int q = 0; q < T; ++q) av[0][q] = read_a(abase_next, astride_next, q, 0);           \
       bw[0] = pm_v_operand<false>(vsl[0]);                                                                     \
       vsl[0] = load_v(p2, 0);                                                                                  \
     }                                                                                                          \
-    _Pragma("unroll") for (int t = 0; t < R; ++t) acc[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(           \
-        __builtin_bit_cast(half8, av[(B) % 2]), __builtin_bit_cast(half16, bw[(B) % 2]), acc[t],              \
+    _Pragma("unroll") for (int t = 0; t < R; ++t) _Pragma("unroll") for (int q = 0; q < T; ++q)              \
+      acc[q][t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(                                                    \
+        __builtin_bit_cast(half8, av[(B) % 2][q]), __builtin_bit_cast(half16, bw[(B) % 2]), acc[q][t],        \
         (int)(plane_even(B) ? ix_even[t] : ix_odd[t]), 0, plane_half(B));                                      \
     /* one MFMA, then up to two VALU operations: the preparation of the next plane runs */                    \
     /* in the matrix core's shadow instead of between bursts of MFMAs */                                      \
-    _Pragma("unroll") for (int t = 0; t < R; ++t) {                                                            \
+    _Pragma("unroll") for (int t = 0; t < R * T; ++t) {                                                        \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                                       \
       __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);                                                       \
     }                                                                                                          \
@@ -1689,13 +1706,16 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
       for (int t = 0; t < R; ++t) {
         const half2v u01 = as_half2(uw[t][0]), u23 = as_half2(uw[t][1]);
-        float4v w;
-        w[0] = (float)u01[0] * acc[t][0];
-        w[1] = (float)u01[1] * acc[t][1];
-        w[2] = (float)u23[0] * acc[t][2];
-        w[3] = (float)u23[1] * acc[t][3];
-        accy[t] += reduce_columns(w, lane);
-        acc[t] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < T; ++q) {
+          float4v w;
+          w[0] = (float)u01[0] * acc[q][t][0];
+          w[1] = (float)u01[1] * acc[q][t][1];
+          w[2] = (float)u23[0] * acc[q][t][2];
+          w[3] = (float)u23[1] * acc[q][t][3];
+          accy[q][t] += reduce_columns(w, lane);
+          acc[q][t] = (float4v){0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
     if (group_end(c0)) store_piece(c0);
@@ -1706,6 +1726,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     p1 = p2;
     p2 = p3;
     abase = abase_next;
+    astride = astride_next;
   };
 
   const uint32_t item_first = c0.rg_begin + c0.rg;
@@ -1749,21 +1770,20 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     if (seen != o1 - o0 + 1) continue;
     if (lane == 0) __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const WeightDesc& Wd = args.w[j];
-#pragma unroll
-    for (int q = 0; q < kWpRows / 64; ++q) {
-      const int rr = q * 64 + lane;
-      const float* base = args.pieces + (size_t)item * kWpRows + rr;
+    for (int e = lane; e < ROWS * T; e += 64) {  // e = token * ROWS + row in the group
+      const int tok = e / ROWS, rr = e % ROWS;
+      const float* base = args.pieces + (size_t)item * (ROWS * T) + e;
       float acc_y = 0.f;
       for (uint32_t o = o0; o <= o1; o += 16) {  // (16 loads in flight per round trip)
         float v[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k)
-          v[k] = __hip_atomic_load(base + (size_t)min(o + k, o1) * kWpRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[k] = __hip_atomic_load(base + (size_t)min(o + k, o1) * (ROWS * T), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc_y += o + k <= o1 ? v[k] : 0.f;
       }
-      const int row = (int)(item - Wd.rg_begin) * kWpRows + rr;
-      if (row < Wd.m) store_y(Wd.y, row, acc_y, args.y_fp32);
+      const int row = (int)(item - Wd.rg_begin) * ROWS + rr;
+      if (row < Wd.m && tok < args.M) store_y(Wd.y, (size_t)tok * Wd.m + row, acc_y, args.y_fp32);
     }
   }
 }
@@ -1828,9 +1848,15 @@ int launch_decode_m1(const GroupArgs& args, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_decode_wp(const GroupArgs& args, void* stream) {
+int launch_decode_wp(const GroupArgs& args, int tokens, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(decode_wp_kernel, dim3((1u << args.grid_log2) / kWpWaves), dim3(kWpWaves * 64), 0, st, args);
+  const dim3 grid((1u << args.grid_log2) / kWpWaves), block(kWpWaves * 64);
+  switch (tokens) {
+    case 1: hipLaunchKernelGGL((decode_wp_kernel<16, 1>), grid, block, 0, st, args); break;
+    case 2: hipLaunchKernelGGL((decode_wp_kernel<8, 2>), grid, block, 0, st, args); break;
+    case 4: hipLaunchKernelGGL((decode_wp_kernel<4, 4>), grid, block, 0, st, args); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 

@@ -177,7 +177,11 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *     allocates the workspace (the eight largest weights' W_hat) and a rocBLAS handle
  *     (BSL_ENOMEM if that fails; the path is then unchanged).  M = 1 keeps the
  *     single-token kernel.
- *   BSL_PATH_AUTO (the default): FACTORED for M below 8, TILE from M = 8 on. */
+ *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 to 4 on the
+ *     wave-private kernel of BSL_DECODE_PRIVATE taking T = 2 or 4 tokens at once (3 runs
+ *     as 4, the fourth on zeros), whose tokens share every sign, U and V operand and load,
+ *     when the T tokens' activations fit its LDS (148 KiB per workgroup), else the
+ *     factored multi-token kernel; TILE from M = 5 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2
@@ -190,7 +194,7 @@ int bsl_set_path(bsl_stack* s, int32_t path);
  *     through LDS, one barrier per unit.
  *   BSL_DECODE_PRIVATE: every wave builds its own B operands (+-V) and carries x in the
  *     sparse MFMA's A operand, so the products V x are exact and no barrier is needed.
- *     A workgroup keeps the activations of the weights it works on in LDS (128 KiB);
+ *     A workgroup keeps the activations of the weights it works on in LDS (148 KiB);
  *     a launch that does not fit fails with BSL_EUNSUPPORTED.
  *   BSL_DECODE_AUTO (the default): SHARED, the faster of the two on this hardware. */
 #define BSL_DECODE_AUTO 0

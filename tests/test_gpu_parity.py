@@ -355,6 +355,86 @@ def test_private_decode_fits_the_layer_shapes(layer):
         assert rel_err(ys[j][:, rows], oracle.forward_rows(xs[j], blocks, rows, 2)) <= REL_TOL
 
 
+# ---------------------------------------------------------------- a few tokens (wave-private kernel)
+# Under BSL_PATH_AUTO, 2 to 4 tokens run on the wave-private kernel with every operand but
+# the activations shared by the tokens (3 tokens as 4, the fourth on zeros) whenever the
+# activations fit its LDS, else on the factored multi-token kernel.
+@pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1),
+                                   (3000, 1544, 5)])
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_integer_few_tokens_bit_exact(m, d, n, M):
+    blocks = integer_blocks(m, d, n)
+    x = synth.integer_activations(4, M, d)
+    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_AUTO) as st:
+        st.load([n])
+        y = st.forward(0, x)
+    assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_few_tokens_grouped_with_empty_weights_between(M):
+    shapes = [(512, 1024), (1024, 512), (300, 1536), (64, 2048), (2048, 1024)]
+    counts = [0, 3, 0, 2, 0]
+    ws = [(m, d, synth.synthetic_blocks(45, m, d, 3, 16, j)) for j, (m, d) in enumerate(shapes)]
+    xs = [synth.activations(45, M, d, j) for j, (_, d) in enumerate(shapes)]
+    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(counts)
+        for fp32 in (True, False):
+            ys = st.forward_group(list(range(len(shapes))), xs, fp32=fp32)
+            for j, (m, d, blocks) in enumerate(ws):
+                if counts[j] == 0:
+                    assert not ys[j].any()
+                else:
+                    assert rel_err(ys[j], oracle.forward(xs[j], blocks, counts[j])) <= REL_TOL
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_few_tokens_agree_with_the_factored_kernel(cfg1_blocks, M):
+    x = synth.activations(46, M, 1024)
+    outs = []
+    for path in (bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED):
+        with Stack([(1024, 1024, cfg1_blocks)], path=path) as st:
+            st.load([4])
+            outs.append(st.forward(0, x))
+    ref = oracle.forward(x, cfg1_blocks, 4)
+    for y in outs:
+        assert rel_err(y, ref) <= REL_TOL
+    assert rel_err(outs[0], outs[1]) <= 1e-3
+    # each token's row equals that token run alone (the tokens share no arithmetic)
+    with Stack([(1024, 1024, cfg1_blocks)]) as st:
+        st.load([4])
+        for t in range(M):
+            assert rel_err(st.forward(0, x[t:t + 1]), outs[0][t:t + 1]) <= 1e-3
+
+
+@pytest.mark.parametrize("M", [2, 4])
+def test_few_tokens_wide_input_falls_back(M):
+    """A weight whose activations for 4 tokens exceed the kernel's LDS (d = 20480: 160 KiB)
+    takes the factored kernel at 4 tokens and the wave-private one at 2; both are exact."""
+    m, d, n = 96, 20480, 2
+    blocks = integer_blocks(m, d, n)
+    x = synth.integer_activations(5, M, d)
+    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_AUTO) as st:
+        st.load([n])
+        y = st.forward(0, x)
+    assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [2, 3])
+def test_llama3_8b_layer_few_tokens_grouped(M):
+    shapes = synth.LLAMA3_8B_LAYER
+    counts = [8] * 7
+    weights = layer_blocks(shapes, counts, seed=47)
+    xs = [synth.activations(47, M, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(weights, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(7)), xs)
+        check_sampled(weights, counts, ys, xs)
+        again = st.forward_group(list(range(7)), xs)
+        assert all(np.array_equal(a, b) for a, b in zip(ys, again))
+
+
 # ---------------------------------------------------------------- input-channel scale
 @pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
 @pytest.mark.parametrize("M", [1, 4, 40])

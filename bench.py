@@ -410,6 +410,7 @@ def main() -> None:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-svd", action="store_true", help="skip the equal-size vanilla-SVD decode baseline")
+    ap.add_argument("--no-few", action="store_true", help="skip the few-token (M = 2, 4) decode runs")
     ap.add_argument("--decode", choices=["auto", "shared", "private"], default="auto",
                     help="single-token kernel of the headline (auto: the shared-operand kernel)")
     ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
@@ -523,6 +524,29 @@ def main() -> None:
     result["decode_other_kernel"] = other
 
     # ---------------- prefill M = 2048: tile path (the default for batches), then factored
+    # ---------------- a few tokens (batched decode): the wave-private kernel over T tokens
+    if not args.no_few:
+        few = []
+        for M in (2, 4):
+            row = {"M": M}
+            for name, path in (("auto", bsl.BSL_PATH_AUTO), ("factored", bsl.BSL_PATH_FACTORED)):
+                log(f"few tokens: 8B-shaped layer, n=8, M={M}, {name} path")
+                lay = Layers(bsl, torch, shapes, [[8] * 7] * 2, 2, args.seed + 5, M=M, path=path)
+                w_, k_, b_, _ = time_steps(torch, lay, 100, 10)
+                row[f"{name}_us_per_step"] = round(w_ * 1e6 / 100, 1)
+                row[f"{name}_kernel_us"] = round(float(np.mean(k_)) * 1e3, 1)
+                row[f"{name}_GB_per_s"] = round(b_ / w_ / 1e9, 1)
+                lay.close()
+                del lay
+                torch.cuda.empty_cache()
+            row["kernel"] = "decode_wp_kernel<8, 2>" if M == 2 else "decode_wp_kernel<4, 4>"
+            row["speedup_vs_factored"] = round(row["factored_us_per_step"] / row["auto_us_per_step"], 2)
+            few.append(row)
+            log(f"few tokens M={M}: {row}")
+        result["few_token_decode"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M tokens per grouped launch, 2 rotated layers",
+            "runs": few}
+
     if not args.no_prefill:
         log("prefill: one 8B-shaped layer, n=8, M=2048, tile path")
         pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_TILE)

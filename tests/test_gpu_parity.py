@@ -435,6 +435,22 @@ def test_llama3_8b_layer_few_tokens_grouped(M):
         assert all(np.array_equal(a, b) for a, b in zip(ys, again))
 
 
+@pytest.mark.slow
+@pytest.mark.parametrize("M", [2, 4])
+def test_llama2_70b_layer_few_tokens(M):
+    """The 70B-shaped layer in one grouped launch: 2 tokens fit the wave-private kernel;
+    at 4 the down projection's activations (4 x 28672 fp16) exceed its LDS, so the launch
+    takes the factored kernel.  Both are checked on sampled rows."""
+    shapes = synth.LLAMA2_70B_LAYER
+    counts = [2] * len(shapes)
+    ws = [(m, d, synth.synthetic_blocks(48, m, d, 2, 16, j)) for j, (_, m, d) in enumerate(shapes)]
+    xs = [synth.activations(48, M, d, j) for j, (_, _, d) in enumerate(shapes)]
+    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(counts)
+        ys = st.forward_group(list(range(len(shapes))), xs)
+    check_sampled(ws, counts, ys, xs, rows_per_weight=32, seed=48)
+
+
 # ---------------------------------------------------------------- input-channel scale
 @pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
 @pytest.mark.parametrize("M", [1, 4, 40])

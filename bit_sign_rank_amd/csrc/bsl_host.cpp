@@ -766,10 +766,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   };
   // Units [o U / 2^lg, (o + 1) U / 2^lg) of worker o, as the kernels compute them.
   auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
-  // Plan of the wave-private kernel for T tokens (row groups of 256 / T rows); false when
-  // a workgroup's activations do not fit its LDS.
+  // Plan of the wave-private kernel for T tokens (row groups of 256, 128, 64 and 64 rows
+  // for T = 1 to 4); false when a workgroup's activations do not fit its LDS.
   auto plan_private = [&](int T, int& lg) {
-    plan_units(kWpRows / T);
+    plan_units(T == 3 ? kWpRows / 4 : kWpRows / T);
     // workers: four per workgroup, at most one workgroup per CU, at most one per unit
     int32_t workers = kWpWaves * s->decode_grid_max;
     while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
@@ -820,8 +820,8 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   }
   if (M <= kWpMaxTokens && s->path == BSL_PATH_AUTO) {
     // a few tokens: the wave-private kernel with every operand but the activations shared
-    // by the tokens (3 tokens run as 4, the fourth on zeros), when they fit its LDS
-    const int T = M <= 2 ? 2 : 4;
+    // by the tokens, when they fit its LDS
+    const int T = M;
     int lg = 0;
     if (plan_private(T, lg)) {
       launch_units(lg);

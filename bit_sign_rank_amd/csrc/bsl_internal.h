@@ -82,7 +82,7 @@ struct GroupArgs {
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
 int launch_decode_m1(const GroupArgs& args, void* stream);
-int launch_decode_wp(const GroupArgs& args, int tokens, void* stream);  // tokens: 1, 2 or 4
+int launch_decode_wp(const GroupArgs& args, int tokens, void* stream);  // tokens: 1 to 4
 // Dense path: W_hat of each weight into WeightDesc::y (fp16, [m][d_pad]); items are
 // (128-row group, half chunk) pairs.
 int launch_restore(const GroupArgs& args, void* stream);
@@ -104,8 +104,8 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 // Single-token path, wave-private kernel: one worker per wave, four waves per workgroup
 // (one per SIMD), one workgroup per CU; units of 16 row tiles (256 rows).  A workgroup
 // keeps the activations of the weights its units belong to in LDS (at most kWpXBytes).
-// The same kernel takes T = 2 or 4 tokens with units of 16 / T row tiles, so that a
-// piece (rows x tokens) stays kWpRows floats.
+// The same kernel takes T = 2, 3 or 4 tokens with units of 8, 4 and 4 row tiles, so that
+// a piece (rows x tokens) holds at most kWpRows floats.
 constexpr int kWpTiles = 16;
 constexpr int kWpRows = kWpTiles * 16;
 constexpr int kWpWaves = 4;

@@ -1438,7 +1438,7 @@ __device__ __forceinline__ u32x8 pm_v_operand(const u32x4& v) {
 // s_waitcnt immediate for "at most n vector memory operations outstanding" (n < 64).
 __host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// R row tiles per wave and T tokens (R T = 16: the accumulators of a 16-tile wave): the
+// R row tiles per wave and T tokens (R T <= 16: the accumulators of a 16-tile wave): the
 // tokens share every B operand, sign index and load; each has its own A operand (its
 // activations), accumulators and pieces.  Tokens past args.M are zeros and not stored.
 template <int R, int T>
@@ -1854,6 +1854,7 @@ int launch_decode_wp(const GroupArgs& args, int tokens, void* stream) {
   switch (tokens) {
     case 1: hipLaunchKernelGGL((decode_wp_kernel<16, 1>), grid, block, 0, st, args); break;
     case 2: hipLaunchKernelGGL((decode_wp_kernel<8, 2>), grid, block, 0, st, args); break;
+    case 3: hipLaunchKernelGGL((decode_wp_kernel<4, 3>), grid, block, 0, st, args); break;
     case 4: hipLaunchKernelGGL((decode_wp_kernel<4, 4>), grid, block, 0, st, args); break;
     default: return (int)hipErrorInvalidValue;
   }

@@ -178,10 +178,9 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *     (BSL_ENOMEM if that fails; the path is then unchanged).  M = 1 keeps the
  *     single-token kernel.
  *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 to 4 on the
- *     wave-private kernel of BSL_DECODE_PRIVATE taking T = 2 or 4 tokens at once (3 runs
- *     as 4, the fourth on zeros), whose tokens share every sign, U and V operand and load,
- *     when the T tokens' activations fit its LDS (148 KiB per workgroup), else the
- *     factored multi-token kernel; TILE from M = 5 on. */
+ *     wave-private kernel of BSL_DECODE_PRIVATE taking the M tokens at once, which share
+ *     every sign, U and V operand and load, when their activations fit its LDS (148 KiB
+ *     per workgroup), else the factored multi-token kernel; TILE from M = 5 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2

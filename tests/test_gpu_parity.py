@@ -357,8 +357,8 @@ def test_private_decode_fits_the_layer_shapes(layer):
 
 # ---------------------------------------------------------------- a few tokens (wave-private kernel)
 # Under BSL_PATH_AUTO, 2 to 4 tokens run on the wave-private kernel with every operand but
-# the activations shared by the tokens (3 tokens as 4, the fourth on zeros) whenever the
-# activations fit its LDS, else on the factored multi-token kernel.
+# the activations shared by the tokens whenever the activations fit its LDS, else on the
+# factored multi-token kernel.
 @pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1),
                                    (3000, 1544, 5)])
 @pytest.mark.parametrize("M", [2, 3, 4])

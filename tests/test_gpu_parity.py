@@ -453,13 +453,16 @@ def test_llama2_70b_layer_few_tokens(M):
 
 # ---------------------------------------------------------------- input-channel scale
 @pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
-@pytest.mark.parametrize("M", [1, 4, 40])
-@pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
-def test_input_scale_folded_at_load(m, d, n, M, path):
+@pytest.mark.parametrize("M", [1, 3, 4, 40])
+@pytest.mark.parametrize("path,decode", [(p, None) for p in PATHS] + [(bsl.BSL_PATH_AUTO, bsl.BSL_DECODE_PRIVATE)],
+                         ids=PATH_IDS + ["auto-private"])
+def test_input_scale_folded_at_load(m, d, n, M, path, decode):
+    # (auto-private: the wave-private kernel at M = 1 and the few-token kernel at M = 3, 4,
+    # both reading the B-operand copy of the scaled V)
     blocks = synth.synthetic_blocks(23, m, d, n, 16, m, d)
     t = synth.inv_input_scale(23, d)
     x = synth.outlier_activations(23, M, d, synth.channel_magnitudes(23, d))
-    with Stack([(m, d, blocks)], path=path) as st:
+    with Stack([(m, d, blocks)], path=path, decode=decode) as st:
         bsl.bsl_set_input_scale(st.h, 0, t)
         st.load([n])
         y = st.forward(0, x)

@@ -1390,11 +1390,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void r
 
 // ============================================================ single-token kernel, wave-private operands
 // One worker per wave: four waves per workgroup (one per SIMD), one workgroup per CU.  The
-// work is the list of units (weight, 256-row group = 16 row tiles, block, 512-column chunk)
-// in that order; with U units and 2^lg workers, worker o walks units [o U / 2^lg,
-// (o + 1) U / 2^lg).  No operand is shared between waves, so the unit loop has no barrier.
+// work is the list of units (weight, row group of R row tiles, block, 512-column chunk) in
+// that order (R = 16 for one token, fewer when the wave carries several tokens, below);
+// with U units and 2^lg workers, worker o walks units [o U / 2^lg, (o + 1) U / 2^lg).  No
+// operand is shared between waves, so the unit loop has no barrier.
 //
-// Per unit a wave contracts its 16 row tiles with the chunk's 16 planes on
+// Per unit a wave contracts its R row tiles with the chunk's 16 planes on
 // v_smfmac_f32_16x16x64_f16 with A = the plane's activations and B = +-V:
 //  * B holds V of the plane's columns in both signs, in the odd or even group form of
 //    the plane (group G = columns 2G, 2G + 1: rows (V_a, V_b, -V_a, -V_b) or (V_a, -V_a,

@@ -151,8 +151,10 @@ uint64_t bsl_resident_bytes(const bsl_stack* s);
  *   x: device, fp16 [M][d] row-major, 16-byte aligned.
  *   y: device, [M][m] row-major, fp16 (y_is_fp32 == 0, round to nearest even) or fp32.
  *   M >= 1 tokens.  With n = 0 loaded blocks y is all zeros.
- * Only enqueues kernels on `stream` (no synchronisation, no allocation).  Two forwards
- * of the same weight must not run concurrently (they share its workspace). */
+ * Only enqueues kernels on `stream` (no synchronisation, no allocation).  Forwards on
+ * one stack must not run concurrently, even for different weights: they share the
+ * stack's workspaces (partial sums and arrival counters).  Forwards queued on one stream
+ * are ordered, so that is the simple way to issue them. */
 int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int32_t y_is_fp32, void* stream);
 
 /* Several weights in one kernel launch (count <= 8, distinct weights): weights[j] reads

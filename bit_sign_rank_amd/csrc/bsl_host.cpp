@@ -829,6 +829,32 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
       return BSL_OK;
     }
+    // The group does not fit as a whole: the weights whose activations take at most half
+    // of the LDS (so that any two neighbours fit together) go to one launch, which may
+    // still fall back, and the rest to the multi-token kernel.
+    int32_t narrow[kMaxGroup], wide[kMaxGroup];
+    const void* xn[kMaxGroup];
+    const void* xw[kMaxGroup];
+    void* yn[kMaxGroup];
+    void* yw[kMaxGroup];
+    int32_t nn = 0, nw = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const uint64_t bytes = (uint64_t)T * s->w[weights[j]].nch * kChunkCols * 2;
+      if (2 * bytes <= (uint64_t)kWpXBytes) {
+        narrow[nn] = weights[j];
+        xn[nn] = x[j];
+        yn[nn++] = y[j];
+      } else {
+        wide[nw] = weights[j];
+        xw[nw] = x[j];
+        yw[nw++] = y[j];
+      }
+    }
+    if (nn > 0 && nw > 0) {
+      const int rc = forward_impl(s, nn, narrow, xn, yn, M, y_is_fp32, stream);
+      if (rc != BSL_OK) return rc;
+      return forward_impl(s, nw, wide, xw, yw, M, y_is_fp32, stream);
+    }
   }
   const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
   const int token_groups = (M + nt - 1) / nt;

@@ -182,7 +182,9 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 to 4 on the
  *     wave-private kernel of BSL_DECODE_PRIVATE taking the M tokens at once, which share
  *     every sign, U and V operand and load, when their activations fit its LDS (148 KiB
- *     per workgroup), else the factored multi-token kernel; TILE from M = 5 on. */
+ *     per workgroup); in a grouped call that does not fit as a whole, the weights whose
+ *     activations take at most half of it go to that kernel and the others to the
+ *     factored multi-token kernel, in a second launch; TILE from M = 5 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2

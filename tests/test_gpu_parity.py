@@ -436,11 +436,12 @@ def test_llama3_8b_layer_few_tokens_grouped(M):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("M", [2, 4])
+@pytest.mark.parametrize("M", [2, 3, 4])
 def test_llama2_70b_layer_few_tokens(M):
-    """The 70B-shaped layer in one grouped launch: 2 tokens fit the wave-private kernel;
-    at 4 the down projection's activations (4 x 28672 fp16) exceed its LDS, so the launch
-    takes the factored kernel.  Both are checked on sampled rows."""
+    """The 70B-shaped layer in one grouped call: 2 tokens fit the wave-private kernel;
+    at 3 and 4 the down projection's activations (M x 28672 fp16) exceed its LDS, so the
+    call splits: the other six weights take the wave-private kernel and the down
+    projection the factored kernel.  All are checked on sampled rows."""
     shapes = synth.LLAMA2_70B_LAYER
     counts = [2] * len(shapes)
     ws = [(m, d, synth.synthetic_blocks(48, m, d, 2, 16, j)) for j, (_, m, d) in enumerate(shapes)]

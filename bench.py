@@ -9,8 +9,7 @@ of the layer are resident (about 0.96 GB) and the steps rotate over them, so the
 256 MB last-level cache cannot serve the reads.  Bytes are the algorithmic bytes of
 the loaded blocks, n * (m d / 8 + 2 k (m + d)) per weight, counted once.
 
-Also reported: prefill on the dense path (W_hat restored to a workspace, then a library
-GEMM); the same decode with every linear held as n = 8 equal-size vanilla-SVD
+Also reported: the same decode with every linear held as n = 8 equal-size vanilla-SVD
 blocks (rank k' = 16 + m d / (16 (m + d)), fp16 factors, no signs: the "w/o AVD"
 baseline, the same bytes per block); prefill at M = 2048 tokens through one such layer, on the tile path
 (W_hat rebuilt per tile, then a GEMM; executed MFMA work (2 k n G + 2 M) m d per weight
@@ -567,22 +566,6 @@ def main() -> None:
             "gemm_equivalent_tflops": round(pre.gemm_flops(0) / t_step / 1e12, 1),
         }
         log(f"prefill (tile): {t_step * 1e3:.2f} ms/step, {tfl_t:.1f} TFLOP/s executed MFMA work")
-        pre.close()
-        del pre
-        torch.cuda.empty_cache()
-        log("prefill: one 8B-shaped layer, n=8, M=2048, dense path (restore W_hat, then a rocBLAS GEMM)")
-        pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_DENSE)
-        wall_d, kms_d, _, _ = time_steps(torch, pre, args.tile_steps, 2)
-        d_step = wall_d / args.tile_steps
-        result["prefill_dense"] = {
-            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, dense path: one restore launch "
-                        "(W_hat in fp16, 436 MB) then one rocBLAS fp16 GEMM per linear",
-            "ms_per_step": round(d_step * 1e3, 3),
-            "tokens_per_s": round(2048 / d_step, 1),
-            "gemm_equivalent_tflops": round(pre.gemm_flops(0) / d_step / 1e12, 1),
-            "speedup_vs_tile": round(t_step / d_step, 2),
-        }
-        log(f"prefill (dense): {d_step * 1e3:.2f} ms/step")
         pre.close()
         del pre
         torch.cuda.empty_cache()

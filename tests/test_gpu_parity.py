@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 import bit_sign_rank_amd as bsl  # noqa: E402  (no skip: a missing library must fail here)
 from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
 
-PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE, bsl.BSL_PATH_DENSE]
-PATH_IDS = ["factored", "tile", "dense"]
+PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE]
+PATH_IDS = ["factored", "tile"]
 
 
 @pytest.fixture(scope="module", autouse=True)

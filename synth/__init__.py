@@ -71,6 +71,13 @@ def factor(seed: int, rows: int, k: int, *tags: int, scale: float = FACTOR_SCALE
     return (np.abs(g.standard_normal((rows, k))) * scale).astype(np.float16)
 
 
+def dyadic_factor(seed: int, rows: int, k: int, *tags: int) -> np.ndarray:
+    """fp16 factor ``[rows, k]`` whose entries are 1/4 or 1/2, each drawn with
+    probability 1/2 (seeded per array, so every row, column and rank varies)."""
+    g = rng(seed, 10, *tags)
+    return np.where(g.integers(0, 2, size=(rows, k)) == 1, 0.5, 0.25).astype(np.float16)
+
+
 def activations(seed: int, M: int, d: int, *tags: int) -> np.ndarray:
     """fp16 activations ``x[M, d]`` ~ N(0, 1)."""
     g = rng(seed, 4, *tags)
@@ -96,6 +103,18 @@ def block_counts(seed: int, count: int, lo: int, hi: int, *tags: int) -> np.ndar
     """Per-weight block counts drawn uniformly from the integers ``lo..hi``."""
     g = rng(seed, 5, *tags)
     return g.integers(lo, hi + 1, size=count).astype(np.int32)
+
+
+def dyadic_blocks(seed: int, m: int, d: int, n: int, k: int = 16, *tags: int):
+    """``n`` blocks with Bernoulli(0.5) sign bits and ``dyadic_factor`` U and V."""
+    return [
+        {
+            "bits": sign_bits(seed, m, d, *tags, i),
+            "u": dyadic_factor(seed, m, k, *tags, i, 0),
+            "v": dyadic_factor(seed, d, k, *tags, i, 1),
+        }
+        for i in range(n)
+    ]
 
 
 def integer_activations(seed: int, M: int, d: int, lo: int = -2, hi: int = 2, *tags: int) -> np.ndarray:

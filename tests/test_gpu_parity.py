@@ -33,10 +33,10 @@ def _device():
 
 
 def integer_blocks(m, d, n, seed=21):
-    return [
-        {"bits": synth.sign_bits(seed, m, d, i), "u": np.full((m, 16), 0.25, np.float16), "v": np.full((d, 16), 0.25, np.float16)}
-        for i in range(n)
-    ]
+    # dyadic factors (entries 1/4 or 1/2 per row, column and rank) and Bernoulli signs:
+    # with integer activations every partial sum of every path is exact in fp32 while
+    # max|x| 4 n d < 2^20 (tests/test_exact_dyadic.py), so outputs are compared bit for bit
+    return synth.dyadic_blocks(seed, m, d, n)
 
 
 # ---------------------------------------------------------------- sign unpack
@@ -58,9 +58,8 @@ def test_debug_unpack_bit_exact(m, d, path):
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8, 17, 130])
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)
 def test_integer_forward_bit_exact(m, d, n, M, path):
-    # U = V = 0.25 with k = 16 makes U V^T == 1, so y = x (sum_i S_i)^T is an integer of
-    # magnitude < 2^20; every partial sum is exact in fp32, so any order gives the same bits.
-    # (On the tile path W_hat itself is a sum of n <= 16 signs: exact in fp16.)
+    # U V^T is a multiple of 1/16 in [1, 4], W_hat a multiple of 1/16 below 64 (exact in
+    # fp16 on the tile path), y a multiple of 1/16 below 2^20: exact in fp32 in any order.
     blocks = integer_blocks(m, d, n)
     x = synth.integer_activations(9, M, d)
     with Stack([(m, d, blocks)], path=path) as st:

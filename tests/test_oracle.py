@@ -57,17 +57,21 @@ def test_block_bytes_equal_vanilla_svd_rank(m, d):
 
 
 # ---------------------------------------------------------------- sign bits
-def test_sign_bits_round_trip_and_order():
-    bits = synth.sign_bits(3, 5, 24)
-    s = osigns.signs_from_bits(bits)
-    assert s.dtype == np.int8 and set(np.unique(s)) <= {-1, 1}
-    assert np.array_equal(osigns.bits_from_signs(s), bits)
+def _bit_order_pin_holds():
     # bit order: LSB of byte 0 is column 0, set bit is -1
     one = np.zeros((1, 2), np.uint8)
     one[0, 0] = 0b0000_0101
     one[0, 1] = 0b1000_0000
     s1 = osigns.signs_from_bits(one)[0]
-    assert s1.tolist() == [-1, 1, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, -1]
+    return s1.tolist() == [-1, 1, -1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, -1]
+
+
+def test_sign_bits_round_trip_and_order():
+    bits = synth.sign_bits(3, 5, 24)
+    s = osigns.signs_from_bits(bits)
+    assert s.dtype == np.int8 and set(np.unique(s)) <= {-1, 1}
+    assert np.array_equal(osigns.bits_from_signs(s), bits)
+    assert _bit_order_pin_holds()
 
 
 def test_sign_of_zero_is_plus_one():
@@ -168,17 +172,22 @@ def test_nonnegative_weight_is_plain_low_rank():
     assert np.allclose(oracle.forward(x, blocks, 1), expect, rtol=1e-12, atol=1e-12)
 
 
-def test_integer_forward_is_exact_sign_sum():
-    # U = V = 0.25 with k = 16 gives U V^T == 1, so W_hat = sum_i S_i and y = x sum_i S_i^T.
+def _integer_pin_holds():
+    # U = V = 0.25 with k = 16 gives U V^T == 1, so W_hat = sum_i S_i and y = x sum_i S_i^T
+    # (the expected value uses numpy's own unpacking, not the oracle's).
     m, d, n, k = 48, 64, 3, 16
     blocks = []
     for i in range(n):
         bits = synth.sign_bits(21, m, d, i)
         blocks.append({"bits": bits, "u": np.full((m, k), 0.25, np.float16), "v": np.full((d, k), 0.25, np.float16)})
     x = synth.integer_activations(3, 2, d)
-    Ssum = sum(osigns.signs_from_bits(b["bits"]).astype(np.int64) for b in blocks)
+    Ssum = sum(1 - 2 * np.unpackbits(b["bits"], axis=1, bitorder="little").astype(np.int64) for b in blocks)
     expect = x.astype(np.int64) @ Ssum.T
-    assert np.array_equal(oracle.forward(x, blocks, n), expect.astype(np.float64))
+    return np.array_equal(oracle.forward(x, blocks, n), expect.astype(np.float64))
+
+
+def test_integer_forward_is_exact_sign_sum():
+    assert _integer_pin_holds()
 
 
 def test_zero_blocks_give_zero_output():
@@ -397,18 +406,20 @@ def test_planted_mistakes_are_caught(monkeypatch):
     blk, Rn, sigma = oavd.avd_step(R, 4)
     assert not (np.all(blk["u"][:, 0] >= 0) and np.all(blk["v"][:, 0] >= 0))
     monkeypatch.undo()
-    # 2) a dropped sign matrix in the restoration breaks the integer pin
-    m, d, k = 16, 16, 16
-    bits = synth.sign_bits(21, m, d, 0)
-    blocks = [{"bits": bits, "u": np.full((m, k), 0.25, np.float16), "v": np.full((d, k), 0.25, np.float16)}]
-    x = synth.integer_activations(3, 1, d)
-    no_sign = x.astype(np.float64) @ np.ones((m, d)).T
-    pin = x.astype(np.int64) @ osigns.signs_from_bits(bits).astype(np.int64).T
-    assert not np.array_equal(no_sign, pin)
-    # 3) flipped bit polarity breaks the bit-order pin
-    one = np.array([[0b101]], np.uint8)
-    flipped = 2 * np.unpackbits(one, axis=1, bitorder="little").astype(np.int8) - 1
-    assert flipped[0, :3].tolist() != osigns.signs_from_bits(one)[0, :3].tolist()
+    # 2) a restoration that drops the sign matrix fails the integer pin
+    monkeypatch.setattr(orest, "signs_from_bits", lambda bits, d=None: np.ones_like(osigns.signs_from_bits(bits, d)))
+    assert not _integer_pin_holds()
+    monkeypatch.undo()
+    assert _integer_pin_holds()
+    # 3) an unpacking with the opposite bit order (most significant bit first) fails the
+    # bit-order pin, and so does one with the opposite polarity
+    real = osigns.signs_from_bits
+    monkeypatch.setattr(osigns, "signs_from_bits", lambda bits, d=None: real(np.asarray(bits)[:, ::-1], d)[:, ::-1])
+    assert not _bit_order_pin_holds()
+    monkeypatch.setattr(osigns, "signs_from_bits", lambda bits, d=None: -real(bits, d))
+    assert not _bit_order_pin_holds()
+    monkeypatch.undo()
+    assert _bit_order_pin_holds()
     # 4) a transposed product (x W instead of x W^T) fails brute force on a square shape
     blocks = synth.synthetic_blocks(17, 8, 8, 2, 2)
     xx = synth.activations(2, 1, 8)

@@ -43,6 +43,7 @@ EXPORTED = (
     "bsl_resident_bytes",
     "bsl_forward",
     "bsl_forward_group",
+    "bsl_forward_group_static",
     "bsl_debug_unpack",
     "bsl_last_error",
     "bsl_destroy",
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_resident_bytes.argtypes = [c_vp]
         L.bsl_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
+        L.bsl_forward_group_static.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_set_path.argtypes = [c_vp, c_i32]
         L.bsl_set_decode.argtypes = [c_vp, c_i32]
         L.bsl_debug_unpack.argtypes = [c_vp, c_i32, c_i32, c_i32, c_vp, c_vp]
@@ -120,7 +122,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_lr_destroy.restype = None
         L.bsl_lr_destroy.argtypes = [c_vp]
         for f in ("bsl_pack_signs", "bsl_unpack_signs", "bsl_init", "bsl_set_source", "bsl_load_blocks",
-                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_set_path", "bsl_debug_unpack", "bsl_set_decode",
+                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_forward_group_static", "bsl_set_path", "bsl_debug_unpack", "bsl_set_decode",
                   "bsl_set_input_scale", "bsl_lr_init", "bsl_lr_set_source", "bsl_lr_load_blocks", "bsl_lr_forward",
                   "bsl_lr_forward_group"):
             getattr(L, f).restype = c_i32
@@ -227,6 +229,15 @@ def bsl_forward_group(stack: int, weights, x_ptrs, y_ptrs, M: int, y_is_fp32: bo
     ys = (ctypes.c_void_p * n)(*y_ptrs)
     _check(lib().bsl_forward_group(stack, n, ctypes.addressof(ws), ctypes.addressof(xs), ctypes.addressof(ys), M,
                                    1 if y_is_fp32 else 0, stream))
+
+
+def bsl_forward_group_static(stack: int, weights, x_ptrs, y_ptrs, M: int, y_is_fp32: bool, stream: int = 0) -> None:
+    n = len(weights)
+    ws = (ctypes.c_int32 * n)(*weights)
+    xs = (ctypes.c_void_p * n)(*x_ptrs)
+    ys = (ctypes.c_void_p * n)(*y_ptrs)
+    _check(lib().bsl_forward_group_static(stack, n, ctypes.addressof(ws), ctypes.addressof(xs), ctypes.addressof(ys), M,
+                                          1 if y_is_fp32 else 0, stream))
 
 
 def bsl_set_path(stack: int, path: int) -> None:

@@ -199,6 +199,7 @@ struct bsl_stack {
   size_t staging_bytes = 0;
   hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] finished
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
+  void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
   std::vector<Weight> w;
 };
 
@@ -359,6 +360,10 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
     else if ((e = hipMalloc(&s->tile_ctr, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile counters)");
     else if ((e = hipMemset(s->tile_ctr, 0, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(tile counters)");
+  }
+  if (rc == BSL_OK) {
+    const int se = static_scratch_setup(device, &s->static_scratch);
+    if (se != 0) rc = hip_fail(static_cast<hipError_t>(se), "hipGetSymbolAddress(static scratch)");
   }
   if (rc == BSL_OK && (e = hipDeviceSynchronize()) != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
   if (rc != BSL_OK) {
@@ -646,16 +651,21 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
   return BSL_OK;
 }
 
+// use_static: the allocation-free variant (bsl_forward_group_static): 1 to 4 tokens on the
+// single- and few-token kernels only, their pieces and arrival counters in the device's
+// static scratch array instead of the stack's workspace.
 int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
-                 int32_t y_is_fp32, void* stream) {
+                 int32_t y_is_fp32, void* stream, bool use_static = false) {
   if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");
   if (M < 1 || M > (1 << 24)) return fail(BSL_EINVAL, "forward: M must be >= 1");
+  if (use_static && M > kWpMaxTokens)
+    return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: takes 1 to 4 tokens (the single- and few-token kernels)");
   GroupArgs args;
   std::memset(&args, 0, sizeof(args));
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  const bool tile = s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens);
+  const bool tile = !use_static && (s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens));
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
@@ -722,13 +732,28 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     }
     return fits;
   };
-  auto launch_units = [&](int lg) {
+  // piece_floats: floats per piece of the kernel about to run (pieces are indexed by row
+  // group + worker, so (groups + workers) pieces)
+  auto launch_units = [&](int lg, size_t piece_floats) {
     args.total_units = (uint32_t)units;
     args.total_groups = (uint32_t)groups;
     args.grid_log2 = lg;
     args.zero_page = s->zero_page;
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
+    if (!use_static) return BSL_OK;
+    const size_t need = (groups + ((size_t)1 << lg)) * piece_floats * sizeof(float);
+    const size_t room = kStaticScratchBytes - kStaticArrivals * sizeof(uint32_t);
+    if (groups > kStaticArrivals || need > room)
+      return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: this launch needs " + std::to_string(groups) +
+                                        " arrival counters and " + std::to_string(need) + " bytes of partial sums; the static scratch holds " +
+                                        std::to_string(kStaticArrivals) + " and " + std::to_string(room));
+    uint32_t* arrivals = static_cast<uint32_t*>(s->static_scratch);
+    args.arrivals = arrivals;
+    args.pieces = reinterpret_cast<float*>(arrivals + kStaticArrivals);
+    // the kernels expect zero counters; a kernel, not a memset, so that captured streams hold no memset node
+    const int fe = launch_fill_u32(arrivals, (uint32_t)groups, 0u, stream);
+    return fe == 0 ? BSL_OK : hip_fail(static_cast<hipError_t>(fe), "scratch counter clear");
   };
   if (M == 1) {
     // AUTO takes the shared-operand kernel: on the 8B-shaped layer it measured faster
@@ -746,18 +771,20 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       while ((1 << lg) < grid) ++lg;
       if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
     }
-    launch_units(lg);
+    const int rc = launch_units(lg, wp ? (size_t)kWpRows : (size_t)kDecodeGroupRows);
+    if (rc != BSL_OK) return rc;
     e = wp ? launch_decode_wp(args, 1, stream) : launch_decode_m1(args, stream);
     if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
     return BSL_OK;
   }
-  if (M <= kWpMaxTokens && s->path == BSL_PATH_AUTO) {
+  if (M <= kWpMaxTokens && (s->path == BSL_PATH_AUTO || use_static)) {
     // a few tokens: the wave-private kernel with every operand but the activations shared
     // by the tokens, when they fit its LDS
     const int T = M;
     int lg = 0;
     if (plan_private(T, lg)) {
-      launch_units(lg);
+      const int rc = launch_units(lg, (size_t)kWpRows);
+      if (rc != BSL_OK) return rc;
       e = launch_decode_wp(args, T, stream);
       if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
       return BSL_OK;
@@ -783,6 +810,8 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
         yw[nw++] = y[j];
       }
     }
+    if (use_static)
+      return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: the activations of this group do not fit the few-token kernel's LDS");
     if (nn > 0 && nw > 0) {
       const int rc = forward_impl(s, nn, narrow, xn, yn, M, y_is_fp32, stream);
       if (rc != BSL_OK) return rc;
@@ -834,6 +863,13 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
                       int32_t M, int32_t y_is_fp32, void* stream) {
   if (!s || !weights || !x || !y) return fail(BSL_EINVAL, "bsl_forward_group: null pointer");
   return forward_impl(s, count, weights, x, y, M, y_is_fp32, stream);
+}
+
+int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
+                             int32_t M, int32_t y_is_fp32, void* stream) {
+  if (!s || !weights || !x || !y) return fail(BSL_EINVAL, "bsl_forward_group_static: null pointer");
+  if (!s->static_scratch) return fail(BSL_EHIP, "bsl_forward_group_static: no static scratch on this device");
+  return forward_impl(s, count, weights, x, y, M, y_is_fp32, stream, true);
 }
 
 int bsl_set_path(bsl_stack* s, int32_t path) {

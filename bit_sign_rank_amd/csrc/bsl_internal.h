@@ -127,6 +127,19 @@ constexpr size_t kTileWorkspaceFloats = (size_t)16 << 20;  // 64 MiB
 constexpr int kTileItemsPerCu = 2;     // aim of the column-range cutting
 constexpr int kTileCounters = 1 << 16;
 
+// Allocation-free forward (bsl_forward_group_static): the single- and few-token kernels
+// pieces and arrival counters in one static device array per device (see
+// bsl_kernels.hip), arrival counters first.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+constexpr size_t kStaticArrivals = 16384;  // counters (64 KiB) before the pieces
+constexpr int kMaxDevices = 64;
+// Address of this process's static scratch array on `device` (which must be the current
+// device), taken with hipGetSymbolAddress on the first call for that device.  Returns a
+// hipError_t value.
+int static_scratch_setup(int device, void** out);
+// p[0 .. n) = v on `stream` (a kernel, so that captured streams hold no memset node).
+int launch_fill_u32(uint32_t* p, uint32_t n, uint32_t v, void* stream);
+
 // Records the calling thread's error message (bsl_last_error) and returns code.
 int set_error(int code, const std::string& msg);
 

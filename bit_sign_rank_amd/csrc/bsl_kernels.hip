@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1747,6 +1748,44 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
   const int row = rt * kTileRows + (lane & 15);
   if (row >= m) return;
   debug_planes(std::make_integer_sequence<int, kPlanes>{}, w, path, lane >> 4, ch, row, d, out);
+}
+
+// ============================================================ static scratch
+// Scratch memory of the allocation-free forward: the pieces and arrival counters of the
+// single- and few-token kernels, kStaticScratchBytes per device for the life of the
+// process, shared by every such call on the device.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the symbol): it uses
+// the device address static_scratch_setup takes once per device.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int static_scratch_setup(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return 0;
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, uint32_t n, uint32_t v) {
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = v;
+}
+
+int launch_fill_u32(uint32_t* p, uint32_t n, uint32_t v, void* stream) {
+  if (n == 0) return 0;
+  const uint32_t blocks = std::min<uint32_t>(64, (n + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), p, n, v);
+  return (int)hipGetLastError();
 }
 
 // ============================================================ launchers

@@ -202,6 +202,31 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Partial sums go from the workgroups (or waves) that compute them to the one that adds
+// them, which may sit on another XCD.  Every access to them and to the arrival counters
+// is an atomic at agent scope, and the ordering is made explicit instead of with agent
+// fences, following the gfx950 memory model as the compiler implements it (LLVM AMDGPU
+// memory model, GFX942 family):
+//  * an atomic store or read-modify-write at agent scope is issued with SC1 set and
+//    writes through the XCD's L2; the vector memory counter counts it until the write is
+//    acknowledged, so after s_waitcnt vmcnt(0) it is visible to every agent-scope access
+//    of the device;
+//  * an atomic load at agent scope (SC1) is not served from a non-coherent L2 line;
+//  * publish_partials() waits for this wave's stores (vmcnt(0)) before the workgroup
+//    barrier that precedes the arrival count, so every partial sum is visible before the
+//    count is;
+//  * the last arriver's loads of the partial sums are issued after, and only because of,
+//    the returned count (a branch on it), so none is performed before the count.
+// An agent-scope release fence adds buffer_wbl2 (write back every dirty L2 line) and an
+// acquire fence buffer_inv (invalidate the L2); both exist for ordinary, non-atomic
+// accesses, which the combines do not make.  Measured on MI355X, the fenced form costs
+// 27 us per single-token launch (75 -> 102 us, 8B-shaped layer) and 50 us per split
+// tile-path launch at 16 tokens.
+__device__ __forceinline__ void publish_partials() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ uint32_t count_arrival(uint32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Pick the descriptor of the weight that owns `item` (uniform across the wave).
 __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int item) {
   WeightDesc W = args.w[0];
@@ -598,7 +623,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   int je = 0;
   while (je + 1 < args.count && u_end - 1 >= args.w[je + 1].unit_begin) ++je;
   const uint32_t item_last = args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's piece stores have completed
+  publish_partials();  // this wave's pieces are visible before any arrival is counted
   __syncthreads();
   // row groups of the range, NW * 64 at a time: one thread each counts the workgroup in
   for (uint32_t k0 = 0; k0 <= item_last - item_first; k0 += NW * 64) {
@@ -613,7 +638,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       const bool has_units = args.w[j].units != 0;
       const uint32_t expected = has_units ? owner(last) - owner(first) + 1 : 0u;
       const uint32_t seen =
-          has_units ? __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 : 0u;
+          has_units ? count_arrival(&args.arrivals[item]) + 1 : 0u;
       if (has_units && seen == expected) {
         __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_items[atomicAdd(&n_last, 1u)] = item;
@@ -899,11 +924,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
-  __syncthreads();                // ... in every wave, and every wave is done with zs
+  publish_partials();  // the partial sums above are visible before the arrival is counted
+  __syncthreads();     // ... in every wave, and every wave is done with zs
   uint32_t* last = reinterpret_cast<uint32_t*>(&zs[0][0][0]);
-  if (threadIdx.x == 0)
-    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
+  if (threadIdx.x == 0) *last = count_arrival(&W.counters[rest]) == (uint32_t)(W.splits - 1);
   __syncthreads();
   if (!*last) return;
   const int rbeg = rg * kPrefillGroupRows;
@@ -994,14 +1018,6 @@ __device__ __forceinline__ float16v rebuild_mfma(const half8& a, const half8& b)
 __device__ __forceinline__ void mfma_result_ready(float16v& d0, float16v& d1) {
   asm("s_nop 15\n\ts_nop 3" : "+v"(d0), "+v"(d1));
 }
-// The same once two later rebuild MFMAs (whose results n0, n1 are) have been issued:
-// each waits for the matrix pipe (32 cycles per 32x32x16 MFMA), so d0 and d1 are long
-// ready; tying the hand-over to n0, n1 keeps it from moving above those MFMAs.
-__device__ __forceinline__ void mfma_result_ready_after(float16v& d0, float16v& d1, const float16v& n0,
-                                                        const float16v& n1) {
-  asm("" : "+v"(d0), "+v"(d1) : "v"(n0), "v"(n1));
-}
-
 template <int TT, int TH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_kernel(GroupArgs args, int token_groups) {
   constexpr int TG = TT * TH;             // 32-token tiles per workgroup
@@ -1238,10 +1254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           }
 #pragma unroll
           for (int g = g0; g < g1; ++g) gemm_one(g, xa[g - g0], bw);
-          if (PIPE && i + 1 < BPW)
-            mfma_result_ready_after(d0, d1, dn0, dn1);
-          else
-            mfma_result_ready(d0, d1);
+          mfma_result_ready(d0, d1);
           recon_math(d0, d1, i, qkn, wp);
         }
         // Every load issued after this body's activation loads is one of the 2 BPW V loads
@@ -1281,11 +1294,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __hip_atomic_store(&W.partial[((size_t)split * tokpad + t) * rows_pad + row], acc[tt][v], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
-  __builtin_amdgcn_s_waitcnt(0);  // the write-through stores above have completed
-  __syncthreads();                // ... in every wave, and every wave is done with xs
+  publish_partials();  // the partial sums above are visible before the arrival is counted
+  __syncthreads();     // ... in every wave, and every wave is done with xs
   uint32_t* last = reinterpret_cast<uint32_t*>(&xs0[0][0][0][0]);
-  if (threadIdx.x == 0)
-    *last = __hip_atomic_fetch_add(&W.counters[rest], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(W.splits - 1);
+  if (threadIdx.x == 0) *last = count_arrival(&W.counters[rest]) == (uint32_t)(W.splits - 1);
   __syncthreads();
   if (!*last) return;
   const int rbeg = rg * GROUP_ROWS;
@@ -1671,14 +1683,14 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
   const int je = weight_of(u_end - 1);
   const uint32_t item_last =
       args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's piece stores have completed
+  publish_partials();  // this wave's pieces are visible before its arrivals are counted
   for (uint32_t item = item_first; item <= item_last; ++item) {
     uint32_t first, last;
     const int j = group_units(item, first, last);
     if (args.w[j].units == 0) continue;  // a weight without blocks (y = 0 is written above)
     const uint32_t o0 = owner(first), o1 = owner(last);
     uint32_t seen = 0;
-    if (lane == 0) seen = __hip_atomic_fetch_add(&args.arrivals[item], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+    if (lane == 0) seen = count_arrival(&args.arrivals[item]) + 1;
     seen = __builtin_amdgcn_readfirstlane(seen);
     if (seen != o1 - o0 + 1) continue;
     if (lane == 0) __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -197,40 +197,77 @@ __global__ __launch_bounds__(256) void lds_kernel(int iters, uint32_t* out, uint
 // The single-token kernel's inner pattern: 16 planes per round; per plane every wave
 // reads that plane's 32-byte B operand per lane from LDS (two 16-byte reads, shared by
 // the workgroup) and runs R sparse MFMAs with it (R independent accumulators, an index
-// per accumulator).  R = 4, 8 or 16.
-template <int R>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_lds_kernel(int iters, float* out, uint64_t* clocks) {
+// per accumulator).  R = 4, 8 or 16.  MODE 0: A = 1.0, B near 1.0 (few mantissa bits);
+// MODE 1: A = 1.0, B pseudo-random fp16 of magnitude 2^-8..2^-2 (the shared-operand
+// decode: A all ones, B = +-V x); MODE 2: A and B pseudo-random (the wave-private decode:
+// A = x, B = +-V).  With src non-null every wave also streams one 16-byte non-temporal
+// load per lane per 16 MFMAs (the decode's sign bytes per MFMA), each consumed four
+// loads later.
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// fp16 pair with random sign and mantissa, exponent 2^-8..2^-2
+__device__ __forceinline__ uint32_t rand_half2(uint32_t h) {
+  const uint32_t e0 = 7u + (h & 7u), e1 = 7u + ((h >> 3) & 7u);
+  const uint32_t lo = ((h >> 6) & 0x83FFu) | (e0 << 10), hi = ((h >> 16) & 0x83FFu) | (e1 << 10);
+  return lo | (hi << 16);
+}
+
+template <int R, int MODE, bool STREAM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void mfma_lds_kernel(int iters, float* out, uint64_t* clocks, const u32x4* src, uint64_t n16) {
   __shared__ u32x4 zs[16][2][64];
   const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   const int lane = threadIdx.x & 63;
-  for (int k = threadIdx.x; k < 16 * 2 * 64; k += 256)
-    (&zs[0][0][0])[k] = (u32x4){0x3c003c00u ^ (uint32_t)k, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+  for (int k = threadIdx.x; k < 16 * 2 * 64; k += 256) {
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) v[q] = MODE == 0 ? (q == 0 ? 0x3c003c00u ^ (uint32_t)k : 0x3c003c00u) : rand_half2(hash32(4 * k + q));
+    (&zs[0][0][0])[k] = v;
+  }
   __syncthreads();
-  half8 a;
+  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+  u32x4 araw;
+  for (int q = 0; q < 4; ++q) araw[q] = MODE == 2 ? rand_half2(hash32(0x9e3779b9u * (threadIdx.x + 1) + q)) : 0x3c003c00u;
+  half8 a = __builtin_bit_cast(half8, araw);
+  constexpr int NI = R < 8 ? R : 8;  // distinct sparse indices
+  int idx[NI];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a[k] = (_Float16)1.0f;
-  int idx[R];
-#pragma unroll
-  for (int t = 0; t < R; ++t) idx[t] = 0x44444444 | (t & 1 ? 0x22222222 : 0);
+  for (int t = 0; t < NI; ++t) idx[t] = (int)(0x44444444u | (hash32(t * 64 + lane) & 0xAAAAAAAAu));
   asm volatile("" : "+v"(a));
   float4v c[R];
 #pragma unroll
   for (int t = 0; t < R; ++t) c[t] = (float4v){0.f, 0.f, 0.f, 0.f};
-  typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
   auto read_b = [&](int b) {
     const u32x4 lo = zs[b][0][lane], hi = zs[b][1][lane];
     return __builtin_bit_cast(half16, (u32x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   };
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t li = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 pend[4] = {};
+  u32x4 sacc = {0u, 0u, 0u, 0u};
+  constexpr int PLANES_PER_LOAD = 16 / R;  // planes per 16 MFMAs
   half16 cur = read_b(0);
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (STREAM) {
+        if (b % PLANES_PER_LOAD == 0) {
+          const int slot = (b / PLANES_PER_LOAD) & 3;
+          sacc ^= pend[slot];
+          pend[slot] = load_nt(src + (li & (n16 - 1)));
+          li += stride;
+        }
+      }
       const half16 nxt = read_b((b + 1) & 15);  // the next plane's operand, read while this one runs
 #pragma unroll
       for (int t = 0; t < R; ++t) {
-        if (b & 1) c[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, cur, c[t], idx[t], 0, 1);
-        else c[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, cur, c[t], idx[t], 0, 0);
+        if (b & 1) c[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, cur, c[t], idx[t % NI], 0, 1);
+        else c[t] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a, cur, c[t], idx[t % NI], 0, 0);
       }
       cur = nxt;
     }
@@ -238,7 +275,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float total = 0.f;
 #pragma unroll
   for (int t = 0; t < R; ++t) total += c[t][0] + c[t][1] + c[t][2] + c[t][3];
-  out[(uint64_t)blockIdx.x * blockDim.x + threadIdx.x] = total;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sacc ^= pend[k];
+  out[(uint64_t)blockIdx.x * blockDim.x + threadIdx.x] = total + (float)(sacc[0] ^ sacc[1] ^ sacc[2] ^ sacc[3]) * 1e-30f;
   __syncthreads();
   stamp(clocks, 1, __builtin_amdgcn_s_memtime(), __builtin_amdgcn_s_memrealtime());
   if (threadIdx.x == 0) {
@@ -290,14 +329,25 @@ int bslp_lds(int iters, uint32_t* out, uint64_t* clocks, int grid, void* stream)
   return (int)hipGetLastError();
 }
 
-// Sparse MFMAs fed from LDS: r = 4, 8 or 16 MFMAs per 2 KiB B operand read per wave.
-int bslp_mfma_lds(int r, int iters, float* out, uint64_t* clocks, int grid, void* stream) {
+// Sparse MFMAs fed from LDS: r = 4, 8 or 16 MFMAs per 2 KiB B operand read per wave;
+// mode 0, 1, 2 (operand values, see mfma_lds_kernel); src / bytes: the optional stream
+// (bytes a power of two times 16).
+int bslp_mfma_lds(int r, int mode, int iters, float* out, uint64_t* clocks, const void* src, uint64_t bytes, int grid,
+                  void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (r == 4) hipLaunchKernelGGL(mfma_lds_kernel<4>, dim3(grid), dim3(256), 0, st, iters, out, clocks);
-  else if (r == 8) hipLaunchKernelGGL(mfma_lds_kernel<8>, dim3(grid), dim3(256), 0, st, iters, out, clocks);
-  else if (r == 16) hipLaunchKernelGGL(mfma_lds_kernel<16>, dim3(grid), dim3(256), 0, st, iters, out, clocks);
-  else return (int)hipErrorInvalidValue;
-  return (int)hipGetLastError();
+  const u32x4* s = static_cast<const u32x4*>(src);
+  const uint64_t n16 = bytes / 16;
+  const bool str = s != nullptr && n16 > 0;
+#define BSLP_CASE(RR, MM)                                                                                           \
+  if (r == RR && mode == MM) {                                                                                      \
+    if (str) hipLaunchKernelGGL((mfma_lds_kernel<RR, MM, true>), dim3(grid), dim3(256), 0, st, iters, out, clocks, s, n16); \
+    else hipLaunchKernelGGL((mfma_lds_kernel<RR, MM, false>), dim3(grid), dim3(256), 0, st, iters, out, clocks, s, n16);   \
+    return (int)hipGetLastError();                                                                                  \
+  }
+  BSLP_CASE(4, 0) BSLP_CASE(4, 1) BSLP_CASE(4, 2) BSLP_CASE(8, 0) BSLP_CASE(8, 1) BSLP_CASE(8, 2)
+  BSLP_CASE(16, 0) BSLP_CASE(16, 1) BSLP_CASE(16, 2)
+#undef BSLP_CASE
+  return (int)hipErrorInvalidValue;
 }
 
 }  // extern "C"

@@ -28,7 +28,8 @@ def lib():
         L.bslp_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         L.bslp_lds.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-        L.bslp_mfma_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        L.bslp_mfma_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
         for f in (L.bslp_read, L.bslp_copy, L.bslp_mfma, L.bslp_lds, L.bslp_mfma_lds):
             f.restype = ctypes.c_int
         _LIB = L
@@ -104,15 +105,23 @@ def measure(torch, cus: int, reps: int = 20, gib: float = 2.0) -> dict:
     ck = _clock_ghz(mclk)
     res["lds_read"] = {"TBs": round(lds_bytes / t / 1e12, 1), "clock_ghz": ck,
                        "bytes_per_clk_per_cu": round(lds_bytes / t / (ck * 1e9) / cus, 1) if ck else None}
-    # sparse MFMAs whose B operand (2 KiB per wave) is read from LDS every r instructions
+    # sparse MFMAs whose B operand (2 KiB per wave) is read from LDS every r instructions,
+    # with three operand profiles (mode 0: A = 1, B ~ 1; mode 1: A = 1, B random; mode 2:
+    # both random), alone and beside the matched sign-byte stream
     for r in (4, 8, 16):
-        for wps, g in ((4, mgrid), (1, cus)):
-            n_instr = 16 * r * iters // 4
-            flops = FLOP[1] * n_instr * g * 4
-            t = _time(torch, lambda: _check(L.bslp_mfma_lds(r, iters // 4, mout.data_ptr(), mclk.data_ptr(), g, st), "mfma_lds"), reps // 4 + 1)
-            ck = _clock_ghz(mclk[: g * 4])
-            res[f"sparse_mfma_lds_r{r}_{wps}wps"] = {"tflops": round(flops / t / 1e12, 1), "clock_ghz": ck,
-                                                  "cycles_per_instr": round(t * ck * 1e9 / (wps * n_instr), 2) if ck else None}
+        for mode in (0, 1, 2):
+            for stream in (False, True):
+                it = iters // 4
+                n_instr = 16 * r * it
+                flops = FLOP[1] * n_instr * mgrid * 4
+                sp, sb = (src.data_ptr(), n16 * 16) if stream else (None, 0)
+                t = _time(torch, lambda: _check(L.bslp_mfma_lds(r, mode, it, mout.data_ptr(), mclk.data_ptr(), sp, sb, mgrid, st), "mfma_lds"), reps // 4 + 1)
+                ck = _clock_ghz(mclk)
+                key = f"sparse_mfma_lds_r{r}_mode{mode}" + ("_stream" if stream else "")
+                res[key] = {"tflops": round(flops / t / 1e12, 1), "clock_ghz": ck,
+                            "cycles_per_instr": round(t * ck * 1e9 / (4 * n_instr), 2) if ck else None}
+                if stream:
+                    res[key]["stream_GBs"] = round(n_instr // 16 * 1024 * mgrid * 4 / t / 1e9, 1)
     # the sparse loop beside an HBM stream of 1 KiB per wave per 16 instructions
     flops = FLOP[1] * 16 * iters * mgrid * 4
     streamed = 16 * 64 * iters * mgrid * 4

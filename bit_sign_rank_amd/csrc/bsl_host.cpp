@@ -193,7 +193,8 @@ struct bsl_stack {
   uint64_t budget = 0, resident = 0;
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
   float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
-  uint32_t* arrivals = nullptr;   // single-token arrival counters, one per row group of a launch
+  uint32_t* arrivals = nullptr;   // wave-private kernel's arrival counters, one per row group of a launch
+  uint64_t* acc64 = nullptr;      // shared-operand kernel's row accumulators ([row groups of a launch][1024], zero)
   float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
   uint8_t* staging[2] = {nullptr, nullptr};  // pinned host buffers of bsl_load_blocks (allocated on first use)
   size_t staging_bytes = 0;
@@ -357,6 +358,10 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
     else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
     else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
+    else if ((e = hipMalloc(&s->acc64, (size_t)kMaxGroup * max_groups * kDecodeGroupRows * sizeof(uint64_t))) != hipSuccess)
+      rc = hip_fail(e, "hipMalloc(row accumulators)");
+    else if ((e = hipMemset(s->acc64, 0, (size_t)kMaxGroup * max_groups * kDecodeGroupRows * sizeof(uint64_t))) != hipSuccess)
+      rc = hip_fail(e, "hipMemset(row accumulators)");
     else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
     else if ((e = hipMalloc(&s->tile_ctr, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile counters)");
     else if ((e = hipMemset(s->tile_ctr, 0, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(tile counters)");
@@ -732,8 +737,9 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     }
     return fits;
   };
-  // piece_floats: floats per piece of the kernel about to run (pieces are indexed by row
-  // group + worker, so (groups + workers) pieces)
+  // piece_floats: floats per piece of the wave-private kernel about to run (pieces are
+  // indexed by row group + worker, so (groups + workers) pieces); 0 for the shared-operand
+  // kernel, which keeps one 64-bit accumulator per row of its row groups instead
   auto launch_units = [&](int lg, size_t piece_floats) {
     args.total_units = (uint32_t)units;
     args.total_groups = (uint32_t)groups;
@@ -741,8 +747,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     args.zero_page = s->zero_page;
     args.pieces = s->pieces;
     args.arrivals = s->arrivals;
+    args.acc = s->acc64;
     if (!use_static) return BSL_OK;
-    const size_t need = (groups + ((size_t)1 << lg)) * piece_floats * sizeof(float);
+    const size_t need = piece_floats ? (groups + ((size_t)1 << lg)) * piece_floats * sizeof(float)
+                                     : groups * kDecodeGroupRows * sizeof(uint64_t);
     const size_t room = kStaticScratchBytes - kStaticArrivals * sizeof(uint32_t);
     if (groups > kStaticArrivals || need > room)
       return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: this launch needs " + std::to_string(groups) +
@@ -751,8 +759,11 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     uint32_t* arrivals = static_cast<uint32_t*>(s->static_scratch);
     args.arrivals = arrivals;
     args.pieces = reinterpret_cast<float*>(arrivals + kStaticArrivals);
-    // the kernels expect zero counters; a kernel, not a memset, so that captured streams hold no memset node
-    const int fe = launch_fill_u32(arrivals, (uint32_t)groups, 0u, stream);
+    args.acc = reinterpret_cast<uint64_t*>(arrivals + kStaticArrivals);
+    // the kernels expect zero counters (and zero accumulators); a kernel, not a memset, so
+    // that captured streams hold no memset node
+    const int fe = piece_floats ? launch_fill_u32(arrivals, (uint32_t)groups, 0u, stream)
+                                : launch_fill_u32(arrivals + kStaticArrivals, (uint32_t)(need / sizeof(uint32_t)), 0u, stream);
     return fe == 0 ? BSL_OK : hip_fail(static_cast<hipError_t>(fe), "scratch counter clear");
   };
   if (M == 1) {
@@ -765,13 +776,35 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     } else {
       plan_units(kDecodeGroupRows);
       // Persistent grid: the largest power of two that is no more than one workgroup per
-      // CU and no more than the number of units (so no workgroup's share is empty).
+      // CU and no more than the number of units (so no workgroup's share is empty), and
+      // small enough that no row group is shared by more workgroups than its rows'
+      // accumulators can count.
       int32_t grid = s->decode_grid_max;
       while (grid > 1 && (uint64_t)grid > units) grid /= 2;
       while ((1 << lg) < grid) ++lg;
+      auto owner = [&](uint64_t u) {  // the kernel's owner(): o with start(o) <= u < start(o + 1)
+        uint64_t o = (u << lg) / units;
+        while (o + 1 < ((uint64_t)1 << lg) && start(o + 1, lg) <= u) ++o;
+        while (start(o, lg) > u) --o;
+        return o;
+      };
+      auto max_parts = [&]() {
+        uint64_t worst = 0;
+        for (int32_t j = 0; j < count; ++j) {
+          const WeightDesc& D = args.w[j];
+          if (D.units == 0) continue;
+          const uint64_t per = D.units / (uint64_t)D.groups;
+          for (int32_t g = 0; g < D.groups; ++g) {
+            const uint64_t first = D.unit_begin + (uint64_t)g * per;
+            worst = std::max<uint64_t>(worst, owner(first + per - 1) - owner(first) + 1);
+          }
+        }
+        return worst;
+      };
+      while (lg > 0 && units > 0 && max_parts() > (uint64_t)kAccMaxParts) --lg;
       if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
     }
-    const int rc = launch_units(lg, wp ? (size_t)kWpRows : (size_t)kDecodeGroupRows);
+    const int rc = launch_units(lg, wp ? (size_t)kWpRows : 0);
     if (rc != BSL_OK) return rc;
     e = wp ? launch_decode_wp(args, 1, stream) : launch_decode_m1(args, stream);
     if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
@@ -914,6 +947,7 @@ void bsl_destroy(bsl_stack* s) {
   if (s->zero_page) (void)hipFree(s->zero_page);
   if (s->pieces) (void)hipFree(s->pieces);
   if (s->arrivals) (void)hipFree(s->arrivals);
+  if (s->acc64) (void)hipFree(s->acc64);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);
   for (int k = 0; k < 2; ++k) {

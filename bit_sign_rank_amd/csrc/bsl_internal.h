@@ -77,7 +77,9 @@ struct GroupArgs {
   int32_t grid_log2;     // single-token path: log2 of the (power-of-two) grid
   const void* zero_page; // kZeroPageBytes of zeros: target of prefetches past the end of the work
   float* pieces;         // single-/few-token path: [total_groups + workers][piece] partial sums (workspace)
-  uint32_t* arrivals;    // single-token path: [total_groups] counters, zero between launches (workspace)
+  uint32_t* arrivals;    // wave-private path: [total_groups] counters, zero between launches (workspace)
+  uint64_t* acc;         // shared-operand single-token path: [total_groups][1024] row accumulators,
+                         // zero between launches (workspace)
 };
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
@@ -90,13 +92,15 @@ int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t
 
 // Single-token path: rows are taken in row groups of 64 tiles (1024 rows), one
 // persistent 16-wave workgroup per CU.  A workgroup walks an equal share of the (row
-// group, block, chunk) units and stores one 1024-float "piece" of partial sums per row
-// group it touches; the last workgroup to finish a row group adds its pieces in a fixed
-// order.
+// group, block, chunk) units and adds its share of every row of a row group it touches to
+// that row's 64-bit accumulator; the workgroup that completes a row writes y.
 constexpr int kDecodeGroupTiles = 64;
 constexpr int kDecodeWaves = 16;
 constexpr int kDecodeGroupRows = kDecodeGroupTiles * 16;
 constexpr int kZeroPageBytes = 65536;
+// Workgroups that may share one row group of the single-token kernel: the row
+// accumulators count them in 6 bits (the host shrinks the grid to stay within this).
+constexpr int kAccMaxParts = 63;
 constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCDs
 // Single-token path, wave-private kernel: one worker per wave, four waves per workgroup
 // (one per SIMD), one workgroup per CU; units of 16 row tiles (256 rows).  A workgroup

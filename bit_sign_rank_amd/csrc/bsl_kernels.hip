@@ -227,6 +227,34 @@ __device__ __forceinline__ uint32_t count_arrival(uint32_t* ctr) {
   return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Row accumulators of the single-token kernel: one 64-bit word per output row of a
+// launch, zero between launches.  Bits 63..58 count the workgroups that have added their
+// share of the row, bits 57..0 hold the sum of their shares in fixed point with 28
+// fraction bits, each share biased by 2^51 so that the field only grows.  A workgroup
+// adds its share with one atomic add that returns the previous word; the one whose add
+// completes the count holds the whole sum, writes y and clears the word.  Integer
+// addition is associative, so the result does not depend on the order of arrival.  A
+// share is rounded to a multiple of 2^-28 (exact for every share that is a multiple of
+// 2^-28 below 2^23, such as the integer-valued checks) and clamped to |share| < 2^23.
+// At most kAccMaxParts workgroups share a row (the host keeps the grid within that), so
+// the count and the biased sum (below 63 * 2^52 < 2^58) never overflow their fields.
+constexpr int kAccCountShift = 58;
+static_assert(kAccMaxParts < (1 << (64 - kAccCountShift)) && kAccMaxParts * (2ull << 51) < (1ull << kAccCountShift), "row accumulator fields");
+constexpr int kAccFracBits = 28;
+constexpr uint64_t kAccBias = 1ull << 51;
+constexpr uint64_t kAccSumMask = (1ull << kAccCountShift) - 1;
+__device__ __forceinline__ uint64_t acc_share(float v) {
+  const double q = rint((double)v * (double)(1ull << kAccFracBits));
+  const double lim = (double)(kAccBias - 1);
+  const int64_t qi = (int64_t)fmin(fmax(q, -lim), lim);  // (NaN becomes 0)
+  return (1ull << kAccCountShift) + (uint64_t)(qi + (int64_t)kAccBias);
+}
+__device__ __forceinline__ uint32_t acc_count(uint64_t w) { return (uint32_t)(w >> kAccCountShift); }
+__device__ __forceinline__ float acc_value(uint64_t w) {
+  const int64_t sum = (int64_t)(w & kAccSumMask) - (int64_t)(acc_count(w) * kAccBias);
+  return (float)((double)sum * (1.0 / (double)(1ull << kAccFracBits)));
+}
+
 // Pick the descriptor of the weight that owns `item` (uniform across the wave).
 __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int item) {
   WeightDesc W = args.w[0];
@@ -248,10 +276,10 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 // two planes), accumulating P over the chunks of a block in registers.  After a block's
 // last chunk (or the end of the range) P is weighted by U (the r-sum is linear, so a
 // block split over two workgroups is fine); after a row group's last unit (or the end
-// of the range) each wave sums its
-// tiles over r and stores the workgroup's 1024-row "piece" of the row group.  At the end
-// of its range the workgroup counts itself in for every row group it touched; the last
-// workgroup to arrive at a row group adds its pieces in workgroup order and writes y.
+// of the range) each wave sums its tiles over r and adds the workgroup's share of each
+// row to the row's fixed-point accumulator (acc_share); the workgroup whose add completes
+// a row's count writes that row of y.  So the end of a range costs one atomic round trip,
+// and the result does not depend on which workgroup arrives last.
 //
 // Sign tiles are fetched one unit ahead, V fragments and activations two units ahead and
 // U fragments one unit ahead, across block, row-group and weight boundaries, so the HBM
@@ -475,18 +503,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       acc[k] = (float4v){0.f, 0.f, 0.f, 0.f};
     }
   };
-  // After a row group: this workgroup's piece of it, summed over r.  Stored write-through
-  // at device scope: the workgroup that adds the pieces may sit on another XCD.
+  // After a row group: this workgroup's share of each of its rows, summed over r, added
+  // to the row's accumulator; the workgroup that completes a row's count writes y.
   const int rsel = reduced_row(lane);
-  auto store_piece = [&](const DecodeCursor& c) {
+  // workgroup that owns unit u
+  auto owner = [&](uint32_t u) {
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < G && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  auto add_shares = [&](const DecodeCursor& c) {
     const uint32_t item = c.rg_begin + c.rg;
-    float* piece = args.pieces + (size_t)(item + L) * kDecodeGroupRows;
+    // workgroups that share this row group: the owners of its first and last unit and all between
+    const uint32_t first = args.w[c.j].unit_begin + (uint32_t)c.rg * (uint32_t)(c.nch * c.nb);
+    const uint32_t parts = owner(first + (uint32_t)(c.nch * c.nb) - 1) - owner(first) + 1;
+    uint64_t* words = args.acc + (size_t)item * kDecodeGroupRows;
+    void* y = args.w[c.j].y;
+    const int m = args.w[c.j].m;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
       const float v = reduce_columns(accl[wave][t][lane], lane);
       accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
-      if ((lane & 3) == 0)
-        __hip_atomic_store(&piece[(wave * R + t) * kTileRows + rsel], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int rr = (wave * R + t) * kTileRows + rsel;
+      const int row = c.rg * kDecodeGroupRows + rr;
+      if ((lane & 3) == 0 && row < m) {
+        const uint64_t share = acc_share(v);
+        const uint64_t now = __hip_atomic_fetch_add(&words[rr], share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + share;
+        if (acc_count(now) == parts) {
+          store_y(y, row, acc_value(now), args.y_fp32);
+          __hip_atomic_store(&words[rr], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
     }
   };
 
@@ -581,7 +629,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     __builtin_amdgcn_sched_barrier(0);
     if (block_end(c0)) weight_block();
     __builtin_amdgcn_sched_barrier(0);
-    if (group_end(c0)) store_piece(c0);
+    if (group_end(c0)) add_shares(c0);
     load_u(p1);
     c0 = c1;
     c1 = c2;
@@ -591,83 +639,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   };
 
   const uint32_t n = u_end - u_begin;
-  const uint32_t item_first = c0.rg_begin + c0.rg;
   for (uint32_t s = 0; s < n; s += 2) {
     step(sgn[0], 0);
     if (s + 1 < n) step(sgn[1], 1);
-  }
-
-  // ---- end of the range: count this workgroup in for every row group it touched; the
-  // last one to arrive at a row group adds the pieces (one per workgroup owner(first) ..
-  // owner(last), in that order) and writes y.
-  __shared__ uint32_t last_items[kDecodeGroupRows];
-  __shared__ uint32_t n_last;
-  const uint32_t tid = threadIdx.x;
-  auto owner = [&](uint32_t u) {
-    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
-    while (o + 1 < G && range_start(o + 1, U, lg) <= u) ++o;
-    while (range_start(o, U, lg) > u) --o;
-    return o;
-  };
-  // global row group -> its weight slot and its first and last unit
-  auto group_units = [&](uint32_t item, uint32_t& first, uint32_t& last) {
-    int j = 0;
-    while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
-    const WeightDesc& W = args.w[j];
-    const uint32_t per_rg = (uint32_t)W.nblocks * W.nch;
-    first = W.unit_begin + (item - W.rg_begin) * per_rg;
-    last = first + per_rg - 1;
-    return j;
-  };
-  // row group of the range's last unit
-  int je = 0;
-  while (je + 1 < args.count && u_end - 1 >= args.w[je + 1].unit_begin) ++je;
-  const uint32_t item_last = args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
-  publish_partials();  // this wave's pieces are visible before any arrival is counted
-  __syncthreads();
-  // row groups of the range, NW * 64 at a time: one thread each counts the workgroup in
-  for (uint32_t k0 = 0; k0 <= item_last - item_first; k0 += NW * 64) {
-    if (tid == 0) n_last = 0;
-    __syncthreads();
-    if (k0 + tid <= item_last - item_first) {
-      const uint32_t item = item_first + k0 + tid;
-      uint32_t first, last;
-      const int j = group_units(item, first, last);
-      // (row groups of a weight without blocks lie between those of its neighbours in
-      // the launch; they have no units and no pieces: y = 0 is written at the start)
-      const bool has_units = args.w[j].units != 0;
-      const uint32_t expected = has_units ? owner(last) - owner(first) + 1 : 0u;
-      const uint32_t seen =
-          has_units ? count_arrival(&args.arrivals[item]) + 1 : 0u;
-      if (has_units && seen == expected) {
-        __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_items[atomicAdd(&n_last, 1u)] = item;
-      }
-    }
-    __syncthreads();
-    const uint32_t nl = n_last;
-    for (uint32_t k = 0; k < nl; ++k) {
-      const uint32_t item = __builtin_amdgcn_readfirstlane(last_items[k]);
-      uint32_t first, last;
-      const int j = group_units(item, first, last);
-      const WeightDesc& W = args.w[j];
-      const uint32_t o0 = owner(first), o1 = owner(last);
-      for (uint32_t rr = tid; rr < (uint32_t)kDecodeGroupRows; rr += NW * 64) {
-        const float* base = args.pieces + (size_t)item * kDecodeGroupRows + rr;
-        float acc_y = 0.f;
-        for (uint32_t o = o0; o <= o1; o += 32) {  // (32 loads in flight per round trip)
-          float v[32];
-#pragma unroll
-          for (int q = 0; q < 32; ++q)
-            v[q] = __hip_atomic_load(base + (size_t)min(o + q, o1) * kDecodeGroupRows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int q = 0; q < 32; ++q) acc_y += o + q <= o1 ? v[q] : 0.f;
-        }
-        const int row = (int)(item - W.rg_begin) * kDecodeGroupRows + rr;
-        if (row < W.m) store_y(W.y, row, acc_y, args.y_fp32);
-      }
-    }
-    __syncthreads();  // n_last and last_items are rewritten by the next batch
   }
 }
 

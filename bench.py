@@ -51,9 +51,15 @@ def block_bytes(m: int, d: int) -> int:
 
 
 class Layers:
-    """One bitstack stack holding `layers` copies of a decoder layer's linears."""
+    """One bitstack stack holding `layers` copies of a decoder layer's linears.
 
-    def __init__(self, bsl, torch, shapes, counts, layers, seed, M, path=None, decode=None):
+    Every layer gets its own device blocks.  With `shared_sources` the host blocks of a
+    weight shape are drawn once (as many as the largest count needs) and every layer loads
+    its own count of them into its own slots, so large stacks are built without holding
+    every layer's blocks on the host; layers are then loaded `batch` at a time."""
+
+    def __init__(self, bsl, torch, shapes, counts, layers, seed, M, path=None, decode=None, shared_sources=False,
+                 batch=8):
         self.bsl, self.torch = bsl, torch
         self.shapes = shapes
         self.layers = layers
@@ -65,15 +71,26 @@ class Layers:
             bsl.bsl_set_path(self.h, path)
         if decode is not None:
             bsl.bsl_set_decode(self.h, decode)
-        self.counts = []
-        for l in range(layers):
-            for j, (_, m, d) in enumerate(shapes):
-                n = int(counts[l][j])
-                blocks = synth.synthetic_blocks(seed, m, d, n, 16, l, j)
-                bsl.bsl_set_source(self.h, l * self.per + j, blocks)
-                self.counts.append(n)
-            log(f"  generated layer {l + 1}/{layers}")
-        bsl.bsl_load_blocks(self.h, self.counts, 0)
+        self.counts = [int(counts[l][j]) for l in range(layers) for j in range(self.per)]
+        loaded = [0] * (layers * self.per)
+        if shared_sources:
+            nmax = [max(int(counts[l][j]) for l in range(layers)) for j in range(self.per)]
+            src = [synth.synthetic_blocks(seed, m, d, nmax[j], 16, 0, j) for j, (_, m, d) in enumerate(shapes)]
+            for l0 in range(0, layers, batch):
+                for l in range(l0, min(layers, l0 + batch)):
+                    for j in range(self.per):
+                        bsl.bsl_set_source(self.h, l * self.per + j, src[j])
+                        loaded[l * self.per + j] = self.counts[l * self.per + j]
+                bsl.bsl_load_blocks(self.h, loaded, 0)
+                log(f"  loaded layers {l0 + 1}..{min(layers, l0 + batch)}/{layers}")
+        else:
+            for l in range(layers):
+                for j, (_, m, d) in enumerate(shapes):
+                    n = self.counts[l * self.per + j]
+                    blocks = synth.synthetic_blocks(seed, m, d, n, 16, l, j)
+                    bsl.bsl_set_source(self.h, l * self.per + j, blocks)
+                log(f"  generated layer {l + 1}/{layers}")
+            bsl.bsl_load_blocks(self.h, self.counts, 0)
         # the host copies are no longer needed once loaded
         for key in [k for k in bsl._sources if k[0] == self.h]:
             del bsl._sources[key]
@@ -140,36 +157,50 @@ def time_steps(torch, layers: Layers, steps: int, warmup: int):
     return wall, kern_ms, total_bytes, total_flops
 
 
-def cpu_baseline(seed: int, layers: int = 4) -> dict:
+def cpu_baseline(seed: int, layers: int = 4, single_layers: int = 1) -> dict:
     """The oracle, untouched, on a bounded sample of the decode workload: `layers`
     distinct 8B-shaped layers (all seven linears each) with n = 8 and M = 1, i.e.
-    `layers` steps of the GPU benchmark (about 10-30 s of CPU work)."""
+    `layers` steps of the GPU benchmark (about 10-30 s of CPU work) with the BLAS library's
+    own threads (one per host core the process may use), and `single_layers` more with
+    BLAS limited to one thread."""
     import oracle
 
     try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    total_bytes = 0
-    elapsed = 0.0
-    for l in range(layers):
-        for j, (_, m, d) in enumerate(synth.LLAMA3_8B_LAYER):
-            blocks = synth.synthetic_blocks(seed, m, d, 8, 16, 99, l, j)
-            x = synth.activations(seed + 1, 1, d, 99, l, j)
-            t0 = time.perf_counter()
-            oracle.forward(x, blocks, 8)
-            elapsed += time.perf_counter() - t0
-            total_bytes += 8 * block_bytes(m, d)
-    return {
-        "value": round(total_bytes / elapsed / 1e9, 4),
+        threadpool_info = threadpool_limits = None
+    host_cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]) \
+        if threadpool_info else host_cores
+
+    def run(n_layers, tag):
+        total_bytes, elapsed = 0, 0.0
+        for l in range(n_layers):
+            for j, (_, m, d) in enumerate(synth.LLAMA3_8B_LAYER):
+                blocks = synth.synthetic_blocks(seed, m, d, 8, 16, tag, l, j)
+                x = synth.activations(seed + 1, 1, d, tag, l, j)
+                t0 = time.perf_counter()
+                oracle.forward(x, blocks, 8)
+                elapsed += time.perf_counter() - t0
+                total_bytes += 8 * block_bytes(m, d)
+        return total_bytes, elapsed
+
+    tb, el = run(layers, 99)
+    out = {
+        "value": round(tb / el / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(cores),
+        "cores": int(blas_threads),
+        "host_cores": int(host_cores),
         "kind": "oracle",
         "sample": f"{layers} Llama-3-8B-shaped layers (7 linears each), n=8, M=1: fp64 reconstruct-then-matmul per linear",
-        "seconds": round(elapsed, 2),
+        "seconds": round(el, 2),
     }
+    if threadpool_limits and single_layers > 0:
+        with threadpool_limits(limits=1, user_api="blas"):
+            tb1, el1 = run(single_layers, 98)
+        out["one_thread"] = {"value": round(tb1 / el1 / 1e9, 4), "unit": "GB/s", "cores": 1, "seconds": round(el1, 2),
+                             "sample": f"{single_layers} Llama-3-8B-shaped layer(s), n=8, M=1, BLAS limited to one thread"}
+    return out
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_m1_kernel_llama3_8b_layer_traffic.txt")
@@ -409,19 +440,26 @@ def main() -> None:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-svd", action="store_true", help="skip the equal-size vanilla-SVD decode baseline")
-    ap.add_argument("--no-few", action="store_true", help="skip the few-token (M = 2, 4) decode runs")
+    ap.add_argument("--no-few", action="store_true", help="skip the few-token (M = 2, 3, 4) decode runs")
     ap.add_argument("--decode", choices=["auto", "shared", "private"], default="auto",
                     help="single-token kernel of the headline (auto: the shared-operand kernel)")
-    ap.add_argument("--sweep", action="store_true", help="also run variable block counts at M = 1, 4, 16")
-    ap.add_argument("--llama70b", action="store_true", help="also run the 80-layer 70B-shaped decode stack")
+    ap.add_argument("--no-sweep", action="store_true", help="skip variable block counts at M = 1, 4, 16")
+    ap.add_argument("--no-70b", action="store_true", help="skip the 80-layer 70B-shaped decode stack")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM / matrix-core peaks")
+    ap.add_argument("--no-load", action="store_true", help="skip host -> device block streaming")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="only the kernels the committed profiles cover: the decode headline, the few-token kernel at "
+                         "M = 4 and the tile-path prefill, plus a 1 GiB copy for counter calibration")
     ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--load", action="store_true", help="also measure host -> device block streaming, alone and beside decode")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--write-profile-summaries", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
                     help="write profiles/ summaries from rocprofv3 outputs (no GPU work)")
     args = ap.parse_args()
+    if args.profile_set:
+        args.no_cpu = args.no_svd = args.no_sweep = args.no_70b = args.no_load = args.no_peaks = True
+        args.calibrate_copy = True
     if args.write_profile_summaries:
         write_profile_summaries(*args.write_profile_summaries)
         return
@@ -522,28 +560,85 @@ def main() -> None:
         result["decode_single_weight_launches"] = per_weight
     result["decode_other_kernel"] = other
 
+    # ---------------- measured peaks of this GPU (the roofline fractions are also given against them)
+    if not args.no_peaks:
+        from bit_sign_rank_amd import peaks as _peaks
+
+        log("peaks: HBM read / copy, matrix-core loops")
+        pk = _peaks.measure(torch, dev.multi_processor_count, reps=10, gib=1.0)
+        result["measured_peaks"] = {
+            "hbm_read_GBs": pk["hbm_read_GBs"],
+            "hbm_copy_GBs": pk["hbm_copy_GBs"],
+            "fp16_dense_mfma_tflops": pk["mfma_v_mfma_f32_16x16x32_f16"]["tflops"],
+            "fp16_dense_mfma_clock_ghz": round(pk["mfma_v_mfma_f32_16x16x32_f16"]["clock_ghz"] or 0, 3),
+            "sparse_mfma_tflops": pk["mfma_v_smfmac_f32_16x16x64_f16"]["tflops"],
+            "sparse_mfma_decode_operands_with_sign_stream": {
+                k: pk["sparse_mfma_lds_r4_mode1_stream"][k] for k in ("tflops", "stream_GBs", "clock_ghz")},
+            "note": "bench_peaks kernels (libbsl_peaks.so): grid-stride non-temporal 16-byte loads of 1 GiB; "
+                    "16 independent MFMA chains per wave, 4 waves per SIMD; the last line is the sparse MFMA with "
+                    "A = 1, B random fp16 from LDS and a matched 1 KiB-per-16-MFMA HBM stream (the single-token "
+                    "kernel's operand profile and byte rate)",
+        }
+        rf = result["roofline"]
+        rf["frac_of_measured_read_peak"] = round(rf["achieved"] / pk["hbm_read_GBs"], 4)
+        torch.cuda.empty_cache()
+
+    # ---------------- resident bytes against the blocks' payload (one 8B-shaped layer, n = 8)
+    probe = bsl.bsl_init(0, [m for _, m, _ in shapes], [d for _, _, d in shapes], 16, 16, 0)
+    for j, (_, m, d) in enumerate(shapes):
+        bsl.bsl_set_source(probe, j, synth.synthetic_blocks(args.seed + 61, m, d, 8, 16, j))
+    bsl.bsl_load_blocks(probe, [8] * 7, 0)
+    payload = sum(8 * block_bytes(m, d) for _, m, d in shapes)
+    resident = bsl.bsl_resident_bytes(probe)
+    result["resident_bytes"] = {"workload": "one Llama-3-8B-shaped layer, n=8", "payload_bytes": payload,
+                                "resident_bytes": int(resident), "ratio": round(resident / payload, 4)}
+    torch.cuda.synchronize()
+    bsl.bsl_destroy(probe)
+    for key in [k for k in bsl._sources if k[0] == probe]:
+        del bsl._sources[key]
+
+    # ---------------- 1024 x 1024, n = 4, M = 1 (the parity workload's shape; launch-bound)
+    c1 = Layers(bsl, torch, [("w", 1024, 1024)], [[4]] * 64, 64, args.seed + 71, M=1)
+    w1, k1, b1, _ = time_steps(torch, c1, 640, 64)
+    result["single_1024x1024_n4_decode"] = {
+        "workload": "one 1024x1024 linear, n=4 blocks (k=16), M=1, 64 resident copies rotated; blocks synthetic of the "
+                    "decomposed shape (the CPU decomposition is not on the timed path)",
+        "us_per_launch": round(float(np.mean(k1)) * 1e3, 2), "bytes_per_launch": c1.bytes(0)}
+    c1.close()
+    del c1
+    torch.cuda.empty_cache()
+
     # ---------------- prefill M = 2048: tile path (the default for batches), then factored
     # ---------------- a few tokens (batched decode): the wave-private kernel over T tokens
     if not args.no_few:
         few = []
-        for M in (2, 4):
-            row = {"M": M}
-            for name, path in (("auto", bsl.BSL_PATH_AUTO), ("factored", bsl.BSL_PATH_FACTORED)):
-                log(f"few tokens: 8B-shaped layer, n=8, M={M}, {name} path")
-                lay = Layers(bsl, torch, shapes, [[8] * 7] * 2, 2, args.seed + 5, M=M, path=path)
-                w_, k_, b_, _ = time_steps(torch, lay, 100, 10)
-                row[f"{name}_us_per_step"] = round(w_ * 1e6 / 100, 1)
-                row[f"{name}_kernel_us"] = round(float(np.mean(k_)) * 1e3, 1)
-                row[f"{name}_GB_per_s"] = round(b_ / w_ / 1e9, 1)
-                lay.close()
-                del lay
-                torch.cuda.empty_cache()
-            row["kernel"] = "decode_wp_kernel<8, 2>" if M == 2 else "decode_wp_kernel<4, 4>"
-            row["speedup_vs_factored"] = round(row["factored_us_per_step"] / row["auto_us_per_step"], 2)
-            few.append(row)
-            log(f"few tokens M={M}: {row}")
+        kern = {2: "decode_wp_kernel<8, 2>", 3: "decode_wp_kernel<4, 3>", 4: "decode_wp_kernel<4, 4>"}
+        sets = (("8B", shapes, [8] * 7), ("70B", synth.LLAMA2_70B_LAYER, [3] * 7))
+        for label, lshapes, counts in (sets[:1] if args.profile_set else sets):
+            for M in ((4,) if args.profile_set else (2, 3, 4)):
+                row = {"layer": label, "n": counts[0], "M": M}
+                for name, path in (("auto", bsl.BSL_PATH_AUTO), ("factored", bsl.BSL_PATH_FACTORED)):
+                    log(f"few tokens: {label}-shaped layer, n={counts[0]}, M={M}, {name} path")
+                    lay = Layers(bsl, torch, lshapes, [counts] * 2, 2, args.seed + 5, M=M, path=path, shared_sources=True)
+                    w_, k_, b_, f_ = time_steps(torch, lay, 60, 6)
+                    row[f"{name}_us_per_step"] = round(w_ * 1e6 / 60, 1)
+                    row[f"{name}_kernel_us"] = round(float(np.mean(k_)) * 1e3, 1)
+                    if name == "auto":
+                        kus = float(np.mean(k_)) * 1e-3
+                        row["sz_flops_per_step"] = int(f_ // 60)
+                        row["mfma_tflops"] = round(f_ / 60 / kus / 1e12, 1)
+                        row["mfma_frac_of_peak"] = round(f_ / 60 / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)
+                        row["GB_per_s"] = round(b_ / 60 / kus / 1e9, 1)
+                    lay.close()
+                    del lay
+                    torch.cuda.empty_cache()
+                row["kernel"] = kern[M] + ("" if label == "8B" or M == 2 else " (down projection: prefill_kernel, second launch)")
+                row["speedup_vs_factored"] = round(row["factored_kernel_us"] / row["auto_kernel_us"], 2)
+                few.append(row)
+                log(f"few tokens: {row}")
         result["few_token_decode"] = {
-            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M tokens per grouped launch, 2 rotated layers",
+            "workload": "decoder-layer linears (Llama-3-8B shapes at n=8; Llama-2-70B shapes at n=3), k=16, M tokens per "
+                        "grouped launch, 2 rotated layers; MFMA work = the S Z contraction 2 n k M m d",
             "runs": few}
 
     if not args.no_prefill:
@@ -569,6 +664,7 @@ def main() -> None:
         pre.close()
         del pre
         torch.cuda.empty_cache()
+    if not args.no_prefill and not args.profile_set:
         log("prefill: one 8B-shaped layer, n=8, M=2048, factored path")
         pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_FACTORED)
         wall_p, kms_p, tb_p, tf_p = time_steps(torch, pre, args.prefill_steps, 1)
@@ -598,32 +694,63 @@ def main() -> None:
         log(f"equal-size SVD baseline: {r['us_per_step']} us/step, {r['GB_per_s']} GB/s")
         torch.cuda.empty_cache()
 
-    # ---------------- optional sweeps
-    if args.sweep:
+    # ---------------- variable block counts (n_w drawn in 1..16), M = 1, 4, 16
+    if not args.no_sweep:
         sweep = []
         counts = synth.block_counts(13, 7, 1, 16)
         for M in (1, 4, 16):
-            lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M)
-            w_, k_, b_, f_ = time_steps(torch, lay, 50, 5)
-            sweep.append({"M": M, "n_w": [int(c) for c in counts], "GB/s": round(b_ / w_ / 1e9, 1),
-                          "path": "single-token" if M == 1 else ("tile" if M >= 5 else "few-token"),
-                          "sz_equivalent_tflops": round(f_ / w_ / 1e12, 1), "us_per_step": round(w_ * 1e6 / 50, 1)})
+            lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M, shared_sources=True)
+            steps = 100 if M < 16 else 50
+            w_, k_, b_, f_ = time_steps(torch, lay, steps, 5)
+            kus = float(np.mean(k_)) * 1e-3
+            row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
+                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel)" if M >= 5 else "few-token (decode_wp_kernel<4, 4>)"),
+                   "bytes_per_step": lay.bytes(0), "GB_per_s": round(lay.bytes(0) / kus / 1e9, 1)}
+            if M == 1:
+                row["roofline"] = {"bound": "hbm", "achieved": row["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(row["GB_per_s"] / HBM_PEAK_GBS, 4)}
+            else:
+                fl = lay.tile_flops(0) if M >= 5 else lay.flops(0)
+                row["roofline"] = {"bound": "mfma", "achieved": round(fl / kus / 1e12, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(fl / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                                   "flops": "executed MFMA work of the path: " + ("(2 k n G + 2 M) m d, G = ceil(M/512)" if M >= 5 else "2 n k M m d")}
+            sweep.append(row)
             lay.close()
             del lay
             torch.cuda.empty_cache()
-            log(f"sweep M={M}: {sweep[-1]}")
-        result["variable_blocks_sweep"] = sweep
-    if args.llama70b:
+            log(f"sweep M={M}: {row}")
+        result["variable_blocks_sweep"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n_w drawn in 1..16 per weight (seeded), k=16, 2 rotated layers, "
+                        "M tokens per grouped launch", "runs": sweep}
+    # ---------------- 80-layer Llama-2-70B-shaped stack, n_w drawn in 1..6, M = 1
+    if not args.no_70b:
         counts = [synth.block_counts(18, 7, 1, 6, l) for l in range(synth.LLAMA2_70B_LAYERS)]
-        log("llama70b: building 80 layers (this takes a while)")
-        lay = Layers(bsl, torch, synth.LLAMA2_70B_LAYER, counts, synth.LLAMA2_70B_LAYERS, args.seed + 21, M=1)
-        w_, k_, b_, f_ = time_steps(torch, lay, synth.LLAMA2_70B_LAYERS * 3, synth.LLAMA2_70B_LAYERS)
-        tok_ms = w_ * 1e3 / 3
-        result["llama2_70b_decode"] = {"ms_per_token": round(tok_ms, 3), "GB/s": round(b_ / w_ / 1e9, 1),
-                                       "bytes_per_token": int(b_ // 3)}
+        log("llama70b: building 80 layers (device copies of shared host blocks, 8 layers per load)")
+        lay = Layers(bsl, torch, synth.LLAMA2_70B_LAYER, counts, synth.LLAMA2_70B_LAYERS, args.seed + 21, M=1,
+                     shared_sources=True, batch=8)
+        tokens = 3
+        w_, k_, b_, f_ = time_steps(torch, lay, synth.LLAMA2_70B_LAYERS * tokens, synth.LLAMA2_70B_LAYERS)
+        tok_us = float(np.mean(k_)) * 1e-3 * synth.LLAMA2_70B_LAYERS
+        per_token = sum(lay.bytes(l) for l in range(synth.LLAMA2_70B_LAYERS))
+        nsum = sum(int(c) for cc in counts for c in cc)
+        result["llama2_70b_decode"] = {
+            "workload": "80 Llama-2-70B-shaped decoder layers (q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192, "
+                        f"down 8192x28672), n_w drawn in 1..6 per weight (mean {nsum / 560:.2f}), k=16, M=1, one grouped "
+                        "launch per layer, 80 launches per token; all 80 layers resident",
+            "ms_per_token": round(tok_us * 1e3, 3),
+            "bytes_per_token": per_token,
+            "GB_per_s": round(per_token / tok_us / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(per_token / tok_us / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(per_token / tok_us / 1e9 / HBM_PEAK_GBS, 4)},
+            "resident_bytes": int(bsl.bsl_resident_bytes(lay.h)),
+            "wall_ms_per_token": round(w_ * 1e3 / tokens, 3),
+        }
+        log(f"llama70b: {result['llama2_70b_decode']}")
         lay.close()
+        del lay
+        torch.cuda.empty_cache()
 
-    if args.load:
+    if not args.no_load:
         log("block streaming: loading an 8B-shaped layer, alone and beside decode")
         result["block_streaming"] = block_streaming(bsl, torch, args.seed + 31)
         log(f"block streaming: {result['block_streaming']}")

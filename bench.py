@@ -228,59 +228,132 @@ def measured_traffic():
     return int(fields["hbm_bytes_per_launch"])
 
 
-def write_profile_summaries(trace_dir: str, fetch_dir: str, write_dir: str, command: str) -> None:
-    """Turn rocprofv3 outputs (kernel-trace --stats of a bench run, then one --pmc
-    FETCH_SIZE and one --pmc WRITE_SIZE pass of a bench run with --calibrate-copy) into
-    the short text summaries kept under profiles/."""
+PROFILE_KERNELS = (
+    # (label, kernel name prefix, grid size of the profiled launch or None, algorithmic flops per launch)
+    ("decode_m1_kernel (8B-shaped layer, n=8, M=1)", "void bsl::decode_m1_kernel", 256 * 1024,
+     sum(2 * 8 * K_RANK * 1 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
+    ("decode_wp_kernel<4, 4> (8B-shaped layer, n=8, M=4)", "void bsl::decode_wp_kernel<4, 4>", None,
+     sum(2 * 8 * K_RANK * 4 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
+    ("tile_kernel (8B-shaped layer, n=8, M=2048)", "void bsl::tile_kernel", None,
+     sum((2 * K_RANK * 8 * 4 + 2 * 2048) * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
+)
+
+
+def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_dir: str, write_dir: str,
+                            command: str) -> None:
+    """Turn rocprofv3 outputs of `bench.py --profile-set` runs (one --kernel-trace --stats
+    run, two --pmc passes of SQ counters, one FETCH_SIZE and one WRITE_SIZE pass) into the
+    short text summaries kept under profiles/."""
     import csv
     import glob
     import hashlib
+    import statistics
 
-    def one(pattern):
-        files = glob.glob(os.path.join(pattern))
-        assert files, pattern
+    def one(d, suffix):
+        files = glob.glob(os.path.join(d, "*" + suffix))
+        assert files, (d, suffix)
         return files[0]
 
+    def pick(name, grid, want_name, want_grid):
+        return name.startswith(want_name) and (want_grid is None or int(grid) == want_grid)
+
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    stats = list(csv.DictReader(open(one(os.path.join(trace_dir, "*kernel_stats.csv")))))
-    lines = [f"# rocprofv3 --kernel-trace --stats, Llama-3-8B-shaped layer (n=8, k=16): decode M=1 and prefill M=2048",
-             f"command: {command.split(';')[0]}",
-             "", f"{'kernel':58s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
-    for r in stats:
-        lines.append(f"{r['Name'][:58]:58s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+    with open(KERNEL_SOURCE, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    cmd = command.split(";")
+    # --- kernel trace: durations per (kernel, grid)
+    durs = {}
+    for r in csv.DictReader(open(one(trace_dir, "kernel_trace.csv"))):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0))
+        durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["# rocprofv3 --kernel-trace --stats of bench.py --profile-set (Llama-3-8B-shaped layer, n=8, k=16):",
+             "# decode M=1 (both single-token kernels), few-token M=4, tile-path prefill M=2048",
+             f"command: {cmd[0].strip()}", f"kernel_source_sha256: {digest}", "",
+             f"{'kernel':58s} {'grid':>8s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
+    for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        if not name.startswith("void bsl::"):
+            continue
+        lines.append(f"{name[:58]:58s} {grid:8d} {len(v):6d} {statistics.mean(v):10.2f} {min(v):10.2f} {max(v):10.2f}")
     with open(os.path.join(ROOT, "profiles", "kernel_stats_llama3_8b_layer.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    def counters(d, name):
+    # --- counters: median per dispatch, per kernel of interest
+    def counters(d):
         vals = {}
-        for r in csv.DictReader(open(one(os.path.join(d, "*counter_collection.csv")))):
-            if r["Counter_Name"] == name:
-                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        for r in csv.DictReader(open(one(d, "counter_collection.csv"))):
+            key = (r["Kernel_Name"], int(r["Grid_Size"]))
+            e = vals.setdefault(key, {})
+            e.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            e.setdefault("_dur_us", {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         return vals
 
-    fetch, write = counters(fetch_dir, "FETCH_SIZE"), counters(write_dir, "WRITE_SIZE")
-    copy_name = next(k for k in fetch if "neg_kernel" in k)  # the torch.neg copy of copy_calibration()
-    dec_name = next(k for k in fetch if "decode_m1_kernel" in k)
-    med = lambda v: sorted(v)[len(v) // 2]
+    med = statistics.median
+    c1, c2 = counters(sq1_dir), counters(sq2_dir)
+    out = ["# rocprofv3 --pmc SQ counters, two passes of bench.py --profile-set; medians per dispatch.",
+           "# SQ counters are sums over the 32 shader engines (8 XCDs); the shader clock is SQ_BUSY_CYCLES / 32 over",
+           "# the dispatch's duration in the counter run (dispatches run one at a time there); MFMA busy is",
+           "# SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over those cycles; MFMA flops are SQ_INSTS_VALU_MFMA_MOPS_F16 * 512",
+           "# (the sparse 16x16x64 instruction counts at its dense-equivalent 32768 flops, twice the 16384 it does",
+           "# for the layer).",
+           f"pass 1: {cmd[1].strip() if len(cmd) > 1 else ''}", f"pass 2: {cmd[2].strip() if len(cmd) > 2 else ''}",
+           f"kernel_source_sha256: {digest}", ""]
+    for label, prefix, grid, algo in PROFILE_KERNELS:
+        k1 = [k for k in c1 if pick(k[0], k[1], prefix, grid)]
+        k2 = [k for k in c2 if pick(k[0], k[1], prefix, grid)]
+        if not k1 or not k2:
+            continue
+        a, b = c1[k1[0]], c2[k2[0]]
+        dur = med(list(a["_dur_us"].values()))
+        cyc = med(a["SQ_BUSY_CYCLES"]) / 32
+        clock = cyc / (dur * 1e3)
+        mfma = med(a["SQ_INSTS_MFMA"])
+        flops_ctr = med(a["SQ_INSTS_VALU_MFMA_MOPS_F16"]) * 512
+        busy = med(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024 / cyc
+        waves = med(a["SQ_WAVES"])
+        useful = flops_ctr / 2 if "decode" in prefix else flops_ctr
+        out += [f"## {label}",
+                f"dispatch duration (counter run): {dur:.1f} us over {len(a['_dur_us'])} dispatches",
+                f"shader clock: {clock:.3f} GHz",
+                f"waves: {waves:.0f}",
+                f"MFMA instructions: {mfma:.0f}",
+                f"MFMA flops from counters: {flops_ctr:.4g} (useful for the layer: {useful:.4g}; algorithmic: {algo:.4g})",
+                f"MFMA TFLOP/s (useful, counter run): {useful / dur / 1e6:.1f} = {useful / dur / 1e6 / FP16_MFMA_PEAK_TFLOPS:.3f} of {FP16_MFMA_PEAK_TFLOPS} TFLOP/s",
+                f"MFMA busy: {busy:.3f} of the SIMD cycles",
+                f"VALU instructions per wave: {med(a['SQ_INSTS_VALU']) / waves:.0f}",
+                f"LDS instructions per wave: {med(a['SQ_INSTS_LDS']) / waves:.0f}",
+                f"vector memory reads per wave: {med(b['SQ_INSTS_VMEM_RD']) / waves:.0f}",
+                f"wave cycles waiting on dependencies (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES): {med(b['SQ_WAIT_INST_ANY']) / med(b['SQ_WAVE_CYCLES']):.3f}",
+                f"VALU active / wave cycles: {med(b['SQ_ACTIVE_INST_VALU']) / med(b['SQ_WAVE_CYCLES']):.3f}",
+                f"LDS active (SQ_LDS_IDX_ACTIVE / (32 x cycles x 8 CUs)): {med(b['SQ_LDS_IDX_ACTIVE']) / (cyc * 256):.3f}",
+                f"LDS bank conflicts: {med(b['SQ_LDS_BANK_CONFLICT']):.0f}", ""]
+    with open(os.path.join(ROOT, "profiles", "sq_counters_llama3_8b_layer.txt"), "w") as f:
+        f.write("\n".join(out) + "\n")
+
+    # --- HBM traffic of the decode kernel, copy-calibrated
+    def tcc(d, name):
+        vals = {}
+        for r in csv.DictReader(open(one(d, "counter_collection.csv"))):
+            if r["Counter_Name"] == name:
+                vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = tcc(fetch_dir, "FETCH_SIZE"), tcc(write_dir, "WRITE_SIZE")
+    copy_key = next(k for k in fetch if "neg_kernel" in k[0])  # the torch.neg copy of copy_calibration()
+    dec_key = next(k for k in fetch if pick(k[0], k[1], PROFILE_KERNELS[0][1], PROFILE_KERNELS[0][2]))
     copy_bytes = 1024 * (1 << 20)  # each copy dispatch reads and writes exactly 1 GiB
-    f_copy = med(fetch[copy_name])
-    w_copy = med(write[copy_name])
-    f_scale = copy_bytes / (f_copy * 1024)
-    w_scale = copy_bytes / (w_copy * 1024)
-    f_dec = med(fetch[dec_name]) * 1024 * f_scale
-    w_dec = med(write[dec_name]) * 1024 * w_scale
-    with open(KERNEL_SOURCE, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
+    f_copy, w_copy = med(fetch[copy_key]), med(write[copy_key])
+    f_scale, w_scale = copy_bytes / (f_copy * 1024), copy_bytes / (w_copy * 1024)
+    f_dec = med(fetch[dec_key]) * 1024 * f_scale
+    w_dec = med(write[dec_key]) * 1024 * w_scale
     algo = sum(8 * block_bytes(m, d) for _, m, d in synth.LLAMA3_8B_LAYER)
     text = f"""# HBM traffic of decode_m1_kernel, one grouped launch over a Llama-3-8B-shaped layer (n=8, k=16, M=1)
-fetch command: {command.split(';')[1].strip() if ';' in command else ''}
-write command: {command.split(';')[2].strip() if command.count(';') > 1 else ''}
+fetch command: {cmd[3].strip() if len(cmd) > 3 else ''}
+write command: {cmd[4].strip() if len(cmd) > 4 else ''}
 calibration: a 1 GiB fp16 elementwise copy (torch.neg) in the same runs reads FETCH_SIZE {f_copy:.1f} KiB and writes WRITE_SIZE {w_copy:.1f} KiB per dispatch
 fetch_scale: {f_scale:.4f}
 write_scale: {w_scale:.4f}
-decode_fetch_kib_median: {med(fetch[dec_name]):.2f} over {len(fetch[dec_name])} dispatches
-decode_write_kib_median: {med(write[dec_name]):.2f} over {len(write[dec_name])} dispatches
+decode_fetch_kib_median: {med(fetch[dec_key]):.2f} over {len(fetch[dec_key])} dispatches
+decode_write_kib_median: {med(write[dec_key]):.2f} over {len(write[dec_key])} dispatches
 fetch_bytes_per_launch: {int(f_dec)}
 write_bytes_per_launch: {int(w_dec)}
 hbm_bytes_per_launch: {int(f_dec + w_dec)}
@@ -454,7 +527,8 @@ def main() -> None:
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--write-profile-summaries", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
+    ap.add_argument("--write-profile-summaries", nargs=6,
+                    metavar=("TRACE_DIR", "SQ1_DIR", "SQ2_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
                     help="write profiles/ summaries from rocprofv3 outputs (no GPU work)")
     args = ap.parse_args()
     if args.profile_set:
@@ -598,15 +672,16 @@ def main() -> None:
         del bsl._sources[key]
 
     # ---------------- 1024 x 1024, n = 4, M = 1 (the parity workload's shape; launch-bound)
-    c1 = Layers(bsl, torch, [("w", 1024, 1024)], [[4]] * 64, 64, args.seed + 71, M=1)
-    w1, k1, b1, _ = time_steps(torch, c1, 640, 64)
-    result["single_1024x1024_n4_decode"] = {
-        "workload": "one 1024x1024 linear, n=4 blocks (k=16), M=1, 64 resident copies rotated; blocks synthetic of the "
-                    "decomposed shape (the CPU decomposition is not on the timed path)",
-        "us_per_launch": round(float(np.mean(k1)) * 1e3, 2), "bytes_per_launch": c1.bytes(0)}
-    c1.close()
-    del c1
-    torch.cuda.empty_cache()
+    if not args.profile_set:
+        c1 = Layers(bsl, torch, [("w", 1024, 1024)], [[4]] * 64, 64, args.seed + 71, M=1)
+        w1, k1, b1, _ = time_steps(torch, c1, 640, 64)
+        result["single_1024x1024_n4_decode"] = {
+            "workload": "one 1024x1024 linear, n=4 blocks (k=16), M=1, 64 resident copies rotated; blocks synthetic of "
+                        "the decomposed shape (the CPU decomposition is not on the timed path)",
+            "us_per_launch": round(float(np.mean(k1)) * 1e3, 2), "bytes_per_launch": c1.bytes(0)}
+        c1.close()
+        del c1
+        torch.cuda.empty_cache()
 
     # ---------------- prefill M = 2048: tile path (the default for batches), then factored
     # ---------------- a few tokens (batched decode): the wave-private kernel over T tokens

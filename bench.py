@@ -422,7 +422,7 @@ def block_streaming(bsl, torch, seed: int) -> dict:
     dec.close()
     bsl.bsl_destroy(h)
     return {
-        "workload": "Llama-3-8B-shaped layer, 7 linears x 8 blocks (k=16), packed on the host and copied to the device",
+        "workload": "Llama-3-8B-shaped layer, 7 linears x 8 blocks (k=16): row-major sign bits copied to the device and repacked there by a kernel, factor layouts written on the host",
         "layer_bytes": layer_bytes,
         "load_ms": round(alone * 1e3, 1),
         "load_GB_per_s": round(layer_bytes / alone / 1e9, 2),

@@ -105,6 +105,22 @@ void pack_signs_mt(const uint8_t* src, int64_t m, int64_t d, uint8_t* out) {
   for (auto& t : th) t.join();
 }
 
+// memcpy in up to 8 threads (large copies into pinned staging are host-bandwidth bound)
+void copy_mt(uint8_t* dst, const uint8_t* src, size_t bytes) {
+  const size_t nt = bytes < ((size_t)8 << 20) ? 1 : 8;
+  if (nt == 1) {
+    std::memcpy(dst, src, bytes);
+    return;
+  }
+  std::vector<std::thread> th;
+  const size_t per = (bytes + nt - 1) / nt;
+  for (size_t k = 0; k < nt; ++k) {
+    const size_t a = k * per, b = std::min(bytes, a + per);
+    if (a < b) th.emplace_back([=] { std::memcpy(dst + a, src + a, b - a); });
+  }
+  for (auto& t : th) t.join();
+}
+
 // U (m x 16, row-major fp16) -> [m_pad/16][64][4]: lane L, slot v holds U[16 t + 4 (L/16) + v][L % 16].
 void tile_u(const uint16_t* u, int64_t m, uint16_t* out) {
   const int64_t mt = pad_rows(m) / kTileRows;
@@ -198,7 +214,9 @@ struct bsl_stack {
   float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
   uint8_t* staging[2] = {nullptr, nullptr};  // pinned host buffers of bsl_load_blocks (allocated on first use)
   size_t staging_bytes = 0;
-  hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] finished
+  hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] and the repack from raw_dev[k] finished
+  uint8_t* raw_dev[2] = {nullptr, nullptr};   // device buffers of row-major sign bits awaiting the repack
+  size_t raw_dev_bytes = 0;
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
   void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
   std::vector<Weight> w;
@@ -458,25 +476,37 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     undo();
     return hip_fail(e, "hipMalloc(block)");
   }
-  // phase 2: pack on the host and copy the new blocks.  Two pinned staging buffers take
-  // turns: block k is packed into one while the copy of block k - 1 runs from the other
-  // (asynchronous DMA on `stream`, so forwards queued on other streams keep running).
-  size_t need = 0;
-  for (const NewSlot& a : added) need = std::max(need, slot_bytes(s->w[a.w].m, s->w[a.w].d));
-  if (need > s->staging_bytes) {
+  // phase 2: copy the new blocks.  A block's row-major sign bits go to the device as they
+  // are and a kernel repacks them into the slot's tiled layout; the factor layouts (9% of
+  // an 8B-shaped block) are written on the host.  Two pinned staging buffers and two device
+  // buffers of raw bits take turns: block k is staged into one pair while the copies and
+  // the repack of block k - 1 run from the other (asynchronously on `stream`, so forwards
+  // queued on other streams keep running).
+  size_t need = 0, need_raw = 0;
+  for (const NewSlot& a : added) {
+    const Weight& W = s->w[a.w];
+    const size_t raw = (size_t)W.m * (W.d / 8), sb = (size_t)pad_rows(W.m) * pad_cols(W.d) / 8;
+    need = std::max(need, raw + slot_bytes(W.m, W.d) - sb);
+    need_raw = std::max(need_raw, raw);
+  }
+  if (need > s->staging_bytes || need_raw > s->raw_dev_bytes) {
     for (int k = 0; k < 2; ++k) {
       if (s->staging[k]) (void)hipHostFree(s->staging[k]);
+      if (s->raw_dev[k]) (void)hipFree(s->raw_dev[k]);
       s->staging[k] = nullptr;
+      s->raw_dev[k] = nullptr;
     }
-    s->staging_bytes = 0;
+    s->staging_bytes = s->raw_dev_bytes = 0;
     for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipHostMalloc(reinterpret_cast<void**>(&s->staging[k]), need, hipHostMallocDefault);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipMalloc(reinterpret_cast<void**>(&s->raw_dev[k]), need_raw);
     for (int k = 0; k < 2 && e == hipSuccess; ++k)
       if (!s->staged[k]) e = hipEventCreateWithFlags(&s->staged[k], hipEventDisableTiming);
     if (e != hipSuccess) {
       undo();
-      return hip_fail(e, "pinned staging buffers");
+      return hip_fail(e, "staging buffers");
     }
     s->staging_bytes = need;
+    s->raw_dev_bytes = need_raw;
   }
   std::vector<uint16_t> vscaled;  // V of a scaled weight
   NewSlot overflow = {-1, -1};
@@ -484,27 +514,41 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     const NewSlot& a = added[k];
     Weight& W = s->w[a.w];
     const bsl_block_src& src = W.src[a.i];
+    const size_t raw = (size_t)W.m * (W.d / 8);
     const size_t sb = (size_t)pad_rows(W.m) * pad_cols(W.d) / 8;
     const size_t ub = (size_t)pad_rows(W.m) * kRank * 2;
     const size_t vb = (size_t)pad_cols(W.d) * kRank * 2;
     uint8_t* buf = s->staging[k % 2];
-    if (k >= 2 && (e = hipEventSynchronize(s->staged[k % 2])) != hipSuccess) break;  // its last copy is done
-    pack_signs_mt(src.sign_bits, W.m, W.d, buf);
-    tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(buf + sb));
-    const uint16_t* v = src.v;
-    if (!W.inv_scale.empty()) {
-      vscaled.resize((size_t)W.d * kRank);
-      if (!scale_v(v, W.d, W.inv_scale.data(), vscaled.data())) {
-        overflow = a;
-        break;
+    uint8_t* fac = buf + raw;  // the factor layouts, in slot order after the signs
+    if (k >= 2 && (e = hipEventSynchronize(s->staged[k % 2])) != hipSuccess) break;  // its last copy and repack are done
+    // the factor layouts on one thread while the raw sign bits are copied on the others
+    bool scaled_ok = true;
+    std::thread factors([&] {
+      tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac));
+      rowmajor_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac + ub + 3 * vb));
+      const uint16_t* v = src.v;
+      if (!W.inv_scale.empty()) {
+        vscaled.resize((size_t)W.d * kRank);
+        if (!scale_v(v, W.d, W.inv_scale.data(), vscaled.data())) {
+          scaled_ok = false;
+          return;
+        }
+        v = vscaled.data();
       }
-      v = vscaled.data();
+      tile_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub));
+      rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub + vb));
+      bop_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub + 2 * vb));
+    });
+    copy_mt(buf, src.sign_bits, raw);
+    factors.join();
+    if (!scaled_ok) {
+      overflow = a;
+      break;
     }
-    tile_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub));
-    rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + vb));
-    bop_v(v, W.d, reinterpret_cast<uint16_t*>(buf + sb + ub + 2 * vb));
-    rowmajor_u(src.u, W.m, reinterpret_cast<uint16_t*>(buf + sb + ub + 3 * vb));
-    e = hipMemcpyAsync(W.slots[a.i].mem, buf, sb + 2 * ub + 3 * vb, hipMemcpyHostToDevice, st);
+    uint8_t* slot = static_cast<uint8_t*>(W.slots[a.i].mem);
+    e = hipMemcpyAsync(s->raw_dev[k % 2], buf, raw, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot + sb, fac, 2 * ub + 3 * vb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = static_cast<hipError_t>(launch_repack_signs(s->raw_dev[k % 2], W.m, W.d, W.mt, W.nch, slot, st));
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -953,6 +997,7 @@ void bsl_destroy(bsl_stack* s) {
   for (int k = 0; k < 2; ++k) {
     if (s->staging[k]) (void)hipHostFree(s->staging[k]);
     if (s->staged[k]) (void)hipEventDestroy(s->staged[k]);
+    if (s->raw_dev[k]) (void)hipFree(s->raw_dev[k]);
   }
   delete s;
 }

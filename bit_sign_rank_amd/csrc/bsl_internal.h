@@ -87,6 +87,9 @@ int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_decode_wp(const GroupArgs& args, int tokens, void* stream);  // tokens: 1 to 4
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream);
+// Row-major sign bits (device, m rows of d/8 bytes) -> the tiled sign layout (device, the
+// first bsl_packed_sign_bytes(m, d) bytes of a block slot).
+int launch_repack_signs(const uint8_t* raw, int64_t m, int64_t d, int32_t mt, int32_t nch, uint8_t* out, void* stream);
 int launch_debug_unpack(BlockPtrs blk, int32_t m, int32_t d, int32_t mt, int32_t nch, int path, int8_t* out,
                         void* stream);
 

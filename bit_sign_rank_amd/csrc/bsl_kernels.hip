@@ -1736,6 +1736,52 @@ __global__ __launch_bounds__(64) void debug_unpack_kernel(BlockPtrs blk, int32_t
   debug_planes(std::make_integer_sequence<int, kPlanes>{}, w, path, lane >> 4, ch, row, d, out);
 }
 
+// ============================================================ sign repack (load time)
+// Row-major sign bits (m rows of d/8 bytes, least significant bit = lowest column) into
+// the tiled layout of bsl_pack_signs, on the device: one thread per 16-byte lane word.
+// Lane L = 16 g + i of tile (chunk c, row tile t) holds row 16 t + i; its word q gathers
+// the bytes 16 q + g, 16 q + 4 + g, 16 q + 8 + g and 16 q + 12 + g of the row's 64-byte
+// segment of chunk c (planes 4 q .. 4 q + 3), each spread to every second bit and placed
+// at the odd positions of half 0 / half 1 (planes 4 q, 4 q + 1) and the even positions of
+// half 0 / half 1 (planes 4 q + 2, 4 q + 3).  Rows past m and columns past d are 0 (+1).
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+  x = (x | (x << 4)) & 0x0F0Fu;
+  x = (x | (x << 2)) & 0x3333u;
+  return (x | (x << 1)) & 0x5555u;
+}
+
+__global__ __launch_bounds__(256) void repack_signs_kernel(const uint8_t* raw, int64_t m, int64_t rowbytes, int32_t mt,
+                                                           uint64_t words, u32x4* out) {
+  const uint64_t w = (uint64_t)blockIdx.x * 256 + threadIdx.x;  // (chunk, row tile, lane)
+  if (w >= words) return;
+  const int lane = (int)(w & 63);
+  const uint64_t tile = w >> 6;
+  const int64_t t = (int64_t)(tile % (uint64_t)mt), c = (int64_t)(tile / (uint64_t)mt);
+  const int g = lane >> 4, i = lane & 15;
+  const int64_t r = 16 * t + i;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (r < m) {
+    const uint8_t* seg = raw + r * rowbytes + 64 * c;
+    const int64_t have = rowbytes - 64 * c;  // bytes of this chunk present in the row (> 0)
+    auto byte = [&](int k) -> uint32_t { return k < have ? (uint32_t)seg[k] : 0u; };
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = (spread8(byte(16 * q + g)) << 1) | (spread8(byte(16 * q + 4 + g)) << 17) | spread8(byte(16 * q + 8 + g)) |
+             (spread8(byte(16 * q + 12 + g)) << 16);
+  }
+  out[w] = v;
+}
+
+int launch_repack_signs(const uint8_t* raw, int64_t m, int64_t d, int32_t mt, int32_t nch, uint8_t* out, void* stream) {
+  const uint64_t words = (uint64_t)nch * mt * 64;
+  const uint64_t blocks = (words + 255) / 256;
+  if (blocks == 0) return 0;
+  if (blocks > 0x7fffffffull) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(repack_signs_kernel, dim3((uint32_t)blocks), dim3(256), 0, static_cast<hipStream_t>(stream), raw, m,
+                     d / 8, mt, words, reinterpret_cast<u32x4*>(out));
+  return (int)hipGetLastError();
+}
+
 // ============================================================ static scratch
 // Scratch memory of the allocation-free forward: the pieces and arrival counters of the
 // single- and few-token kernels, kStaticScratchBytes per device for the life of the

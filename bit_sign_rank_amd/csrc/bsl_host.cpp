@@ -208,9 +208,8 @@ struct bsl_stack {
   int32_t decode = BSL_DECODE_AUTO;  // single-token kernel (bsl_set_decode)
   uint64_t budget = 0, resident = 0;
   void* zero_page = nullptr;      // kZeroPageBytes of zeros on the device
-  float* pieces = nullptr;        // single-token partial sums (shared by the stack's launches)
-  uint32_t* arrivals = nullptr;   // wave-private kernel's arrival counters, one per row group of a launch
-  uint64_t* acc64 = nullptr;      // shared-operand kernel's row accumulators ([row groups of a launch][1024], zero)
+  uint64_t* acc64 = nullptr;      // single- and few-token row accumulators, one per (row, token) of a launch (zero)
+  size_t acc64_words = 0;
   float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
   uint8_t* staging[2] = {nullptr, nullptr};  // pinned host buffers of bsl_load_blocks (allocated on first use)
   size_t staging_bytes = 0;
@@ -367,19 +366,12 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     else if ((e = hipMemset(W.dtable, 0, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMemset(table)");
   }
   if (rc == BSL_OK) {
-    // single- and few-token pieces: at most (row groups of one launch) + (workers) of them,
-    // 1024 floats a piece for decode_m1_kernel, 256 a piece for the wave-private kernel,
-    // whose row groups take 256 / T rows for T tokens
-    const size_t n = ((size_t)kMaxGroup * max_groups * kWpMaxTokens + (size_t)s->decode_grid_max) * kDecodeGroupRows;
-    // (arrival counters per row group: the wave-private kernel's are the smallest)
-    const size_t na = (size_t)kMaxGroup * max_groups * (kDecodeGroupRows / kWpRows) * kWpMaxTokens;
-    if ((e = hipMalloc(&s->pieces, n * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(pieces)");
-    else if ((e = hipMalloc(&s->arrivals, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(arrivals)");
-    else if ((e = hipMemset(s->arrivals, 0, na * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(arrivals)");
-    else if ((e = hipMalloc(&s->acc64, (size_t)kMaxGroup * max_groups * kDecodeGroupRows * sizeof(uint64_t))) != hipSuccess)
-      rc = hip_fail(e, "hipMalloc(row accumulators)");
-    else if ((e = hipMemset(s->acc64, 0, (size_t)kMaxGroup * max_groups * kDecodeGroupRows * sizeof(uint64_t))) != hipSuccess)
-      rc = hip_fail(e, "hipMemset(row accumulators)");
+    // row accumulators of the single- and few-token kernels: one per row and token of a
+    // launch (at most kMaxGroup weights of at most max_groups 1024-row groups, at most
+    // kWpMaxTokens tokens)
+    s->acc64_words = (size_t)kMaxGroup * max_groups * kDecodeGroupRows * kWpMaxTokens;
+    if ((e = hipMalloc(&s->acc64, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(row accumulators)");
+    else if ((e = hipMemset(s->acc64, 0, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(row accumulators)");
     else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
     else if ((e = hipMalloc(&s->tile_ctr, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile counters)");
     else if ((e = hipMemset(s->tile_ctr, 0, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(tile counters)");
@@ -758,6 +750,27 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   };
   // Units [o U / 2^lg, (o + 1) U / 2^lg) of worker o, as the kernels compute them.
   auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
+  // Largest number of workers (2^lg of them, each with units [start(o), start(o + 1)))
+  // that share one row group; the row accumulators count at most kAccMaxParts.
+  auto max_parts = [&](int lg) {
+    auto owner = [&](uint64_t u) {  // the kernels' owner(): o with start(o) <= u < start(o + 1)
+      uint64_t o = (u << lg) / units;
+      while (o + 1 < ((uint64_t)1 << lg) && start(o + 1, lg) <= u) ++o;
+      while (start(o, lg) > u) --o;
+      return o;
+    };
+    uint64_t worst = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const WeightDesc& D = args.w[j];
+      if (D.units == 0) continue;
+      const uint64_t per = D.units / (uint64_t)D.groups;
+      for (int32_t g = 0; g < D.groups; ++g) {
+        const uint64_t first = D.unit_begin + (uint64_t)g * per;
+        worst = std::max<uint64_t>(worst, owner(first + per - 1) - owner(first) + 1);
+      }
+    }
+    return worst;
+  };
   // Plan of the wave-private kernel for T tokens (row groups of 256, 128, 64 and 64 rows
   // for T = 1 to 4); false when a workgroup's activations do not fit its LDS.
   auto plan_private = [&](int T, int& lg) {
@@ -767,8 +780,14 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
     lg = 0;
     while ((1 << lg) < workers) ++lg;
+    // no row group shared by more workers than its accumulators count
+    while (workers > kWpWaves && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) {
+      workers /= 2;
+      --lg;
+    }
     // (no units at all: one workgroup writes y = 0)
-    bool fits = (units == 0 || units >= (uint64_t)workers) && (units << lg) < (1ull << 32);
+    bool fits = (units == 0 || units >= (uint64_t)workers) && (units << lg) < (1ull << 32) &&
+                (units == 0 || max_parts(lg) <= (uint64_t)kAccMaxParts);
     // every workgroup keeps the activations of the weights its units belong to in LDS
     for (int32_t L = 0; fits && units > 0 && L < workers / kWpWaves; ++L) {
       const uint64_t a = start((uint64_t)L * kWpWaves, lg), b = start((uint64_t)(L + 1) * kWpWaves, lg) - 1;
@@ -781,34 +800,24 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     }
     return fits;
   };
-  // piece_floats: floats per piece of the wave-private kernel about to run (pieces are
-  // indexed by row group + worker, so (groups + workers) pieces); 0 for the shared-operand
-  // kernel, which keeps one 64-bit accumulator per row of its row groups instead
-  auto launch_units = [&](int lg, size_t piece_floats) {
+  // Row accumulators of a launch: `words` per row group (rows x tokens of the kernel about
+  // to run).  In the allocation-free variant they live in the static scratch, cleared here.
+  auto launch_units = [&](int lg, size_t words) {
     args.total_units = (uint32_t)units;
     args.total_groups = (uint32_t)groups;
     args.grid_log2 = lg;
     args.zero_page = s->zero_page;
-    args.pieces = s->pieces;
-    args.arrivals = s->arrivals;
     args.acc = s->acc64;
-    if (!use_static) return BSL_OK;
-    const size_t need = piece_floats ? (groups + ((size_t)1 << lg)) * piece_floats * sizeof(float)
-                                     : groups * kDecodeGroupRows * sizeof(uint64_t);
-    const size_t room = kStaticScratchBytes - kStaticArrivals * sizeof(uint32_t);
-    if (groups > kStaticArrivals || need > room)
-      return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: this launch needs " + std::to_string(groups) +
-                                        " arrival counters and " + std::to_string(need) + " bytes of partial sums; the static scratch holds " +
-                                        std::to_string(kStaticArrivals) + " and " + std::to_string(room));
-    uint32_t* arrivals = static_cast<uint32_t*>(s->static_scratch);
-    args.arrivals = arrivals;
-    args.pieces = reinterpret_cast<float*>(arrivals + kStaticArrivals);
-    args.acc = reinterpret_cast<uint64_t*>(arrivals + kStaticArrivals);
-    // the kernels expect zero counters (and zero accumulators); a kernel, not a memset, so
-    // that captured streams hold no memset node
-    const int fe = piece_floats ? launch_fill_u32(arrivals, (uint32_t)groups, 0u, stream)
-                                : launch_fill_u32(arrivals + kStaticArrivals, (uint32_t)(need / sizeof(uint32_t)), 0u, stream);
-    return fe == 0 ? BSL_OK : hip_fail(static_cast<hipError_t>(fe), "scratch counter clear");
+    const size_t need = groups * words * sizeof(uint64_t);
+    if (!use_static) return need <= s->acc64_words * sizeof(uint64_t) ? BSL_OK : fail(BSL_EUNSUPPORTED, "forward: row accumulators");
+    if (need > kStaticScratchBytes)
+      return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: this launch needs " + std::to_string(need) +
+                                        " bytes of row accumulators; the static scratch holds " + std::to_string(kStaticScratchBytes));
+    args.acc = static_cast<uint64_t*>(s->static_scratch);
+    // the kernels expect zero accumulators; a kernel, not a memset, so that captured
+    // streams hold no memset node
+    const int fe = launch_fill_u32(static_cast<uint32_t*>(s->static_scratch), (uint32_t)(need / sizeof(uint32_t)), 0u, stream);
+    return fe == 0 ? BSL_OK : hip_fail(static_cast<hipError_t>(fe), "scratch clear");
   };
   if (M == 1) {
     // AUTO takes the shared-operand kernel: on the 8B-shaped layer it measured faster
@@ -826,29 +835,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       int32_t grid = s->decode_grid_max;
       while (grid > 1 && (uint64_t)grid > units) grid /= 2;
       while ((1 << lg) < grid) ++lg;
-      auto owner = [&](uint64_t u) {  // the kernel's owner(): o with start(o) <= u < start(o + 1)
-        uint64_t o = (u << lg) / units;
-        while (o + 1 < ((uint64_t)1 << lg) && start(o + 1, lg) <= u) ++o;
-        while (start(o, lg) > u) --o;
-        return o;
-      };
-      auto max_parts = [&]() {
-        uint64_t worst = 0;
-        for (int32_t j = 0; j < count; ++j) {
-          const WeightDesc& D = args.w[j];
-          if (D.units == 0) continue;
-          const uint64_t per = D.units / (uint64_t)D.groups;
-          for (int32_t g = 0; g < D.groups; ++g) {
-            const uint64_t first = D.unit_begin + (uint64_t)g * per;
-            worst = std::max<uint64_t>(worst, owner(first + per - 1) - owner(first) + 1);
-          }
-        }
-        return worst;
-      };
-      while (lg > 0 && units > 0 && max_parts() > (uint64_t)kAccMaxParts) --lg;
+      while (lg > 0 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
       if ((units << lg) >= (1ull << 32)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
     }
-    const int rc = launch_units(lg, wp ? (size_t)kWpRows : 0);
+    const int rc = launch_units(lg, wp ? (size_t)kWpRows : (size_t)kDecodeGroupRows);
     if (rc != BSL_OK) return rc;
     e = wp ? launch_decode_wp(args, 1, stream) : launch_decode_m1(args, stream);
     if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
@@ -860,7 +850,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     const int T = M;
     int lg = 0;
     if (plan_private(T, lg)) {
-      const int rc = launch_units(lg, (size_t)kWpRows);
+      const int rc = launch_units(lg, (size_t)kWpRows);  // (rows x tokens of a row group: at most kWpRows)
       if (rc != BSL_OK) return rc;
       e = launch_decode_wp(args, T, stream);
       if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
@@ -989,8 +979,6 @@ void bsl_destroy(bsl_stack* s) {
     if (W.counters) (void)hipFree(W.counters);
   }
   if (s->zero_page) (void)hipFree(s->zero_page);
-  if (s->pieces) (void)hipFree(s->pieces);
-  if (s->arrivals) (void)hipFree(s->arrivals);
   if (s->acc64) (void)hipFree(s->acc64);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);

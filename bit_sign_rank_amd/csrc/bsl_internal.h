@@ -76,10 +76,8 @@ struct GroupArgs {
   uint32_t total_groups; // single-token path: row groups over all weights
   int32_t grid_log2;     // single-token path: log2 of the (power-of-two) grid
   const void* zero_page; // kZeroPageBytes of zeros: target of prefetches past the end of the work
-  float* pieces;         // single-/few-token path: [total_groups + workers][piece] partial sums (workspace)
-  uint32_t* arrivals;    // wave-private path: [total_groups] counters, zero between launches (workspace)
-  uint64_t* acc;         // shared-operand single-token path: [total_groups][1024] row accumulators,
-                         // zero between launches (workspace)
+  uint64_t* acc;         // single- and few-token paths: row accumulators, [total_groups][rows x tokens of a
+                         // row group], zero between launches (workspace)
 };
 
 // Kernel launchers (bsl_kernels.hip).  Return a hipError_t value.
@@ -135,10 +133,8 @@ constexpr int kTileItemsPerCu = 2;     // aim of the column-range cutting
 constexpr int kTileCounters = 1 << 16;
 
 // Allocation-free forward (bsl_forward_group_static): the single- and few-token kernels
-// pieces and arrival counters in one static device array per device (see
-// bsl_kernels.hip), arrival counters first.
+// row accumulators in one static device array per device (see bsl_kernels.hip).
 constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
-constexpr size_t kStaticArrivals = 16384;  // counters (64 KiB) before the pieces
 constexpr int kMaxDevices = 64;
 // Address of this process's static scratch array on `device` (which must be the current
 // device), taken with hipGetSymbolAddress on the first call for that device.  Returns a

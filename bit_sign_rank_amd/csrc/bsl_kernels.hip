@@ -1515,16 +1515,17 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
   __syncthreads();
 
   // acc: P of the current block; accy: its U-weighted, r-summed rows over the blocks done
-  // (one row per lane and tile, see reduce_columns)
+  // (one row per lane and tile, see reduce_columns; tile t in element t % 4 of accy[q][t / 4])
+  static_assert(R % 4 == 0, "row tiles are spread over the four lanes of a quad");
   float4v acc[T][R];
-  float accy[T][R];
+  float4v accy[T][R / 4];
 #pragma unroll
-  for (int q = 0; q < T; ++q)
+  for (int q = 0; q < T; ++q) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      acc[q][t] = (float4v){0.f, 0.f, 0.f, 0.f};
-      accy[q][t] = 0.f;
-    }
+    for (int t = 0; t < R; ++t) acc[q][t] = (float4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < R / 4; ++s) accy[q][s] = (float4v){0.f, 0.f, 0.f, 0.f};
+  }
   uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
   asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs: one v_and_or_b32 each)
   uint32_t ix_odd[R], ix_even[R];
@@ -1541,17 +1542,75 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
   vsl[0] = load_v(p1, 0);
 
   const int rsel = reduced_row(lane);
-  auto store_piece = [&](const Cur& c) {
-    const uint32_t item = c.rg_begin + c.rg;
-    float* piece = args.pieces + (size_t)(item + worker) * (ROWS * T);  // [T][ROWS]
+  // After a row group: this worker's share of each row of each token, added to the
+  // row's fixed-point accumulator (acc_share); the worker whose add completes a row's
+  // count writes that row of y.  Every lane of a quad holds the same reduced sums, so
+  // lane L adds the rows of the tiles t = 4 s + (L & 3): R / 4 adds per lane, all lanes
+  // busy.  The adds return the previous words, which are looked at only at the next row
+  // group's end (or the end of the range): waiting for them at once would stall this
+  // wave, the only one on its SIMD, on the atomics' round trip.
+  constexpr int RS = R / 4;
+  const int quad = lane & 3;
+  const uint32_t NWK = 1u << lg;  // workers
+  auto owner = [&](uint32_t u) {
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < NWK && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  struct Pending {
+    uint64_t* words;  // [T][ROWS] accumulators of the row group (null: nothing pending)
+    void* y;
+    int32_t m, row0;
+    uint32_t parts;
+  } pend = {nullptr, nullptr, 0, 0, 0u};
+  uint64_t pold[T][RS];  // previous words returned by the pending adds
+  uint64_t pshare[T][RS];
+  // (forced inline: called out of line, this wave's live registers would be saved to
+  // scratch around every call)
+  auto resolve = [&]() __attribute__((always_inline)) {
+    if (pend.words == nullptr) return;
 #pragma unroll
     for (int q = 0; q < T; ++q)
 #pragma unroll
-      for (int t = 0; t < R; ++t) {
-        if ((lane & 3) == 0)
-          __hip_atomic_store(&piece[q * ROWS + t * kTileRows + rsel], accy[q][t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        accy[q][t] = 0.f;
+      for (int s = 0; s < RS; ++s) {
+        const int rr = (4 * s + quad) * kTileRows + rsel;
+        const int row = pend.row0 + rr;
+        if (row < pend.m) {
+          const uint64_t now = pold[q][s] + pshare[q][s];
+          if (acc_count(now) == pend.parts) {
+            store_y(pend.y, (size_t)q * pend.m + row, acc_value(now), args.y_fp32);
+            __hip_atomic_store(&pend.words[q * ROWS + rr], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
+    pend.words = nullptr;
+  };
+  auto add_shares = [&](const Cur& c) __attribute__((always_inline)) {
+    resolve();
+    const uint32_t item = c.rg_begin + c.rg;
+    const uint32_t per_rg = (uint32_t)c.nch * c.nb;
+    const uint32_t first = args.w[c.j].unit_begin + (uint32_t)c.rg * per_rg;
+    pend.parts = owner(first + per_rg - 1) - owner(first) + 1;
+    pend.words = args.acc + (size_t)item * (ROWS * T);  // [T][ROWS]
+    pend.y = args.w[c.j].y;
+    pend.m = args.w[c.j].m;
+    pend.row0 = c.rg * ROWS;
+#pragma unroll
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+      for (int s = 0; s < RS; ++s) {
+        const float v = accy[q][s][quad];  // (a vector element: selected in registers)
+        const int rr = (4 * s + quad) * kTileRows + rsel;
+        pshare[q][s] = acc_share(v);
+        pold[q][s] = 0;
+        if (pend.row0 + rr < pend.m)
+          pold[q][s] = __hip_atomic_fetch_add(&pend.words[q * ROWS + rr], pshare[q][s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+    for (int q = 0; q < T; ++q)
+#pragma unroll
+      for (int s = 0; s < RS; ++s) accy[q][s] = (float4v){0.f, 0.f, 0.f, 0.f};
   };
 
   // ---- one unit: c0 with signs in `cur`; on entry plane 0's operands are ready, V of
@@ -1612,12 +1671,12 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
           w[1] = (float)u01[1] * acc[q][t][1];
           w[2] = (float)u23[0] * acc[q][t][2];
           w[3] = (float)u23[1] * acc[q][t][3];
-          accy[q][t] += reduce_columns(w, lane);
+          accy[q][t / 4][t % 4] += reduce_columns(w, lane);
           acc[q][t] = (float4v){0.f, 0.f, 0.f, 0.f};
         }
       }
     }
-    if (group_end(c0)) store_piece(c0);
+    if (group_end(c0)) add_shares(c0);
     c0 = c1;
     c1 = c2;
     c2 = c3;
@@ -1628,63 +1687,12 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
     astride = astride_next;
   };
 
-  const uint32_t item_first = c0.rg_begin + c0.rg;
   const uint32_t n = u_end - u_begin;
   for (uint32_t s = 0; s < n; s += 2) {
     step(sgn[0], sgn[1]);
     if (s + 1 < n) step(sgn[1], sgn[0]);
   }
-
-  // ---- end of the range: count this worker in for every row group it touched; the
-  // last one to arrive at a row group adds the pieces (one per worker owner(first) ..
-  // owner(last), in that order) and writes y.
-  const uint32_t W = 1u << lg;
-  auto owner = [&](uint32_t u) {
-    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
-    while (o + 1 < W && range_start(o + 1, U, lg) <= u) ++o;
-    while (range_start(o, U, lg) > u) --o;
-    return o;
-  };
-  auto group_units = [&](uint32_t item, uint32_t& first, uint32_t& last) {
-    int j = 0;
-    while (j + 1 < args.count && item >= args.w[j + 1].rg_begin) ++j;
-    const WeightDesc& Wd = args.w[j];
-    const uint32_t per_rg = (uint32_t)Wd.nblocks * Wd.nch;
-    first = Wd.unit_begin + (item - Wd.rg_begin) * per_rg;
-    last = first + per_rg - 1;
-    return j;
-  };
-  const int je = weight_of(u_end - 1);
-  const uint32_t item_last =
-      args.w[je].rg_begin + (u_end - 1 - args.w[je].unit_begin) / ((uint32_t)args.w[je].nch * args.w[je].nblocks);
-  publish_partials();  // this wave's pieces are visible before its arrivals are counted
-  for (uint32_t item = item_first; item <= item_last; ++item) {
-    uint32_t first, last;
-    const int j = group_units(item, first, last);
-    if (args.w[j].units == 0) continue;  // a weight without blocks (y = 0 is written above)
-    const uint32_t o0 = owner(first), o1 = owner(last);
-    uint32_t seen = 0;
-    if (lane == 0) seen = count_arrival(&args.arrivals[item]) + 1;
-    seen = __builtin_amdgcn_readfirstlane(seen);
-    if (seen != o1 - o0 + 1) continue;
-    if (lane == 0) __hip_atomic_store(&args.arrivals[item], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const WeightDesc& Wd = args.w[j];
-    for (int e = lane; e < ROWS * T; e += 64) {  // e = token * ROWS + row in the group
-      const int tok = e / ROWS, rr = e % ROWS;
-      const float* base = args.pieces + (size_t)item * (ROWS * T) + e;
-      float acc_y = 0.f;
-      for (uint32_t o = o0; o <= o1; o += 16) {  // (16 loads in flight per round trip)
-        float v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-          v[k] = __hip_atomic_load(base + (size_t)min(o + k, o1) * (ROWS * T), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) acc_y += o + k <= o1 ? v[k] : 0.f;
-      }
-      const int row = (int)(item - Wd.rg_begin) * ROWS + rr;
-      if (row < Wd.m && tok < args.M) store_y(Wd.y, (size_t)tok * Wd.m + row, acc_y, args.y_fp32);
-    }
-  }
+  resolve();
 }
 
 // ============================================================ debug unpack

@@ -167,15 +167,15 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
  * memory or must not let a call allocate: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, same results as
  * bsl_forward_group for 1 <= M <= 4 (the same kernels in the same launch configuration),
- * with the kernels' partial sums and arrival counters in a scratch array of
- * 8 MiB (kStaticScratchBytes: 16384 counters and ~8 MiB of partial sums) that the library
- * holds on each device it runs on until the process ends (its address is taken by
- * bsl_init).  The call allocates nothing, on the device or the host; it clears the
- * counters it uses with a small kernel on `stream`, then launches the forward there.
+ * with the kernels' row accumulators (one 64-bit word per output row and token) in a
+ * scratch array of 8 MiB that the library holds on each device it runs on until the
+ * process ends (its address is taken by bsl_init).  The call allocates nothing, on the
+ * device or the host; it clears the accumulators it uses with a small kernel on
+ * `stream`, then launches the forward there.
  *   M = 1 takes the single-token kernel bsl_set_decode selects; M = 2..4 the few-token
  *   kernel whatever bsl_set_path says.
  * Errors (nothing is launched): BSL_EUNSUPPORTED if M > 4, if the launch needs more
- * partial sums or counters than the scratch holds (the message gives both sizes), or if
+ * accumulators than the scratch holds (the message gives both sizes), or if
  * the group's activations do not fit the few-token kernel (where bsl_forward_group would
  * split the group); the argument errors of bsl_forward_group.
  * Every such call on one device shares that device's scratch: calls that may overlap in

@@ -27,6 +27,7 @@ BSL_PATH_TILE = 2
 BSL_DECODE_AUTO = 0
 BSL_DECODE_SHARED = 1
 BSL_DECODE_PRIVATE = 2
+BSL_KERNEL_KINDS = 4
 
 EXPORTED = (
     "bsl_block_bytes",
@@ -41,6 +42,7 @@ EXPORTED = (
     "bsl_load_blocks",
     "bsl_active_blocks",
     "bsl_resident_bytes",
+    "bsl_launch_counts",
     "bsl_forward",
     "bsl_forward_group",
     "bsl_forward_group_static",
@@ -98,6 +100,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_active_blocks.argtypes = [c_vp, c_i32, ctypes.POINTER(c_i32)]
         L.bsl_resident_bytes.restype = c_u64
         L.bsl_resident_bytes.argtypes = [c_vp]
+        L.bsl_launch_counts.argtypes = [c_vp, c_vp]
         L.bsl_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group_static.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
@@ -122,7 +125,7 @@ def lib() -> ctypes.CDLL:
         L.bsl_lr_destroy.restype = None
         L.bsl_lr_destroy.argtypes = [c_vp]
         for f in ("bsl_pack_signs", "bsl_unpack_signs", "bsl_init", "bsl_set_source", "bsl_load_blocks",
-                  "bsl_active_blocks", "bsl_forward", "bsl_forward_group", "bsl_forward_group_static", "bsl_set_path", "bsl_debug_unpack", "bsl_set_decode",
+                  "bsl_active_blocks", "bsl_launch_counts", "bsl_forward", "bsl_forward_group", "bsl_forward_group_static", "bsl_set_path", "bsl_debug_unpack", "bsl_set_decode",
                   "bsl_set_input_scale", "bsl_lr_init", "bsl_lr_set_source", "bsl_lr_load_blocks", "bsl_lr_forward",
                   "bsl_lr_forward_group"):
             getattr(L, f).restype = c_i32
@@ -216,6 +219,14 @@ def bsl_active_blocks(stack: int, w: int) -> int:
 
 def bsl_resident_bytes(stack: int) -> int:
     return int(lib().bsl_resident_bytes(stack))
+
+
+def bsl_launch_counts(stack: int) -> list:
+    """Forward launches so far per kernel: [shared single-token, wave-private single- and
+    few-token, factored multi-token, tile-reconstruct]."""
+    c = np.zeros(BSL_KERNEL_KINDS, dtype=np.uint64)
+    _check(lib().bsl_launch_counts(stack, _ptr(c)))
+    return [int(v) for v in c]
 
 
 def bsl_forward(stack: int, w: int, x_ptr: int, y_ptr: int, M: int, y_is_fp32: bool, stream: int = 0) -> None:

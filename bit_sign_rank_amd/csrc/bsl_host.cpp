@@ -218,6 +218,7 @@ struct bsl_stack {
   size_t raw_dev_bytes = 0;
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
   void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
+  uint64_t launches[BSL_KERNEL_KINDS] = {0, 0, 0, 0};  // forward launches per kernel (bsl_launch_counts)
   std::vector<Weight> w;
 };
 
@@ -596,6 +597,12 @@ int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out) {
 
 uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
 
+int bsl_launch_counts(const bsl_stack* s, uint64_t* counts) {
+  if (!s || !counts) return fail(BSL_EINVAL, "bsl_launch_counts: null pointer");
+  for (int k = 0; k < BSL_KERNEL_KINDS; ++k) counts[k] = s->launches[k];
+  return BSL_OK;
+}
+
 namespace {
 
 // Tile-reconstruct path.  Items are (weight, token group, 128-row group, column range);
@@ -688,6 +695,7 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.total_items = (int32_t)items;
   DeviceGuard guard(s->device);
   const int e = launch_tile(args, tt, (int)token_groups, stream);
+  if (e == 0) ++s->launches[3];
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
 }
@@ -842,6 +850,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     if (rc != BSL_OK) return rc;
     e = wp ? launch_decode_wp(args, 1, stream) : launch_decode_m1(args, stream);
     if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+    ++s->launches[wp ? 1 : 0];
     return BSL_OK;
   }
   if (M <= kWpMaxTokens && (s->path == BSL_PATH_AUTO || use_static)) {
@@ -854,6 +863,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
       if (rc != BSL_OK) return rc;
       e = launch_decode_wp(args, T, stream);
       if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+      ++s->launches[1];
       return BSL_OK;
     }
     // The group does not fit as a whole: the weights whose activations take at most half
@@ -914,6 +924,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.zero_page = s->zero_page;
   e = launch_prefill(args, nt, token_groups, stream);
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+  ++s->launches[2];
   return BSL_OK;
 }
 

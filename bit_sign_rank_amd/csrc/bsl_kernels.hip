@@ -1339,7 +1339,7 @@ __host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4
 
 // R row tiles per wave and T tokens (R T <= 16: the accumulators of a 16-tile wave): the
 // tokens share every B operand, sign index and load; each has its own A operand (its
-// activations), accumulators and pieces.  Tokens past args.M are zeros and not stored.
+// activations), accumulators and row-accumulator adds.  T is the launch's token count.
 template <int R, int T>
 __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wp_kernel(GroupArgs args) {
   constexpr int ROWS = 16 * R;  // rows per unit

@@ -154,12 +154,16 @@ uint64_t bsl_resident_bytes(const bsl_stack* s);
  *   M >= 1 tokens.  With n = 0 loaded blocks y is all zeros.
  * Only enqueues kernels on `stream` (no synchronisation, no allocation).  Forwards on
  * one stack must not run concurrently, even for different weights: they share the
- * stack's workspaces (partial sums and arrival counters).  Forwards queued on one stream
+ * stack's workspaces (row accumulators, split partial sums and their counters).  Forwards queued on one stream
  * are ordered, so that is the simple way to issue them. */
 int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int32_t y_is_fp32, void* stream);
 
-/* Several weights in one kernel launch (count <= 8, distinct weights): weights[j] reads
- * x[j] and writes y[j] exactly as bsl_forward would.  All share M and y_is_fp32. */
+/* Several weights in one call (count <= 8, distinct weights): weights[j] reads x[j] and
+ * writes y[j] exactly as bsl_forward would.  All share M and y_is_fp32.  The group runs
+ * as one kernel launch, except on BSL_PATH_AUTO at M = 2..4 when the group's activations
+ * do not fit the few-token kernel as a whole: then it is split into two launches (see
+ * bsl_set_path).  An error returned after the first of the two was enqueued leaves the y[j]
+ * of the weights in that launch written and the others unspecified. */
 int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
                       int32_t M, int32_t y_is_fp32, void* stream);
 
@@ -224,6 +228,14 @@ int bsl_set_decode(bsl_stack* s, int32_t kind);
  * path 0: the single-token kernel's sparse-MFMA indices; path 1: the multi-token
  * kernel's +-1 fp16 A fragments; path 2: the tile-reconstruct kernel's +-1 fp16 pairs. */
 int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream);
+
+/* Forward kernel launches the stack has enqueued since bsl_init, per kernel: counts[0] the
+ * shared-operand single-token kernel, [1] the wave-private single- and few-token kernel,
+ * [2] the factored multi-token kernel, [3] the tile-reconstruct kernel (host array of
+ * BSL_KERNEL_KINDS entries).  A diagnostic: it tells a caller which formulation a call
+ * took (bsl_set_path, bsl_set_decode), and how many launches a grouped call made. */
+#define BSL_KERNEL_KINDS 4
+int bsl_launch_counts(const bsl_stack* s, uint64_t* counts);
 
 /* Message for the calling thread's last failure ("" if none). */
 const char* bsl_last_error(void);

@@ -70,3 +70,33 @@ class Stack:
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+U16 = 2.0**-11  # unit roundoff of fp16
+U32 = 2.0**-24  # unit roundoff of fp32
+
+
+def abs_bound(x, blocks, n):
+    """A[t, j] = sum_c |x[t, c]| sum_i (|U_i| |V_i|^T)[j, c]: the scale of every rounding."""
+    d = x.shape[1]
+    m = blocks[0]["u"].shape[0] if blocks else 0
+    W = np.zeros((m, d))
+    for b in blocks[:n]:
+        W += np.abs(b["u"].astype(np.float64)) @ np.abs(b["v"].astype(np.float64)).T
+    return np.abs(x.astype(np.float64)) @ W.T
+
+
+def elem_factor(kernel, n, d):
+    """Per-element error bound / A for each kernel's arithmetic (fp32 output):
+    factored paths round Z = V x to fp16 once (U16) then sum in fp32 over d + 16 n terms;
+    the wave-private kernels multiply V and x exactly inside the matrix core; the tile
+    path rounds each block's U_i V_i^T and each running sum of W_hat to fp16 (n + 1 U16)."""
+    acc = (d + 16 * n) * U32
+    return {"z16": U16 + acc, "exact": acc, "tile": (n + 1) * U16 + acc}[kernel]
+
+
+def assert_elementwise(y, ref, bound, ctx=""):
+    """|y - ref| <= bound everywhere (bound: per-element array)."""
+    ratio = np.abs(y - ref) / np.maximum(bound, 1e-300)
+    worst = np.unravel_index(int(ratio.argmax()), ratio.shape) if ratio.size else None
+    assert ratio.size == 0 or ratio.max() <= 1.0, f"{ctx}: worst element {worst} at {ratio.max():.3f} of its bound"

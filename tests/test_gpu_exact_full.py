@@ -25,7 +25,7 @@ torch = pytest.importorskip("torch")
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 import bit_sign_rank_amd as bsl  # noqa: E402
-from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
+from gpu_util import REL_TOL, Stack, abs_bound, elem_factor, rel_err  # noqa: E402
 
 AUTO, FACT, TILE = bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE
 SHARED, PRIVATE = bsl.BSL_DECODE_SHARED, bsl.BSL_DECODE_PRIVATE
@@ -163,29 +163,6 @@ def test_dyadic_70b_layer_grouped_bit_exact():
 
 
 # ---------------------------------------------------------------- float blocks, all rows
-U16 = 2.0**-11  # unit roundoff of fp16
-U32 = 2.0**-24  # unit roundoff of fp32
-
-
-def abs_bound(x, blocks, n):
-    """A[t, j] = sum_c |x[t, c]| sum_i (|U_i| |V_i|^T)[j, c]: the scale of every rounding."""
-    d = x.shape[1]
-    m = blocks[0]["u"].shape[0]
-    W = np.zeros((m, d))
-    for b in blocks[:n]:
-        W += np.abs(b["u"].astype(np.float64)) @ np.abs(b["v"].astype(np.float64)).T
-    return np.abs(x.astype(np.float64)) @ W.T
-
-
-def elem_factor(kernel, n, d):
-    """Per-element error bound / A for each kernel's arithmetic (fp32 output):
-    factored paths round Z = V x to fp16 once (U16) then sum in fp32 over d + 16 n terms;
-    the wave-private kernels multiply V and x exactly inside the matrix core; the tile
-    path rounds each block's U_i V_i^T and each running sum of W_hat to fp16 (n + 1 U16)."""
-    acc = (d + 16 * n) * U32
-    return {"z16": U16 + acc, "exact": acc, "tile": (n + 1) * U16 + acc}[kernel]
-
-
 @pytest.fixture(scope="module")
 def float_8b():
     shapes = synth.LLAMA3_8B_LAYER

@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 import bit_sign_rank_amd as bsl  # noqa: E402  (no skip: a missing library must fail here)
-from gpu_util import REL_TOL, Stack, rel_err  # noqa: E402
+from gpu_util import REL_TOL, Stack, abs_bound, assert_elementwise, elem_factor, rel_err  # noqa: E402
 
 PATHS = [bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE]
 PATH_IDS = ["factored", "tile"]
@@ -417,6 +417,67 @@ def test_few_tokens_wide_input_falls_back(M):
         st.load([n])
         y = st.forward(0, x)
     assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+# A grouped few-token call whose activations do not fit the wave-private kernel's LDS
+# (148 KiB per workgroup): the weights taking at most half of it (narrow) go to that kernel
+# in one launch, the rest (wide) to the factored multi-token kernel in a second one.
+# d = 28672 needs 168 / 224 KiB at 3 / 4 tokens.  The zero-block weight writes zeros.
+SPLIT_SHAPES = [(96, 1024), (200, 28672), (64, 2560), (300, 512), (1024, 4096)]
+SPLIT_COUNTS = [3, 2, 0, 4, 2]
+
+
+def _counts(st):
+    return np.array(bsl.bsl_launch_counts(st.h))
+
+
+@pytest.mark.parametrize("M", [3, 4])
+def test_few_tokens_grouped_split_bit_exact(M):
+    ws = [(m, d, integer_blocks(m, d, max(n, 1), 60 + j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
+    xs = [synth.integer_activations(61, M, d, -1, 1, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
+    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(SPLIT_COUNTS)
+        before = _counts(st)
+        ys = st.forward_group(list(range(5)), xs)
+        assert (_counts(st) - before).tolist() == [0, 1, 1, 0]
+    for j, ((m, d, blocks), n) in enumerate(zip(ws, SPLIT_COUNTS)):
+        assert np.array_equal(ys[j], oracle.forward(xs[j], blocks, n)), (j, SPLIT_SHAPES[j], n)
+
+
+@pytest.mark.parametrize("M", [3, 4])
+def test_few_tokens_grouped_split_float_all_rows(M):
+    ws = [(m, d, synth.synthetic_blocks(62, m, d, max(n, 1), 16, j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
+    xs = [synth.activations(63, M, d, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
+    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(SPLIT_COUNTS)
+        ys = st.forward_group(list(range(5)), xs)
+    for j, ((m, d, blocks), n) in enumerate(zip(ws, SPLIT_COUNTS)):
+        ref = oracle.forward(xs[j], blocks, n)
+        if n == 0:
+            assert not ys[j].any()
+            continue
+        assert rel_err(ys[j], ref) <= REL_TOL
+        # exact products in the wave-private kernel; fp16 Z in the multi-token kernel
+        kind = "z16" if d == 28672 else "exact"
+        assert_elementwise(ys[j], ref, elem_factor(kind, n, d) * abs_bound(xs[j], blocks, n), f"weight {j} {SPLIT_SHAPES[j]}")
+
+
+def test_few_tokens_narrow_subset_that_does_not_fit_falls_back():
+    """Narrow weights (64 KiB of activations each at 4 tokens) whose units are so few that
+    one workgroup's range spans three of them plus the start of a long one: that workgroup
+    would need 208 KiB of LDS, so the narrow subset runs on the multi-token kernel too (one
+    launch), and the wide weight in a second one; results stay exact."""
+    shapes = [(64, 8192), (64, 8192), (64, 8192), (16384, 2048), (200, 20480)]
+    counts = [1, 0, 1, 16, 2]
+    ws = [(m, d, integer_blocks(m, d, max(n, 1), 70 + j)) for j, ((m, d), n) in enumerate(zip(shapes, counts))]
+    xs = [synth.integer_activations(71, 4, d, -1, 1, j) for j, (_, d) in enumerate(shapes)]
+    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+        st.load(counts)
+        before = _counts(st)
+        ys = st.forward_group(list(range(5)), xs)
+        assert (_counts(st) - before).tolist() == [0, 0, 2, 0]
+    for j, ((m, d, blocks), n) in enumerate(zip(ws, counts)):
+        assert np.array_equal(ys[j], oracle.forward(xs[j], blocks, n)), (j, shapes[j], n)
 
 
 @pytest.mark.slow

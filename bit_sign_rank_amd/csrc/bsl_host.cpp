@@ -605,7 +605,7 @@ int bsl_launch_counts(const bsl_stack* s, uint64_t* counts) {
 
 namespace {
 
-// Tile-reconstruct path.  Items are (weight, token group, 128-row group, column range);
+// Tile-reconstruct path.  Items are (weight, token group, 64-row group, column range);
 // weights go longest item first, so the long items of a launch start first.  A weight's
 // chunks are cut into ranges when the launch has too few items to keep every CU busy, as
 // far as the stack's tile workspace holds the ranges' partial sums.
@@ -645,9 +645,10 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
     p.cps = W.nch;
     total += p.rgroups * token_groups * W.nch * p.batches;
   }
-  // Items of about half a CU's share.  (Finer cutting measured slower: every range adds
-  // a pipeline start and a partial-sum pass.)
-  const int64_t slots = (int64_t)kTileItemsPerCu * s->decode_grid_max;
+  // Items of about half a CU's share (a quarter at tt = 1, where two workgroups share a
+  // CU).  (Finer cutting measured slower: every range adds a pipeline start and a
+  // partial-sum pass.)
+  const int64_t slots = (int64_t)kTileItemsPerCu * (tt == 1 ? 2 : 1) * s->decode_grid_max;
   const int64_t target = std::max<int64_t>(1, (total + slots - 1) / slots);
   size_t ws_used = 0, ctr_used = 0;
   for (Plan& p : plan) {

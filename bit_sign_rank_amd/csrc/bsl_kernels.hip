@@ -923,15 +923,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // rebuilt tile is multiplied with the activations at once, so the sign / low-rank work
 // is paid once per group of up to 512 tokens instead of once per token:
 //     W_hat[j, c] = sum_i S_i[j, c] (U_i V_i^T)[j, c],     y[t, j] = sum_c x[t, c] W_hat[j, c].
-// One workgroup of 4 waves (one per SIMD, so each wave's VALU work overlaps its own MFMAs)
-// per item = (weight, 128-row group, group of 32 TT tokens); wave w owns rows 32 w ..
-// 32 w + 31 and all the group's tokens.  The column loop runs in steps of two planes (64
-// columns).  For each step and block, two v_mfma_f32_32x32x16_f16 with K = 16 = the rank
-// give (U_i V_i^T) for the wave's 32 rows and the step's two planes; each fp32 result pair
-// (same row and column offset in both planes) is rounded to an fp16 pair and added into
-// the running W_hat pair with a +-1 fp16 pair built from the stored sign word (one shift
-// and one AND-OR).  After the batch's blocks the pairs are split by plane and feed the
-// GEMM: 4 MFMAs per 32-token tile and step, fp16 inputs, fp32 accumulation.
+// One workgroup of 4 waves (one per SIMD; two workgroups per CU with TT = 1) per item =
+// (weight, 64-row group, group of 2 x 32 TT tokens, column range); wave w owns row tile
+// w / TH (32 rows) and token half w % TH (TT tiles of 32 tokens).  The column loop runs in
+// steps of two planes (64 columns).  The two waves of a row tile split the blocks of a
+// batch: for each step and own block, two v_mfma_f32_32x32x16_f16 with K = 16 = the rank
+// give (U_i V_i^T) for the 32 rows and the step's two planes; each fp32 result pair (same
+// row and column offset in both planes) is rounded to an fp16 pair and added into the
+// running W_hat pair with a +-1 fp16 pair built from the stored sign word (one shift and
+// one AND-OR).  The partner's share arrives through LDS; the completed pairs are split by
+// plane and feed the GEMM: 4 MFMAs per 32-token tile and step, fp16 inputs, fp32
+// accumulation.
 //
 // Layouts (lane l, h = l / 32, j = l % 32):
 //  * reconstruct: A = V rows (the step plane's column sigma(j), ranks 8 h .. 8 h + 7,
@@ -992,8 +994,12 @@ __device__ __forceinline__ float16v rebuild_mfma(const half8& a, const half8& b)
 __device__ __forceinline__ void mfma_result_ready(float16v& d0, float16v& d1) {
   asm("s_nop 15\n\ts_nop 3" : "+v"(d0), "+v"(d1));
 }
+// With one 32-token tile per wave (TT = 1: a few tokens, where the rebuild's VALU work is
+// nearly all of it) the kernel fits 256 registers and two workgroups share a CU, so one
+// wave's rebuild runs while the other waits on its loads (M = 16, 8B-shaped layer, n = 8:
+// 310 -> 239 us); larger TT keep one wave per SIMD and all 512 registers.
 template <int TT, int TH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_kernel(GroupArgs args, int token_groups) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2 : 1, TT == 1 ? 2 : 1))) void tile_kernel(GroupArgs args, int token_groups) {
   constexpr int TG = TT * TH;             // 32-token tiles per workgroup
   constexpr int RT = 4 / TH;              // 32-row tiles per workgroup
   constexpr int GROUP_ROWS = 32 * RT;

@@ -227,7 +227,7 @@ __device__ __forceinline__ uint32_t count_arrival(uint32_t* ctr) {
   return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Row accumulators of the single-token kernel: one 64-bit word per output row of a
+// Row accumulators of the single- and few-token kernels: one 64-bit word per output row of a
 // launch, zero between launches.  Bits 63..58 count the workgroups that have added their
 // share of the row, bits 57..0 hold the sum of their shares in fixed point with 28
 // fraction bits, each share biased by 2^51 so that the field only grows.  A workgroup

@@ -1292,6 +1292,260 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ tile path, 512-token groups
+// The item, arithmetic and results of tile_kernel<8, 2>, with the rebuild and the GEMM in
+// different waves: 8 waves, two per SIMD (256 registers each).  Waves 0-3 (GEMM waves)
+// own row tile w / 2 and token half w % 2 (8 tiles of 32 tokens), stage the activations
+// and multiply; waves 4-7 (rebuild waves) own row tile (w - 4) / 2 and block half
+// (w - 4) % 2 of each batch, and hand their partial W_hat pairs of the next step to the
+// GEMM waves through LDS.  A SIMD then runs one wave's sign work while the other's MFMAs
+// execute, and a wave that waits for its loads or the barrier leaves the SIMD to the
+// other: a wave alone on its SIMD would take the rebuild's VALU chain, the activation
+// loads and the step barrier one after the other.  The two partial tiles are added in
+// the order tile_kernel adds them, so both kernels give the same bits.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void tile_split_kernel(GroupArgs args, int token_groups) {
+  constexpr int TT = 8, TH = 2, TG = TT * TH, GROUP_ROWS = 64, BPW = kTileBatch / 2;
+  __shared__ u32x4 xs[2][TH][TT][32][8];  // activations of a step (layout of tile_kernel's xs0 / xs1), two buffers
+  __shared__ u32x4 wpart[2][4][4][64];     // partial W_hat pairs of a step from the rebuild waves, two buffers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, jl = lane & 31;
+  const bool gemm = wave < 4;
+  const int role = gemm ? wave : wave - 4;
+  const int rtile = role >> 1, half = role & 1;  // GEMM waves: token half; rebuild waves: block half
+  const WeightDesc W = find_weight(args, blockIdx.x);
+  const int local = blockIdx.x - W.item_begin;
+  const int split = local % W.splits;
+  const int rest = local / W.splits;
+  const int rg = rest % W.groups;
+  const int tg = rest / W.groups;
+  const int M = args.M;
+  const int tok0 = tg * 32 * TG;
+  const int wtok0 = tok0 + half * 32 * TT;  // (GEMM waves)
+  const int row0 = rg * GROUP_ROWS + 32 * rtile;
+  const int row = row0 + jl;
+  const int nb = W.nblocks, d = W.d;
+  const int cps = (W.nch + W.splits - 1) / W.splits;
+  const int c_begin = split * cps, c_end = min(W.nch, c_begin + cps);
+
+  float16v acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = (float16v){};
+
+  if (gemm) {
+    // activation staging straight into LDS: GEMM wave g fetches tokens 8 g .. 8 g + 7 of
+    // every tile (as tile_kernel's waves do)
+    const uint16_t* xbase = W.x + (size_t)tok0 * d;
+    const uint32_t xbytes = (uint32_t)min(M - tok0, 32 * TG) * 2u * (uint32_t)d;
+    const int dtok = 8 * role + (lane >> 3);
+    const int dunit = (lane & 7) ^ ((dtok >> 1) & 7);
+    const uint32_t dvo = (uint32_t)dtok * 2u * (uint32_t)d + 16u * dunit, xstep = 64u * (uint32_t)d;
+    auto stage_dma = [&](int c, int qk, int nb1) {
+      const int col0 = c * kChunkCols + 64 * qk;  // (uniform)
+      const uint32_t so = __builtin_amdgcn_readfirstlane(2u * (uint32_t)col0);
+      const rsrc_t xr = make_rsrc(xbase, xbytes);
+      uint32_t vo = dvo;
+      asm volatile("" : "+v"(vo));  // (keeps the per-tile offsets below from being hoisted out of the loop)
+      if (col0 + 8 * dunit >= d) vo = kBufOutOfRange;
+#pragma unroll
+      for (int t = 0; t < TG; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)&xs[nb1][t / TT][t % TT][8 * role][0], 16,
+                                                 vo >= kBufOutOfRange ? vo : vo + (uint32_t)t * xstep, so, 0, 0);
+    };
+    for (int b0 = 0; b0 < nb && c_begin < c_end; b0 += kTileBatch) {
+      stage_dma(c_begin, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0);  // (the staged activations are in LDS)
+      lds_barrier();                  // ... and the rebuild waves' first step is published
+      for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+        for (int qk = 0; qk < 8; ++qk) {
+          const int buf = qk & 1;
+          stage_dma(qk == 7 ? c + 1 : c, (qk + 1) & 7, buf ^ 1);  // the next step's activations
+          // the step's W_hat pairs: the two rebuild waves' shares, block half 0 first,
+          // split by plane: bw[z][s] = W_hat[row][plane 2 qk + z, columns 16 h + 8 s .. + 7]
+          u32x4 bw[2][2];
+          {
+            half2v full[16];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const u32x4 a = wpart[buf][2 * rtile][k][lane], b = wpart[buf][2 * rtile + 1][k][lane];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) full[4 * k + e] = as_half2(a[e]) + as_half2(b[e]);
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+              for (int m2 = 0; m2 < 4; ++m2) {
+                const uint32_t lo = as_u32(full[8 * s2 + 2 * m2]), hi = as_u32(full[8 * s2 + 2 * m2 + 1]);
+                bw[0][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+                bw[1][s2][m2] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+              }
+          }
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) {
+            half8 xa[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int z = g >> 1, s2 = g & 1;
+              xa[g] = as_half8(xs[buf][half][tt][jl][(4 * z + 2 * h + s2) ^ ((jl >> 1) & 7)]);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[g], as_half8(bw[g >> 1][g & 1]), acc[tt], 0, 0, 0);
+          }
+          __builtin_amdgcn_s_waitcnt(0);  // this wave's staging of the next step is in LDS
+          lds_barrier();                  // next step staged and published; this step's buffers are free
+        }
+      }
+    }
+  } else {
+    const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
+    const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
+    const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
+    const uint32_t uoff = (uint32_t)row * (kRank * 2) + 16u * h;
+    const uint32_t chunk_sign_bytes = (uint32_t)W.mt * kTileBytes;
+    uint32_t vmask = 0x80008000u;
+    asm volatile("" : "+v"(vmask));
+    for (int b0 = 0; b0 < nb && c_begin < c_end; b0 += kTileBatch) {
+      const int nbw = min(BPW, max(0, nb - b0 - half * BPW));
+      const uint8_t* sbase[BPW];
+      const uint16_t* vbase[BPW];
+      half8 uf[BPW];
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + half * BPW + i : b0);
+        sbase[i] = bp.signs;
+        vbase[i] = bp.vr;
+        uf[i] = as_half8(buf_load16(make_rsrc(bp.ur), i < nbw ? uoff : kBufOutOfRange));
+      }
+      uint32_t sw[BPW][2][4];
+      auto load_signs = [&](int c, int hq) {
+        const uint32_t cb = __builtin_amdgcn_readfirstlane((uint32_t)min(c, c_end - 1) * chunk_sign_bytes);
+#pragma unroll
+        for (int i = 0; i < BPW; ++i)
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            const u32x2 v = buf_load8(make_rsrc(sbase[i]), soff + 256u * g2 + 8u * hq, cb);
+            sw[i][g2][2 * hq] = v[0];
+            sw[i][g2][2 * hq + 1] = v[1];
+          }
+      };
+      struct VP { u32x4 a, b; };
+      auto load_v = [&](int c, int qk, int i) {
+        const int cc = min(c, c_end - 1);
+        const uint32_t cb = __builtin_amdgcn_readfirstlane((uint32_t)(cc * kChunkCols + 64 * qk) * (kRank * 2));
+        VP v;
+        v.a = buf_load16(make_rsrc(vbase[i]), voff, cb);
+        v.b = buf_load16(make_rsrc(vbase[i]), voff + 32u * kRank * 2u, cb);
+        return v;
+      };
+      auto recon_math = [&](const float16v& d0, const float16v& d1, int i, int qk, half2v (&wp)[16]) {
+        const int q = qk >> 1, kp = qk & 1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t sp = tile_sign_pair(sw[i][v >> 3][q], v & 7, kp, vmask);
+          const half2v dp = __builtin_convertvector((float2v){d0[v], d1[v]}, half2v);
+          wp[v] = as_half2(sp) * dp + wp[v];
+        }
+      };
+      auto publish = [&](const half2v (&wp)[16], int slot) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          wpart[slot][role][k][lane] = (u32x4){as_u32(wp[4 * k]), as_u32(wp[4 * k + 1]), as_u32(wp[4 * k + 2]), as_u32(wp[4 * k + 3])};
+      };
+      load_signs(c_begin, 0);
+      load_signs(c_begin, 1);
+      VP vq[BPW];  // V rows of every block of the next step to rebuild
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) vq[i] = load_v(c_begin, 0, i);
+      half2v wp[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+#pragma unroll
+      for (int i = 0; i < BPW; ++i) {
+        const VP cur = vq[i];
+        vq[i] = load_v(c_begin, 1, i);
+        float16v d0 = rebuild_mfma(as_half8(cur.a), uf[i]);
+        float16v d1 = rebuild_mfma(as_half8(cur.b), uf[i]);
+        mfma_result_ready(d0, d1);
+        recon_math(d0, d1, i, 0, wp);
+      }
+      publish(wp, 0);
+      lds_barrier();
+      for (int c = c_begin; c < c_end; ++c) {
+#pragma unroll
+        for (int qk = 0; qk < 8; ++qk) {
+          const int buf = qk & 1;
+          const int qkn = (qk + 1) & 7;                               // the step rebuilt now
+          const int cnn = qk >= 6 ? c + 1 : c, qknn = (qk + 2) & 7;  // the one after
+          if (qk == 3) load_signs(c + 1, 0);  // quads 0-1 of this chunk are done with
+          if (qk == 7) load_signs(c + 1, 1);  // quads 2-3 likewise
+#pragma unroll
+          for (int v = 0; v < 16; ++v) wp[v] = (half2v){};
+          // each block's MFMAs are issued before the previous block's sign work, which
+          // covers their latency
+          float16v dn0 = rebuild_mfma(as_half8(vq[0].a), uf[0]);
+          float16v dn1 = rebuild_mfma(as_half8(vq[0].b), uf[0]);
+#pragma unroll
+          for (int i = 0; i < BPW; ++i) {
+            vq[i] = load_v(cnn, qknn, i);
+            float16v d0 = dn0, d1 = dn1;
+            if (i + 1 < BPW) {
+              dn0 = rebuild_mfma(as_half8(vq[i + 1].a), uf[i + 1]);
+              dn1 = rebuild_mfma(as_half8(vq[i + 1].b), uf[i + 1]);
+            }
+            mfma_result_ready(d0, d1);
+            recon_math(d0, d1, i, qkn, wp);
+          }
+          publish(wp, buf ^ 1);
+          lds_barrier();
+        }
+      }
+    }
+  }
+
+  // GEMM lane (h, j) holds row row0 + j and tokens 8 (v / 4) + 4 h + v % 4 of every tile
+  if (W.splits == 1) {
+    if (gemm && row < W.m) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int t = wtok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (t < M) store_y(W.y, (size_t)t * W.m + row, acc[tt][v], args.y_fp32);
+        }
+    }
+    return;
+  }
+  const size_t tokpad = (size_t)token_groups * 32 * TG;
+  const size_t rows_pad = (size_t)W.mt * kTileRows;
+  if (gemm) {
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = wtok0 + 32 * tt + 8 * (v >> 2) + 4 * h + (v & 3);
+        __hip_atomic_store(&W.partial[((size_t)split * tokpad + t) * rows_pad + row], acc[tt][v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+  }
+  publish_partials();  // the partial sums above are visible before the arrival is counted
+  __syncthreads();     // ... in every wave, and every wave is done with xs
+  uint32_t* last = reinterpret_cast<uint32_t*>(&xs[0][0][0][0][0]);
+  if (threadIdx.x == 0) *last = count_arrival(&W.counters[rest]) == (uint32_t)(W.splits - 1);
+  __syncthreads();
+  if (!*last) return;
+  const int rbeg = rg * GROUP_ROWS;
+  for (int e = threadIdx.x; e < GROUP_ROWS * 32 * TG; e += 512) {
+    const int t = tok0 + e / GROUP_ROWS, r = rbeg + e % GROUP_ROWS;
+    if (r >= W.m || t >= M) continue;
+    float sum = 0.f;
+    for (int sp = 0; sp < W.splits; ++sp)
+      sum += __hip_atomic_load(&W.partial[((size_t)sp * tokpad + t) * rows_pad + r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_y(W.y, (size_t)t * W.m + r, sum, args.y_fp32);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ============================================================ single-token kernel, wave-private operands
 // One worker per wave: four waves per workgroup (one per SIMD), one workgroup per CU.  The
 // work is the list of units (weight, row group of R row tiles, block, 512-column chunk) in
@@ -1880,7 +2134,7 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
     case 1: hipLaunchKernelGGL((tile_kernel<1, 2>), grid, dim3(256), 0, st, args, token_groups); break;
     case 2: hipLaunchKernelGGL((tile_kernel<2, 2>), grid, dim3(256), 0, st, args, token_groups); break;
     case 4: hipLaunchKernelGGL((tile_kernel<4, 2>), grid, dim3(256), 0, st, args, token_groups); break;
-    case 8: hipLaunchKernelGGL((tile_kernel<8, 2>), grid, dim3(256), 0, st, args, token_groups); break;
+    case 8: hipLaunchKernelGGL(tile_split_kernel, grid, dim3(512), 0, st, args, token_groups); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -1292,10 +1292,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------ tile path, 512-token groups
-// The item, arithmetic and results of tile_kernel<8, 2>, with the rebuild and the GEMM in
-// different waves: 8 waves, two per SIMD (256 registers each).  Waves 0-3 (GEMM waves)
-// own row tile w / 2 and token half w % 2 (8 tiles of 32 tokens), stage the activations
+// ------------------------------------------------------------ tile path, split roles
+// The item, arithmetic and results of tile_kernel<TT, 2>, with the rebuild and the GEMM
+// in different waves: 8 waves, two per SIMD (256 registers each).  Waves 0-3 (GEMM waves)
+// own row tile w / 2 and token half w % 2 (TT tiles of 32 tokens), stage the activations
 // and multiply; waves 4-7 (rebuild waves) own row tile (w - 4) / 2 and block half
 // (w - 4) % 2 of each batch, and hand their partial W_hat pairs of the next step to the
 // GEMM waves through LDS.  A SIMD then runs one wave's sign work while the other's MFMAs
@@ -1303,8 +1303,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
 // other: a wave alone on its SIMD would take the rebuild's VALU chain, the activation
 // loads and the step barrier one after the other.  The two partial tiles are added in
 // the order tile_kernel adds them, so both kernels give the same bits.
+template <int TT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void tile_split_kernel(GroupArgs args, int token_groups) {
-  constexpr int TT = 8, TH = 2, TG = TT * TH, GROUP_ROWS = 64, BPW = kTileBatch / 2;
+  constexpr int TH = 2, TG = TT * TH, GROUP_ROWS = 64, BPW = kTileBatch / 2;
   __shared__ u32x4 xs[2][TH][TT][32][8];  // activations of a step (layout of tile_kernel's xs0 / xs1), two buffers
   __shared__ u32x4 wpart[2][4][4][64];     // partial W_hat pairs of a step from the rebuild waves, two buffers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2132,9 +2133,9 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
   const dim3 grid((unsigned)args.total_items);
   switch (token_tiles) {
     case 1: hipLaunchKernelGGL((tile_kernel<1, 2>), grid, dim3(256), 0, st, args, token_groups); break;
-    case 2: hipLaunchKernelGGL((tile_kernel<2, 2>), grid, dim3(256), 0, st, args, token_groups); break;
-    case 4: hipLaunchKernelGGL((tile_kernel<4, 2>), grid, dim3(256), 0, st, args, token_groups); break;
-    case 8: hipLaunchKernelGGL(tile_split_kernel, grid, dim3(512), 0, st, args, token_groups); break;
+    case 2: hipLaunchKernelGGL(tile_split_kernel<2>, grid, dim3(512), 0, st, args, token_groups); break;
+    case 4: hipLaunchKernelGGL(tile_split_kernel<4>, grid, dim3(512), 0, st, args, token_groups); break;
+    case 8: hipLaunchKernelGGL(tile_split_kernel<8>, grid, dim3(512), 0, st, args, token_groups); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

@@ -234,16 +234,17 @@ PROFILE_KERNELS = (
      sum(2 * 8 * K_RANK * 1 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
     ("decode_wp_kernel<4, 4> (8B-shaped layer, n=8, M=4)", "void bsl::decode_wp_kernel<4, 4>", None,
      sum(2 * 8 * K_RANK * 4 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
-    ("tile_kernel (8B-shaped layer, n=8, M=2048)", "void bsl::tile_kernel", None,
+    ("tile_split_kernel<8> (8B-shaped layer, n=8, M=2048)", "void bsl::tile_split_kernel<8>", None,
      sum((2 * K_RANK * 8 * 4 + 2 * 2048) * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
 )
 
 
 def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_dir: str, write_dir: str,
-                            command: str) -> None:
+                            command: str, mem_dir: str | None = None) -> None:
     """Turn rocprofv3 outputs of `bench.py --profile-set` runs (one --kernel-trace --stats
-    run, two --pmc passes of SQ counters, one FETCH_SIZE and one WRITE_SIZE pass) into the
-    short text summaries kept under profiles/."""
+    run, two --pmc passes of SQ counters, one FETCH_SIZE and one WRITE_SIZE pass, and
+    optionally a pass of vector-memory-path counters) into the short text summaries kept
+    under profiles/."""
     import csv
     import glob
     import hashlib
@@ -289,6 +290,7 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
 
     med = statistics.median
     c1, c2 = counters(sq1_dir), counters(sq2_dir)
+    c3 = counters(mem_dir) if mem_dir else {}
     out = ["# rocprofv3 --pmc SQ counters, two passes of bench.py --profile-set; medians per dispatch.",
            "# SQ counters are sums over the 32 shader engines (8 XCDs); the shader clock is SQ_BUSY_CYCLES / 32 over",
            "# the dispatch's duration in the counter run (dispatches run one at a time there); MFMA busy is",
@@ -296,6 +298,8 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
            "# (the sparse 16x16x64 instruction counts at its dense-equivalent 32768 flops, twice the 16384 it does",
            "# for the layer).",
            f"pass 1: {cmd[1].strip() if len(cmd) > 1 else ''}", f"pass 2: {cmd[2].strip() if len(cmd) > 2 else ''}",
+           *([f"pass 3 (vector memory path; busy fractions over GRBM_GUI_ACTIVE / 8 cycles and 256 CUs): {cmd[5].strip()}"]
+             if mem_dir and len(cmd) > 5 else []),
            f"kernel_source_sha256: {digest}", ""]
     for label, prefix, grid, algo in PROFILE_KERNELS:
         k1 = [k for k in c1 if pick(k[0], k[1], prefix, grid)]
@@ -325,7 +329,18 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
                 f"wave cycles waiting on dependencies (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES): {med(b['SQ_WAIT_INST_ANY']) / med(b['SQ_WAVE_CYCLES']):.3f}",
                 f"VALU active / wave cycles: {med(b['SQ_ACTIVE_INST_VALU']) / med(b['SQ_WAVE_CYCLES']):.3f}",
                 f"LDS active (SQ_LDS_IDX_ACTIVE / (32 x cycles x 8 CUs)): {med(b['SQ_LDS_IDX_ACTIVE']) / (cyc * 256):.3f}",
-                f"LDS bank conflicts: {med(b['SQ_LDS_BANK_CONFLICT']):.0f}", ""]
+                f"LDS bank conflicts: {med(b['SQ_LDS_BANK_CONFLICT']):.0f}"]
+        k3 = [k for k in c3 if pick(k[0], k[1], prefix, grid)]
+        if k3:
+            m = c3[k3[0]]
+            gui = med(m["GRBM_GUI_ACTIVE"]) / 8
+            req = med(m["TCP_TCC_READ_REQ_sum"])
+            hit, miss = med(m["TCC_HIT_sum"]), med(m["TCC_MISS_sum"])
+            out += [f"TA busy (address unit, per CU): {med(m['TA_TA_BUSY_sum']) / 256 / gui:.3f}",
+                    f"TD busy (data return unit, per CU): {med(m['TD_TD_BUSY_sum']) / 256 / gui:.3f}",
+                    f"L2 hit rate: {hit / (hit + miss):.3f}",
+                    f"average L1-to-L2 read latency: {med(m['TCP_TCC_READ_REQ_LATENCY_sum']) / req:.0f} cycles"]
+        out.append("")
     with open(os.path.join(ROOT, "profiles", "sq_counters_llama3_8b_layer.txt"), "w") as f:
         f.write("\n".join(out) + "\n")
 
@@ -530,12 +545,14 @@ def main() -> None:
     ap.add_argument("--write-profile-summaries", nargs=6,
                     metavar=("TRACE_DIR", "SQ1_DIR", "SQ2_DIR", "FETCH_DIR", "WRITE_DIR", "COMMANDS"),
                     help="write profiles/ summaries from rocprofv3 outputs (no GPU work)")
+    ap.add_argument("--mem-dir", default=None,
+                    help="with --write-profile-summaries: rocprofv3 output of the vector-memory-path counter pass")
     args = ap.parse_args()
     if args.profile_set:
         args.no_cpu = args.no_svd = args.no_sweep = args.no_70b = args.no_load = args.no_peaks = True
         args.calibrate_copy = True
     if args.write_profile_summaries:
-        write_profile_summaries(*args.write_profile_summaries)
+        write_profile_summaries(*args.write_profile_summaries, mem_dir=args.mem_dir)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
@@ -727,7 +744,7 @@ def main() -> None:
             "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M=2048, one grouped launch per step, tile path",
             "ms_per_step": round(t_step * 1e3, 3),
             "tokens_per_s": round(2048 / t_step, 1),
-            "kernel": "tile_kernel",
+            "kernel": "tile_split_kernel<8>",
             "mfma_flops_per_step": pre.tile_flops(0),
             "roofline": {"bound": "mfma", "achieved": round(pre.tile_flops(0) / k_step / 1e12, 1),
                          "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -779,7 +796,7 @@ def main() -> None:
             w_, k_, b_, f_ = time_steps(torch, lay, steps, 5)
             kus = float(np.mean(k_)) * 1e-3
             row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
-                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel)" if M >= 5 else "few-token (decode_wp_kernel<4, 4>)"),
+                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel<1, 2>)" if M >= 5 else "few-token (decode_wp_kernel<4, 4>)"),
                    "bytes_per_step": lay.bytes(0), "GB_per_s": round(lay.bytes(0) / kus / 1e9, 1)}
             if M == 1:
                 row["roofline"] = {"bound": "hbm", "achieved": row["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -575,7 +575,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // buffer, c0's Z tile in zs[buf], its U fragments in uf, and unit c1's V fragments
   // and activations in vv / xv.  Unit c2's signs are fetched into `cur` as soon as the
   // tiles are done with it, so a sign tile is requested well over one unit ahead.
-  auto step = [&](u32x4 (&cur)[R], const int buf) {
+  auto step = [&](u32x4 (&cur)[R], const int buf) __attribute__((always_inline)) {
     lds_barrier();  // the B operands of c0 are complete; zs[buf ^ 1] (unit c - 1) is free
     // Unit c1's B operands, the next V / x loads and the cursor advance: the upper half
     // of the waves does them before its tiles and the lower half after, so on every SIMD
@@ -1876,7 +1876,7 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 
   // ---- one unit: c0 with signs in `cur`; on entry plane 0's operands are ready, V of
   // planes 1..15 of c0 and of plane 0 of c1 are in vsl
-  auto step = [&](u32x4 (&cur)[R], u32x4 (&nxt)[R]) {
+  auto step = [&](u32x4 (&cur)[R], u32x4 (&nxt)[R]) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
     load_signs(p1, nxt);
     __builtin_amdgcn_sched_barrier(0);

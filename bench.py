@@ -232,7 +232,7 @@ PROFILE_KERNELS = (
     # (label, kernel name prefix, grid size of the profiled launch or None, algorithmic flops per launch)
     ("decode_m1_kernel (8B-shaped layer, n=8, M=1)", "void bsl::decode_m1_kernel", 256 * 1024,
      sum(2 * 8 * K_RANK * 1 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
-    ("decode_wp_kernel<4, 4> (8B-shaped layer, n=8, M=4)", "void bsl::decode_wp_kernel<4, 4>", None,
+    ("decode_wp_kernel<8, 4> (8B-shaped layer, n=8, M=4)", "void bsl::decode_wp_kernel<8, 4>", None,
      sum(2 * 8 * K_RANK * 4 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
     ("tile_split_kernel<8> (8B-shaped layer, n=8, M=2048)", "void bsl::tile_split_kernel<8>", None,
      sum((2 * K_RANK * 8 * 4 + 2 * 2048) * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
@@ -704,7 +704,7 @@ def main() -> None:
     # ---------------- a few tokens (batched decode): the wave-private kernel over T tokens
     if not args.no_few:
         few = []
-        kern = {2: "decode_wp_kernel<8, 2>", 3: "decode_wp_kernel<4, 3>", 4: "decode_wp_kernel<4, 4>"}
+        kern = {2: "decode_wp_kernel<8, 2>", 3: "decode_wp_kernel<8, 3>", 4: "decode_wp_kernel<8, 4>"}
         sets = (("8B", shapes, [8] * 7), ("70B", synth.LLAMA2_70B_LAYER, [3] * 7))
         for label, lshapes, counts in (sets[:1] if args.profile_set else sets):
             for M in ((4,) if args.profile_set else (2, 3, 4)):
@@ -796,7 +796,7 @@ def main() -> None:
             w_, k_, b_, f_ = time_steps(torch, lay, steps, 5)
             kus = float(np.mean(k_)) * 1e-3
             row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
-                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel<1, 2>)" if M >= 5 else "few-token (decode_wp_kernel<4, 4>)"),
+                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel<1, 2>)" if M >= 5 else "few-token (decode_wp_kernel<8, 4>)"),
                    "bytes_per_step": lay.bytes(0), "GB_per_s": round(lay.bytes(0) / kus / 1e9, 1)}
             if M == 1:
                 row["roofline"] = {"bound": "hbm", "achieved": row["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -780,10 +780,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     }
     return worst;
   };
-  // Plan of the wave-private kernel for T tokens (row groups of 256, 128, 64 and 64 rows
-  // for T = 1 to 4); false when a workgroup's activations do not fit its LDS.
+  // Plan of the wave-private kernel for T tokens (row groups of 256 rows for T = 1, 128
+  // rows for T = 2 to 4); false when a workgroup's activations do not fit its LDS.
   auto plan_private = [&](int T, int& lg) {
-    plan_units(T == 3 ? kWpRows / 4 : kWpRows / T);
+    plan_units(T == 1 ? kWpRows : kWpFewRows);
     // workers: four per workgroup, at most one workgroup per CU, at most one per unit
     int32_t workers = kWpWaves * s->decode_grid_max;
     while (workers > kWpWaves && (uint64_t)workers > units) workers /= 2;
@@ -860,7 +860,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     const int T = M;
     int lg = 0;
     if (plan_private(T, lg)) {
-      const int rc = launch_units(lg, (size_t)kWpRows);  // (rows x tokens of a row group: at most kWpRows)
+      const int rc = launch_units(lg, (size_t)kWpFewRows * T);  // (rows x tokens of a row group)
       if (rc != BSL_OK) return rc;
       e = launch_decode_wp(args, T, stream);
       if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");

@@ -106,10 +106,10 @@ constexpr int kXcds = 8;  // MI355X: workgroups are dealt round-robin over 8 XCD
 // Single-token path, wave-private kernel: one worker per wave, four waves per workgroup
 // (one per SIMD), one workgroup per CU; units of 16 row tiles (256 rows).  A workgroup
 // keeps the activations of the weights its units belong to in LDS (at most kWpXBytes).
-// The same kernel takes T = 2, 3 or 4 tokens with units of 8, 4 and 4 row tiles, so that
-// a piece (rows x tokens) holds at most kWpRows floats.
+// The same kernel takes T = 2, 3 or 4 tokens with units of 8 row tiles (kWpFewRows).
 constexpr int kWpTiles = 16;
 constexpr int kWpRows = kWpTiles * 16;
+constexpr int kWpFewRows = 128;
 constexpr int kWpWaves = 4;
 constexpr int kWpXBytes = 148 * 1024;
 constexpr int kWpMaxTokens = 4;

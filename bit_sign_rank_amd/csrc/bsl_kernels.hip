@@ -1598,9 +1598,11 @@ __device__ __forceinline__ u32x8 pm_v_operand(const u32x4& v) {
 // s_waitcnt immediate for "at most n vector memory operations outstanding" (n < 64).
 __host__ __device__ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-// R row tiles per wave and T tokens (R T <= 16: the accumulators of a 16-tile wave): the
-// tokens share every B operand, sign index and load; each has its own A operand (its
-// activations), accumulators and row-accumulator adds.  T is the launch's token count.
+// R row tiles per wave and T tokens (R T <= 32 accumulator tiles): the tokens share every
+// B operand, sign index and load; each has its own A operand (its activations),
+// accumulators and row-accumulator adds.  T is the launch's token count.  A unit's V
+// (16 KiB) does not depend on its rows, so units of 128 rows or more keep the V bytes at
+// most twice the sign bytes.
 template <int R, int T>
 __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wp_kernel(GroupArgs args) {
   constexpr int ROWS = 16 * R;  // rows per unit
@@ -2106,8 +2108,8 @@ int launch_decode_wp(const GroupArgs& args, int tokens, void* stream) {
   switch (tokens) {
     case 1: hipLaunchKernelGGL((decode_wp_kernel<16, 1>), grid, block, 0, st, args); break;
     case 2: hipLaunchKernelGGL((decode_wp_kernel<8, 2>), grid, block, 0, st, args); break;
-    case 3: hipLaunchKernelGGL((decode_wp_kernel<4, 3>), grid, block, 0, st, args); break;
-    case 4: hipLaunchKernelGGL((decode_wp_kernel<4, 4>), grid, block, 0, st, args); break;
+    case 3: hipLaunchKernelGGL((decode_wp_kernel<8, 3>), grid, block, 0, st, args); break;
+    case 4: hipLaunchKernelGGL((decode_wp_kernel<8, 4>), grid, block, 0, st, args); break;
     default: return (int)hipErrorInvalidValue;
   }
   return (int)hipGetLastError();

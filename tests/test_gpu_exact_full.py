@@ -66,6 +66,8 @@ RUNS = [
     (4, FACT, None, "factored"),
     (16, AUTO, None, "tile"),
     (16, FACT, None, "factored"),
+    (100, AUTO, None, "tile"),
+    (200, AUTO, None, "tile"),
     (2048, AUTO, None, "tile"),
     (2048, FACT, None, "factored"),
 ]

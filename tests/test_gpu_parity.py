@@ -258,10 +258,11 @@ def test_prefill_ragged_shapes(m, d, M, path):
     assert rel_err(y, oracle.forward(x, blocks, 3)) <= REL_TOL
 
 
-# token-group edges of the tile path (groups of up to 512 tokens; the last group partial),
-# one and two 8-block batches, ragged rows / columns
+# token-group edges of the tile path (groups of 64, 128, 256 and 512 tokens; the last group
+# partial), one and two 8-block batches, ragged rows / columns
 @pytest.mark.parametrize("m,d,M,n", [(130, 1032, 511, 3), (256, 512, 512, 9), (37, 520, 513, 1), (300, 1536, 1100, 11),
-                                     (1024, 2048, 7, 16), (16, 8, 40, 2)])
+                                     (1024, 2048, 7, 16), (16, 8, 40, 2), (200, 1536, 100, 5), (72, 2560, 128, 9),
+                                     (300, 2560, 250, 9), (64, 512, 256, 2)])
 def test_tile_token_groups_and_batches(m, d, M, n):
     blocks = synth.synthetic_blocks(31, m, d, n, 16, m, d)
     x = synth.activations(32, M, d)
@@ -272,6 +273,7 @@ def test_tile_token_groups_and_batches(m, d, M, n):
     ref = oracle.forward(x, blocks, n)
     assert rel_err(y, ref) <= REL_TOL
     assert rel_err(y16, ref) <= REL_TOL
+    assert_elementwise(y, ref, elem_factor("tile", n, d) * abs_bound(x, blocks, n), f"tile m={m} d={d} M={M} n={n}")
 
 
 @pytest.mark.parametrize("path", PATHS, ids=PATH_IDS)

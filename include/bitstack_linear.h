@@ -78,7 +78,9 @@ size_t bsl_block_bytes(int64_t m, int64_t d, int32_t k);
 size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
 
 /* Host-side "bitstack_pack": convert row-major sign bits (format of bsl_block_src)
- * into the tiled device layout.  tiled_out (host) must hold bsl_packed_sign_bytes(m, d)
+ * into the tiled device layout (the sign matrix packed into a GPU data layout:
+ * paper-review page, Figure 3 caption).  bsl_load_blocks produces the same layout on
+ * the device; this host version serves checks and callers that pack ahead of time.  tiled_out (host) must hold bsl_packed_sign_bytes(m, d)
  * bytes.  Layout: tiles of 16 rows x 512 columns, ordered [column chunk][row tile];
  * each tile is 64 lanes x 16 bytes; lane L = 16*g + i holds row i of the tile and four
  * little-endian 32-bit words q = 0..3.  Of the chunk's 32-column plane b = 4*q + k
@@ -90,7 +92,8 @@ size_t bsl_packed_sign_bytes(int64_t m, int64_t d);
 int bsl_pack_signs(const uint8_t* rowmajor_bits, int64_t m, int64_t d, uint8_t* tiled_out);
 
 /* Inverse of bsl_pack_signs, for checking: writes int8 +1/-1 into pm1_out (host,
- * m*d bytes, row-major).  Padding is ignored. */
+ * m*d bytes, row-major), i.e. the unpack step of the weight restoration (OpenReview
+ * discussion, weight-restoration reply).  Padding is ignored. */
 int bsl_unpack_signs(const uint8_t* tiled, int64_t m, int64_t d, int8_t* pm1_out);
 
 /* Create a stack for num_weights weights with shapes m[w] x d[w] (host arrays), rank k
@@ -138,7 +141,8 @@ int bsl_set_input_scale(bsl_stack* s, int32_t w, const float* inv_scale);
  * Figure 2 caption.) */
 int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
 
-/* Number of loaded blocks of weight w. */
+/* Number of loaded blocks of weight w: the n of W_hat_n, which sets the weight's size
+ * (paper-review page, Figure 2 caption). */
 int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
 
 /* Device bytes currently held by loaded blocks (what budget_bytes caps).  A loaded block
@@ -148,7 +152,10 @@ int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
  * row). */
 uint64_t bsl_resident_bytes(const bsl_stack* s);
 
-/* y = x W_hat_n^T for weight w with its n loaded blocks.
+/* y = x W_hat_n^T for weight w with its n loaded blocks: the linear layer with the
+ * weight the authors restore block by block (OpenReview discussion, weight-restoration
+ * reply), computed from the packed blocks (BSL_PATH_FACTORED never forms W_hat;
+ * BSL_PATH_TILE forms it only per tile in registers).
  *   x: device, fp16 [M][d] row-major, 16-byte aligned.
  *   y: device, [M][m] row-major, fp16 (y_is_fp32 == 0, round to nearest even) or fp32.
  *   M >= 1 tokens.  With n = 0 loaded blocks y is all zeros.
@@ -224,7 +231,10 @@ int bsl_set_path(bsl_stack* s, int32_t path);
 int bsl_set_decode(bsl_stack* s, int32_t kind);
 
 /* Run a forward kernel's own sign-unpack code on block i of weight w and write the
- * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes).
+ * signs as int8 +1/-1, row-major m x d, to pm1_out (device, m*d bytes): the unpack
+ * step of the weight restoration (OpenReview discussion, weight-restoration reply), as
+ * each kernel performs it.  The `path` argument, which selects the kernel, is an
+ * addition for checking.
  * path 0: the single-token kernel's sparse-MFMA indices; path 1: the multi-token
  * kernel's +-1 fp16 A fragments; path 2: the tile-reconstruct kernel's +-1 fp16 pairs. */
 int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* pm1_out, void* stream);

@@ -151,27 +151,6 @@ void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
   std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
 }
 
-// U (m x 16, row-major fp16) -> [m_pad][16], zero past m.
-void rowmajor_u(const uint16_t* u, int64_t m, uint16_t* out) {
-  std::memcpy(out, u, (size_t)m * kRank * 2);
-  std::memset(out + m * kRank, 0, (size_t)(pad_rows(m) - m) * kRank * 2);
-}
-
-// V (d x 16, row-major fp16) -> [d_pad/512][16][64][8] in the single-token kernel's
-// B-operand order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] for
-// j < 4 and V[512 c + 32 b + 16 + 4 kk + j - 4][r] for j >= 4 (zero past d).
-void bop_v(const uint16_t* v, int64_t d, uint16_t* out) {
-  const int64_t nch = pad_cols(d) / kChunkCols;
-  for (int64_t c = 0; c < nch; ++c)
-    for (int b = 0; b < kPlanes; ++b)
-      for (int L = 0; L < 64; ++L)
-        for (int j = 0; j < 8; ++j) {
-          const int kk = L / 16, r = L % 16;
-          const int64_t col = 512 * c + 32 * b + (j < 4 ? 4 * kk + j : 16 + 4 * kk + j - 4);
-          out[((c * kPlanes + b) * 64 + L) * 8 + j] = col < d ? v[col * kRank + r] : 0;
-        }
-}
-
 // V (d x 16) with row c multiplied by inv_scale[c]: one rounding of the exact product.
 bool scale_v(const uint16_t* v, int64_t d, const float* inv_scale, uint16_t* out) {
   for (int64_t c = 0; c < d; ++c)
@@ -224,9 +203,9 @@ struct bsl_stack {
 
 namespace {
 
-// signs + tiled U + tiled V + row-major V + B-ordered V + row-major U (see BlockPtrs)
+// signs + tiled U + tiled V + row-major V (see BlockPtrs)
 size_t slot_bytes(int64_t m, int64_t d) {
-  return (size_t)pad_rows(m) * pad_cols(d) / 8 + 2 * (size_t)pad_rows(m) * kRank * 2 + 3 * (size_t)pad_cols(d) * kRank * 2;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 2 * (size_t)pad_cols(d) * kRank * 2;
 }
 
 BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
@@ -239,8 +218,6 @@ BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
   p.u = reinterpret_cast<const uint16_t*>(base + sb);
   p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
   p.vr = reinterpret_cast<const uint16_t*>(base + sb + ub + vb);
-  p.vb = reinterpret_cast<const uint16_t*>(base + sb + ub + 2 * vb);
-  p.ur = reinterpret_cast<const uint16_t*>(base + sb + ub + 3 * vb);
   return p;
 }
 
@@ -261,7 +238,7 @@ int upload_table(Weight& W, int32_t lo, int32_t hi, hipStream_t st) {
   if (hi <= lo) return BSL_OK;
   std::vector<BlockPtrs> tab(hi - lo);
   for (int32_t i = lo; i < hi; ++i)
-    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
   hipError_t e = hipMemcpyAsync(W.dtable + lo, tab.data(), sizeof(BlockPtrs) * (hi - lo), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
@@ -518,7 +495,6 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     bool scaled_ok = true;
     std::thread factors([&] {
       tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac));
-      rowmajor_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac + ub + 3 * vb));
       const uint16_t* v = src.v;
       if (!W.inv_scale.empty()) {
         vscaled.resize((size_t)W.d * kRank);
@@ -530,7 +506,6 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
       }
       tile_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub));
       rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub + vb));
-      bop_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub + 2 * vb));
     });
     copy_mt(buf, src.sign_bits, raw);
     factors.join();
@@ -540,7 +515,7 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     }
     uint8_t* slot = static_cast<uint8_t*>(W.slots[a.i].mem);
     e = hipMemcpyAsync(s->raw_dev[k % 2], buf, raw, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(slot + sb, fac, 2 * ub + 3 * vb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot + sb, fac, ub + 2 * vb, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = static_cast<hipError_t>(launch_repack_signs(s->raw_dev[k % 2], W.m, W.d, W.mt, W.nch, slot, st));
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }

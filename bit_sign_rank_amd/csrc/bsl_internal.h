@@ -30,20 +30,16 @@ inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * 
 //   u:     [m_pad/16][64 lanes][4] fp16  lane L holds U[16 t + 4 (L/16) + v][L % 16]
 //   v:     [d_pad/512][16 planes][64 lanes][8] fp16
 //          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
-//   vr:    [d_pad][16] fp16, V row-major (zero past d): the tile-reconstruct kernel's
-//          matrix-core operand, 8 consecutive ranks of one column per 16-byte load
-//   vb:    [d_pad/512][16 planes][64 lanes][8] fp16, V in the single-token B-operand
-//          order: lane L = 16 kk + r of plane b holds V[512 c + 32 b + 4 kk + j][r] (j < 4)
-//          and V[512 c + 32 b + 16 + 4 kk + j - 4][r] (4 <= j < 8)
-//   ur:    [m_pad][16] fp16, U row-major (zero past m): the rebuild MFMA's B operand, 8
-//          consecutive ranks of one row per 16-byte load
+//   vr:    [d_pad][16] fp16, V row-major (zero past d): the tile-reconstruct kernels'
+//          matrix-core operand, 8 consecutive ranks of one column per 16-byte load (the
+//          rebuild contracts over the rank, the tiled copy holds 8 columns of one rank)
+// The wave-private kernel forms its B-operand order from two 8-byte loads of v, and
+// the tile kernels gather each row's 8 ranks of U from u once per batch.
 struct BlockPtrs {
   const uint8_t* signs;
   const uint16_t* u;
   const uint16_t* v;
   const uint16_t* vr;
-  const uint16_t* vb;
-  const uint16_t* ur;
 };
 
 // One weight of a (grouped) forward launch; passed by value in the kernel arguments.

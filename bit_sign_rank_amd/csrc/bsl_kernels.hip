@@ -134,8 +134,6 @@ __device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
   r.u = uniform_ptr(b.u);
   r.v = uniform_ptr(b.v);
   r.vr = uniform_ptr(b.vr);
-  r.vb = uniform_ptr(b.vb);
-  r.ur = uniform_ptr(b.ur);
   return r;
 }
 
@@ -148,8 +146,6 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.u = t->u;
   b.v = t->v;
   b.vr = t->vr;
-  b.vb = t->vb;
-  b.ur = t->ur;
   return b;
 }
 
@@ -977,6 +973,19 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off, uint32_t sof
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
+// U[row][8 h .. 8 h + 7] (eight ranks of one row, the rebuild MFMA's B operand) gathered
+// from the tiled U, where rank r of row j is element j % 4 of lane 16 ((j % 16) / 4) + r
+// of row tile j / 16 (8 bytes per lane, 512 bytes per row tile).  Zeros when !valid.
+__device__ __forceinline__ half8 load_u_ranks(const uint16_t* u, int row, int h, bool valid) {
+  const rsrc_t r = make_rsrc(u);
+  const uint32_t base = valid ? (uint32_t)(row >> 4) * 512u + (uint32_t)(16 * ((row & 15) >> 2) + 8 * h) * 8u + (uint32_t)(row & 3) * 2u
+                              : kBufOutOfRange;
+  half8 out;
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    out[k] = __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, base + 8u * k, 0u, 0));
+  return out;
+}
 
 // The rebuild's K = 16 MFMA, written out so that its result lands in VGPRs: a kernel
 // that may use all 512 registers gets every compiler-built MFMA in the accumulator-
@@ -1046,7 +1055,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
   const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
   const int row = row0 + jl;
   const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
-  const uint32_t uoff = (uint32_t)row * (kRank * 2) + 16u * h;  // U[row][8 h ..] in the row-major copy
   const uint32_t chunk_sign_bytes = (uint32_t)W.mt * kTileBytes;  // (a block's signs are < 2 GiB here)
 
   uint32_t vmask = 0x80008000u;
@@ -1066,7 +1074,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
       sbase[i] = bp.signs;
       vbase[i] = bp.vr;
       // U[row][8 h .. 8 h + 7] from the row-major copy (zeros for the repeated slots)
-      uf[i] = as_half8(buf_load16(make_rsrc(bp.ur), i < nbw ? uoff : kBufOutOfRange));
+      uf[i] = load_u_ranks(bp.u, row, h, i < nbw);
     }
     // sign words sw[i][g2][q] of the current chunk (quads 0-1 and 2-3 refilled separately)
     uint32_t sw[BPW][2][4];
@@ -1402,7 +1410,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
     const uint32_t voff = (uint32_t)sigma * (kRank * 2) + 16u * h;
     const uint32_t soff = ((uint32_t)(row >> 4) * 64u + 32u * h + (row & 15)) * 16u;
-    const uint32_t uoff = (uint32_t)row * (kRank * 2) + 16u * h;
     const uint32_t chunk_sign_bytes = (uint32_t)W.mt * kTileBytes;
     uint32_t vmask = 0x80008000u;
     asm volatile("" : "+v"(vmask));
@@ -1416,7 +1423,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + half * BPW + i : b0);
         sbase[i] = bp.signs;
         vbase[i] = bp.vr;
-        uf[i] = as_half8(buf_load16(make_rsrc(bp.ur), i < nbw ? uoff : kBufOutOfRange));
+        uf[i] = load_u_ranks(bp.u, row, h, i < nbw);
       }
       uint32_t sw[BPW][2][4];
       auto load_signs = [&](int c, int hq) {
@@ -1578,7 +1585,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // prepared during plane 15.
 struct WpPtrs {
   const uint8_t* signs;  // sign tiles of the unit's 16 row tiles (1 KiB each, consecutive)
-  const uint8_t* vb;     // B-ordered V of the unit's chunk, 16 planes x 1 KiB
+  const uint8_t* v;      // tiled V of the unit's chunk, 16 planes x 1 KiB
   const uint8_t* u;      // tiled U of the unit's 16 row tiles (512 B each)
 };
 
@@ -1698,14 +1705,13 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
                                    : uniform_ptr(reinterpret_cast<const uint8_t*>(bbase[c.j][c.i]));
       const size_t sb = (size_t)c.mt * c.nch * kTileBytes;  // signs
       const size_t ub = (size_t)c.mt * 64 * 8;              // tiled U
-      const size_t vbytes = (size_t)c.nch * kPlanes * 64 * 16;  // tiled V = row-major V = B-ordered V
       p.signs = base + ((size_t)c.ch * c.mt + (size_t)c.rg * R) * kTileBytes;
       p.u = base + sb + (size_t)c.rg * R * 64 * 8;
-      p.vb = base + sb + ub + 2 * vbytes + (size_t)c.ch * kPlanes * 64 * 16;
+      p.v = base + sb + ub + (size_t)c.ch * kPlanes * 64 * 16;
     } else {
       p.signs = zero_page;
       p.u = zero_page;
-      p.vb = zero_page;
+      p.v = zero_page;
     }
     return p;
   };
@@ -1718,7 +1724,17 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 #pragma unroll
     for (int t = 0; t < R; ++t) s[t] = load16_stream(p.signs + t * kTileBytes + lane * 16);
   };
-  auto load_v = [&](const WpPtrs& p, int b) { return load16(p.vb + (b * 64 + lane) * 16); };
+  // V words of plane b in the B-operand order (lane L = 16 kk + r: columns 4 kk .. 4 kk + 3
+  // and 16 + 4 kk .. 16 + 4 kk + 3 of the plane, rank r), from the tiled copy, where lane
+  // 16 g + r holds columns 8 g .. 8 g + 7: two 8-byte halves of lanes 16 (kk / 2) + r and
+  // 16 (2 + kk / 2) + r
+  const int vkk = lane >> 4, vr_ = lane & 15;
+  const uint32_t voff0 = (uint32_t)((16 * (vkk >> 1) + vr_) * 16 + 8 * (vkk & 1));
+  const uint32_t voff1 = voff0 + 32u * 16u;
+  auto load_v = [&](const WpPtrs& p, int b) {
+    const u32x2 lo = load8(p.v + b * 1024 + voff0), hi = load8(p.v + b * 1024 + voff1);
+    return (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  };
   auto load_u = [&](const uint8_t* u) {
 #pragma unroll
     for (int t = 0; t < R; ++t) uw[t] = load8(u + (t * 64 + lane) * 8);

@@ -677,8 +677,8 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
 }
 
 // use_static: the allocation-free variant (bsl_forward_group_static): 1 to 4 tokens on the
-// single- and few-token kernels only, their pieces and arrival counters in the device's
-// static scratch array instead of the stack's workspace.
+// single- and few-token kernels only, their row accumulators in the device's static
+// scratch array instead of the stack's workspace.
 int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
                  int32_t y_is_fp32, void* stream, bool use_static = false) {
   if (count < 1 || count > kMaxGroup) return fail(BSL_EINVAL, "forward: 1..8 weights per launch");

@@ -1007,6 +1007,8 @@ __device__ __forceinline__ void mfma_result_ready(float16v& d0, float16v& d1) {
 // nearly all of it) the kernel fits 256 registers and two workgroups share a CU, so one
 // wave's rebuild runs while the other waits on its loads (M = 16, 8B-shaped layer, n = 8:
 // 310 -> 239 us); larger TT keep one wave per SIMD and all 512 registers.
+// (Launched for TT = 1, groups of 64 tokens; larger groups take tile_split_kernel, which
+// keeps this kernel's arithmetic and layouts.)
 template <int TT, int TH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2 : 1, TT == 1 ? 2 : 1))) void tile_kernel(GroupArgs args, int token_groups) {
   constexpr int TG = TT * TH;             // 32-token tiles per workgroup
@@ -2070,8 +2072,8 @@ int launch_repack_signs(const uint8_t* raw, int64_t m, int64_t d, int32_t mt, in
 }
 
 // ============================================================ static scratch
-// Scratch memory of the allocation-free forward: the pieces and arrival counters of the
-// single- and few-token kernels, kStaticScratchBytes per device for the life of the
+// Scratch memory of the allocation-free forward: the row accumulators of the single- and
+// few-token kernels, kStaticScratchBytes per device for the life of the
 // process, shared by every such call on the device.  Host code never passes the array's
 // name to a kernel or a copy (on the host it is only a stand-in for the symbol): it uses
 // the device address static_scratch_setup takes once per device.

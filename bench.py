@@ -681,8 +681,14 @@ def main() -> None:
     bsl.bsl_load_blocks(probe, [8] * 7, 0)
     payload = sum(8 * block_bytes(m, d) for _, m, d in shapes)
     resident = bsl.bsl_resident_bytes(probe)
+    vbytes = sorted((8 * d * 32 for _, _, d in shapes), reverse=True)[:8]
     result["resident_bytes"] = {"workload": "one Llama-3-8B-shaped layer, n=8", "payload_bytes": payload,
-                                "resident_bytes": int(resident), "ratio": round(resident / payload, 4)}
+                                "resident_bytes": int(resident), "ratio": round(resident / payload, 4),
+                                "stack_workspace_bytes": int(bsl.bsl_workspace_bytes(probe)),
+                                "of_which_rank_major_v": int(sum(vbytes)),
+                                "note": "blocks hold one copy of each factor; the tile path forms V in rank-major "
+                                        "order per call in a stack workspace sized for the 8 weights with the most "
+                                        "V bytes (one per stack, whatever the number of layers)"}
     torch.cuda.synchronize()
     bsl.bsl_destroy(probe)
     for key in [k for k in bsl._sources if k[0] == probe]:

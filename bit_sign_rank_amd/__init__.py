@@ -42,6 +42,7 @@ EXPORTED = (
     "bsl_load_blocks",
     "bsl_active_blocks",
     "bsl_resident_bytes",
+    "bsl_workspace_bytes",
     "bsl_launch_counts",
     "bsl_forward",
     "bsl_forward_group",
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.bsl_active_blocks.argtypes = [c_vp, c_i32, ctypes.POINTER(c_i32)]
         L.bsl_resident_bytes.restype = c_u64
         L.bsl_resident_bytes.argtypes = [c_vp]
+        L.bsl_workspace_bytes.restype = c_u64
+        L.bsl_workspace_bytes.argtypes = [c_vp]
         L.bsl_launch_counts.argtypes = [c_vp, c_vp]
         L.bsl_forward.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp]
         L.bsl_forward_group.argtypes = [c_vp, c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_vp]
@@ -219,6 +222,10 @@ def bsl_active_blocks(stack: int, w: int) -> int:
 
 def bsl_resident_bytes(stack: int) -> int:
     return int(lib().bsl_resident_bytes(stack))
+
+
+def bsl_workspace_bytes(stack: int) -> int:
+    return int(lib().bsl_workspace_bytes(stack))
 
 
 def bsl_launch_counts(stack: int) -> list:

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <string>
 #include <thread>
@@ -145,12 +146,6 @@ void tile_v(const uint16_t* v, int64_t d, uint16_t* out) {
         }
 }
 
-// V (d x 16, row-major fp16) -> [d_pad][16], zero past d.
-void rowmajor_v(const uint16_t* v, int64_t d, uint16_t* out) {
-  std::memcpy(out, v, (size_t)d * kRank * 2);
-  std::memset(out + d * kRank, 0, (size_t)(pad_cols(d) - d) * kRank * 2);
-}
-
 // V (d x 16) with row c multiplied by inv_scale[c]: one rounding of the exact product.
 bool scale_v(const uint16_t* v, int64_t d, const float* inv_scale, uint16_t* out) {
   for (int64_t c = 0; c < d; ++c)
@@ -196,6 +191,10 @@ struct bsl_stack {
   uint8_t* raw_dev[2] = {nullptr, nullptr};   // device buffers of row-major sign bits awaiting the repack
   size_t raw_dev_bytes = 0;
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
+  uint16_t* vr_ws = nullptr;      // tile path: V of a launch's blocks in rank-major order (formed per call)
+  size_t vr_cap = 0;              // its bytes: enough for the kMaxGroup weights with the most V bytes
+  std::vector<void*> vr_retired;  // outgrown vr_ws buffers, freed once the device has drained
+  size_t vr_retired_bytes = 0;
   void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
   uint64_t launches[BSL_KERNEL_KINDS] = {0, 0, 0, 0};  // forward launches per kernel (bsl_launch_counts)
   std::vector<Weight> w;
@@ -203,9 +202,27 @@ struct bsl_stack {
 
 namespace {
 
-// signs + tiled U + tiled V + row-major V (see BlockPtrs)
+// Bytes of rank-major V that a tile-path launch of any group of weights may need with
+// `counts` loaded blocks: the kMaxGroup largest n pad_cols(d) 32 bytes.
+size_t vr_bytes_needed(const bsl_stack* s, const int32_t* counts) {
+  std::vector<size_t> b(s->w.size());
+  for (size_t w = 0; w < s->w.size(); ++w) b[w] = (size_t)counts[w] * pad_cols(s->w[w].d) * kRank * 2;
+  const size_t k = std::min<size_t>(kMaxGroup, b.size());
+  std::partial_sort(b.begin(), b.begin() + k, b.end(), std::greater<size_t>());
+  size_t t = 0;
+  for (size_t i = 0; i < k; ++i) t += b[i];
+  return t;
+}
+
+void free_retired(bsl_stack* s) {
+  for (void* p : s->vr_retired) (void)hipFree(p);
+  s->vr_retired.clear();
+  s->vr_retired_bytes = 0;
+}
+
+// signs + tiled U + tiled V (see BlockPtrs)
 size_t slot_bytes(int64_t m, int64_t d) {
-  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + 2 * (size_t)pad_cols(d) * kRank * 2;
+  return (size_t)pad_rows(m) * pad_cols(d) / 8 + (size_t)pad_rows(m) * kRank * 2 + (size_t)pad_cols(d) * kRank * 2;
 }
 
 BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
@@ -213,11 +230,9 @@ BlockPtrs slot_ptrs(const Slot& s, int64_t m, int64_t d) {
   const uint8_t* base = static_cast<const uint8_t*>(s.mem);
   const size_t sb = (size_t)pad_rows(m) * pad_cols(d) / 8;
   const size_t ub = (size_t)pad_rows(m) * kRank * 2;
-  const size_t vb = (size_t)pad_cols(d) * kRank * 2;
   p.signs = base;
   p.u = reinterpret_cast<const uint16_t*>(base + sb);
   p.v = reinterpret_cast<const uint16_t*>(base + sb + ub);
-  p.vr = reinterpret_cast<const uint16_t*>(base + sb + ub + vb);
   return p;
 }
 
@@ -238,7 +253,7 @@ int upload_table(Weight& W, int32_t lo, int32_t hi, hipStream_t st) {
   if (hi <= lo) return BSL_OK;
   std::vector<BlockPtrs> tab(hi - lo);
   for (int32_t i = lo; i < hi; ++i)
-    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr, nullptr};
+    tab[i - lo] = W.slots[i].mem ? slot_ptrs(W.slots[i], W.m, W.d) : BlockPtrs{nullptr, nullptr, nullptr};
   hipError_t e = hipMemcpyAsync(W.dtable + lo, tab.data(), sizeof(BlockPtrs) * (hi - lo), hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   return e == hipSuccess ? BSL_OK : hip_fail(e, "pointer table upload");
@@ -434,6 +449,11 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
       added.push_back({w, i});
     }
   }
+  // The tile path's rank-major V workspace grows here, so that no forward allocates.  An
+  // outgrown buffer may still be read by forwards queued on other streams: it is retired
+  // and freed where the device has drained (a shrink, bsl_destroy).
+  uint16_t* vr_new = nullptr;
+  size_t vr_new_cap = 0;
   auto undo = [&]() {
     for (const NewSlot& a : added) {
       Slot& sl = s->w[a.w].slots[a.i];
@@ -441,10 +461,20 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
       sl.mem = nullptr;
       sl.bytes = 0;
     }
+    if (vr_new) (void)hipFree(vr_new);
+    vr_new = nullptr;
   };
   if (e != hipSuccess) {
     undo();
     return hip_fail(e, "hipMalloc(block)");
+  }
+  if (const size_t vneed = vr_bytes_needed(s, n_per_weight); vneed > s->vr_cap) {
+    vr_new_cap = std::max(vneed, s->vr_cap + s->vr_cap / 2);
+    if ((e = hipMalloc(reinterpret_cast<void**>(&vr_new), vr_new_cap)) != hipSuccess) {
+      vr_new = nullptr;
+      undo();
+      return hip_fail(e, "hipMalloc(rank-major V workspace)");
+    }
   }
   // phase 2: copy the new blocks.  A block's row-major sign bits go to the device as they
   // are and a kernel repacks them into the slot's tiled layout; the factor layouts (9% of
@@ -505,7 +535,6 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
         v = vscaled.data();
       }
       tile_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub));
-      rowmajor_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub + vb));
     });
     copy_mt(buf, src.sign_bits, raw);
     factors.join();
@@ -515,7 +544,7 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     }
     uint8_t* slot = static_cast<uint8_t*>(W.slots[a.i].mem);
     e = hipMemcpyAsync(s->raw_dev[k % 2], buf, raw, hipMemcpyHostToDevice, st);
-    if (e == hipSuccess) e = hipMemcpyAsync(slot + sb, fac, ub + 2 * vb, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(slot + sb, fac, ub + vb, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = static_cast<hipError_t>(launch_repack_signs(s->raw_dev[k % 2], W.m, W.d, W.mt, W.nch, slot, st));
     if (e == hipSuccess) e = hipEventRecord(s->staged[k % 2], st);
   }
@@ -549,6 +578,7 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     undo();
     return hip_fail(e, "hipDeviceSynchronize");
   }
+  if (shrink) free_retired(s);
   for (int32_t w = 0; w < nw; ++w) {
     Weight& W = s->w[w];
     const int32_t n = n_per_weight[w];
@@ -560,6 +590,14 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     W.n = n;
   }
   for (const NewSlot& a : added) s->resident += s->w[a.w].slots[a.i].bytes;
+  if (vr_new) {
+    if (s->vr_ws) {
+      s->vr_retired.push_back(s->vr_ws);
+      s->vr_retired_bytes += s->vr_cap;
+    }
+    s->vr_ws = vr_new;
+    s->vr_cap = vr_new_cap;
+  }
   return BSL_OK;
 }
 
@@ -571,6 +609,15 @@ int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out) {
 }
 
 uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
+
+uint64_t bsl_workspace_bytes(const bsl_stack* s) {
+  if (!s) return 0;
+  uint64_t t = kZeroPageBytes + s->acc64_words * sizeof(uint64_t) + kTileWorkspaceFloats * sizeof(float) +
+               kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes;
+  for (const Weight& W : s->w)
+    t += sizeof(BlockPtrs) * (uint64_t)s->n_cap + W.partial_floats * sizeof(float) + W.counter_count * sizeof(uint32_t);
+  return t;
+}
 
 int bsl_launch_counts(const bsl_stack* s, uint64_t* counts) {
   if (!s || !counts) return fail(BSL_EINVAL, "bsl_launch_counts: null pointer");
@@ -669,8 +716,24 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
     if (items > (int64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
   }
   args.total_items = (int32_t)items;
+  // V of the launch's blocks in rank-major order, formed in the workspace first
+  GroupArgs vargs = args;
+  size_t vr_used = 0;
+  int64_t pairs = 0;
+  for (int32_t k = 0; k < count; ++k) {
+    WeightDesc& D = args.w[k];
+    D.vr = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(s->vr_ws) + vr_used);
+    vr_used += (size_t)D.nblocks * D.nch * kChunkCols * kRank * 2;
+    vargs.w[k] = D;
+    vargs.w[k].item_begin = (int32_t)pairs;
+    pairs += (int64_t)D.nblocks * D.nch * 8;
+  }
+  if (vr_used > s->vr_cap || pairs > (int64_t)INT32_MAX)
+    return fail(BSL_EUNSUPPORTED, "forward: the rank-major V of this launch does not fit the stack's workspace");
+  vargs.total_items = (int32_t)pairs;
   DeviceGuard guard(s->device);
-  const int e = launch_tile(args, tt, (int)token_groups, stream);
+  int e = launch_v_rank_major(vargs, stream);
+  if (e == 0) e = launch_tile(args, tt, (int)token_groups, stream);
   if (e == 0) ++s->launches[3];
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
@@ -969,6 +1032,8 @@ void bsl_destroy(bsl_stack* s) {
   if (s->acc64) (void)hipFree(s->acc64);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);
+  if (s->vr_ws) (void)hipFree(s->vr_ws);
+  free_retired(s);
   for (int k = 0; k < 2; ++k) {
     if (s->staging[k]) (void)hipHostFree(s->staging[k]);
     if (s->staged[k]) (void)hipEventDestroy(s->staged[k]);

@@ -30,16 +30,14 @@ inline int64_t pad_cols(int64_t d) { return (d + kChunkCols - 1) / kChunkCols * 
 //   u:     [m_pad/16][64 lanes][4] fp16  lane L holds U[16 t + 4 (L/16) + v][L % 16]
 //   v:     [d_pad/512][16 planes][64 lanes][8] fp16
 //          lane L of plane b holds V[512 c + 32 b + 8 (L/16) + j][L % 16], j = 0..7
-//   vr:    [d_pad][16] fp16, V row-major (zero past d): the tile-reconstruct kernels'
-//          matrix-core operand, 8 consecutive ranks of one column per 16-byte load (the
-//          rebuild contracts over the rank, the tiled copy holds 8 columns of one rank)
-// The wave-private kernel forms its B-operand order from two 8-byte loads of v, and
-// the tile kernels gather each row's 8 ranks of U from u once per batch.
+//          (zero past d)
+// That is the only copy of each factor.  The wave-private kernel forms its B-operand
+// order from two 8-byte loads of v; the tile kernels gather each row's 8 ranks of U from
+// u once per batch and read V in rank order from a copy formed per call (WeightDesc::vr).
 struct BlockPtrs {
   const uint8_t* signs;
   const uint16_t* u;
   const uint16_t* v;
-  const uint16_t* vr;
 };
 
 // One weight of a (grouped) forward launch; passed by value in the kernel arguments.
@@ -50,6 +48,8 @@ struct WeightDesc {
   float* partial;           // multi-token path: [split][token][row] partial sums (workspace)
   uint32_t* counters;       // multi-token path: arrival counters, one per (row group, token group)
                             // (workspace, zero between calls)
+  uint16_t* vr;             // tile path: V of the loaded blocks in rank-major order, [block][d_pad][16]
+                            // fp16 (workspace, formed by launch_v_rank_major at the start of the call)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks
@@ -81,6 +81,9 @@ int launch_decode_m1(const GroupArgs& args, void* stream);
 int launch_decode_wp(const GroupArgs& args, int tokens, void* stream);  // tokens: 1 to 4
 int launch_prefill(const GroupArgs& args, int token_tile, int token_groups, void* stream);
 int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* stream);
+// V of every loaded block of args' weights -> WeightDesc::vr; item_begin / total_items
+// count (block, 64-column step) pairs.
+int launch_v_rank_major(const GroupArgs& args, void* stream);
 // Row-major sign bits (device, m rows of d/8 bytes) -> the tiled sign layout (device, the
 // first bsl_packed_sign_bytes(m, d) bytes of a block slot).
 int launch_repack_signs(const uint8_t* raw, int64_t m, int64_t d, int32_t mt, int32_t nch, uint8_t* out, void* stream);

@@ -133,7 +133,6 @@ __device__ __forceinline__ BlockPtrs uniform_block(const BlockPtrs& b) {
   r.signs = uniform_ptr(b.signs);
   r.u = uniform_ptr(b.u);
   r.v = uniform_ptr(b.v);
-  r.vr = uniform_ptr(b.vr);
   return r;
 }
 
@@ -145,7 +144,6 @@ __device__ __forceinline__ BlockPtrs load_block(const BlockPtrs* table, int i) {
   b.signs = t->signs;
   b.u = t->u;
   b.v = t->v;
-  b.vr = t->vr;
   return b;
 }
 
@@ -933,7 +931,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //
 // Layouts (lane l, h = l / 32, j = l % 32):
 //  * reconstruct: A = V rows (the step plane's column sigma(j), ranks 8 h .. 8 h + 7,
-//    one 16-byte load from the row-major copy), B = U (row row0 + j, ranks 8 h ..);
+//    one 16-byte load from the launch's rank-major V), B = U (row row0 + j, ranks 8 h ..);
 //    result value i of lane l is column 16 h + i of the plane for row row0 + j (sigma
 //    orders the A rows so).  Those columns are lane groups g = 2 h, 2 h + 1 of the stored
 //    sign tile, so a lane reads the 16 stored bytes of (row, g) for its two groups.
@@ -985,6 +983,49 @@ __device__ __forceinline__ half8 load_u_ranks(const uint16_t* u, int row, int h,
   for (int k = 0; k < 8; ++k)
     out[k] = __builtin_bit_cast(_Float16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, base + 8u * k, 0u, 0));
   return out;
+}
+
+// V in rank order.  The stored (tiled) V of a 32-column plane gives lane L columns
+// 8 (L / 16) .. + 7 of rank L % 16; the rebuild contracts over the rank and wants 8 ranks
+// of one column per lane.  v_rank_order gives lane (h, j) ranks 8 h .. 8 h + 7 of column
+// sigma(j) = 16 (j / 4 % 2) + 4 (j / 8) + j % 4 of each of two planes: a wave writes the
+// planes to 2 KiB of LDS of its own and reads them back with the transposing 16-bit LDS
+// read (ds_read_b64_tr_b16; measured on the device: in every group of 16 lanes, lane
+// 4 a + b receives element b of the 8-byte rows that lanes 4 s + a address, s = 0..3).
+// Lane L's 16 bytes are stored at slot L ^ 4 (L / 16 % 2) of the plane, which spreads
+// every read over the banks at two dwords per bank.  LDS operations of one wave are
+// performed in order, so neither the reads after the writes nor the next writes after
+// the reads need a wait.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+struct VRank {
+  half8 a, b;  // A operands of the step's two planes
+};
+struct VRankLane {
+  uint32_t wpos, r0, r1;  // this lane's store offset and its two read offsets in a plane
+};
+__device__ __forceinline__ VRankLane vrank_lane(int lane) {
+  const auto slot = [](uint32_t L) { return L ^ (((L >> 4) & 1u) << 2); };
+  const uint32_t g = (uint32_t)lane >> 4, s = ((uint32_t)lane >> 2) & 3u, a = (uint32_t)lane & 3u;
+  const uint32_t row = 16u * (2u * (a & 1u) + (g & 1u)) + 8u * (g >> 1) + s;  // stored lane of rank 8 (g / 2) + s
+  VRankLane o;
+  o.wpos = 16u * slot((uint32_t)lane);
+  o.r0 = 16u * slot(row) + 8u * (a >> 1);
+  o.r1 = 16u * slot(row + 4u) + 8u * (a >> 1);
+  return o;
+}
+__device__ __forceinline__ u32x2 lds_read_tr16(lds_u8* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<__attribute__((address_space(3))) s16x4*>(p)));
+}
+__device__ __forceinline__ VRank v_rank_order(const u32x4& pa, const u32x4& pb, lds_u8* region, const VRankLane& o) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + o.wpos) = pa;
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(region + 1024 + o.wpos) = pb;
+  const u32x2 a0 = lds_read_tr16(region + o.r0), a1 = lds_read_tr16(region + o.r1);
+  const u32x2 b0 = lds_read_tr16(region + 1024 + o.r0), b1 = lds_read_tr16(region + 1024 + o.r1);
+  VRank v;
+  v.a = as_half8((u32x4){a0[0], a0[1], a1[0], a1[1]});
+  v.b = as_half8((u32x4){b0[0], b0[1], b1[0], b1[1]});
+  return v;
 }
 
 // The rebuild's K = 16 MFMA, written out so that its result lands in VGPRs: a kernel
@@ -1074,8 +1115,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
     for (int i = 0; i < BPW; ++i) {
       const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + th * BPW + i : b0);
       sbase[i] = bp.signs;
-      vbase[i] = bp.vr;
-      // U[row][8 h .. 8 h + 7] from the row-major copy (zeros for the repeated slots)
+      vbase[i] = W.vr + (size_t)(i < nbw ? b0 + th * BPW + i : b0) * W.nch * kChunkCols * kRank;
+      // U[row][8 h .. 8 h + 7] (zeros for the repeated slots)
       uf[i] = load_u_ranks(bp.u, row, h, i < nbw);
     }
     // sign words sw[i][g2][q] of the current chunk (quads 0-1 and 2-3 refilled separately)
@@ -1302,6 +1343,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
   if (threadIdx.x == 0) __hip_atomic_store(&W.counters[rest], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------ tile path, V in rank order
+// First kernel of a tile-path launch: the V of every loaded block of the launch's weights
+// in rank-major order, [block][d_pad][16] fp16 at WeightDesc::vr (a workspace of the
+// stack), which the rebuild reads 8 ranks of one column at a time.  A block keeps V only
+// in the tiled order of the single- and few-token kernels; forming this order per call
+// costs one read and one write of the launch's V (32 bytes per block and column).  The
+// work is the list of (weight, block, 64-column step) pairs, item_begin giving each
+// weight's first pair; one pair per wave and iteration.
+__global__ __launch_bounds__(256) void v_rank_major_kernel(GroupArgs args) {
+  __shared__ u32x4 region[4][128];  // 2 KiB per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int jl = lane & 31, h = lane >> 5;
+  const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
+  const VRankLane vro = vrank_lane(lane);
+  const uint32_t total = (uint32_t)args.total_items;
+  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u) {
+    int j = 0;
+    while (j + 1 < args.count && p >= (uint32_t)args.w[j + 1].item_begin) ++j;
+    const WeightDesc& W = args.w[j];
+    const uint32_t per_block = (uint32_t)W.nch * 8u;  // steps of a block
+    const uint32_t local = p - (uint32_t)W.item_begin;
+    const uint32_t i = local / per_block, step = local - i * per_block;
+    const rsrc_t r = make_rsrc(load_block(W.blocks, (int)i).v);
+    const uint32_t off = step * 2048u + 16u * (uint32_t)lane;  // the step's two planes
+    const u32x4 pa = buf_load16(r, off), pb = buf_load16(r, off + 1024u);
+    const VRank t = v_rank_order(pa, pb, (lds_u8*)&region[wave][0], vro);
+    uint16_t* out = W.vr + ((size_t)i * W.nch * kChunkCols + (size_t)step * 64 + sigma) * kRank + 8 * h;
+    *reinterpret_cast<u32x4*>(out) = __builtin_bit_cast(u32x4, t.a);
+    *reinterpret_cast<u32x4*>(out + 32 * kRank) = __builtin_bit_cast(u32x4, t.b);
+  }
+}
+
 // ------------------------------------------------------------ tile path, split roles
 // The item, arithmetic and results of tile_kernel<TT, 2>, with the rebuild and the GEMM
 // in different waves: 8 waves, two per SIMD (256 registers each).  Waves 0-3 (GEMM waves)
@@ -1424,7 +1498,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int i = 0; i < BPW; ++i) {
         const BlockPtrs bp = load_block(W.blocks, i < nbw ? b0 + half * BPW + i : b0);
         sbase[i] = bp.signs;
-        vbase[i] = bp.vr;
+        vbase[i] = W.vr + (size_t)(i < nbw ? b0 + half * BPW + i : b0) * W.nch * kChunkCols * kRank;
         uf[i] = load_u_ranks(bp.u, row, h, i < nbw);
       }
       uint32_t sw[BPW][2][4];
@@ -2158,6 +2232,14 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
     case 8: hipLaunchKernelGGL(tile_split_kernel<8>, grid, dim3(512), 0, st, args, token_groups); break;
     default: return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int launch_v_rank_major(const GroupArgs& args, void* stream) {
+  if (args.total_items == 0) return 0;
+  const unsigned waves = (unsigned)args.total_items;
+  const dim3 grid(std::min((waves + 3u) / 4u, 2048u));
+  hipLaunchKernelGGL(v_rank_major_kernel, grid, dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }
 

@@ -146,9 +146,18 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream);
 int bsl_active_blocks(const bsl_stack* s, int32_t w, int32_t* n_out);
 
 /* Device bytes currently held by loaded blocks (what budget_bytes caps).  A loaded block
- * occupies its padded tiled signs and factors plus one more copy of V, row-major, for
- * the tile-reconstruct kernels' rebuild (32 bytes per padded column). */
+ * occupies its tiled signs, U and V, with rows padded to 1024 and columns to 512, and
+ * nothing else: for aligned shapes that is bsl_block_bytes(m, d, 16) exactly.  (The
+ * kernels form every other operand order they need on the fly.) */
 uint64_t bsl_resident_bytes(const bsl_stack* s);
+
+/* Device bytes the stack holds besides its loaded blocks (not capped by budget_bytes):
+ * the forward paths' workspaces (row accumulators, split partial sums and their counters,
+ * block tables, the tile path's V in rank-major order) and bsl_load_blocks' device
+ * buffers.  The rank-major V workspace holds the V of the kMaxGroup = 8 weights with the
+ * most V bytes, whatever the number of weights: the tile path forms it for the launch's
+ * blocks at the start of each call (one read and one write of their V). */
+uint64_t bsl_workspace_bytes(const bsl_stack* s);
 
 /* y = x W_hat_n^T for weight w with its n loaded blocks: the linear layer with the
  * weight the authors restore block by block (OpenReview discussion, weight-restoration

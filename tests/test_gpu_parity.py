@@ -102,8 +102,10 @@ def test_grow_shrink_and_zero_blocks(cfg1_blocks):
             else:
                 assert rel_err(y, oracle.forward(x, cfg1_blocks, n)) <= REL_TOL
         resident = bsl.bsl_resident_bytes(st.h)
+        # aligned shapes: the four slots hold the blocks' payload and nothing else
+        assert resident == 4 * bsl.bsl_block_bytes(1024, 1024, 16)
         st.load([0])
-        assert bsl.bsl_resident_bytes(st.h) == 0 and resident > 0
+        assert bsl.bsl_resident_bytes(st.h) == 0
 
 
 def test_non_default_stream(cfg1_blocks):
@@ -146,6 +148,34 @@ def test_load_overlaps_forwards_on_another_stream(cfg1_blocks):
             assert rel_err(y.cpu().numpy().astype(np.float64), ref2) <= REL_TOL
         assert rel_err(y0.cpu().numpy().astype(np.float64), oracle.forward(x, cfg1_blocks, 4)) <= REL_TOL
         assert rel_err(y1.cpu().numpy().astype(np.float64), oracle.forward(x, other, 3)) <= REL_TOL
+
+
+def test_tile_rank_major_v_workspace():
+    # A block keeps V only in the tiled order; the tile path forms the launch's V in rank-
+    # major order in a workspace sized at load for the 8 weights with the most V bytes.
+    # Ten weights: a group of exactly those 8 fits and matches the oracle, and the
+    # workspace does not grow with the other two.
+    ds = [512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 512, 1024]
+    ns = [2, 3, 1, 2, 2, 1, 2, 1, 3, 1]
+    weights = [(256, d, synth.synthetic_blocks(40 + j, 256, d, n, 16, 0, j)) for j, (d, n) in enumerate(zip(ds, ns))]
+    vbytes = [n * d * 32 for d, n in zip(ds, ns)]  # (d is a multiple of 512: no column padding)
+    top = sorted(range(len(ds)), key=lambda j: -vbytes[j])[:8]
+    with Stack(weights) as st:
+        before = bsl.bsl_workspace_bytes(st.h)
+        st.load(ns)
+        grown = bsl.bsl_workspace_bytes(st.h) - before
+        raw = max(256 * d // 8 for d in ds)  # plus the load's two device buffers of raw sign bits
+        assert sum(vbytes[j] for j in top) <= grown <= sum(vbytes[j] for j in top) + 2 * raw
+        assert bsl.bsl_resident_bytes(st.h) == sum(n * bsl.bsl_block_bytes(256, d, 16) + n * (1024 - 256) * (d // 8 + 32)
+                                                   for d, n in zip(ds, ns))
+        tiles = bsl.bsl_launch_counts(st.h)[3]
+        xs = [synth.activations(41, 24, ds[j], j) for j in top]
+        ys = st.forward_group(top, xs)  # 24 tokens: the tile path
+        assert bsl.bsl_launch_counts(st.h)[3] == tiles + 1
+        for k, j in enumerate(top):
+            blocks = weights[j][2]
+            ref = oracle.forward(xs[k], blocks, ns[j])
+            assert_elementwise(ys[k], ref, elem_factor("tile", ns[j], ds[j]) * abs_bound(xs[k], blocks, ns[j]), f"weight {j} d={ds[j]}")
 
 
 # ---------------------------------------------------------------- 8B decoder layer

@@ -272,7 +272,7 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
              f"command: {cmd[0].strip()}", f"kernel_source_sha256: {digest}", "",
              f"{'kernel':58s} {'grid':>8s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
     for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-        if not name.startswith("void bsl::"):
+        if not name.startswith(("void bsl::", "bsl::")):
             continue
         lines.append(f"{name[:58]:58s} {grid:8d} {len(v):6d} {statistics.mean(v):10.2f} {min(v):10.2f} {max(v):10.2f}")
     with open(os.path.join(ROOT, "profiles", "kernel_stats_llama3_8b_layer.txt"), "w") as f:

@@ -841,6 +841,7 @@ def main() -> None:
             "roofline": {"bound": "hbm", "achieved": round(per_token / tok_us / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(per_token / tok_us / 1e9 / HBM_PEAK_GBS, 4)},
             "resident_bytes": int(bsl.bsl_resident_bytes(lay.h)),
+            "stack_workspace_bytes": int(bsl.bsl_workspace_bytes(lay.h)),
             "wall_ms_per_token": round(w_ * 1e3 / tokens, 3),
         }
         log(f"llama70b: {result['llama2_70b_decode']}")

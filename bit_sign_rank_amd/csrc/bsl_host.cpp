@@ -169,9 +169,7 @@ struct Weight {
   std::vector<Slot> slots;          // [n_cap]
   std::vector<float> inv_scale;     // [d] input-channel scale folded into V at load (empty: none)
   BlockPtrs* dtable = nullptr;      // device [n_cap]
-  float* partial = nullptr;         // workspace
-  uint32_t* counters = nullptr;     // workspace: arrival counters of the multi-token path
-  size_t partial_floats = 0, counter_count = 0;
+  size_t partial_floats = 0, counter_count = 0;  // its share of the multi-token path's workspace
 };
 
 struct bsl_stack {
@@ -185,6 +183,9 @@ struct bsl_stack {
   uint64_t* acc64 = nullptr;      // single- and few-token row accumulators, one per (row, token) of a launch (zero)
   size_t acc64_words = 0;
   float* tile_ws = nullptr;       // tile path: partial sums of column ranges (kTileWorkspaceFloats)
+  float* mt_partial = nullptr;    // multi-token path: split partial sums of a launch's weights
+  uint32_t* mt_counters = nullptr;  // ... and their arrival counters (zero between launches)
+  size_t mt_partial_floats = 0, mt_counter_words = 0;  // the kMaxGroup largest weights' shares
   uint8_t* staging[2] = {nullptr, nullptr};  // pinned host buffers of bsl_load_blocks (allocated on first use)
   size_t staging_bytes = 0;
   hipEvent_t staged[2] = {nullptr, nullptr};  // copy out of staging[k] and the repack from raw_dev[k] finished
@@ -350,13 +351,29 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     W.partial_floats = (size_t)kSplitTokens * mpad;
     // split items have at most kSplitTokens / 2 padded tokens, so at most 32 token groups
     W.counter_count = (size_t)prefill_groups(W) * (kSplitTokens / 4);
-    const size_t words = W.counter_count;
     max_groups = std::max<size_t>(max_groups, (size_t)decode_groups(W));
     if ((e = hipMalloc(&W.dtable, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(table)");
-    else if ((e = hipMalloc(&W.partial, W.partial_floats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(workspace)");
-    else if ((e = hipMalloc(&W.counters, words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(counters)");
-    else if ((e = hipMemset(W.counters, 0, words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
     else if ((e = hipMemset(W.dtable, 0, sizeof(BlockPtrs) * n_cap)) != hipSuccess) rc = hip_fail(e, "hipMemset(table)");
+  }
+  // The multi-token path's split partial sums and counters: launches on one stack do not
+  // overlap, so one workspace serves every launch, with room for the kMaxGroup weights
+  // that need the most.
+  if (rc == BSL_OK) {
+    std::vector<size_t> pf, cw;
+    for (const Weight& W : s->w) {
+      pf.push_back(W.partial_floats);
+      cw.push_back(W.counter_count);
+    }
+    const size_t k = std::min<size_t>(kMaxGroup, pf.size());
+    std::partial_sort(pf.begin(), pf.begin() + k, pf.end(), std::greater<size_t>());
+    std::partial_sort(cw.begin(), cw.begin() + k, cw.end(), std::greater<size_t>());
+    for (size_t i = 0; i < k; ++i) {
+      s->mt_partial_floats += pf[i];
+      s->mt_counter_words += cw[i];
+    }
+    if ((e = hipMalloc(&s->mt_partial, s->mt_partial_floats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(workspace)");
+    else if ((e = hipMalloc(&s->mt_counters, s->mt_counter_words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(counters)");
+    else if ((e = hipMemset(s->mt_counters, 0, s->mt_counter_words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
   }
   if (rc == BSL_OK) {
     // row accumulators of the single- and few-token kernels: one per row and token of a
@@ -614,8 +631,8 @@ uint64_t bsl_workspace_bytes(const bsl_stack* s) {
   if (!s) return 0;
   uint64_t t = kZeroPageBytes + s->acc64_words * sizeof(uint64_t) + kTileWorkspaceFloats * sizeof(float) +
                kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes;
-  for (const Weight& W : s->w)
-    t += sizeof(BlockPtrs) * (uint64_t)s->n_cap + W.partial_floats * sizeof(float) + W.counter_count * sizeof(uint32_t);
+  t += s->mt_partial_floats * sizeof(float) + s->mt_counter_words * sizeof(uint32_t);
+  t += sizeof(BlockPtrs) * (uint64_t)s->n_cap * s->w.size();
   return t;
 }
 
@@ -755,6 +772,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.y_fp32 = y_is_fp32 ? 1 : 0;
   const bool tile = !use_static && (s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens));
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
+  size_t mt_floats = 0, mt_words = 0;  // this launch's shares of the multi-token workspace
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -767,8 +785,10 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     D.blocks = W.dtable;
     D.x = static_cast<const uint16_t*>(x[j]);
     D.y = y[j];
-    D.partial = W.partial;
-    D.counters = W.counters;
+    D.partial = s->mt_partial + mt_floats;  // (distinct weights: within the kMaxGroup largest shares)
+    D.counters = s->mt_counters + mt_words;
+    mt_floats += W.partial_floats;
+    mt_words += W.counter_count;
     D.m = W.m;
     D.d = W.d;
     D.mt = W.mt;
@@ -1025,13 +1045,13 @@ void bsl_destroy(bsl_stack* s) {
     for (Slot& sl : W.slots)
       if (sl.mem) (void)hipFree(sl.mem);
     if (W.dtable) (void)hipFree(W.dtable);
-    if (W.partial) (void)hipFree(W.partial);
-    if (W.counters) (void)hipFree(W.counters);
   }
   if (s->zero_page) (void)hipFree(s->zero_page);
   if (s->acc64) (void)hipFree(s->acc64);
   if (s->tile_ws) (void)hipFree(s->tile_ws);
   if (s->tile_ctr) (void)hipFree(s->tile_ctr);
+  if (s->mt_partial) (void)hipFree(s->mt_partial);
+  if (s->mt_counters) (void)hipFree(s->mt_counters);
   if (s->vr_ws) (void)hipFree(s->vr_ws);
   free_retired(s);
   for (int k = 0; k < 2; ++k) {

@@ -178,6 +178,28 @@ def test_tile_rank_major_v_workspace():
             assert_elementwise(ys[k], ref, elem_factor("tile", ns[j], ds[j]) * abs_bound(xs[k], blocks, ns[j]), f"weight {j} d={ds[j]}")
 
 
+def test_multi_token_workspace_shared_by_groups():
+    # The factored multi-token path cuts its items along the (block, chunk) sequence when
+    # there are few of them and sums the pieces from a partial-sum workspace that the
+    # stack shares among its weights (room for the 8 weights needing the most).  Ten
+    # weights: groups of 8 in two different orders, twice each, all match the oracle (the
+    # arrival counters are back at zero after every launch).
+    ms = [512, 1024, 1536, 2048, 2560, 3072, 3584, 4096, 1024, 2048]
+    weights = [(m, 1536, synth.synthetic_blocks(50 + j, m, 1536, 2, 16, 0, j)) for j, m in enumerate(ms)]
+    groups = [[7, 6, 5, 4, 3, 2, 9, 1], [0, 8, 1, 9, 2, 3, 4, 5]]
+    with Stack(weights, path=bsl.BSL_PATH_FACTORED) as st:
+        st.load([2] * len(ms))
+        for rep in range(2):
+            for g, ws in enumerate(groups):
+                xs = [synth.activations(51 + g, 6, 1536, j) for j in ws]
+                ys = st.forward_group(ws, xs)
+                for k, j in enumerate(ws):
+                    blocks = weights[j][2]
+                    ref = oracle.forward(xs[k], blocks, 2)
+                    assert_elementwise(ys[k], ref, elem_factor("z16", 2, 1536) * abs_bound(xs[k], blocks, 2),
+                                       f"group {g} weight {j} pass {rep}")
+
+
 # ---------------------------------------------------------------- 8B decoder layer
 def layer_blocks(shapes, counts, seed, layer=0):
     return [(m, d, synth.synthetic_blocks(seed, m, d, int(n), 16, layer, j)) for j, ((_, m, d), n) in enumerate(zip(shapes, counts))]

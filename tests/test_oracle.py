@@ -21,7 +21,9 @@ import pytest
 
 import oracle
 from oracle import avd as oavd
+from oracle import lowrank as olowrank
 from oracle import restore as orest
+from oracle import scaling as oscaling
 from oracle import signs as osigns
 import synth
 
@@ -399,6 +401,19 @@ def _mutant_svd_of_R(R, k, round_fp16=True):
     return {"signs": S, "bits": None, "u": U, "v": V}, R - S * L, sigma
 
 
+def _mutant(module, old: str, new: str):
+    """A copy of an oracle module with one planted mistake: its source with `old`
+    (which must occur exactly once) replaced by `new`, run as a fresh module."""
+    import inspect
+    import types
+    src = inspect.getsource(module)
+    assert src.count(old) == 1, old
+    m = types.ModuleType(module.__name__ + "_mutant")
+    m.__package__ = module.__package__
+    exec(compile(src.replace(old, new), module.__file__ + " (mutant)", "exec"), m.__dict__)
+    return m
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     # 1) SVD of R instead of |R| breaks Perron-Frobenius orientation / energy pin.
     monkeypatch.setattr(oavd, "avd_step", _mutant_svd_of_R)
@@ -423,19 +438,20 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # 4) a transposed product (x W instead of x W^T) fails brute force on a square shape
     blocks = synth.synthetic_blocks(17, 8, 8, 2, 2)
     xx = synth.activations(2, 1, 8)
-    wrong = xx.astype(np.float64) @ orest.reconstruct(blocks, 2)
     exact = np.array([[float(v) for v in row] for row in _brute_force(xx, blocks, 2)])
-    assert np.abs(wrong - exact).max() > 1e-3 * np.abs(exact).max()
+    mut = _mutant(orest, "return x64 @ reconstruct(blocks, n).T", "return x64 @ reconstruct(blocks, n)")
+    assert np.abs(mut.forward(xx, blocks, 2) - exact).max() > 1e-3 * np.abs(exact).max()
     assert np.abs(oracle.forward(xx, blocks, 2) - exact).max() <= 1e-13 * np.abs(exact).max()
     # 5) the input-channel factor applied to the output channels fails brute force
     t = synth.inv_input_scale(6, 8)
-    wrong = orest.forward(xx, blocks, 2) * t[None, :].astype(np.float64)
     exact = np.array([[float(v) for v in row] for row in _brute_force(xx, blocks, 2, inv_scale=t)])
-    assert np.abs(wrong - exact).max() > 1e-3 * np.abs(exact).max()
+    mut = _mutant(oscaling, "return forward(x64 * s[None, :], blocks, n)", "return forward(x64, blocks, n) * s[None, :]")
+    assert np.abs(mut.forward_scaled(xx, blocks, t, 2) - exact).max() > 1e-3 * np.abs(exact).max()
     assert np.abs(oracle.forward_scaled(xx, blocks, t, 2) - exact).max() <= 1e-13 * np.abs(exact).max()
     # 6) a low-rank forward with the factors swapped (x U V^T) fails brute force
     lb = _lowrank_blocks(9, 6, 6, 2, 2)
     xs = synth.activations(9, 1, 6)
     exact = np.array([[float(v) for v in row] for row in _brute_force_lowrank(xs, lb, 2)])
-    swapped = sum((xs.astype(np.float64) @ b["u"].astype(np.float64)) @ b["v"].astype(np.float64).T for b in lb)
-    assert np.abs(swapped - exact).max() > 1e-3 * np.abs(exact).max()
+    mut = _mutant(olowrank, "y += (x64 @ V) @ U.T", "y += (x64 @ U) @ V.T")
+    assert np.abs(mut.forward_lowrank(xs, lb, 2) - exact).max() > 1e-3 * np.abs(exact).max()
+    assert np.abs(olowrank.forward_lowrank(xs, lb, 2) - exact).max() <= 1e-13 * np.abs(exact).max()

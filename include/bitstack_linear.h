@@ -168,16 +168,21 @@ uint64_t bsl_workspace_bytes(const bsl_stack* s);
  *   M >= 1 tokens.  With n = 0 loaded blocks y is all zeros.
  * Only enqueues kernels on `stream` (no synchronisation, no allocation).  Forwards on
  * one stack must not run concurrently, even for different weights: they share the
- * stack's workspaces (row accumulators, split partial sums and their counters).  Forwards queued on one stream
- * are ordered, so that is the simple way to issue them. */
+ * stack's workspaces (row accumulators, split partial sums and their counters, the tile
+ * path's rank-major V).  Forwards queued on one stream are ordered, so that is the simple
+ * way to issue them. */
 int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int32_t y_is_fp32, void* stream);
 
 /* Several weights in one call (count <= 8, distinct weights): weights[j] reads x[j] and
  * writes y[j] exactly as bsl_forward would.  All share M and y_is_fp32.  The group runs
- * as one kernel launch, except on BSL_PATH_AUTO at M = 2..4 when the group's activations
- * do not fit the few-token kernel as a whole: then it is split into two launches (see
- * bsl_set_path).  An error returned after the first of the two was enqueued leaves the y[j]
- * of the weights in that launch written and the others unspecified. */
+ * as one kernel launch, except
+ *   - on the tile path (BSL_PATH_TILE, and BSL_PATH_AUTO from M = 5 on), which first
+ *     runs a short pass that puts the V of the group's loaded blocks in rank-major order
+ *     in the stack's workspace, then the tile kernel;
+ *   - on BSL_PATH_AUTO at M = 2..4 when the group's activations do not fit the few-token
+ *     kernel as a whole: then it is split into two forward launches (see bsl_set_path).
+ *     An error returned after the first of the two was enqueued leaves the y[j] of the
+ *     weights in that launch written and the others unspecified. */
 int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
                       int32_t M, int32_t y_is_fp32, void* stream);
 

@@ -507,28 +507,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     while (range_start(o, U, lg) > u) --o;
     return o;
   };
+  // The reduction leaves a row's sum in all four lanes of a quad, so lane L adds the row
+  // of tile L % 4: one add per lane.  The returned word is examined only after the next
+  // step's barrier (resolve), so the wave does not wait for the add's round trip, nor,
+  // since loads complete in order, for the sign request issued just before it.
+  const int rt = lane & 3;                                   // this lane's tile of the four
+  const int rrow = (wave * R + rt) * kTileRows + rsel;       // its row in a row group
+  struct PendingAdd {
+    bool on;            // (uniform) an add waits to be examined
+    uint64_t prev;      // the word before the add
+    float v;            // the share added
+    uint32_t item;      // its row group in the launch
+    int32_t row;        // the lane's output row (or -1: no add)
+    uint32_t parts;     // contributions the row group receives
+    void* y;
+  } pa = {false, 0ull, 0.f, 0u, -1, 0u, nullptr};
   auto add_shares = [&](const DecodeCursor& c) {
     const uint32_t item = c.rg_begin + c.rg;
     // workgroups that share this row group: the owners of its first and last unit and all between
     const uint32_t first = args.w[c.j].unit_begin + (uint32_t)c.rg * (uint32_t)(c.nch * c.nb);
     const uint32_t parts = owner(first + (uint32_t)(c.nch * c.nb) - 1) - owner(first) + 1;
-    uint64_t* words = args.acc + (size_t)item * kDecodeGroupRows;
-    void* y = args.w[c.j].y;
-    const int m = args.w[c.j].m;
+    float v = 0.f;
 #pragma unroll
     for (int t = 0; t < R; ++t) {
-      const float v = reduce_columns(accl[wave][t][lane], lane);
+      const float s = reduce_columns(accl[wave][t][lane], lane);
       accl[wave][t][lane] = (float4v){0.f, 0.f, 0.f, 0.f};
-      const int rr = (wave * R + t) * kTileRows + rsel;
-      const int row = c.rg * kDecodeGroupRows + rr;
-      if ((lane & 3) == 0 && row < m) {
-        const uint64_t share = acc_share(v);
-        const uint64_t now = __hip_atomic_fetch_add(&words[rr], share, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + share;
-        if (acc_count(now) == parts) {
-          store_y(y, row, acc_value(now), args.y_fp32);
-          __hip_atomic_store(&words[rr], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
+      v = t == rt ? s : v;
+    }
+    const int row = c.rg * kDecodeGroupRows + rrow;
+    pa.on = true;
+    pa.v = v;
+    pa.item = item;
+    pa.row = row < args.w[c.j].m ? row : -1;
+    pa.parts = parts;
+    pa.y = args.w[c.j].y;
+    pa.prev = 0;
+    if (pa.row >= 0)
+      pa.prev = __hip_atomic_fetch_add(&args.acc[(size_t)item * kDecodeGroupRows + rrow], acc_share(v), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // the contributor whose add completed the row's count holds the whole sum: it writes y
+  // and clears the word
+  auto resolve = [&]() {
+    if (!pa.on) return;
+    pa.on = false;
+    if (pa.row < 0) return;
+    const uint64_t now = pa.prev + acc_share(pa.v);
+    if (acc_count(now) == pa.parts) {
+      store_y(pa.y, pa.row, acc_value(now), args.y_fp32);
+      __hip_atomic_store(&args.acc[(size_t)pa.item * kDecodeGroupRows + rrow], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -571,6 +598,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // tiles are done with it, so a sign tile is requested well over one unit ahead.
   auto step = [&](u32x4 (&cur)[R], const int buf) __attribute__((always_inline)) {
     lds_barrier();  // the B operands of c0 are complete; zs[buf ^ 1] (unit c - 1) is free
+    resolve();      // (the add of the last step's row-group end)
     // Unit c1's B operands, the next V / x loads and the cursor advance: the upper half
     // of the waves does them before its tiles and the lower half after, so on every SIMD
     // some waves keep the matrix cores busy while the others do this work.
@@ -619,11 +647,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     __builtin_amdgcn_sched_barrier(0);
     if (!early) prework(vx_late);
     __builtin_amdgcn_sched_barrier(0);
-    load_signs(p2, cur);
-    __builtin_amdgcn_sched_barrier(0);
+    // (a row-group end's adds go out before the next sign request: the check of their
+    // results after the next barrier then waits only for loads issued before them)
     if (block_end(c0)) weight_block();
     __builtin_amdgcn_sched_barrier(0);
     if (group_end(c0)) add_shares(c0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_signs(p2, cur);
     load_u(p1);
     c0 = c1;
     c1 = c2;
@@ -637,6 +667,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     step(sgn[0], 0);
     if (s + 1 < n) step(sgn[1], 1);
   }
+  resolve();
 }
 
 // ============================================================ multi-token kernel

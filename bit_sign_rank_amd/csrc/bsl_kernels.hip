@@ -436,6 +436,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // 16 + 4 kk .. 16 + 4 kk + 3 (group G <-> columns 2 G, 2 G + 1); in the stored V tile
   // those are the halves kk % 2 of lanes 16 (kk / 2) + r and 16 (2 + kk / 2) + r.
   const int kk = lane >> 4;
+  // (the 16 lanes of a lane group need the same four activations: one of them loads them
+  // and build_z broadcasts them, which spares the data-return path 15 of 16 copies)
   auto load_vx = [&](const UnitPtrs& p, VX& d) {
 #pragma unroll
     for (int pp = 0; pp < PP; ++pp)
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int hpart = 0; hpart < 2; ++hpart) {
         d.v[pp][hpart] = load8(p.v + (pp * 64 + 16 * (2 * hpart + (kk >> 1)) + r16) * 8 + 4 * (kk & 1));
         const int col = 32 * (PP * wave + pp) + 16 * hpart + 4 * kk;
-        d.x[pp][hpart] = load8(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
+        if (r16 == 0) d.x[pp][hpart] = load8(col < p.xcols ? static_cast<const void*>(p.x + col) : static_cast<const void*>(zero_page));
       }
   };
   // B operand of this wave's plane: Z = V x (fp16 products, as the layer defines Z)
@@ -456,7 +458,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
     for (int hpart = 0; hpart < 2; ++hpart)
 #pragma unroll
-      for (int k = 0; k < 2; ++k) z[2 * hpart + k] = as_u32(as_half2(d.v[pp][hpart][k]) * as_half2(d.x[pp][hpart][k]));
+      for (int k = 0; k < 2; ++k) {
+        // lane 16 g's activations to every lane of group g (ds_swizzle, and-mask 0x10)
+        const uint32_t xb = (uint32_t)__builtin_amdgcn_ds_swizzle((int)d.x[pp][hpart][k], 0x10);
+        z[2 * hpart + k] = as_u32(as_half2(d.v[pp][hpart][k]) * as_half2(xb));
+      }
     u32x8 t;
     if (plane_even(b)) {  // (wave-uniform branch)
 #pragma unroll
@@ -654,7 +660,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     if (group_end(c0)) add_shares(c0);
     __builtin_amdgcn_sched_barrier(0);
     load_signs(p2, cur);
-    load_u(p1);
+    if (block_end(c1)) load_u(p1);  // (U is needed only where a block ends)
     c0 = c1;
     c1 = c2;
     c2 = c3;

@@ -272,15 +272,17 @@ __device__ __forceinline__ WeightDesc find_weight(const GroupArgs& args, int ite
 // block split over two workgroups is fine); after a row group's last unit (or the end
 // of the range) each wave sums its tiles over r and adds the workgroup's share of each
 // row to the row's fixed-point accumulator (acc_share); the workgroup whose add completes
-// a row's count writes that row of y.  So the end of a range costs one atomic round trip,
-// and the result does not depend on which workgroup arrives last.
+// a row's count writes that row of y.  The returned words are examined a step later, so
+// no wave waits for the adds, and the result does not depend on which workgroup arrives
+// last.
 //
-// Sign tiles are fetched one unit ahead, V fragments and activations two units ahead and
-// U fragments one unit ahead, across block, row-group and weight boundaries, so the HBM
-// stream never waits on compute; fetches past the end of the range read a page of zeros.
-// Sign tiles are read once, so they are loaded non-temporally and leave the L2 to the V
-// and U fragments that other workgroups re-read.  Nothing waits on outstanding loads
-// before the end of the range.
+// Sign tiles are fetched two units ahead, V fragments and activations one unit ahead
+// (the activations by one lane of each 16-lane group, broadcast with ds_swizzle), and U
+// fragments one unit ahead where a block ends, across block, row-group and weight
+// boundaries, so the HBM stream never waits on compute; fetches past the end of the
+// range read a page of zeros.  Sign tiles are read once, so they are loaded
+// non-temporally and leave the L2 to the V and U fragments that other workgroups re-read.
+// Nothing waits on outstanding loads before the end of the range.
 struct DecodeCursor {
   int32_t j, rg, i, ch;  // weight slot in the launch, row group, block, chunk
   uint32_t u;            // unit index
@@ -599,8 +601,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- one unit.  On entry unit c0's signs are in `cur` and unit c1's in the other
-  // buffer, c0's Z tile in zs[buf], its U fragments in uf, and unit c1's V fragments
-  // and activations in vv / xv.  Unit c2's signs are fetched into `cur` as soon as the
+  // buffer, c0's Z tile in zs[buf], its U fragments in uf (if c0 ends a block), and unit
+  // c1's V fragments and activations in vx_early / vx_late.  Unit c2's signs are fetched into `cur` as soon as the
   // tiles are done with it, so a sign tile is requested well over one unit ahead.
   auto step = [&](u32x4 (&cur)[R], const int buf) __attribute__((always_inline)) {
     lds_barrier();  // the B operands of c0 are complete; zs[buf ^ 1] (unit c - 1) is free

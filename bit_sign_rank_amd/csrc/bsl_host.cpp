@@ -108,7 +108,8 @@ void pack_signs_mt(const uint8_t* src, int64_t m, int64_t d, uint8_t* out) {
 
 // memcpy in up to 8 threads (large copies into pinned staging are host-bandwidth bound)
 void copy_mt(uint8_t* dst, const uint8_t* src, size_t bytes) {
-  const size_t nt = bytes < ((size_t)8 << 20) ? 1 : 8;
+  // one thread per MiB, up to 8 (a pageable-to-pinned copy runs at a few GB/s per thread)
+  const size_t nt = std::min<size_t>(8, std::max<size_t>(1, bytes >> 20));
   if (nt == 1) {
     std::memcpy(dst, src, bytes);
     return;

@@ -8,9 +8,11 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <condition_variable>
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <new>
 #include <string>
 #include <thread>
@@ -106,27 +108,10 @@ void pack_signs_mt(const uint8_t* src, int64_t m, int64_t d, uint8_t* out) {
   for (auto& t : th) t.join();
 }
 
-// memcpy in up to 8 threads (large copies into pinned staging are host-bandwidth bound)
-void copy_mt(uint8_t* dst, const uint8_t* src, size_t bytes) {
-  // one thread per MiB, up to 8 (a pageable-to-pinned copy runs at a few GB/s per thread)
-  const size_t nt = std::min<size_t>(8, std::max<size_t>(1, bytes >> 20));
-  if (nt == 1) {
-    std::memcpy(dst, src, bytes);
-    return;
-  }
-  std::vector<std::thread> th;
-  const size_t per = (bytes + nt - 1) / nt;
-  for (size_t k = 0; k < nt; ++k) {
-    const size_t a = k * per, b = std::min(bytes, a + per);
-    if (a < b) th.emplace_back([=] { std::memcpy(dst + a, src + a, b - a); });
-  }
-  for (auto& t : th) t.join();
-}
-
-// U (m x 16, row-major fp16) -> [m_pad/16][64][4]: lane L, slot v holds U[16 t + 4 (L/16) + v][L % 16].
-void tile_u(const uint16_t* u, int64_t m, uint16_t* out) {
-  const int64_t mt = pad_rows(m) / kTileRows;
-  for (int64_t t = 0; t < mt; ++t)
+// U (m x 16, row-major fp16) -> [m_pad/16][64][4]: lane L, slot v holds U[16 t + 4 (L/16) + v][L % 16]
+// (row tiles [t0, t1) of it).
+void tile_u(const uint16_t* u, int64_t m, uint16_t* out, int64_t t0, int64_t t1) {
+  for (int64_t t = t0; t < t1; ++t)
     for (int L = 0; L < 64; ++L)
       for (int v = 0; v < 4; ++v) {
         const int64_t row = 16 * t + 4 * (L / 16) + v;
@@ -135,10 +120,9 @@ void tile_u(const uint16_t* u, int64_t m, uint16_t* out) {
 }
 
 // V (d x 16, row-major fp16) -> [d_pad/512][16][64][8]: lane L of plane b, slot j holds
-// V[512 c + 32 b + 8 (L/16) + j][L % 16].
-void tile_v(const uint16_t* v, int64_t d, uint16_t* out) {
-  const int64_t nch = pad_cols(d) / kChunkCols;
-  for (int64_t c = 0; c < nch; ++c)
+// V[512 c + 32 b + 8 (L/16) + j][L % 16] (chunks [c0, c1) of it).
+void tile_v(const uint16_t* v, int64_t d, uint16_t* out, int64_t c0, int64_t c1) {
+  for (int64_t c = c0; c < c1; ++c)
     for (int b = 0; b < kPlanes; ++b)
       for (int L = 0; L < 64; ++L)
         for (int j = 0; j < 8; ++j) {
@@ -147,13 +131,81 @@ void tile_v(const uint16_t* v, int64_t d, uint16_t* out) {
         }
 }
 
-// V (d x 16) with row c multiplied by inv_scale[c]: one rounding of the exact product.
-bool scale_v(const uint16_t* v, int64_t d, const float* inv_scale, uint16_t* out) {
-  for (int64_t c = 0; c < d; ++c)
+// V rows [c0, c1) (of d x 16) multiplied by inv_scale[c]: one rounding of the exact product.
+bool scale_v(const uint16_t* v, int64_t c0, int64_t c1, const float* inv_scale, uint16_t* out) {
+  for (int64_t c = c0; c < c1; ++c)
     for (int r = 0; r < kRank; ++r)
       if (!double_to_fp16(fp16_to_double(v[c * kRank + r]) * (double)inv_scale[c], &out[c * kRank + r])) return false;
   return true;
 }
+
+// Host threads for bsl_load_blocks' staging work (copies into pinned memory and the factor
+// layouts): started on first use, joined when the stack is destroyed.  run(n, fn) calls
+// fn(0) .. fn(n - 1) on the workers and the calling thread and returns when all are done.
+class WorkerPool {
+ public:
+  ~WorkerPool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      quit_ = true;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  void run(int n, const std::function<void(int)>& fn) {
+    if (th_.empty())
+      for (int k = 0; k < kWorkers; ++k) th_.emplace_back([this] { loop(); });
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      fn_ = &fn;
+      next_ = 0;
+      total_ = pending_ = n;
+      ++gen_;
+    }
+    cv_.notify_all();
+    work();
+    std::unique_lock<std::mutex> lk(mu_);
+    done_.wait(lk, [&] { return pending_ == 0; });
+    fn_ = nullptr;
+  }
+
+ private:
+  static constexpr int kWorkers = 8;
+  void work() {  // take tasks until none is left
+    for (;;) {
+      int i;
+      const std::function<void(int)>* f;
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        if (!fn_ || next_ >= total_) return;
+        i = next_++;
+        f = fn_;
+      }
+      (*f)(i);
+      std::lock_guard<std::mutex> lk(mu_);
+      if (--pending_ == 0) done_.notify_all();
+    }
+  }
+  void loop() {
+    uint64_t seen = 0;
+    std::unique_lock<std::mutex> lk(mu_);
+    for (;;) {
+      cv_.wait(lk, [&] { return quit_ || gen_ != seen; });
+      if (quit_) return;
+      seen = gen_;
+      lk.unlock();
+      work();
+      lk.lock();
+    }
+  }
+  std::vector<std::thread> th_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_;
+  const std::function<void(int)>* fn_ = nullptr;
+  int next_ = 0, total_ = 0, pending_ = 0;
+  uint64_t gen_ = 0;
+  bool quit_ = false;
+};
 
 }  // namespace
 
@@ -199,6 +251,7 @@ struct bsl_stack {
   size_t vr_retired_bytes = 0;
   void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
   uint64_t launches[BSL_KERNEL_KINDS] = {0, 0, 0, 0};  // forward launches per kernel (bsl_launch_counts)
+  WorkerPool loaders;             // host threads of bsl_load_blocks' staging
   std::vector<Weight> w;
 };
 
@@ -539,23 +592,41 @@ int bsl_load_blocks(bsl_stack* s, const int32_t* n_per_weight, void* stream) {
     uint8_t* buf = s->staging[k % 2];
     uint8_t* fac = buf + raw;  // the factor layouts, in slot order after the signs
     if (k >= 2 && (e = hipEventSynchronize(s->staged[k % 2])) != hipSuccess) break;  // its last copy and repack are done
-    // the factor layouts on one thread while the raw sign bits are copied on the others
-    bool scaled_ok = true;
-    std::thread factors([&] {
-      tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac));
-      const uint16_t* v = src.v;
-      if (!W.inv_scale.empty()) {
-        vscaled.resize((size_t)W.d * kRank);
-        if (!scale_v(v, W.d, W.inv_scale.data(), vscaled.data())) {
-          scaled_ok = false;
-          return;
+    // The raw sign bits are copied in slices of about 1 MiB, and the factor layouts written
+    // in row-tile and chunk ranges (a scaled V is scaled range by range first), all as
+    // tasks of the worker threads.
+    const int64_t mt = pad_rows(W.m) / kTileRows, nch = pad_cols(W.d) / kChunkCols;
+    const int ncopy = (int)std::min<size_t>(8, std::max<size_t>(1, raw >> 20));
+    const int nu = (int)std::min<int64_t>(4, std::max<int64_t>(1, mt / 64));
+    const int nv = (int)std::min<int64_t>(4, std::max<int64_t>(1, nch / 4));
+    const bool scaled = !W.inv_scale.empty();
+    if (scaled) vscaled.resize((size_t)W.d * kRank);
+    std::vector<char> vok(nv, 1);
+    const std::function<void(int)> task = [&](int t) {
+      if (t < ncopy) {
+        const size_t per = (raw + ncopy - 1) / ncopy, a = (size_t)t * per, b = std::min(raw, a + per);
+        if (a < b) std::memcpy(buf + a, src.sign_bits + a, b - a);
+      } else if (t < ncopy + nu) {
+        const int64_t k = t - ncopy, per = (mt + nu - 1) / nu;
+        tile_u(src.u, W.m, reinterpret_cast<uint16_t*>(fac), k * per, std::min(mt, (k + 1) * per));
+      } else {
+        const int64_t k = t - ncopy - nu, per = (nch + nv - 1) / nv;
+        const int64_t c0 = k * per, c1 = std::min(nch, (k + 1) * per);
+        const uint16_t* v = src.v;
+        if (scaled) {
+          if (!scale_v(v, std::min<int64_t>(W.d, c0 * kChunkCols), std::min<int64_t>(W.d, c1 * kChunkCols), W.inv_scale.data(),
+                       vscaled.data())) {
+            vok[k] = 0;
+            return;
+          }
+          v = vscaled.data();
         }
-        v = vscaled.data();
+        tile_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub), c0, c1);
       }
-      tile_v(v, W.d, reinterpret_cast<uint16_t*>(fac + ub));
-    });
-    copy_mt(buf, src.sign_bits, raw);
-    factors.join();
+    };
+    s->loaders.run(ncopy + nu + nv, task);
+    bool scaled_ok = true;
+    for (char ok : vok) scaled_ok = scaled_ok && ok;
     if (!scaled_ok) {
       overflow = a;
       break;

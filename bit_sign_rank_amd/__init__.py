@@ -24,10 +24,11 @@ BSL_EUNSUPPORTED = -4
 BSL_PATH_AUTO = 0
 BSL_PATH_FACTORED = 1
 BSL_PATH_TILE = 2
+BSL_PATH_PRODUCT = 3
 BSL_DECODE_AUTO = 0
 BSL_DECODE_SHARED = 1
 BSL_DECODE_PRIVATE = 2
-BSL_KERNEL_KINDS = 4
+BSL_KERNEL_KINDS = 5
 
 EXPORTED = (
     "bsl_block_bytes",

@@ -246,11 +246,13 @@ struct bsl_stack {
   size_t raw_dev_bytes = 0;
   uint32_t* tile_ctr = nullptr;   // tile path: arrival counters (kTileCounters), zero between launches
   uint16_t* vr_ws = nullptr;      // tile path: V of a launch's blocks in rank-major order (formed per call)
+  uint32_t* xt_ws = nullptr;      // product-index path: a launch's x in B-lane order (formed per call)
+  size_t xt_cap = 0;              // its bytes: kMaxGroup weights of the stack's most chunks
   size_t vr_cap = 0;              // its bytes: enough for the kMaxGroup weights with the most V bytes
   std::vector<void*> vr_retired;  // outgrown vr_ws buffers, freed once the device has drained
   size_t vr_retired_bytes = 0;
   void* static_scratch = nullptr; // this device's static scratch array (bsl_forward_group_static)
-  uint64_t launches[BSL_KERNEL_KINDS] = {0, 0, 0, 0};  // forward launches per kernel (bsl_launch_counts)
+  uint64_t launches[BSL_KERNEL_KINDS] = {0, 0, 0, 0, 0};  // forward launches per kernel (bsl_launch_counts)
   WorkerPool loaders;             // host threads of bsl_load_blocks' staging
   std::vector<Weight> w;
 };
@@ -430,15 +432,24 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     else if ((e = hipMemset(s->mt_counters, 0, s->mt_counter_words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
   }
   if (rc == BSL_OK) {
-    // row accumulators of the single- and few-token kernels: one per row and token of a
-    // launch (at most kMaxGroup weights of at most max_groups 1024-row groups, at most
-    // kWpMaxTokens tokens)
-    s->acc64_words = (size_t)kMaxGroup * max_groups * kDecodeGroupRows * kWpMaxTokens;
+    // row accumulators of the single-token, few-token and product-index kernels: one per
+    // row and token of a launch (at most kMaxGroup weights of at most max_groups 1024-row
+    // groups, at most kPxMaxTokens tokens: the product-index kernel keeps [32 tokens][32
+    // rows] per row tile)
+    s->acc64_words = (size_t)kMaxGroup * max_groups * kDecodeGroupRows * kPxMaxTokens;
     if ((e = hipMalloc(&s->acc64, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(row accumulators)");
     else if ((e = hipMemset(s->acc64, 0, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(row accumulators)");
     else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
     else if ((e = hipMalloc(&s->tile_ctr, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile counters)");
     else if ((e = hipMemset(s->tile_ctr, 0, kTileCounters * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(tile counters)");
+  }
+  if (rc == BSL_OK) {
+    // the product-index path's activations in B-lane order: kMaxGroup weights of the most
+    // 512-column chunks
+    int32_t max_nch = 0;
+    for (const Weight& W : s->w) max_nch = std::max(max_nch, W.nch);
+    s->xt_cap = (size_t)kMaxGroup * max_nch * kPxLaneBytesPerChunk;
+    if ((e = hipMalloc(&s->xt_ws, s->xt_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(x lanes)");
   }
   if (rc == BSL_OK) {
     const int se = static_scratch_setup(device, &s->static_scratch);
@@ -702,7 +713,7 @@ uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
 uint64_t bsl_workspace_bytes(const bsl_stack* s) {
   if (!s) return 0;
   uint64_t t = kZeroPageBytes + s->acc64_words * sizeof(uint64_t) + kTileWorkspaceFloats * sizeof(float) +
-               kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes;
+               kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes + s->xt_cap;
   t += s->mt_partial_floats * sizeof(float) + s->mt_counter_words * sizeof(uint32_t);
   t += sizeof(BlockPtrs) * (uint64_t)s->n_cap * s->w.size();
   return t;
@@ -715,6 +726,33 @@ int bsl_launch_counts(const bsl_stack* s, uint64_t* counts) {
 }
 
 namespace {
+
+// V of a launch's loaded blocks in rank-major order ([block][d_pad][16] fp16, read by the
+// tile and product-index kernels), in the stack's workspace: plan_rank_major_v points
+// each weight's vr into it, launch_rank_major_v runs the pass that fills it.
+int plan_rank_major_v(bsl_stack* s, GroupArgs& args) {
+  size_t vr_used = 0;
+  int64_t pairs = 0;
+  for (int32_t k = 0; k < args.count; ++k) {
+    WeightDesc& D = args.w[k];
+    D.vr = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(s->vr_ws) + vr_used);
+    vr_used += (size_t)D.nblocks * D.nch * kChunkCols * kRank * 2;
+    pairs += (int64_t)D.nblocks * D.nch * 8;
+  }
+  if (vr_used > s->vr_cap || pairs > (int64_t)INT32_MAX)
+    return fail(BSL_EUNSUPPORTED, "forward: the rank-major V of this launch does not fit the stack's workspace");
+  return BSL_OK;
+}
+int launch_rank_major_v(const GroupArgs& args, void* stream) {
+  GroupArgs vargs = args;  // items: (weight, block, 64-column step) pairs
+  int64_t pairs = 0;
+  for (int32_t k = 0; k < args.count; ++k) {
+    vargs.w[k].item_begin = (int32_t)pairs;
+    pairs += (int64_t)args.w[k].nblocks * args.w[k].nch * 8;
+  }
+  vargs.total_items = (int32_t)pairs;
+  return launch_v_rank_major(vargs, stream);
+}
 
 // Tile-reconstruct path.  Items are (weight, token group, 64-row group, column range);
 // weights go longest item first, so the long items of a launch start first.  A weight's
@@ -805,25 +843,109 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
     if (items > (int64_t)INT32_MAX) return fail(BSL_EUNSUPPORTED, "forward: too many tokens for one launch");
   }
   args.total_items = (int32_t)items;
-  // V of the launch's blocks in rank-major order, formed in the workspace first
-  GroupArgs vargs = args;
-  size_t vr_used = 0;
-  int64_t pairs = 0;
-  for (int32_t k = 0; k < count; ++k) {
-    WeightDesc& D = args.w[k];
-    D.vr = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(s->vr_ws) + vr_used);
-    vr_used += (size_t)D.nblocks * D.nch * kChunkCols * kRank * 2;
-    vargs.w[k] = D;
-    vargs.w[k].item_begin = (int32_t)pairs;
-    pairs += (int64_t)D.nblocks * D.nch * 8;
-  }
-  if (vr_used > s->vr_cap || pairs > (int64_t)INT32_MAX)
-    return fail(BSL_EUNSUPPORTED, "forward: the rank-major V of this launch does not fit the stack's workspace");
-  vargs.total_items = (int32_t)pairs;
+  const int rc = plan_rank_major_v(s, args);
+  if (rc != BSL_OK) return rc;
   DeviceGuard guard(s->device);
-  int e = launch_v_rank_major(vargs, stream);
+  int e = launch_rank_major_v(args, stream);
   if (e == 0) e = launch_tile(args, tt, (int)token_groups, stream);
   if (e == 0) ++s->launches[3];
+  if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
+  return BSL_OK;
+}
+
+// Product-index path: units (weight, group of kPxTiles 32-row tiles, batch of kPxBatch
+// blocks, 512-column chunk), an equal share per wave, two waves per SIMD; the shares of a
+// row group meet in the row accumulators (one word per row and token), so any split of a
+// group's units is exact up to each share's fp32 rounding.
+int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
+                    int32_t y_is_fp32, void* stream) {
+  if (M > kPxMaxTokens) return fail(BSL_EUNSUPPORTED, "forward: the product-index path takes at most 32 tokens");
+  GroupArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.count = count;
+  args.M = M;
+  args.y_fp32 = y_is_fp32 ? 1 : 0;
+  args.zero_page = s->zero_page;
+  uint64_t units = 0, tiles = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    const int32_t w = weights[j];
+    if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
+    for (int32_t jj = 0; jj < j; ++jj)
+      if (weights[jj] == w) return fail(BSL_EINVAL, "forward: a weight appears twice in one launch");
+    if (!x[j] || !y[j]) return fail(BSL_EINVAL, "forward: null x or y");
+    if ((reinterpret_cast<uintptr_t>(x[j]) & 15) != 0) return fail(BSL_EINVAL, "forward: x must be 16-byte aligned");
+    const Weight& W = s->w[w];
+    if ((uint64_t)pad_rows(W.m) * pad_cols(W.d) / 8 >= (1ull << 31))
+      return fail(BSL_EUNSUPPORTED, "forward: the product-index path needs each block's signs below 2 GiB");
+    WeightDesc& D = args.w[j];
+    D.blocks = W.dtable;
+    D.x = static_cast<const uint16_t*>(x[j]);
+    D.y = y[j];
+    D.m = W.m;
+    D.d = W.d;
+    D.mt = W.mt;
+    D.nch = W.nch;
+    D.nblocks = W.n;
+    D.groups = (W.m + kPxTiles * kPxTileRows - 1) / (kPxTiles * kPxTileRows);  // row groups
+    const uint64_t batches = (uint64_t)(W.n + kPxBatch - 1) / kPxBatch;
+    D.unit_begin = (uint32_t)units;
+    D.units = (uint32_t)(D.groups * batches * W.nch);
+    D.rg_begin = (uint32_t)tiles;  // first 32-row tile (row accumulators)
+    units += (uint64_t)D.groups * batches * W.nch;
+    tiles += (uint64_t)D.groups * kPxTiles;
+  }
+  if (units >= (1ull << 30)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+  if (tiles * kPxTileRows * kPxMaxTokens > s->acc64_words) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
+  args.total_units = (uint32_t)units;
+  args.total_groups = (uint32_t)tiles;
+  args.acc = s->acc64;
+  // Workers: a power of two, two per SIMD at most, at least four (one workgroup), no
+  // more than the units, and no row tile shared by more workers than its accumulators
+  // count.
+  auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
+  auto max_parts = [&](int lg) {
+    auto owner = [&](uint64_t u) {
+      uint64_t o = (u << lg) / units;
+      while (o + 1 < ((uint64_t)1 << lg) && start(o + 1, lg) <= u) ++o;
+      while (start(o, lg) > u) --o;
+      return o;
+    };
+    uint64_t worst = 0;
+    for (int32_t j = 0; j < count; ++j) {
+      const WeightDesc& D = args.w[j];
+      if (D.units == 0) continue;
+      const uint64_t per = D.units / (uint64_t)D.groups;
+      for (int32_t g = 0; g < D.groups; ++g) {
+        const uint64_t first = D.unit_begin + (uint64_t)g * per;
+        worst = std::max<uint64_t>(worst, owner(first + per - 1) - owner(first) + 1);
+      }
+    }
+    return worst;
+  };
+  int64_t workers = (int64_t)8 * s->decode_grid_max;
+  while (workers > 4 && (uint64_t)workers > units) workers /= 2;
+  int lg = 0;
+  while ((1ll << lg) < workers) ++lg;
+  while (lg > 2 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
+  if (units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
+  args.grid_log2 = lg;
+  // the activations in B-lane order, one (weight, chunk) item each
+  int64_t chunks = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    WeightDesc& D = args.w[j];
+    D.xt = s->xt_ws + (size_t)chunks * (kPxLaneBytesPerChunk / 4);
+    D.item_begin = (int32_t)chunks;
+    chunks += D.nch;
+  }
+  if ((size_t)chunks * kPxLaneBytesPerChunk > s->xt_cap) return fail(BSL_EUNSUPPORTED, "forward: x lanes workspace");
+  args.total_items = (int32_t)chunks;
+  const int rc = plan_rank_major_v(s, args);
+  if (rc != BSL_OK) return rc;
+  DeviceGuard guard(s->device);
+  int e = launch_rank_major_v(args, stream);
+  if (e == 0) e = launch_x_lanes(args, stream);
+  if (e == 0) e = launch_product(args, stream);
+  if (e == 0) ++s->launches[4];
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
 }
@@ -842,6 +964,8 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
+  if (!use_static && s->path == BSL_PATH_PRODUCT && M >= 2)
+    return forward_product(s, count, weights, x, y, M, y_is_fp32, stream);
   const bool tile = !use_static && (s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens));
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
   size_t mt_floats = 0, mt_words = 0;  // this launch's shares of the multi-token workspace
@@ -1083,7 +1207,7 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
 
 int bsl_set_path(bsl_stack* s, int32_t path) {
   if (!s) return fail(BSL_EINVAL, "bsl_set_path: null stack");
-  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE)
+  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE && path != BSL_PATH_PRODUCT)
     return fail(BSL_EINVAL, "bsl_set_path: unknown path");
   s->path = path;
   return BSL_OK;
@@ -1125,6 +1249,7 @@ void bsl_destroy(bsl_stack* s) {
   if (s->mt_partial) (void)hipFree(s->mt_partial);
   if (s->mt_counters) (void)hipFree(s->mt_counters);
   if (s->vr_ws) (void)hipFree(s->vr_ws);
+  if (s->xt_ws) (void)hipFree(s->xt_ws);
   free_retired(s);
   for (int k = 0; k < 2; ++k) {
     if (s->staging[k]) (void)hipHostFree(s->staging[k]);

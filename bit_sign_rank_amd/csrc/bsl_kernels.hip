@@ -2089,6 +2089,361 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
   resolve();
 }
 
+// ============================================================ activations in B-lane order
+// Per product-index launch: x of each weight (M <= 32 tokens) rewritten so that the
+// kernel's B operand of plane P, MFMA k is one 16-byte load per lane: lane l = 32 b + t
+// gets x[t][c + 4 b .. + 3] and x[t][c + 8 + 4 b .. + 3], c = 512 ch + 32 P + 16 k
+// (zeros for t >= M and for columns >= d).  One wave per (weight, chunk, plane, k).
+__global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int b = lane >> 5, t = lane & 31;
+  const uint32_t total = (uint32_t)args.total_items * (kPlanes * 2);
+  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u) {
+    const uint32_t pair = p / (kPlanes * 2), pk = p % (kPlanes * 2);  // (weight, chunk) pair; plane, k
+    int j = 0;
+    while (j + 1 < args.count && pair >= (uint32_t)args.w[j + 1].item_begin) ++j;
+    const WeightDesc& W = args.w[j];
+    const uint32_t ch = pair - (uint32_t)W.item_begin;
+    const int c = (int)ch * kChunkCols + 32 * (int)(pk >> 1) + 16 * (int)(pk & 1) + 4 * b;
+    u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+    if (t < args.M) {
+      const uint16_t* row = W.x + (size_t)t * W.d;
+      if (c < W.d) lo = load8(row + c);          // (d % 8 == 0: a 4-column run lies below d or past it)
+      if (c + 8 < W.d) hi = load8(row + c + 8);
+    }
+    *reinterpret_cast<u32x4*>(W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 256 + 4 * lane) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+  }
+}
+
+// ============================================================ product-index kernel
+// A few to 32 tokens.  The restoration adds, per block, the signs times the block's
+// products P_i = U_i V_i^T (OpenReview discussion, weight-restoration reply).  Here each
+// block's P_i, rounded to fp16 as the restoration forms it, is the value operand of the
+// 2:4 sparse MFMA and the stored sign bits are its indices, against B = +-x:
+//     y[t, j] = sum_i sum_c s_i[j, c] P_i[j, c] x[t, c],
+// so no sign is expanded to a number and the sums over blocks and columns run in the
+// fp32 accumulators.  Per 32-row tile, 32-column plane and block: one
+// v_mfma_f32_32x32x16_f16 (K = 16 = the rank) gives P for the tile and the plane, eight
+// conversions give two fp16 A operands, and two v_smfmac_f32_32x32x32_f16 add the plane's
+// columns for up to 32 tokens.  Per 1024 (row, column) pairs of a block that is 96
+// matrix-core cycles whatever the token count up to 32, against 64 per token for the
+// few-token kernel and a sign-application VALU cost of 2 operations per pair for the tile
+// kernel.
+//
+// Work: units (weight, 32-row tile, batch of NB blocks, 512-column chunk) in that order.
+// Every wave is a worker with a contiguous range of units (no LDS, no barrier), two
+// waves per SIMD, so one wave's conversions and loads run under the other's MFMAs.  A
+// batch past the weight's last block repeats a loaded block with U = 0 (read out of
+// range): those slots add exact zeros and need no branch.  The wave keeps its row tile's
+// y in registers across its units and adds it, when the row tile or its range ends, to
+// the row accumulators (acc_share); the worker whose add completes a (row, token) word
+// writes that element of y.
+//
+// Layouts (lane l, h = l / 32, j = l % 32):
+//  * rebuild: A = V[column cp(j) of the plane][ranks 8 h .. 8 h + 7] from the launch's
+//    rank-major V, B = U[row j][ranks 8 h ..]; cp(j) swaps bits 2 and 3 of j, so result
+//    register v of lane l is column 8 h + v % 8 + 16 (v / 8) of the plane for row j:
+//    registers 0-7 hold lane group g = h of the stored sign tile and 8-15 group 2 + h.
+//  * sparse MFMA k (k = 0, 1): A = registers 8 k .. 8 k + 7 as fp16 (column 8 g + e of
+//    group g = 2 k + h in value e, the order of the index fields of the stored word),
+//    index = the stored word of the row and group.  B: lane l holds token j and, as
+//    measured for this instruction, the 4-row groups of both A lane halves' value pairs
+//    2 h and 2 h + 1, i.e. columns 16 k + 4 h + {0, 1}, {2, 3}, 16 k + 8 + 4 h + {0, 1},
+//    {2, 3} of the plane in its odd or even form (the same forms as the single-token
+//    kernel's +-Z).  C: lane l holds token j, rows 8 (v / 4) + 4 h + v % 4.
+//
+// Loads: sign words of the next unit are requested at plane 0 (words of planes 0-7 and
+// 8-15 in two halves), V and x one plane ahead (V from L2: the rank-major copy; x from
+// L2: at most 32 tokens), U where a row tile or batch begins.  Tokens past M and columns
+// past d read zeros through the x descriptor's bound.
+__device__ __forceinline__ void px_result_ready(float16v& d) { asm("s_nop 15\n\ts_nop 3" : "+v"(d)); }
+static_assert(kPxTiles == 1 || kPxTiles == 2, "one hand-over wait per batch of rebuilds");
+
+template <int R, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void product_kernel(GroupArgs args) {
+  constexpr int KA = R == 1 ? 2 : 1;  // accumulators per row tile (R > 1: the tiles' MFMAs interleave)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, jl = lane & 31;
+  const uint32_t U = args.total_units;
+  const int lg = args.grid_log2;
+  const uint32_t G = gridDim.x, bid = blockIdx.x;
+  // XCD-contiguous workgroup index (workgroups are dealt round-robin over the XCDs)
+  const uint32_t L = G >= (uint32_t)kXcds ? (bid % kXcds) * (G / kXcds) + bid / kXcds : bid;
+  const uint32_t worker = L * 4u + (uint32_t)wave;
+  const uint32_t u_begin = range_start(worker, U, lg), u_end = range_start(worker + 1, U, lg);
+  const int M = args.M;
+  const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
+  if (worker >= (1u << lg)) return;  // (the host launches exactly 2^lg waves)
+  if (L == 0) {  // weights without blocks: y = 0, the empty sum
+    for (int j = 0; j < args.count; ++j)
+      if (args.w[j].units == 0)
+        for (int e = threadIdx.x; e < args.w[j].m * M; e += 256) store_y(args.w[j].y, e, 0.f, args.y_fp32);
+  }
+  if (u_begin >= u_end) return;
+
+  auto weight_of = [&](uint32_t u) {
+    int j = 0;
+    while (j + 1 < args.count && u >= args.w[j + 1].unit_begin) ++j;
+    return j;
+  };
+  struct Cur {
+    int32_t j, rt, bb, ch;
+    uint32_t u;
+    bool valid;
+    int32_t nb, nch, batches, d;
+  };
+  auto load_weight = [&](Cur& c) {
+    const WeightDesc& W = args.w[c.j];
+    c.nb = W.nblocks;
+    c.nch = W.nch;
+    c.batches = (W.nblocks + NB - 1) / NB;
+    c.d = W.d;
+  };
+  auto locate = [&](uint32_t u) {
+    Cur c;
+    c.j = weight_of(u);
+    load_weight(c);
+    const uint32_t local = u - args.w[c.j].unit_begin;
+    const uint32_t per_rt = (uint32_t)(c.batches * c.nch);
+    c.rt = (int32_t)(local / per_rt);
+    const uint32_t rem = local - (uint32_t)c.rt * per_rt;
+    c.bb = (int32_t)(rem / (uint32_t)c.nch);
+    c.ch = (int32_t)(rem - (uint32_t)c.bb * (uint32_t)c.nch);
+    c.u = u;
+    c.valid = true;
+    return c;
+  };
+  auto next = [&](Cur c) {
+    if (!c.valid || c.u + 1 >= u_end) {
+      c.valid = false;
+      return c;
+    }
+    ++c.u;
+    if (++c.ch == c.nch) {
+      c.ch = 0;
+      if (++c.bb == c.batches) {
+        c.bb = 0;
+        if (++c.rt == args.w[c.j].groups) {
+          c.rt = 0;
+          do ++c.j;
+          while (args.w[c.j].units == 0);
+          load_weight(c);
+        }
+      }
+    }
+    return c;
+  };
+
+  // ---- per-unit addresses (wave-uniform; few scalar registers: the blocks' sign
+  // addresses are formed where they are loaded)
+  struct UnitP {
+    rsrc_t v;           // rank-major V from the chunk of the batch's first block
+    uint32_t vstride;   // bytes per block of the rank-major V
+    int32_t nok;        // slots of the batch holding a loaded block
+    rsrc_t x;           // the chunk's activations in B-lane order (32 KiB)
+  };
+  auto unit_ptrs = [&](const Cur& c) {
+    UnitP p;
+    if (c.valid) {
+      const WeightDesc& W = args.w[c.j];
+      const int b0 = c.bb * NB;
+      p.nok = min(NB, c.nb - b0);
+      p.vstride = (uint32_t)c.nch * kChunkCols * kRank * 2u;
+      p.v = make_rsrc(reinterpret_cast<const uint8_t*>(W.vr) + ((size_t)b0 * c.nch + c.ch) * (kChunkCols * kRank * 2));
+      p.x = make_rsrc(W.xt + (size_t)c.ch * (kPxLaneBytesPerChunk / 4), (uint32_t)kPxLaneBytesPerChunk);
+    } else {
+      p.nok = 0;
+      p.vstride = 0;
+      p.v = make_rsrc(zero_page, (uint32_t)kZeroPageBytes);
+      p.x = make_rsrc(zero_page, 0u);
+    }
+    return p;
+  };
+
+  // per-lane offsets: this lane's row in the stored tiles (groups h and 2 + h), its V
+  // column
+  const int cpj = (jl & 0x13) | (((jl >> 3) & 1) << 2) | (((jl >> 2) & 1) << 3);
+  const uint32_t s_lane = (uint32_t)(((jl >> 4) * 64 + 16 * h + (jl & 15)) * 16);
+  const uint32_t v_lane = (uint32_t)((cpj * kRank + 8 * h) * 2);
+
+  u32x2 sw[R][NB][2][2];  // sign words [row tile][block][k][words 0-1 | 2-3] of the current unit
+  half8 uf[R][NB];        // U operands of the current row group and batch
+  u32x4 vv[2][NB];     // V operands of two planes
+  u32x4 xv[2][2];         // x words of two planes ([plane][k], B-lane order)
+  // sign words of unit c (slots past the batch's loaded blocks repeat its first block;
+  // their U is zero)
+  auto load_sw = [&](const Cur& c, int half) {
+    if (c.valid) {
+      const WeightDesc& W = args.w[c.j];
+      const uint32_t off = ((uint32_t)c.ch * (uint32_t)W.mt + 2u * (uint32_t)(R * c.rt)) * kTileBytes;  // (< 2 GiB)
+      const int b0 = c.bb * NB, nok = min(NB, c.nb - b0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const rsrc_t rs = make_rsrc(load_block(W.blocks, i < nok ? b0 + i : b0).signs);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) sw[r][i][k][half] = buf_load8(rs, s_lane, off + 2048u * r + 512u * k + 8u * half);
+      }
+    } else {
+      const rsrc_t rs = make_rsrc(zero_page, (uint32_t)kZeroPageBytes);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) sw[r][i][k][half] = buf_load8(rs, s_lane, 2048u * r + 512u * k + 8u * half);
+    }
+  };
+  auto load_v = [&](const UnitP& p, int P, u32x4 (&dst)[NB]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      dst[i] = buf_load16(p.v, v_lane, (uint32_t)P * (32u * kRank * 2u) + (uint32_t)(i < p.nok ? i : 0) * p.vstride);
+  };
+  auto load_x = [&](const UnitP& p, int P, u32x4 (&dst)[2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) dst[kk] = buf_load16(p.x, 16u * (uint32_t)lane, (uint32_t)(2 * P + kk) * 1024u);
+  };
+  auto load_u = [&](const Cur& c) {
+    const WeightDesc& W = args.w[c.j];
+    const int b0 = c.bb * NB, nok = min(NB, c.nb - b0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const uint16_t* u = load_block(W.blocks, i < nok ? b0 + i : b0).u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) uf[r][i] = load_u_ranks(u, 32 * (R * c.rt + r) + jl, h, i < nok);
+    }
+  };
+
+  // ---- flush: this wave's share of the row tile's y into the row accumulators
+  const uint32_t NWK = 1u << lg;
+  auto owner = [&](uint32_t u) {
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < NWK && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  float16v acc[R][KA];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
+  auto flush = [&](const Cur& c) __attribute__((always_inline)) {
+    const WeightDesc& W = args.w[c.j];
+    const uint32_t per_rg = (uint32_t)(c.batches * c.nch);
+    const uint32_t first = W.unit_begin + (uint32_t)c.rt * per_rg;
+    // the workers whose ranges hold units of the row group (with fewer units than
+    // workers some ranges are empty and add nothing)
+    uint32_t parts = 0;
+    for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
+      parts += range_start(o, U, lg) < range_start(o + 1, U, lg) ? 1u : 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int tile = R * c.rt + r;  // 32-row tile of the weight
+      uint64_t* words = args.acc + ((size_t)W.rg_begin + (size_t)tile) * (32 * kPxMaxTokens);
+      if (jl < M) {
+        // four rows at a time (the adds' returned words are needed at once)
+#pragma unroll
+        for (int v0 = 0; v0 < 16; v0 += 4) {
+          uint64_t share[4], old[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = v0 + e, m = 8 * (v >> 2) + 4 * h + (v & 3);
+            share[e] = acc_share(KA == 2 ? acc[r][0][v] + acc[r][KA - 1][v] : acc[r][0][v]);
+            old[e] = 0;
+            if (32 * tile + m < W.m)
+              old[e] = __hip_atomic_fetch_add(&words[jl * 32 + m], share[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int v = v0 + e, m = 8 * (v >> 2) + 4 * h + (v & 3);
+            const int row = 32 * tile + m;
+            const uint64_t now = old[e] + share[e];
+            if (row < W.m && acc_count(now) == parts) {
+              store_y(W.y, (size_t)jl * W.m + row, acc_value(now), args.y_fp32);
+              __hip_atomic_store(&words[jl * 32 + m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
+    }
+  };
+
+  uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
+  asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs: one v_and_or_b32 each)
+
+  Cur c = locate(u_begin);
+  Cur cn = next(c);
+  UnitP p0 = unit_ptrs(c), p1 = unit_ptrs(cn);
+  load_sw(c, 0);
+  load_sw(c, 1);
+  load_u(c);
+  load_v(p0, 0, vv[0]);
+  load_x(p0, 0, xv[0]);
+  uint32_t ix[R][NB][2];
+
+  // One plane P of the current unit: prefetch, indices, B operands, then per block the
+  // rebuild, its conversion and the two sparse MFMAs (the next block's rebuild issued
+  // before this block's conversion).
+#define BSL_PX_PLANE(P)                                                                                        \
+  __builtin_amdgcn_sched_barrier(0);                                                                           \
+  {                                                                                                            \
+    constexpr bool EV = plane_even(P);                                                                         \
+    if ((P) < kPlanes - 1) {                                                                                   \
+      load_v(p0, ((P) + 1) % kPlanes, vv[((P) + 1) % 2]);                                                     \
+      load_x(p0, ((P) + 1) % kPlanes, xv[((P) + 1) % 2]);                                                     \
+    } else {                                                                                                   \
+      load_v(p1, 0, vv[0]);                                                                                    \
+      load_x(p1, 0, xv[0]);                                                                                    \
+    }                                                                                                          \
+    if ((P) == 7) load_sw(cn, 0);  /* planes 0-7 of this unit are indexed: words 0-1 free */                  \
+    if ((P) == kPlanes - 1) load_sw(cn, 1);                                                                    \
+    if ((P) % 2 == 0) {                                                                                         \
+      _Pragma("unroll") for (int r = 0; r < R; ++r) _Pragma("unroll") for (int i = 0; i < NB; ++i)              \
+        _Pragma("unroll") for (int k = 0; k < 2; ++k)                                                           \
+          ix[r][i][k] = sign_index_v(sw[r][i][k][plane_word(P) / 2][plane_word(P) % 2], EV ? m_even : m_odd, EV);\
+    }                                                                                                           \
+    const u32x8 b0 = pm_v_operand<EV>(xv[(P) % 2][0]);                                                                     \
+    const u32x8 b1 = pm_v_operand<EV>(xv[(P) % 2][1]);                                                                     \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                                            \
+      /* the R tiles' rebuilds, one hand-over wait, then the conversions and the sparse MFMAs */                \
+      float16v pr[R];                                                                                           \
+      _Pragma("unroll") for (int r = 0; r < R; ++r) pr[r] = rebuild_mfma(as_half8(vv[(P) % 2][i]), uf[r][i]);   \
+      if constexpr (R == 2) mfma_result_ready(pr[0], pr[1]); else px_result_ready(pr[0]);                                     \
+      u32x4 a0[R], a1[R];                                                                                       \
+      _Pragma("unroll") for (int r = 0; r < R; ++r) _Pragma("unroll") for (int e = 0; e < 4; ++e) {             \
+        a0[r][e] = as_u32(__builtin_convertvector((float2v){pr[r][2 * e], pr[r][2 * e + 1]}, half2v));          \
+        a1[r][e] = as_u32(__builtin_convertvector((float2v){pr[r][8 + 2 * e], pr[r][9 + 2 * e]}, half2v));      \
+      }                                                                                                         \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                                             \
+        acc[r][0] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a0[r]), __builtin_bit_cast(half16, b0), acc[r][0],\
+                                                            (int)ix[r][i][0], 0, plane_half(P));                \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                                             \
+        acc[r][KA - 1] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a1[r]), __builtin_bit_cast(half16, b1),\
+                                                                 acc[r][KA - 1], (int)ix[r][i][1], 0, plane_half(P));\
+    }                                                                                                           \
+  }
+
+  while (true) {
+    BSL_PX_PLANE(0) BSL_PX_PLANE(1) BSL_PX_PLANE(2) BSL_PX_PLANE(3) BSL_PX_PLANE(4) BSL_PX_PLANE(5)
+    BSL_PX_PLANE(6) BSL_PX_PLANE(7) BSL_PX_PLANE(8) BSL_PX_PLANE(9) BSL_PX_PLANE(10) BSL_PX_PLANE(11)
+    BSL_PX_PLANE(12) BSL_PX_PLANE(13) BSL_PX_PLANE(14) BSL_PX_PLANE(15)
+    const bool tile_ends = !cn.valid || cn.j != c.j || cn.rt != c.rt;  // (the row group ends)
+    if (tile_ends) flush(c);
+    if (!cn.valid) break;
+    if (tile_ends || cn.bb != c.bb) load_u(cn);
+    c = cn;
+    p0 = p1;
+    cn = next(c);
+    p1 = unit_ptrs(cn);
+  }
+#undef BSL_PX_PLANE
+}
+
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write the signs.
 // Path 0: the single-token kernel's sparse indices (odd form: field 2 s + j, even form:
@@ -2271,6 +2626,20 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
     case 8: hipLaunchKernelGGL(tile_split_kernel<8>, grid, dim3(512), 0, st, args, token_groups); break;
     default: return (int)hipErrorInvalidValue;
   }
+  return (int)hipGetLastError();
+}
+
+int launch_product(const GroupArgs& args, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned workers = 1u << args.grid_log2;  // one per wave, four waves per workgroup
+  hipLaunchKernelGGL((product_kernel<kPxTiles, kPxBatch>), dim3(std::max(1u, workers / 4u)), dim3(256), 0, st, args);
+  return (int)hipGetLastError();
+}
+
+int launch_x_lanes(const GroupArgs& args, void* stream) {
+  if (args.total_items == 0) return 0;
+  const unsigned waves = (unsigned)args.total_items * (kPlanes * 2);
+  hipLaunchKernelGGL(x_lanes_kernel, dim3(std::min((waves + 3u) / 4u, 2048u)), dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }
 

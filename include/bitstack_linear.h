@@ -226,6 +226,7 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2
+#define BSL_PATH_PRODUCT 3
 int bsl_set_path(bsl_stack* s, int32_t path);
 
 /* Kernel of the single-token forward (M = 1; bsl_set_decode).  Both compute the same
@@ -256,7 +257,7 @@ int bsl_debug_unpack(bsl_stack* s, int32_t w, int32_t i, int32_t path, int8_t* p
  * [2] the factored multi-token kernel, [3] the tile-reconstruct kernel (host array of
  * BSL_KERNEL_KINDS entries).  A diagnostic: it tells a caller which formulation a call
  * took (bsl_set_path, bsl_set_decode), and how many launches a grouped call made. */
-#define BSL_KERNEL_KINDS 4
+#define BSL_KERNEL_KINDS 5
 int bsl_launch_counts(const bsl_stack* s, uint64_t* counts);
 
 /* Message for the calling thread's last failure ("" if none). */

@@ -90,9 +90,12 @@ def elem_factor(kernel, n, d):
     """Per-element error bound / A for each kernel's arithmetic (fp32 output):
     factored paths round Z = V x to fp16 once (U16) then sum in fp32 over d + 16 n terms;
     the wave-private kernels multiply V and x exactly inside the matrix core; the tile
-    path rounds each block's U_i V_i^T and each running sum of W_hat to fp16 (n + 1 U16)."""
+    path rounds each block's U_i V_i^T and each running sum of W_hat to fp16 (n + 1 U16);
+    the product-index kernel rounds each block's U_i V_i^T to fp16 once (U16) and sums
+    all n d products in fp32."""
     acc = (d + 16 * n) * U32
-    return {"z16": U16 + acc, "exact": acc, "tile": (n + 1) * U16 + acc}[kernel]
+    return {"z16": U16 + acc, "exact": acc, "tile": (n + 1) * U16 + acc,
+            "product": U16 + (n * d + 16 * n) * U32}[kernel]
 
 
 def assert_elementwise(y, ref, bound, ctx=""):

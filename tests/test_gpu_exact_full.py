@@ -27,7 +27,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 import bit_sign_rank_amd as bsl  # noqa: E402
 from gpu_util import REL_TOL, Stack, abs_bound, elem_factor, rel_err  # noqa: E402
 
-AUTO, FACT, TILE = bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE
+AUTO, FACT, TILE, PROD = bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE, bsl.BSL_PATH_PRODUCT
 SHARED, PRIVATE = bsl.BSL_DECODE_SHARED, bsl.BSL_DECODE_PRIVATE
 MAX_TOKENS = 2048
 
@@ -66,6 +66,10 @@ RUNS = [
     (4, FACT, None, "factored"),
     (16, AUTO, None, "tile"),
     (16, FACT, None, "factored"),
+    (2, PROD, None, "product-index"),
+    (4, PROD, None, "product-index"),
+    (16, PROD, None, "product-index"),
+    (32, PROD, None, "product-index"),
     (100, AUTO, None, "tile"),
     (200, AUTO, None, "tile"),
     (2048, AUTO, None, "tile"),
@@ -116,7 +120,7 @@ def test_dyadic_8b_variable_block_counts_bit_exact():
     with Stack(weights) as st:
         st.load([int(n) for n in counts])
         for M, path, decode in ((1, AUTO, SHARED), (1, AUTO, PRIVATE), (4, AUTO, None), (4, FACT, None),
-                                (16, AUTO, None), (16, FACT, None)):
+                                (16, AUTO, None), (16, FACT, None), (4, PROD, None), (16, PROD, None)):
             ys = run(st, range(7), xs, M, path, decode)
             for j, (y, ref) in enumerate(zip(ys, refs)):
                 assert_exact(y, ref[:M], f"8B variable counts {counts.tolist()}, {shapes[j][0]}, M={M}, path={path}, decode={decode}")
@@ -145,7 +149,7 @@ def test_dyadic_70b_weight_every_path_bit_exact(j):
         st.load([n])
         for M, path, decode in ((1, AUTO, SHARED), (1, AUTO, PRIVATE), (2, AUTO, None), (3, AUTO, None),
                                 (4, AUTO, None), (4, FACT, None), (16, AUTO, None), (16, FACT, None),
-                                (MAX_TOKENS, AUTO, None)):
+                                (16, PROD, None), (MAX_TOKENS, AUTO, None)):
             (y,) = run(st, [0], [x], M, path, decode)
             assert_exact(y, ref[:M], f"70B {synth.LLAMA2_70B_LAYER[j][0]} (n={n}), M={M}, path={path}, decode={decode}")
 
@@ -180,7 +184,8 @@ def float_8b():
 
 
 FLOAT_RUNS = [(1, AUTO, SHARED, "z16"), (1, AUTO, PRIVATE, "exact"), (4, AUTO, None, "exact"),
-              (4, FACT, None, "z16"), (16, AUTO, None, "tile"), (16, FACT, None, "z16")]
+              (4, FACT, None, "z16"), (16, AUTO, None, "tile"), (16, FACT, None, "z16"),
+              (4, PROD, None, "product"), (16, PROD, None, "product")]
 
 
 @pytest.mark.parametrize("M,path,decode,kind", FLOAT_RUNS, ids=[f"M{r[0]}-p{r[1]}-{r[3]}" for r in FLOAT_RUNS])

@@ -124,6 +124,12 @@ class Layers:
         return sum((2 * K_RANK * self.counts[l * self.per + j] * groups + 2 * self.M) * m * d
                    for j, (_, m, d) in enumerate(self.shapes))
 
+    def product_flops(self, l: int) -> int:
+        """MFMA work the product-index kernel executes: per block the K = k products
+        (2 k n m d) and the sparse contraction with the tokens padded to 32 (2 * 32 n m d,
+        counted as the instruction's useful work, half its dense equivalent)."""
+        return sum((2 * K_RANK + 2 * 32) * self.counts[l * self.per + j] * m * d for j, (_, m, d) in enumerate(self.shapes))
+
     def gemm_flops(self, l: int) -> int:
         return sum(2 * self.M * m * d for (_, m, d) in self.shapes)
 
@@ -739,6 +745,40 @@ def main() -> None:
                         "grouped launch, 2 rotated layers; MFMA work = the S Z contraction 2 n k M m d",
             "runs": few}
 
+    # ---------------- 4 to 32 tokens: the product-index kernel against the tile kernel (and the
+    # few-token kernel at M = 4) on the same stack
+    if not args.no_few:
+        prod = []
+        lay = Layers(bsl, torch, shapes, [[8] * 7] * 2, 2, args.seed + 9, M=32, shared_sources=True)
+        for M in ((16,) if args.profile_set else (4, 8, 16, 32)):
+            lay.M = M  # (the first M rows of the layer's 32-token x and y)
+            row = {"M": M}
+            paths = [("product", bsl.BSL_PATH_PRODUCT), ("tile", bsl.BSL_PATH_TILE)]
+            if M == 4:
+                paths.append(("few_token", bsl.BSL_PATH_AUTO))
+            for name, path in paths:
+                bsl.bsl_set_path(lay.h, path)
+                w_, k_, _, _ = time_steps(torch, lay, 40, 5)
+                row[f"{name}_us"] = round(float(np.mean(k_)) * 1e3, 1)
+            kus = row["product_us"] * 1e-6
+            row["auto_takes"] = "product" if 5 <= M <= 16 else ("few_token" if M <= 4 else "tile")
+            row["product_roofline"] = {"bound": "mfma", "achieved": round(lay.product_flops(0) / kus / 1e12, 1),
+                                       "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": round(lay.product_flops(0) / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
+                                       "flops": "executed MFMA work: (2 k + 2 * 32) n m d (tokens padded to 32)"}
+            row["tokens_per_s"] = round(M / kus, 1)
+            prod.append(row)
+            log(f"product-index: {row}")
+        bsl.bsl_set_path(lay.h, bsl.BSL_PATH_AUTO)
+        lay.close()
+        del lay
+        torch.cuda.empty_cache()
+        result["product_index"] = {
+            "workload": "Llama-3-8B-shaped layer linears, n=8, k=16, M tokens per grouped launch, 2 rotated layers; "
+                        "product_kernel (with its per-call V and x layout passes) against the tile path and, at M = 4, "
+                        "the few-token kernel",
+            "runs": prod}
+
     if not args.no_prefill:
         log("prefill: one 8B-shaped layer, n=8, M=2048, tile path")
         pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_TILE)
@@ -802,16 +842,21 @@ def main() -> None:
             w_, k_, b_, f_ = time_steps(torch, lay, steps, 5)
             kus = float(np.mean(k_)) * 1e-3
             row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
-                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("tile (tile_kernel<1, 2>)" if M >= 5 else "few-token (decode_wp_kernel<8, 4>)"),
+                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("product-index (product_kernel)" if M >= 5 else "few-token (decode_wp_kernel<8, 4>)"),
                    "bytes_per_step": lay.bytes(0), "GB_per_s": round(lay.bytes(0) / kus / 1e9, 1)}
             if M == 1:
                 row["roofline"] = {"bound": "hbm", "achieved": row["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(row["GB_per_s"] / HBM_PEAK_GBS, 4)}
             else:
-                fl = lay.tile_flops(0) if M >= 5 else lay.flops(0)
+                fl = lay.product_flops(0) if M >= 5 else lay.flops(0)
                 row["roofline"] = {"bound": "mfma", "achieved": round(fl / kus / 1e12, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(fl / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
-                                   "flops": "executed MFMA work of the path: " + ("(2 k n G + 2 M) m d, G = ceil(M/512)" if M >= 5 else "2 n k M m d")}
+                                   "flops": "executed MFMA work of the path: " + ("(2 k + 2 * 32) n m d (tokens padded to 32)" if M >= 5 else "2 n k M m d")}
+                if M >= 5:  # the tile path on the same stack, for comparison
+                    bsl.bsl_set_path(lay.h, bsl.BSL_PATH_TILE)
+                    _, kt_, _, _ = time_steps(torch, lay, steps, 5)
+                    bsl.bsl_set_path(lay.h, bsl.BSL_PATH_AUTO)
+                    row["tile_path_us_per_step"] = round(float(np.mean(kt_)) * 1e3, 1)
             sweep.append(row)
             lay.close()
             del lay

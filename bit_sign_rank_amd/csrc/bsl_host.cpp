@@ -853,10 +853,10 @@ int forward_tile(bsl_stack* s, int32_t count, const int32_t* weights, const void
   return BSL_OK;
 }
 
-// Product-index path: units (weight, group of kPxTiles 32-row tiles, batch of kPxBatch
-// blocks, 512-column chunk), an equal share per wave, two waves per SIMD; the shares of a
-// row group meet in the row accumulators (one word per row and token), so any split of a
-// group's units is exact up to each share's fp32 rounding.
+// Product-index path: units (weight, row group of kPxWaves x kPxTiles 32-row tiles, batch
+// of kPxBatch blocks, 512-column chunk), an equal share per workgroup of kPxWaves waves;
+// the shares of a row group meet in the row accumulators (one word per row and token),
+// so any split of a group's units is exact up to each share's fp32 rounding.
 int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y, int32_t M,
                     int32_t y_is_fp32, void* stream) {
   if (M > kPxMaxTokens) return fail(BSL_EUNSUPPORTED, "forward: the product-index path takes at most 32 tokens");
@@ -886,22 +886,21 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
     D.mt = W.mt;
     D.nch = W.nch;
     D.nblocks = W.n;
-    D.groups = (W.m + kPxTiles * kPxTileRows - 1) / (kPxTiles * kPxTileRows);  // row groups
+    D.groups = (W.m + kPxWaves * kPxTiles * kPxTileRows - 1) / (kPxWaves * kPxTiles * kPxTileRows);  // row groups
     const uint64_t batches = (uint64_t)(W.n + kPxBatch - 1) / kPxBatch;
     D.unit_begin = (uint32_t)units;
     D.units = (uint32_t)(D.groups * batches * W.nch);
     D.rg_begin = (uint32_t)tiles;  // first 32-row tile (row accumulators)
     units += (uint64_t)D.groups * batches * W.nch;
-    tiles += (uint64_t)D.groups * kPxTiles;
+    tiles += (uint64_t)D.groups * kPxWaves * kPxTiles;
   }
   if (units >= (1ull << 30)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
   if (tiles * kPxTileRows * kPxMaxTokens > s->acc64_words) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
   args.total_units = (uint32_t)units;
   args.total_groups = (uint32_t)tiles;
   args.acc = s->acc64;
-  // Workers: a power of two, two per SIMD at most, at least four (one workgroup), no
-  // more than the units, and no row tile shared by more workers than its accumulators
-  // count.
+  // Workers (workgroups): a power of two, one per CU at most, no more than the units, and
+  // no row group shared by more workers than its accumulators count.
   auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
   auto max_parts = [&](int lg) {
     auto owner = [&](uint64_t u) {
@@ -922,11 +921,11 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
     }
     return worst;
   };
-  int64_t workers = (int64_t)8 * s->decode_grid_max;
-  while (workers > 4 && (uint64_t)workers > units) workers /= 2;
+  int64_t workers = s->decode_grid_max;
+  while (workers > 1 && (uint64_t)workers > units) workers /= 2;
   int lg = 0;
   while ((1ll << lg) < workers) ++lg;
-  while (lg > 2 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
+  while (lg > 0 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
   if (units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
   args.grid_log2 = lg;
   // the activations in B-lane order, one (weight, chunk) item each
@@ -964,8 +963,13 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  if (!use_static && s->path == BSL_PATH_PRODUCT && M >= 2)
-    return forward_product(s, count, weights, x, y, M, y_is_fp32, stream);
+  // BSL_PATH_AUTO: 5 to 16 tokens on the product-index kernel (measured faster there than
+  // the tile kernel, whose sign application is VALU work per element and block, and than
+  // the few-token kernel, whose matrix work grows with every token)
+  const bool product = !use_static && M >= 2 &&
+                       (s->path == BSL_PATH_PRODUCT ||
+                        (s->path == BSL_PATH_AUTO && M >= kPxAutoMinTokens && M < kTileAutoMinTokens));
+  if (product) return forward_product(s, count, weights, x, y, M, y_is_fp32, stream);
   const bool tile = !use_static && (s->path == BSL_PATH_TILE || (s->path == BSL_PATH_AUTO && M >= kTileAutoMinTokens));
   if (tile) return forward_tile(s, count, weights, x, y, M, y_is_fp32, stream);
   size_t mt_floats = 0, mt_words = 0;  // this launch's shares of the multi-token workspace

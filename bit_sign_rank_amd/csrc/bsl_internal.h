@@ -50,8 +50,8 @@ struct WeightDesc {
                             // (workspace, zero between calls)
   uint16_t* vr;             // tile path: V of the loaded blocks in rank-major order, [block][d_pad][16]
                             // fp16 (workspace, formed by launch_v_rank_major at the start of the call)
-  uint32_t* xt;             // product-index path: x in the sparse MFMA's B-lane order, [chunk][plane][k]
-                            // [64 lanes][4 words] (workspace, formed by launch_x_lanes at the start)
+  uint32_t* xt;             // product-index path: the sparse MFMA's B operands (+-x), [chunk][plane][k]
+                            // [64 lanes][8 words] (workspace, formed by launch_x_lanes at the start)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks
@@ -86,14 +86,14 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
 // V of every loaded block of args' weights -> WeightDesc::vr; item_begin / total_items
 // count (block, 64-column step) pairs.
 int launch_v_rank_major(const GroupArgs& args, void* stream);
-// Product-index kernel: units and workers as args.total_units / grid_log2 (2^grid_log2 >= 4
-// waves), WeightDesc::groups = row groups, rg_begin = first 32-row tile, acc = row
-// accumulators, xt = the activations laid out by launch_x_lanes.
+// Product-index kernel: units and workers as args.total_units / grid_log2 (2^grid_log2
+// workgroups), WeightDesc::groups = row groups, rg_begin = first 32-row tile, acc = row
+// accumulators, vr / xt = the per-call layouts of V and x.
 int launch_product(const GroupArgs& args, void* stream);
 // x of args' weights (M <= kPxMaxTokens tokens) -> WeightDesc::xt; total_items counts the
 // (weight, chunk) pairs, item_begin each weight's first.
 int launch_x_lanes(const GroupArgs& args, void* stream);
-constexpr size_t kPxLaneBytesPerChunk = (size_t)kPlanes * 2 * 64 * 16;  // 32 KiB
+constexpr size_t kPxLaneBytesPerChunk = (size_t)kPlanes * 2 * 64 * 32;  // 64 KiB
 // Row-major sign bits (device, m rows of d/8 bytes) -> the tiled sign layout (device, the
 // first bsl_packed_sign_bytes(m, d) bytes of a block slot).
 int launch_repack_signs(const uint8_t* raw, int64_t m, int64_t d, int32_t mt, int32_t nch, uint8_t* out, void* stream);
@@ -134,10 +134,14 @@ constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-su
 constexpr int kTileGroupRows = 64;
 constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
-constexpr int kTileAutoMinTokens = 5;   // BSL_PATH_AUTO takes the tile path from this M on
-// Product-index path (M = 2..32 under BSL_PATH_PRODUCT): one worker per wave, two waves
-// per SIMD; units (weight, group of kPxTiles 32-row tiles, batch of kPxBatch blocks,
-// 512-column chunk).  Row accumulators: [32 tokens][32 rows] words per 32-row tile.
+constexpr int kTileAutoMinTokens = 17;  // BSL_PATH_AUTO takes the tile path from this M on
+constexpr int kPxAutoMinTokens = 5;     // and the product-index path from this M to kTileAutoMinTokens - 1
+// Product-index path (M = 2..32 under BSL_PATH_PRODUCT): one worker per workgroup of
+// kPxWaves waves (two per SIMD, one workgroup per CU); units (weight, row group of
+// kPxWaves x kPxTiles 32-row tiles, batch of kPxBatch blocks, 512-column chunk), each wave
+// owning kPxTiles tiles of the group.  Row accumulators: [32 tokens][32 rows] words per
+// 32-row tile.
+constexpr int kPxWaves = 8;
 constexpr int kPxTiles = 2;
 constexpr int kPxBatch = 2;
 constexpr int kPxMaxTokens = 32;

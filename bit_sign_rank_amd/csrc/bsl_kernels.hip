@@ -1010,6 +1010,11 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off, uint32_t sof
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off, uint32_t soff = 0) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 0));
 }
+// The same for data read exactly once (sign words): non-temporal (cache policy bit 1, nt
+// on this target), so the stream does not evict the L2 lines other waves re-read.
+__device__ __forceinline__ u32x2 buf_load8_stream(rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, 2));
+}
 // U[row][8 h .. 8 h + 7] (eight ranks of one row, the rebuild MFMA's B operand) gathered
 // from the tiled U, where rank r of row j is element j % 4 of lane 16 ((j % 16) / 4) + r
 // of row tile j / 16 (8 bytes per lane, 512 bytes per row tile).  Zeros when !valid.
@@ -2090,10 +2095,11 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 }
 
 // ============================================================ activations in B-lane order
-// Per product-index launch: x of each weight (M <= 32 tokens) rewritten so that the
-// kernel's B operand of plane P, MFMA k is one 16-byte load per lane: lane l = 32 b + t
-// gets x[t][c + 4 b .. + 3] and x[t][c + 8 + 4 b .. + 3], c = 512 ch + 32 P + 16 k
-// (zeros for t >= M and for columns >= d).  One wave per (weight, chunk, plane, k).
+// Per product-index launch: x of each weight (M <= 32 tokens) rewritten as the kernel's B
+// operands, so that the one of plane P, MFMA k is one 32-byte read per lane: lane
+// l = 32 b + t gets x[t][c + 4 b .. + 3] and x[t][c + 8 + 4 b .. + 3], c = 512 ch + 32 P
+// + 16 k (zeros for t >= M and for columns >= d), each pair in both signs in the plane's
+// odd or even group form.  One wave per (weight, chunk, plane, k).
 __global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -2112,7 +2118,11 @@ __global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
       if (c < W.d) lo = load8(row + c);          // (d % 8 == 0: a 4-column run lies below d or past it)
       if (c + 8 < W.d) hi = load8(row + c + 8);
     }
-    *reinterpret_cast<u32x4*>(W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 256 + 4 * lane) = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+    const u32x4 z = {lo[0], lo[1], hi[0], hi[1]};
+    const u32x8 bw = plane_even((int)(pk >> 1)) ? pm_v_operand<true>(z) : pm_v_operand<false>(z);
+    u32x4* out = reinterpret_cast<u32x4*>(W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 512 + 8 * lane);
+    out[0] = (u32x4){bw[0], bw[1], bw[2], bw[3]};
+    out[1] = (u32x4){bw[4], bw[5], bw[6], bw[7]};
   }
 }
 
@@ -2161,8 +2171,13 @@ __device__ __forceinline__ void px_result_ready(float16v& d) { asm("s_nop 15\n\t
 static_assert(kPxTiles == 1 || kPxTiles == 2, "one hand-over wait per batch of rebuilds");
 
 template <int R, int NB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void product_kernel(GroupArgs args) {
+__global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void product_kernel(GroupArgs args) {
   constexpr int KA = R == 1 ? 2 : 1;  // accumulators per row tile (R > 1: the tiles' MFMAs interleave)
+  constexpr int PARTS = NB + 4;       // 1 KiB parts of a plane's staging: V of the NB blocks, B for k = 0, 1 (2 KiB each)
+  static_assert(PARTS <= kPxWaves, "one 1 KiB part per staging wave");
+  constexpr int GP = 4;               // planes per staging group: one workgroup barrier per group
+  static_assert(kPlanes % GP == 0, "a unit is whole groups");
+  __shared__ __attribute__((aligned(16))) uint8_t stg[2][GP][PARTS * 1024];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int h = lane >> 5, jl = lane & 31;
@@ -2171,35 +2186,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   // XCD-contiguous workgroup index (workgroups are dealt round-robin over the XCDs)
   const uint32_t L = G >= (uint32_t)kXcds ? (bid % kXcds) * (G / kXcds) + bid / kXcds : bid;
-  const uint32_t worker = L * 4u + (uint32_t)wave;
-  const uint32_t u_begin = range_start(worker, U, lg), u_end = range_start(worker + 1, U, lg);
+  const uint32_t u_begin = range_start(L, U, lg), u_end = range_start(L + 1, U, lg);
   const int M = args.M;
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
-  if (worker >= (1u << lg)) return;  // (the host launches exactly 2^lg waves)
   if (L == 0) {  // weights without blocks: y = 0, the empty sum
     for (int j = 0; j < args.count; ++j)
       if (args.w[j].units == 0)
-        for (int e = threadIdx.x; e < args.w[j].m * M; e += 256) store_y(args.w[j].y, e, 0.f, args.y_fp32);
+        for (int e = threadIdx.x; e < args.w[j].m * M; e += kPxWaves * 64) store_y(args.w[j].y, e, 0.f, args.y_fp32);
   }
-  if (u_begin >= u_end) return;
+  if (u_begin >= u_end) return;  // (uniform over the workgroup)
 
   auto weight_of = [&](uint32_t u) {
     int j = 0;
     while (j + 1 < args.count && u >= args.w[j + 1].unit_begin) ++j;
     return j;
   };
+  // cursor over the unit list (uniform over the workgroup): rt is the row group of
+  // kPxWaves R 32-row tiles, of which this wave owns the R tiles R (kPxWaves rt + wave) ..
   struct Cur {
     int32_t j, rt, bb, ch;
     uint32_t u;
     bool valid;
-    int32_t nb, nch, batches, d;
+    int32_t nb, nch, batches;
   };
   auto load_weight = [&](Cur& c) {
     const WeightDesc& W = args.w[c.j];
     c.nb = W.nblocks;
     c.nch = W.nch;
     c.batches = (W.nblocks + NB - 1) / NB;
-    c.d = W.d;
   };
   auto locate = [&](uint32_t u) {
     Cur c;
@@ -2235,49 +2249,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     return c;
   };
+  // this wave's row group of the unit's rows (R 32-row tiles)
+  auto my_rg = [&](const Cur& c) { return kPxWaves * c.rt + wave; };
 
-  // ---- per-unit addresses (wave-uniform; few scalar registers: the blocks' sign
-  // addresses are formed where they are loaded)
-  struct UnitP {
-    rsrc_t v;           // rank-major V from the chunk of the batch's first block
-    uint32_t vstride;   // bytes per block of the rank-major V
-    int32_t nok;        // slots of the batch holding a loaded block
-    rsrc_t x;           // the chunk's activations in B-lane order (32 KiB)
+  // ---- staging: wave w < PARTS brings 1 KiB of every plane to LDS (part w), lane l 16
+  // bytes at l * 16: parts 0 .. NB - 1 hold the rank-major V of the plane (1 KiB per
+  // block), parts NB .. NB + 3 the plane's B operands for k = 0, 1 (2 KiB each)
+  const bool stager = wave < PARTS;  // (wave-uniform)
+  struct Src {
+    rsrc_t r;          // this wave's part of the unit's chunk
+    uint32_t pstride;  // bytes per plane in it
   };
-  auto unit_ptrs = [&](const Cur& c) {
-    UnitP p;
-    if (c.valid) {
+  auto unit_src = [&](const Cur& c) {
+    Src s;
+    if (c.valid && stager) {
       const WeightDesc& W = args.w[c.j];
-      const int b0 = c.bb * NB;
-      p.nok = min(NB, c.nb - b0);
-      p.vstride = (uint32_t)c.nch * kChunkCols * kRank * 2u;
-      p.v = make_rsrc(reinterpret_cast<const uint8_t*>(W.vr) + ((size_t)b0 * c.nch + c.ch) * (kChunkCols * kRank * 2));
-      p.x = make_rsrc(W.xt + (size_t)c.ch * (kPxLaneBytesPerChunk / 4), (uint32_t)kPxLaneBytesPerChunk);
+      if (wave < NB) {
+        const int b0 = c.bb * NB, nok = min(NB, c.nb - b0);
+        const int b = wave < nok ? b0 + wave : b0;  // (spare slots repeat the first block; their U is zero)
+        s.r = make_rsrc(reinterpret_cast<const uint8_t*>(W.vr) + ((size_t)b * c.nch + c.ch) * (kChunkCols * kRank * 2));
+        s.pstride = 32u * kRank * 2u;
+      } else {
+        s.r = make_rsrc(reinterpret_cast<const uint8_t*>(W.xt + (size_t)c.ch * (kPxLaneBytesPerChunk / 4)) + (wave - NB) * 1024,
+                        (uint32_t)kPxLaneBytesPerChunk);
+        s.pstride = 4096u;
+      }
     } else {
-      p.nok = 0;
-      p.vstride = 0;
-      p.v = make_rsrc(zero_page, (uint32_t)kZeroPageBytes);
-      p.x = make_rsrc(zero_page, 0u);
+      s.r = make_rsrc(zero_page, (uint32_t)kZeroPageBytes);
+      s.pstride = 0;
     }
-    return p;
+    return s;
+  };
+  u32x4 sr[GP];  // staged bytes of the next group's planes
+  auto stage_load = [&](const Src& s, int P) { return buf_load16(s.r, 16u * (uint32_t)lane, (uint32_t)P * s.pstride); };
+  auto stage_write = [&](int buf, int q, const u32x4& v) {
+    if (stager) *reinterpret_cast<u32x4*>(&stg[buf][q][wave * 1024 + 16 * lane]) = v;
   };
 
   // per-lane offsets: this lane's row in the stored tiles (groups h and 2 + h), its V
-  // column
+  // column's 16 bytes within a staged V part
   const int cpj = (jl & 0x13) | (((jl >> 3) & 1) << 2) | (((jl >> 2) & 1) << 3);
   const uint32_t s_lane = (uint32_t)(((jl >> 4) * 64 + 16 * h + (jl & 15)) * 16);
   const uint32_t v_lane = (uint32_t)((cpj * kRank + 8 * h) * 2);
 
   u32x2 sw[R][NB][2][2];  // sign words [row tile][block][k][words 0-1 | 2-3] of the current unit
   half8 uf[R][NB];        // U operands of the current row group and batch
-  u32x4 vv[2][NB];     // V operands of two planes
-  u32x4 xv[2][2];         // x words of two planes ([plane][k], B-lane order)
-  // sign words of unit c (slots past the batch's loaded blocks repeat its first block;
-  // their U is zero)
   auto load_sw = [&](const Cur& c, int half) {
     if (c.valid) {
       const WeightDesc& W = args.w[c.j];
-      const uint32_t off = ((uint32_t)c.ch * (uint32_t)W.mt + 2u * (uint32_t)(R * c.rt)) * kTileBytes;  // (< 2 GiB)
+      const uint32_t off = ((uint32_t)c.ch * (uint32_t)W.mt + 2u * (uint32_t)(R * my_rg(c))) * kTileBytes;  // (< 2 GiB)
       const int b0 = c.bb * NB, nok = min(NB, c.nb - b0);
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
@@ -2285,7 +2305,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-          for (int k = 0; k < 2; ++k) sw[r][i][k][half] = buf_load8(rs, s_lane, off + 2048u * r + 512u * k + 8u * half);
+          for (int k = 0; k < 2; ++k) sw[r][i][k][half] = buf_load8_stream(rs, s_lane, off + 2048u * r + 512u * k + 8u * half);
       }
     } else {
       const rsrc_t rs = make_rsrc(zero_page, (uint32_t)kZeroPageBytes);
@@ -2297,15 +2317,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int k = 0; k < 2; ++k) sw[r][i][k][half] = buf_load8(rs, s_lane, 2048u * r + 512u * k + 8u * half);
     }
   };
-  auto load_v = [&](const UnitP& p, int P, u32x4 (&dst)[NB]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      dst[i] = buf_load16(p.v, v_lane, (uint32_t)P * (32u * kRank * 2u) + (uint32_t)(i < p.nok ? i : 0) * p.vstride);
-  };
-  auto load_x = [&](const UnitP& p, int P, u32x4 (&dst)[2]) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) dst[kk] = buf_load16(p.x, 16u * (uint32_t)lane, (uint32_t)(2 * P + kk) * 1024u);
-  };
   auto load_u = [&](const Cur& c) {
     const WeightDesc& W = args.w[c.j];
     const int b0 = c.bb * NB, nok = min(NB, c.nb - b0);
@@ -2313,11 +2324,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < NB; ++i) {
       const uint16_t* u = load_block(W.blocks, i < nok ? b0 + i : b0).u;
 #pragma unroll
-      for (int r = 0; r < R; ++r) uf[r][i] = load_u_ranks(u, 32 * (R * c.rt + r) + jl, h, i < nok);
+      for (int r = 0; r < R; ++r) uf[r][i] = load_u_ranks(u, 32 * (R * my_rg(c) + r) + jl, h, i < nok);
     }
   };
 
-  // ---- flush: this wave's share of the row tile's y into the row accumulators
+  // ---- flush: this wave's share of its row tiles' y into the row accumulators
   const uint32_t NWK = 1u << lg;
   auto owner = [&](uint32_t u) {
     uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
@@ -2334,16 +2345,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const WeightDesc& W = args.w[c.j];
     const uint32_t per_rg = (uint32_t)(c.batches * c.nch);
     const uint32_t first = W.unit_begin + (uint32_t)c.rt * per_rg;
-    // the workers whose ranges hold units of the row group (with fewer units than
-    // workers some ranges are empty and add nothing)
+    // the workgroups whose ranges hold units of the row group (with fewer units than
+    // workgroups some ranges are empty and add nothing)
     uint32_t parts = 0;
     for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
       parts += range_start(o, U, lg) < range_start(o + 1, U, lg) ? 1u : 0u;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int tile = R * c.rt + r;  // 32-row tile of the weight
+      const int tile = R * my_rg(c) + r;  // 32-row tile of the weight
       uint64_t* words = args.acc + ((size_t)W.rg_begin + (size_t)tile) * (32 * kPxMaxTokens);
-      if (jl < M) {
+      if (jl < M && 32 * tile < W.m) {
         // four rows at a time (the adds' returned words are needed at once)
 #pragma unroll
         for (int v0 = 0; v0 < 16; v0 += 4) {
@@ -2376,55 +2387,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint32_t m_odd = 0xAAAAAAAAu, m_even = 0x55555555u;
   asm volatile("" : "+v"(m_odd), "+v"(m_even));  // (keeps the masks in VGPRs: one v_and_or_b32 each)
 
+  // ---- prologue: the first unit's signs and U, planes 0 .. D - 1 staged, plane 0 in LDS
   Cur c = locate(u_begin);
   Cur cn = next(c);
-  UnitP p0 = unit_ptrs(c), p1 = unit_ptrs(cn);
+  Src s0 = unit_src(c), s1 = unit_src(cn);
   load_sw(c, 0);
   load_sw(c, 1);
   load_u(c);
-  load_v(p0, 0, vv[0]);
-  load_x(p0, 0, xv[0]);
+#pragma unroll
+  for (int q = 0; q < GP; ++q) sr[q] = stage_load(s0, q);
+#pragma unroll
+  for (int q = 0; q < GP; ++q) stage_write(0, q, sr[q]);
+  lds_barrier();
   uint32_t ix[R][NB][2];
 
-  // One plane P of the current unit: prefetch, indices, B operands, then per block the
-  // rebuild, its conversion and the two sparse MFMAs (the next block's rebuild issued
-  // before this block's conversion).
-#define BSL_PX_PLANE(P)                                                                                        \
-  __builtin_amdgcn_sched_barrier(0);                                                                           \
-  {                                                                                                            \
-    constexpr bool EV = plane_even(P);                                                                         \
-    if ((P) < kPlanes - 1) {                                                                                   \
-      load_v(p0, ((P) + 1) % kPlanes, vv[((P) + 1) % 2]);                                                     \
-      load_x(p0, ((P) + 1) % kPlanes, xv[((P) + 1) % 2]);                                                     \
-    } else {                                                                                                   \
-      load_v(p1, 0, vv[0]);                                                                                    \
-      load_x(p1, 0, xv[0]);                                                                                    \
-    }                                                                                                          \
-    if ((P) == 7) load_sw(cn, 0);  /* planes 0-7 of this unit are indexed: words 0-1 free */                  \
-    if ((P) == kPlanes - 1) load_sw(cn, 1);                                                                    \
+  // One plane P of the current unit (group P / GP, in LDS buffer (P / GP) % 2): at a
+  // group's first plane the staging loads of the next group, the operands from LDS, per
+  // block the rebuilds, their conversion and the sparse MFMAs; after a group's last plane
+  // the next group's bytes go to the other buffer and the workgroup meets.
+#define BSL_PX_PLANE(P)                                                                                         \
+  {                                                                                                             \
+    constexpr bool EV = plane_even(P);                                                                          \
+    constexpr int SB = ((P) / GP) % 2, SQ = (P) % GP;                                                          \
+    if (SQ == 0) {                                                                                              \
+      __builtin_amdgcn_sched_barrier(0);                                                                        \
+      _Pragma("unroll") for (int q = 0; q < GP; ++q) {                                                         \
+        if ((P) + GP + q < kPlanes) sr[q] = stage_load(s0, (P) + GP + q);                                      \
+        else sr[q] = stage_load(s1, (P) + GP + q - kPlanes);                                                   \
+      }                                                                                                         \
+    }                                                                                                           \
+    if ((P) == 7) load_sw(cn, 0);  /* planes 0-7 of this unit are indexed: words 0-1 free */                    \
+    if ((P) == kPlanes - 1) load_sw(cn, 1);                                                                     \
     if ((P) % 2 == 0) {                                                                                         \
       _Pragma("unroll") for (int r = 0; r < R; ++r) _Pragma("unroll") for (int i = 0; i < NB; ++i)              \
         _Pragma("unroll") for (int k = 0; k < 2; ++k)                                                           \
-          ix[r][i][k] = sign_index_v(sw[r][i][k][plane_word(P) / 2][plane_word(P) % 2], EV ? m_even : m_odd, EV);\
+          ix[r][i][k] = sign_index_v(sw[r][i][k][plane_word(P) / 2][plane_word(P) % 2], EV ? m_even : m_odd, EV); \
     }                                                                                                           \
-    const u32x8 b0 = pm_v_operand<EV>(xv[(P) % 2][0]);                                                                     \
-    const u32x8 b1 = pm_v_operand<EV>(xv[(P) % 2][1]);                                                                     \
+    u32x4 va[NB];                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) va[i] = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][i * 1024 + v_lane]); \
+    const u32x8 b0 = *reinterpret_cast<const u32x8*>(&stg[SB][SQ][NB * 1024 + 32 * lane]);                    \
+    const u32x8 b1 = *reinterpret_cast<const u32x8*>(&stg[SB][SQ][(NB + 2) * 1024 + 32 * lane]);              \
+    /* block i: its rebuilds were issued one step earlier (block 0 at the top of the plane);                    \
+       the next block's are issued before block i's conversions, so the matrix core works                       \
+       on them meanwhile */                                                                                     \
+    float16v pn[R];                                                                                             \
+    _Pragma("unroll") for (int r = 0; r < R; ++r) pn[r] = rebuild_mfma(as_half8(va[0]), uf[r][0]);              \
     _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                                            \
-      /* the R tiles' rebuilds, one hand-over wait, then the conversions and the sparse MFMAs */                \
-      float16v pr[R];                                                                                           \
-      _Pragma("unroll") for (int r = 0; r < R; ++r) pr[r] = rebuild_mfma(as_half8(vv[(P) % 2][i]), uf[r][i]);   \
-      if constexpr (R == 2) mfma_result_ready(pr[0], pr[1]); else px_result_ready(pr[0]);                                     \
+      float16v pc[R];                                                                                           \
+      _Pragma("unroll") for (int r = 0; r < R; ++r) pc[r] = pn[r];                                              \
+      if (i + 1 < NB) {                                                                                         \
+        _Pragma("unroll") for (int r = 0; r < R; ++r) pn[r] = rebuild_mfma(as_half8(va[i + 1]), uf[r][i + 1]);  \
+      }                                                                                                         \
+      __builtin_amdgcn_sched_barrier(0x0120);                                                                   \
+      /* the wait states an MFMA result needs before a VALU read, after the last MFMA issued */                 \
+      if constexpr (R == 2) mfma_result_ready(pc[0], pc[1]); else px_result_ready(pc[0]);                       \
+      __builtin_amdgcn_sched_barrier(0);                                                                        \
       u32x4 a0[R], a1[R];                                                                                       \
       _Pragma("unroll") for (int r = 0; r < R; ++r) _Pragma("unroll") for (int e = 0; e < 4; ++e) {             \
-        a0[r][e] = as_u32(__builtin_convertvector((float2v){pr[r][2 * e], pr[r][2 * e + 1]}, half2v));          \
-        a1[r][e] = as_u32(__builtin_convertvector((float2v){pr[r][8 + 2 * e], pr[r][9 + 2 * e]}, half2v));      \
+        a0[r][e] = as_u32(__builtin_convertvector((float2v){pc[r][2 * e], pc[r][2 * e + 1]}, half2v));          \
+        a1[r][e] = as_u32(__builtin_convertvector((float2v){pc[r][8 + 2 * e], pc[r][9 + 2 * e]}, half2v));      \
       }                                                                                                         \
       _Pragma("unroll") for (int r = 0; r < R; ++r)                                                             \
-        acc[r][0] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a0[r]), __builtin_bit_cast(half16, b0), acc[r][0],\
+        acc[r][0] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a0[r]), __builtin_bit_cast(half16, b0), acc[r][0], \
                                                             (int)ix[r][i][0], 0, plane_half(P));                \
       _Pragma("unroll") for (int r = 0; r < R; ++r)                                                             \
-        acc[r][KA - 1] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a1[r]), __builtin_bit_cast(half16, b1),\
-                                                                 acc[r][KA - 1], (int)ix[r][i][1], 0, plane_half(P));\
+        acc[r][KA - 1] = __builtin_amdgcn_smfmac_f32_32x32x32_f16(as_half8(a1[r]), __builtin_bit_cast(half16, b1), \
+                                                                 acc[r][KA - 1], (int)ix[r][i][1], 0, plane_half(P)); \
+    }                                                                                                           \
+    if (SQ == GP - 1) {                                                                                         \
+      _Pragma("unroll") for (int q = 0; q < GP; ++q) stage_write(SB ^ 1, q, sr[q]);                            \
+      lds_barrier();                                                                                            \
     }                                                                                                           \
   }
 
@@ -2432,14 +2464,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     BSL_PX_PLANE(0) BSL_PX_PLANE(1) BSL_PX_PLANE(2) BSL_PX_PLANE(3) BSL_PX_PLANE(4) BSL_PX_PLANE(5)
     BSL_PX_PLANE(6) BSL_PX_PLANE(7) BSL_PX_PLANE(8) BSL_PX_PLANE(9) BSL_PX_PLANE(10) BSL_PX_PLANE(11)
     BSL_PX_PLANE(12) BSL_PX_PLANE(13) BSL_PX_PLANE(14) BSL_PX_PLANE(15)
-    const bool tile_ends = !cn.valid || cn.j != c.j || cn.rt != c.rt;  // (the row group ends)
-    if (tile_ends) flush(c);
+    const bool group_ends = !cn.valid || cn.j != c.j || cn.rt != c.rt;
+    if (group_ends) flush(c);
     if (!cn.valid) break;
-    if (tile_ends || cn.bb != c.bb) load_u(cn);
+    if (group_ends || cn.bb != c.bb) load_u(cn);
     c = cn;
-    p0 = p1;
+    s0 = s1;
     cn = next(c);
-    p1 = unit_ptrs(cn);
+    s1 = unit_src(cn);
   }
 #undef BSL_PX_PLANE
 }
@@ -2631,8 +2663,7 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
 
 int launch_product(const GroupArgs& args, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const unsigned workers = 1u << args.grid_log2;  // one per wave, four waves per workgroup
-  hipLaunchKernelGGL((product_kernel<kPxTiles, kPxBatch>), dim3(std::max(1u, workers / 4u)), dim3(256), 0, st, args);
+  hipLaunchKernelGGL((product_kernel<kPxTiles, kPxBatch>), dim3(1u << args.grid_log2), dim3(kPxWaves * 64), 0, st, args);
   return (int)hipGetLastError();
 }
 

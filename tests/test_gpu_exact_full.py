@@ -64,8 +64,9 @@ RUNS = [
     (2, FACT, None, "factored"),
     (3, FACT, None, "factored"),
     (4, FACT, None, "factored"),
-    (16, AUTO, None, "tile"),
+    (16, AUTO, None, "product-index"),
     (16, FACT, None, "factored"),
+    (16, TILE, None, "tile"),
     (2, PROD, None, "product-index"),
     (4, PROD, None, "product-index"),
     (16, PROD, None, "product-index"),
@@ -184,7 +185,7 @@ def float_8b():
 
 
 FLOAT_RUNS = [(1, AUTO, SHARED, "z16"), (1, AUTO, PRIVATE, "exact"), (4, AUTO, None, "exact"),
-              (4, FACT, None, "z16"), (16, AUTO, None, "tile"), (16, FACT, None, "z16"),
+              (4, FACT, None, "z16"), (16, AUTO, None, "product"), (16, TILE, None, "tile"), (16, FACT, None, "z16"),
               (4, PROD, None, "product"), (16, PROD, None, "product")]
 
 

@@ -242,7 +242,12 @@ PROFILE_KERNELS = (
      sum(2 * 8 * K_RANK * 4 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
     ("tile_split_kernel<8> (8B-shaped layer, n=8, M=2048)", "void bsl::tile_split_kernel<8>", None,
      sum((2 * K_RANK * 8 * 4 + 2 * 2048) * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
+    ("product_kernel<2, 2> (8B-shaped layer, n=8, M=16)", "void bsl::product_kernel<2, 2>", None,
+     sum((2 * K_RANK * 8 + 2 * 16 * 8) * m * d for _, m, d in synth.LLAMA3_8B_LAYER)),
 )
+# K = 16 rebuild MFMA work of the product-index kernel per launch of the profile set (rows and
+# columns of the 8B-shaped layer are multiples of its 512-row groups and 512-column chunks)
+PRODUCT_REBUILD_FLOPS = sum(2 * K_RANK * 8 * m * d for _, m, d in synth.LLAMA3_8B_LAYER)
 
 
 def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_dir: str, write_dir: str,
@@ -274,7 +279,7 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
         key = (r["Kernel_Name"], int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0))
         durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# rocprofv3 --kernel-trace --stats of bench.py --profile-set (Llama-3-8B-shaped layer, n=8, k=16):",
-             "# decode M=1 (both single-token kernels), few-token M=4, tile-path prefill M=2048",
+             "# decode M=1 (both single-token kernels), few-token M=4, product-index M=16 (against the tile path), tile-path prefill M=2048",
              f"command: {cmd[0].strip()}", f"kernel_source_sha256: {digest}", "",
              f"{'kernel':58s} {'grid':>8s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}"]
     for (name, grid), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
@@ -302,7 +307,7 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
            "# the dispatch's duration in the counter run (dispatches run one at a time there); MFMA busy is",
            "# SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over those cycles; MFMA flops are SQ_INSTS_VALU_MFMA_MOPS_F16 * 512",
            "# (the sparse 16x16x64 instruction counts at its dense-equivalent 32768 flops, twice the 16384 it does",
-           "# for the layer).",
+           "# for the layer; likewise the product kernel's sparse 32x32x32, with the tokens padded to 32).",
            f"pass 1: {cmd[1].strip() if len(cmd) > 1 else ''}", f"pass 2: {cmd[2].strip() if len(cmd) > 2 else ''}",
            *([f"pass 3 (vector memory path; busy fractions over GRBM_GUI_ACTIVE / 8 cycles and 256 CUs): {cmd[5].strip()}"]
              if mem_dir and len(cmd) > 5 else []),
@@ -320,7 +325,10 @@ def write_profile_summaries(trace_dir: str, sq1_dir: str, sq2_dir: str, fetch_di
         flops_ctr = med(a["SQ_INSTS_VALU_MFMA_MOPS_F16"]) * 512
         busy = med(a["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024 / cyc
         waves = med(a["SQ_WAVES"])
-        useful = flops_ctr / 2 if "decode" in prefix else flops_ctr
+        # the sparse instructions count at their dense equivalent, twice their useful work
+        # (the product kernel's K = 16 rebuild MFMAs are dense)
+        useful = (flops_ctr / 2 if "decode" in prefix else
+                  (flops_ctr + PRODUCT_REBUILD_FLOPS) / 2 if "product" in prefix else flops_ctr)
         out += [f"## {label}",
                 f"dispatch duration (counter run): {dur:.1f} us over {len(a['_dur_us'])} dispatches",
                 f"shader clock: {clock:.3f} GHz",

@@ -51,7 +51,7 @@ struct WeightDesc {
   uint16_t* vr;             // tile path: V of the loaded blocks in rank-major order, [block][d_pad][16]
                             // fp16 (workspace, formed by launch_v_rank_major at the start of the call)
   uint32_t* xt;             // product-index path: the sparse MFMA's B operands (+-x), [chunk][plane][k]
-                            // [64 lanes][8 words] (workspace, formed by launch_x_lanes at the start)
+                            // [words 0-3 | 4-7][64 lanes][4 words] (workspace, formed by launch_x_lanes)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks

@@ -2096,7 +2096,8 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 
 // ============================================================ activations in B-lane order
 // Per product-index launch: x of each weight (M <= 32 tokens) rewritten as the kernel's B
-// operands, so that the one of plane P, MFMA k is one 32-byte read per lane: lane
+// operands, so that the one of plane P, MFMA k is two 16-byte reads per lane (words 0-3
+// of every lane, then words 4-7, so that each read is contiguous across the lanes): lane
 // l = 32 b + t gets x[t][c + 4 b .. + 3] and x[t][c + 8 + 4 b .. + 3], c = 512 ch + 32 P
 // + 16 k (zeros for t >= M and for columns >= d), each pair in both signs in the plane's
 // odd or even group form.  One wave per (weight, chunk, plane, k).
@@ -2120,9 +2121,9 @@ __global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
     }
     const u32x4 z = {lo[0], lo[1], hi[0], hi[1]};
     const u32x8 bw = plane_even((int)(pk >> 1)) ? pm_v_operand<true>(z) : pm_v_operand<false>(z);
-    u32x4* out = reinterpret_cast<u32x4*>(W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 512 + 8 * lane);
-    out[0] = (u32x4){bw[0], bw[1], bw[2], bw[3]};
-    out[1] = (u32x4){bw[4], bw[5], bw[6], bw[7]};
+    uint32_t* out = W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 512 + 4 * lane;  // two 1 KiB halves
+    *reinterpret_cast<u32x4*>(out) = (u32x4){bw[0], bw[1], bw[2], bw[3]};
+    *reinterpret_cast<u32x4*>(out + 256) = (u32x4){bw[4], bw[5], bw[6], bw[7]};
   }
 }
 
@@ -2252,6 +2253,12 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
   // this wave's row group of the unit's rows (R 32-row tiles)
   auto my_rg = [&](const Cur& c) { return kPxWaves * c.rt + wave; };
 
+  // per-lane offsets: this lane's row in the stored tiles (groups h and 2 + h), its V
+  // column's 16 bytes within a plane of rank-major V
+  const int cpj = (jl & 0x13) | (((jl >> 3) & 1) << 2) | (((jl >> 2) & 1) << 3);
+  const uint32_t s_lane = (uint32_t)(((jl >> 4) * 64 + 16 * h + (jl & 15)) * 16);
+  const uint32_t v_lane = (uint32_t)((cpj * kRank + 8 * h) * 2);
+
   // ---- staging: wave w < PARTS brings 1 KiB of every plane to LDS (part w), lane l 16
   // bytes at l * 16: parts 0 .. NB - 1 hold the rank-major V of the plane (1 KiB per
   // block), parts NB .. NB + 3 the plane's B operands for k = 0, 1 (2 KiB each)
@@ -2281,16 +2288,14 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     return s;
   };
   u32x4 sr[GP];  // staged bytes of the next group's planes
-  auto stage_load = [&](const Src& s, int P) { return buf_load16(s.r, 16u * (uint32_t)lane, (uint32_t)P * s.pstride); };
+  // (a V part is fetched in the order its readers take it: lane l the 16 bytes of column
+  // cp(l % 32), ranks 8 (l / 32) .., so every LDS read and write is contiguous)
+  auto stage_load = [&](const Src& s, int P) {
+    return buf_load16(s.r, wave < NB ? v_lane : 16u * (uint32_t)lane, (uint32_t)P * s.pstride);
+  };
   auto stage_write = [&](int buf, int q, const u32x4& v) {
     if (stager) *reinterpret_cast<u32x4*>(&stg[buf][q][wave * 1024 + 16 * lane]) = v;
   };
-
-  // per-lane offsets: this lane's row in the stored tiles (groups h and 2 + h), its V
-  // column's 16 bytes within a staged V part
-  const int cpj = (jl & 0x13) | (((jl >> 3) & 1) << 2) | (((jl >> 2) & 1) << 3);
-  const uint32_t s_lane = (uint32_t)(((jl >> 4) * 64 + 16 * h + (jl & 15)) * 16);
-  const uint32_t v_lane = (uint32_t)((cpj * kRank + 8 * h) * 2);
 
   u32x2 sw[R][NB][2][2];  // sign words [row tile][block][k][words 0-1 | 2-3] of the current unit
   half8 uf[R][NB];        // U operands of the current row group and batch
@@ -2424,9 +2429,13 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
           ix[r][i][k] = sign_index_v(sw[r][i][k][plane_word(P) / 2][plane_word(P) % 2], EV ? m_even : m_odd, EV); \
     }                                                                                                           \
     u32x4 va[NB];                                                                                               \
-    _Pragma("unroll") for (int i = 0; i < NB; ++i) va[i] = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][i * 1024 + v_lane]); \
-    const u32x8 b0 = *reinterpret_cast<const u32x8*>(&stg[SB][SQ][NB * 1024 + 32 * lane]);                    \
-    const u32x8 b1 = *reinterpret_cast<const u32x8*>(&stg[SB][SQ][(NB + 2) * 1024 + 32 * lane]);              \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) va[i] = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][i * 1024 + 16 * lane]); \
+    const u32x4 b0l = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][NB * 1024 + 16 * lane]);                   \
+    const u32x4 b0h = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][(NB + 1) * 1024 + 16 * lane]);             \
+    const u32x8 b0 = {b0l[0], b0l[1], b0l[2], b0l[3], b0h[0], b0h[1], b0h[2], b0h[3]};                        \
+    const u32x4 b1l = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][(NB + 2) * 1024 + 16 * lane]);             \
+    const u32x4 b1h = *reinterpret_cast<const u32x4*>(&stg[SB][SQ][(NB + 3) * 1024 + 16 * lane]);             \
+    const u32x8 b1 = {b1l[0], b1l[1], b1l[2], b1l[3], b1h[0], b1h[1], b1h[2], b1h[3]};                        \
     /* block i: its rebuilds were issued one step earlier (block 0 at the top of the plane);                    \
        the next block's are issued before block i's conversions, so the matrix core works                       \
        on them meanwhile */                                                                                     \

@@ -928,21 +928,31 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
   while (lg > 0 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
   if (units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
   args.grid_log2 = lg;
-  // the activations in B-lane order, one (weight, chunk) item each
+  // the activations as the kernel's B operands, in the stack's workspace
   int64_t chunks = 0;
   for (int32_t j = 0; j < count; ++j) {
     WeightDesc& D = args.w[j];
     D.xt = s->xt_ws + (size_t)chunks * (kPxLaneBytesPerChunk / 4);
-    D.item_begin = (int32_t)chunks;
     chunks += D.nch;
   }
   if ((size_t)chunks * kPxLaneBytesPerChunk > s->xt_cap) return fail(BSL_EUNSUPPORTED, "forward: x lanes workspace");
-  args.total_items = (int32_t)chunks;
   const int rc = plan_rank_major_v(s, args);
   if (rc != BSL_OK) return rc;
+  // one launch for both layout passes: the V pass's (weight, block, step) pairs, then the
+  // x pass's (weight, chunk, plane, k) items
+  GroupArgs largs = args;
+  int64_t pairs = 0, xpairs = 0;
+  for (int32_t j = 0; j < count; ++j) {
+    largs.w[j].item_begin = (int32_t)pairs;
+    largs.w[j].unit_begin = (uint32_t)xpairs;
+    pairs += (int64_t)args.w[j].nblocks * args.w[j].nch * 8;
+    xpairs += args.w[j].nch;
+  }
+  if (xpairs * kPlanes * 2 > (int64_t)UINT32_MAX - pairs) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
+  largs.total_items = (int32_t)pairs;
+  largs.total_units = (uint32_t)(xpairs * kPlanes * 2);
   DeviceGuard guard(s->device);
-  int e = launch_rank_major_v(args, stream);
-  if (e == 0) e = launch_x_lanes(args, stream);
+  int e = launch_layout_pass(largs, stream);
   if (e == 0) e = launch_product(args, stream);
   if (e == 0) ++s->launches[4];
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");

@@ -51,7 +51,7 @@ struct WeightDesc {
   uint16_t* vr;             // tile path: V of the loaded blocks in rank-major order, [block][d_pad][16]
                             // fp16 (workspace, formed by launch_v_rank_major at the start of the call)
   uint32_t* xt;             // product-index path: the sparse MFMA's B operands (+-x), [chunk][plane][k]
-                            // [words 0-3 | 4-7][64 lanes][4 words] (workspace, formed by launch_x_lanes)
+                            // [words 0-3 | 4-7][64 lanes][4 words] (workspace, formed by launch_layout_pass)
   int32_t m, d;             // true sizes
   int32_t mt, nch;          // row tiles (m_pad / 16), column chunks (d_pad / 512)
   int32_t nblocks;          // loaded blocks
@@ -90,9 +90,11 @@ int launch_v_rank_major(const GroupArgs& args, void* stream);
 // workgroups), WeightDesc::groups = row groups, rg_begin = first 32-row tile, acc = row
 // accumulators, vr / xt = the per-call layouts of V and x.
 int launch_product(const GroupArgs& args, void* stream);
-// x of args' weights (M <= kPxMaxTokens tokens) -> WeightDesc::xt; total_items counts the
-// (weight, chunk) pairs, item_begin each weight's first.
-int launch_x_lanes(const GroupArgs& args, void* stream);
+// The product-index path's layout passes in one launch: the rank-major V pass (total_items
+// (weight, block, 64-column step) pairs, item_begin per weight) and x of args' weights (M
+// <= kPxMaxTokens tokens) as the kernel's B operands -> WeightDesc::xt (total_units items
+// of (weight, chunk, plane, k), unit_begin = each weight's first (weight, chunk) pair).
+int launch_layout_pass(const GroupArgs& args, void* stream);
 constexpr size_t kPxLaneBytesPerChunk = (size_t)kPlanes * 2 * 64 * 32;  // 64 KiB
 // Row-major sign bits (device, m rows of d/8 bytes) -> the tiled sign layout (device, the
 // first bsl_packed_sign_bytes(m, d) bytes of a block slot).

@@ -1395,15 +1395,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TT == 1 ? 2
 // costs one read and one write of the launch's V (32 bytes per block and column).  The
 // work is the list of (weight, block, 64-column step) pairs, item_begin giving each
 // weight's first pair; one pair per wave and iteration.
-__global__ __launch_bounds__(256) void v_rank_major_kernel(GroupArgs args) {
-  __shared__ u32x4 region[4][128];  // 2 KiB per wave
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// One (weight, block, 64-column step) pair p of the pass; `region` is the wave's 2 KiB of LDS.
+__device__ __forceinline__ void v_rank_item(const GroupArgs& args, uint32_t p, lds_u8* region, int lane) {
   const int jl = lane & 31, h = lane >> 5;
   const int sigma = 16 * ((jl >> 2) & 1) + 4 * (jl >> 3) + (jl & 3);
   const VRankLane vro = vrank_lane(lane);
-  const uint32_t total = (uint32_t)args.total_items;
-  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u) {
+  {
     int j = 0;
     while (j + 1 < args.count && p >= (uint32_t)args.w[j + 1].item_begin) ++j;
     const WeightDesc& W = args.w[j];
@@ -1413,11 +1410,19 @@ __global__ __launch_bounds__(256) void v_rank_major_kernel(GroupArgs args) {
     const rsrc_t r = make_rsrc(load_block(W.blocks, (int)i).v);
     const uint32_t off = step * 2048u + 16u * (uint32_t)lane;  // the step's two planes
     const u32x4 pa = buf_load16(r, off), pb = buf_load16(r, off + 1024u);
-    const VRank t = v_rank_order(pa, pb, (lds_u8*)&region[wave][0], vro);
+    const VRank t = v_rank_order(pa, pb, region, vro);
     uint16_t* out = W.vr + ((size_t)i * W.nch * kChunkCols + (size_t)step * 64 + sigma) * kRank + 8 * h;
     *reinterpret_cast<u32x4*>(out) = __builtin_bit_cast(u32x4, t.a);
     *reinterpret_cast<u32x4*>(out + 32 * kRank) = __builtin_bit_cast(u32x4, t.b);
   }
+}
+__global__ __launch_bounds__(256) void v_rank_major_kernel(GroupArgs args) {
+  __shared__ u32x4 region[4][128];  // 2 KiB per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t total = (uint32_t)args.total_items;
+  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u)
+    v_rank_item(args, p, (lds_u8*)&region[wave][0], lane);
 }
 
 // ------------------------------------------------------------ tile path, split roles
@@ -2100,18 +2105,17 @@ __global__ __launch_bounds__(kWpWaves * 64) __attribute__((amdgpu_waves_per_eu(1
 // of every lane, then words 4-7, so that each read is contiguous across the lanes): lane
 // l = 32 b + t gets x[t][c + 4 b .. + 3] and x[t][c + 8 + 4 b .. + 3], c = 512 ch + 32 P
 // + 16 k (zeros for t >= M and for columns >= d), each pair in both signs in the plane's
-// odd or even group form.  One wave per (weight, chunk, plane, k).
-__global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// odd or even group form.  One wave per (weight, chunk, plane, k) item p; WeightDesc::
+// unit_begin holds each weight's first (weight, chunk) pair.  The pass runs in the launch
+// of the rank-major V pass (layout_pass_kernel), after its V items.
+__device__ __forceinline__ void x_lanes_item(const GroupArgs& args, uint32_t p, int lane) {
   const int b = lane >> 5, t = lane & 31;
-  const uint32_t total = (uint32_t)args.total_items * (kPlanes * 2);
-  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u) {
+  {
     const uint32_t pair = p / (kPlanes * 2), pk = p % (kPlanes * 2);  // (weight, chunk) pair; plane, k
     int j = 0;
-    while (j + 1 < args.count && pair >= (uint32_t)args.w[j + 1].item_begin) ++j;
+    while (j + 1 < args.count && pair >= args.w[j + 1].unit_begin) ++j;
     const WeightDesc& W = args.w[j];
-    const uint32_t ch = pair - (uint32_t)W.item_begin;
+    const uint32_t ch = pair - W.unit_begin;
     const int c = (int)ch * kChunkCols + 32 * (int)(pk >> 1) + 16 * (int)(pk & 1) + 4 * b;
     u32x2 lo = {0u, 0u}, hi = {0u, 0u};
     if (t < args.M) {
@@ -2124,6 +2128,19 @@ __global__ __launch_bounds__(256) void x_lanes_kernel(GroupArgs args) {
     uint32_t* out = W.xt + ((size_t)ch * (kPlanes * 2) + pk) * 512 + 4 * lane;  // two 1 KiB halves
     *reinterpret_cast<u32x4*>(out) = (u32x4){bw[0], bw[1], bw[2], bw[3]};
     *reinterpret_cast<u32x4*>(out + 256) = (u32x4){bw[4], bw[5], bw[6], bw[7]};
+  }
+}
+// The product-index path's two layout passes in one launch: items [0, total_items) are
+// the rank-major V pass's (weight, block, 64-column step) pairs (item_begin per weight),
+// items [total_items, total_items + total_units) the x pass's (weight, chunk, plane, k).
+__global__ __launch_bounds__(256) void layout_pass_kernel(GroupArgs args) {
+  __shared__ u32x4 region[4][128];  // 2 KiB per wave (V pass)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t nv = (uint32_t)args.total_items, total = nv + args.total_units;
+  for (uint32_t p = blockIdx.x * 4u + (uint32_t)wave; p < total; p += gridDim.x * 4u) {
+    if (p < nv) v_rank_item(args, p, (lds_u8*)&region[wave][0], lane);
+    else x_lanes_item(args, p - nv, lane);
   }
 }
 
@@ -2676,10 +2693,10 @@ int launch_product(const GroupArgs& args, void* stream) {
   return (int)hipGetLastError();
 }
 
-int launch_x_lanes(const GroupArgs& args, void* stream) {
-  if (args.total_items == 0) return 0;
-  const unsigned waves = (unsigned)args.total_items * (kPlanes * 2);
-  hipLaunchKernelGGL(x_lanes_kernel, dim3(std::min((waves + 3u) / 4u, 2048u)), dim3(256), 0, static_cast<hipStream_t>(stream), args);
+int launch_layout_pass(const GroupArgs& args, void* stream) {
+  const unsigned waves = (unsigned)args.total_items + args.total_units;
+  if (waves == 0) return 0;
+  hipLaunchKernelGGL(layout_pass_kernel, dim3(std::min((waves + 3u) / 4u, 2048u)), dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }
 

@@ -769,7 +769,7 @@ def main() -> None:
                 w_, k_, _, _ = time_steps(torch, lay, 40, 5)
                 row[f"{name}_us"] = round(float(np.mean(k_)) * 1e3, 1)
             kus = row["product_us"] * 1e-6
-            row["auto_takes"] = "product" if 5 <= M <= 16 else ("few_token" if M <= 4 else "tile")
+            row["auto_takes"] = "product" if 5 <= M <= 32 else ("few_token" if M <= 4 else "tile")
             row["product_roofline"] = {"bound": "mfma", "achieved": round(lay.product_flops(0) / kus / 1e12, 1),
                                        "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                        "frac": round(lay.product_flops(0) / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),

@@ -248,6 +248,8 @@ struct bsl_stack {
   uint16_t* vr_ws = nullptr;      // tile path: V of a launch's blocks in rank-major order (formed per call)
   uint32_t* xt_ws = nullptr;      // product-index path: a launch's x in B-lane order (formed per call)
   size_t xt_cap = 0;              // its bytes: kMaxGroup weights of the stack's most chunks
+  float* px_part = nullptr;       // product-index path: workgroup shares of row groups
+  size_t px_part_slots = 0;       // kMaxGroup weights of the most 512-row groups + one per workgroup
   size_t vr_cap = 0;              // its bytes: enough for the kMaxGroup weights with the most V bytes
   std::vector<void*> vr_retired;  // outgrown vr_ws buffers, freed once the device has drained
   size_t vr_retired_bytes = 0;
@@ -432,11 +434,10 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     else if ((e = hipMemset(s->mt_counters, 0, s->mt_counter_words * sizeof(uint32_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(counters)");
   }
   if (rc == BSL_OK) {
-    // row accumulators of the single-token, few-token and product-index kernels: one per
-    // row and token of a launch (at most kMaxGroup weights of at most max_groups 1024-row
-    // groups, at most kPxMaxTokens tokens: the product-index kernel keeps [32 tokens][32
-    // rows] per row tile)
-    s->acc64_words = (size_t)kMaxGroup * max_groups * kDecodeGroupRows * kPxMaxTokens;
+    // row accumulators of the single- and few-token kernels: one per row and token of a
+    // launch (at most kMaxGroup weights of at most max_groups 1024-row groups, at most
+    // kWpMaxTokens tokens)
+    s->acc64_words = (size_t)kMaxGroup * max_groups * kDecodeGroupRows * kWpMaxTokens;
     if ((e = hipMalloc(&s->acc64, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMalloc(row accumulators)");
     else if ((e = hipMemset(s->acc64, 0, s->acc64_words * sizeof(uint64_t))) != hipSuccess) rc = hip_fail(e, "hipMemset(row accumulators)");
     else if ((e = hipMalloc(&s->tile_ws, kTileWorkspaceFloats * sizeof(float))) != hipSuccess) rc = hip_fail(e, "hipMalloc(tile workspace)");
@@ -450,6 +451,14 @@ int bsl_init(bsl_stack** out, int device, int32_t num_weights, const int32_t* m,
     for (const Weight& W : s->w) max_nch = std::max(max_nch, W.nch);
     s->xt_cap = (size_t)kMaxGroup * max_nch * kPxLaneBytesPerChunk;
     if ((e = hipMalloc(&s->xt_ws, s->xt_cap)) != hipSuccess) rc = hip_fail(e, "hipMalloc(x lanes)");
+    // shares of row groups: a workgroup's contiguous range of units meets each row group
+    // once, so (row group + workgroup) numbers the (row group, workgroup) pairs without
+    // collisions and needs at most row groups + workgroups slots
+    int64_t max_rg = 0;
+    for (const Weight& W : s->w) max_rg = std::max<int64_t>(max_rg, (W.m + kPxWaves * kPxTiles * kPxTileRows - 1) / (kPxWaves * kPxTiles * kPxTileRows));
+    s->px_part_slots = (size_t)kMaxGroup * max_rg + s->decode_grid_max;
+    if (rc == BSL_OK && (e = hipMalloc(&s->px_part, s->px_part_slots * kPxPartFloats * sizeof(float))) != hipSuccess)
+      rc = hip_fail(e, "hipMalloc(product shares)");
   }
   if (rc == BSL_OK) {
     const int se = static_scratch_setup(device, &s->static_scratch);
@@ -713,7 +722,8 @@ uint64_t bsl_resident_bytes(const bsl_stack* s) { return s ? s->resident : 0; }
 uint64_t bsl_workspace_bytes(const bsl_stack* s) {
   if (!s) return 0;
   uint64_t t = kZeroPageBytes + s->acc64_words * sizeof(uint64_t) + kTileWorkspaceFloats * sizeof(float) +
-               kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes + s->xt_cap;
+               kTileCounters * sizeof(uint32_t) + 2 * (uint64_t)s->raw_dev_bytes + s->vr_cap + s->vr_retired_bytes + s->xt_cap +
+               s->px_part_slots * kPxPartFloats * sizeof(float);
   t += s->mt_partial_floats * sizeof(float) + s->mt_counter_words * sizeof(uint32_t);
   t += sizeof(BlockPtrs) * (uint64_t)s->n_cap * s->w.size();
   return t;
@@ -866,7 +876,7 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
   args.zero_page = s->zero_page;
-  uint64_t units = 0, tiles = 0;
+  uint64_t units = 0, groups = 0;
   for (int32_t j = 0; j < count; ++j) {
     const int32_t w = weights[j];
     if (w < 0 || w >= (int32_t)s->w.size()) return fail(BSL_EINVAL, "forward: weight index out of range");
@@ -890,43 +900,21 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
     const uint64_t batches = (uint64_t)(W.n + kPxBatch - 1) / kPxBatch;
     D.unit_begin = (uint32_t)units;
     D.units = (uint32_t)(D.groups * batches * W.nch);
-    D.rg_begin = (uint32_t)tiles;  // first 32-row tile (row accumulators)
+    D.rg_begin = (uint32_t)groups;  // first row group of the launch (share slots)
     units += (uint64_t)D.groups * batches * W.nch;
-    tiles += (uint64_t)D.groups * kPxWaves * kPxTiles;
+    groups += (uint64_t)D.groups;
   }
   if (units >= (1ull << 30)) return fail(BSL_EUNSUPPORTED, "forward: too much work for one launch");
-  if (tiles * kPxTileRows * kPxMaxTokens > s->acc64_words) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
   args.total_units = (uint32_t)units;
-  args.total_groups = (uint32_t)tiles;
-  args.acc = s->acc64;
-  // Workers (workgroups): a power of two, one per CU at most, no more than the units, and
-  // no row group shared by more workers than its accumulators count.
-  auto start = [&](uint64_t o, int lg) { return (o * units) >> lg; };
-  auto max_parts = [&](int lg) {
-    auto owner = [&](uint64_t u) {
-      uint64_t o = (u << lg) / units;
-      while (o + 1 < ((uint64_t)1 << lg) && start(o + 1, lg) <= u) ++o;
-      while (start(o, lg) > u) --o;
-      return o;
-    };
-    uint64_t worst = 0;
-    for (int32_t j = 0; j < count; ++j) {
-      const WeightDesc& D = args.w[j];
-      if (D.units == 0) continue;
-      const uint64_t per = D.units / (uint64_t)D.groups;
-      for (int32_t g = 0; g < D.groups; ++g) {
-        const uint64_t first = D.unit_begin + (uint64_t)g * per;
-        worst = std::max<uint64_t>(worst, owner(first + per - 1) - owner(first) + 1);
-      }
-    }
-    return worst;
-  };
+  args.total_groups = (uint32_t)groups;
+  // Workers (workgroups): a power of two, one per CU at most, no more than the units.
   int64_t workers = s->decode_grid_max;
   while (workers > 1 && (uint64_t)workers > units) workers /= 2;
   int lg = 0;
   while ((1ll << lg) < workers) ++lg;
-  while (lg > 0 && units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) --lg;
-  if (units > 0 && max_parts(lg) > (uint64_t)kAccMaxParts) return fail(BSL_EUNSUPPORTED, "forward: row accumulators");
+  // a slot per (row group, workgroup) pair: at most row groups + workgroups of them
+  if (groups + ((uint64_t)1 << lg) > s->px_part_slots) return fail(BSL_EUNSUPPORTED, "forward: product share slots");
+  args.part = s->px_part;
   args.grid_log2 = lg;
   // the activations as the kernel's B operands, in the stack's workspace
   int64_t chunks = 0;
@@ -954,6 +942,7 @@ int forward_product(bsl_stack* s, int32_t count, const int32_t* weights, const v
   DeviceGuard guard(s->device);
   int e = launch_layout_pass(largs, stream);
   if (e == 0) e = launch_product(args, stream);
+  if (e == 0) e = launch_product_finish(args, stream);
   if (e == 0) ++s->launches[4];
   if (e != 0) return hip_fail(static_cast<hipError_t>(e), "kernel launch");
   return BSL_OK;
@@ -973,7 +962,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  // BSL_PATH_AUTO: 5 to 16 tokens on the product-index kernel (measured faster there than
+  // BSL_PATH_AUTO: 5 to 32 tokens on the product-index kernel (measured faster there than
   // the tile kernel, whose sign application is VALU work per element and block, and than
   // the few-token kernel, whose matrix work grows with every token)
   const bool product = !use_static && M >= 2 &&
@@ -1264,6 +1253,7 @@ void bsl_destroy(bsl_stack* s) {
   if (s->mt_counters) (void)hipFree(s->mt_counters);
   if (s->vr_ws) (void)hipFree(s->vr_ws);
   if (s->xt_ws) (void)hipFree(s->xt_ws);
+  if (s->px_part) (void)hipFree(s->px_part);
   free_retired(s);
   for (int k = 0; k < 2; ++k) {
     if (s->staging[k]) (void)hipHostFree(s->staging[k]);

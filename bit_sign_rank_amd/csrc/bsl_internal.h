@@ -74,6 +74,8 @@ struct GroupArgs {
   uint32_t total_groups; // single-token path: row groups over all weights
   int32_t grid_log2;     // single-token path: log2 of the (power-of-two) grid
   const void* zero_page; // kZeroPageBytes of zeros: target of prefetches past the end of the work
+  float* part;           // product-index path: each workgroup's fp32 share of each row group it works on,
+                         // slot (row group + workgroup) of kPxPartFloats floats (workspace)
   uint64_t* acc;         // single- and few-token paths: row accumulators, [total_groups][rows x tokens of a
                          // row group], zero between launches (workspace)
 };
@@ -90,6 +92,9 @@ int launch_v_rank_major(const GroupArgs& args, void* stream);
 // workgroups), WeightDesc::groups = row groups, rg_begin = first 32-row tile, acc = row
 // accumulators, vr / xt = the per-call layouts of V and x.
 int launch_product(const GroupArgs& args, void* stream);
+// After launch_product on the same stream: y from the row groups' shares, added in
+// workgroup order.
+int launch_product_finish(const GroupArgs& args, void* stream);
 // The product-index path's layout passes in one launch: the rank-major V pass (total_items
 // (weight, block, 64-column step) pairs, item_begin per weight) and x of args' weights (M
 // <= kPxMaxTokens tokens) as the kernel's B operands -> WeightDesc::xt (total_units items
@@ -136,17 +141,18 @@ constexpr int kSplitTokens = 128;       // splits x padded tokens the partial-su
 constexpr int kTileGroupRows = 64;
 constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
-constexpr int kTileAutoMinTokens = 17;  // BSL_PATH_AUTO takes the tile path from this M on
+constexpr int kTileAutoMinTokens = 33;  // BSL_PATH_AUTO takes the tile path from this M on
 constexpr int kPxAutoMinTokens = 5;     // and the product-index path from this M to kTileAutoMinTokens - 1
 // Product-index path (M = 2..32 under BSL_PATH_PRODUCT): one worker per workgroup of
 // kPxWaves waves (two per SIMD, one workgroup per CU); units (weight, row group of
 // kPxWaves x kPxTiles 32-row tiles, batch of kPxBatch blocks, 512-column chunk), each wave
-// owning kPxTiles tiles of the group.  Row accumulators: [32 tokens][32 rows] words per
-// 32-row tile.
+// owning kPxTiles tiles of the group.  The shares of a row group go to slots of
+// kPxPartFloats floats, in each wave's MFMA result layout [wave][tile][register][lane].
 constexpr int kPxWaves = 8;
 constexpr int kPxTiles = 2;
 constexpr int kPxBatch = 2;
 constexpr int kPxMaxTokens = 32;
+constexpr int kPxPartFloats = 8 * 2 * 16 * 64;  // kPxWaves x kPxTiles x 16 registers x 64 lanes
 constexpr int kPxTileRows = 32;
 // Tile-path items may be cut along the columns (chunk ranges) when a launch has too few
 // of them to fill the chip; the ranges' partial sums go to a workspace of the stack.

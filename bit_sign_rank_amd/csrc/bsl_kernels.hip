@@ -2159,14 +2159,14 @@ __global__ __launch_bounds__(256) void layout_pass_kernel(GroupArgs args) {
 // few-token kernel and a sign-application VALU cost of 2 operations per pair for the tile
 // kernel.
 //
-// Work: units (weight, 32-row tile, batch of NB blocks, 512-column chunk) in that order.
-// Every wave is a worker with a contiguous range of units (no LDS, no barrier), two
-// waves per SIMD, so one wave's conversions and loads run under the other's MFMAs.  A
-// batch past the weight's last block repeats a loaded block with U = 0 (read out of
-// range): those slots add exact zeros and need no branch.  The wave keeps its row tile's
-// y in registers across its units and adds it, when the row tile or its range ends, to
-// the row accumulators (acc_share); the worker whose add completes a (row, token) word
-// writes that element of y.
+// Work: units (weight, row group of 8 x R 32-row tiles, batch of NB blocks, 512-column
+// chunk) in that order.  One 8-wave workgroup per CU (two waves per SIMD) walks an equal
+// contiguous share of the units; wave w owns the R tiles of rows 32 R w .. of the group.
+// A batch past the weight's last block repeats a loaded block with U = 0 (read out of
+// range): those slots add exact zeros and need no branch.  Each wave keeps its tiles' y
+// in registers across its units and, when the row group or its range ends, stores it in
+// the workgroup's slot for the row group; product_finish_kernel, next in the stream, adds
+// a row group's slots in workgroup order (deterministic, and no atomics).
 //
 // Layouts (lane l, h = l / 32, j = l % 32):
 //  * rebuild: A = V[column cp(j) of the plane][ranks 8 h .. 8 h + 7] from the launch's
@@ -2181,10 +2181,11 @@ __global__ __launch_bounds__(256) void layout_pass_kernel(GroupArgs args) {
 //    {2, 3} of the plane in its odd or even form (the same forms as the single-token
 //    kernel's +-Z).  C: lane l holds token j, rows 8 (v / 4) + 4 h + v % 4.
 //
-// Loads: sign words of the next unit are requested at plane 0 (words of planes 0-7 and
-// 8-15 in two halves), V and x one plane ahead (V from L2: the rank-major copy; x from
-// L2: at most 32 tokens), U where a row tile or batch begins.  Tokens past M and columns
-// past d read zeros through the x descriptor's bound.
+// Loads: the V of the batch and the plane's B operands (+-x, laid out per call by
+// layout_pass_kernel) are the same for every wave, so the workgroup stages them in LDS:
+// four planes per group and barrier, a group ahead.  Sign words are each wave's own and
+// are requested (non-temporal) at planes 7 and 15 of the previous unit; U where a row
+// group or batch begins.
 __device__ __forceinline__ void px_result_ready(float16v& d) { asm("s_nop 15\n\ts_nop 3" : "+v"(d)); }
 static_assert(kPxTiles == 1 || kPxTiles == 2, "one hand-over wait per batch of rebuilds");
 
@@ -2207,11 +2208,6 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t u_begin = range_start(L, U, lg), u_end = range_start(L + 1, U, lg);
   const int M = args.M;
   const uint8_t* zero_page = static_cast<const uint8_t*>(args.zero_page);
-  if (L == 0) {  // weights without blocks: y = 0, the empty sum
-    for (int j = 0; j < args.count; ++j)
-      if (args.w[j].units == 0)
-        for (int e = threadIdx.x; e < args.w[j].m * M; e += kPxWaves * 64) store_y(args.w[j].y, e, 0.f, args.y_fp32);
-  }
   if (u_begin >= u_end) return;  // (uniform over the workgroup)
 
   auto weight_of = [&](uint32_t u) {
@@ -2350,57 +2346,22 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
-  // ---- flush: this wave's share of its row tiles' y into the row accumulators
-  const uint32_t NWK = 1u << lg;
-  auto owner = [&](uint32_t u) {
-    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
-    while (o + 1 < NWK && range_start(o + 1, U, lg) <= u) ++o;
-    while (range_start(o, U, lg) > u) --o;
-    return o;
-  };
+  // ---- flush: this wave's share of its row tiles' y (fp32, in the MFMA result layout)
+  // into the workgroup's slot for the row group, (row group + L): plain stores, each 256
+  // contiguous bytes per instruction.  product_finish_kernel, next in the stream, adds
+  // the slots of a row group in workgroup order.
   float16v acc[R][KA];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
   auto flush = [&](const Cur& c) __attribute__((always_inline)) {
-    const WeightDesc& W = args.w[c.j];
-    const uint32_t per_rg = (uint32_t)(c.batches * c.nch);
-    const uint32_t first = W.unit_begin + (uint32_t)c.rt * per_rg;
-    // the workgroups whose ranges hold units of the row group (with fewer units than
-    // workgroups some ranges are empty and add nothing)
-    uint32_t parts = 0;
-    for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
-      parts += range_start(o, U, lg) < range_start(o + 1, U, lg) ? 1u : 0u;
+    float* slot = args.part + ((size_t)args.w[c.j].rg_begin + (size_t)c.rt + L) * kPxPartFloats;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int tile = R * my_rg(c) + r;  // 32-row tile of the weight
-      uint64_t* words = args.acc + ((size_t)W.rg_begin + (size_t)tile) * (32 * kPxMaxTokens);
-      if (jl < M && 32 * tile < W.m) {
-        // four rows at a time (the adds' returned words are needed at once)
 #pragma unroll
-        for (int v0 = 0; v0 < 16; v0 += 4) {
-          uint64_t share[4], old[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = v0 + e, m = 8 * (v >> 2) + 4 * h + (v & 3);
-            share[e] = acc_share(KA == 2 ? acc[r][0][v] + acc[r][KA - 1][v] : acc[r][0][v]);
-            old[e] = 0;
-            if (32 * tile + m < W.m)
-              old[e] = __hip_atomic_fetch_add(&words[jl * 32 + m], share[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int v = v0 + e, m = 8 * (v >> 2) + 4 * h + (v & 3);
-            const int row = 32 * tile + m;
-            const uint64_t now = old[e] + share[e];
-            if (row < W.m && acc_count(now) == parts) {
-              store_y(W.y, (size_t)jl * W.m + row, acc_value(now), args.y_fp32);
-              __hip_atomic_store(&words[jl * 32 + m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-          }
-        }
-      }
+      for (int v = 0; v < 16; ++v)
+        slot[((wave * R + r) * 16 + v) * 64 + lane] = KA == 2 ? acc[r][0][v] + acc[r][KA - 1][v] : acc[r][0][v];
 #pragma unroll
       for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
     }
@@ -2501,6 +2462,46 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
   }
 #undef BSL_PX_PLANE
 }
+
+// Finishing pass of a product-index launch: y[t][row] is the sum, in workgroup order,
+// of the shares of the workgroups whose (non-empty) unit ranges hold units of the row's
+// row group (zero for a weight without blocks).  The product kernel precedes this kernel
+// in the stream, so its stores are complete.
+template <int R, int NB>
+__global__ __launch_bounds__(256) void product_finish_kernel(GroupArgs args) {
+  const int M = args.M;
+  const uint32_t U = args.total_units;
+  const int lg = args.grid_log2;
+  const uint32_t NWK = 1u << lg;
+  auto owner = [&](uint32_t u) {  // the workgroup o with range_start(o) <= u < range_start(o + 1)
+    uint32_t o = (uint32_t)(((uint64_t)u << lg) / U);
+    while (o + 1 < NWK && range_start(o + 1, U, lg) <= u) ++o;
+    while (range_start(o, U, lg) > u) --o;
+    return o;
+  };
+  constexpr int GROUP_ROWS = kPxWaves * R * 32;
+  for (int j = 0; j < args.count; ++j) {
+    const WeightDesc& W = args.w[j];
+    const uint64_t n = (uint64_t)W.m * (uint64_t)M;
+    const uint32_t per_rg = (uint32_t)(((W.nblocks + NB - 1) / NB) * W.nch);  // units of a row group
+    for (uint64_t e = (uint64_t)blockIdx.x * 256u + threadIdx.x; e < n; e += (uint64_t)gridDim.x * 256u) {
+      const int t = (int)(e / (uint64_t)W.m), row = (int)(e - (uint64_t)t * W.m);
+      float sum = 0.f;
+      if (per_rg > 0) {
+        const int rg = row / GROUP_ROWS, wr = row % GROUP_ROWS;
+        const int wave = wr >> 6, r = (wr >> 5) & (R - 1), mm = wr & 31;  // (R = 2)
+        const int v = ((mm >> 3) << 2) | (mm & 3), lane = 32 * ((mm >> 2) & 1) + t;
+        const uint32_t first = W.unit_begin + (uint32_t)rg * per_rg;
+        const size_t at = ((size_t)(wave * R + r) * 16 + v) * 64 + lane;
+        for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
+          if (range_start(o, U, lg) < range_start(o + 1, U, lg))
+            sum += args.part[((size_t)W.rg_begin + rg + o) * kPxPartFloats + at];
+      }
+      store_y(W.y, (size_t)e, sum, args.y_fp32);  // y[t][row]
+    }
+  }
+}
+static_assert(kPxTiles == 2, "product_finish_kernel indexes two tiles per wave");
 
 // ============================================================ debug unpack
 // One wave per sign tile: unpack exactly as the forward kernels do and write the signs.
@@ -2690,6 +2691,14 @@ int launch_tile(const GroupArgs& args, int token_tiles, int token_groups, void* 
 int launch_product(const GroupArgs& args, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL((product_kernel<kPxTiles, kPxBatch>), dim3(1u << args.grid_log2), dim3(kPxWaves * 64), 0, st, args);
+  return (int)hipGetLastError();
+}
+
+int launch_product_finish(const GroupArgs& args, void* stream) {
+  uint64_t n = 0;
+  for (int j = 0; j < args.count; ++j) n += (uint64_t)args.w[j].m * (uint64_t)args.M;
+  const unsigned blocks = (unsigned)std::min<uint64_t>(1024, std::max<uint64_t>(1, (n + 255) / 256));
+  hipLaunchKernelGGL((product_finish_kernel<kPxTiles, kPxBatch>), dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }
 

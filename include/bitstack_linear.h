@@ -176,12 +176,13 @@ int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int3
 /* Several weights in one call (count <= 8, distinct weights): weights[j] reads x[j] and
  * writes y[j] exactly as bsl_forward would.  All share M and y_is_fp32.  The group runs
  * as one kernel launch, except
- *   - on the tile path (BSL_PATH_TILE, and BSL_PATH_AUTO from M = 17 on), which first
+ *   - on the tile path (BSL_PATH_TILE, and BSL_PATH_AUTO from M = 33 on), which first
  *     runs a short pass that puts the V of the group's loaded blocks in rank-major order
  *     in the stack's workspace, then the tile kernel;
  *   - on the product-index path (BSL_PATH_PRODUCT at M = 2..32, BSL_PATH_AUTO at
- *     M = 5..16): the same V pass, a pass that writes x as the kernel's B operands, then
- *     the product-index kernel;
+ *     M = 5..32): one launch of the same V pass and of a pass that writes x as the
+ *     kernel's B operands, the product-index kernel, then a pass that adds the
+ *     workgroups' shares of every row group in a fixed order into y;
  *   - on BSL_PATH_AUTO at M = 2..4 when the group's activations do not fit the few-token
  *     kernel as a whole: then it is split into two forward launches (see bsl_set_path).
  *     An error returned after the first of the two was enqueued leaves the y[j] of the
@@ -226,15 +227,17 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
  *     the value operand of the 2:4 sparse MFMA, and the stored sign bits are its indices
  *     against B = +x / -x, so no sign is expanded; blocks and columns sum in fp32.  Work
  *     grows as (k + 32) * n * m * d whatever the token count up to 32.  A call first runs
- *     two short passes (V in rank-major order, x as the MFMA's B operands) into the
- *     stack's workspaces.  M > 32: BSL_EUNSUPPORTED.
+ *     two short passes in one launch (V in rank-major order, x as the MFMA's B operands)
+ *     into the stack's workspaces; after the kernel a third adds the workgroups' fp32
+ *     shares of each row group in workgroup order (deterministic: the same launch gives
+ *     the same bits).  M > 32: BSL_EUNSUPPORTED.
  *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 to 4 on the
  *     wave-private kernel of BSL_DECODE_PRIVATE taking the M tokens at once, which share
  *     every sign, U and V operand and load, when their activations fit its LDS (148 KiB
  *     per workgroup); in a grouped call that does not fit as a whole, the weights whose
  *     activations take at most half of it go to that kernel and the others to the
- *     factored multi-token kernel, in a second launch; PRODUCT for M = 5 to 16; TILE
- *     from M = 17 on. */
+ *     factored multi-token kernel, in a second launch; PRODUCT for M = 5 to 32; TILE
+ *     from M = 33 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2

@@ -3,8 +3,8 @@
 A forward only enqueues kernels (no allocation, no synchronisation, no memset: the
 allocation-free entry point clears its accumulators with a kernel, and the row
 accumulators of the other entry points clear themselves), so a caller may capture it.
-The graph below holds single- and few-token forwards through both entry points and a
-tile-path forward; it is replayed several times with ordinary forwards and
+The graph below holds single- and few-token forwards through both entry points, a
+product-index forward and a tile-path forward; it is replayed several times with ordinary forwards and
 synchronisations between the replays, and every replay must give the eager results bit
 for bit (the launches are deterministic).
 """
@@ -41,7 +41,8 @@ def test_graph_replay_matches_eager():
         (bsl.bsl_forward_group_static, 1),
         (bsl.bsl_forward_group, 3),
         (bsl.bsl_forward_group_static, 4),
-        (bsl.bsl_forward_group, 24),  # tile path: the rank-major V pass, then the tile kernel
+        (bsl.bsl_forward_group, 12),  # product-index path: the layout passes, then the product kernel
+        (bsl.bsl_forward_group, 40),  # tile path: the rank-major V pass, then the tile kernel
     ]
     with Stack(weights) as st:
         st.load([n] * len(SHAPES))

@@ -160,7 +160,7 @@ def test_tile_rank_major_v_workspace():
     weights = [(256, d, synth.synthetic_blocks(40 + j, 256, d, n, 16, 0, j)) for j, (d, n) in enumerate(zip(ds, ns))]
     vbytes = [n * d * 32 for d, n in zip(ds, ns)]  # (d is a multiple of 512: no column padding)
     top = sorted(range(len(ds)), key=lambda j: -vbytes[j])[:8]
-    with Stack(weights) as st:
+    with Stack(weights, path=bsl.BSL_PATH_TILE) as st:
         before = bsl.bsl_workspace_bytes(st.h)
         st.load(ns)
         grown = bsl.bsl_workspace_bytes(st.h) - before

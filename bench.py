@@ -138,12 +138,24 @@ class Layers:
         self.bsl.bsl_destroy(self.h)
 
 
-def time_steps(torch, layers: Layers, steps: int, warmup: int):
+WARM_S = 0.2  # seconds of untimed launches before a non-headline section's timing
+
+
+def time_steps(torch, layers: Layers, steps: int, warmup: int, warm_s: float = 0.0):
     """Warm up, then time exactly `steps` steps (one grouped launch each) between two
     device synchronisations.  One HIP event pair on the launch stream brackets the same
-    steps, so the average launch duration carries no per-launch event overhead."""
+    steps, so the average launch duration carries no per-launch event overhead.  With
+    `warm_s`, the same launches first run for that many seconds (the sections other than
+    the headline: each builds its layers on the host first, and launches that follow an
+    idle GPU run slower while its clock ramps up)."""
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
+    t_end, s = time.perf_counter() + warm_s, 0
+    while time.perf_counter() < t_end:
+        layers.launch(s % layers.layers, sp)
+        s += 1
+        if s % 16 == 0:
+            torch.cuda.synchronize()
     for s in range(warmup):
         layers.launch(s % layers.layers, sp)
     torch.cuda.synchronize()
@@ -716,7 +728,7 @@ def main() -> None:
     # ---------------- 1024 x 1024, n = 4, M = 1 (the parity workload's shape; launch-bound)
     if not args.profile_set:
         c1 = Layers(bsl, torch, [("w", 1024, 1024)], [[4]] * 64, 64, args.seed + 71, M=1)
-        w1, k1, b1, _ = time_steps(torch, c1, 640, 64)
+        w1, k1, b1, _ = time_steps(torch, c1, 640, 64, warm_s=WARM_S)
         result["single_1024x1024_n4_decode"] = {
             "workload": "one 1024x1024 linear, n=4 blocks (k=16), M=1, 64 resident copies rotated; blocks synthetic of "
                         "the decomposed shape (the CPU decomposition is not on the timed path)",
@@ -737,7 +749,7 @@ def main() -> None:
                 for name, path in (("auto", bsl.BSL_PATH_AUTO), ("factored", bsl.BSL_PATH_FACTORED)):
                     log(f"few tokens: {label}-shaped layer, n={counts[0]}, M={M}, {name} path")
                     lay = Layers(bsl, torch, lshapes, [counts] * 2, 2, args.seed + 5, M=M, path=path, shared_sources=True)
-                    w_, k_, b_, f_ = time_steps(torch, lay, 60, 6)
+                    w_, k_, b_, f_ = time_steps(torch, lay, 60, 6, warm_s=WARM_S)
                     row[f"{name}_us_per_step"] = round(w_ * 1e6 / 60, 1)
                     row[f"{name}_kernel_us"] = round(float(np.mean(k_)) * 1e3, 1)
                     if name == "auto":
@@ -771,7 +783,7 @@ def main() -> None:
                 paths.append(("few_token", bsl.BSL_PATH_AUTO))
             for name, path in paths:
                 bsl.bsl_set_path(lay.h, path)
-                w_, k_, _, _ = time_steps(torch, lay, 40, 5)
+                w_, k_, _, _ = time_steps(torch, lay, 40, 5, warm_s=WARM_S)
                 row[f"{name}_us"] = round(float(np.mean(k_)) * 1e3, 1)
             kus = row["product_us"] * 1e-6
             row["auto_takes"] = "product" if 5 <= M <= 32 else ("few_token" if M <= 4 else "tile")
@@ -795,7 +807,7 @@ def main() -> None:
     if not args.no_prefill:
         log("prefill: one 8B-shaped layer, n=8, M=2048, tile path")
         pre = Layers(bsl, torch, shapes, [[8] * 7], 1, args.seed + 7, M=2048, path=bsl.BSL_PATH_TILE)
-        wall_t, kms_t, _, _ = time_steps(torch, pre, args.tile_steps, 2)
+        wall_t, kms_t, _, _ = time_steps(torch, pre, args.tile_steps, 2, warm_s=WARM_S)
         t_step = wall_t / args.tile_steps
         tfl_t = pre.tile_flops(0) / t_step / 1e12
         k_step = float(np.mean(kms_t)) * 1e-3
@@ -852,7 +864,7 @@ def main() -> None:
         for M in (1, 4, 16):
             lay = Layers(bsl, torch, shapes, [counts] * 2, 2, args.seed + 11, M=M, shared_sources=True)
             steps = 100 if M < 16 else 50
-            w_, k_, b_, f_ = time_steps(torch, lay, steps, 5)
+            w_, k_, b_, f_ = time_steps(torch, lay, steps, 5, warm_s=WARM_S)
             kus = float(np.mean(k_)) * 1e-3
             row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
                    "path": "single-token (decode_m1_kernel)" if M == 1 else ("product-index (product_kernel)" if M >= 5 else "few-token (decode_wp_kernel<8, 4>)"),
@@ -867,7 +879,7 @@ def main() -> None:
                                    "flops": "executed MFMA work of the path: " + ("(2 k + 2 * 32) n m d (tokens padded to 32)" if M >= 5 else "2 n k M m d")}
                 if M >= 5:  # the tile path on the same stack, for comparison
                     bsl.bsl_set_path(lay.h, bsl.BSL_PATH_TILE)
-                    _, kt_, _, _ = time_steps(torch, lay, steps, 5)
+                    _, kt_, _, _ = time_steps(torch, lay, steps, 5, warm_s=WARM_S)
                     bsl.bsl_set_path(lay.h, bsl.BSL_PATH_AUTO)
                     row["tile_path_us_per_step"] = round(float(np.mean(kt_)) * 1e3, 1)
             sweep.append(row)
@@ -885,7 +897,7 @@ def main() -> None:
         lay = Layers(bsl, torch, synth.LLAMA2_70B_LAYER, counts, synth.LLAMA2_70B_LAYERS, args.seed + 21, M=1,
                      shared_sources=True, batch=8)
         tokens = 3
-        w_, k_, b_, f_ = time_steps(torch, lay, synth.LLAMA2_70B_LAYERS * tokens, synth.LLAMA2_70B_LAYERS)
+        w_, k_, b_, f_ = time_steps(torch, lay, synth.LLAMA2_70B_LAYERS * tokens, synth.LLAMA2_70B_LAYERS, warm_s=WARM_S)
         tok_us = float(np.mean(k_)) * 1e-3 * synth.LLAMA2_70B_LAYERS
         per_token = sum(lay.bytes(l) for l in range(synth.LLAMA2_70B_LAYERS))
         nsum = sum(int(c) for cc in counts for c in cc)

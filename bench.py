@@ -562,8 +562,9 @@ def main() -> None:
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM / matrix-core peaks")
     ap.add_argument("--no-load", action="store_true", help="skip host -> device block streaming")
     ap.add_argument("--profile-set", action="store_true",
-                    help="only the kernels the committed profiles cover: the decode headline, the few-token kernel at "
-                         "M = 4 and the tile-path prefill, plus a 1 GiB copy for counter calibration")
+                    help="only the kernels the committed profiles cover: the decode headline (after the measured "
+                         "peaks, as in the full run), the few-token kernel at M = 4, the product-index kernel at "
+                         "M = 16 and the tile-path prefill, plus a 1 GiB copy for counter calibration")
     ap.add_argument("--per-weight", action="store_true", help="also time single-weight launches of each linear")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--cpu-layers", type=int, default=4)
@@ -575,7 +576,7 @@ def main() -> None:
                     help="with --write-profile-summaries: rocprofv3 output of the vector-memory-path counter pass")
     args = ap.parse_args()
     if args.profile_set:
-        args.no_cpu = args.no_svd = args.no_sweep = args.no_70b = args.no_load = args.no_peaks = True
+        args.no_cpu = args.no_svd = args.no_sweep = args.no_70b = args.no_load = True
         args.calibrate_copy = True
     if args.write_profile_summaries:
         write_profile_summaries(*args.write_profile_summaries, mem_dir=args.mem_dir)
@@ -745,14 +746,18 @@ def main() -> None:
         sets = (("8B", shapes, [8] * 7), ("70B", synth.LLAMA2_70B_LAYER, [3] * 7))
         for label, lshapes, counts in (sets[:1] if args.profile_set else sets):
             for M in ((4,) if args.profile_set else (2, 3, 4)):
-                row = {"layer": label, "n": counts[0], "M": M}
-                for name, path in (("auto", bsl.BSL_PATH_AUTO), ("factored", bsl.BSL_PATH_FACTORED)):
+                row = {"layer": label, "n": counts[0], "M": M,
+                       "auto_takes": "few-token" if M < 4 else "product-index (product_kernel<2, 2>)"}
+                paths = [("few_token", bsl.BSL_PATH_DECODE), ("factored", bsl.BSL_PATH_FACTORED)]
+                if M == 4 and not args.profile_set:
+                    paths.append(("auto", bsl.BSL_PATH_AUTO))
+                for name, path in paths:
                     log(f"few tokens: {label}-shaped layer, n={counts[0]}, M={M}, {name} path")
                     lay = Layers(bsl, torch, lshapes, [counts] * 2, 2, args.seed + 5, M=M, path=path, shared_sources=True)
                     w_, k_, b_, f_ = time_steps(torch, lay, 60, 6, warm_s=WARM_S)
                     row[f"{name}_us_per_step"] = round(w_ * 1e6 / 60, 1)
                     row[f"{name}_kernel_us"] = round(float(np.mean(k_)) * 1e3, 1)
-                    if name == "auto":
+                    if name == "few_token":
                         kus = float(np.mean(k_)) * 1e-3
                         row["sz_flops_per_step"] = int(f_ // 60)
                         row["mfma_tflops"] = round(f_ / 60 / kus / 1e12, 1)
@@ -762,12 +767,14 @@ def main() -> None:
                     del lay
                     torch.cuda.empty_cache()
                 row["kernel"] = kern[M] + ("" if label == "8B" or M == 2 else " (down projection: prefill_kernel, second launch)")
-                row["speedup_vs_factored"] = round(row["factored_kernel_us"] / row["auto_kernel_us"], 2)
+                row["speedup_vs_factored"] = round(row["factored_kernel_us"] / row["few_token_kernel_us"], 2)
                 few.append(row)
                 log(f"few tokens: {row}")
         result["few_token_decode"] = {
             "workload": "decoder-layer linears (Llama-3-8B shapes at n=8; Llama-2-70B shapes at n=3), k=16, M tokens per "
-                        "grouped launch, 2 rotated layers; MFMA work = the S Z contraction 2 n k M m d",
+                        "grouped launch, 2 rotated layers; the few-token kernel (BSL_PATH_DECODE) against the factored "
+                        "path, and at M = 4 the product-index path AUTO takes there; MFMA work = the S Z contraction "
+                        "2 n k M m d",
             "runs": few}
 
     # ---------------- 4 to 32 tokens: the product-index kernel against the tile kernel (and the
@@ -780,13 +787,13 @@ def main() -> None:
             row = {"M": M}
             paths = [("product", bsl.BSL_PATH_PRODUCT), ("tile", bsl.BSL_PATH_TILE)]
             if M == 4:
-                paths.append(("few_token", bsl.BSL_PATH_AUTO))
+                paths.append(("few_token", bsl.BSL_PATH_DECODE))
             for name, path in paths:
                 bsl.bsl_set_path(lay.h, path)
                 w_, k_, _, _ = time_steps(torch, lay, 40, 5, warm_s=WARM_S)
                 row[f"{name}_us"] = round(float(np.mean(k_)) * 1e3, 1)
             kus = row["product_us"] * 1e-6
-            row["auto_takes"] = "product" if 5 <= M <= 32 else ("few_token" if M <= 4 else "tile")
+            row["auto_takes"] = "product" if 4 <= M <= 32 else ("few_token" if M <= 3 else "tile")
             row["product_roofline"] = {"bound": "mfma", "achieved": round(lay.product_flops(0) / kus / 1e12, 1),
                                        "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                        "frac": round(lay.product_flops(0) / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
@@ -867,21 +874,23 @@ def main() -> None:
             w_, k_, b_, f_ = time_steps(torch, lay, steps, 5, warm_s=WARM_S)
             kus = float(np.mean(k_)) * 1e-3
             row = {"M": M, "n_w": [int(c) for c in counts], "us_per_step": round(kus * 1e6, 1),
-                   "path": "single-token (decode_m1_kernel)" if M == 1 else ("product-index (product_kernel)" if M >= 5 else "few-token (decode_wp_kernel<8, 4>)"),
+                   "path": "single-token (decode_m1_kernel)" if M == 1 else "product-index (product_kernel)",
                    "bytes_per_step": lay.bytes(0), "GB_per_s": round(lay.bytes(0) / kus / 1e9, 1)}
             if M == 1:
                 row["roofline"] = {"bound": "hbm", "achieved": row["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(row["GB_per_s"] / HBM_PEAK_GBS, 4)}
             else:
-                fl = lay.product_flops(0) if M >= 5 else lay.flops(0)
+                fl = lay.product_flops(0)
                 row["roofline"] = {"bound": "mfma", "achieved": round(fl / kus / 1e12, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(fl / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4),
-                                   "flops": "executed MFMA work of the path: " + ("(2 k + 2 * 32) n m d (tokens padded to 32)" if M >= 5 else "2 n k M m d")}
-                if M >= 5:  # the tile path on the same stack, for comparison
-                    bsl.bsl_set_path(lay.h, bsl.BSL_PATH_TILE)
-                    _, kt_, _, _ = time_steps(torch, lay, steps, 5, warm_s=WARM_S)
-                    bsl.bsl_set_path(lay.h, bsl.BSL_PATH_AUTO)
-                    row["tile_path_us_per_step"] = round(float(np.mean(kt_)) * 1e3, 1)
+                                   "flops": "executed MFMA work of the path: (2 k + 2 * 32) n m d (tokens padded to 32)"}
+                row["sz_work_frac"] = round(lay.flops(0) / kus / 1e12 / FP16_MFMA_PEAK_TFLOPS, 4)
+                # on the same stack, for comparison: the few-token kernel at 4 tokens, the tile path at 16
+                name, path = ("few_token", bsl.BSL_PATH_DECODE) if M == 4 else ("tile_path", bsl.BSL_PATH_TILE)
+                bsl.bsl_set_path(lay.h, path)
+                _, kt_, _, _ = time_steps(torch, lay, steps, 5, warm_s=WARM_S)
+                bsl.bsl_set_path(lay.h, bsl.BSL_PATH_AUTO)
+                row[f"{name}_us_per_step"] = round(float(np.mean(kt_)) * 1e3, 1)
             sweep.append(row)
             lay.close()
             del lay

@@ -25,6 +25,7 @@ BSL_PATH_AUTO = 0
 BSL_PATH_FACTORED = 1
 BSL_PATH_TILE = 2
 BSL_PATH_PRODUCT = 3
+BSL_PATH_DECODE = 4
 BSL_DECODE_AUTO = 0
 BSL_DECODE_SHARED = 1
 BSL_DECODE_PRIVATE = 2

@@ -957,14 +957,17 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
   if (M < 1 || M > (1 << 24)) return fail(BSL_EINVAL, "forward: M must be >= 1");
   if (use_static && M > kWpMaxTokens)
     return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: takes 1 to 4 tokens (the single- and few-token kernels)");
+  if (s->path == BSL_PATH_DECODE && M > kWpMaxTokens)
+    return fail(BSL_EUNSUPPORTED, "forward: BSL_PATH_DECODE takes 1 to 4 tokens (the single- and few-token kernels)");
   GroupArgs args;
   std::memset(&args, 0, sizeof(args));
   args.count = count;
   args.M = M;
   args.y_fp32 = y_is_fp32 ? 1 : 0;
-  // BSL_PATH_AUTO: 5 to 32 tokens on the product-index kernel (measured faster there than
+  // BSL_PATH_AUTO: 4 to 32 tokens on the product-index kernel (measured faster there than
   // the tile kernel, whose sign application is VALU work per element and block, and than
-  // the few-token kernel, whose matrix work grows with every token)
+  // the few-token kernel, whose matrix work grows with every token; at 2 and 3 tokens the
+  // few-token kernel is the faster)
   const bool product = !use_static && M >= 2 &&
                        (s->path == BSL_PATH_PRODUCT ||
                         (s->path == BSL_PATH_AUTO && M >= kPxAutoMinTokens && M < kTileAutoMinTokens));
@@ -1111,7 +1114,7 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     ++s->launches[wp ? 1 : 0];
     return BSL_OK;
   }
-  if (M <= kWpMaxTokens && (s->path == BSL_PATH_AUTO || use_static)) {
+  if (M <= kWpMaxTokens && (s->path == BSL_PATH_AUTO || s->path == BSL_PATH_DECODE || use_static)) {
     // a few tokens: the wave-private kernel with every operand but the activations shared
     // by the tokens, when they fit its LDS
     const int T = M;
@@ -1210,7 +1213,8 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
 
 int bsl_set_path(bsl_stack* s, int32_t path) {
   if (!s) return fail(BSL_EINVAL, "bsl_set_path: null stack");
-  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE && path != BSL_PATH_PRODUCT)
+  if (path != BSL_PATH_AUTO && path != BSL_PATH_FACTORED && path != BSL_PATH_TILE && path != BSL_PATH_PRODUCT &&
+      path != BSL_PATH_DECODE)
     return fail(BSL_EINVAL, "bsl_set_path: unknown path");
   s->path = path;
   return BSL_OK;

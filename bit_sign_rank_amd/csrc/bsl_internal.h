@@ -142,7 +142,7 @@ constexpr int kTileGroupRows = 64;
 constexpr int kTileMaxTokenTiles = 8;   // 32-token tiles per wave
 constexpr int kTileBatch = 8;           // blocks whose U fragments and sign words stay in registers
 constexpr int kTileAutoMinTokens = 33;  // BSL_PATH_AUTO takes the tile path from this M on
-constexpr int kPxAutoMinTokens = 5;     // and the product-index path from this M to kTileAutoMinTokens - 1
+constexpr int kPxAutoMinTokens = 4;     // and the product-index path from this M to kTileAutoMinTokens - 1
 // Product-index path (M = 2..32 under BSL_PATH_PRODUCT): one worker per workgroup of
 // kPxWaves waves (two per SIMD, one workgroup per CU); units (weight, row group of
 // kPxWaves x kPxTiles 32-row tiles, batch of kPxBatch blocks, 512-column chunk), each wave

@@ -180,11 +180,12 @@ int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int3
  *     runs a short pass that puts the V of the group's loaded blocks in rank-major order
  *     in the stack's workspace, then the tile kernel;
  *   - on the product-index path (BSL_PATH_PRODUCT at M = 2..32, BSL_PATH_AUTO at
- *     M = 5..32): one launch of the same V pass and of a pass that writes x as the
+ *     M = 4..32): one launch of the same V pass and of a pass that writes x as the
  *     kernel's B operands, the product-index kernel, then a pass that adds the
  *     workgroups' shares of every row group in a fixed order into y;
- *   - on BSL_PATH_AUTO at M = 2..4 when the group's activations do not fit the few-token
- *     kernel as a whole: then it is split into two forward launches (see bsl_set_path).
+ *   - on BSL_PATH_AUTO at M = 2..3 and BSL_PATH_DECODE at M = 2..4 when the group's
+ *     activations do not fit the few-token kernel as a whole: then it is split into two
+ *     forward launches (see bsl_set_path).
  *     An error returned after the first of the two was enqueued leaves the y[j] of the
  *     weights in that launch written and the others unspecified. */
 int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
@@ -193,7 +194,8 @@ int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const
 /* Allocation-free variant of bsl_forward_group, for callers that cannot allocate device
  * memory or must not let a call allocate: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  Same arguments, same results as
- * bsl_forward_group for 1 <= M <= 4 (the same kernels in the same launch configuration),
+ * bsl_forward_group under BSL_PATH_DECODE for 1 <= M <= 4 (the same kernels in the same
+ * launch configuration),
  * with the kernels' row accumulators (one 64-bit word per output row and token) in a
  * scratch array of 8 MiB that the library holds on each device it runs on until the
  * process ends (its address is taken by bsl_init).  The call allocates nothing, on the
@@ -231,17 +233,20 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
  *     into the stack's workspaces; after the kernel a third adds the workgroups' fp32
  *     shares of each row group in workgroup order (deterministic: the same launch gives
  *     the same bits).  M > 32: BSL_EUNSUPPORTED.
- *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 to 4 on the
- *     wave-private kernel of BSL_DECODE_PRIVATE taking the M tokens at once, which share
- *     every sign, U and V operand and load, when their activations fit its LDS (148 KiB
- *     per workgroup); in a grouped call that does not fit as a whole, the weights whose
- *     activations take at most half of it go to that kernel and the others to the
- *     factored multi-token kernel, in a second launch; PRODUCT for M = 5 to 32; TILE
- *     from M = 33 on. */
+ *   BSL_PATH_DECODE (1 to 4 tokens; M > 4: BSL_EUNSUPPORTED): M = 1 as under FACTORED;
+ *     M = 2 to 4 on the wave-private kernel of BSL_DECODE_PRIVATE taking the M tokens at
+ *     once, which share every sign, U and V operand and load, when their activations fit
+ *     its LDS (148 KiB per workgroup); in a grouped call that does not fit as a whole, the
+ *     weights whose activations take at most half of it go to that kernel and the others
+ *     to the factored multi-token kernel, in a second launch.
+ *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 and 3 as under DECODE;
+ *     PRODUCT for M = 4 to 32; TILE from M = 33 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2
 #define BSL_PATH_PRODUCT 3
+#define BSL_PATH_DECODE 4
+/* Errors: BSL_EINVAL for a null stack or a value other than the five above. */
 int bsl_set_path(bsl_stack* s, int32_t path);
 
 /* Kernel of the single-token forward (M = 1; bsl_set_decode).  Both compute the same

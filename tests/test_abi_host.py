@@ -43,6 +43,16 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(bsl.EXPORTED)
 
 
+def test_binding_constants_match_the_header():
+    defines = {}
+    for path in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        for name, value in re.findall(r"^#define (BSL_[A-Z0-9_]+) \(?(-?\d+)\)?", open(path).read(), flags=re.M):
+            defines[name] = int(value)
+    assert {"BSL_PATH_AUTO", "BSL_PATH_DECODE", "BSL_PATH_PRODUCT", "BSL_KERNEL_KINDS"} <= set(defines)
+    for name, value in defines.items():
+        assert getattr(bsl, name) == value, name
+
+
 @pytest.mark.parametrize("m,d", [(14336, 4096), (4096, 14336), (1024, 1024), (8, 8), (11008, 4096)])
 def test_block_bytes(m, d):
     assert bsl.bsl_block_bytes(m, d, 16) == oracle.block_bytes(m, d, 16)

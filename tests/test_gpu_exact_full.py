@@ -28,6 +28,7 @@ import bit_sign_rank_amd as bsl  # noqa: E402
 from gpu_util import REL_TOL, Stack, abs_bound, elem_factor, rel_err  # noqa: E402
 
 AUTO, FACT, TILE, PROD = bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED, bsl.BSL_PATH_TILE, bsl.BSL_PATH_PRODUCT
+DEC = bsl.BSL_PATH_DECODE
 SHARED, PRIVATE = bsl.BSL_DECODE_SHARED, bsl.BSL_DECODE_PRIVATE
 MAX_TOKENS = 2048
 
@@ -60,7 +61,7 @@ RUNS = [
     (1, AUTO, PRIVATE, "decode private"),
     (2, AUTO, None, "few-token"),
     (3, AUTO, None, "few-token"),
-    (4, AUTO, None, "few-token"),
+    (4, DEC, None, "few-token"),
     (2, FACT, None, "factored"),
     (3, FACT, None, "factored"),
     (4, FACT, None, "factored"),
@@ -68,7 +69,7 @@ RUNS = [
     (16, FACT, None, "factored"),
     (16, TILE, None, "tile"),
     (2, PROD, None, "product-index"),
-    (4, PROD, None, "product-index"),
+    (4, AUTO, None, "product-index"),
     (16, PROD, None, "product-index"),
     (32, PROD, None, "product-index"),
     (100, AUTO, None, "tile"),
@@ -120,8 +121,8 @@ def test_dyadic_8b_variable_block_counts_bit_exact():
     refs = [oracle.forward(x, b, int(n)) for (_, _, b), x, n in zip(weights, xs, counts)]
     with Stack(weights) as st:
         st.load([int(n) for n in counts])
-        for M, path, decode in ((1, AUTO, SHARED), (1, AUTO, PRIVATE), (4, AUTO, None), (4, FACT, None),
-                                (16, AUTO, None), (16, FACT, None), (4, PROD, None), (16, PROD, None)):
+        for M, path, decode in ((1, AUTO, SHARED), (1, AUTO, PRIVATE), (4, DEC, None), (4, FACT, None),
+                                (16, AUTO, None), (16, FACT, None), (4, AUTO, None), (16, PROD, None)):
             ys = run(st, range(7), xs, M, path, decode)
             for j, (y, ref) in enumerate(zip(ys, refs)):
                 assert_exact(y, ref[:M], f"8B variable counts {counts.tolist()}, {shapes[j][0]}, M={M}, path={path}, decode={decode}")
@@ -149,8 +150,8 @@ def test_dyadic_70b_weight_every_path_bit_exact(j):
     with Stack([(m, d, blocks)]) as st:
         st.load([n])
         for M, path, decode in ((1, AUTO, SHARED), (1, AUTO, PRIVATE), (2, AUTO, None), (3, AUTO, None),
-                                (4, AUTO, None), (4, FACT, None), (16, AUTO, None), (16, FACT, None),
-                                (16, PROD, None), (MAX_TOKENS, AUTO, None)):
+                                (4, DEC, None), (4, AUTO, None), (4, FACT, None), (16, AUTO, None),
+                                (16, FACT, None), (16, PROD, None), (MAX_TOKENS, AUTO, None)):
             (y,) = run(st, [0], [x], M, path, decode)
             assert_exact(y, ref[:M], f"70B {synth.LLAMA2_70B_LAYER[j][0]} (n={n}), M={M}, path={path}, decode={decode}")
 
@@ -184,7 +185,7 @@ def float_8b():
     st.close()
 
 
-FLOAT_RUNS = [(1, AUTO, SHARED, "z16"), (1, AUTO, PRIVATE, "exact"), (4, AUTO, None, "exact"),
+FLOAT_RUNS = [(1, AUTO, SHARED, "z16"), (1, AUTO, PRIVATE, "exact"), (4, DEC, None, "exact"),
               (4, FACT, None, "z16"), (16, AUTO, None, "product"), (16, TILE, None, "tile"), (16, FACT, None, "z16"),
               (4, PROD, None, "product"), (16, PROD, None, "product")]
 

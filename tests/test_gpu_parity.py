@@ -409,16 +409,16 @@ def test_private_decode_fits_the_layer_shapes(layer):
 
 
 # ---------------------------------------------------------------- a few tokens (wave-private kernel)
-# Under BSL_PATH_AUTO, 2 to 4 tokens run on the wave-private kernel with every operand but
-# the activations shared by the tokens whenever the activations fit its LDS, else on the
-# factored multi-token kernel.
+# Under BSL_PATH_DECODE (and BSL_PATH_AUTO at 2 and 3 tokens), 2 to 4 tokens run on the
+# wave-private kernel with every operand but the activations shared by the tokens whenever
+# the activations fit its LDS, else on the factored multi-token kernel.
 @pytest.mark.parametrize("m,d,n", [(64, 1024, 3), (37, 520, 2), (200, 2560, 4), (1024, 4096, 16), (16, 8, 1),
                                    (3000, 1544, 5)])
 @pytest.mark.parametrize("M", [2, 3, 4])
 def test_integer_few_tokens_bit_exact(m, d, n, M):
     blocks = integer_blocks(m, d, n)
     x = synth.integer_activations(4, M, d)
-    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_AUTO) as st:
+    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_DECODE) as st:
         st.load([n])
         y = st.forward(0, x)
     assert np.array_equal(y, oracle.forward(x, blocks, n))
@@ -430,7 +430,7 @@ def test_few_tokens_grouped_with_empty_weights_between(M):
     counts = [0, 3, 0, 2, 0]
     ws = [(m, d, synth.synthetic_blocks(45, m, d, 3, 16, j)) for j, (m, d) in enumerate(shapes)]
     xs = [synth.activations(45, M, d, j) for j, (_, d) in enumerate(shapes)]
-    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
         st.load(counts)
         for fp32 in (True, False):
             ys = st.forward_group(list(range(len(shapes))), xs, fp32=fp32)
@@ -445,7 +445,7 @@ def test_few_tokens_grouped_with_empty_weights_between(M):
 def test_few_tokens_agree_with_the_factored_kernel(cfg1_blocks, M):
     x = synth.activations(46, M, 1024)
     outs = []
-    for path in (bsl.BSL_PATH_AUTO, bsl.BSL_PATH_FACTORED):
+    for path in (bsl.BSL_PATH_DECODE, bsl.BSL_PATH_FACTORED):
         with Stack([(1024, 1024, cfg1_blocks)], path=path) as st:
             st.load([4])
             outs.append(st.forward(0, x))
@@ -467,7 +467,7 @@ def test_few_tokens_wide_input_falls_back(M):
     m, d, n = 96, 20480, 2
     blocks = integer_blocks(m, d, n)
     x = synth.integer_activations(5, M, d)
-    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_AUTO) as st:
+    with Stack([(m, d, blocks)], path=bsl.BSL_PATH_DECODE) as st:
         st.load([n])
         y = st.forward(0, x)
     assert np.array_equal(y, oracle.forward(x, blocks, n))
@@ -489,7 +489,7 @@ def _counts(st):
 def test_few_tokens_grouped_split_bit_exact(M):
     ws = [(m, d, integer_blocks(m, d, max(n, 1), 60 + j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
     xs = [synth.integer_activations(61, M, d, -1, 1, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
-    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
         st.load(SPLIT_COUNTS)
         before = _counts(st)
         ys = st.forward_group(list(range(5)), xs)
@@ -502,7 +502,7 @@ def test_few_tokens_grouped_split_bit_exact(M):
 def test_few_tokens_grouped_split_float_all_rows(M):
     ws = [(m, d, synth.synthetic_blocks(62, m, d, max(n, 1), 16, j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
     xs = [synth.activations(63, M, d, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
-    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
         st.load(SPLIT_COUNTS)
         ys = st.forward_group(list(range(5)), xs)
     for j, ((m, d, blocks), n) in enumerate(zip(ws, SPLIT_COUNTS)):
@@ -525,7 +525,7 @@ def test_few_tokens_narrow_subset_that_does_not_fit_falls_back():
     counts = [1, 0, 1, 16, 2]
     ws = [(m, d, integer_blocks(m, d, max(n, 1), 70 + j)) for j, ((m, d), n) in enumerate(zip(shapes, counts))]
     xs = [synth.integer_activations(71, 4, d, -1, 1, j) for j, (_, d) in enumerate(shapes)]
-    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
         st.load(counts)
         before = _counts(st)
         ys = st.forward_group(list(range(5)), xs)
@@ -541,7 +541,7 @@ def test_llama3_8b_layer_few_tokens_grouped(M):
     counts = [8] * 7
     weights = layer_blocks(shapes, counts, seed=47)
     xs = [synth.activations(47, M, d, j) for j, (_, _, d) in enumerate(shapes)]
-    with Stack(weights, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(weights, path=bsl.BSL_PATH_DECODE) as st:
         st.load(counts)
         ys = st.forward_group(list(range(7)), xs)
         check_sampled(weights, counts, ys, xs)
@@ -560,7 +560,7 @@ def test_llama2_70b_layer_few_tokens(M):
     counts = [2] * len(shapes)
     ws = [(m, d, synth.synthetic_blocks(48, m, d, 2, 16, j)) for j, (_, m, d) in enumerate(shapes)]
     xs = [synth.activations(48, M, d, j) for j, (_, _, d) in enumerate(shapes)]
-    with Stack(ws, path=bsl.BSL_PATH_AUTO) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
         st.load(counts)
         ys = st.forward_group(list(range(len(shapes))), xs)
     check_sampled(ws, counts, ys, xs, rows_per_weight=32, seed=48)
@@ -569,11 +569,15 @@ def test_llama2_70b_layer_few_tokens(M):
 # ---------------------------------------------------------------- input-channel scale
 @pytest.mark.parametrize("m,d,n", [(1024, 1536, 3), (37, 520, 2)])
 @pytest.mark.parametrize("M", [1, 3, 4, 40])
-@pytest.mark.parametrize("path,decode", [(p, None) for p in PATHS] + [(bsl.BSL_PATH_AUTO, bsl.BSL_DECODE_PRIVATE)],
-                         ids=PATH_IDS + ["auto-private"])
+@pytest.mark.parametrize("path,decode", [(p, None) for p in PATHS] + [(bsl.BSL_PATH_AUTO, bsl.BSL_DECODE_PRIVATE),
+                                                                       (bsl.BSL_PATH_DECODE, bsl.BSL_DECODE_PRIVATE)],
+                         ids=PATH_IDS + ["auto-private", "decode-private"])
 def test_input_scale_folded_at_load(m, d, n, M, path, decode):
-    # (auto-private: the wave-private kernel at M = 1 and the few-token kernel at M = 3, 4,
-    # both reading the B-operand copy of the scaled V)
+    # (auto-private: the wave-private kernel at M = 1, the few-token kernel at M = 3, the
+    # product-index kernel at M = 4; decode-private: the few-token kernel at M = 3 and 4,
+    # reading the B-operand copy of the scaled V)
+    if path == bsl.BSL_PATH_DECODE and M > 4:
+        pytest.skip("BSL_PATH_DECODE takes at most 4 tokens")
     blocks = synth.synthetic_blocks(23, m, d, n, 16, m, d)
     t = synth.inv_input_scale(23, d)
     x = synth.outlier_activations(23, M, d, synth.channel_magnitudes(23, d))
@@ -679,7 +683,7 @@ def test_errors_leave_state_unchanged(cfg1_blocks):
             bsl.bsl_load_blocks(st.h, [5], 0)  # only 4 source blocks
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
-            bsl.bsl_set_path(st.h, 4)  # no such formulation
+            bsl.bsl_set_path(st.h, 5)  # no such formulation
         assert e.value.code == bsl.BSL_EINVAL
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_set_decode(st.h, 3)  # no such kernel

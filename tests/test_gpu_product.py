@@ -93,9 +93,11 @@ def test_product_float_decomposed_weight(M):
 
 
 def test_product_same_bits_run_to_run_and_grouped_vs_single():
-    # the row accumulators add fixed-point shares: the same launch gives the same bits
-    # every time, and a grouped launch (another split of the units over the waves) the
-    # same bits as single-weight launches when every share is exact (dyadic pins)
+    # every workgroup stores its fp32 share of a row group in a slot of its own and the
+    # finishing pass adds the slots in workgroup order: the same launch gives the same
+    # bits every time, and a grouped launch (another split of the units over the
+    # workgroups) the same bits as single-weight launches when every share is exact
+    # (dyadic pins)
     shapes = [(1000, 1544), (256, 4096), (4096, 512)]
     n = 6
     ws = [(m, d, synth.dyadic_blocks(66, m, d, n, 16, j)) for j, (m, d) in enumerate(shapes)]
@@ -118,4 +120,31 @@ def test_product_rejects_more_than_32_tokens():
         y = torch.empty((33, 64), dtype=torch.float32, device="cuda")
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_forward(st.h, 0, x.data_ptr(), y.data_ptr(), 33, True, 0)
+        assert e.value.code == bsl.BSL_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("M,kind", [(2, 1), (3, 1), (4, 4), (5, 4), (32, 4), (33, 3)])
+def test_auto_takes_the_documented_kernel(M, kind):
+    # BSL_PATH_AUTO: the few-token kernel at 2 and 3 tokens, the product-index kernel from
+    # 4 to 32, the tile kernel from 33 (launch-count kinds 1, 4 and 3); exact either way
+    m, d, n = 200, 1544, 3
+    blocks = synth.dyadic_blocks(90, m, d, n, 16)
+    x = synth.integer_activations(91, M, d, -2, 2)
+    with Stack([(m, d, blocks)]) as st:
+        st.load([n])
+        before = np.array(bsl.bsl_launch_counts(st.h))
+        y = st.forward(0, x)
+        delta = np.array(bsl.bsl_launch_counts(st.h)) - before
+    assert delta.tolist() == [1 if i == kind else 0 for i in range(bsl.BSL_KERNEL_KINDS)]
+    assert np.array_equal(y, oracle.forward(x, blocks, n))
+
+
+def test_decode_path_rejects_more_than_4_tokens():
+    blocks = synth.synthetic_blocks(92, 64, 512, 2)
+    with Stack([(64, 512, blocks)], path=bsl.BSL_PATH_DECODE) as st:
+        st.load([2])
+        x = torch.zeros((5, 512), dtype=torch.float16, device="cuda")
+        y = torch.empty((5, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(bsl.BslError) as e:
+            bsl.bsl_forward(st.h, 0, x.data_ptr(), y.data_ptr(), 5, True, 0)
         assert e.value.code == bsl.BSL_EUNSUPPORTED

@@ -1,4 +1,5 @@
-"""The allocation-free forward (bsl_forward_group_static) against bsl_forward_group.
+"""The allocation-free forward (bsl_forward_group_static) against bsl_forward_group
+under BSL_PATH_DECODE (the single- and few-token kernels at 1 to 4 tokens).
 
 Two calls in a row on one device, the second with a smaller input, each compared with
 the existing entry point's output (same kernels, same launch configuration: identical
@@ -54,7 +55,7 @@ def test_static_forward_matches_group_forward(decode, kind):
     else:
         weights = [(m, d, synth.synthetic_blocks(63, m, d, n, 16, j)) for j, (m, d) in enumerate(SHAPES)]
         make_x = lambda M, d, j: synth.activations(64, M, d, j)  # noqa: E731
-    with Stack(weights, decode=decode) as st:
+    with Stack(weights, path=bsl.BSL_PATH_DECODE, decode=decode) as st:
         st.load([n] * len(SHAPES))
         # first call: every weight, 4 tokens; second call: a smaller input (2 weights, 1 token)
         for ws, M in (([0, 1, 2, 3], 4), ([3, 1], 1)):

@@ -2466,9 +2466,23 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
 // Finishing pass of a product-index launch: y[t][row] is the sum, in workgroup order,
 // of the shares of the workgroups whose (non-empty) unit ranges hold units of the row's
 // row group (zero for a weight without blocks).  The product kernel precedes this kernel
-// in the stream, so its stores are complete.
+// in the stream, so its stores are complete.  One workgroup per (row group, 32-row tile):
+// thread i reads floats 4 i .. 4 i + 3 of the tile's [16 registers][64 lanes] share (16
+// contiguous bytes per thread and share, skipped where every token is past M), adds the
+// shares in workgroup order, and the tile goes through LDS as [token][row], so that each
+// token's 32 rows are stored as one contiguous run.
 template <int R, int NB>
 __global__ __launch_bounds__(256) void product_finish_kernel(GroupArgs args) {
+  constexpr int TILES = kPxWaves * R;  // 32-row tiles of a row group
+  constexpr int GROUP_ROWS = TILES * 32;
+  __shared__ float tile[32][33];
+  const uint32_t g = blockIdx.x / TILES;  // row group of the launch
+  const int tau = (int)(blockIdx.x % TILES);  // tile wave * R + r
+  if (g >= args.total_groups) return;
+  int j = 0;
+  while (j + 1 < args.count && args.w[j + 1].rg_begin <= g) ++j;
+  const WeightDesc& W = args.w[j];
+  const uint32_t rg = g - W.rg_begin;
   const int M = args.M;
   const uint32_t U = args.total_units;
   const int lg = args.grid_log2;
@@ -2479,26 +2493,33 @@ __global__ __launch_bounds__(256) void product_finish_kernel(GroupArgs args) {
     while (range_start(o, U, lg) > u) --o;
     return o;
   };
-  constexpr int GROUP_ROWS = kPxWaves * R * 32;
-  for (int j = 0; j < args.count; ++j) {
-    const WeightDesc& W = args.w[j];
-    const uint64_t n = (uint64_t)W.m * (uint64_t)M;
-    const uint32_t per_rg = (uint32_t)(((W.nblocks + NB - 1) / NB) * W.nch);  // units of a row group
-    for (uint64_t e = (uint64_t)blockIdx.x * 256u + threadIdx.x; e < n; e += (uint64_t)gridDim.x * 256u) {
-      const int t = (int)(e / (uint64_t)W.m), row = (int)(e - (uint64_t)t * W.m);
-      float sum = 0.f;
-      if (per_rg > 0) {
-        const int rg = row / GROUP_ROWS, wr = row % GROUP_ROWS;
-        const int wave = wr >> 6, r = (wr >> 5) & (R - 1), mm = wr & 31;  // (R = 2)
-        const int v = ((mm >> 3) << 2) | (mm & 3), lane = 32 * ((mm >> 2) & 1) + t;
-        const uint32_t first = W.unit_begin + (uint32_t)rg * per_rg;
-        const size_t at = ((size_t)(wave * R + r) * 16 + v) * 64 + lane;
-        for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
-          if (range_start(o, U, lg) < range_start(o + 1, U, lg))
-            sum += args.part[((size_t)W.rg_begin + rg + o) * kPxPartFloats + at];
+  const int i = threadIdx.x;
+  const int v = i >> 4, lane0 = (i & 15) << 2;  // accumulator register, first of four lanes
+  const int h = lane0 >> 5, t0 = lane0 & 31;    // lane half (row bit 2), first token
+  const uint32_t per_rg = (uint32_t)(((W.nblocks + NB - 1) / NB) * W.nch);  // units of a row group
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  if (per_rg > 0 && t0 < M) {
+    const uint32_t first = W.unit_begin + rg * per_rg;
+    const float* share = args.part + (size_t)g * kPxPartFloats + (size_t)tau * 1024 + 4 * i;
+    for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
+      if (range_start(o, U, lg) < range_start(o + 1, U, lg)) {
+        const float4 p = *reinterpret_cast<const float4*>(share + (size_t)o * kPxPartFloats);
+        s0 += p.x;
+        s1 += p.y;
+        s2 += p.z;
+        s3 += p.w;
       }
-      store_y(W.y, (size_t)e, sum, args.y_fp32);  // y[t][row]
-    }
+  }
+  const int mm = ((v >> 2) << 3) | (h << 2) | (v & 3);  // row of the tile
+  tile[t0][mm] = s0;
+  tile[t0 + 1][mm] = s1;
+  tile[t0 + 2][mm] = s2;
+  tile[t0 + 3][mm] = s3;
+  __syncthreads();
+  const int row0 = (int)rg * GROUP_ROWS + tau * 32;
+  for (int e = i; e < M * 32; e += 256) {
+    const int t = e >> 5, r = e & 31;
+    if (row0 + r < W.m) store_y(W.y, (size_t)t * W.m + row0 + r, tile[t][r], args.y_fp32);  // y[t][row]
   }
 }
 static_assert(kPxTiles == 2, "product_finish_kernel indexes two tiles per wave");
@@ -2695,9 +2716,8 @@ int launch_product(const GroupArgs& args, void* stream) {
 }
 
 int launch_product_finish(const GroupArgs& args, void* stream) {
-  uint64_t n = 0;
-  for (int j = 0; j < args.count; ++j) n += (uint64_t)args.w[j].m * (uint64_t)args.M;
-  const unsigned blocks = (unsigned)std::min<uint64_t>(1024, std::max<uint64_t>(1, (n + 255) / 256));
+  if (args.total_groups == 0) return 0;
+  const unsigned blocks = args.total_groups * (unsigned)(kPxWaves * kPxTiles);  // one per (row group, 32-row tile)
   hipLaunchKernelGGL((product_finish_kernel<kPxTiles, kPxBatch>), dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), args);
   return (int)hipGetLastError();
 }

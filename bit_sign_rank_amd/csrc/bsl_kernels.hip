@@ -2501,14 +2501,23 @@ __global__ __launch_bounds__(256) void product_finish_kernel(GroupArgs args) {
   if (per_rg > 0 && t0 < M) {
     const uint32_t first = W.unit_begin + rg * per_rg;
     const float* share = args.part + (size_t)g * kPxPartFloats + (size_t)tau * 1024 + 4 * i;
-    for (uint32_t o = owner(first), oe = owner(first + per_rg - 1); o <= oe; ++o)
-      if (range_start(o, U, lg) < range_start(o + 1, U, lg)) {
-        const float4 p = *reinterpret_cast<const float4*>(share + (size_t)o * kPxPartFloats);
-        s0 += p.x;
-        s1 += p.y;
-        s2 += p.z;
-        s3 += p.w;
+    // four shares' loads in flight at once, then their additions in workgroup order
+    const uint32_t oe = owner(first + per_rg - 1);
+    for (uint32_t ob = owner(first); ob <= oe; ob += 4) {
+      float4 p[4];
+      bool ok[4];
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {
+        const uint32_t o = ob + q;
+        ok[q] = o <= oe && range_start(o, U, lg) < range_start(o + 1, U, lg);
+        p[q] = ok[q] ? *reinterpret_cast<const float4*>(share + (size_t)o * kPxPartFloats) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) if (ok[q]) {
+        s0 += p[q].x;
+        s1 += p[q].y;
+        s2 += p[q].z;
+        s3 += p[q].w;
+      }
+    }
   }
   const int mm = ((v >> 2) << 3) | (h << 2) | (v & 3);  // row of the tile
   tile[t0][mm] = s0;

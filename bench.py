@@ -747,9 +747,10 @@ def main() -> None:
         for label, lshapes, counts in (sets[:1] if args.profile_set else sets):
             for M in ((4,) if args.profile_set else (2, 3, 4)):
                 row = {"layer": label, "n": counts[0], "M": M,
-                       "auto_takes": "few-token" if M < 4 else "product-index (product_kernel<2, 2>)"}
+                       "auto_takes": ("few-token" + (" (down projection: product-index)" if label == "70B" and M == 3 else ""))
+                       if M < 4 else "product-index (product_kernel<2, 2>)"}
                 paths = [("few_token", bsl.BSL_PATH_DECODE), ("factored", bsl.BSL_PATH_FACTORED)]
-                if M == 4 and not args.profile_set:
+                if M >= 3 and not args.profile_set:  # (at 3 tokens AUTO differs from DECODE where a weight is wide)
                     paths.append(("auto", bsl.BSL_PATH_AUTO))
                 for name, path in paths:
                     log(f"few tokens: {label}-shaped layer, n={counts[0]}, M={M}, {name} path")

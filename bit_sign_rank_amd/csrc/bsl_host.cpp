@@ -1150,11 +1150,17 @@ int forward_impl(bsl_stack* s, int32_t count, const int32_t* weights, const void
     }
     if (use_static)
       return fail(BSL_EUNSUPPORTED, "bsl_forward_group_static: the activations of this group do not fit the few-token kernel's LDS");
+    // Under AUTO the wide weights take the product-index path (measured faster there than
+    // the factored multi-token kernel: a 28672-column down projection at 3 tokens);
+    // under DECODE the multi-token kernel.
+    const bool wide_product = s->path == BSL_PATH_AUTO && nw > 0;
     if (nn > 0 && nw > 0) {
       const int rc = forward_impl(s, nn, narrow, xn, yn, M, y_is_fp32, stream);
       if (rc != BSL_OK) return rc;
+      if (wide_product) return forward_product(s, nw, wide, xw, yw, M, y_is_fp32, stream);
       return forward_impl(s, nw, wide, xw, yw, M, y_is_fp32, stream);
     }
+    if (wide_product && nn == 0) return forward_product(s, count, weights, x, y, M, y_is_fp32, stream);
   }
   const int nt = M <= 2 ? 2 : (M <= 4 ? 4 : 8);  // tokens per multi-token item
   const int token_groups = (M + nt - 1) / nt;

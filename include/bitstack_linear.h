@@ -185,7 +185,7 @@ int bsl_forward(bsl_stack* s, int32_t w, const void* x, void* y, int32_t M, int3
  *     workgroups' shares of every row group in a fixed order into y;
  *   - on BSL_PATH_AUTO at M = 2..3 and BSL_PATH_DECODE at M = 2..4 when the group's
  *     activations do not fit the few-token kernel as a whole: then it is split into two
- *     forward launches (see bsl_set_path).
+ *     forwards (see bsl_set_path), the second on the product-index path under AUTO.
  *     An error returned after the first of the two was enqueued leaves the y[j] of the
  *     weights in that launch written and the others unspecified. */
 int bsl_forward_group(bsl_stack* s, int32_t count, const int32_t* weights, const void* const* x, void* const* y,
@@ -239,8 +239,10 @@ int bsl_forward_group_static(bsl_stack* s, int32_t count, const int32_t* weights
  *     its LDS (148 KiB per workgroup); in a grouped call that does not fit as a whole, the
  *     weights whose activations take at most half of it go to that kernel and the others
  *     to the factored multi-token kernel, in a second launch.
- *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 and 3 as under DECODE;
- *     PRODUCT for M = 4 to 32; TILE from M = 33 on. */
+ *   BSL_PATH_AUTO (the default): M = 1 as under FACTORED; M = 2 and 3 as under DECODE,
+ *     except that the weights whose activations take more than half of the few-token
+ *     kernel's LDS, when the group does not fit it as a whole, take PRODUCT instead of the
+ *     factored kernel; PRODUCT for M = 4 to 32; TILE from M = 33 on. */
 #define BSL_PATH_AUTO 0
 #define BSL_PATH_FACTORED 1
 #define BSL_PATH_TILE 2

@@ -485,24 +485,28 @@ def _counts(st):
     return np.array(bsl.bsl_launch_counts(st.h))
 
 
-@pytest.mark.parametrize("M", [3, 4])
-def test_few_tokens_grouped_split_bit_exact(M):
+@pytest.mark.parametrize("M,path,launches", [(3, "decode", [0, 1, 1, 0, 0]), (4, "decode", [0, 1, 1, 0, 0]),
+                                             (3, "auto", [0, 1, 0, 0, 1]),
+                                             (4, "auto", [0, 0, 0, 0, 1])])
+def test_few_tokens_grouped_split_bit_exact(M, path, launches):
+    # DECODE: the weight that does not fit the few-token kernel takes the factored
+    # multi-token kernel; AUTO: the product-index path (and every weight from 4 tokens on)
     ws = [(m, d, integer_blocks(m, d, max(n, 1), 60 + j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
     xs = [synth.integer_activations(61, M, d, -1, 1, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
-    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE if path == "decode" else bsl.BSL_PATH_AUTO) as st:
         st.load(SPLIT_COUNTS)
         before = _counts(st)
         ys = st.forward_group(list(range(5)), xs)
-        assert (_counts(st) - before).tolist() == [0, 1, 1, 0, 0]
+        assert (_counts(st) - before).tolist() == launches
     for j, ((m, d, blocks), n) in enumerate(zip(ws, SPLIT_COUNTS)):
         assert np.array_equal(ys[j], oracle.forward(xs[j], blocks, n)), (j, SPLIT_SHAPES[j], n)
 
 
-@pytest.mark.parametrize("M", [3, 4])
-def test_few_tokens_grouped_split_float_all_rows(M):
+@pytest.mark.parametrize("M,path", [(3, "decode"), (4, "decode"), (3, "auto")])
+def test_few_tokens_grouped_split_float_all_rows(M, path):
     ws = [(m, d, synth.synthetic_blocks(62, m, d, max(n, 1), 16, j)) for j, ((m, d), n) in enumerate(zip(SPLIT_SHAPES, SPLIT_COUNTS))]
     xs = [synth.activations(63, M, d, j) for j, (_, d) in enumerate(SPLIT_SHAPES)]
-    with Stack(ws, path=bsl.BSL_PATH_DECODE) as st:
+    with Stack(ws, path=bsl.BSL_PATH_DECODE if path == "decode" else bsl.BSL_PATH_AUTO) as st:
         st.load(SPLIT_COUNTS)
         ys = st.forward_group(list(range(5)), xs)
     for j, ((m, d, blocks), n) in enumerate(zip(ws, SPLIT_COUNTS)):
@@ -511,8 +515,9 @@ def test_few_tokens_grouped_split_float_all_rows(M):
             assert not ys[j].any()
             continue
         assert rel_err(ys[j], ref) <= REL_TOL
-        # exact products in the wave-private kernel; fp16 Z in the multi-token kernel
-        kind = "z16" if d == 28672 else "exact"
+        # exact products in the wave-private kernel; fp16 Z in the multi-token kernel, fp16
+        # U V^T products in the product-index kernel
+        kind = ("z16" if path == "decode" else "product") if d == 28672 else "exact"
         assert_elementwise(ys[j], ref, elem_factor(kind, n, d) * abs_bound(xs[j], blocks, n), f"weight {j} {SPLIT_SHAPES[j]}")
 
 

@@ -2357,11 +2357,12 @@ __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2
     for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
   auto flush = [&](const Cur& c) __attribute__((always_inline)) {
     float* slot = args.part + ((size_t)args.w[c.j].rg_begin + (size_t)c.rt + L) * kPxPartFloats;
+    const bool live = (lane & 31) < M;  // (the finishing pass reads tokens below M only)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int v = 0; v < 16; ++v)
-        slot[((wave * R + r) * 16 + v) * 64 + lane] = KA == 2 ? acc[r][0][v] + acc[r][KA - 1][v] : acc[r][0][v];
+        if (live) slot[((wave * R + r) * 16 + v) * 64 + lane] = KA == 2 ? acc[r][0][v] + acc[r][KA - 1][v] : acc[r][0][v];
 #pragma unroll
       for (int a = 0; a < KA; ++a) acc[r][a] = (float16v){};
     }

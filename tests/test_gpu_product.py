@@ -148,3 +148,19 @@ def test_decode_path_rejects_more_than_4_tokens():
         with pytest.raises(bsl.BslError) as e:
             bsl.bsl_forward(st.h, 0, x.data_ptr(), y.data_ptr(), 5, True, 0)
         assert e.value.code == bsl.BSL_EUNSUPPORTED
+
+
+def test_product_smaller_call_after_larger_leaves_no_stale_shares():
+    # the share slots keep the last call's contents and a call stores only the lanes of
+    # its own tokens: a 5-token call after a 32-token one on the same stack must not pick
+    # up the earlier call's tokens 5..31 (exact on dyadic blocks)
+    shapes = [(1000, 1544), (256, 4096)]
+    n = 5
+    ws = [(m, d, synth.dyadic_blocks(93, m, d, n, 16, j)) for j, (m, d) in enumerate(shapes)]
+    with Stack(ws, path=PRODUCT) as st:
+        st.load([n] * 2)
+        for M, seed in ((32, 94), (5, 95), (7, 96)):
+            xs = [synth.integer_activations(seed, M, d, -2, 2, j) for j, (_, d) in enumerate(shapes)]
+            ys = st.forward_group([0, 1], xs)
+            for j in range(2):
+                assert np.array_equal(ys[j], oracle.forward(xs[j], ws[j][2], n)), (M, j)
